@@ -1,0 +1,193 @@
+"""fp64 CPU oracle for causal attention with accumulated SO(2) rotations.
+
+TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's CPU
+baseline leg may import this package; the GPU library never does, and the two
+share no code.  The arithmetic lives in ``arp_oracle.c`` (plain C, fp64,
+OpenMP over rows); this module only marshals numpy arrays into it.
+
+Array conventions (numpy, C-contiguous):
+  q, k, v   [B, H, L, d]   float32, or uint16 holding bf16 bit patterns
+  phi       [B, Hphi, L, d/2] float32, Hphi in {1, H}
+  alibi     [H] float32 slopes (used only with the ALIBI flag)
+Outputs are float64.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+(brute-force route products, closed-form RoPE, shift invariance,
+orthogonality, textbook attention, closed-form softmax weights, the matched
+score of the method paper's App. B.6, and the RoPE post's worked numbers).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+# A test of the pins themselves may point this package at a deliberately
+# broken build of the same source (see tests/test_oracle_mutants.py).
+_LIB_OVERRIDE = os.environ.get("ARP_ORACLE_LIB")
+
+ROTATE_QK = 1
+ROTATE_V = 2
+ALIBI = 4
+SCAN_EXCLUSIVE = 16
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("heads", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+        ("phi_heads", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("scale", ctypes.c_double),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("phi", ctypes.c_void_p),
+        ("alibi_slopes", ctypes.c_void_p),
+    ]
+
+
+_LIB = None
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        path = _LIB_OVERRIDE or LIB_PATH
+        if not os.path.exists(path):
+            raise RuntimeError(f"oracle library missing: {path}; run `python oracle/build.py`")
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_angle_scan.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int, dp]
+        lib.oracle_angle_scan.restype = None
+        lib.oracle_wrap.argtypes = [ctypes.c_double]
+        lib.oracle_wrap.restype = ctypes.c_double
+        lib.oracle_wrap_array.argtypes = [dp, ctypes.c_int64, dp]
+        lib.oracle_wrap_array.restype = None
+        lib.oracle_rotate_rows.argtypes = [ctypes.c_void_p, ctypes.c_int32, dp, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int, dp]
+        lib.oracle_rotate_rows.restype = None
+        lib.oracle_theta.argtypes = [ctypes.POINTER(_Problem), dp]
+        lib.oracle_theta.restype = ctypes.c_int
+        lib.oracle_scores_row.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int64, dp]
+        lib.oracle_scores_row.restype = ctypes.c_int
+        lib.oracle_attention_rows.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p,
+                                              ctypes.c_int64, ctypes.c_int, dp]
+        lib.oracle_attention_rows.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def _dptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _io_dtype(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return DTYPE_F32
+    if a.dtype == np.uint16:
+        return DTYPE_BF16
+    raise TypeError(f"q/k/v must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def angle_scan(phi: np.ndarray, exclusive: bool = False) -> np.ndarray:
+    """Unwrapped fp64 prefix sums of phi along axis -2 (phi is [..., L, P] float32)."""
+    phi = np.ascontiguousarray(phi, dtype=np.float32)
+    L, P = phi.shape[-2], phi.shape[-1]
+    nseg = int(np.prod(phi.shape[:-2], dtype=np.int64)) if phi.ndim > 2 else 1
+    out = np.empty(phi.shape, dtype=np.float64)
+    _lib().oracle_angle_scan(phi.ctypes.data, nseg, L, P, int(exclusive), _dptr(out))
+    return out
+
+
+def wrap(x) -> np.ndarray:
+    """Angles reduced into [-pi, pi)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    _lib().oracle_wrap_array(_dptr(x), x.size, _dptr(out))
+    return out
+
+
+def rotate_rows(x: np.ndarray, angle: np.ndarray, inverse: bool = False) -> np.ndarray:
+    """R(angle) x per pair for rows of x ([..., d]); angle is [..., d/2] (any float dtype)."""
+    x = np.ascontiguousarray(x)
+    d = x.shape[-1]
+    nrows = x.size // d
+    ang = np.ascontiguousarray(angle, dtype=np.float64)
+    assert ang.size == nrows * (d // 2)
+    out = np.empty(x.shape, dtype=np.float64)
+    _lib().oracle_rotate_rows(x.ctypes.data, _io_dtype(x), _dptr(ang), nrows, d, int(inverse),
+                              _dptr(out))
+    return out
+
+
+class Problem:
+    """Holds the arrays of one attention problem and the C descriptor pointing at them."""
+
+    def __init__(self, q, k, v, phi, flags: int, scale: float | None = None, alibi=None):
+        self.q = np.ascontiguousarray(q)
+        self.k = np.ascontiguousarray(k)
+        self.v = np.ascontiguousarray(v)
+        self.phi = np.ascontiguousarray(phi, dtype=np.float32)
+        if self.q.shape != self.k.shape or self.q.shape != self.v.shape or self.q.ndim != 4:
+            raise ValueError("q, k, v must share one [B, H, L, d] shape")
+        if not (self.q.dtype == self.k.dtype == self.v.dtype):
+            raise ValueError("q, k, v must share one dtype")
+        B, H, L, d = self.q.shape
+        if self.phi.shape[0] != B or self.phi.shape[2:] != (L, d // 2) or self.phi.shape[1] not in (1, H):
+            raise ValueError(f"phi shape {self.phi.shape} does not match q {self.q.shape}")
+        self.alibi = None if alibi is None else np.ascontiguousarray(alibi, dtype=np.float32)
+        if flags & ALIBI and (self.alibi is None or self.alibi.shape != (H,)):
+            raise ValueError("ALIBI needs one slope per head")
+        self.shape = (B, H, L, d)
+        self.flags = int(flags)
+        self.scale = float(1.0 / np.sqrt(d) if scale is None else scale)
+        self.c = _Problem(B, H, L, d, self.phi.shape[1], _io_dtype(self.q), self.flags, self.scale,
+                          self.q.ctypes.data, self.k.ctypes.data, self.v.ctypes.data,
+                          self.phi.ctypes.data,
+                          None if self.alibi is None else self.alibi.ctypes.data)
+
+    def theta(self) -> np.ndarray:
+        B, H, L, d = self.shape
+        out = np.empty((B, self.phi.shape[1], L, d // 2), dtype=np.float64)
+        rc = _lib().oracle_theta(ctypes.byref(self.c), _dptr(out))
+        if rc:
+            raise RuntimeError(f"oracle_theta failed: {rc}")
+        return out
+
+    def scores_row(self, b: int, h: int, i: int) -> np.ndarray:
+        out = np.empty(i + 1, dtype=np.float64)
+        rc = _lib().oracle_scores_row(ctypes.byref(self.c), b, h, i, _dptr(out))
+        if rc:
+            raise RuntimeError(f"oracle_scores_row failed: {rc}")
+        return out
+
+    def rows(self, rows, nthreads: int = 0) -> np.ndarray:
+        """Output rows; rows holds flat indices (b*H + h)*L + i."""
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((rows.size, self.shape[3]), dtype=np.float64)
+        rc = _lib().oracle_attention_rows(ctypes.byref(self.c), rows.ctypes.data, rows.size,
+                                          int(nthreads), _dptr(out))
+        if rc:
+            raise RuntimeError(f"oracle_attention_rows failed: {rc}")
+        return out
+
+    def output(self, nthreads: int = 0) -> np.ndarray:
+        """The full output [B, H, L, d] (small problems only: O(L^2 d) per head)."""
+        B, H, L, d = self.shape
+        return self.rows(np.arange(B * H * L, dtype=np.int64), nthreads).reshape(B, H, L, d)
+
+
+def attention(q, k, v, phi, flags: int, scale=None, alibi=None, nthreads: int = 0) -> np.ndarray:
+    return Problem(q, k, v, phi, flags, scale, alibi).output(nthreads)

@@ -1,0 +1,318 @@
+/*
+ * arp_oracle.c -- plain fp64 CPU oracle for causal attention with accumulated
+ * SO(2) rotations.
+ *
+ * TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg call it; the GPU library never does, and the
+ * two share no source.  It is written to be read against the pages, not to be
+ * fast: every step is the plain definition, computed in double precision from
+ * the exact bits the GPU reads (fp32, or bf16 widened by a 16-bit shift).
+ *
+ * Sources (page title, then the place on it):
+ *  [ACC]  "Why Do Accumulated Transformations Extrapolate?" (arXiv 2606.24975)
+ *  [ADA]  "AdaRoPE: Not All Attention Heads Should Rotate and Scale Equally"
+ *         (arXiv 2607.19363)
+ *  [POST] "The RoPE decay curve everyone plots is noise ..." (dev.to)
+ *
+ * What is computed, step by step:
+ *  1. Accumulated angles.  Each position t carries a block-diagonal step
+ *     rotation with one angle phi_t[p] per two-dimensional block p; the
+ *     blocks commute, so the product of steps is a rotation by the summed
+ *     angle ([ACC] Sec. 5, "SO(2) notation").  The route from source j to
+ *     query i holds the steps j+1 .. i ([ACC] Sec. 2.2, eq. (6)), so the
+ *     angle attached to position t is the inclusive sum
+ *         Theta_t[p] = sum_{s <= t} phi_s[p],
+ *     and the route rotation is the difference Theta_i - Theta_j.
+ *     (ORACLE_SCAN_EXCLUSIVE gives the exclusive sum over s < t.)
+ *  2. Rotation.  Block p acts on the adjacent pair (x[2p], x[2p+1]) as
+ *         R(a) = [[cos a, -sin a], [sin a, cos a]]
+ *     ([ADA] Sec. 2.1 eq. (1) and the preliminaries' eq. (7)-(8); [POST] rope()).
+ *     q~_t = R(Theta_t) q_t, k~_t = R(Theta_t) k_t, and v~_t = R(Theta_t) v_t
+ *     when values are transported.  Then
+ *         <q~_i, k~_j> = q_i^T R(Theta_j - Theta_i) k_j = q_i^T P_{j->i} k_j,
+ *     the routed score of [ACC] eq. (7)-(8), with P_{j->i} a rotation by
+ *     minus the summed angles of steps j+1..i ([ACC] App. B.8, position-only
+ *     case; App. B.2 writes the step as e^{-i psi_t}).
+ *  3. Scores s_ij = scale * <q~_i, k~_j> - m_h (i - j) [distance bias on],
+ *     for the causal set j <= i ([ACC] eq. (2), (11); [ADA] eq. (5)).
+ *  4. Softmax over j <= i, computed in two passes: the row maximum M, then
+ *     w_ij = exp(s_ij - M) and l_i = sum_j w_ij ([ACC] eq. (2)).
+ *  5. Aggregation c_i = sum_j (w_ij / l_i) P_{j->i} v_j ([ACC] eq. (4)); with
+ *     value transport this is R(Theta_i)^T sum_j alpha_ij v~_j, without it the
+ *     plain sum of eq. (3).
+ */
+#include "arp_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_PI 3.14159265358979323846
+
+/* Widen one stored element to double.  bf16 is the top half of an fp32. */
+static double load_elem(const void* base, int32_t dtype, int64_t idx) {
+  if (dtype == ORACLE_DTYPE_F32) {
+    return (double)((const float*)base)[idx];
+  }
+  uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Step 1: prefix sum along the sequence, one running total per (segment, pair). */
+void oracle_angle_scan(const float* phi, int64_t nseg, int64_t seqlen, int64_t npairs,
+                       int exclusive, double* theta) {
+  for (int64_t s = 0; s < nseg; ++s) {
+    for (int64_t p = 0; p < npairs; ++p) {
+      double run = 0.0;
+      for (int64_t t = 0; t < seqlen; ++t) {
+        int64_t idx = (s * seqlen + t) * npairs + p;
+        if (exclusive) {
+          theta[idx] = run;
+          run += (double)phi[idx];
+        } else {
+          run += (double)phi[idx];
+          theta[idx] = run;
+        }
+      }
+    }
+  }
+}
+
+/* x - 2 pi k with k chosen so the result lies in [-pi, pi). */
+double oracle_wrap(double x) {
+  const double two_pi = 2.0 * ORACLE_PI;
+  double r = x - two_pi * floor((x + ORACLE_PI) / two_pi);
+  if (r < -ORACLE_PI) r += two_pi;
+  if (r >= ORACLE_PI) r -= two_pi;
+  return r;
+}
+
+void oracle_wrap_array(const double* x, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_wrap(x[i]);
+}
+
+/* Step 2 for one vector: y = R(a) x per pair, or R(a)^T x when inverse. */
+static void rotate_vec(const double* x, const double* angle, int64_t npairs, int inverse,
+                       double* y) {
+  for (int64_t p = 0; p < npairs; ++p) {
+    double c = cos(angle[p]);
+    double s = sin(angle[p]);
+    if (inverse) s = -s;
+    double a = x[2 * p];
+    double b = x[2 * p + 1];
+    y[2 * p] = a * c - b * s;
+    y[2 * p + 1] = a * s + b * c;
+  }
+}
+
+void oracle_rotate_rows(const void* x, int32_t io_dtype, const double* angle, int64_t nrows,
+                        int64_t dim, int inverse, double* out) {
+  int64_t npairs = dim / 2;
+  double* row = (double*)malloc(sizeof(double) * (size_t)dim);
+  if (!row) return;
+  for (int64_t r = 0; r < nrows; ++r) {
+    for (int64_t c = 0; c < dim; ++c) row[c] = load_elem(x, io_dtype, r * dim + c);
+    rotate_vec(row, angle + r * npairs, npairs, inverse, out + r * dim);
+  }
+  free(row);
+}
+
+static int check_problem(const oracle_problem* p) {
+  if (!p || p->batch <= 0 || p->heads <= 0 || p->seqlen <= 0 || p->head_dim <= 0) return ORACLE_ERR_ARG;
+  if (p->head_dim % 2 != 0) return ORACLE_ERR_ARG;
+  if (p->phi_heads != 1 && p->phi_heads != p->heads) return ORACLE_ERR_ARG;
+  if (p->io_dtype != ORACLE_DTYPE_F32 && p->io_dtype != ORACLE_DTYPE_BF16) return ORACLE_ERR_ARG;
+  if (!p->q || !p->k || !p->v || !p->phi) return ORACLE_ERR_ARG;
+  if ((p->flags & ORACLE_ALIBI) && !p->alibi_slopes) return ORACLE_ERR_ARG;
+  return ORACLE_OK;
+}
+
+int oracle_theta(const oracle_problem* p, double* theta) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  oracle_angle_scan(p->phi, p->batch * p->phi_heads, p->seqlen, p->head_dim / 2,
+                    (p->flags & ORACLE_SCAN_EXCLUSIVE) != 0, theta);
+  return ORACLE_OK;
+}
+
+/* Everything one (b, h) needs for rows i <= imax: unwrapped angles, and the
+ * rotated keys and values of positions 0..imax. */
+typedef struct head_state {
+  int64_t n;        /* positions held: imax + 1 */
+  double* theta;    /* [n, P] */
+  double* krot;     /* [n, d] */
+  double* vrot;     /* [n, d] */
+} head_state;
+
+static void head_free(head_state* hs) {
+  free(hs->theta);
+  free(hs->krot);
+  free(hs->vrot);
+  memset(hs, 0, sizeof *hs);
+}
+
+static int head_build(const oracle_problem* p, int64_t b, int64_t h, int64_t imax, head_state* hs) {
+  const int64_t d = p->head_dim, P = d / 2, L = p->seqlen;
+  const int64_t hphi = (p->phi_heads == 1) ? 0 : h;
+  const int64_t n = imax + 1;
+  memset(hs, 0, sizeof *hs);
+  hs->n = n;
+  hs->theta = (double*)malloc(sizeof(double) * (size_t)(n * P));
+  hs->krot = (double*)malloc(sizeof(double) * (size_t)(n * d));
+  hs->vrot = (double*)malloc(sizeof(double) * (size_t)(n * d));
+  if (!hs->theta || !hs->krot || !hs->vrot) {
+    head_free(hs);
+    return ORACLE_ERR_NOMEM;
+  }
+  /* Step 1 on this head's angle stream (only the first n positions are needed). */
+  const float* phi = p->phi + (b * p->phi_heads + hphi) * L * P;
+  oracle_angle_scan(phi, 1, n, P, (p->flags & ORACLE_SCAN_EXCLUSIVE) != 0, hs->theta);
+  /* Step 2 on keys and values. */
+  const int64_t base = ((b * p->heads + h) * L) * d;
+  double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
+  if (!tmp) {
+    head_free(hs);
+    return ORACLE_ERR_NOMEM;
+  }
+  for (int64_t j = 0; j < n; ++j) {
+    for (int64_t c = 0; c < d; ++c) tmp[c] = load_elem(p->k, p->io_dtype, base + j * d + c);
+    if (p->flags & ORACLE_ROTATE_QK) {
+      rotate_vec(tmp, hs->theta + j * P, P, 0, hs->krot + j * d);
+    } else {
+      memcpy(hs->krot + j * d, tmp, sizeof(double) * (size_t)d);
+    }
+    for (int64_t c = 0; c < d; ++c) tmp[c] = load_elem(p->v, p->io_dtype, base + j * d + c);
+    if (p->flags & ORACLE_ROTATE_V) {
+      rotate_vec(tmp, hs->theta + j * P, P, 0, hs->vrot + j * d);
+    } else {
+      memcpy(hs->vrot + j * d, tmp, sizeof(double) * (size_t)d);
+    }
+  }
+  free(tmp);
+  return ORACLE_OK;
+}
+
+/* Step 3 for row i: scores[j] for j = 0..i.  qrot is scratch of length d. */
+static void row_scores(const oracle_problem* p, const head_state* hs, int64_t b, int64_t h,
+                       int64_t i, double* qrot, double* scores) {
+  const int64_t d = p->head_dim, P = d / 2, L = p->seqlen;
+  const int64_t base = ((b * p->heads + h) * L) * d;
+  double* qraw = qrot + d; /* caller gives 2*d doubles */
+  for (int64_t c = 0; c < d; ++c) qraw[c] = load_elem(p->q, p->io_dtype, base + i * d + c);
+  if (p->flags & ORACLE_ROTATE_QK) {
+    rotate_vec(qraw, hs->theta + i * P, P, 0, qrot);
+  } else {
+    memcpy(qrot, qraw, sizeof(double) * (size_t)d);
+  }
+  const double slope = (p->flags & ORACLE_ALIBI) ? (double)p->alibi_slopes[h] : 0.0;
+  for (int64_t j = 0; j <= i; ++j) {
+    const double* kj = hs->krot + j * d;
+    double dot = 0.0;
+    for (int64_t c = 0; c < d; ++c) dot += qrot[c] * kj[c];
+    scores[j] = p->scale * dot - slope * (double)(i - j);
+  }
+}
+
+int oracle_scores_row(const oracle_problem* p, int64_t b, int64_t h, int64_t i, double* out) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (b < 0 || b >= p->batch || h < 0 || h >= p->heads || i < 0 || i >= p->seqlen) return ORACLE_ERR_ARG;
+  head_state hs;
+  rc = head_build(p, b, h, i, &hs);
+  if (rc) return rc;
+  double* q2 = (double*)malloc(sizeof(double) * (size_t)(2 * p->head_dim));
+  if (!q2) {
+    head_free(&hs);
+    return ORACLE_ERR_NOMEM;
+  }
+  row_scores(p, &hs, b, h, i, q2, out);
+  free(q2);
+  head_free(&hs);
+  return ORACLE_OK;
+}
+
+/* Steps 3-5 for one row. */
+static int attention_row(const oracle_problem* p, const head_state* hs, int64_t b, int64_t h,
+                         int64_t i, double* out) {
+  const int64_t d = p->head_dim, P = d / 2;
+  double* scores = (double*)malloc(sizeof(double) * (size_t)(i + 1));
+  double* work = (double*)malloc(sizeof(double) * (size_t)(3 * d));
+  if (!scores || !work) {
+    free(scores);
+    free(work);
+    return ORACLE_ERR_NOMEM;
+  }
+  double* qrot = work;      /* 2*d: rotated query + raw query */
+  double* acc = work + 2 * d;
+  row_scores(p, hs, b, h, i, qrot, scores);
+
+  /* Step 4, pass 1: the row maximum over the causal set. */
+  double m = scores[0];
+  for (int64_t j = 1; j <= i; ++j)
+    if (scores[j] > m) m = scores[j];
+  /* Step 4, pass 2, and step 5: weights, their sum, and the weighted values. */
+  double l = 0.0;
+  for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
+  for (int64_t j = 0; j <= i; ++j) {
+    double w = exp(scores[j] - m);
+    l += w;
+    const double* vj = hs->vrot + j * d;
+    for (int64_t c = 0; c < d; ++c) acc[c] += w * vj[c];
+  }
+  for (int64_t c = 0; c < d; ++c) acc[c] /= l;
+  if (p->flags & ORACLE_ROTATE_V) {
+    /* Bring the sum of R(Theta_j) v_j back to the query's frame: R(Theta_i)^T. */
+    rotate_vec(acc, hs->theta + i * P, P, 1, out);
+  } else {
+    memcpy(out, acc, sizeof(double) * (size_t)d);
+  }
+  free(scores);
+  free(work);
+  return ORACLE_OK;
+}
+
+int oracle_attention_rows(const oracle_problem* p, const int64_t* rows, int64_t nrows,
+                          int nthreads, double* out) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  const int64_t L = p->seqlen, BH = p->batch * p->heads;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= BH * L) return ORACLE_ERR_ARG;
+
+  /* Highest query position requested per (b, h). */
+  int64_t* imax = (int64_t*)malloc(sizeof(int64_t) * (size_t)BH);
+  if (!imax) return ORACLE_ERR_NOMEM;
+  for (int64_t bh = 0; bh < BH; ++bh) imax[bh] = -1;
+  for (int64_t r = 0; r < nrows; ++r) {
+    int64_t bh = rows[r] / L, i = rows[r] % L;
+    if (i > imax[bh]) imax[bh] = i;
+  }
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  for (int64_t bh = 0; bh < BH && rc == ORACLE_OK; ++bh) {
+    if (imax[bh] < 0) continue;
+    const int64_t b = bh / p->heads, h = bh % p->heads;
+    head_state hs;
+    rc = head_build(p, b, h, imax[bh], &hs);
+    if (rc) break;
+    int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (int64_t r = 0; r < nrows; ++r) {
+      if (rows[r] / L != bh) continue;
+      err |= attention_row(p, &hs, b, h, rows[r] % L, out + r * p->head_dim);
+    }
+    head_free(&hs);
+    rc = err;
+  }
+  free(imax);
+  return rc;
+}

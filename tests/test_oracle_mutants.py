@@ -1,0 +1,51 @@
+"""The pins must bite: plant one plausible mistake at a time into a copy of
+the oracle's C source (CPU only), build it, and check that the pin suite
+fails against it.  The committed oracle is never modified."""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "arp_oracle.c")
+
+# (name, text in the source, replacement)
+MUTANTS = [
+    ("sine sign", "y[2 * p] = a * c - b * s;", "y[2 * p] = a * c + b * s;"),
+    ("exclusive route", "run += (double)phi[idx];\n          theta[idx] = run;",
+     "theta[idx] = run;\n          run += (double)phi[idx];"),
+    ("no value un-rotation", "rotate_vec(acc, hs->theta + i * P, P, 1, out);",
+     "memcpy(out, acc, sizeof(double) * (size_t)d);"),
+    ("diagonal masked", "for (int64_t j = 0; j <= i; ++j) {\n    double w",
+     "for (int64_t j = 0; j < i; ++j) {\n    double w"),
+    ("bias sign", "scores[j] = p->scale * dot - slope * (double)(i - j);",
+     "scores[j] = p->scale * dot + slope * (double)(i - j);"),
+    ("scale dropped", "scores[j] = p->scale * dot - slope", "scores[j] = dot - slope"),
+    ("un-rotation direction", "rotate_vec(acc, hs->theta + i * P, P, 1, out);",
+     "rotate_vec(acc, hs->theta + i * P, P, 0, out);"),
+    ("keys not rotated", "rotate_vec(tmp, hs->theta + j * P, P, 0, hs->krot + j * d);\n    } else {\n      memcpy(hs->krot",
+     "memcpy(hs->krot + j * d, tmp, sizeof(double) * (size_t)d);\n    } else {\n      memcpy(hs->krot"),
+    ("pair layout half-split", "double b = x[2 * p + 1];", "double b = x[p + npairs];"),
+    ("bf16 decode shift", "<< 16;", "<< 15;"),
+    ("softmax max not subtracted", "double w = exp(scores[j] - m);", "double w = exp(scores[j] - 1.0);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_fail_on_planted_mistake(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name!r} not found"
+    mutant = src.replace(old, new, 1)
+    c_path = tmp_path / "mutant.c"
+    c_path.write_text(mutant)
+    so_path = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-w",
+                    "-I", os.path.join(ROOT, "oracle"), str(c_path), "-o", str(so_path), "-lm"],
+                   check=True)
+    env = dict(os.environ, ARP_ORACLE_LIB=str(so_path))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"no pin caught the planted mistake {name!r}:\n{r.stdout[-2000:]}"
