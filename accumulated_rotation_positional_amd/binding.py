@@ -1,0 +1,239 @@
+"""ctypes binding of libarp.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (``include/arp.h``).  torch is used for device memory
+and the current stream, nothing else.  There is no CPU fallback: if the
+library is missing, or a tensor is not on a GPU, the call raises.
+
+Tensor conventions (C-contiguous, on the GPU):
+  q, k, v, o   [B, H, L, d]   float32 or bfloat16 (all the same dtype)
+  phi, theta   [B, Hphi, L, d/2] float32, Hphi in {1, H}
+  alibi        [H] float32 slopes
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libarp.so")
+
+# Status codes and flags of include/arp.h.
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_WORKSPACE, ERR_HIP = range(6)
+DTYPE_F32, DTYPE_BF16 = 0, 1
+ROTATE_QK = 0x1
+ROTATE_V = 0x2
+ALIBI = 0x4
+PHI_SHARED_HEADS = 0x8
+SCAN_EXCLUSIVE = 0x10
+FUSED_ROTATION = 0x20
+
+# Every function the header declares (tests check the library exports them all).
+EXPORTS = ("arp_abi_version", "arp_status_string", "arp_check", "arp_scan_state_bytes",
+           "arp_workspace_bytes",
+           "arp_angle_scan", "arp_rotate_qkv", "arp_attn_rotated", "arp_attn_fwd",
+           "arp_forward", "arp_rotate")
+
+
+class ArpError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("scale", ctypes.c_float), ("reserved", ctypes.c_int32)]
+
+
+_LIB = None
+_LOCK = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """Load libarp.so once; raise if it has not been built."""
+    global _LIB
+    with _LOCK:
+        if _LIB is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                                   "`python -c 'import __graft_entry__ as g; g.build()'`")
+            L = ctypes.CDLL(LIB_PATH)
+            P, S, D = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Desc)
+            sig = {
+                "arp_abi_version": ([], ctypes.c_int),
+                "arp_status_string": ([ctypes.c_int], ctypes.c_char_p),
+                "arp_check": ([D], ctypes.c_int),
+                "arp_scan_state_bytes": ([D], S),
+                "arp_workspace_bytes": ([D], S),
+                "arp_angle_scan": ([D, P, P, P, S, P], ctypes.c_int),
+                "arp_rotate_qkv": ([D, P, P, P, P, P, S, P], ctypes.c_int),
+                "arp_attn_rotated": ([D, P, P, P, P, S, P], ctypes.c_int),
+                "arp_attn_fwd": ([D, P, P, P, P, P, P, P, S, P], ctypes.c_int),
+                "arp_forward": ([D, P, P, P, P, P, P, P, P, S, P, S, P], ctypes.c_int),
+                "arp_rotate": ([D, P, P, P, ctypes.c_int, P], ctypes.c_int),
+            }
+            for name, (args, res) in sig.items():
+                f = getattr(L, name)
+                f.argtypes, f.restype = args, res
+            _LIB = L
+    return _LIB
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise ArpError(fn, status, lib().arp_status_string(status).decode())
+
+
+def make_desc(batch: int, heads: int, seqlen: int, head_dim: int, dtype, flags: int,
+              scale: float | None = None) -> Desc:
+    if dtype in (torch.float32, "f32", DTYPE_F32):
+        code = DTYPE_F32
+    elif dtype in (torch.bfloat16, "bf16", DTYPE_BF16):
+        code = DTYPE_BF16
+    else:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return Desc(batch, heads, seqlen, head_dim, code, flags, 0.0 if scale is None else scale, 0)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _require_gpu(*ts) -> None:
+    for t in ts:
+        if t is not None:
+            _ptr(t)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def flags_for(*, rotate_qk: bool = True, rotate_v: bool = False, alibi: bool = False,
+              shared_phi: bool = False, exclusive: bool = False, fused: bool = False) -> int:
+    return ((ROTATE_QK if rotate_qk else 0) | (ROTATE_V if rotate_v else 0) |
+            (ALIBI if alibi else 0) | (PHI_SHARED_HEADS if shared_phi else 0) |
+            (SCAN_EXCLUSIVE if exclusive else 0) | (FUSED_ROTATION if fused else 0))
+
+
+def desc_for(q: torch.Tensor, flags: int, scale: float | None = None) -> Desc:
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d]")
+    B, H, L, d = q.shape
+    return make_desc(B, H, L, d, q.dtype, flags, scale)
+
+
+def workspace_bytes(desc: Desc) -> int:
+    return int(lib().arp_workspace_bytes(ctypes.byref(desc)))
+
+
+def scan_state_bytes(desc: Desc) -> int:
+    return int(lib().arp_scan_state_bytes(ctypes.byref(desc)))
+
+
+_STATE: dict = {}
+_WS: dict = {}
+
+
+def scan_state(desc: Desc, device: torch.device) -> torch.Tensor:
+    """The angle scan's look-back state, zero-filled once and cached per
+    (device, stream); every completed scan leaves it zeroed again, so one buffer
+    serves every later call on that stream that fits in it."""
+    need = max(scan_state_bytes(desc), 256)
+    key = (device.index, _stream(device))
+    st = _STATE.get(key)
+    if st is None or st.numel() < need:
+        st = torch.zeros(need, dtype=torch.uint8, device=device)
+        _STATE[key] = st
+    return st
+
+
+def workspace(desc: Desc, device: torch.device) -> torch.Tensor:
+    """Operand workspace (rotated bf16 q/k/v of the pre-rotation path), cached
+    per (device, stream); needs no initialisation."""
+    need = max(workspace_bytes(desc), 256)
+    key = (device.index, _stream(device))
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < need:
+        ws = None
+        _WS.pop(key, None)
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        _WS[key] = ws
+    return ws
+
+
+def angle_scan(phi: torch.Tensor, desc: Desc, theta: torch.Tensor | None = None,
+               state: torch.Tensor | None = None) -> torch.Tensor:
+    _require_gpu(phi, theta, state)
+    theta = torch.empty_like(phi) if theta is None else theta
+    state = scan_state(desc, phi.device) if state is None else state
+    _check("arp_angle_scan", lib().arp_angle_scan(ctypes.byref(desc), _ptr(phi), _ptr(theta),
+                                                  _ptr(state), state.numel(), _stream(phi.device)))
+    return theta
+
+
+def rotate_qkv(q, k, v, theta, desc: Desc, ws: torch.Tensor | None = None) -> torch.Tensor:
+    _require_gpu(q, k, v, theta, ws)
+    ws = workspace(desc, q.device) if ws is None else ws
+    _check("arp_rotate_qkv", lib().arp_rotate_qkv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                                  _ptr(theta), _ptr(ws), ws.numel(),
+                                                  _stream(q.device)))
+    return ws
+
+
+def attn_rotated(theta, alibi, out, desc: Desc, ws: torch.Tensor) -> torch.Tensor:
+    _require_gpu(theta, alibi, out, ws)
+    _check("arp_attn_rotated", lib().arp_attn_rotated(ctypes.byref(desc), _ptr(theta), _ptr(alibi),
+                                                      _ptr(out), _ptr(ws), ws.numel(),
+                                                      _stream(out.device)))
+    return out
+
+
+def attn_fwd(q, k, v, theta, desc: Desc, alibi=None, out=None, ws=None) -> torch.Tensor:
+    _require_gpu(q, k, v, theta, alibi, out, ws)
+    out = torch.empty_like(q) if out is None else out
+    ws = workspace(desc, q.device) if ws is None else ws
+    _check("arp_attn_fwd", lib().arp_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(theta), _ptr(alibi), _ptr(out), _ptr(ws),
+                                              ws.numel(), _stream(q.device)))
+    return out
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.Tensor, *,
+            rotate_qk: bool = True, rotate_v: bool = False, alibi: torch.Tensor | None = None,
+            scale: float | None = None, exclusive: bool = False, fused: bool = False,
+            out: torch.Tensor | None = None, theta: torch.Tensor | None = None,
+            state: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """(q, k, v, phi, flags) -> (o, theta): the whole forward pass on the GPU."""
+    _require_gpu(q, k, v, phi, alibi, out, theta, state, ws)
+    flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi is not None,
+                      shared_phi=phi.shape[1] == 1 and q.shape[1] != 1, exclusive=exclusive,
+                      fused=fused)
+    desc = desc_for(q, flags, scale)
+    out = torch.empty_like(q) if out is None else out
+    theta = torch.empty_like(phi) if theta is None else theta
+    state = scan_state(desc, q.device) if state is None else state
+    ws = workspace(desc, q.device) if ws is None else ws
+    _check("arp_forward", lib().arp_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(phi), _ptr(alibi), _ptr(theta), _ptr(out),
+                                            _ptr(state), state.numel(), _ptr(ws), ws.numel(),
+                                            _stream(q.device)))
+    return out, theta
+
+
+def rotate(x: torch.Tensor, theta: torch.Tensor, desc: Desc, inverse: bool = False) -> torch.Tensor:
+    out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _check("arp_rotate", lib().arp_rotate(ctypes.byref(desc), _ptr(x), _ptr(theta), _ptr(out),
+                                          int(inverse), _stream(x.device)))
+    return out

@@ -1,0 +1,232 @@
+// api.hip -- the C ABI of libarp.so (declared in include/arp.h).
+//
+// Host side only: validate the descriptor and pointers, derive the problem
+// geometry, carve the caller's workspace, and enqueue kernels on the caller's
+// stream.  Nothing here allocates, synchronises, or touches device memory
+// from the host.
+#include <math.h>
+#include <string.h>
+
+#include "arp_internal.hpp"
+
+namespace arp {
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+arp_status make_geometry(const arp_desc* d, Geometry* g) {
+  if (d == nullptr) return ARP_ERR_INVALID_ARG;
+  if (d->batch <= 0 || d->heads <= 0 || d->seqlen <= 0 || d->head_dim <= 0) return ARP_ERR_INVALID_ARG;
+  if (d->head_dim % 2 != 0) return ARP_ERR_INVALID_ARG;
+  if (d->dtype != ARP_DTYPE_F32 && d->dtype != ARP_DTYPE_BF16) return ARP_ERR_INVALID_ARG;
+  if ((d->flags & ~ARP_ALL_FLAGS) != 0u) return ARP_ERR_INVALID_ARG;
+  if (d->reserved != 0) return ARP_ERR_INVALID_ARG;
+  if (!(d->scale == d->scale) || isinf(d->scale)) return ARP_ERR_INVALID_ARG;
+  // Sizes: every tensor index must fit comfortably in 64 bits and the grids in
+  // their limits; the sequence is capped at 2^24 tokens.
+  if (d->seqlen > (1 << 24) || (long long)d->batch * d->heads > 65535) return ARP_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return ARP_ERR_UNSUPPORTED;
+  g->B = d->batch;
+  g->H = d->heads;
+  g->L = d->seqlen;
+  g->D = d->head_dim;
+  g->P = d->head_dim / 2;
+  g->Hphi = (d->flags & ARP_PHI_SHARED_HEADS) ? 1 : d->heads;
+  g->dtype = d->dtype;
+  g->flags = d->flags;
+  g->scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->head_dim);
+  g->Lp = (int)(((long long)d->seqlen + 255) / 256 * 256);
+  return ARP_OK;
+}
+
+bool needs_operands(const Geometry& g) {
+  return g.dtype == ARP_DTYPE_BF16 && !(g.flags & ARP_FUSED_ROTATION);
+}
+
+arp_status check_buffer(const void* p, size_t have, size_t need) {
+  if (need == 0) return ARP_OK;
+  if (p == nullptr || have < need) return ARP_ERR_WORKSPACE;
+  if (((uintptr_t)p & (ALIGN - 1)) != 0) return ARP_ERR_ALIGNMENT;
+  return ARP_OK;
+}
+arp_status check_ws(const Geometry& g, const void* ws, size_t bytes) {
+  return check_buffer(ws, bytes, workspace_layout(g).total);
+}
+arp_status check_scan_state(const Geometry& g, const void* st, size_t bytes) {
+  return check_buffer(st, bytes, align_up(scan_state_bytes(g)));
+}
+
+arp_status hip_status(hipError_t e) { return e == hipSuccess ? ARP_OK : ARP_ERR_HIP; }
+arp_status fused_status(hipError_t e) {
+  return e == hipErrorNotSupported ? ARP_ERR_UNSUPPORTED : hip_status(e);
+}
+
+bool rotates(const Geometry& g) { return (g.flags & (ARP_ROTATE_QK | ARP_ROTATE_V)) != 0; }
+
+}  // namespace
+
+WorkspaceLayout workspace_layout(const Geometry& g) {
+  WorkspaceLayout lay{};
+  size_t off = 0;
+  if (needs_operands(g)) {
+    lay.operand_bytes = align_up((size_t)g.B * g.H * g.Lp * g.D * sizeof(uint16_t));
+    lay.q_off = off;
+    lay.k_off = off + lay.operand_bytes;
+    lay.vt_off = off + 2 * lay.operand_bytes;
+    off += 3 * lay.operand_bytes;
+  }
+  lay.total = off;
+  return lay;
+}
+
+}  // namespace arp
+
+using namespace arp;
+
+extern "C" {
+
+int arp_abi_version(void) { return ARP_ABI_VERSION; }
+
+const char* arp_status_string(int status) {
+  switch (status) {
+    case ARP_OK: return "ok";
+    case ARP_ERR_INVALID_ARG: return "invalid argument";
+    case ARP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ARP_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case ARP_ERR_WORKSPACE: return "workspace missing or too small";
+    case ARP_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+arp_status arp_check(const arp_desc* desc) {
+  Geometry g;
+  return make_geometry(desc, &g);
+}
+
+size_t arp_scan_state_bytes(const arp_desc* desc) {
+  Geometry g;
+  if (make_geometry(desc, &g) != ARP_OK) return 0;
+  return align_up(scan_state_bytes(g));
+}
+
+size_t arp_workspace_bytes(const arp_desc* desc) {
+  Geometry g;
+  if (make_geometry(desc, &g) != ARP_OK) return 0;
+  return workspace_layout(g).total;
+}
+
+arp_status arp_angle_scan(const arp_desc* desc, const float* phi, float* theta, void* scan_state,
+                          size_t scan_state_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (phi == nullptr || theta == nullptr) return ARP_ERR_INVALID_ARG;
+  if (!aligned16(phi) || !aligned16(theta)) return ARP_ERR_ALIGNMENT;
+  if ((st = check_scan_state(g, scan_state, scan_state_bytes)) != ARP_OK) return st;
+  return hip_status(launch_angle_scan(g, phi, theta, scan_state, (hipStream_t)stream));
+}
+
+arp_status arp_rotate_qkv(const arp_desc* desc, const void* q, const void* k, const void* v,
+                          const float* theta, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (!needs_operands(g)) return ARP_ERR_UNSUPPORTED;
+  if (q == nullptr || k == nullptr || v == nullptr || (rotates(g) && theta == nullptr))
+    return ARP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (theta && !aligned16(theta)))
+    return ARP_ERR_ALIGNMENT;
+  if ((st = check_ws(g, workspace, workspace_bytes)) != ARP_OK) return st;
+  const WorkspaceLayout lay = workspace_layout(g);
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(launch_rotate_qkv(g, q, k, v, theta, reinterpret_cast<uint16_t*>(ws + lay.q_off),
+                                      reinterpret_cast<uint16_t*>(ws + lay.k_off),
+                                      reinterpret_cast<uint16_t*>(ws + lay.vt_off),
+                                      (hipStream_t)stream));
+}
+
+arp_status arp_attn_rotated(const arp_desc* desc, const float* theta, const float* alibi, void* o,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (!needs_operands(g)) return ARP_ERR_UNSUPPORTED;
+  if (o == nullptr || ((g.flags & ARP_ROTATE_V) && theta == nullptr) ||
+      ((g.flags & ARP_ALIBI) && alibi == nullptr))
+    return ARP_ERR_INVALID_ARG;
+  if (!aligned16(o) || (theta && !aligned16(theta)) || (alibi && !aligned16(alibi)))
+    return ARP_ERR_ALIGNMENT;
+  if ((st = check_ws(g, workspace, workspace_bytes)) != ARP_OK) return st;
+  const WorkspaceLayout lay = workspace_layout(g);
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(launch_attn_bf16_rotated(
+      g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
+      reinterpret_cast<const uint16_t*>(ws + lay.k_off),
+      reinterpret_cast<const uint16_t*>(ws + lay.vt_off), theta, alibi,
+      static_cast<uint16_t*>(o), (hipStream_t)stream));
+}
+
+arp_status arp_attn_fwd(const arp_desc* desc, const void* q, const void* k, const void* v,
+                        const float* theta, const float* alibi, void* o, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr ||
+      (rotates(g) && theta == nullptr) || ((g.flags & ARP_ALIBI) && alibi == nullptr))
+    return ARP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (theta && !aligned16(theta)) || (alibi && !aligned16(alibi)))
+    return ARP_ERR_ALIGNMENT;
+  if ((st = check_ws(g, workspace, workspace_bytes)) != ARP_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (g.dtype == ARP_DTYPE_F32)
+    return hip_status(launch_attn_f32(g, static_cast<const float*>(q), static_cast<const float*>(k),
+                                      static_cast<const float*>(v), theta, alibi,
+                                      static_cast<float*>(o), s));
+  if (g.flags & ARP_FUSED_ROTATION)
+    return fused_status(launch_attn_bf16_fused(
+        g, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+        static_cast<const uint16_t*>(v), theta, alibi, static_cast<uint16_t*>(o), s));
+  st = arp_rotate_qkv(desc, q, k, v, theta, workspace, workspace_bytes, stream);
+  if (st != ARP_OK) return st;
+  return arp_attn_rotated(desc, theta, alibi, o, workspace, workspace_bytes, stream);
+}
+
+arp_status arp_forward(const arp_desc* desc, const void* q, const void* k, const void* v,
+                       const float* phi, const float* alibi, float* theta, void* o,
+                       void* scan_state, size_t scan_state_bytes, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || phi == nullptr ||
+      theta == nullptr || ((g.flags & ARP_ALIBI) && alibi == nullptr))
+    return ARP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(phi) ||
+      !aligned16(theta) || (alibi && !aligned16(alibi)))
+    return ARP_ERR_ALIGNMENT;
+  if ((st = check_scan_state(g, scan_state, scan_state_bytes)) != ARP_OK) return st;
+  if ((st = check_ws(g, workspace, workspace_bytes)) != ARP_OK) return st;
+  st = arp_angle_scan(desc, phi, theta, scan_state, scan_state_bytes, stream);
+  if (st != ARP_OK) return st;
+  return arp_attn_fwd(desc, q, k, v, theta, alibi, o, workspace, workspace_bytes, stream);
+}
+
+arp_status arp_rotate(const arp_desc* desc, const void* x, const float* theta, float* out,
+                      int inverse, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (x == nullptr || theta == nullptr || out == nullptr) return ARP_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(theta) || !aligned16(out)) return ARP_ERR_ALIGNMENT;
+  return hip_status(launch_rotate_diag(g, x, theta, out, inverse, (hipStream_t)stream));
+}
+
+}  // extern "C"

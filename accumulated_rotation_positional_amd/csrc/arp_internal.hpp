@@ -1,0 +1,58 @@
+// arp_internal.hpp -- host-side interface between the C ABI layer (api.hip)
+// and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/arp.h"
+
+namespace arp {
+
+// Problem geometry derived once from a validated descriptor.
+struct Geometry {
+  int B, H, L, D, P;   // batch, heads, seqlen, head_dim, pairs (D/2)
+  int Hphi;            // angle heads: 1 (shared) or H
+  int dtype;           // arp_dtype
+  uint32_t flags;
+  float scale;         // resolved logit scale
+  int Lp;              // seqlen padded for the pre-rotated operands (multiple of 256)
+};
+
+// ---- buffers ----------------------------------------------------------------
+// scan state: per (batch, angle head) segment a 16-byte header {ticket, done}
+//   and [nchunks][P][2] 64-bit look-back words; kept zeroed between calls.
+// workspace:  [ q~ (bf16, [B*H, Lp, D]) | k~ (bf16, [B*H, Lp, D]) | v~^T (bf16, [B*H, D, Lp]) ]
+//   for bf16 without ARP_FUSED_ROTATION; empty otherwise.
+struct ScanPlan {
+  int rows_per_thread;  // tokens each thread scans serially (T)
+  int chunk;            // tokens per workgroup
+  int nchunks;          // chunks per (batch, angle head) segment
+};
+ScanPlan scan_plan(const Geometry& g);
+size_t scan_state_bytes(const Geometry& g);  // upper bound over every plan
+struct WorkspaceLayout {
+  size_t q_off, k_off, vt_off, operand_bytes;  // each operand block
+  size_t total;
+};
+WorkspaceLayout workspace_layout(const Geometry& g);
+
+// ---- launchers (enqueue only; return hipSuccess or the launch error) -------
+hipError_t launch_angle_scan(const Geometry& g, const float* phi, float* theta, void* scan_state,
+                             hipStream_t stream);
+hipError_t launch_rotate_qkv(const Geometry& g, const void* q, const void* k, const void* v,
+                             const float* theta, uint16_t* qr, uint16_t* kr, uint16_t* vt,
+                             hipStream_t stream);
+hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
+                                    const uint16_t* vt, const float* theta, const float* alibi,
+                                    uint16_t* o, hipStream_t stream);
+hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const float* theta, const float* alibi,
+                                  uint16_t* o, hipStream_t stream);
+hipError_t launch_attn_f32(const Geometry& g, const float* q, const float* k, const float* v,
+                           const float* theta, const float* alibi, float* o, hipStream_t stream);
+hipError_t launch_rotate_diag(const Geometry& g, const void* x, const float* theta, float* out,
+                              int inverse, hipStream_t stream);
+
+}  // namespace arp

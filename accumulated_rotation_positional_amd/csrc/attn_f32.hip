@@ -1,0 +1,158 @@
+// attn_f32.hip -- fp32 causal attention with accumulated rotations (gfx950).
+//
+// The fp32-I/O path: every product and sum in fp32, so outputs stay within
+// ~1e-6 of the exact result.  One thread owns one query row; a workgroup of
+// 64 queries stages 32-key tiles of k and v in LDS, rotating each (key, pair)
+// by R(Theta_j) while staging (the rotation is fused into the staging, one
+// sin/cos per (key, pair) shared by k and v).  Online softmax in base 2 with
+// an exact running maximum.
+//
+// Method: "Why Do Accumulated Transformations Extrapolate?" eq. (2) scores
+// and softmax, eq. (4) transported values (un-rotated by R(Theta_i)^T in the
+// epilogue), eq. (6)/(8) routed scores as <R(Theta_i) q_i, R(Theta_j) k_j>;
+// rotation map from AdaRoPE Sec. 2.1 eq. (1).
+#include "arp_device.hpp"
+#include "arp_internal.hpp"
+
+namespace arp {
+
+namespace {
+
+constexpr int F32_Q = 64;   // queries per workgroup (one per thread)
+constexpr int F32_K = 32;   // keys per staged tile
+
+template <int D, bool ROT_QK, bool ROT_V, bool ALIBI>
+__global__ __launch_bounds__(F32_Q) void attn_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ theta, const float* __restrict__ alibi, float* __restrict__ o, int L,
+    int H, int Hphi, float qscale) {
+  constexpr int P = D / 2;
+  __shared__ float sk[F32_K][D];
+  __shared__ float sv[F32_K][D];
+
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh % H;
+  const int g = (Hphi == 1) ? 0 : h;
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x * F32_Q + tid;
+  const bool valid = i < L;
+  const int irow = valid ? i : L - 1;
+  const float* th_base = theta + (size_t)(b * Hphi + g) * L * P;
+
+  float qv[D];
+  const float* qrow = q + ((size_t)bh * L + irow) * D;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    float a = qrow[2 * p], c = qrow[2 * p + 1];
+    if (ROT_QK) {
+      float sn, cs;
+      sincosf(th_base[(size_t)irow * P + p], &sn, &cs);
+      rotate_pair(a, c, cs, sn);
+    }
+    qv[2 * p] = a * qscale;
+    qv[2 * p + 1] = c * qscale;
+  }
+  const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
+
+  float acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) acc[d] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  const int i_last = min(L - 1, blockIdx.x * F32_Q + F32_Q - 1);
+  for (int j0 = 0; j0 <= i_last; j0 += F32_K) {
+    __syncthreads();
+    // Stage and rotate keys/values j0 .. j0+31 (one sin/cos per (key, pair)).
+    for (int e = tid; e < F32_K * P; e += F32_Q) {
+      const int jj = e / P, p = e % P;
+      const int j = j0 + jj;
+      float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
+      if (j < L) {
+        const size_t off = ((size_t)bh * L + j) * D + 2 * p;
+        k0 = k[off];
+        k1 = k[off + 1];
+        v0 = v[off];
+        v1 = v[off + 1];
+        if (ROT_QK || ROT_V) {
+          float sn, cs;
+          sincosf(th_base[(size_t)j * P + p], &sn, &cs);
+          if (ROT_QK) rotate_pair(k0, k1, cs, sn);
+          if (ROT_V) rotate_pair(v0, v1, cs, sn);
+        }
+      }
+      sk[jj][2 * p] = k0;
+      sk[jj][2 * p + 1] = k1;
+      sv[jj][2 * p] = v0;
+      sv[jj][2 * p + 1] = v1;
+    }
+    __syncthreads();
+    const int jn = min(F32_K, i + 1 - j0);  // keys j <= i in this tile
+    for (int jj = 0; jj < jn; ++jj) {
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) s = fmaf(qv[d], sk[jj][d], s);
+      if (ALIBI) s -= slope2 * (float)(i - (j0 + jj));
+      if (s > m) {
+        const float alpha = exp2f(m - s);
+        l *= alpha;
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc[d] *= alpha;
+        m = s;
+      }
+      const float pexp = exp2f(s - m);
+      l += pexp;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(pexp, sv[jj][d], acc[d]);
+    }
+  }
+  if (!valid) return;
+  const float inv = 1.f / l;
+  float* orow = o + ((size_t)bh * L + i) * D;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    float a = acc[2 * p] * inv, c = acc[2 * p + 1] * inv;
+    if (ROT_V) {
+      float sn, cs;
+      sincosf(th_base[(size_t)i * P + p], &sn, &cs);
+      rotate_pair(a, c, cs, -sn);  // R(Theta_i)^T
+    }
+    orow[2 * p] = a;
+    orow[2 * p + 1] = c;
+  }
+}
+
+template <int D>
+hipError_t launch_f32_d(const Geometry& g, const float* q, const float* k, const float* v,
+                        const float* theta, const float* alibi, float* o, hipStream_t stream) {
+  dim3 grid((g.L + F32_Q - 1) / F32_Q, g.B * g.H);
+  const float qscale = g.scale * LOG2E;
+  const bool rqk = g.flags & ARP_ROTATE_QK, rv = g.flags & ARP_ROTATE_V, al = g.flags & ARP_ALIBI;
+#define ARP_F32_LAUNCH(A, B, C)                                                                \
+  hipLaunchKernelGGL((attn_f32_kernel<D, A, B, C>), grid, dim3(F32_Q), 0, stream, q, k, v,    \
+                     theta, alibi, o, g.L, g.H, g.Hphi, qscale)
+  if (rqk) {
+    if (rv) {
+      if (al) ARP_F32_LAUNCH(true, true, true); else ARP_F32_LAUNCH(true, true, false);
+    } else {
+      if (al) ARP_F32_LAUNCH(true, false, true); else ARP_F32_LAUNCH(true, false, false);
+    }
+  } else {
+    if (rv) {
+      if (al) ARP_F32_LAUNCH(false, true, true); else ARP_F32_LAUNCH(false, true, false);
+    } else {
+      if (al) ARP_F32_LAUNCH(false, false, true); else ARP_F32_LAUNCH(false, false, false);
+    }
+  }
+#undef ARP_F32_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(const Geometry& g, const float* q, const float* k, const float* v,
+                           const float* theta, const float* alibi, float* o, hipStream_t stream) {
+  if (g.D == 64) return launch_f32_d<64>(g, q, k, v, theta, alibi, o, stream);
+  return launch_f32_d<128>(g, q, k, v, theta, alibi, o, stream);
+}
+
+}  // namespace arp

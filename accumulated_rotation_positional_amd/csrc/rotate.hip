@@ -1,0 +1,164 @@
+// rotate.hip -- the rotation step on gfx950.
+//
+//   x~_t = R(Theta_t) x_t,  R(a) = [[cos a, -sin a], [sin a, cos a]] on (x[2p], x[2p+1])
+//
+// ("AdaRoPE: Not All Attention Heads Should Rotate and Scale Equally",
+// Sec. 2.1 eq. (1); the RoPE decay-curve post's rope(): adjacent pairs, sine
+// term negative in the first component.)
+//
+// rotate_qkv_kernel: the pre-rotation pass in front of the bf16 attention
+// kernel.  One workgroup handles 64 tokens x head_dim of one (batch, head):
+//  * q, k, v and theta are read with 16-byte coalesced loads (one chunk of 8
+//    elements = 4 pairs per thread, with the matching float4 of angles);
+//  * sin/cos of the wrapped angle are computed once per (token, pair) and
+//    shared by q, k and v;
+//  * q~ is pre-multiplied by scale * log2(e) so the attention kernel's
+//    matrix-core products are already base-2 logits;
+//  * q~ and k~ are written row-major [Lp, D]; v~ is transposed through LDS and
+//    written [D, Lp], the layout the P V product reads (keys contiguous);
+//  * tokens in [L, Lp) are written as zeros (the attention kernel reads whole
+//    tiles without bounds checks).
+#include "arp_device.hpp"
+#include "arp_internal.hpp"
+
+namespace arp {
+
+namespace {
+
+constexpr int ROT_TOKENS = 64;
+
+template <int D>
+__global__ __launch_bounds__(256) void rotate_qkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ theta, uint16_t* __restrict__ qr, uint16_t* __restrict__ kr,
+    uint16_t* __restrict__ vt, int L, int Lp, int H, int Hphi, uint32_t flags, float qscale) {
+  constexpr int P = D / 2;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int ITER = ROT_TOKENS * CPR / 256;
+  constexpr int VT_STRIDE = ROT_TOKENS + 8;  // padded LDS row (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VT_STRIDE];
+
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh % H;
+  const int g = (Hphi == 1) ? 0 : h;
+  const int t0 = blockIdx.x * ROT_TOKENS;
+  const int tid = threadIdx.x;
+  const bool rot_qk = (flags & ARP_ROTATE_QK) != 0;
+  const bool rot_v = (flags & ARP_ROTATE_V) != 0;
+
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int idx = it * 256 + tid;
+    const int r = idx / CPR, c = idx % CPR;
+    const int tok = t0 + r;
+    u32x4 qa = {0, 0, 0, 0}, ka = {0, 0, 0, 0}, va = {0, 0, 0, 0};
+    if (tok < L) {
+      const size_t off = ((size_t)bh * L + tok) * D + c * 8;
+      qa = *reinterpret_cast<const u32x4*>(q + off);
+      ka = *reinterpret_cast<const u32x4*>(k + off);
+      va = *reinterpret_cast<const u32x4*>(v + off);
+      float4 th = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (rot_qk || rot_v)
+        th = *reinterpret_cast<const float4*>(theta + ((size_t)(b * Hphi + g) * L + tok) * P + c * 4);
+      const float ang[4] = {th.x, th.y, th.z, th.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float sn, cs;
+        sincosf(ang[e], &sn, &cs);
+        float q0 = lo_bf16(qa[e]), q1 = hi_bf16(qa[e]);
+        float k0 = lo_bf16(ka[e]), k1 = hi_bf16(ka[e]);
+        float v0 = lo_bf16(va[e]), v1 = hi_bf16(va[e]);
+        if (rot_qk) {
+          rotate_pair(q0, q1, cs, sn);
+          rotate_pair(k0, k1, cs, sn);
+        }
+        if (rot_v) rotate_pair(v0, v1, cs, sn);
+        qa[e] = pack_bf16x2(q0 * qscale, q1 * qscale);
+        ka[e] = pack_bf16x2(k0, k1);
+        va[e] = pack_bf16x2(v0, v1);
+      }
+    }
+    const size_t roff = ((size_t)bh * Lp + tok) * D + c * 8;
+    *reinterpret_cast<u32x4*>(qr + roff) = qa;
+    *reinterpret_cast<u32x4*>(kr + roff) = ka;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s_vt[(c * 8 + 2 * e) * VT_STRIDE + r] = (uint16_t)(va[e] & 0xFFFFu);
+      s_vt[(c * 8 + 2 * e + 1) * VT_STRIDE + r] = (uint16_t)(va[e] >> 16);
+    }
+  }
+  __syncthreads();
+  // v~^T rows: D rows x 64 tokens = 8 chunks of 16 bytes per row.
+#pragma unroll
+  for (int it = 0; it < D * 8 / 256; ++it) {
+    const int idx = it * 256 + tid;
+    const int drow = idx / 8, cc = idx % 8;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(&s_vt[drow * VT_STRIDE + cc * 8]);
+    *reinterpret_cast<u32x4*>(vt + ((size_t)bh * D + drow) * Lp + t0 + cc * 8) = w;
+  }
+}
+
+// Diagnostic rotation with fp32 output: one thread per (row, pair).
+template <typename TIn>
+__global__ __launch_bounds__(256) void rotate_diag_kernel(const TIn* __restrict__ x,
+                                                          const float* __restrict__ theta,
+                                                          float* __restrict__ out, long npairs_total,
+                                                          int L, int H, int Hphi, int P, int inverse) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= npairs_total) return;
+  const int p = (int)(i % P);
+  const long row = i / P;  // (b*H + h)*L + t
+  const int t = (int)(row % L);
+  const long bh = row / L;
+  const int h = (int)(bh % H), b = (int)(bh / H);
+  const int g = (Hphi == 1) ? 0 : h;
+  float a, bb;
+  if constexpr (sizeof(TIn) == 4) {
+    a = x[2 * i];
+    bb = x[2 * i + 1];
+  } else {
+    a = bf16_bits_to_f32(x[2 * i]);
+    bb = bf16_bits_to_f32(x[2 * i + 1]);
+  }
+  float sn, cs;
+  sincosf(theta[((size_t)(b * Hphi + g) * L + t) * P + p], &sn, &cs);
+  if (inverse) sn = -sn;
+  rotate_pair(a, bb, cs, sn);
+  out[2 * i] = a;
+  out[2 * i + 1] = bb;
+}
+
+}  // namespace
+
+hipError_t launch_rotate_qkv(const Geometry& g, const void* q, const void* k, const void* v,
+                             const float* theta, uint16_t* qr, uint16_t* kr, uint16_t* vt,
+                             hipStream_t stream) {
+  dim3 grid(g.Lp / ROT_TOKENS, g.B * g.H);
+  const float qscale = g.scale * LOG2E;
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* kb = static_cast<const uint16_t*>(k);
+  const auto* vb = static_cast<const uint16_t*>(v);
+  if (g.D == 64)
+    hipLaunchKernelGGL((rotate_qkv_kernel<64>), grid, dim3(256), 0, stream, qb, kb, vb, theta, qr,
+                       kr, vt, g.L, g.Lp, g.H, g.Hphi, g.flags, qscale);
+  else
+    hipLaunchKernelGGL((rotate_qkv_kernel<128>), grid, dim3(256), 0, stream, qb, kb, vb, theta,
+                       qr, kr, vt, g.L, g.Lp, g.H, g.Hphi, g.flags, qscale);
+  return hipGetLastError();
+}
+
+hipError_t launch_rotate_diag(const Geometry& g, const void* x, const float* theta, float* out,
+                              int inverse, hipStream_t stream) {
+  const long n = (long)g.B * g.H * g.L * g.P;
+  dim3 grid((unsigned)((n + 255) / 256));
+  if (g.dtype == ARP_DTYPE_F32)
+    hipLaunchKernelGGL((rotate_diag_kernel<float>), grid, dim3(256), 0, stream,
+                       static_cast<const float*>(x), theta, out, n, g.L, g.H, g.Hphi, g.P, inverse);
+  else
+    hipLaunchKernelGGL((rotate_diag_kernel<uint16_t>), grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), theta, out, n, g.L, g.H, g.Hphi, g.P,
+                       inverse);
+  return hipGetLastError();
+}
+
+}  // namespace arp

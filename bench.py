@@ -1,0 +1,192 @@
+"""Benchmark: accumulated-rotation causal attention forward on one MI355X.
+
+One step = the whole hot path on one batch of the 16x-extrapolation workload
+(B=2, H=8, L=16384, d=64, bf16, learned token-dependent angles, q/k/v
+rotation): angle scan -> rotation pass -> attention kernel, through the C ABI,
+with inputs resident in HBM.  Prints ONE JSON line.
+
+  value      whole-step throughput in TFLOP/s of algorithmic attention work,
+             4 d per causal (query, key) pair (the two contractions only)
+  roofline   the attention kernel against the bf16 matrix-core peak, its
+             duration measured with HIP events on the stream it runs on
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+             workload (a strided subset of query rows of every head)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense)
+HBM_PEAK_GBS = 8000.0
+METRIC = "accum-rotation causal attention fwd TFLOP/s + tokens/s at L=16K, d=64"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="extrap_16k")
+    p.add_argument("--fused", action="store_true", help="rotate k/v inside the attention kernel")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target duration of the CPU oracle sample")
+    return p.parse_args()
+
+
+def _strided_rows(w, stride: int, offset: int = 0) -> np.ndarray:
+    L = w.seqlen
+    i = np.arange(offset % stride, L, stride, dtype=np.int64)
+    return np.concatenate([bh * L + i for bh in range(w.batch * w.heads)])
+
+
+def run_cpu_baseline(w, flags: int, alibi, target_s: float) -> dict:
+    import oracle
+
+    nthreads = min(len(os.sched_getaffinity(0)), 16)
+    prob = oracle.Problem(w.q, w.k, w.v, w.phi, flags, alibi=alibi)
+    # calibrate on a small sample, then size the timed sample for ~target_s
+    stride = 4096
+    t0 = time.perf_counter()
+    prob.rows(_strided_rows(w, stride, 17), nthreads)
+    t_cal = time.perf_counter() - t0
+    stride = int(max(1, min(4096, stride * t_cal / target_s)))
+    rows = _strided_rows(w, stride, 5)
+    t0 = time.perf_counter()
+    prob.rows(rows, nthreads)
+    dt = time.perf_counter() - t0
+    i = rows % w.seqlen
+    flops = float(4.0 * w.head_dim * (i + 1).sum())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{rows.size} query rows (every {stride}th row of each of the "
+                      f"{w.batch * w.heads} heads, with the angle scan and key/value "
+                      f"rotation of each head), fp64, {dt:.1f} s",
+            "seconds": dt, "tokens_per_s": rows.size / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards over (batch, head) with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from accumulated_rotation_positional_amd import binding
+    from accumulated_rotation_positional_amd import workloads as wl
+
+    w = wl.make(args.workload)
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v, phi = (to_dev(getattr(w, n)) for n in ("q", "k", "v", "phi"))
+    alibi = to_dev(w.alibi) if w.alibi is not None else None
+    flags = binding.flags_for(rotate_qk=True, rotate_v=w.rotate_v, alibi=w.use_alibi,
+                              shared_phi=w.phi_heads == 1 and w.heads != 1, fused=args.fused)
+    desc = binding.desc_for(q, flags)
+    ws = binding.workspace(desc, dev)
+    state = binding.scan_state(desc, dev)
+    theta = torch.empty_like(phi)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    fused = args.fused or w.dtype == "f32"
+    n_ev = 3 if not fused else 2
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        binding.angle_scan(phi, desc, theta=theta, state=state)
+        if evs is not None:
+            evs[1].record(stream)
+        if fused:
+            binding.attn_fwd(q, k, v, theta, desc, alibi=alibi, out=o, ws=ws)
+        else:
+            binding.rotate_qkv(q, k, v, theta, desc, ws=ws)
+            if evs is not None:
+                evs[2].record(stream)
+            binding.attn_rotated(theta, alibi, o, desc, ws)
+        if evs is not None:
+            evs[n_ev].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)]
+              for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        step(events[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    seg = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(n_ev)] for e in events])
+    scan_ms = float(seg[:, 0].mean())
+    attn_ms = float(seg[:, -1].mean())
+    rot_ms = float(seg[:, 1].mean()) if n_ev == 3 else 0.0
+
+    flops = w.flops
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    tokens = w.batch * w.seqlen / (ms_step * 1e-3)
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    scan_bytes = 8.0 * w.batch * w.phi_heads * w.seqlen * (w.head_dim // 2)
+    scan_gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "tokens_per_s": round(tokens, 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "wall_s_timed": round(t_wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; learned-angle generator phi = W x)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seqlen,
+                   "head_dim": w.head_dim, "rotate_v": w.rotate_v, "alibi": w.use_alibi,
+                   "rotation": "fused-in-staging" if fused else "pre-rotation pass"},
+        "kernels_ms": {"angle_scan": round(scan_ms, 5), "rotate_qkv": round(rot_ms, 5),
+                       "attn_fwd": round(attn_ms, 5)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "scan_roofline": {"bound": "hbm", "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        of = (oracle.ROTATE_QK | (oracle.ROTATE_V if w.rotate_v else 0) |
+              (oracle.ALIBI if w.use_alibi else 0))
+        result["cpu_baseline"] = run_cpu_baseline(w, of, w.alibi, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

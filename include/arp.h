@@ -1,0 +1,159 @@
+/*
+ * arp.h -- C ABI of libarp.so: causal softmax attention with accumulated,
+ * token-dependent SO(2) rotations, for AMD MI355X (gfx950).
+ *
+ * The method ("Why Do Accumulated Transformations Extrapolate?", arXiv
+ * 2606.24975):
+ *  - each position t carries one step angle phi_t[p] per two-dimensional
+ *    rotary block p; blocks commute, so a route of steps is a rotation by
+ *    the summed angle (Sec. 5, "SO(2) notation");
+ *  - the route from source j to query i holds the steps j+1..i (Sec. 2.2,
+ *    eq. (6)), so position t gets the inclusive prefix sum
+ *    Theta_t = sum_{s<=t} phi_s and the route is a rotation by
+ *    Theta_j - Theta_i (App. B.8 fixes the sign: a position-only route by
+ *    k steps of angle w is R(-w k));
+ *  - q, k (and v, with value transport) are rotated by R(Theta_t), the pair
+ *    map [[cos, -sin], [sin, cos]] on elements (2p, 2p+1) (AdaRoPE, "AdaRoPE:
+ *    Not All Attention Heads Should Rotate and Scale Equally", Sec. 2.1
+ *    eq. (1));
+ *  - scores s_ij = scale <q~_i, k~_j> - m_h (i - j) [distance bias] over the
+ *    causal set j <= i, softmax, and the transported sum
+ *    c_i = sum_j alpha_ij P_{j->i} v_j (eq. (2), (4), (8), (11)); with value
+ *    transport the library returns R(Theta_i)^T sum_j alpha_ij R(Theta_j) v_j,
+ *    which is exactly eq. (4).
+ * RoPE is the special case of a constant phi_t[p] = theta_p (AdaRoPE
+ * Sec. 2.1), NoPE the case without ARP_ROTATE_QK.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are caller-owned DEVICE memory, C-contiguous:
+ *      q, k, v, o : [batch, heads, seqlen, head_dim]     (dtype of the desc)
+ *      phi, theta : [batch, phi_heads, seqlen, head_dim/2] float32,
+ *                   phi_heads = 1 with ARP_PHI_SHARED_HEADS, else heads
+ *      alibi      : [heads] float32 slopes m_h (ARP_ALIBI only)
+ *    Rotary pair p is elements (2p, 2p+1) of the last axis.
+ *  - Every pointer must be 16-byte aligned.
+ *  - stream is a hipStream_t (NULL: the default stream).  Work is enqueued
+ *    asynchronously; nothing is synchronised; no host memory is touched.
+ *  - The library allocates nothing.  It uses two caller-provided buffers:
+ *      scan_state (arp_scan_state_bytes): the look-back flags of the angle
+ *        scan.  Zero-fill it once before its first use; every completed scan
+ *        leaves it zeroed again, so one buffer serves any number of calls and
+ *        problem sizes (when large enough).  Nothing else may write to it.
+ *      workspace (arp_workspace_bytes): the rotated bf16 operands of the
+ *        pre-rotation path; no initialisation needed.
+ *    Calls that share a buffer must be ordered (same stream).
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    error code means nothing was launched.  ARP_ERR_HIP reports a failed
+ *    launch; faults inside kernels surface at the caller's next sync.
+ */
+#ifndef ARP_H
+#define ARP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ARP_ABI_VERSION 1
+
+typedef enum arp_status {
+  ARP_OK = 0,
+  ARP_ERR_INVALID_ARG = 1, /* null desc/pointer, bad size, odd head_dim, unknown flag or dtype */
+  ARP_ERR_UNSUPPORTED = 2, /* well-formed but not built: head_dim other than 64 or 128 */
+  ARP_ERR_ALIGNMENT = 3,   /* a pointer is not 16-byte aligned */
+  ARP_ERR_WORKSPACE = 4,   /* scan state or workspace null or smaller than required */
+  ARP_ERR_HIP = 5          /* a kernel launch failed */
+} arp_status;
+
+typedef enum arp_dtype {
+  ARP_DTYPE_F32 = 0,  /* fp32 I/O, fp32 arithmetic throughout */
+  ARP_DTYPE_BF16 = 1  /* bf16 I/O, bf16 matrix-core products, fp32 accumulation */
+} arp_dtype;
+
+/* Flags (arp_desc.flags). */
+#define ARP_ROTATE_QK 0x1u        /* rotate q and k by R(Theta_t) */
+#define ARP_ROTATE_V 0x2u         /* value transport (eq. (4)): rotate v, un-rotate o */
+#define ARP_ALIBI 0x4u            /* add the distance bias -m_h (i - j) to every score */
+#define ARP_PHI_SHARED_HEADS 0x8u /* phi/theta have one head shared by all heads */
+#define ARP_SCAN_EXCLUSIVE 0x10u  /* Theta_t = sum_{s<t} phi_s (route steps j..i-1) */
+#define ARP_FUSED_ROTATION 0x20u  /* bf16: rotate k/v while staging tiles in LDS
+                                     instead of a separate pre-rotation pass */
+#define ARP_ALL_FLAGS 0x3Fu
+
+typedef struct arp_desc {
+  int32_t batch;
+  int32_t heads;
+  int32_t seqlen;
+  int32_t head_dim;  /* even; 64 or 128 are built */
+  int32_t dtype;     /* arp_dtype of q, k, v, o */
+  uint32_t flags;    /* ARP_* flags above */
+  float scale;       /* logit scale; <= 0 selects 1/sqrt(head_dim) */
+  int32_t reserved;  /* must be 0 */
+} arp_desc;
+
+/* ARP_ABI_VERSION of the loaded library. */
+int arp_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char* arp_status_string(int status);
+
+/* Host-only validation of a descriptor (no pointers, no launch). */
+arp_status arp_check(const arp_desc* desc);
+
+/* Bytes of the angle scan's look-back state for desc (0 when desc is invalid).
+ * The state must be zero before first use and is left zeroed by every call. */
+size_t arp_scan_state_bytes(const arp_desc* desc);
+
+/* Bytes of the operand workspace for desc: the rotated bf16 q~, k~, v~^T of
+ * the pre-rotation path; 0 for fp32 I/O or ARP_FUSED_ROTATION (and when desc is
+ * invalid). */
+size_t arp_workspace_bytes(const arp_desc* desc);
+
+/* a1. Accumulated angles: theta[b,g,t,p] = wrap(sum_{s<=t} phi[b,g,s,p]) in
+ * [-pi, pi) (exclusive sum with ARP_SCAN_EXCLUSIVE).  Compensated fp32
+ * (two-float) prefix sum, single pass with chained look-back across chunks of
+ * the sequence.  Method: Sec. 5 "SO(2) notation" and eq. (6). */
+arp_status arp_angle_scan(const arp_desc* desc, const float* phi, float* theta, void* scan_state,
+                          size_t scan_state_bytes, void* stream);
+
+/* a2. Pre-rotation pass (bf16): writes R(Theta_t) q_t (times scale*log2(e)),
+ * R(Theta_t) k_t and R(Theta_t) v_t (or the unrotated tensors, per the flags)
+ * as bf16 into the workspace, in the layout arp_attn_rotated reads.
+ * Method: AdaRoPE Sec. 2.1 eq. (1); RoPE post, rope(). */
+arp_status arp_rotate_qkv(const arp_desc* desc, const void* q, const void* k, const void* v,
+                          const float* theta, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* a3-a6 over operands already in the workspace (bf16, after arp_rotate_qkv):
+ * scores, causal mask, distance bias, online softmax, P V, and the
+ * value-transport epilogue o_i = R(Theta_i)^T o~_i.  Method: eq. (2)-(4),
+ * (8), (11).  theta is read only with ARP_ROTATE_V, alibi only with ARP_ALIBI. */
+arp_status arp_attn_rotated(const arp_desc* desc, const float* theta, const float* alibi,
+                            void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* a2-a6: attention given accumulated angles.  bf16: arp_rotate_qkv then
+ * arp_attn_rotated, or one kernel that rotates while staging with
+ * ARP_FUSED_ROTATION.  fp32: one kernel, rotation fused into staging. */
+arp_status arp_attn_fwd(const arp_desc* desc, const void* q, const void* k, const void* v,
+                        const float* theta, const float* alibi, void* o, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* a1-a6: the whole forward pass, (q, k, v, phi, flags) -> o.  theta receives
+ * the accumulated angles (caller-owned, same layout as phi). */
+arp_status arp_forward(const arp_desc* desc, const void* q, const void* k, const void* v,
+                       const float* phi, const float* alibi, float* theta, void* o,
+                       void* scan_state, size_t scan_state_bytes, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Diagnostic: out = R(theta) x (or R(theta)^T x when inverse != 0) in fp32.
+ * x has the desc's dtype and q's layout; out is float32 of the same shape. */
+arp_status arp_rotate(const arp_desc* desc, const void* x, const float* theta, float* out,
+                      int inverse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARP_H */

@@ -1,0 +1,151 @@
+"""The C ABI of libarp.so, on the CPU: the library loads, exports every
+function include/arp.h declares, and rejects bad arguments on the host before
+anything is enqueued (every call below fails validation, so no kernel is ever
+launched and no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from accumulated_rotation_positional_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "arp.h")
+
+
+def _declared():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(arp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared()
+    assert set(names) == set(b.EXPORTS), names
+    lib = ctypes.CDLL(b.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    L = b.lib()
+    assert L.arp_abi_version() == 1
+    for s in range(6):
+        assert L.arp_status_string(s)
+    assert L.arp_status_string(99) == b"unknown status"
+
+
+def _desc(**kw):
+    base = dict(batch=2, heads=8, seqlen=1024, head_dim=64, dtype="bf16", flags=b.ROTATE_QK)
+    base.update(kw)
+    return b.make_desc(base["batch"], base["heads"], base["seqlen"], base["head_dim"],
+                       base["dtype"], base["flags"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), b.OK),
+    (dict(dtype="f32"), b.OK),
+    (dict(head_dim=128), b.OK),
+    (dict(batch=0), b.ERR_INVALID_ARG),
+    (dict(heads=-1), b.ERR_INVALID_ARG),
+    (dict(seqlen=0), b.ERR_INVALID_ARG),
+    (dict(head_dim=63), b.ERR_INVALID_ARG),
+    (dict(head_dim=96), b.ERR_UNSUPPORTED),
+    (dict(head_dim=32), b.ERR_UNSUPPORTED),
+    (dict(flags=0x40), b.ERR_INVALID_ARG),
+    (dict(seqlen=(1 << 24) + 1), b.ERR_INVALID_ARG),
+])
+def test_check_descriptor(kw, status):
+    d = _desc(**kw)
+    assert b.lib().arp_check(ctypes.byref(d)) == status
+
+
+def test_check_rejects_bad_dtype_reserved_scale_and_null():
+    L = b.lib()
+    d = _desc()
+    d.dtype = 7
+    assert L.arp_check(ctypes.byref(d)) == b.ERR_INVALID_ARG
+    d = _desc()
+    d.reserved = 1
+    assert L.arp_check(ctypes.byref(d)) == b.ERR_INVALID_ARG
+    d = _desc()
+    d.scale = float("nan")
+    assert L.arp_check(ctypes.byref(d)) == b.ERR_INVALID_ARG
+    d.scale = float("inf")
+    assert L.arp_check(ctypes.byref(d)) == b.ERR_INVALID_ARG
+    assert L.arp_check(None) == b.ERR_INVALID_ARG
+
+
+def test_workspace_and_scan_state_bytes():
+    L = b.lib()
+    d = _desc(batch=2, heads=8, seqlen=16384)
+    ws = L.arp_workspace_bytes(ctypes.byref(d))
+    operands = 3 * 2 * 8 * 16384 * 64 * 2
+    assert operands <= ws < operands + 4096 and ws % 256 == 0
+    st = L.arp_scan_state_bytes(ctypes.byref(d))
+    assert 0 < st < (16 << 20) and st % 256 == 0
+    fused = _desc(batch=2, heads=8, seqlen=16384, flags=b.ROTATE_QK | b.FUSED_ROTATION)
+    assert L.arp_workspace_bytes(ctypes.byref(fused)) == 0
+    assert L.arp_workspace_bytes(ctypes.byref(_desc(dtype="f32"))) == 0
+    bad = _desc(head_dim=63)
+    assert L.arp_workspace_bytes(ctypes.byref(bad)) == 0
+    assert L.arp_scan_state_bytes(ctypes.byref(bad)) == 0
+    # shared angle heads need state for one angle head per batch only
+    shared = _desc(batch=2, heads=8, seqlen=16384, flags=b.ROTATE_QK | b.PHI_SHARED_HEADS)
+    assert L.arp_scan_state_bytes(ctypes.byref(shared)) < st
+
+
+# Fake device addresses: never dereferenced, because every call fails validation.
+A = 0x10000          # 16-byte aligned
+M = 0x10004          # misaligned
+
+
+def test_entry_points_reject_null_and_misaligned_pointers():
+    L = b.lib()
+    d = _desc()
+    big = L.arp_workspace_bytes(ctypes.byref(d))
+    st = L.arp_scan_state_bytes(ctypes.byref(d))
+    by = ctypes.byref(d)
+    assert L.arp_angle_scan(by, None, A, A, st, None) == b.ERR_INVALID_ARG
+    assert L.arp_angle_scan(by, M, A, A, st, None) == b.ERR_ALIGNMENT
+    assert L.arp_angle_scan(by, A, A, None, st, None) == b.ERR_WORKSPACE
+    assert L.arp_angle_scan(by, A, A, A, 16, None) == b.ERR_WORKSPACE
+    assert L.arp_angle_scan(by, A, A, A + 16, st, None) == b.ERR_ALIGNMENT
+    assert L.arp_rotate_qkv(by, A, None, A, A, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_rotate_qkv(by, A, A, M, A, A, big, None) == b.ERR_ALIGNMENT
+    assert L.arp_rotate_qkv(by, A, A, A, None, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_rotated(by, A, A, None, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_rotated(by, A, A, A, A, 8, None) == b.ERR_WORKSPACE
+    assert L.arp_attn_fwd(by, A, A, A, A, None, None, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_fwd(by, A, A, A, A, None, M, A, big, None) == b.ERR_ALIGNMENT
+    assert L.arp_forward(by, A, A, A, None, None, A, A, A, st, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_forward(by, A, A, A, A, None, None, A, A, st, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_forward(by, A, A, A, A, None, A, A, A, st, A, 0, None) == b.ERR_WORKSPACE
+    assert L.arp_forward(by, A, A, A, A, None, A, A, A, 0, A, big, None) == b.ERR_WORKSPACE
+    assert L.arp_rotate(by, A, None, A, 0, None) == b.ERR_INVALID_ARG
+    assert L.arp_rotate(by, A, A, M, 0, None) == b.ERR_ALIGNMENT
+
+
+def test_alibi_requires_slopes_and_rotation_requires_theta():
+    L = b.lib()
+    d = _desc(flags=b.ROTATE_QK | b.ALIBI)
+    big = L.arp_workspace_bytes(ctypes.byref(d))
+    st = L.arp_scan_state_bytes(ctypes.byref(d))
+    by = ctypes.byref(d)
+    assert L.arp_forward(by, A, A, A, A, None, A, A, A, st, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_fwd(by, A, A, A, A, None, A, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_rotated(by, A, None, A, A, big, None) == b.ERR_INVALID_ARG
+    dv = _desc(flags=b.ROTATE_V)
+    assert L.arp_attn_rotated(ctypes.byref(dv), None, None, A, A, big, None) == b.ERR_INVALID_ARG
+    df32 = _desc(dtype="f32")
+    # the pre-rotation pass and its attention kernel exist for bf16 only
+    assert L.arp_rotate_qkv(ctypes.byref(df32), A, A, A, A, A, big, None) == b.ERR_UNSUPPORTED
+    assert L.arp_attn_rotated(ctypes.byref(df32), A, None, A, A, big, None) == b.ERR_UNSUPPORTED
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    phi = torch.zeros(1, 1, 8, 32)
+    with pytest.raises(ValueError):
+        b.forward(q, q, q, phi)
