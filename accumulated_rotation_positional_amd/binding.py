@@ -148,7 +148,7 @@ _WS: dict = {}
 
 def scan_state(desc: Desc, device: torch.device) -> torch.Tensor:
     """The angle scan's look-back state, zero-filled once and cached per
-    (device, stream); every completed scan leaves it zeroed again, so one buffer
+    (device, stream); each scan leaves it ready for the next, so one buffer
     serves every later call on that stream that fits in it."""
     need = max(scan_state_bytes(desc), 256)
     key = (device.index, _stream(device))

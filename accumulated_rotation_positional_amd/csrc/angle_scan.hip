@@ -8,35 +8,50 @@
 // Sec. 2.2 eq. (6): the route from j to i holds steps j+1..i, hence the
 // inclusive sum.)
 //
-// Design (HBM-bound; 4 bytes read + 4 bytes written per element):
-//  * A workgroup (256 threads) owns one chunk of CH consecutive tokens of one
-//    segment, all P pairs.  Each thread loads float4s (4 adjacent pairs) of
-//    T consecutive tokens -- a wave reads whole 128/256-byte rows -- and keeps
-//    them in registers, so phi is read from HBM exactly once.
-//  * Angles are accumulated as 64-bit fixed-point turns: an angle a maps to
-//    the integer round(frac(a / 2 pi) * 2^63) * 2 (mod 2^64), whose signed
-//    value spans [-pi, pi).  Integer addition mod 2^64 is exact and
-//    associative, so (i) the sum is the exact sum of the converted steps --
-//    no drift with the sequence length (a plain fp32 running sum of 32K
-//    angles drifts by ~1e-3 rad), (ii) the reduction mod 2 pi is the
-//    overflow itself, and (iii) the result does not depend on the order in
-//    which chunk totals are combined: runs are bit-reproducible.  Each step's
-//    conversion (in fp64) is accurate to ~4e-16 rad.
-//  * Chunks are chained with decoupled look-back (Merrill & Garland,
-//    "Single-pass Parallel Prefix Scan with Decoupled Look-back", 2016): a
-//    chunk publishes its aggregate at once, then sums its predecessors'
-//    published aggregates, back to the nearest published inclusive prefix.
-//    All 256 threads take part: each pass reads a window of 16-32
-//    predecessors per pair in parallel, so the look-back costs a pass or
-//    two of memory latency instead of one round trip per predecessor.
-//    Fixed-point values are even, so the low bit of each published 64-bit
-//    word is free to be the "ready" tag (zeroed memory = not ready): one
-//    atomic load sees value and flag together and no fence is needed.
-//  * Chunk order comes from a per-segment ticket (atomic counter), so a
-//    chunk only ever waits on chunks that were already running.
-//  * The last chunk of a segment to finish clears that segment's state, so
-//    the state buffer is zero again for the next call on the stream.
-//  * Every wait is bounded; a chunk that gives up writes NaN angles.
+// The kernel is HBM-bound (4 bytes read + 4 bytes written per element), so
+// it is built like a copy: one read of phi, one write of theta, little
+// arithmetic per element, and no memory fences.
+//
+// Number format.  Angles are accumulated as fixed-point turns with 48
+// fractional bits, held in 64-bit integers: an angle a becomes
+// round(frac(a / 2 pi) * 2^48).  Integer addition is exact and associative,
+// so the result is the exact sum of the converted steps (each step is
+// rounded once, by at most 2^-49 turn = 1.1e-14 rad), the reduction mod 2 pi
+// is the wrap-around of the low 48 bits, and the result does not depend on
+// the order in which partial sums are combined: runs are bit-reproducible.
+// The conversion is a few fp64 operations: after subtracting the nearest
+// whole turn, adding 24 = 1.5 * 2^4 pins the exponent, so the low 48
+// mantissa bits of the sum are the wanted fraction.  The way back puts the
+// 48 bits into a double of fixed exponent again, so every output is the
+// correctly rounded fp32 of an exact fixed-point value.
+//
+// Work split.  A workgroup (256 threads) owns one chunk of CH consecutive
+// tokens of one segment, all P pairs: each thread loads T consecutive token
+// rows of 4 pairs (one float4 per row; a wave reads whole rows) and keeps
+// them in registers.  Thread, wave and workgroup partial sums are combined
+// with lane shuffles and one LDS exchange.
+//
+// Chunks are chained with decoupled look-back (Merrill & Garland,
+// "Single-pass Parallel Prefix Scan with Decoupled Look-back", 2016): a
+// chunk publishes its aggregate as soon as it has it, sums the published
+// aggregates of its predecessors back to the nearest published inclusive
+// prefix, and then publishes its own inclusive prefix.  Value and status
+// share one 64-bit word (48 value bits, 2 status bits), so a single atomic
+// load sees both and no fence is needed.  Chunks are numbered in launch
+// order (blockIdx), with no ticket counter; a chunk that finds a predecessor
+// still unpublished after a bounded number of polls reduces that
+// predecessor's angles itself from phi ("decoupled fallback", Smith, Levien
+// and Owens, 2025), so progress never depends on the order in which the
+// hardware schedules workgroups, and every wait ends.
+//
+// State reuse without clearing kernels or fences.  The caller's state buffer
+// holds a 256-byte header and two interleaved halves of 64-bit words
+// (completion counters, then status words).  A call uses the half named by
+// the header's parity (all zero on entry), clears the other half (which the
+// previous call used) and, in its last workgroup to finish, flips the parity
+// and records how many words it dirtied.  The next launch on the stream sees all of it at the kernel
+// boundary.  A buffer zero-filled once therefore serves any number of calls
+// of any size that fits it.
 #include "arp_device.hpp"
 #include "arp_internal.hpp"
 
@@ -45,231 +60,311 @@ namespace arp {
 namespace {
 
 constexpr int SCAN_THREADS = 256;
-constexpr uint32_t SPIN_LIMIT = 1u << 22;  // look-back passes before giving up
-constexpr int LB_R = 4;                    // predecessors per look-back slot
-constexpr int LB_ALL = 0, LB_FOUND = 1, LB_BLOCKED = 2;
+constexpr int FALLBACK_POLLS = 256;  // polls of an unpublished word before reducing it here
+constexpr int GROUP = 16;            // workgroups per completion counter
+constexpr uint64_t ST_AGG = 1, ST_INC = 2, ST_MASK = 3;
+constexpr uint64_t MASK48 = (1ull << 48) - 1;
+constexpr double INV_2PI = 0.15915494309189533577;
+constexpr double TWO_PI = 6.28318530717958647693;
 
-// Angle (radians, fp32) -> even 64-bit fixed-point turns.  frac() is taken
-// in fp64, exact for |a| < 2^50 turns.
-__device__ __forceinline__ uint64_t to_turns(float a) {
-  const double t = (double)a * 0.15915494309189533577;  // 1 / (2 pi)
-  const double f = t - rint(t);                           // [-0.5, 0.5]
-  return ((uint64_t)(int64_t)rint(f * 9223372036854775808.0)) << 1;
+// Header of the state buffer, padded to 256 bytes so that every 128-byte
+// cache line of the status words belongs to exactly one half (the halves are
+// written by different kinds of store).  Read and written with agent-scope
+// atomics only.
+struct ScanHeader {
+  uint32_t parity;     // half used by the next call
+  uint32_t pad;
+  uint32_t done[2];    // finished groups of workgroups of the call using each half
+  uint64_t used[2];    // words dirtied by the last use of each half
+  uint64_t reserved[28];
+};
+static_assert(sizeof(ScanHeader) == 256, "header size");
+
+// Logical status word w of half h: halves interleave in blocks of 32 words,
+// a layout that does not depend on the problem's shape.
+__device__ __forceinline__ size_t phys_word(size_t w, uint32_t h) {
+  return ((w >> 5) * 2 + h) * 32 + (w & 31);
 }
-// Fixed-point turns -> radians in [-pi, pi) (then rounded to fp32).
-__device__ __forceinline__ float to_radians(uint64_t u) {
-  return (float)((double)(int64_t)u * 3.4061215800865545e-19);  // 2 pi / 2^64
+
+// Radians (fp32) -> fixed-point turns, low 48 bits meaningful.
+// n is the nearest whole number of turns; fma(a, 1/(2 pi), 24 - n) rounds
+// a / (2 pi) - n + 24 once, to a multiple of 2^-48 (the result lies in
+// [23.5, 24.5], so its exponent is that of 16), and the low 48 mantissa bits
+// are the fraction of the turn.  Branch-free and exact in n for any finite
+// angle below 2^50 turns.
+__device__ __forceinline__ uint64_t to_fixed(float a) {
+#pragma clang fp contract(off)
+  const double x = (double)a;
+  const double n = __builtin_rint(x * INV_2PI);
+  const double y = __builtin_fma(x, INV_2PI, 24.0 - n);
+  return (uint64_t)__double_as_longlong(y) & MASK48;
 }
-__device__ __forceinline__ void publish(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+// Fixed-point turns (already offset by 2^47) -> radians in [-pi, pi).
+// The 48 bits become the mantissa of a double in [16, 17); subtracting 16.5
+// is exact and yields the signed turn in [-1/2, 1/2).
+__device__ __forceinline__ float to_radians_offset(uint64_t u) {
+#pragma clang fp contract(off)
+  const uint64_t bits = (0x4030000000000000ull) | (u & MASK48);
+  const double z = __longlong_as_double((long long)bits) - 16.5;
+  return (float)(z * TWO_PI);
 }
-__device__ __forceinline__ uint64_t peek(uint64_t* p) {
+
+__device__ __forceinline__ uint64_t shfl_up64(uint64_t v, int delta) {
+  const uint32_t lo = __shfl_up((uint32_t)v, delta);
+  const uint32_t hi = __shfl_up((uint32_t)(v >> 32), delta);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t peek(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ bool is_ready(uint64_t w) { return (w & 1u) != 0; }
-__device__ __forceinline__ uint64_t value_of(uint64_t w) { return w & ~(uint64_t)1; }
+__device__ __forceinline__ void publish(uint64_t* p, uint64_t value, uint64_t status) {
+  __hip_atomic_store(p, (value << 16) | status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-// hdr: 4 words per segment {ticket, done, failed, unused}.
-// words: per segment [nchunks][P][2] (aggregate, inclusive prefix).
+// Sum of the converted angles of pair p over tokens t0, t0 + step, ... < t1,
+// read directly from phi (the fallback when a predecessor's aggregate is not
+// yet published).
+__device__ uint64_t reduce_pair(const float* __restrict__ seg_phi, int P, int p, int t0, int t1,
+                                int step) {
+  uint64_t acc = 0;
+  for (int t = t0; t < t1; t += step) acc += to_fixed(seg_phi[(size_t)t * P + p]);
+  return acc;
+}
+
+// Look-back of one chunk, run by wave 0.  Lane l serves pair p = l % P and
+// every K-th predecessor (K = 64 / P lanes per pair), W predecessors each per
+// pass, so a pass reads K * W predecessors of every pair at once.  Returns
+// the sum of the aggregates of chunks 0 .. chunk-1 of the segment for pair p
+// (the same value on the K lanes of a pair).
+template <int P>
+__device__ uint64_t look_back(const uint64_t* __restrict__ wh, size_t wbase, uint32_t half,
+                              int chunk, const float* __restrict__ seg_phi, int L, int CH,
+                              int lane) {
+  constexpr int K = 64 / P;
+  constexpr int W = 8;
+  constexpr int SPAN = K * W;  // predecessors per pass
+  const int p = lane % P, k0 = lane / P;
+  uint64_t acc = 0;
+  int d = chunk - 1;  // nearest predecessor not yet accounted for
+  int polls = 0;
+  while (d >= 0) {
+    // All W loads are issued unconditionally (indices clamped into the
+    // segment) so that they are in flight together; words before the first
+    // chunk are then replaced by a final prefix of zero.
+    uint64_t wv[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const int c = d - (k0 + K * i);
+      wv[i] = peek(wh + phys_word(wbase + (size_t)max(c, 0) * P + p, half));
+    }
+#pragma unroll
+    for (int i = 0; i < W; ++i)
+      if (d - (k0 + K * i) < 0) wv[i] = ST_INC;
+    // First predecessor (by distance) whose word is not an aggregate.
+    int stop = SPAN;
+#pragma unroll
+    for (int i = W - 1; i >= 0; --i)
+      if ((wv[i] & ST_MASK) != ST_AGG) stop = k0 + K * i;
+    if (K == 2) stop = min(stop, __shfl_xor(stop, 32));
+    uint64_t part = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i)
+      if (k0 + K * i < stop) part += wv[i] >> 16;
+    if (stop < SPAN && (stop % K) == k0) {
+      const uint64_t w = wv[stop / K];
+      if ((w & ST_MASK) == ST_INC) part += (w >> 16) | (1ull << 62);  // mark: found final prefix
+    }
+    if (K == 2) {
+      const uint32_t lo = __shfl_xor((uint32_t)part, 32), hi = __shfl_xor((uint32_t)(part >> 32), 32);
+      part += ((uint64_t)hi << 32) | lo;
+    }
+    const bool found = (part >> 62) & 1;
+    acc += part & ~(1ull << 62);
+    if (found) break;
+    if (stop == SPAN) {
+      d -= SPAN;
+      polls = 0;
+      continue;
+    }
+    // Predecessor d - stop has published nothing yet: wait for it, or after
+    // enough polls reduce its angles from phi here.
+    d -= stop;
+    if (stop > 0) polls = 0;
+    if (++polls > FALLBACK_POLLS) {
+      const int t0 = d * CH, t1 = min(t0 + CH, L);
+      uint64_t r = reduce_pair(seg_phi, P, p, t0 + k0, t1, K);
+      if (K == 2) {
+        const uint32_t lo = __shfl_xor((uint32_t)r, 32), hi = __shfl_xor((uint32_t)(r >> 32), 32);
+        r += ((uint64_t)hi << 32) | lo;
+      }
+      acc += r;
+      --d;
+      polls = 0;
+    } else {
+      if (polls < 8) __builtin_amdgcn_s_sleep(1);
+      else __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  return acc;
+}
+
 template <int P, int T>
 __global__ __launch_bounds__(SCAN_THREADS) void angle_scan_kernel(
-    const float* __restrict__ phi, float* __restrict__ theta, uint32_t* __restrict__ hdr,
+    const float* __restrict__ phi, float* __restrict__ theta, ScanHeader* __restrict__ hdr,
     uint64_t* __restrict__ words, int L, int nchunks, int exclusive) {
-  constexpr int CPT = P / 4;              // threads per token row
+  constexpr int CPT = P / 4;              // threads per token row (4 pairs each)
   constexpr int RG = SCAN_THREADS / CPT;  // row groups per chunk
   constexpr int CH = RG * T;              // tokens per chunk
-  static_assert(P % 4 == 0 && SCAN_THREADS % CPT == 0 && P <= 64, "P must be 32 or 64");
+  constexpr int RGW = 64 / CPT;           // row groups per wave
+  constexpr int NWAVE = SCAN_THREADS / 64;
+  static_assert(P == 32 || P == 64, "P must be 32 or 64");
 
-  constexpr int SLOTS = SCAN_THREADS / P;  // look-back slots per pair
-  __shared__ int s_chunk;
-  __shared__ int s_last;
-  __shared__ int s_fail;
-  __shared__ uint64_t s_tot[RG * P];
-  __shared__ uint64_t s_pre[P];   // exclusive prefix of this chunk, per pair
-  __shared__ uint64_t s_agg[P];   // aggregate of this chunk, per pair
-  __shared__ int s_chi[P];        // next predecessor to examine, per pair
-  __shared__ int s_done[P];
-  __shared__ uint64_t s_part[SLOTS * P];
-  __shared__ int s_stat[SLOTS * P];
+  __shared__ uint64_t s_wtot[NWAVE][P];  // per-wave totals
+  __shared__ uint64_t s_carry[P];        // exclusive prefix of this chunk (+ 2^47)
 
-  const int seg = blockIdx.y;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int cq = tid % CPT;
   const int rg = tid / CPT;
-  uint32_t* h = hdr + 4 * seg;
-  uint64_t* wseg = words + (size_t)seg * nchunks * P * 2;
-
-  if (tid == 0) {
-    s_chunk = (int)atomicAdd(&h[0], 1u);
-    s_fail = 0;
-  }
-  __syncthreads();
-  const int chunk = s_chunk;
+  const int nblocks = gridDim.x;
+  const int seg = blockIdx.x / nchunks;
+  const int chunk = blockIdx.x % nchunks;
   const int tbase = chunk * CH + rg * T;
 
-  // Load this thread's T x 4 step angles (one HBM read of phi).
-  const float* src = phi + (size_t)seg * L * P + cq * 4;
+  // The header was last written by an earlier launch, so plain (cached)
+  // loads see it; every workgroup reads it before it counts itself done.
+  const uint32_t half = hdr->parity & 1u;
+  const uint64_t stale = hdr->used[half ^ 1u];
+  const int ngroups = (nblocks + GROUP - 1) / GROUP;
+
+  // ---- load T rows x 4 pairs; thread totals of the converted angles ----
+  const float* seg_phi = phi + (size_t)seg * L * P;
+  // Loads are unconditional (rows clamped into the segment) so that all T of
+  // them are in flight at once; rows past the end then count as zero.
   float4 x[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const int tok = tbase + t;
-    x[t] = (tok < L) ? *reinterpret_cast<const float4*>(src + (size_t)tok * P)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int tok = min(tbase + t, L - 1);
+    x[t] = *reinterpret_cast<const float4*>(seg_phi + (size_t)tok * P + cq * 4);
   }
-
-  // Thread totals.
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+    if (tbase + t >= L) x[t] = make_float4(0.f, 0.f, 0.f, 0.f);
   uint64_t tot[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    tot[0] += to_turns(x[t].x);
-    tot[1] += to_turns(x[t].y);
-    tot[2] += to_turns(x[t].z);
-    tot[3] += to_turns(x[t].w);
+    tot[0] += to_fixed(x[t].x);
+    tot[1] += to_fixed(x[t].y);
+    tot[2] += to_fixed(x[t].z);
+    tot[3] += to_fixed(x[t].w);
   }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) s_tot[rg * P + cq * 4 + c] = tot[c];
-  __syncthreads();
 
-  // One thread per pair (all in wave 0): exclusive scan over the row groups
-  // and publication of the chunk aggregate (the inclusive prefix for chunk 0).
-  if (tid < P) {
-    uint64_t run = 0;
-    for (int r = 0; r < RG; ++r) {
-      const uint64_t v = s_tot[r * P + tid];
-      s_tot[r * P + tid] = run;
-      run += v;
+  // ---- exclusive prefix of this thread within the chunk ----
+  // Inclusive scan over the wave's row groups (lanes CPT apart), then the
+  // totals of the earlier waves from LDS.
+  uint64_t pre[4];
+  const int rgw = lane / CPT;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint64_t v = tot[c];
+#pragma unroll
+    for (int off = 1; off < RGW; off <<= 1) {
+      const uint64_t u = shfl_up64(v, off * CPT);
+      if (rgw >= off) v += u;
     }
-    s_agg[tid] = run;
-    publish(&wseg[((size_t)chunk * P + tid) * 2 + (chunk == 0 ? 1 : 0)], run);
-    s_pre[tid] = 0;
-    s_chi[tid] = chunk - 1;
-    s_done[tid] = (chunk == 0);
+    pre[c] = v - tot[c];
+    if (rgw == RGW - 1) s_wtot[wave][cq * 4 + c] = v;
   }
   __syncthreads();
-
-  // Look-back over earlier chunks with every thread: per pair, SLOTS slots of
-  // LB_R consecutive predecessors each, i.e. SLOTS * LB_R predecessors per
-  // pass, loaded in parallel.  A pass stops at the nearest published inclusive
-  // prefix (done), or at the first predecessor whose aggregate is not yet
-  // published (retry from there).
-  if (chunk > 0) {
-    const int p = tid % P, slot = tid / P;
-    uint32_t passes = 0;
-    bool all_done = false;
-    while (!all_done) {
-      uint64_t part = 0;
-      int stat = LB_ALL, used = LB_R;
-      if (!s_done[p]) {
-        const int c0 = s_chi[p] - slot * LB_R;
-        uint64_t wi[LB_R], wa[LB_R];
 #pragma unroll
-        for (int r = 0; r < LB_R; ++r) {
-          const int c = c0 - r;
-          wi[r] = (c >= 0) ? peek(&wseg[((size_t)c * P + p) * 2 + 1]) : 0;
-          wa[r] = (c >= 0) ? peek(&wseg[((size_t)c * P + p) * 2 + 0]) : 0;
-        }
-#pragma unroll
-        for (int r = 0; r < LB_R; ++r) {
-          if (stat != LB_ALL) break;
-          const int c = c0 - r;
-          if (c < 0) {
-            stat = LB_FOUND;
-            used = r;
-          } else if (is_ready(wi[r])) {
-            part += value_of(wi[r]);
-            stat = LB_FOUND;
-            used = r + 1;
-          } else if (is_ready(wa[r])) {
-            part += value_of(wa[r]);
-          } else {
-            stat = LB_BLOCKED;
-            used = r;
-          }
-        }
-      }
-      s_part[slot * P + p] = part;
-      s_stat[slot * P + p] = stat | (used << 2);
-      __syncthreads();
-      int blocked = 0;
-      if (tid < P && !s_done[tid]) {
-        uint64_t acc = s_pre[tid];
-        int chi = s_chi[tid];
-        int done = 0;
-        for (int sl = 0; sl < SLOTS; ++sl) {
-          const int st = s_stat[sl * P + tid];
-          acc += s_part[sl * P + tid];
-          if ((st & 3) == LB_FOUND) {
-            done = 1;
-            break;
-          }
-          if ((st & 3) == LB_BLOCKED) {
-            chi -= sl * LB_R + (st >> 2);
-            blocked = 1;
-            break;
-          }
-          if (sl == SLOTS - 1) chi -= SLOTS * LB_R;
-        }
-        if (!done && ++passes > SPIN_LIMIT) {
-          // give up: this segment's angles read NaN (flag seen by later chunks)
-          s_fail = 1;
-          __hip_atomic_store(&h[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          done = 1;
-        }
-        s_pre[tid] = acc;
-        s_chi[tid] = chi;
-        s_done[tid] = done;
-      }
-      if (__syncthreads_or(blocked)) __builtin_amdgcn_s_sleep(2);
-      all_done = __syncthreads_and(tid < P ? s_done[tid] : 1);
-    }
-  }
+  for (int c = 0; c < 4; ++c)
+    for (int w = 0; w < wave; ++w) pre[c] += s_wtot[w][cq * 4 + c];
 
-  // Publish this chunk's inclusive prefix; lane 0 of the same wave then counts
-  // the chunk as finished (its release covers the wave's publications).
-  if (tid < P) {
-    if (chunk > 0) publish(&wseg[((size_t)chunk * P + tid) * 2 + 1], s_pre[tid] + s_agg[tid]);
-    if (tid == 0) {
-      uint32_t prev = __hip_atomic_fetch_add(&h[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (prev == (uint32_t)(nchunks - 1));
+  // ---- publish the aggregate, look back, publish the inclusive prefix ----
+  const size_t wbase = (size_t)ngroups + ((size_t)seg * nchunks) * P;
+  if (wave == 0) {
+    const int p = lane % P;
+    uint64_t agg = 0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) agg += s_wtot[w][p];
+    uint64_t* my = words + phys_word(wbase + (size_t)chunk * P + p, half);
+    if (lane < P) publish(my, agg, chunk == 0 ? ST_INC : ST_AGG);
+    uint64_t acc = 0;
+    if (chunk > 0) {
+      acc = look_back<P>(words, wbase, half, chunk, seg_phi, L, CH, lane);
+      if (lane < P) publish(my, acc + agg, ST_INC);
     }
+    if (lane < P) s_carry[p] = acc + (1ull << 47);  // turns [0,1) into [-1/2,1/2) below
   }
   __syncthreads();
 
-  // Second pass over the registers: running angle from the thread's start.
+  // ---- outputs: running angle from the thread's first row ----
+  // The steps are converted again from the raw angles rather than kept from
+  // the first pass: holding T x 4 64-bit values live across the look-back
+  // would cut the number of resident workgroups by up to four.  The empty asm
+  // hides the equality from the compiler so that it cannot merge the two
+  // conversions.
+#pragma unroll
+  for (int t = 0; t < T; ++t) asm volatile("" : "+v"(x[t].x), "+v"(x[t].y), "+v"(x[t].z), "+v"(x[t].w));
+  float* seg_theta = theta + (size_t)seg * L * P;
   uint64_t run[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) run[c] = s_pre[cq * 4 + c] + s_tot[rg * P + cq * 4 + c];
-  const bool fail =
-      s_fail != 0 || __hip_atomic_load(&h[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-  float* dst = theta + (size_t)seg * L * P + cq * 4;
+  for (int c = 0; c < 4; ++c) run[c] = pre[c] + s_carry[cq * 4 + c];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const float xs[4] = {x[t].x, x[t].y, x[t].z, x[t].w};
     float out[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint64_t step = to_turns(xs[c]);
+      const uint64_t step = to_fixed(xs[c]);
       if (exclusive) {
-        out[c] = to_radians(run[c]);
+        out[c] = to_radians_offset(run[c]);
         run[c] += step;
       } else {
         run[c] += step;
-        out[c] = to_radians(run[c]);
+        out[c] = to_radians_offset(run[c]);
       }
-      if (fail) out[c] = __builtin_nanf("");
     }
     const int tok = tbase + t;
     if (tok < L)
-      *reinterpret_cast<float4*>(dst + (size_t)tok * P) = make_float4(out[0], out[1], out[2], out[3]);
+      *reinterpret_cast<float4*>(seg_theta + (size_t)tok * P + cq * 4) =
+          make_float4(out[0], out[1], out[2], out[3]);
   }
 
-  // The last chunk of the segment leaves the state zeroed for the next call.
-  if (s_last) {
-    for (int i = tid; i < nchunks * P * 2; i += SCAN_THREADS) wseg[i] = 0;
-    if (tid == 0) {
-      h[0] = 0;
-      h[1] = 0;
-      h[2] = 0;
+  // ---- state upkeep: clear this block's share of the other half ----
+  {
+    const uint64_t per = (stale + nblocks - 1) / nblocks;
+    const uint64_t w0 = per * blockIdx.x;
+    const uint64_t w1 = min(stale, w0 + per);
+    for (uint64_t w = w0 + tid; w < w1; w += SCAN_THREADS) words[phys_word(w, half ^ 1u)] = 0;
+  }
+  __syncthreads();  // every thread of the block is past its last use of the state
+
+  // Completion count in two levels (a counter per GROUP workgroups, then one
+  // for the groups), so that no single address takes an atomic from every
+  // workgroup.  The workgroup that completes the last group hands the state
+  // to the next call: every other workgroup has read the header and finished
+  // with the status words by then, and the next launch sees these header
+  // fields at the kernel boundary.
+  if (tid == 0) {
+    const int grp = blockIdx.x / GROUP;
+    const uint32_t gsize = (uint32_t)min(GROUP, nblocks - grp * GROUP);
+    uint64_t* gc = words + phys_word((size_t)grp, half);
+    const uint64_t pg =
+        __hip_atomic_fetch_add(gc, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (pg == gsize - 1) {
+      const uint32_t pd =
+          __hip_atomic_fetch_add(&hdr->done[half], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (pd == (uint32_t)(ngroups - 1)) {
+        __hip_atomic_store(&hdr->done[half], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&hdr->used[half], (uint64_t)ngroups + (uint64_t)nblocks * P,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&hdr->used[half ^ 1u], (uint64_t)0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&hdr->parity, half ^ 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
@@ -279,16 +374,15 @@ constexpr int rows_per_group(int P) { return SCAN_THREADS / (P / 4); }
 }  // namespace
 
 ScanPlan scan_plan(const Geometry& g) {
-  const int rg = rows_per_group(g.P);
+  // Rows per thread: 16 (64 KB of phi per workgroup) amortises the look-back
+  // latency best once the grid has a workgroup per SIMD; smaller problems
+  // take smaller chunks so that the grid still covers the chip.
   const long nseg = (long)g.B * g.Hphi;
+  const int rg = rows_per_group(g.P);
+  auto blocks = [&](int T) { return nseg * ((g.L + (long)rg * T - 1) / ((long)rg * T)); };
   int T = 4;
-  for (int cand : {16, 8}) {
-    const long nch = (g.L + (long)rg * cand - 1) / ((long)rg * cand);
-    if (nseg * nch >= 1024) {
-      T = cand;
-      break;
-    }
-  }
+  if (blocks(16) >= 1024) T = 16;
+  else if (blocks(8) >= 512) T = 8;
   ScanPlan sp;
   sp.rows_per_thread = T;
   sp.chunk = rg * T;
@@ -297,21 +391,26 @@ ScanPlan scan_plan(const Geometry& g) {
 }
 
 size_t scan_state_bytes(const Geometry& g) {
-  const size_t nseg = (size_t)g.B * g.Hphi;
+  // Sized for the smallest chunk any plan uses, so the bound holds whatever
+  // rows-per-thread the plan picks.
   const size_t min_chunk = (size_t)rows_per_group(g.P) * 4;
-  const size_t nchunks_max = (g.L + min_chunk - 1) / min_chunk;
-  size_t bytes = nseg * 16 + nseg * nchunks_max * g.P * 2 * sizeof(uint64_t);
+  const size_t nchunks = (g.L + min_chunk - 1) / min_chunk;
+  const size_t nblocks = (size_t)g.B * g.Hphi * nchunks;
+  const size_t words = (nblocks + GROUP - 1) / GROUP + nblocks * g.P;  // counters + status
+  const size_t blocks = (words + 31) / 32;  // both halves, 32-word blocks
+  const size_t bytes = sizeof(ScanHeader) + blocks * 2 * 32 * sizeof(uint64_t);
   return (bytes + 255) & ~(size_t)255;
 }
 
 hipError_t launch_angle_scan(const Geometry& g, const float* phi, float* theta, void* scan_state,
                              hipStream_t stream) {
   const ScanPlan sp = scan_plan(g);
-  const int nseg = g.B * g.Hphi;
-  uint32_t* hdr = reinterpret_cast<uint32_t*>(scan_state);
-  uint64_t* words = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(scan_state) + (size_t)nseg * 16);
+  const long nblocks = (long)g.B * g.Hphi * sp.nchunks;
+  auto* hdr = reinterpret_cast<ScanHeader*>(scan_state);
+  auto* words = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(scan_state) + sizeof(ScanHeader));
   const int excl = (g.flags & ARP_SCAN_EXCLUSIVE) ? 1 : 0;
-  dim3 grid(sp.nchunks, nseg);
+  if (nblocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)nblocks);
   dim3 block(SCAN_THREADS);
 #define ARP_SCAN_LAUNCH(PP, TT)                                                                   \
   hipLaunchKernelGGL((angle_scan_kernel<PP, TT>), grid, block, 0, stream, phi, theta, hdr, words, \

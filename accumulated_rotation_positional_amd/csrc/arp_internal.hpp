@@ -21,8 +21,8 @@ struct Geometry {
 };
 
 // ---- buffers ----------------------------------------------------------------
-// scan state: per (batch, angle head) segment a 16-byte header {ticket, done}
-//   and [nchunks][P][2] 64-bit look-back words; kept zeroed between calls.
+// scan state: a 256-byte header and two interleaved halves of 64-bit
+//   look-back status words, [B*Hphi][nchunks][P] per half (angle_scan.hip).
 // workspace:  [ q~ (bf16, [B*H, Lp, D]) | k~ (bf16, [B*H, Lp, D]) | v~^T (bf16, [B*H, D, Lp]) ]
 //   for bf16 without ARP_FUSED_ROTATION; empty otherwise.
 struct ScanPlan {

@@ -35,10 +35,12 @@
  *  - stream is a hipStream_t (NULL: the default stream).  Work is enqueued
  *    asynchronously; nothing is synchronised; no host memory is touched.
  *  - The library allocates nothing.  It uses two caller-provided buffers:
- *      scan_state (arp_scan_state_bytes): the look-back flags of the angle
- *        scan.  Zero-fill it once before its first use; every completed scan
- *        leaves it zeroed again, so one buffer serves any number of calls and
- *        problem sizes (when large enough).  Nothing else may write to it.
+ *      scan_state (arp_scan_state_bytes): the look-back status words of the
+ *        angle scan.  Zero-fill it once before its first use and never write
+ *        to it afterwards: each scan leaves it ready for the next one (it
+ *        keeps two halves and alternates between them), so one buffer serves
+ *        any number of calls and problem sizes, as long as each call's
+ *        arp_scan_state_bytes fits in it.
  *      workspace (arp_workspace_bytes): the rotated bf16 operands of the
  *        pre-rotation path; no initialisation needed.
  *    Calls that share a buffer must be ordered (same stream).
@@ -103,7 +105,7 @@ const char* arp_status_string(int status);
 arp_status arp_check(const arp_desc* desc);
 
 /* Bytes of the angle scan's look-back state for desc (0 when desc is invalid).
- * The state must be zero before first use and is left zeroed by every call. */
+ * The state must be zero before first use; every call leaves it ready for the next. */
 size_t arp_scan_state_bytes(const arp_desc* desc);
 
 /* Bytes of the operand workspace for desc: the rotated bf16 q~, k~, v~^T of
