@@ -1,20 +1,27 @@
 """Benchmark: accumulated-rotation causal attention forward on one MI355X.
 
 One step = the whole hot path on one batch of the 16x-extrapolation workload
-(B=2, H=8, L=16384, d=64, bf16, learned token-dependent angles, q/k/v
-rotation): angle scan -> rotation pass -> attention kernel, through the C ABI,
-with inputs resident in HBM.  Prints ONE JSON line.
+(B=2, H=8, L=16384, d=64, bf16, learned token-dependent angles, rotation of
+q, k and v): angle scan -> rotation pass -> attention kernel, through the C
+ABI, with inputs resident in HBM.  Prints ONE JSON line.
 
-  value      whole-step throughput in TFLOP/s of algorithmic attention work,
-             4 d per causal (query, key) pair (the two contractions only)
-  roofline   the attention kernel against the bf16 matrix-core peak, its
-             duration measured with HIP events on the stream it runs on
+  value         whole-step throughput in TFLOP/s of algorithmic attention
+                work, 4 d per causal (query, key) pair (the two contractions)
+  tokens_per_s  B * L / step time
+  roofline      the attention kernel (the dominant one) against the bf16
+                matrix-core peak; its duration is measured with HIP events on
+                the stream it is launched on.  traffic = HBM bytes per launch
+                from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary in
+                profiles/, when that summary was taken on the current kernel
+                source (else null)
+  scan_roofline the angle scan against the HBM peak (8 bytes per element)
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
-             workload (a strided subset of query rows of every head)
+                workload (strided query rows of every head)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +35,10 @@ import numpy as np  # noqa: E402
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense)
 HBM_PEAK_GBS = 8000.0
 METRIC = "accum-rotation causal attention fwd TFLOP/s + tokens/s at L=16K, d=64"
+CSRC = os.path.join(ROOT, "accumulated_rotation_positional_amd", "csrc")
+ATTN_SOURCES = ("attn_bf16.hip", "arp_device.hpp")
+SCAN_SOURCES = ("angle_scan.hip",)
+COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_extrap_16k_hbm_counters.json")
 
 
 def parse():
@@ -40,7 +51,35 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target duration of the CPU oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run one plain device copy of 256 MiB (the reference kernel "
+                        "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return p.parse_args()
+
+
+def source_hash(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel and of the angle scan from
+    the committed counter summary; each is None when the summary is missing,
+    was taken on another workload, or is older than that kernel's source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None, None
+    if c.get("workload") != workload:
+        return None, None
+    attn = c.get("hbm_bytes_per_launch") if c.get("source_hash") == source_hash(ATTN_SOURCES) else None
+    scan = (c.get("scan_hbm_bytes_per_launch")
+            if c.get("scan_source_hash") == source_hash(SCAN_SOURCES) else None)
+    return attn, scan
 
 
 def _strided_rows(w, stride: int, offset: int = 0) -> np.ndarray:
@@ -50,16 +89,24 @@ def _strided_rows(w, stride: int, offset: int = 0) -> np.ndarray:
 
 
 def run_cpu_baseline(w, flags: int, alibi, target_s: float) -> dict:
+    """Time the oracle on strided query rows.  Its cost is a fixed part per
+    head (angle scan and key/value rotation) plus a part per row, so two
+    calibration runs fix both before the timed sample is sized."""
     import oracle
 
     nthreads = min(len(os.sched_getaffinity(0)), 16)
     prob = oracle.Problem(w.q, w.k, w.v, w.phi, flags, alibi=alibi)
-    # calibrate on a small sample, then size the timed sample for ~target_s
-    stride = 4096
-    t0 = time.perf_counter()
-    prob.rows(_strided_rows(w, stride, 17), nthreads)
-    t_cal = time.perf_counter() - t0
-    stride = int(max(1, min(4096, stride * t_cal / target_s)))
+    samples = []
+    for stride in (2048, 512):
+        rows = _strided_rows(w, stride, 17)
+        t0 = time.perf_counter()
+        prob.rows(rows, nthreads)
+        samples.append((rows.size, time.perf_counter() - t0))
+    (n1, t1), (n2, t2) = samples
+    per_row = max((t2 - t1) / max(n2 - n1, 1), 1e-9)
+    fixed = max(t1 - per_row * n1, 0.0)
+    want_rows = max((target_s - fixed) / per_row, n2)
+    stride = int(max(1, min(512, round(w.batch * w.heads * w.seqlen / want_rows))))
     rows = _strided_rows(w, stride, 5)
     t0 = time.perf_counter()
     prob.rows(rows, nthreads)
@@ -70,15 +117,15 @@ def run_cpu_baseline(w, flags: int, alibi, target_s: float) -> dict:
             "sample": f"{rows.size} query rows (every {stride}th row of each of the "
                       f"{w.batch * w.heads} heads, with the angle scan and key/value "
                       f"rotation of each head), fp64, {dt:.1f} s",
-            "seconds": dt, "tokens_per_s": rows.size / dt}
+            "seconds": round(dt, 3), "tokens_per_s": rows.size / dt}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards over (batch, head) with no exchange; see DESIGN.md)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the path "
+              "shards over (batch, head) with no exchange, so one GPU's share is the "
+              "measured unit (see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -128,6 +175,16 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # The timed region holds exactly the K steps, bracketed by device
+    # synchronisation; events between the kernels of each step give the
+    # per-kernel durations on the stream the kernels run on.
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)]
               for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -139,9 +196,7 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
+    ms_step = start.elapsed_time(end) / args.steps
     seg = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(n_ev)] for e in events])
     scan_ms = float(seg[:, 0].mean())
     attn_ms = float(seg[:, -1].mean())
@@ -153,6 +208,9 @@ def main():
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     scan_bytes = 8.0 * w.batch * w.phi_heads * w.seqlen * (w.head_dim // 2)
     scan_gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
+    traffic, scan_traffic = measured_traffic(w.name)
+    if fused:
+        traffic = None
 
     result = {
         "metric": METRIC,
@@ -176,9 +234,10 @@ def main():
                        "attn_fwd": round(attn_ms, 5)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
         "scan_roofline": {"bound": "hbm", "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS,
-                          "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4)},
+                          "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+                          "traffic": scan_traffic},
     }
     if not args.no_cpu_baseline:
         import oracle
