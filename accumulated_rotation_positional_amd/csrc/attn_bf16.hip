@@ -1,7 +1,7 @@
 // attn_bf16.hip -- causal attention over rotated bf16 operands, on the gfx950
 // matrix cores.
 //
-//   s_ij  = <q~_i, k~_j> (q~ already carries scale * log2 e)  [- m_h log2e (i-j)]
+//   s_ij  = <q~_i, k~_j> (q~ already carries scale * log2 e)  [+ m_h log2e (j - i)]
 //   o~_i  = sum_{j<=i} 2^(s_ij - M_i) v~_j / sum_{j<=i} 2^(s_ij - M_i)
 //   o_i   = R(Theta_i)^T o~_i  (value transport)  or  o~_i
 //
@@ -11,28 +11,31 @@
 // Work decomposition
 //  * A workgroup owns BM = NW * QPW consecutive queries of one (batch, head)
 //    and walks the key tiles j0 = 0, BN, 2BN, ... up to its last query.
-//    Each of its NW waves owns QPW queries; a wave skips tiles past its own
-//    last query and masks only the tile that crosses its diagonal.
+//    Each of its NW waves owns QPW queries; a wave skips the tiles past its
+//    own last query and masks only the tile that holds its diagonal.
 //  * Both products put the query on the matrix-core N axis, so one lane owns
 //    one query and the softmax row statistics are per lane:
 //      S^T [keys x queries] = K~ [keys x D] . Q~^T          (v_mfma_f32_32x32x16_bf16)
 //      O^T [D x queries]   += V~^T [D x keys] . P^T         (same instruction)
-//    The row maximum needs one cross-lane exchange (lane ^ 32) per tile.
-//  * K~ rows are stored in LDS in an order (bits 2 and 3 of the row index
-//    swapped) that makes the S^T accumulator layout coincide with the P^T
-//    operand layout: a lane's 8 consecutive accumulator values are its 8
-//    consecutive keys, so P^T is built with no data movement.
-//  * Q~ stays in registers for the whole key loop.  K~ and V~^T tiles are
-//    double-buffered in LDS with an XOR swizzle of 16-byte chunks (no bank
-//    conflicts on the 128-bit reads); the next tile's global loads are in
-//    flight while the current tile is computed; one barrier per tile.
-//  * The running max is subtracted inside the matrix-core product (the
-//    accumulator is initialised to -m), and it is only raised when a row's
-//    tile maximum exceeds it by more than TAU = 8 (so 2^(s-m) <= 256): most
-//    tiles need no rescale of the output accumulator.  Row sums are formed
-//    from the bf16 probabilities with v_dot2_f32_bf16 (two per instruction).
-//  * Workgroups are numbered so that each XCD (blockIdx % 8) gets whole heads
-//    (its L2 then holds that head's K/V), longest query tiles first.
+//    A row maximum needs one exchange between the two half-waves.
+//  * K~ rows sit in LDS in an order (bits 2 and 3 of the row index swapped)
+//    that makes the S^T accumulator layout coincide with the P^T operand
+//    layout: a lane's 8 consecutive accumulator values are its 8 consecutive
+//    keys, so P^T is built in registers with no data movement.
+//  * K~ and V~^T tiles go from global memory straight into LDS
+//    (global_load_lds_dwordx4, no staging registers) through a ring of NST
+//    stages: the loads of the next NST-1 tiles are in flight while a tile is
+//    computed; one barrier per tile.  The LDS layout XOR-swizzles 16-byte chunks (no bank
+//    conflicts on the 128-bit operand reads); since a direct load writes lane
+//    l's 16 bytes to position 16 l, the swizzle is applied to the global
+//    addresses instead.
+//  * The running maximum is subtracted inside the matrix-core product (the
+//    accumulator input is -m, kept in registers), and it is only raised when
+//    a row's tile maximum exceeds it by more than TAU = 8 (so 2^(s-m) <= 256):
+//    most tiles need no rescale of the output accumulator.  Row sums are
+//    formed from the bf16 probabilities with v_dot2_f32_bf16.
+//  * Workgroups are numbered so that each XCD (blockIdx % 8) gets whole
+//    heads (its L2 then holds that head's K/V), longest query tiles first.
 #include "arp_device.hpp"
 #include "arp_internal.hpp"
 
@@ -43,6 +46,10 @@ namespace {
 constexpr int BN = 64;        // keys per tile
 constexpr float TAU = 8.0f;   // lazy-rescale threshold (base-2 logits)
 
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef const __attribute__((address_space(1))) void* global_void_ptr;
+
+// Row order of K~ in LDS: bits 2 and 3 of the key index swapped (an involution).
 __device__ __forceinline__ int swap_bits23(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
@@ -51,13 +58,31 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D, int QPW, int NW, bool ALIBI, bool ROTV>
+// Max and sum of a value over the two half-waves (lanes l and l ^ 32), with
+// one v_permlane32_swap: afterwards each lane holds both halves' values.
+__device__ __forceinline__ float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Wait until at most N global->LDS loads of this wave are still in flight
+// (s_waitcnt vmcnt(N), the other counters untouched).
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+template <int D, int QPW, int NW, int NST, bool ALIBI, bool ROTV>
 __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const float* __restrict__ theta,
     const float* __restrict__ alibi, uint16_t* __restrict__ o, int L, int Lp, int H, int Hphi,
     int nqt, int total_tiles) {
-  constexpr int NT = NW * 64;
   constexpr int BM = QPW * NW;
   constexpr int QB = QPW / 32;         // 32-query blocks per wave
   constexpr int KS = D / 16;           // k-steps of S^T (16 of D each)
@@ -68,14 +93,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
   constexpr int KTILE = BN * KROW;
   constexpr int VROW = BN * 2;         // bytes per V~^T row in LDS
   constexpr int VTILE = D * VROW;
-  constexpr int STAGE = KTILE + VTILE;
-  constexpr int KCH = D / 8;           // 16-byte chunks per K~ row
-  constexpr int NKL = BN * KCH / NT;   // K chunks each thread stages
-  constexpr int NVL = D * (BN / 8) / NT;
-  static_assert(NKL * NT == BN * KCH && NVL * NT == D * (BN / 8), "staging split");
+  constexpr int KLD = KTILE / (1024 * NW);  // 1 KB direct loads per wave per tile
+  constexpr int VLD = VTILE / (1024 * NW);
+  static_assert(KLD * 1024 * NW == KTILE && VLD * 1024 * NW == VTILE, "staging split");
   static_assert(QPW % 32 == 0 && BN == 64, "tile shape");
+  static_assert(NST == 2 || NST == 3, "load-wait counts are written for 2 or 3 stages");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  constexpr int STAGE = KTILE + VTILE;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
   // ---- which tile: XCD-aware, heads grouped per XCD, longest tiles first ----
   const int per = (total_tiles + 7) / 8;
@@ -91,8 +116,33 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
   const int ln = lane & 31, hf = lane >> 5;
   const int qw = q0 + wave * QPW;  // first query of this wave
   const int last_tile = min(q0 + BM - 1, L - 1) / BN;
-  const int last_tile_w = min(qw + QPW - 1, L - 1) / BN;
+  const int last_w = (qw < L) ? min(qw + QPW - 1, L - 1) / BN : -1;
 
+  // ---- direct global -> LDS loads of one K~ / V~^T tile ----
+  const uint16_t* kbase = kr + (size_t)bh * Lp * D;
+  const uint16_t* vbase = vt + (size_t)bh * D * Lp;
+  auto issue = [&](int tile, uint8_t* stage) __attribute__((always_inline)) {
+    const int j0 = tile * BN;
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int p0 = (wave * KLD + i) * 1024;
+      const int p = p0 + 16 * lane;
+      const int row = p / KROW, cs = (p % KROW) / 16;
+      const int c = cs ^ (row & 7);
+      const uint16_t* src = kbase + (size_t)(j0 + swap_bits23(row)) * D + 8 * c;
+      __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + p0), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int p0 = (wave * VLD + i) * 1024;
+      const int p = p0 + 16 * lane;
+      const int row = p / VROW, cs = (p % VROW) / 16;
+      const int c = cs ^ (row & 7);
+      const uint16_t* src = vbase + (size_t)row * Lp + j0 + 8 * c;
+      __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + KTILE + p0), 16,
+                                       0, 0);
+    }
+  };
   // ---- Q~ operand: lane (ln, hf) holds query qw+32qb+ln, d = 16ks+8hf..+7 ----
   bf16x8 qop[QB][KS];
 #pragma unroll
@@ -101,6 +151,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
     for (int ks = 0; ks < KS; ++ks)
       qop[qb][ks] = *reinterpret_cast<const bf16x8*>(
           qr + ((size_t)bh * Lp + qw + 32 * qb + ln) * D + 16 * ks + 8 * hf);
+
+  // First NST-1 tiles in flight before the loop.
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t)
+    if (t <= last_tile) issue(t, smem + t * STAGE);
 
   f32x16 oacc[DB][QB];
 #pragma unroll
@@ -120,165 +175,133 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
   }
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
 
-  // ---- staging: global -> registers -> LDS (swizzled) ----
-  const uint16_t* kbase = kr + (size_t)bh * Lp * D;
-  const uint16_t* vbase = vt + (size_t)bh * D * Lp;
-  u32x4 kreg[NKL], vreg[NVL];
-  auto stage_load = [&](int tile) {
-    const int j0 = tile * BN;
-#pragma unroll
-    for (int i = 0; i < NKL; ++i) {
-      const int idx = i * NT + tid;
-      const int r = idx / KCH, c = idx % KCH;
-      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(j0 + r) * D + 8 * c);
-    }
-#pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-      const int idx = i * NT + tid;
-      const int drow = idx / (BN / 8), c = idx % (BN / 8);
-      vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)drow * Lp + j0 + 8 * c);
-    }
-  };
-  auto stage_store = [&](int buf) {
-    uint8_t* base = smem + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < NKL; ++i) {
-      const int idx = i * NT + tid;
-      const int r = idx / KCH, c = idx % KCH;
-      const int row = (r & ~31) | swap_bits23(r & 31);
-      *reinterpret_cast<u32x4*>(base + row * KROW + ((c ^ (row & 7)) << 4)) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-      const int idx = i * NT + tid;
-      const int drow = idx / (BN / 8), c = idx % (BN / 8);
-      *reinterpret_cast<u32x4*>(base + KTILE + drow * VROW + ((c ^ (drow & 7)) << 4)) = vreg[i];
-    }
-  };
+  // ---- one key tile of this wave's queries ----
+  auto compute = [&](int n, const uint8_t* kt) __attribute__((always_inline)) {
+    const uint8_t* vtile = kt + KTILE;
+    const int j0 = n * BN;
 
-  stage_load(0);
-  stage_store(0);
-  __syncthreads();
-
-  for (int n = 0; n <= last_tile; ++n) {
-    const int cur = n & 1;
-    if (n < last_tile) stage_load(n + 1);
-    if (n <= last_tile_w) {
-      const uint8_t* kt = smem + cur * STAGE;
-      const uint8_t* vtile = kt + KTILE;
-      const int j0 = n * BN;
-
-      // S^T - m = K~ Q~^T + cneg
-      f32x16 s[KB][QB];
+    // S^T - m = K~ Q~^T + cneg
+    f32x16 s[KB][QB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int row = 32 * kb + ln;
-        bf16x8 ka[KS];
+    for (int kb = 0; kb < KB; ++kb) {
+      const int row = 32 * kb + ln;
+      bf16x8 ka[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ka[ks] = *reinterpret_cast<const bf16x8*>(kt + row * KROW + (((2 * ks + hf) ^ (ln & 7)) << 4));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          s[kb][qb] = mfma32(ka[0], qop[qb][0], cneg[qb]);
-#pragma unroll
-          for (int ks = 1; ks < KS; ++ks) s[kb][qb] = mfma32(ka[ks], qop[qb][ks], s[kb][qb]);
-        }
-      }
-
-      // Element r of s[kb][qb] on this lane is key j0 + koff(kb, r) + 8 hf,
-      // koff = 32 kb + 16 (r>>3) + 4 ((r>>2)&1) + (r&3); query qw + 32 qb + ln.
-      const bool diag = (j0 + BN - 1 > qw);
-      if (ALIBI || diag) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int base = j0 + 8 * hf - (qw + 32 * qb + ln);  // key - query minus koff
-          const float fb = slope2 * (float)base;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int koff = 32 * kb + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
-              float x = s[kb][qb][r];
-              if (ALIBI) x += fmaf(slope2, (float)koff, fb);
-              if (diag && koff + base > 0) x = -INFINITY;
-              s[kb][qb][r] = x;
-            }
-        }
-      }
-
-      // Row maxima of the shifted logits (both lane halves).
-      float mx[QB];
-      bool need = (n == 0);
+      for (int ks = 0; ks < KS; ++ks)
+        ka[ks] = *reinterpret_cast<const bf16x8*>(kt + row * KROW + (((2 * ks + hf) ^ (ln & 7)) << 4));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float t = s[0][qb][0];
+        s[kb][qb] = mfma32(ka[0], qop[qb][0], cneg[qb]);
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) s[kb][qb] = mfma32(ka[ks], qop[qb][ks], s[kb][qb]);
+      }
+    }
+
+    // Element r of s[kb][qb] on this lane is key j0 + koff(kb, r) + 8 hf,
+    // koff = 32 kb + 16 (r>>3) + 4 ((r>>2)&1) + (r&3); query qw + 32 qb + ln.
+    const bool diag = (n == last_w);
+    if (ALIBI || diag) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int base = j0 + 8 * hf - (qw + 32 * qb + ln);  // key - query minus koff
+        const float fb = slope2 * (float)base;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int r = (kb == 0 ? 1 : 0); r < 16; r += 2) {
-            if (r + 1 < 16) t = fmaxf(t, fmaxf(s[kb][qb][r], s[kb][qb][r + 1]));
-            else t = fmaxf(t, s[kb][qb][r]);
+          for (int r = 0; r < 16; ++r) {
+            const int koff = 32 * kb + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
+            float x = s[kb][qb][r];
+            if (ALIBI) x += fmaf(slope2, (float)koff, fb);
+            if (diag && koff + base > 0) x = -INFINITY;
+            s[kb][qb][r] = x;
           }
-        t = fmaxf(t, __shfl_xor(t, 32));
-        mx[qb] = t;
-        need |= (t > TAU);
-      }
-      if (__any(need)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float delta = (n == 0) ? mx[qb] : fmaxf(mx[qb], 0.f);
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][qb][r] -= delta;
-          if (n != 0) {
-            const float alpha = __builtin_amdgcn_exp2f(-delta);
-            lsum[qb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha;
-          }
-          mrun[qb] += delta;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) cneg[qb][r] = -mrun[qb];
-        }
-      }
-
-      // P = 2^(s - m) in bf16, row sums, then O^T += V~^T P^T.
-      bf16x8 pop[KS2][QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int ks2 = 0; ks2 < KS2; ++ks2) {
-          const int kb = ks2 >> 1, r0 = 8 * (ks2 & 1);
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(s[kb][qb][r0 + 2 * e]);
-            const float p1 = __builtin_amdgcn_exp2f(s[kb][qb][r0 + 2 * e + 1]);
-            w[e] = pack_bf16x2(p0, p1);
-            lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]),
-                                                       __builtin_bit_cast(bf16x2, 0x3F803F80u),
-                                                       lsum[qb], false);
-          }
-          u32x4 wv = {w[0], w[1], w[2], w[3]};
-          pop[ks2][qb] = __builtin_bit_cast(bf16x8, wv);
-        }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int row = 32 * db + ln;
-#pragma unroll
-        for (int ks2 = 0; ks2 < KS2; ++ks2) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-              vtile + row * VROW + (((2 * ks2 + hf) ^ (ln & 7)) << 4));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma32(va, pop[ks2][qb], oacc[db][qb]);
-        }
       }
     }
-    if (n < last_tile) stage_store(cur ^ 1);
-    __syncthreads();
+
+    // Row maxima of the shifted logits (both half-waves).
+    float mx[QB];
+    bool need = (n == 0);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      // a chain of three-input maxima (v_max3_f32), two new values per step
+      float t = s[0][qb][0];
+#pragma unroll
+      for (int e = 1; e + 1 < 16 * KB; e += 2)
+        t = fmaxf(fmaxf(t, s[e / 16][qb][e % 16]), s[(e + 1) / 16][qb][(e + 1) % 16]);
+      t = fmaxf(t, s[KB - 1][qb][15]);
+      t = halves_max(t);
+      mx[qb] = t;
+      need |= (t > TAU);
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float delta = (n == 0) ? mx[qb] : fmaxf(mx[qb], 0.f);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][qb][r] -= delta;
+        if (n != 0) {
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+          lsum[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha;
+        }
+        mrun[qb] += delta;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cneg[qb][r] = -mrun[qb];
+      }
+    }
+
+    // P = 2^(s - m) in bf16, row sums, then O^T += V~^T P^T.
+    bf16x8 pop[KS2][QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int ks2 = 0; ks2 < KS2; ++ks2) {
+        const int kb = ks2 >> 1, r0 = 8 * (ks2 & 1);
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(s[kb][qb][r0 + 2 * e]);
+          const float p1 = __builtin_amdgcn_exp2f(s[kb][qb][r0 + 2 * e + 1]);
+          w[e] = pack_bf16x2(p0, p1);
+          lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]),
+                                                     __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                                     lsum[qb], false);
+        }
+        u32x4 wv = {w[0], w[1], w[2], w[3]};
+        pop[ks2][qb] = __builtin_bit_cast(bf16x8, wv);
+      }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int row = 32 * db + ln;
+#pragma unroll
+      for (int ks2 = 0; ks2 < KS2; ++ks2) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(
+            vtile + row * VROW + (((2 * ks2 + hf) ^ (ln & 7)) << 4));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma32(va, pop[ks2][qb], oacc[db][qb]);
+      }
+    }
+  };
+
+  // ---- key loop: NST-stage ring; tile n+NST-1 is loaded while n is computed ----
+  constexpr int LOADS = KLD + VLD;  // direct loads per wave per tile
+  for (int n = 0; n <= last_tile; ++n) {
+    const int cur = n % NST;
+    // tile n has landed once at most the loads of the tiles after it are pending
+    if (n + NST - 2 <= last_tile) wait_loads<(NST - 2) * LOADS>();
+    else wait_loads<0>();
+    // Every wave's share of tile n is in place and every wave is done with
+    // tile n-1 (whose stage the next issue overwrites).  A bare s_barrier:
+    // the wait above already covers this wave's loads, and a fenced barrier
+    // would also wait for the loads of the tiles still in flight.
+    __builtin_amdgcn_s_barrier();
+    if (n + NST - 1 <= last_tile) issue(n + NST - 1, smem + ((n + NST - 1) % NST) * STAGE);
+    if (n <= last_w) compute(n, smem + cur * STAGE);
   }
 
   // ---- epilogue: normalise, value-transport un-rotation, store bf16 ----
@@ -286,7 +309,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int i = qw + 32 * qb + ln;
-    const float ltot = lsum[qb] + __shfl_xor(lsum[qb], 32);
+    const float ltot = halves_sum(lsum[qb]);
     if (i >= L) continue;
     const float inv = 1.f / ltot;
     const float* th = theta + ((size_t)(b * Hphi + g) * L + i) * (D / 2);
@@ -313,7 +336,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
   }
 }
 
-template <int D, int QPW, int NW>
+template <int D, int QPW, int NW, int NST>
 hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                            const uint16_t* vt, const float* theta, const float* alibi, uint16_t* o,
                            hipStream_t stream) {
@@ -323,7 +346,7 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
   const int grid = ((total + 7) / 8) * 8;
   const bool al = g.flags & ARP_ALIBI, rv = g.flags & ARP_ROTATE_V;
 #define ARP_BF16_LAUNCH(A, R)                                                                 \
-  hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, A, R>), dim3(grid), dim3(NW * 64), 0,     \
+  hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, A, R>), dim3(grid), dim3(NW * 64), 0,     \
                      stream, qr, kr, vt, theta, alibi, o, g.L, g.Lp, g.H, g.Hphi, nqt, total)
   if (al) {
     if (rv) ARP_BF16_LAUNCH(true, true); else ARP_BF16_LAUNCH(true, false);
@@ -339,8 +362,8 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
 hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                                     const uint16_t* vt, const float* theta, const float* alibi,
                                     uint16_t* o, hipStream_t stream) {
-  if (g.D == 64) return launch_bf16_cfg<64, 64, 4>(g, qr, kr, vt, theta, alibi, o, stream);
-  return launch_bf16_cfg<128, 32, 4>(g, qr, kr, vt, theta, alibi, o, stream);
+  if (g.D == 64) return launch_bf16_cfg<64, 64, 4, 3>(g, qr, kr, vt, theta, alibi, o, stream);
+  return launch_bf16_cfg<128, 32, 4, 2>(g, qr, kr, vt, theta, alibi, o, stream);
 }
 
 hipError_t launch_attn_bf16_fused(const Geometry&, const uint16_t*, const uint16_t*,
