@@ -78,6 +78,8 @@ WorkspaceLayout workspace_layout(const Geometry& g) {
     lay.k_off = off + lay.operand_bytes;
     lay.vt_off = off + 2 * lay.operand_bytes;
     off += 3 * lay.operand_bytes;
+    lay.kmax_off = off;
+    off += align_up((size_t)g.B * g.H * (g.Lp / KEY_TILE) * sizeof(float));
   }
   lay.total = off;
   return lay;
@@ -148,6 +150,7 @@ arp_status arp_rotate_qkv(const arp_desc* desc, const void* q, const void* k, co
   return hip_status(launch_rotate_qkv(g, q, k, v, theta, reinterpret_cast<uint16_t*>(ws + lay.q_off),
                                       reinterpret_cast<uint16_t*>(ws + lay.k_off),
                                       reinterpret_cast<uint16_t*>(ws + lay.vt_off),
+                                      reinterpret_cast<float*>(ws + lay.kmax_off),
                                       (hipStream_t)stream));
 }
 
@@ -168,7 +171,8 @@ arp_status arp_attn_rotated(const arp_desc* desc, const float* theta, const floa
   return hip_status(launch_attn_bf16_rotated(
       g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
       reinterpret_cast<const uint16_t*>(ws + lay.k_off),
-      reinterpret_cast<const uint16_t*>(ws + lay.vt_off), theta, alibi,
+      reinterpret_cast<const uint16_t*>(ws + lay.vt_off),
+      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi,
       static_cast<uint16_t*>(o), (hipStream_t)stream));
 }
 

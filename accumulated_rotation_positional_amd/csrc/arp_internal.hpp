@@ -23,7 +23,8 @@ struct Geometry {
 // ---- buffers ----------------------------------------------------------------
 // scan state: a 256-byte header and two interleaved halves of 64-bit
 //   look-back status words, [B*Hphi][nchunks][P] per half (angle_scan.hip).
-// workspace:  [ q~ (bf16, [B*H, Lp, D]) | k~ (bf16, [B*H, Lp, D]) | v~^T (bf16, [B*H, D, Lp]) ]
+// workspace:  [ q~ (bf16, [B*H, Lp, D]) | k~ (bf16, [B*H, Lp, D]) | v~^T (bf16, [B*H, D, Lp])
+//               | kmax (fp32, [B*H, Lp/64]) ]
 //   for bf16 without ARP_FUSED_ROTATION; empty otherwise.
 struct ScanPlan {
   int rows_per_thread;  // tokens each thread scans serially (T)
@@ -34,8 +35,10 @@ ScanPlan scan_plan(const Geometry& g);
 size_t scan_state_bytes(const Geometry& g);  // upper bound over every plan
 struct WorkspaceLayout {
   size_t q_off, k_off, vt_off, operand_bytes;  // each operand block
+  size_t kmax_off;                             // float [B*H][Lp/64]: max |k~| per key tile
   size_t total;
 };
+constexpr int KEY_TILE = 64;  // keys per tile of the attention kernel (and per kmax entry)
 WorkspaceLayout workspace_layout(const Geometry& g);
 
 // ---- launchers (enqueue only; return hipSuccess or the launch error) -------
@@ -43,10 +46,10 @@ hipError_t launch_angle_scan(const Geometry& g, const float* phi, float* theta, 
                              hipStream_t stream);
 hipError_t launch_rotate_qkv(const Geometry& g, const void* q, const void* k, const void* v,
                              const float* theta, uint16_t* qr, uint16_t* kr, uint16_t* vt,
-                             hipStream_t stream);
+                             float* kmax, hipStream_t stream);
 hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
-                                    const uint16_t* vt, const float* theta, const float* alibi,
-                                    uint16_t* o, hipStream_t stream);
+                                    const uint16_t* vt, const float* kmax, const float* theta,
+                                    const float* alibi, uint16_t* o, hipStream_t stream);
 hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const float* theta, const float* alibi,
                                   uint16_t* o, hipStream_t stream);

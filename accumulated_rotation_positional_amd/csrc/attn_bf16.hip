@@ -43,7 +43,7 @@ namespace arp {
 
 namespace {
 
-constexpr int BN = 64;        // keys per tile
+constexpr int BN = KEY_TILE;  // keys per tile
 constexpr float TAU = 8.0f;   // lazy-rescale threshold (base-2 logits)
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -52,6 +52,17 @@ typedef const __attribute__((address_space(1))) void* global_void_ptr;
 // Row order of K~ in LDS: bits 2 and 3 of the key index swapped (an involution).
 __device__ __forceinline__ int swap_bits23(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// LDS swizzle: the 16-byte chunk c of a row of ROWB bytes is stored at chunk
+// c ^ swz(row).  A 128-bit LDS read serves 16 lanes per cycle from 64 banks,
+// i.e. 256 bytes; the operand reads of 16 consecutive rows must therefore hit
+// 16 distinct 16-byte bank groups, which this choice guarantees for 128- and
+// 256-byte rows.
+template <int ROWB>
+__device__ __forceinline__ int swz(int row) {
+  static_assert(ROWB == 128 || ROWB == 256, "row size");
+  return ROWB == 128 ? ((row >> 1) & 7) : (row & 15);
 }
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -77,12 +88,12 @@ __device__ __forceinline__ void wait_loads() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-template <int D, int QPW, int NW, int NST, bool ALIBI, bool ROTV>
-__global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
+template <int D, int QPW, int NW, int NST, int MINB, bool ALIBI, bool ROTV>
+__global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
-    const uint16_t* __restrict__ vt, const float* __restrict__ theta,
-    const float* __restrict__ alibi, uint16_t* __restrict__ o, int L, int Lp, int H, int Hphi,
-    int nqt, int total_tiles) {
+    const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
+    const float* __restrict__ theta, const float* __restrict__ alibi, uint16_t* __restrict__ o,
+    int L, int Lp, int H, int Hphi, int nqt, int total_tiles) {
   constexpr int BM = QPW * NW;
   constexpr int QB = QPW / 32;         // 32-query blocks per wave
   constexpr int KS = D / 16;           // k-steps of S^T (16 of D each)
@@ -128,7 +139,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
       const int p0 = (wave * KLD + i) * 1024;
       const int p = p0 + 16 * lane;
       const int row = p / KROW, cs = (p % KROW) / 16;
-      const int c = cs ^ (row & 7);
+      const int c = cs ^ swz<KROW>(row);
       const uint16_t* src = kbase + (size_t)(j0 + swap_bits23(row)) * D + 8 * c;
       __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + p0), 16, 0, 0);
     }
@@ -137,7 +148,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
       const int p0 = (wave * VLD + i) * 1024;
       const int p = p0 + 16 * lane;
       const int row = p / VROW, cs = (p % VROW) / 16;
-      const int c = cs ^ (row & 7);
+      const int c = cs ^ swz<VROW>(row);
       const uint16_t* src = vbase + (size_t)row * Lp + j0 + 8 * c;
       __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + KTILE + p0), 16,
                                        0, 0);
@@ -150,7 +161,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qop[qb][ks] = *reinterpret_cast<const bf16x8*>(
-          qr + ((size_t)bh * Lp + qw + 32 * qb + ln) * D + 16 * ks + 8 * hf);
+          qr + ((size_t)bh * Lp + min(qw + 32 * qb + ln, Lp - 1)) * D + 16 * ks + 8 * hf);
+
+  // |q~_i| of this lane's queries (both half-waves hold half of each row).
+  float qn[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float n2 = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) n2 = fmaf((float)qop[qb][ks][e], (float)qop[qb][ks][e], n2);
+    qn[qb] = sqrtf(halves_sum(n2)) * (1.f + 1e-4f);  // margin for the fp32 accumulation
+  }
+  const float* kmax_bh = kmax + (size_t)bh * (Lp / BN);
 
   // First NST-1 tiles in flight before the loop.
 #pragma unroll
@@ -188,7 +212,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
       bf16x8 ka[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        ka[ks] = *reinterpret_cast<const bf16x8*>(kt + row * KROW + (((2 * ks + hf) ^ (ln & 7)) << 4));
+        ka[ks] = *reinterpret_cast<const bf16x8*>(kt + row * KROW + (((2 * ks + hf) ^ swz<KROW>(row)) << 4));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         s[kb][qb] = mfma32(ka[0], qop[qb][0], cneg[qb]);
@@ -218,7 +242,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
       }
     }
 
-    // Row maxima of the shifted logits (both half-waves).
+    // Row maxima of the shifted logits (both half-waves) -- only when the
+    // tile might need them: s_ij <= |q~_i| max_j |k~_j| (Cauchy-Schwarz; the
+    // distance bias and the mask only lower scores), so while that bound
+    // stays within TAU of the running maximum no rescale can be due.
+    bool check = (n == 0);
+    const float km = kmax_bh[n];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) check |= (qn[qb] * km > mrun[qb] + TAU);
+    if (__any(check)) {
     float mx[QB];
     bool need = (n == 0);
 #pragma unroll
@@ -254,6 +286,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
         for (int r = 0; r < 16; ++r) cneg[qb][r] = -mrun[qb];
       }
     }
+    }
 
     // P = 2^(s - m) in bf16, row sums, then O^T += V~^T P^T.
     bf16x8 pop[KS2][QB];
@@ -281,7 +314,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
 #pragma unroll
       for (int ks2 = 0; ks2 < KS2; ++ks2) {
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-            vtile + row * VROW + (((2 * ks2 + hf) ^ (ln & 7)) << 4));
+            vtile + row * VROW + (((2 * ks2 + hf) ^ swz<VROW>(row)) << 4));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma32(va, pop[ks2][qb], oacc[db][qb]);
       }
@@ -336,18 +369,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(
   }
 }
 
-template <int D, int QPW, int NW, int NST>
+template <int D, int QPW, int NW, int NST, int MINB>
 hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
-                           const uint16_t* vt, const float* theta, const float* alibi, uint16_t* o,
-                           hipStream_t stream) {
+                           const uint16_t* vt, const float* kmax, const float* theta,
+                           const float* alibi, uint16_t* o, hipStream_t stream) {
   constexpr int BM = QPW * NW;
   const int nqt = (g.L + BM - 1) / BM;
   const int total = g.B * g.H * nqt;
   const int grid = ((total + 7) / 8) * 8;
   const bool al = g.flags & ARP_ALIBI, rv = g.flags & ARP_ROTATE_V;
 #define ARP_BF16_LAUNCH(A, R)                                                                 \
-  hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, A, R>), dim3(grid), dim3(NW * 64), 0,     \
-                     stream, qr, kr, vt, theta, alibi, o, g.L, g.Lp, g.H, g.Hphi, nqt, total)
+  hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, MINB, A, R>), dim3(grid), dim3(NW * 64), 0,     \
+                     stream, qr, kr, vt, kmax, theta, alibi, o, g.L, g.Lp, g.H, g.Hphi, nqt, total)
   if (al) {
     if (rv) ARP_BF16_LAUNCH(true, true); else ARP_BF16_LAUNCH(true, false);
   } else {
@@ -360,10 +393,11 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
 }  // namespace
 
 hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
-                                    const uint16_t* vt, const float* theta, const float* alibi,
-                                    uint16_t* o, hipStream_t stream) {
-  if (g.D == 64) return launch_bf16_cfg<64, 64, 4, 3>(g, qr, kr, vt, theta, alibi, o, stream);
-  return launch_bf16_cfg<128, 32, 4, 2>(g, qr, kr, vt, theta, alibi, o, stream);
+                                    const uint16_t* vt, const float* kmax, const float* theta,
+                                    const float* alibi, uint16_t* o, hipStream_t stream) {
+  if (g.D == 64)
+    return launch_bf16_cfg<64, 64, 8, 2, 1>(g, qr, kr, vt, kmax, theta, alibi, o, stream);
+  return launch_bf16_cfg<128, 32, 4, 2, 2>(g, qr, kr, vt, kmax, theta, alibi, o, stream);
 }
 
 hipError_t launch_attn_bf16_fused(const Geometry&, const uint16_t*, const uint16_t*,

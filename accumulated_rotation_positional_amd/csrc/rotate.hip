@@ -17,7 +17,9 @@
 //  * q~ and k~ are written row-major [Lp, D]; v~ is transposed through LDS and
 //    written [D, Lp], the layout the P V product reads (keys contiguous);
 //  * tokens in [L, Lp) are written as zeros (the attention kernel reads whole
-//    tiles without bounds checks).
+//    tiles without bounds checks);
+//  * the largest |k~| of the 64 keys (one attention key tile) is recorded, from
+//    the stored bf16 values: the attention kernel bounds its logits with it.
 #include "arp_device.hpp"
 #include "arp_internal.hpp"
 
@@ -31,12 +33,15 @@ template <int D>
 __global__ __launch_bounds__(256) void rotate_qkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ theta, uint16_t* __restrict__ qr, uint16_t* __restrict__ kr,
-    uint16_t* __restrict__ vt, int L, int Lp, int H, int Hphi, uint32_t flags, float qscale) {
+    uint16_t* __restrict__ vt, float* __restrict__ kmax, int L, int Lp, int H, int Hphi,
+    uint32_t flags, float qscale) {
   constexpr int P = D / 2;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int ITER = ROT_TOKENS * CPR / 256;
   constexpr int VT_STRIDE = ROT_TOKENS + 8;  // padded LDS row (elements)
   __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VT_STRIDE];
+  __shared__ uint32_t s_kmax2;  // max |k~|^2 of the tile, as the bits of a non-negative float
+  static_assert(ROT_TOKENS == KEY_TILE, "one workgroup per attention key tile");
 
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh % H;
@@ -45,6 +50,8 @@ __global__ __launch_bounds__(256) void rotate_qkv_kernel(
   const int tid = threadIdx.x;
   const bool rot_qk = (flags & ARP_ROTATE_QK) != 0;
   const bool rot_v = (flags & ARP_ROTATE_V) != 0;
+  if (tid == 0) s_kmax2 = 0u;
+  __syncthreads();
 
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
@@ -81,6 +88,17 @@ __global__ __launch_bounds__(256) void rotate_qkv_kernel(
     const size_t roff = ((size_t)bh * Lp + tok) * D + c * 8;
     *reinterpret_cast<u32x4*>(qr + roff) = qa;
     *reinterpret_cast<u32x4*>(kr + roff) = ka;
+    // |k~|^2 of this row from the stored bf16 values (the CPR threads of a
+    // row are consecutive lanes), then the tile maximum.
+    float n2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float k0 = lo_bf16(ka[e]), k1 = hi_bf16(ka[e]);
+      n2 = fmaf(k0, k0, fmaf(k1, k1, n2));
+    }
+#pragma unroll
+    for (int m = 1; m < CPR; m <<= 1) n2 += __shfl_xor(n2, m);
+    if (c == 0) atomicMax(&s_kmax2, __float_as_uint(n2));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       s_vt[(c * 8 + 2 * e) * VT_STRIDE + r] = (uint16_t)(va[e] & 0xFFFFu);
@@ -88,6 +106,7 @@ __global__ __launch_bounds__(256) void rotate_qkv_kernel(
     }
   }
   __syncthreads();
+  if (tid == 0) kmax[(size_t)bh * (Lp / ROT_TOKENS) + blockIdx.x] = sqrtf(__uint_as_float(s_kmax2));
   // v~^T rows: D rows x 64 tokens = 8 chunks of 16 bytes per row.
 #pragma unroll
   for (int it = 0; it < D * 8 / 256; ++it) {
@@ -132,7 +151,7 @@ __global__ __launch_bounds__(256) void rotate_diag_kernel(const TIn* __restrict_
 
 hipError_t launch_rotate_qkv(const Geometry& g, const void* q, const void* k, const void* v,
                              const float* theta, uint16_t* qr, uint16_t* kr, uint16_t* vt,
-                             hipStream_t stream) {
+                             float* kmax, hipStream_t stream) {
   dim3 grid(g.Lp / ROT_TOKENS, g.B * g.H);
   const float qscale = g.scale * LOG2E;
   const auto* qb = static_cast<const uint16_t*>(q);
@@ -140,10 +159,10 @@ hipError_t launch_rotate_qkv(const Geometry& g, const void* q, const void* k, co
   const auto* vb = static_cast<const uint16_t*>(v);
   if (g.D == 64)
     hipLaunchKernelGGL((rotate_qkv_kernel<64>), grid, dim3(256), 0, stream, qb, kb, vb, theta, qr,
-                       kr, vt, g.L, g.Lp, g.H, g.Hphi, g.flags, qscale);
+                       kr, vt, kmax, g.L, g.Lp, g.H, g.Hphi, g.flags, qscale);
   else
     hipLaunchKernelGGL((rotate_qkv_kernel<128>), grid, dim3(256), 0, stream, qb, kb, vb, theta,
-                       qr, kr, vt, g.L, g.Lp, g.H, g.Hphi, g.flags, qscale);
+                       qr, kr, vt, kmax, g.L, g.Lp, g.H, g.Hphi, g.flags, qscale);
   return hipGetLastError();
 }
 
