@@ -44,8 +44,8 @@ COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_extrap_16k_hbm_counters.json
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="extrap_16k")
     p.add_argument("--fused", action="store_true", help="rotate k/v inside the attention kernel")
     p.add_argument("--no-cpu-baseline", action="store_true")
