@@ -57,12 +57,12 @@ __device__ __forceinline__ int swap_bits23(int x) {
 // LDS swizzle: the 16-byte chunk c of a row of ROWB bytes is stored at chunk
 // c ^ swz(row).  A 128-bit LDS read serves 16 lanes per cycle from 64 banks,
 // i.e. 256 bytes; the operand reads of 16 consecutive rows must therefore hit
-// 16 distinct 16-byte bank groups, which this choice guarantees for 128- and
-// 256-byte rows.
+// 16 distinct 16-byte bank groups, which this choice guarantees for 64-, 128-
+// and 256-byte rows.
 template <int ROWB>
 __device__ __forceinline__ int swz(int row) {
-  static_assert(ROWB == 128 || ROWB == 256, "row size");
-  return ROWB == 128 ? ((row >> 1) & 7) : (row & 15);
+  static_assert(ROWB == 64 || ROWB == 128 || ROWB == 256, "row size");
+  return ROWB == 64 ? ((row >> 2) & 3) : ROWB == 128 ? ((row >> 1) & 7) : (row & 15);
 }
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -199,13 +199,13 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
   }
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
 
-  // ---- one key tile of this wave's queries ----
-  auto compute = [&](int n, const uint8_t* kt) __attribute__((always_inline)) {
-    const uint8_t* vtile = kt + KTILE;
-    const int j0 = n * BN;
+  // ---- the three parts of one key tile of this wave's queries ----
+  f32x16 s[KB][QB];      // logits of the tile in flight
+  bf16x8 pop[KS2][QB];   // its probabilities, P^T operand layout
 
+  auto qk = [&](int n) __attribute__((always_inline)) {
+    const uint8_t* kt = smem + (n % NST) * STAGE;
     // S^T - m = K~ Q~^T + cneg
-    f32x16 s[KB][QB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int row = 32 * kb + ln;
@@ -221,6 +221,10 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
       }
     }
 
+  };
+
+  auto soft = [&](int n) __attribute__((always_inline)) {
+    const int j0 = n * BN;
     // Element r of s[kb][qb] on this lane is key j0 + koff(kb, r) + 8 hf,
     // koff = 32 kb + 16 (r>>3) + 4 ((r>>2)&1) + (r&3); query qw + 32 qb + ln.
     const bool diag = (n == last_w);
@@ -289,7 +293,6 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     }
 
     // P = 2^(s - m) in bf16, row sums, then O^T += V~^T P^T.
-    bf16x8 pop[KS2][QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -308,6 +311,10 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
         u32x4 wv = {w[0], w[1], w[2], w[3]};
         pop[ks2][qb] = __builtin_bit_cast(bf16x8, wv);
       }
+  };
+
+  auto pv = [&](int n) __attribute__((always_inline)) {
+    const uint8_t* vtile = smem + (n % NST) * STAGE + KTILE;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int row = 32 * db + ln;
@@ -324,7 +331,6 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
   // ---- key loop: NST-stage ring; tile n+NST-1 is loaded while n is computed ----
   constexpr int LOADS = KLD + VLD;  // direct loads per wave per tile
   for (int n = 0; n <= last_tile; ++n) {
-    const int cur = n % NST;
     // tile n has landed once at most the loads of the tiles after it are pending
     if (n + NST - 2 <= last_tile) wait_loads<(NST - 2) * LOADS>();
     else wait_loads<0>();
@@ -334,7 +340,11 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     // would also wait for the loads of the tiles still in flight.
     __builtin_amdgcn_s_barrier();
     if (n + NST - 1 <= last_tile) issue(n + NST - 1, smem + ((n + NST - 1) % NST) * STAGE);
-    if (n <= last_w) compute(n, smem + cur * STAGE);
+    if (n <= last_w) {
+      qk(n);
+      soft(n);
+      pv(n);
+    }
   }
 
   // ---- epilogue: normalise, value-transport un-rotation, store bf16 ----

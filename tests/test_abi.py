@@ -81,7 +81,8 @@ def test_workspace_and_scan_state_bytes():
     d = _desc(batch=2, heads=8, seqlen=16384)
     ws = L.arp_workspace_bytes(ctypes.byref(d))
     operands = 3 * 2 * 8 * 16384 * 64 * 2
-    assert operands <= ws < operands + 4096 and ws % 256 == 0
+    kmax = 2 * 8 * (16384 // 64) * 4  # max |k~| per 64-key tile, fp32
+    assert operands + kmax <= ws < operands + kmax + 4096 and ws % 256 == 0
     st = L.arp_scan_state_bytes(ctypes.byref(d))
     assert 0 < st < (16 << 20) and st % 256 == 0
     fused = _desc(batch=2, heads=8, seqlen=16384, flags=b.ROTATE_QK | b.FUSED_ROTATION)
