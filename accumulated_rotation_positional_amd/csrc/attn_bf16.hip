@@ -88,12 +88,19 @@ __device__ __forceinline__ void wait_loads() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-template <int D, int QPW, int NW, int NST, int MINB, bool ALIBI, bool ROTV>
+// FUSED = false: q~, k~ (L padded to Lp) and v~^T come pre-rotated from the
+// rotation pass, K/V tiles load straight into LDS, and the per-tile key-norm
+// maxima kmax bound the logits.
+// FUSED = true: qr, kr, vt are the raw q, k, v ([B, H, L, D]); q is rotated
+// and scaled in the prologue, and each K/V tile is rotated while it is staged
+// through registers into LDS (sin/cos once per (key, pair), shared by k and
+// v); row maxima are always taken exactly.
+template <int D, int QPW, int NW, int NST, int MINB, bool FUSED, bool ALIBI, bool ROTV>
 __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
     const float* __restrict__ theta, const float* __restrict__ alibi, uint16_t* __restrict__ o,
-    int L, int Lp, int H, int Hphi, int nqt, int total_tiles) {
+    int L, int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk, float qscale) {
   constexpr int BM = QPW * NW;
   constexpr int QB = QPW / 32;         // 32-query blocks per wave
   constexpr int KS = D / 16;           // k-steps of S^T (16 of D each)
@@ -109,6 +116,11 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
   static_assert(KLD * 1024 * NW == KTILE && VLD * 1024 * NW == VTILE, "staging split");
   static_assert(QPW % 32 == 0 && BN == 64, "tile shape");
   static_assert(NST == 2 || NST == 3, "load-wait counts are written for 2 or 3 stages");
+  static_assert(!FUSED || NST == 2, "register staging uses two stages");
+  constexpr int P = D / 2;
+  constexpr int NT = NW * 64;
+  constexpr int IPT = P * (BN / 4) / NT;  // fused staging: (pair, 4-key group) items per thread
+  static_assert(!FUSED || IPT * NT == P * (BN / 4), "fused staging split");
 
   constexpr int STAGE = KTILE + VTILE;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
@@ -154,14 +166,92 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
                                        0, 0);
     }
   };
+  // ---- fused staging: raw k, v and angles of one tile -> registers -> rotated into LDS ----
+  // Item it = (pair p, keys 4kg..4kg+3); lanes run over p, so each load
+  // instruction reads whole rows of k, v and theta.
+  const int g = (Hphi == 1) ? 0 : h;
+  const float* th_bh = theta + (size_t)(b * Hphi + g) * L * P;
+  uint32_t kreg[IPT > 0 ? IPT : 1][4], vreg[IPT > 0 ? IPT : 1][4];
+  float treg[IPT > 0 ? IPT : 1][4];
+  auto fetch = [&](int tile) __attribute__((always_inline)) {
+    const uint16_t* kb = kr + (size_t)bh * L * D;
+    const uint16_t* vb = vt + (size_t)bh * L * D;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int it = tid + i * NT;
+      const int p = it % P, kg = it / P;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = min(tile * BN + 4 * kg + e, L - 1);  // rows past L are masked anyway
+        kreg[i][e] = *reinterpret_cast<const uint32_t*>(kb + (size_t)key * D + 2 * p);
+        vreg[i][e] = *reinterpret_cast<const uint32_t*>(vb + (size_t)key * D + 2 * p);
+        treg[i][e] = (rot_qk || ROTV) ? th_bh[(size_t)key * P + p] : 0.f;
+      }
+    }
+  };
+  auto commit = [&](uint8_t* stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int it = tid + i * NT;
+      const int p = it % P, kg = it / P;
+      float v0[4], v1[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float sn, cs;
+        __sincosf(treg[i][e], &sn, &cs);
+        float k0 = lo_bf16(kreg[i][e]), k1 = hi_bf16(kreg[i][e]);
+        v0[e] = lo_bf16(vreg[i][e]);
+        v1[e] = hi_bf16(vreg[i][e]);
+        if (rot_qk) rotate_pair(k0, k1, cs, sn);
+        if (ROTV) rotate_pair(v0[e], v1[e], cs, sn);
+        const int row = swap_bits23(4 * kg + e);  // LDS row holding this key
+        *reinterpret_cast<uint32_t*>(stage + row * KROW + (((p >> 2) ^ swz<KROW>(row)) << 4) +
+                                     4 * (p & 3)) = pack_bf16x2(k0, k1);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int d = 2 * p + j;
+        const float* vv = j ? v1 : v0;
+        u32x2 w = {pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
+        *reinterpret_cast<u32x2*>(stage + KTILE + d * VROW + (((kg >> 1) ^ swz<VROW>(d)) << 4) +
+                                  8 * (kg & 1)) = w;
+      }
+    }
+  };
+
   // ---- Q~ operand: lane (ln, hf) holds query qw+32qb+ln, d = 16ks+8hf..+7 ----
   bf16x8 qop[QB][KS];
+  if constexpr (!FUSED) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qop[qb][ks] = *reinterpret_cast<const bf16x8*>(
-          qr + ((size_t)bh * Lp + min(qw + 32 * qb + ln, Lp - 1)) * D + 16 * ks + 8 * hf);
+      for (int ks = 0; ks < KS; ++ks)
+        qop[qb][ks] = *reinterpret_cast<const bf16x8*>(
+            qr + ((size_t)bh * Lp + min(qw + 32 * qb + ln, Lp - 1)) * D + 16 * ks + 8 * hf);
+  } else {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int i = min(qw + 32 * qb + ln, L - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(qr + ((size_t)bh * L + i) * D + 16 * ks +
+                                                        8 * hf);
+        const float4 a = rot_qk ? *reinterpret_cast<const float4*>(th_bh + (size_t)i * P + 8 * ks + 4 * hf)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float ang[4] = {a.x, a.y, a.z, a.w};
+        u32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float sn, cs;
+          sincosf(ang[e], &sn, &cs);
+          float x0 = lo_bf16(w[e]), x1 = hi_bf16(w[e]);
+          if (rot_qk) rotate_pair(x0, x1, cs, sn);
+          r[e] = pack_bf16x2(x0 * qscale, x1 * qscale);
+        }
+        qop[qb][ks] = __builtin_bit_cast(bf16x8, r);
+      }
+    }
+  }
 
   // |q~_i| of this lane's queries (both half-waves hold half of each row).
   float qn[QB];
@@ -174,12 +264,19 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
       for (int e = 0; e < 8; ++e) n2 = fmaf((float)qop[qb][ks][e], (float)qop[qb][ks][e], n2);
     qn[qb] = sqrtf(halves_sum(n2)) * (1.f + 1e-4f);  // margin for the fp32 accumulation
   }
-  const float* kmax_bh = kmax + (size_t)bh * (Lp / BN);
+  const float* kmax_bh = FUSED ? nullptr : kmax + (size_t)bh * (Lp / BN);
 
-  // First NST-1 tiles in flight before the loop.
+  // First tiles in flight before the loop: NST-1 direct loads, or tile 0
+  // staged and rotated.
+  if constexpr (!FUSED) {
 #pragma unroll
-  for (int t = 0; t < NST - 1; ++t)
-    if (t <= last_tile) issue(t, smem + t * STAGE);
+    for (int t = 0; t < NST - 1; ++t)
+      if (t <= last_tile) issue(t, smem + t * STAGE);
+  } else {
+    fetch(0);
+    commit(smem);
+    __syncthreads();
+  }
 
   f32x16 oacc[DB][QB];
 #pragma unroll
@@ -250,10 +347,12 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     // tile might need them: s_ij <= |q~_i| max_j |k~_j| (Cauchy-Schwarz; the
     // distance bias and the mask only lower scores), so while that bound
     // stays within TAU of the running maximum no rescale can be due.
-    bool check = (n == 0);
-    const float km = kmax_bh[n];
+    bool check = FUSED || (n == 0);
+    if constexpr (!FUSED) {
+      const float km = kmax_bh[n];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) check |= (qn[qb] * km > mrun[qb] + TAU);
+      for (int qb = 0; qb < QB; ++qb) check |= (qn[qb] * km > mrun[qb] + TAU);
+    }
     if (__any(check)) {
     float mx[QB];
     bool need = (n == 0);
@@ -328,27 +427,41 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     }
   };
 
-  // ---- key loop: NST-stage ring; tile n+NST-1 is loaded while n is computed ----
-  constexpr int LOADS = KLD + VLD;  // direct loads per wave per tile
-  for (int n = 0; n <= last_tile; ++n) {
-    // tile n has landed once at most the loads of the tiles after it are pending
-    if (n + NST - 2 <= last_tile) wait_loads<(NST - 2) * LOADS>();
-    else wait_loads<0>();
-    // Every wave's share of tile n is in place and every wave is done with
-    // tile n-1 (whose stage the next issue overwrites).  A bare s_barrier:
-    // the wait above already covers this wave's loads, and a fenced barrier
-    // would also wait for the loads of the tiles still in flight.
-    __builtin_amdgcn_s_barrier();
-    if (n + NST - 1 <= last_tile) issue(n + NST - 1, smem + ((n + NST - 1) % NST) * STAGE);
-    if (n <= last_w) {
-      qk(n);
-      soft(n);
-      pv(n);
+  if constexpr (!FUSED) {
+    // ---- key loop: NST-stage ring; tile n+NST-1 is loaded while n is computed ----
+    constexpr int LOADS = KLD + VLD;  // direct loads per wave per tile
+    for (int n = 0; n <= last_tile; ++n) {
+      // tile n has landed once at most the loads of the tiles after it are pending
+      if (n + NST - 2 <= last_tile) wait_loads<(NST - 2) * LOADS>();
+      else wait_loads<0>();
+      // Every wave's share of tile n is in place and every wave is done with
+      // tile n-1 (whose stage the next issue overwrites).  A bare s_barrier:
+      // the wait above already covers this wave's loads, and a fenced barrier
+      // would also wait for the loads of the tiles still in flight.
+      __builtin_amdgcn_s_barrier();
+      if (n + NST - 1 <= last_tile) issue(n + NST - 1, smem + ((n + NST - 1) % NST) * STAGE);
+      if (n <= last_w) {
+        qk(n);
+        soft(n);
+        pv(n);
+      }
+    }
+  } else {
+    // ---- key loop, fused rotation: tile n+1 is fetched into registers while
+    // n is computed, then rotated into the other stage ----
+    for (int n = 0; n <= last_tile; ++n) {
+      if (n + 1 <= last_tile) fetch(n + 1);
+      if (n <= last_w) {
+        qk(n);
+        soft(n);
+        pv(n);
+      }
+      if (n + 1 <= last_tile) commit(smem + ((n + 1) & 1) * STAGE);
+      __syncthreads();  // tile n+1 is in place; every wave is done with tile n
     }
   }
 
   // ---- epilogue: normalise, value-transport un-rotation, store bf16 ----
-  const int g = (Hphi == 1) ? 0 : h;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int i = qw + 32 * qb + ln;
@@ -379,7 +492,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
   }
 }
 
-template <int D, int QPW, int NW, int NST, int MINB>
+template <int D, int QPW, int NW, int NST, int MINB, bool FUSED>
 hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                            const uint16_t* vt, const float* kmax, const float* theta,
                            const float* alibi, uint16_t* o, hipStream_t stream) {
@@ -388,9 +501,12 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
   const int total = g.B * g.H * nqt;
   const int grid = ((total + 7) / 8) * 8;
   const bool al = g.flags & ARP_ALIBI, rv = g.flags & ARP_ROTATE_V;
-#define ARP_BF16_LAUNCH(A, R)                                                                 \
-  hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, MINB, A, R>), dim3(grid), dim3(NW * 64), 0,     \
-                     stream, qr, kr, vt, kmax, theta, alibi, o, g.L, g.Lp, g.H, g.Hphi, nqt, total)
+  const int rqk = (g.flags & ARP_ROTATE_QK) ? 1 : 0;
+  const float qscale = g.scale * LOG2E;
+#define ARP_BF16_LAUNCH(A, R)                                                                  \
+  hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, MINB, FUSED, A, R>), dim3(grid),      \
+                     dim3(NW * 64), 0, stream, qr, kr, vt, kmax, theta, alibi, o, g.L, g.Lp, g.H, \
+                     g.Hphi, nqt, total, rqk, qscale)
   if (al) {
     if (rv) ARP_BF16_LAUNCH(true, true); else ARP_BF16_LAUNCH(true, false);
   } else {
@@ -406,14 +522,16 @@ hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const
                                     const uint16_t* vt, const float* kmax, const float* theta,
                                     const float* alibi, uint16_t* o, hipStream_t stream) {
   if (g.D == 64)
-    return launch_bf16_cfg<64, 64, 8, 2, 1>(g, qr, kr, vt, kmax, theta, alibi, o, stream);
-  return launch_bf16_cfg<128, 32, 4, 2, 2>(g, qr, kr, vt, kmax, theta, alibi, o, stream);
+    return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, o, stream);
+  return launch_bf16_cfg<128, 32, 4, 2, 2, false>(g, qr, kr, vt, kmax, theta, alibi, o, stream);
 }
 
-hipError_t launch_attn_bf16_fused(const Geometry&, const uint16_t*, const uint16_t*,
-                                  const uint16_t*, const float*, const float*, uint16_t*,
-                                  hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const float* theta, const float* alibi,
+                                  uint16_t* o, hipStream_t stream) {
+  if (g.D == 64)
+    return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, o, stream);
+  return launch_bf16_cfg<128, 32, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, o, stream);
 }
 
 }  // namespace arp

@@ -116,3 +116,38 @@ def test_rope_workload_matches_closed_form_rope():
     # oracle with position angles t*theta_p fed as an exclusive scan of constant steps
     want = oracle_problem(w, exclusive=True).output()
     assert_close(got, want, "bf16", "rope vs closed form")
+
+
+# ---- rotation fused into the attention kernel's staging (ARP_FUSED_ROTATION) ----
+
+@pytest.mark.parametrize("flags", FLAG_SETS, ids=[_ids(f) for f in FLAG_SETS])
+@pytest.mark.parametrize("name,L", [("train_1k", 333), ("rope_8k_d128", 200), ("train_1k", 64)])
+def test_fused_rotation_all_flags(name, L, flags):
+    w = wl.make(name, batch=2, heads=3, seqlen=L)
+    got, theta = run_forward(w, fused=True, **flags)
+    want = oracle_problem(w, **flags).output()
+    assert_close(got, want, "bf16", f"fused {name} L={L} {flags}")
+
+
+@pytest.mark.parametrize("L", [1, 31, 65, 257, 700])
+@pytest.mark.parametrize("name", ["train_1k", "rope_8k_d128"])
+def test_fused_rotation_ragged(name, L):
+    w = wl.make(name, batch=1, heads=2, seqlen=L)
+    got, _ = run_forward(w, rotate_v=True, alibi=True, fused=True)
+    want = oracle_problem(w, rotate_v=True, alibi=True).output()
+    assert_close(got, want, "bf16", f"fused {name} L={L}")
+
+
+@pytest.mark.parametrize("name", ["extrap_16k", "farmass_32k", "rope_8k_d128"])
+def test_fused_rotation_full_size_sampled_rows(name):
+    """The fused variant at full size, compared with the oracle on sampled rows
+    and with the pre-rotation path on every output."""
+    w = wl.make(name)
+    got, _ = run_forward(w, fused=True)
+    rows = sample_rows(w, per_head=12)
+    want = oracle_problem(w).rows(rows)
+    assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", f"fused {name} sampled rows")
+    ref, _ = run_forward(w)
+    d = float(np.abs(got - ref).max())
+    say(f"[gpu] fused vs pre-rotated {name}: max |diff| = {d:.3e}")
+    assert d <= 2e-2
