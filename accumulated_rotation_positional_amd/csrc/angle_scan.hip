@@ -210,8 +210,8 @@ __device__ uint64_t look_back(const uint64_t* __restrict__ wh, size_t wbase, uin
   return acc;
 }
 
-template <int P, int T>
-__global__ __launch_bounds__(SCAN_THREADS) void angle_scan_kernel(
+template <int P, int T, int MINB>
+__global__ __launch_bounds__(SCAN_THREADS, MINB) void angle_scan_kernel(
     const float* __restrict__ phi, float* __restrict__ theta, ScanHeader* __restrict__ hdr,
     uint64_t* __restrict__ words, int L, int nchunks, int exclusive) {
   constexpr int CPT = P / 4;              // threads per token row (4 pairs each)
@@ -329,8 +329,10 @@ __global__ __launch_bounds__(SCAN_THREADS) void angle_scan_kernel(
     }
     const int tok = tbase + t;
     if (tok < L)
-      *reinterpret_cast<float4*>(seg_theta + (size_t)tok * P + cq * 4) =
-          make_float4(out[0], out[1], out[2], out[3]);
+      // Streaming store: theta is not read again by this kernel, and keeping
+      // it out of the caches measured 5-15% faster than a plain store.
+      __builtin_nontemporal_store(f32x4{out[0], out[1], out[2], out[3]},
+                                  reinterpret_cast<f32x4*>(seg_theta + (size_t)tok * P + cq * 4));
   }
 
   // ---- state upkeep: clear this block's share of the other half ----
@@ -376,15 +378,22 @@ constexpr int rows_per_group(int P) { return SCAN_THREADS / (P / 4); }
 ScanPlan scan_plan(const Geometry& g) {
   // Rows per thread: 16 (64 KB of phi per workgroup) amortises the look-back
   // latency best once the grid has a workgroup per SIMD; smaller problems
-  // take smaller chunks so that the grid still covers the chip.
+  // take smaller chunks so that the grid still covers the chip.  A grid of at
+  // most 1024 workgroups of 16 rows is built for four workgroups per CU, so
+  // that all of it is resident at once.
   const long nseg = (long)g.B * g.Hphi;
   const int rg = rows_per_group(g.P);
   auto blocks = [&](int T) { return nseg * ((g.L + (long)rg * T - 1) / ((long)rg * T)); };
-  int T = 4;
-  if (blocks(16) >= 1024) T = 16;
-  else if (blocks(8) >= 512) T = 8;
+  int T = 4, minb = 1;
+  if (blocks(16) >= 512) {
+    T = 16;
+    minb = blocks(16) <= 1024 ? 4 : 1;
+  } else if (blocks(8) >= 512) {
+    T = 8;
+  }
   ScanPlan sp;
   sp.rows_per_thread = T;
+  sp.min_blocks = minb;
   sp.chunk = rg * T;
   sp.nchunks = (g.L + sp.chunk - 1) / sp.chunk;
   return sp;
@@ -412,17 +421,19 @@ hipError_t launch_angle_scan(const Geometry& g, const float* phi, float* theta, 
   if (nblocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)nblocks);
   dim3 block(SCAN_THREADS);
-#define ARP_SCAN_LAUNCH(PP, TT)                                                                   \
-  hipLaunchKernelGGL((angle_scan_kernel<PP, TT>), grid, block, 0, stream, phi, theta, hdr, words, \
-                     g.L, sp.nchunks, excl)
+#define ARP_SCAN_LAUNCH(PP, TT, MB)                                                             \
+  hipLaunchKernelGGL((angle_scan_kernel<PP, TT, MB>), grid, block, 0, stream, phi, theta, hdr,    \
+                     words, g.L, sp.nchunks, excl)
   if (g.P == 32) {
-    if (sp.rows_per_thread == 16) ARP_SCAN_LAUNCH(32, 16);
-    else if (sp.rows_per_thread == 8) ARP_SCAN_LAUNCH(32, 8);
-    else ARP_SCAN_LAUNCH(32, 4);
+    if (sp.rows_per_thread == 16) {
+      if (sp.min_blocks == 4) ARP_SCAN_LAUNCH(32, 16, 4); else ARP_SCAN_LAUNCH(32, 16, 1);
+    } else if (sp.rows_per_thread == 8) ARP_SCAN_LAUNCH(32, 8, 1);
+    else ARP_SCAN_LAUNCH(32, 4, 1);
   } else {
-    if (sp.rows_per_thread == 16) ARP_SCAN_LAUNCH(64, 16);
-    else if (sp.rows_per_thread == 8) ARP_SCAN_LAUNCH(64, 8);
-    else ARP_SCAN_LAUNCH(64, 4);
+    if (sp.rows_per_thread == 16) {
+      if (sp.min_blocks == 4) ARP_SCAN_LAUNCH(64, 16, 4); else ARP_SCAN_LAUNCH(64, 16, 1);
+    } else if (sp.rows_per_thread == 8) ARP_SCAN_LAUNCH(64, 8, 1);
+    else ARP_SCAN_LAUNCH(64, 4, 1);
   }
 #undef ARP_SCAN_LAUNCH
   return hipGetLastError();

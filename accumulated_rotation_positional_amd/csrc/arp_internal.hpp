@@ -28,6 +28,7 @@ struct Geometry {
 //   for bf16 without ARP_FUSED_ROTATION; empty otherwise.
 struct ScanPlan {
   int rows_per_thread;  // tokens each thread scans serially (T)
+  int min_blocks;       // workgroups per CU the kernel is built for (launch bounds)
   int chunk;            // tokens per workgroup
   int nchunks;          // chunks per (batch, angle head) segment
 };
