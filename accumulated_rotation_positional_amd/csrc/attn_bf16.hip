@@ -523,7 +523,7 @@ hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const
                                     const float* alibi, uint16_t* o, hipStream_t stream) {
   if (g.D == 64)
     return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, o, stream);
-  return launch_bf16_cfg<128, 32, 4, 2, 2, false>(g, qr, kr, vt, kmax, theta, alibi, o, stream);
+  return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, o, stream);
 }
 
 hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const uint16_t* k,

@@ -120,6 +120,44 @@ def run_cpu_baseline(w, flags: int, alibi, target_s: float) -> dict:
             "seconds": round(dt, 3), "tokens_per_s": rows.size / dt}
 
 
+def scan_gate(binding, torch, dev, steps: int = 30) -> dict:
+    """The angle scan alone on the largest workload's angle tensor (B=4, H=32,
+    L=8192, 64 pairs: 268 MB in, 268 MB out, beyond the 256 MB Infinity
+    Cache), where its HBM roofline is read.  Before every timed launch a
+    512 MB read (a sum, which leaves only clean lines behind, so no write-back
+    overlaps the scan) evicts the cache, and events bracket the scan alone.
+    Seeded uniform angles: the scan's cost does not depend on the values."""
+    from accumulated_rotation_positional_amd import workloads as wl
+    spec = wl.SPECS["rope_8k_d128"]
+    B, H, L, P = spec.batch, spec.heads, spec.seqlen, spec.head_dim // 2
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    phi = torch.rand(B, H, L, P, device=dev, generator=g) * 6.0 - 3.0
+    theta = torch.empty_like(phi)
+    desc = binding.make_desc(B, H, L, 2 * P, "bf16", binding.flags_for())
+    state = binding.scan_state(desc, dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(10):
+        binding.angle_scan(phi, desc, theta=theta, state=state)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        flush.sum()
+        e0.record(stream)
+        binding.angle_scan(phi, desc, theta=theta, state=state)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+    del flush
+    nbytes = 8.0 * phi.numel()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "rope_8k_d128 angles", "bound": "hbm", "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "us_per_launch": round(ms * 1e3, 2), "bytes_per_launch": nbytes}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -239,6 +277,7 @@ def main():
                           "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
                           "traffic": scan_traffic},
     }
+    result["scan_hbm_gate"] = scan_gate(binding, torch, dev)
     if not args.no_cpu_baseline:
         import oracle
         of = (oracle.ROTATE_QK | (oracle.ROTATE_V if w.rotate_v else 0) |
