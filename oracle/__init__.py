@@ -14,7 +14,11 @@ Outputs are float64.
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (brute-force route products, closed-form RoPE, shift invariance,
 orthogonality, textbook attention, closed-form softmax weights, the matched
-score of the method paper's App. B.6, and the RoPE post's worked numbers).
+score of the method paper's App. B.6, and the RoPE post's worked numbers);
+the gradients by ``tests/test_oracle_backward.py`` (central differences of
+the forward, the one-token closed form, invariance under a common angle
+shift, the column-sum identities of softmax attention, and the textbook
+attention gradient of a library autodiff).
 """
 from __future__ import annotations
 
@@ -85,6 +89,9 @@ def _lib() -> ctypes.CDLL:
         lib.oracle_attention_rows.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p,
                                               ctypes.c_int64, ctypes.c_int, dp]
         lib.oracle_attention_rows.restype = ctypes.c_int
+        lib.oracle_backward.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_int,
+                                        dp, dp, dp, dp, dp]
+        lib.oracle_backward.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -181,6 +188,24 @@ class Problem:
                                           int(nthreads), _dptr(out))
         if rc:
             raise RuntimeError(f"oracle_attention_rows failed: {rc}")
+        return out
+
+    def backward(self, dout, nthreads: int = 0) -> dict:
+        """Gradients for the upstream gradient dout ([B, H, L, d], the dtype of q):
+        dict of fp64 arrays dq, dk, dv [B, H, L, d], dtheta [B, H, L, d/2]
+        (per head) and dphi (the shape of phi).  O(L^2 d) per head."""
+        dout = np.ascontiguousarray(dout)
+        if dout.shape != self.q.shape or dout.dtype != self.q.dtype:
+            raise ValueError("dout must match q in shape and dtype")
+        B, H, L, d = self.shape
+        out = {n: np.empty(self.shape, dtype=np.float64) for n in ("dq", "dk", "dv")}
+        out["dtheta"] = np.empty((B, H, L, d // 2), dtype=np.float64)
+        out["dphi"] = np.empty(self.phi.shape, dtype=np.float64)
+        rc = _lib().oracle_backward(ctypes.byref(self.c), dout.ctypes.data, int(nthreads),
+                                    _dptr(out["dq"]), _dptr(out["dk"]), _dptr(out["dv"]),
+                                    _dptr(out["dtheta"]), _dptr(out["dphi"]))
+        if rc:
+            raise RuntimeError(f"oracle_backward failed: {rc}")
         return out
 
     def output(self, nthreads: int = 0) -> np.ndarray:

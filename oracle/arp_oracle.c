@@ -40,6 +40,23 @@
  *  5. Aggregation c_i = sum_j (w_ij / l_i) P_{j->i} v_j ([ACC] eq. (4)); with
  *     value transport this is R(Theta_i)^T sum_j alpha_ij v~_j, without it the
  *     plain sum of eq. (3).
+ *
+ * Gradients (oracle_backward): the chain rule through steps 1-5 as written,
+ * for an upstream gradient g_i = dL/dc_i.  The pages train these models with
+ * learned angles ([ACC] "Model variants"), which needs dL/dphi; nothing about
+ * the gradient is stated on the pages beyond the forward definition, so this
+ * is that definition differentiated by hand:
+ *  - value transport: c_i = R(Theta_i)^T o~_i, so dL/do~_i = R(Theta_i) g_i;
+ *  - softmax: with alpha_ij = w_ij / l_i and D_i = <dL/do~_i, o~_i>,
+ *    dL/ds_ij = alpha_ij (<dL/do~_i, v~_j> - D_i);
+ *  - scores: dL/dq~_i = scale sum_j dL/ds_ij k~_j, dL/dk~_j = scale
+ *    sum_i dL/ds_ij q~_i, dL/dv~_j = sum_i alpha_ij dL/do~_i;
+ *  - rotation: x~ = R(a) x gives dL/dx = R(a)^T dL/dx~ and, per pair,
+ *    dL/da = <dL/dx~, J x~> with J = [[0, -1], [1, 0]] (dR/da = R J = J R);
+ *    the transport step contributes -<dL/do~_i, J o~_i> at position i;
+ *  - scan: Theta_t sums phi_s over s <= t, so dL/dphi_s sums dL/dTheta_t over
+ *    t >= s (t > s for the exclusive scan), and over the heads that share one
+ *    angle stream.  The wrap into [-pi, pi) has derivative 1.
  */
 #include "arp_oracle.h"
 
@@ -315,4 +332,160 @@ int oracle_attention_rows(const oracle_problem* p, const int64_t* rows, int64_t 
   }
   free(imax);
   return rc;
+}
+
+/* ---------------------------------------------------------------------------
+ * Gradients.
+ * ------------------------------------------------------------------------- */
+
+/* <x, J a> for one pair: J a = (-a1, a0). */
+static double pair_cross(const double* x, const double* a) { return -x[0] * a[1] + x[1] * a[0]; }
+
+/* One (b, h): all gradients of the head, O(L^2 d). dtheta_h is [L, P]. */
+static int backward_head(const oracle_problem* p, const void* dout, int64_t b, int64_t h,
+                         double* dq, double* dk, double* dv, double* dtheta_h) {
+  const int64_t d = p->head_dim, P = d / 2, L = p->seqlen;
+  const int64_t base = ((b * p->heads + h) * L) * d;
+  const int qk = (p->flags & ORACLE_ROTATE_QK) != 0, tv = (p->flags & ORACLE_ROTATE_V) != 0;
+  const double slope = (p->flags & ORACLE_ALIBI) ? (double)p->alibi_slopes[h] : 0.0;
+  head_state hs;
+  int rc = head_build(p, b, h, L - 1, &hs);
+  if (rc) return rc;
+  double* qrot = (double*)calloc((size_t)(L * d), sizeof(double));
+  double* dorot = (double*)calloc((size_t)(L * d), sizeof(double));  /* dL/do~ */
+  double* otil = (double*)calloc((size_t)(L * d), sizeof(double));   /* o~ */
+  double* dqt = (double*)calloc((size_t)(L * d), sizeof(double));
+  double* dkt = (double*)calloc((size_t)(L * d), sizeof(double));
+  double* dvt = (double*)calloc((size_t)(L * d), sizeof(double));
+  double* alpha = (double*)malloc(sizeof(double) * (size_t)L);
+  double* raw = (double*)malloc(sizeof(double) * (size_t)d);
+  if (!qrot || !dorot || !otil || !dqt || !dkt || !dvt || !alpha || !raw) {
+    rc = ORACLE_ERR_NOMEM;
+    goto done;
+  }
+  for (int64_t t = 0; t < L; ++t) {
+    for (int64_t c = 0; c < d; ++c) raw[c] = load_elem(p->q, p->io_dtype, base + t * d + c);
+    if (qk) rotate_vec(raw, hs.theta + t * P, P, 0, qrot + t * d);
+    else memcpy(qrot + t * d, raw, sizeof(double) * (size_t)d);
+    for (int64_t c = 0; c < d; ++c) raw[c] = load_elem(dout, p->io_dtype, base + t * d + c);
+    if (tv) rotate_vec(raw, hs.theta + t * P, P, 0, dorot + t * d);
+    else memcpy(dorot + t * d, raw, sizeof(double) * (size_t)d);
+  }
+  for (int64_t i = 0; i < L; ++i) {
+    /* forward row: scores, normalised weights alpha_ij, o~_i */
+    const double* qi = qrot + i * d;
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= i; ++j) {
+      const double* kj = hs.krot + j * d;
+      double dot = 0.0;
+      for (int64_t c = 0; c < d; ++c) dot += qi[c] * kj[c];
+      alpha[j] = p->scale * dot - slope * (double)(i - j);
+      if (alpha[j] > m) m = alpha[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j <= i; ++j) {
+      alpha[j] = exp(alpha[j] - m);
+      l += alpha[j];
+    }
+    double* oi = otil + i * d;
+    for (int64_t j = 0; j <= i; ++j) {
+      alpha[j] /= l;
+      const double* vj = hs.vrot + j * d;
+      for (int64_t c = 0; c < d; ++c) oi[c] += alpha[j] * vj[c];
+    }
+    /* backward row */
+    const double* gi = dorot + i * d;
+    double Di = 0.0;
+    for (int64_t c = 0; c < d; ++c) Di += gi[c] * oi[c];
+    for (int64_t j = 0; j <= i; ++j) {
+      const double* vj = hs.vrot + j * d;
+      const double* kj = hs.krot + j * d;
+      double dp = 0.0;
+      for (int64_t c = 0; c < d; ++c) dp += gi[c] * vj[c];
+      const double ds = alpha[j] * (dp - Di);
+      for (int64_t c = 0; c < d; ++c) {
+        dqt[i * d + c] += p->scale * ds * kj[c];
+        dkt[j * d + c] += p->scale * ds * qi[c];
+        dvt[j * d + c] += alpha[j] * gi[c];
+      }
+    }
+  }
+  for (int64_t t = 0; t < L; ++t) {
+    const double* th = hs.theta + t * P;
+    for (int64_t pp = 0; pp < P; ++pp) {
+      double g = 0.0;
+      if (qk) {
+        g += pair_cross(dqt + t * d + 2 * pp, qrot + t * d + 2 * pp);
+        g += pair_cross(dkt + t * d + 2 * pp, hs.krot + t * d + 2 * pp);
+      }
+      if (tv) {
+        g += pair_cross(dvt + t * d + 2 * pp, hs.vrot + t * d + 2 * pp);
+        g -= pair_cross(dorot + t * d + 2 * pp, otil + t * d + 2 * pp);
+      }
+      dtheta_h[t * P + pp] = g;
+    }
+    double* oq = dq + base + t * d;
+    double* ok = dk + base + t * d;
+    double* ov = dv + base + t * d;
+    if (qk) {
+      rotate_vec(dqt + t * d, th, P, 1, oq);
+      rotate_vec(dkt + t * d, th, P, 1, ok);
+    } else {
+      memcpy(oq, dqt + t * d, sizeof(double) * (size_t)d);
+      memcpy(ok, dkt + t * d, sizeof(double) * (size_t)d);
+    }
+    if (tv) rotate_vec(dvt + t * d, th, P, 1, ov);
+    else memcpy(ov, dvt + t * d, sizeof(double) * (size_t)d);
+  }
+done:
+  free(qrot);
+  free(dorot);
+  free(otil);
+  free(dqt);
+  free(dkt);
+  free(dvt);
+  free(alpha);
+  free(raw);
+  head_free(&hs);
+  return rc;
+}
+
+int oracle_backward(const oracle_problem* p, const void* dout, int nthreads, double* dq,
+                    double* dk, double* dv, double* dtheta, double* dphi) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!dout || !dq || !dk || !dv || !dtheta || !dphi) return ORACLE_ERR_ARG;
+  const int64_t B = p->batch, H = p->heads, L = p->seqlen, P = p->head_dim / 2;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+  for (int64_t bh = 0; bh < B * H; ++bh)
+    err |= backward_head(p, dout, bh / H, bh % H, dq, dk, dv, dtheta + bh * L * P);
+  if (err) return err;
+  /* dphi_s = sum over heads sharing the stream, and over t >= s (t > s exclusive). */
+  const int excl = (p->flags & ORACLE_SCAN_EXCLUSIVE) != 0;
+  memset(dphi, 0, sizeof(double) * (size_t)(B * p->phi_heads * L * P));
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t h = 0; h < H; ++h) {
+      const int64_t g = (p->phi_heads == 1) ? 0 : h;
+      const double* dth = dtheta + (b * H + h) * L * P;
+      double* out = dphi + (b * p->phi_heads + g) * L * P;
+      for (int64_t pp = 0; pp < P; ++pp) {
+        double run = 0.0;
+        for (int64_t s = L - 1; s >= 0; --s) {
+          if (excl) {
+            out[s * P + pp] += run;
+            run += dth[s * P + pp];
+          } else {
+            run += dth[s * P + pp];
+            out[s * P + pp] += run;
+          }
+        }
+      }
+    }
+  return ORACLE_OK;
 }

@@ -75,6 +75,16 @@ int oracle_scores_row(const oracle_problem* p, int64_t b, int64_t h, int64_t i, 
 int oracle_attention_rows(const oracle_problem* p, const int64_t* rows, int64_t nrows,
                           int nthreads, double* out);
 
+/* Gradients of the attention output (oracle_attention_rows over every row)
+ * for an upstream gradient dout ([batch, heads, seqlen, head_dim], same io
+ * dtype as q).  Outputs, all fp64:
+ *   dq, dk, dv  [batch, heads, seqlen, head_dim]
+ *   dtheta      [batch, heads, seqlen, head_dim/2]   dL/dTheta per head
+ *   dphi        [batch, phi_heads, seqlen, head_dim/2]
+ * O(seqlen^2 head_dim) per head; OpenMP over heads. */
+int oracle_backward(const oracle_problem* p, const void* dout, int nthreads, double* dq,
+                    double* dk, double* dv, double* dtheta, double* dphi);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,8 +33,20 @@ MUTANTS = [
 ]
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_fail_on_planted_mistake(name, old, new, tmp_path):
+# Mistakes in the gradients, caught by the backward pins.
+BACKWARD_MUTANTS = [
+    ("rotation derivative sign", "return -x[0] * a[1] + x[1] * a[0];", "return x[0] * a[1] - x[1] * a[0];"),
+    ("softmax centring dropped", "const double ds = alpha[j] * (dp - Di);", "const double ds = alpha[j] * dp;"),
+    ("transport angle term dropped", "g -= pair_cross(dorot + t * d + 2 * pp, otil + t * d + 2 * pp);", "(void)0;"),
+    ("key gradient scale dropped", "dkt[j * d + c] += p->scale * ds * qi[c];", "dkt[j * d + c] += ds * qi[c];"),
+    ("angle gradient summed forward", "for (int64_t s = L - 1; s >= 0; --s) {", "for (int64_t s = 0; s < L; ++s) {"),
+    ("query gradient rotated forward", "rotate_vec(dqt + t * d, th, P, 1, oq);", "rotate_vec(dqt + t * d, th, P, 0, oq);"),
+    ("upstream gradient rotated backward", "if (tv) rotate_vec(raw, hs.theta + t * P, P, 0, dorot + t * d);",
+     "if (tv) rotate_vec(raw, hs.theta + t * P, P, 1, dorot + t * d);"),
+]
+
+
+def _run_pins_against(old, new, name, tmp_path, pin_file):
     src = open(SRC).read()
     assert src.count(old) >= 1, f"mutation site for {name!r} not found"
     mutant = src.replace(old, new, 1)
@@ -46,6 +58,16 @@ def test_pins_fail_on_planted_mistake(name, old, new, tmp_path):
                    check=True)
     env = dict(os.environ, ARP_ORACLE_LIB=str(so_path))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pin_file)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"no pin caught the planted mistake {name!r}:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_fail_on_planted_mistake(name, old, new, tmp_path):
+    _run_pins_against(old, new, name, tmp_path, "test_oracle_pins.py")
+
+
+@pytest.mark.parametrize("name,old,new", BACKWARD_MUTANTS, ids=[m[0] for m in BACKWARD_MUTANTS])
+def test_backward_pins_fail_on_planted_mistake(name, old, new, tmp_path):
+    _run_pins_against(old, new, name, tmp_path, "test_oracle_backward.py")
