@@ -35,7 +35,8 @@ FUSED_ROTATION = 0x20
 EXPORTS = ("arp_abi_version", "arp_status_string", "arp_check", "arp_scan_state_bytes",
            "arp_workspace_bytes",
            "arp_angle_scan", "arp_rotate_qkv", "arp_attn_rotated", "arp_attn_fwd",
-           "arp_forward", "arp_rotate")
+           "arp_forward", "arp_rotate", "arp_forward_train", "arp_backward_workspace_bytes",
+           "arp_backward")
 
 
 class ArpError(RuntimeError):
@@ -76,6 +77,9 @@ def lib() -> ctypes.CDLL:
                 "arp_attn_fwd": ([D, P, P, P, P, P, P, P, S, P], ctypes.c_int),
                 "arp_forward": ([D, P, P, P, P, P, P, P, P, S, P, S, P], ctypes.c_int),
                 "arp_rotate": ([D, P, P, P, ctypes.c_int, P], ctypes.c_int),
+                "arp_forward_train": ([D, P, P, P, P, P, P, P, P, P, S, P, S, P], ctypes.c_int),
+                "arp_backward_workspace_bytes": ([D], S),
+                "arp_backward": ([D] + [P] * 14 + [S, P], ctypes.c_int),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -237,3 +241,61 @@ def rotate(x: torch.Tensor, theta: torch.Tensor, desc: Desc, inverse: bool = Fal
     _check("arp_rotate", lib().arp_rotate(ctypes.byref(desc), _ptr(x), _ptr(theta), _ptr(out),
                                           int(inverse), _stream(x.device)))
     return out
+
+
+def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.Tensor, *,
+                  rotate_qk: bool = True, rotate_v: bool = False,
+                  alibi: torch.Tensor | None = None, scale: float | None = None,
+                  exclusive: bool = False):
+    """Forward pass that also returns the per-row base-2 log-sum-exp (bf16,
+    pre-rotation path): (o, theta, lse, desc), everything the backward needs."""
+    _require_gpu(q, k, v, phi, alibi)
+    flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi is not None,
+                      shared_phi=phi.shape[1] == 1 and q.shape[1] != 1, exclusive=exclusive)
+    desc = desc_for(q, flags, scale)
+    out = torch.empty_like(q)
+    theta = torch.empty_like(phi)
+    B, H, L, _ = q.shape
+    lse = torch.empty(B, H, L, dtype=torch.float32, device=q.device)
+    state = scan_state(desc, q.device)
+    ws = workspace(desc, q.device)
+    _check("arp_forward_train", lib().arp_forward_train(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(phi), _ptr(alibi), _ptr(theta),
+        _ptr(out), _ptr(lse), _ptr(state), state.numel(), _ptr(ws), ws.numel(),
+        _stream(q.device)))
+    return out, theta, lse, desc
+
+
+def backward_workspace_bytes(desc: Desc) -> int:
+    return int(lib().arp_backward_workspace_bytes(ctypes.byref(desc)))
+
+
+_BWS: dict = {}
+
+
+def backward_workspace(desc: Desc, device: torch.device) -> torch.Tensor:
+    """The backward's operand workspace, cached per (device, stream)."""
+    need = max(backward_workspace_bytes(desc), 256)
+    key = (device.index, _stream(device))
+    ws = _BWS.get(key)
+    if ws is None or ws.numel() < need:
+        _BWS.pop(key, None)
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        _BWS[key] = ws
+    return ws
+
+
+def backward(desc: Desc, q, k, v, phi, theta, o, lse, dout, alibi=None, ws=None):
+    """Gradients for dout = dL/do: (dq, dk, dv, dphi, dtheta), with dtheta the
+    per-head dL/dTheta ([B, H, L, d/2])."""
+    _require_gpu(q, k, v, phi, theta, o, lse, dout, alibi, ws)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    B, H, L, d = q.shape
+    dtheta = torch.empty(B, H, L, d // 2, dtype=torch.float32, device=q.device)
+    dphi = torch.empty_like(phi)
+    ws = backward_workspace(desc, q.device) if ws is None else ws
+    _check("arp_backward", lib().arp_backward(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(alibi), _ptr(o),
+        _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtheta), _ptr(dphi),
+        _ptr(ws), ws.numel(), _stream(q.device)))
+    return dq, dk, dv, dphi, dtheta

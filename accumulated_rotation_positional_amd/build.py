@@ -2,8 +2,8 @@
 
 Every source is compiled for gfx950 only.  ``-packed-fp32-ops`` keeps the
 compiler from emitting packed fp32 arithmetic; ``-ffp-contract=fast`` (the HIP
-default) is kept, and nothing is built with fast-math, so the compensated sums
-of the angle scan are compiled as written.
+default) is kept, and nothing is built with fast-math, so the angle scan's
+fixed-point conversions are compiled as written.
 """
 from __future__ import annotations
 
@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 TARGET = os.path.join(HERE, "libarp.so")
-SOURCES = ["api.hip", "angle_scan.hip", "rotate.hip", "attn_f32.hip", "attn_bf16.hip"]
+SOURCES = ["api.hip", "angle_scan.hip", "rotate.hip", "attn_f32.hip", "attn_bf16.hip", "attn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

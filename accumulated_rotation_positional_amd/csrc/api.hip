@@ -85,6 +85,16 @@ WorkspaceLayout workspace_layout(const Geometry& g) {
   return lay;
 }
 
+BwdWorkspaceLayout bwd_workspace_layout(const Geometry& g) {
+  BwdWorkspaceLayout lay{};
+  lay.operand_bytes = align_up((size_t)g.B * g.H * g.Lp * g.D * sizeof(uint16_t));
+  lay.stats_off = 7 * lay.operand_bytes;
+  lay.totals_off = lay.stats_off + align_up((size_t)g.B * g.H * g.Lp * 2 * sizeof(float));
+  const size_t nch = ((size_t)g.L + 255) / 256;
+  lay.total = lay.totals_off + align_up((size_t)g.B * g.Hphi * nch * g.P * sizeof(float));
+  return lay;
+}
+
 }  // namespace arp
 
 using namespace arp;
@@ -173,7 +183,7 @@ arp_status arp_attn_rotated(const arp_desc* desc, const float* theta, const floa
       reinterpret_cast<const uint16_t*>(ws + lay.k_off),
       reinterpret_cast<const uint16_t*>(ws + lay.vt_off),
       reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi,
-      static_cast<uint16_t*>(o), (hipStream_t)stream));
+      static_cast<uint16_t*>(o), nullptr, (hipStream_t)stream));
 }
 
 arp_status arp_attn_fwd(const arp_desc* desc, const void* q, const void* k, const void* v,
@@ -221,6 +231,84 @@ arp_status arp_forward(const arp_desc* desc, const void* q, const void* k, const
   st = arp_angle_scan(desc, phi, theta, scan_state, scan_state_bytes, stream);
   if (st != ARP_OK) return st;
   return arp_attn_fwd(desc, q, k, v, theta, alibi, o, workspace, workspace_bytes, stream);
+}
+
+arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k, const void* v,
+                             const float* phi, const float* alibi, float* theta, void* o,
+                             float* lse, void* scan_state, size_t scan_state_bytes,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (!needs_operands(g)) return ARP_ERR_UNSUPPORTED;
+  if (lse == nullptr) return ARP_ERR_INVALID_ARG;
+  if (!aligned16(lse)) return ARP_ERR_ALIGNMENT;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || phi == nullptr ||
+      theta == nullptr || ((g.flags & ARP_ALIBI) && alibi == nullptr))
+    return ARP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(phi) ||
+      !aligned16(theta) || (alibi && !aligned16(alibi)))
+    return ARP_ERR_ALIGNMENT;
+  if ((st = check_scan_state(g, scan_state, scan_state_bytes)) != ARP_OK) return st;
+  if ((st = check_ws(g, workspace, workspace_bytes)) != ARP_OK) return st;
+  st = arp_angle_scan(desc, phi, theta, scan_state, scan_state_bytes, stream);
+  if (st != ARP_OK) return st;
+  st = arp_rotate_qkv(desc, q, k, v, theta, workspace, workspace_bytes, stream);
+  if (st != ARP_OK) return st;
+  const WorkspaceLayout lay = workspace_layout(g);
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(launch_attn_bf16_rotated(
+      g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
+      reinterpret_cast<const uint16_t*>(ws + lay.k_off),
+      reinterpret_cast<const uint16_t*>(ws + lay.vt_off),
+      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi,
+      static_cast<uint16_t*>(o), lse, (hipStream_t)stream));
+}
+
+size_t arp_backward_workspace_bytes(const arp_desc* desc) {
+  Geometry g;
+  if (make_geometry(desc, &g) != ARP_OK || g.dtype != ARP_DTYPE_BF16) return 0;
+  return bwd_workspace_layout(g).total;
+}
+
+arp_status arp_backward(const arp_desc* desc, const void* q, const void* k, const void* v,
+                        const float* theta, const float* alibi, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, float* dtheta,
+                        float* dphi, void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (g.dtype != ARP_DTYPE_BF16) return ARP_ERR_UNSUPPORTED;
+  const void* in[] = {q, k, v, o, lse, dout, dq, dk, dv, dtheta, dphi};
+  for (const void* p : in)
+    if (p == nullptr) return ARP_ERR_INVALID_ARG;
+  if ((rotates(g) && theta == nullptr) || ((g.flags & ARP_ALIBI) && alibi == nullptr))
+    return ARP_ERR_INVALID_ARG;
+  for (const void* p : in)
+    if (!aligned16(p)) return ARP_ERR_ALIGNMENT;
+  if ((theta && !aligned16(theta)) || (alibi && !aligned16(alibi))) return ARP_ERR_ALIGNMENT;
+  const BwdWorkspaceLayout lay = bwd_workspace_layout(g);
+  if ((st = check_buffer(workspace, workspace_bytes, lay.total)) != ARP_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  auto blk = [&](int i) { return reinterpret_cast<uint16_t*>(ws + i * lay.operand_bytes); };
+  BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.theta = theta;
+  a.lse = lse;
+  a.alibi = alibi;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.dtheta = dtheta;
+  a.dphi = dphi;
+  a.totals = reinterpret_cast<float*>(ws + lay.totals_off);
+  a.ops = BwdOperands{blk(0), blk(1), blk(2), blk(3), blk(4), blk(5), blk(6),
+                      reinterpret_cast<float*>(ws + lay.stats_off)};
+  return hip_status(launch_backward_bf16(g, a, (hipStream_t)stream));
 }
 
 arp_status arp_rotate(const arp_desc* desc, const void* x, const float* theta, float* out,

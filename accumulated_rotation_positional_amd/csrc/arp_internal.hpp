@@ -50,7 +50,8 @@ hipError_t launch_rotate_qkv(const Geometry& g, const void* q, const void* k, co
                              float* kmax, hipStream_t stream);
 hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                                     const uint16_t* vt, const float* kmax, const float* theta,
-                                    const float* alibi, uint16_t* o, hipStream_t stream);
+                                    const float* alibi, uint16_t* o, float* lse,
+                                    hipStream_t stream);
 hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const float* theta, const float* alibi,
                                   uint16_t* o, hipStream_t stream);
@@ -58,5 +59,37 @@ hipError_t launch_attn_f32(const Geometry& g, const float* q, const float* k, co
                            const float* theta, const float* alibi, float* o, hipStream_t stream);
 hipError_t launch_rotate_diag(const Geometry& g, const void* x, const float* theta, float* out,
                               int inverse, hipStream_t stream);
+
+// ---- backward (bf16) --------------------------------------------------------
+// Operands the gradient kernels read, in the backward workspace (per head):
+//   qs, k, v, dout   bf16 [B*H, Lp, D]: q~ * scale * log2 e, k~, v~, do~
+//   qsT, kT, doutT   bf16 [B*H, D, Lp]: transposes of qs, k, dout
+//   stats            fp32 [B*H, Lp/64, 128]: per 64-row tile, lse (+inf past L)
+//                    then D = <do~, o~> (0 past L)
+struct BwdOperands {
+  uint16_t* qs;
+  uint16_t* qsT;
+  uint16_t* k;
+  uint16_t* kT;
+  uint16_t* v;
+  uint16_t* dout;
+  uint16_t* doutT;
+  float* stats;
+};
+struct BwdArgs {
+  const uint16_t *q, *k, *v, *o, *dout;  // caller tensors [B, H, L, D]
+  const float *theta, *lse, *alibi;
+  uint16_t *dq, *dk, *dv;                // caller gradients [B, H, L, D]
+  float* dtheta;                         // caller [B, H, L, P]
+  float* dphi;                           // caller [B, Hphi, L, P]
+  float* totals;                         // workspace [B*Hphi, ceil(L/256), P]
+  BwdOperands ops;
+};
+struct BwdWorkspaceLayout {
+  size_t operand_bytes;  // one bf16 [B*H, Lp, D] block
+  size_t stats_off, totals_off, total;
+};
+BwdWorkspaceLayout bwd_workspace_layout(const Geometry& g);
+hipError_t launch_backward_bf16(const Geometry& g, const BwdArgs& a, hipStream_t stream);
 
 }  // namespace arp

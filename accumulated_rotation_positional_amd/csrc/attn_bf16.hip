@@ -38,6 +38,7 @@
 //    heads (its L2 then holds that head's K/V), longest query tiles first.
 #include "arp_device.hpp"
 #include "arp_internal.hpp"
+#include "mfma_tile.hpp"
 
 namespace arp {
 
@@ -45,48 +46,6 @@ namespace {
 
 constexpr int BN = KEY_TILE;  // keys per tile
 constexpr float TAU = 8.0f;   // lazy-rescale threshold (base-2 logits)
-
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef const __attribute__((address_space(1))) void* global_void_ptr;
-
-// Row order of K~ in LDS: bits 2 and 3 of the key index swapped (an involution).
-__device__ __forceinline__ int swap_bits23(int x) {
-  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
-
-// LDS swizzle: the 16-byte chunk c of a row of ROWB bytes is stored at chunk
-// c ^ swz(row).  A 128-bit LDS read serves 16 lanes per cycle from 64 banks,
-// i.e. 256 bytes; the operand reads of 16 consecutive rows must therefore hit
-// 16 distinct 16-byte bank groups, which this choice guarantees for 64-, 128-
-// and 256-byte rows.
-template <int ROWB>
-__device__ __forceinline__ int swz(int row) {
-  static_assert(ROWB == 64 || ROWB == 128 || ROWB == 256, "row size");
-  return ROWB == 64 ? ((row >> 2) & 3) : ROWB == 128 ? ((row >> 1) & 7) : (row & 15);
-}
-
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Max and sum of a value over the two half-waves (lanes l and l ^ 32), with
-// one v_permlane32_swap: afterwards each lane holds both halves' values.
-__device__ __forceinline__ float halves_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Wait until at most N global->LDS loads of this wave are still in flight
-// (s_waitcnt vmcnt(N), the other counters untouched).
-template <int N>
-__device__ __forceinline__ void wait_loads() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
 
 // FUSED = false: q~, k~ (L padded to Lp) and v~^T come pre-rotated from the
 // rotation pass, K/V tiles load straight into LDS, and the per-tile key-norm
@@ -100,7 +59,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
     const float* __restrict__ theta, const float* __restrict__ alibi, uint16_t* __restrict__ o,
-    int L, int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk, float qscale) {
+    float* __restrict__ lse, int L, int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk,
+    float qscale) {
   constexpr int BM = QPW * NW;
   constexpr int QB = QPW / 32;         // 32-query blocks per wave
   constexpr int KS = D / 16;           // k-steps of S^T (16 of D each)
@@ -468,6 +428,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     const float ltot = halves_sum(lsum[qb]);
     if (i >= L) continue;
     const float inv = 1.f / ltot;
+    // base-2 log-sum-exp of the row's scaled logits, for the backward pass
+    if (lse != nullptr && hf == 0) lse[(size_t)bh * L + i] = mrun[qb] + __log2f(ltot);
     const float* th = theta + ((size_t)(b * Hphi + g) * L + i) * (D / 2);
     uint16_t* orow = o + ((size_t)bh * L + i) * D;
 #pragma unroll
@@ -495,7 +457,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
 template <int D, int QPW, int NW, int NST, int MINB, bool FUSED>
 hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                            const uint16_t* vt, const float* kmax, const float* theta,
-                           const float* alibi, uint16_t* o, hipStream_t stream) {
+                           const float* alibi, uint16_t* o, float* lse, hipStream_t stream) {
   constexpr int BM = QPW * NW;
   const int nqt = (g.L + BM - 1) / BM;
   const int total = g.B * g.H * nqt;
@@ -505,8 +467,8 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
   const float qscale = g.scale * LOG2E;
 #define ARP_BF16_LAUNCH(A, R)                                                                  \
   hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, MINB, FUSED, A, R>), dim3(grid),      \
-                     dim3(NW * 64), 0, stream, qr, kr, vt, kmax, theta, alibi, o, g.L, g.Lp, g.H, \
-                     g.Hphi, nqt, total, rqk, qscale)
+                     dim3(NW * 64), 0, stream, qr, kr, vt, kmax, theta, alibi, o, lse, g.L, g.Lp, \
+                     g.H, g.Hphi, nqt, total, rqk, qscale)
   if (al) {
     if (rv) ARP_BF16_LAUNCH(true, true); else ARP_BF16_LAUNCH(true, false);
   } else {
@@ -520,18 +482,19 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
 
 hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                                     const uint16_t* vt, const float* kmax, const float* theta,
-                                    const float* alibi, uint16_t* o, hipStream_t stream) {
+                                    const float* alibi, uint16_t* o, float* lse,
+                                    hipStream_t stream) {
   if (g.D == 64)
-    return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, o, stream);
-  return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, o, stream);
+    return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, o, lse, stream);
+  return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, o, lse, stream);
 }
 
 hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const float* theta, const float* alibi,
                                   uint16_t* o, hipStream_t stream) {
   if (g.D == 64)
-    return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, o, stream);
-  return launch_bf16_cfg<128, 32, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, o, stream);
+    return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, o, nullptr, stream);
+  return launch_bf16_cfg<128, 32, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, o, nullptr, stream);
 }
 
 }  // namespace arp

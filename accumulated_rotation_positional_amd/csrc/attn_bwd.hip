@@ -1,0 +1,651 @@
+// attn_bwd.hip -- gradients of causal attention with accumulated SO(2)
+// rotations (bf16 operands, fp32 accumulation) on the gfx950 matrix cores.
+//
+// The forward ("Why Do Accumulated Transformations Extrapolate?" eq. (2)-(4),
+// with q~ = R(Theta) q etc. as in "AdaRoPE" Sec. 2.1 eq. (1)) differentiated:
+//   do~_i = R(Theta_i) dO_i (value transport) or dO_i
+//   D_i   = <do~_i, o~_i>,  o~_i = R(Theta_i) o_i (value transport) or o_i
+//   P_ij  = 2^(s2_ij - lse2_i)                   (base-2 logits of the forward)
+//   dS_ij = P_ij (<do~_i, v~_j> - D_i)
+//   dq~_i = scale sum_j dS_ij k~_j,  dk~_j = scale sum_i dS_ij q~_i,
+//   dv~_j = sum_i P_ij do~_i
+//   dx = R(Theta)^T dx~ for every rotated x, and per pair
+//   dTheta_t = <dq~_t, J q~_t> + <dk~_t, J k~_t> + <dv~_t, J v~_t> - <do~_t, J o~_t>
+//   (J = [[0, -1], [1, 0]]; each term only when that tensor is rotated)
+//   dphi_s = sum_{t >= s} dTheta_t (t > s for the exclusive scan), summed over
+//   the heads that share one angle stream.
+//
+// Kernels, in stream order:
+//  1. bwd_prep: one pass over q, k, v, o, dO and Theta per 64-token tile:
+//     the bf16 operands (q~ scaled by scale log2 e, k~, v~, do~ row-major;
+//     q~^T, k~^T, do~^T transposed through LDS), per-row lse (padded with
+//     +inf) and D, and dTheta initialised with the value-transport term.
+//  2. bwd_dkdv: key-stationary; a lane owns one key.  Per 32-query block:
+//       S    = Q~ K~^T   - lse   (A: q~ rows from LDS, B: k~ row in registers)
+//       dP'  = dO~ V~^T  - D     (A: do~ rows from LDS, B: v~ row in registers)
+//       dS   = P * dP'
+//       dV^T += dO~^T P,  dK^T += Q~^T dS   (A: transposed tiles from LDS)
+//     The query rows sit in LDS in the swap_bits23 order, so the S and dP'
+//     accumulators are directly the B operands of the dV^T / dK^T products.
+//  3. bwd_dq: query-stationary (the forward's orientation); a lane owns one
+//     query.  Per 64-key tile: S^T = K~ Q~^T - lse, dP'^T = V~ dO~^T - D,
+//     dS^T = P^T * dP'^T, dQ^T += K~^T dS^T.
+//  Both kernels end with the un-rotation of their gradients and add their
+//  <dx~, J x~> terms to dTheta (each (t, p) owned by one lane).
+//  4. reverse scan of dTheta into dphi: chunk totals, suffix offsets of the
+//     chunks, then the in-chunk suffix sums.
+#include <type_traits>
+
+#include "arp_device.hpp"
+#include "arp_internal.hpp"
+#include "mfma_tile.hpp"
+
+namespace arp {
+
+namespace {
+
+constexpr int TILE = 64;  // tokens per tile (queries or keys)
+
+// ---------------------------------------------------------------------------
+// 1. prep
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+    const float* __restrict__ theta, const float* __restrict__ lse, BwdOperands ops,
+    float* __restrict__ dtheta, int L, int Lp, int H, int Hphi, uint32_t flags, float qscale) {
+  constexpr int P = D / 2;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  constexpr int ITER = TILE * CPR / 256;
+  constexpr int TS = TILE + 8;  // padded LDS row of a transposed tile (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t s_t[3][D * TS];
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh % H;
+  const int g = (Hphi == 1) ? 0 : h;
+  const int t0 = blockIdx.x * TILE;
+  const int tid = threadIdx.x;
+  const bool rqk = (flags & ARP_ROTATE_QK) != 0, rv = (flags & ARP_ROTATE_V) != 0;
+  const size_t rm = (size_t)bh * Lp * D;  // row-major block of this head
+  float* stats = ops.stats + ((size_t)bh * (Lp / TILE) + blockIdx.x) * (2 * TILE);
+
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int idx = it * 256 + tid;
+    const int r = idx / CPR, c = idx % CPR;
+    const int tok = t0 + r;
+    u32x4 wq = {0, 0, 0, 0}, wk = wq, wv = wq, wd = wq;
+    float dsum = 0.f;
+    if (tok < L) {
+      const size_t off = ((size_t)bh * L + tok) * D + c * 8;
+      const u32x4 xq = *reinterpret_cast<const u32x4*>(q + off);
+      const u32x4 xk = *reinterpret_cast<const u32x4*>(k + off);
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(v + off);
+      const u32x4 xo = *reinterpret_cast<const u32x4*>(o + off);
+      const u32x4 xd = *reinterpret_cast<const u32x4*>(dout + off);
+      float4 th = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (rqk || rv)
+        th = *reinterpret_cast<const float4*>(theta + ((size_t)(b * Hphi + g) * L + tok) * P + c * 4);
+      const float ang[4] = {th.x, th.y, th.z, th.w};
+      float dth[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float sn, cs;
+        sincosf(ang[e], &sn, &cs);
+        float q0 = lo_bf16(xq[e]), q1 = hi_bf16(xq[e]);
+        float k0 = lo_bf16(xk[e]), k1 = hi_bf16(xk[e]);
+        float v0 = lo_bf16(xv[e]), v1 = hi_bf16(xv[e]);
+        float o0 = lo_bf16(xo[e]), o1 = hi_bf16(xo[e]);
+        float d0 = lo_bf16(xd[e]), d1 = hi_bf16(xd[e]);
+        if (rqk) {
+          rotate_pair(q0, q1, cs, sn);
+          rotate_pair(k0, k1, cs, sn);
+        }
+        if (rv) {
+          rotate_pair(v0, v1, cs, sn);
+          rotate_pair(o0, o1, cs, sn);
+          rotate_pair(d0, d1, cs, sn);
+        }
+        wq[e] = pack_bf16x2(q0 * qscale, q1 * qscale);
+        wk[e] = pack_bf16x2(k0, k1);
+        wv[e] = pack_bf16x2(v0, v1);
+        wd[e] = pack_bf16x2(d0, d1);
+        // D and the transport term from the bf16 do~ the products use, so
+        // that sum_j dS_ij = 0 and sum_t dTheta_t = 0 hold for the computed
+        // gradients as they do for the exact ones
+        d0 = lo_bf16(wd[e]);
+        d1 = hi_bf16(wd[e]);
+        dsum = fmaf(d0, o0, fmaf(d1, o1, dsum));
+        // value transport: -<do~, J o~> = d0 o1 - d1 o0
+        dth[e] = rv ? (d0 * o1 - d1 * o0) : 0.f;
+      }
+      *reinterpret_cast<float4*>(dtheta + ((size_t)bh * L + tok) * P + c * 4) =
+          make_float4(dth[0], dth[1], dth[2], dth[3]);
+    }
+    const size_t roff = rm + (size_t)tok * D + c * 8;
+    *reinterpret_cast<u32x4*>(ops.qs + roff) = wq;
+    *reinterpret_cast<u32x4*>(ops.k + roff) = wk;
+    *reinterpret_cast<u32x4*>(ops.v + roff) = wv;
+    *reinterpret_cast<u32x4*>(ops.dout + roff) = wd;
+    // D_i: the CPR threads of a row are consecutive lanes
+#pragma unroll
+    for (int m = 1; m < CPR; m <<= 1) dsum += __shfl_xor(dsum, m);
+    if (c == 0) {
+      stats[r] = (tok < L) ? lse[(size_t)bh * L + tok] : INFINITY;
+      stats[TILE + r] = (tok < L) ? dsum : 0.f;
+    }
+    const u32x4* src[3] = {&wq, &wk, &wd};
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s_t[a][(c * 8 + 2 * e) * TS + r] = (uint16_t)((*src[a])[e] & 0xFFFFu);
+        s_t[a][(c * 8 + 2 * e + 1) * TS + r] = (uint16_t)((*src[a])[e] >> 16);
+      }
+  }
+  __syncthreads();
+  uint16_t* dstT[3] = {ops.qsT, ops.kT, ops.doutT};
+  const size_t tb = (size_t)bh * D * Lp;
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int it = 0; it < D * 8 / 256; ++it) {
+      const int idx = it * 256 + tid;
+      const int drow = idx / 8, cc = idx % 8;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(&s_t[a][drow * TS + cc * 8]);
+      *reinterpret_cast<u32x4*>(dstT[a] + tb + (size_t)drow * Lp + t0 + cc * 8) = w;
+    }
+}
+
+// Direct global -> LDS copy of one 64-row tile, rows row-major [64][D] bf16,
+// stored with rows in the swap_bits23 order and 16-byte chunks swizzled.
+template <int D, int NW>
+__device__ __forceinline__ void load_rows_tile(const uint16_t* base, int r0, uint8_t* lds, int wave,
+                                               int lane) {
+  constexpr int ROWB = D * 2, BYTES = TILE * ROWB, PER = BYTES / (1024 * NW);
+  static_assert(PER * 1024 * NW == BYTES, "row tile split");
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int p0 = (wave * PER + i) * 1024;
+    const int p = p0 + 16 * lane;
+    const int row = p / ROWB, cs = (p % ROWB) / 16;
+    const int c = cs ^ swz<ROWB>(row);
+    const uint16_t* src = base + (size_t)(r0 + swap_bits23(row)) * D + 8 * c;
+    __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(lds + p0), 16, 0, 0);
+  }
+}
+// Same for a transposed tile [D][64] of a [D][Lp] block (columns c0 .. c0+63).
+template <int D, int NW>
+__device__ __forceinline__ void load_cols_tile(const uint16_t* base, int Lp, int c0, uint8_t* lds,
+                                               int wave, int lane) {
+  constexpr int ROWB = TILE * 2, BYTES = D * ROWB, PER = BYTES / (1024 * NW);
+  static_assert(PER * 1024 * NW == BYTES, "column tile split");
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int p0 = (wave * PER + i) * 1024;
+    const int p = p0 + 16 * lane;
+    const int row = p / ROWB, cs = (p % ROWB) / 16;
+    const int c = cs ^ swz<ROWB>(row);
+    const uint16_t* src = base + (size_t)row * Lp + c0 + 8 * c;
+    __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(lds + p0), 16, 0, 0);
+  }
+}
+// A operand (16 bytes) of a row tile: row `row`, chunk ch.
+template <int ROWB>
+__device__ __forceinline__ bf16x8 lds_op(const uint8_t* t, int row, int ch) {
+  return *reinterpret_cast<const bf16x8*>(t + row * ROWB + ((ch ^ swz<ROWB>(row)) << 4));
+}
+
+// Epilogue helper: gradient rows of rotated tensors.  acc[db][r] holds
+// dx~[d] / mul for d = 32 db + 8 (r / 4) + 4 hf + r % 4 of this lane's token;
+// xr is the bf16 operand row the products used (x~ times xmul), th the
+// token's angles.  Writes dx = R^T dx~ (or dx~) as bf16; when rot, adds
+// <dx~, J x~> to dth (per pair), with the same x~ the products used, so that
+// the sum over tokens cancels as it does for the exact gradient.
+template <int DB>
+__device__ __forceinline__ void grad_rows(const f32x16 (&acc)[DB], float mul, const uint16_t* xr,
+                                          float xmul, const float* th, bool rot, uint16_t* out,
+                                          float* dth, int hf) {
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = 32 * db + 8 * j + 4 * hf;
+      float g0 = acc[db][4 * j + 0] * mul, g1 = acc[db][4 * j + 1] * mul;
+      float g2 = acc[db][4 * j + 2] * mul, g3 = acc[db][4 * j + 3] * mul;
+      if (rot) {
+        const u32x2 xw = *reinterpret_cast<const u32x2*>(xr + d0);
+        const float2 a = *reinterpret_cast<const float2*>(th + d0 / 2);
+        float s0, c0, s1, c1;
+        sincosf(a.x, &s0, &c0);
+        sincosf(a.y, &s1, &c1);
+        const float x0 = lo_bf16(xw[0]) * xmul, x1 = hi_bf16(xw[0]) * xmul;
+        const float x2 = lo_bf16(xw[1]) * xmul, x3 = hi_bf16(xw[1]) * xmul;
+        float2 acc_th = *reinterpret_cast<float2*>(dth + d0 / 2);
+        acc_th.x += -g0 * x1 + g1 * x0;
+        acc_th.y += -g2 * x3 + g3 * x2;
+        *reinterpret_cast<float2*>(dth + d0 / 2) = acc_th;
+        rotate_pair(g0, g1, c0, -s0);
+        rotate_pair(g2, g3, c1, -s1);
+      }
+      u32x2 w = {pack_bf16x2(g0, g1), pack_bf16x2(g2, g3)};
+      *reinterpret_cast<u32x2*>(out + d0) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK, dV (key-stationary)
+// ---------------------------------------------------------------------------
+template <int D, int NW, bool ALIBI>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
+    BwdOperands ops, const float* __restrict__ theta, const float* __restrict__ alibi,
+    uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, float* __restrict__ dtheta, int L, int Lp, int H, int Hphi, int nkt,
+    int total_tiles, uint32_t flags) {
+  constexpr int BK = 32 * NW;  // keys per workgroup
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int ROWB = D * 2, RT = TILE * ROWB;     // row tile bytes
+  constexpr int COLB = TILE * 2, CT = D * COLB;     // column tile bytes
+  constexpr int STAGE = 2 * RT + 2 * CT + 2 * TILE * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int per = (total_tiles + 7) / 8;
+  const int logical = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (logical >= total_tiles) return;
+  const int bh = logical / nkt;
+  const int kt = logical % nkt;  // ascending: the longest query ranges first
+  const int K0 = kt * BK;
+  const int b = bh / H, h = bh % H;
+  const int g = (Hphi == 1) ? 0 : h;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 31, hf = lane >> 5;
+  const int kw = K0 + 32 * wave;  // this wave's first key
+  const int j = kw + ln;          // this lane's key
+  const int first_tile = K0 / TILE;
+  const int last_tile = (L - 1) / TILE;
+  const size_t rm = (size_t)bh * Lp * D, tb = (size_t)bh * D * Lp;
+  const float* stats_bh = ops.stats + (size_t)bh * (Lp / TILE) * (2 * TILE);
+
+  auto issue = [&](int t, uint8_t* st) __attribute__((always_inline)) {
+    load_rows_tile<D, NW>(ops.qs + rm, t * TILE, st, wave, lane);
+    load_rows_tile<D, NW>(ops.dout + rm, t * TILE, st + RT, wave, lane);
+    load_cols_tile<D, NW>(ops.qsT + tb, Lp, t * TILE, st + 2 * RT, wave, lane);
+    load_cols_tile<D, NW>(ops.doutT + tb, Lp, t * TILE, st + 2 * RT + CT, wave, lane);
+    if (wave == 0 && lane < 32)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(stats_bh + (size_t)t * 2 * TILE + 4 * lane),
+                                       (lds_void_ptr)(st + 2 * RT + 2 * CT), 16, 0, 0);
+  };
+
+  // B operands: this lane's key row of k~ and v~ (d = 16 ks + 8 hf .. +7)
+  bf16x8 kop[KS], vop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const size_t off = rm + (size_t)min(j, Lp - 1) * D + 16 * ks + 8 * hf;
+    kop[ks] = *reinterpret_cast<const bf16x8*>(ops.k + off);
+    vop[ks] = *reinterpret_cast<const bf16x8*>(ops.v + off);
+  }
+  f32x16 dkt[DB], dvt[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dkt[db][r] = dvt[db][r] = 0.f;
+  const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
+
+  if (first_tile <= last_tile) issue(first_tile, smem);
+  for (int t = first_tile; t <= last_tile; ++t) {
+    uint8_t* st = smem + ((t - first_tile) & 1) * STAGE;
+    wait_loads<0>();
+    __builtin_amdgcn_s_barrier();
+    if (t + 1 <= last_tile) issue(t + 1, smem + ((t + 1 - first_tile) & 1) * STAGE);
+    const uint8_t* tq = st;
+    const uint8_t* tdo = st + RT;
+    const uint8_t* tqT = st + 2 * RT;
+    const uint8_t* tdoT = st + 2 * RT + CT;
+    const float* sl = reinterpret_cast<const float*>(st + 2 * RT + 2 * CT);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qbase = t * TILE + 32 * qb;
+      if (qbase + 31 < kw) continue;  // every query of the block precedes every key of the wave
+      // -lse and -D of the rows of this lane's accumulator elements
+      f32x16 cl, cd;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int ro = 32 * qb + 16 * h2 + 8 * hf;
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(sl + ro);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(sl + ro + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(sl + TILE + ro);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(sl + TILE + ro + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          cl[8 * h2 + e] = -l0[e];
+          cl[8 * h2 + 4 + e] = -l1[e];
+          cd[8 * h2 + e] = -d0[e];
+          cd[8 * h2 + 4 + e] = -d1[e];
+        }
+      }
+      f32x16 s = cl, dp = cd;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(lds_op<ROWB>(tq, 32 * qb + ln, 2 * ks + hf), kop[ks], s);
+        dp = mfma32(lds_op<ROWB>(tdo, 32 * qb + ln, 2 * ks + hf), vop[ks], dp);
+      }
+      const bool diag = (qbase == kw);
+      bf16x8 pop[2], dsop[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        uint32_t wp[4], wd[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 8 * h2 + 2 * e + u;
+            const int i = qbase + 16 * h2 + 8 * hf + 2 * e + u;  // query of element r
+            float sv = s[r];
+            if (ALIBI) sv += slope2 * (float)(j - i);
+            if (diag && j > i) sv = -INFINITY;
+            x[u] = __builtin_amdgcn_exp2f(sv);
+          }
+          wp[e] = pack_bf16x2(x[0], x[1]);
+          wd[e] = pack_bf16x2(x[0] * dp[8 * h2 + 2 * e], x[1] * dp[8 * h2 + 2 * e + 1]);
+        }
+        u32x4 a = {wp[0], wp[1], wp[2], wp[3]}, c = {wd[0], wd[1], wd[2], wd[3]};
+        pop[h2] = __builtin_bit_cast(bf16x8, a);
+        dsop[h2] = __builtin_bit_cast(bf16x8, c);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int ch = 4 * qb + 2 * h2 + hf;
+          dvt[db] = mfma32(lds_op<COLB>(tdoT, 32 * db + ln, ch), pop[h2], dvt[db]);
+          dkt[db] = mfma32(lds_op<COLB>(tqT, 32 * db + ln, ch), dsop[h2], dkt[db]);
+        }
+    }
+  }
+
+  if (j >= L) return;
+  const size_t row = ((size_t)bh * L + j) * D;
+  const uint16_t* oprow = ops.k + rm + (size_t)j * D;
+  const float* th = theta + ((size_t)(b * Hphi + g) * L + j) * (D / 2);
+  float* dth = dtheta + ((size_t)bh * L + j) * (D / 2);
+  // dk~ = scale sum dS q~ = ln 2 * (Q~s^T dS) since q~s carries scale log2 e
+  grad_rows<DB>(dkt, 0.69314718055994531f, oprow, 1.f, th, (flags & ARP_ROTATE_QK) != 0,
+                dk + row, dth, hf);
+  grad_rows<DB>(dvt, 1.f, ops.v + rm + (size_t)j * D, 1.f, th, (flags & ARP_ROTATE_V) != 0,
+                dv + row, dth, hf);
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ (query-stationary)
+// ---------------------------------------------------------------------------
+template <int D, int NW, bool ALIBI>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
+    BwdOperands ops, const float* __restrict__ theta, const float* __restrict__ alibi,
+    uint16_t* __restrict__ dq, float* __restrict__ dtheta, int L, int Lp, int H, int Hphi, int nqt,
+    int total_tiles, uint32_t flags, float scale) {
+  constexpr int BM = 32 * NW;
+  constexpr int KS = D / 16, DB = D / 32, KB = 2, KS2 = 4;
+  constexpr int ROWB = D * 2, RT = TILE * ROWB;
+  constexpr int COLB = TILE * 2, CT = D * COLB;
+  constexpr int STAGE = 2 * RT + CT;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int per = (total_tiles + 7) / 8;
+  const int logical = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (logical >= total_tiles) return;
+  const int bh = logical / nqt;
+  const int qt = nqt - 1 - logical % nqt;  // longest first
+  const int q0 = qt * BM;
+  const int b = bh / H, h = bh % H;
+  const int g = (Hphi == 1) ? 0 : h;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 31, hf = lane >> 5;
+  const int qw = q0 + 32 * wave;
+  const int i = qw + ln;  // this lane's query
+  const int last_tile = min(q0 + BM - 1, L - 1) / TILE;
+  const int last_w = (qw < L) ? min(qw + 31, L - 1) / TILE : -1;
+  const size_t rm = (size_t)bh * Lp * D, tb = (size_t)bh * D * Lp;
+
+  auto issue = [&](int t, uint8_t* st) __attribute__((always_inline)) {
+    load_rows_tile<D, NW>(ops.k + rm, t * TILE, st, wave, lane);
+    load_rows_tile<D, NW>(ops.v + rm, t * TILE, st + RT, wave, lane);
+    load_cols_tile<D, NW>(ops.kT + tb, Lp, t * TILE, st + 2 * RT, wave, lane);
+  };
+
+  bf16x8 qop[KS], doop[KS];
+  const int ic = min(i, Lp - 1);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const size_t off = rm + (size_t)ic * D + 16 * ks + 8 * hf;
+    qop[ks] = *reinterpret_cast<const bf16x8*>(ops.qs + off);
+    doop[ks] = *reinterpret_cast<const bf16x8*>(ops.dout + off);
+  }
+  const float* srow = ops.stats + ((size_t)bh * (Lp / TILE) + ic / TILE) * (2 * TILE);
+  const float nl = -srow[ic % TILE], nd = -srow[TILE + ic % TILE];
+  f32x16 cl, cd, dqt[DB];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    cl[r] = nl;
+    cd[r] = nd;
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
+  const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
+
+  issue(0, smem);
+  for (int n = 0; n <= last_tile; ++n) {
+    uint8_t* st = smem + (n & 1) * STAGE;
+    wait_loads<0>();
+    __builtin_amdgcn_s_barrier();
+    if (n + 1 <= last_tile) issue(n + 1, smem + ((n + 1) & 1) * STAGE);
+    if (n > last_w) continue;
+    const uint8_t* tk = st;
+    const uint8_t* tv = st + RT;
+    const uint8_t* tkT = st + 2 * RT;
+    const bool diag = (n == last_w);
+    bf16x8 dsop[KS2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x16 s = cl, dp = cd;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(lds_op<ROWB>(tk, 32 * kb + ln, 2 * ks + hf), qop[ks], s);
+        dp = mfma32(lds_op<ROWB>(tv, 32 * kb + ln, 2 * ks + hf), doop[ks], dp);
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 8 * h2 + 2 * e + u;
+            const int jj = n * TILE + 32 * kb + 16 * h2 + 8 * hf + 2 * e + u;  // key of element r
+            float sv = s[r];
+            if (ALIBI) sv += slope2 * (float)(jj - i);
+            if (diag && jj > i) sv = -INFINITY;
+            x[u] = __builtin_amdgcn_exp2f(sv) * dp[r];
+          }
+          wd[e] = pack_bf16x2(x[0], x[1]);
+        }
+        u32x4 c = {wd[0], wd[1], wd[2], wd[3]};
+        dsop[2 * kb + h2] = __builtin_bit_cast(bf16x8, c);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ks2 = 0; ks2 < KS2; ++ks2)
+        dqt[db] = mfma32(lds_op<COLB>(tkT, 32 * db + ln, 2 * ks2 + hf), dsop[ks2], dqt[db]);
+  }
+
+  if (i >= L) return;
+  const size_t row = ((size_t)bh * L + i) * D;
+  const float* th = theta + ((size_t)(b * Hphi + g) * L + i) * (D / 2);
+  float* dth = dtheta + ((size_t)bh * L + i) * (D / 2);
+  // q~ = q~s / (scale log2 e)
+  grad_rows<DB>(dqt, scale, ops.qs + rm + (size_t)i * D, 1.f / (scale * LOG2E), th,
+                (flags & ARP_ROTATE_QK) != 0, dq + row, dth, hf);
+}
+
+// ---------------------------------------------------------------------------
+// 4. reverse scan: dphi[b, g, s, p] = sum_{h in g} sum_{t >= s} dTheta[b, h, t, p]
+// ---------------------------------------------------------------------------
+constexpr int RCH = 256;  // tokens per chunk
+
+// chunk totals (summed over the heads of the stream)
+template <int P>
+__global__ __launch_bounds__(256) void rscan_totals_kernel(const float* __restrict__ dtheta,
+                                                           float* __restrict__ totals, int L,
+                                                           int H, int Hphi, int nch) {
+  constexpr int G = 256 / P;
+  __shared__ float part[G][P];
+  const int c = blockIdx.x, bg = blockIdx.y;
+  const int b = bg / Hphi, gg = bg % Hphi;
+  const int p = threadIdx.x % P, rg = threadIdx.x / P;
+  const int hn = (Hphi == 1) ? H : 1;
+  float acc = 0.f;
+  for (int hh = 0; hh < hn; ++hh) {
+    const int h = (Hphi == 1) ? hh : gg;
+    const float* src = dtheta + ((size_t)(b * H + h) * L) * P;
+    for (int t = c * RCH + rg; t < min(L, (c + 1) * RCH); t += G) acc += src[(size_t)t * P + p];
+  }
+  part[rg][p] = acc;
+  __syncthreads();
+  if (rg == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < G; ++r) s += part[r][p];
+    totals[((size_t)bg * nch + c) * P + p] = s;
+  }
+}
+
+// totals -> suffix offsets (sum of the chunks after each chunk), in place
+__global__ __launch_bounds__(256) void rscan_offsets_kernel(float* __restrict__ totals, int nch,
+                                                            int P, int nseg) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nseg * P) return;
+  const int bg = idx / P, p = idx % P;
+  float run = 0.f;
+  for (int c = nch - 1; c >= 0; --c) {
+    float* x = totals + ((size_t)bg * nch + c) * P + p;
+    const float tot = *x;
+    *x = run;
+    run += tot;
+  }
+}
+
+template <int P>
+__global__ __launch_bounds__(256) void rscan_apply_kernel(const float* __restrict__ dtheta,
+                                                          const float* __restrict__ offsets,
+                                                          float* __restrict__ dphi, int L, int H,
+                                                          int Hphi, int nch, int exclusive) {
+  constexpr int G = 256 / P, R = RCH / G;  // each thread: R consecutive tokens of one pair
+  __shared__ float run_tot[G][P];
+  const int c = blockIdx.x, bg = blockIdx.y;
+  const int b = bg / Hphi, gg = bg % Hphi;
+  const int p = threadIdx.x % P, rg = threadIdx.x / P;
+  const int hn = (Hphi == 1) ? H : 1;
+  const int t0 = c * RCH + rg * R;
+  float x[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = 0.f;
+  for (int hh = 0; hh < hn; ++hh) {
+    const int h = (Hphi == 1) ? hh : gg;
+    const float* src = dtheta + ((size_t)(b * H + h) * L) * P;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (t0 + r < L) x[r] += src[(size_t)(t0 + r) * P + p];
+  }
+  float tot = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) tot += x[r];
+  run_tot[rg][p] = tot;
+  __syncthreads();
+  float off = offsets[((size_t)bg * nch + c) * P + p];
+  for (int r2 = rg + 1; r2 < G; ++r2) off += run_tot[r2][p];
+  float* dst = dphi + ((size_t)bg * L) * P;
+  float run = off;
+#pragma unroll
+  for (int r = R - 1; r >= 0; --r) {
+    const float xr = x[r];
+    if (!exclusive) run += xr;
+    if (t0 + r < L) dst[(size_t)(t0 + r) * P + p] = run;
+    if (exclusive) run += xr;
+  }
+}
+
+template <int D, int NW>
+hipError_t launch_bwd_d(const Geometry& g, const BwdArgs& a, hipStream_t stream) {
+  const uint32_t fl = g.flags;
+  const bool al = (fl & ARP_ALIBI) != 0;
+  {
+    dim3 grid(g.Lp / TILE, g.B * g.H);
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), grid, dim3(256), 0, stream, a.q, a.k, a.v, a.o, a.dout,
+                       a.theta, a.lse, a.ops, a.dtheta, g.L, g.Lp, g.H, g.Hphi, fl, g.scale * LOG2E);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int nkt = (g.L + 32 * NW - 1) / (32 * NW);
+    const int total = g.B * g.H * nkt;
+    const int grid = ((total + 7) / 8) * 8;
+    if (al)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, true>), dim3(grid), dim3(NW * 64), 0, stream, a.ops,
+                         a.theta, a.alibi, a.dk, a.dv, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nkt, total,
+                         fl);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, false>), dim3(grid), dim3(NW * 64), 0, stream,
+                         a.ops, a.theta, a.alibi, a.dk, a.dv, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nkt,
+                         total, fl);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int nqt = (g.L + 32 * NW - 1) / (32 * NW);
+    const int total = g.B * g.H * nqt;
+    const int grid = ((total + 7) / 8) * 8;
+    if (al)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, NW, true>), dim3(grid), dim3(NW * 64), 0, stream, a.ops,
+                         a.theta, a.alibi, a.dq, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nqt, total, fl,
+                         g.scale);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, NW, false>), dim3(grid), dim3(NW * 64), 0, stream, a.ops,
+                         a.theta, a.alibi, a.dq, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nqt, total, fl,
+                         g.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int P>
+hipError_t launch_rscan(const Geometry& g, const float* dtheta, float* totals, float* dphi,
+                        hipStream_t stream) {
+  const int nch = (g.L + RCH - 1) / RCH;
+  const int nseg = g.B * g.Hphi;
+  hipLaunchKernelGGL((rscan_totals_kernel<P>), dim3(nch, nseg), dim3(256), 0, stream, dtheta,
+                     totals, g.L, g.H, g.Hphi, nch);
+  hipLaunchKernelGGL(rscan_offsets_kernel, dim3((nseg * P + 255) / 256), dim3(256), 0, stream,
+                     totals, nch, P, nseg);
+  hipLaunchKernelGGL((rscan_apply_kernel<P>), dim3(nch, nseg), dim3(256), 0, stream, dtheta,
+                     totals, dphi, g.L, g.H, g.Hphi, nch, (g.flags & ARP_SCAN_EXCLUSIVE) ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_bf16(const Geometry& g, const BwdArgs& a, hipStream_t stream) {
+  hipError_t e = (g.D == 64) ? launch_bwd_d<64, 8>(g, a, stream) : launch_bwd_d<128, 4>(g, a, stream);
+  if (e != hipSuccess) return e;
+  return (g.P == 32) ? launch_rscan<32>(g, a.dtheta, a.totals, a.dphi, stream)
+                     : launch_rscan<64>(g, a.dtheta, a.totals, a.dphi, stream);
+}
+
+}  // namespace arp

@@ -114,9 +114,12 @@ size_t arp_scan_state_bytes(const arp_desc* desc);
 size_t arp_workspace_bytes(const arp_desc* desc);
 
 /* a1. Accumulated angles: theta[b,g,t,p] = wrap(sum_{s<=t} phi[b,g,s,p]) in
- * [-pi, pi) (exclusive sum with ARP_SCAN_EXCLUSIVE).  Compensated fp32
- * (two-float) prefix sum, single pass with chained look-back across chunks of
- * the sequence.  Method: Sec. 5 "SO(2) notation" and eq. (6). */
+ * [-pi, pi) (exclusive sum with ARP_SCAN_EXCLUSIVE).  Each fp32 step is
+ * converted to 48-bit fixed-point turns and summed exactly as integers (the
+ * wrap is the integer overflow), single pass with chained look-back across
+ * chunks of the sequence; each output is the correctly rounded fp32 of a sum
+ * within 2^-48 turn of the exact one.  Method: Sec. 5 "SO(2) notation" and
+ * eq. (6). */
 arp_status arp_angle_scan(const arp_desc* desc, const float* phi, float* theta, void* scan_state,
                           size_t scan_state_bytes, void* stream);
 
@@ -148,6 +151,39 @@ arp_status arp_forward(const arp_desc* desc, const void* q, const void* k, const
                        const float* phi, const float* alibi, float* theta, void* o,
                        void* scan_state, size_t scan_state_bytes, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* Training forward (bf16, pre-rotation path): arp_forward that also writes
+ * lse[b,h,i] (float32 [batch, heads, seqlen]), the base-2 log-sum-exp of row
+ * i's scaled logits: log2 sum_{j<=i} 2^(log2(e) s_ij).  The backward pass
+ * recomputes the softmax from it.  ARP_ERR_UNSUPPORTED for fp32 I/O or
+ * ARP_FUSED_ROTATION. */
+arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k, const void* v,
+                             const float* phi, const float* alibi, float* theta, void* o,
+                             float* lse, void* scan_state, size_t scan_state_bytes,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the backward workspace for desc (bf16 only; 0 otherwise): the bf16
+ * operands of the gradient kernels (rotated q scaled by scale*log2(e), k, v
+ * and the rotated upstream gradient, row-major and transposed), per-row
+ * statistics, and the reverse scan's chunk totals.  No initialisation needed. */
+size_t arp_backward_workspace_bytes(const arp_desc* desc);
+
+/* Gradients (bf16): given the forward's inputs, theta, o and lse (from
+ * arp_forward_train, same desc) and the upstream gradient dout = dL/do
+ * ([batch, heads, seqlen, head_dim], bf16), writes
+ *   dq, dk, dv  bf16 [batch, heads, seqlen, head_dim]
+ *   dtheta      float32 [batch, heads, seqlen, head_dim/2]: dL/dTheta per head
+ *   dphi        float32, phi's layout: dL/dphi_s = sum over t >= s (t > s with
+ *               ARP_SCAN_EXCLUSIVE) of dL/dTheta_t, summed over the heads that
+ *               share an angle stream.
+ * The chain rule through eq. (2)-(4), (6)-(8) and the rotation AdaRoPE
+ * Sec. 2.1 eq. (1) defines (dR/da = R J, J = [[0,-1],[1,0]]); the wrap into
+ * [-pi, pi) has derivative 1.  The ALiBi slopes and the scale are constants.
+ * ARP_ERR_UNSUPPORTED for fp32 I/O; ARP_FUSED_ROTATION is ignored. */
+arp_status arp_backward(const arp_desc* desc, const void* q, const void* k, const void* v,
+                        const float* theta, const float* alibi, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, float* dtheta,
+                        float* dphi, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Diagnostic: out = R(theta) x (or R(theta)^T x when inverse != 0) in fp32.
  * x has the desc's dtype and q's layout; out is float32 of the same shape. */
