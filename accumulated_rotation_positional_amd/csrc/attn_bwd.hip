@@ -32,8 +32,8 @@
 //     dS^T = P^T * dP'^T, dQ^T += K~^T dS^T.
 //  Both kernels end with the un-rotation of their gradients and add their
 //  <dx~, J x~> terms to dTheta (each (t, p) owned by one lane).
-//  4. reverse scan of dTheta into dphi: chunk totals, suffix offsets of the
-//     chunks, then the in-chunk suffix sums.
+//  4. reverse scan of dTheta into dphi: chunk totals, then the in-chunk
+//     suffix sums plus the totals of the later chunks.
 #include <type_traits>
 
 #include "arp_device.hpp"
@@ -526,24 +526,11 @@ __global__ __launch_bounds__(256) void rscan_totals_kernel(const float* __restri
   }
 }
 
-// totals -> suffix offsets (sum of the chunks after each chunk), in place
-__global__ __launch_bounds__(256) void rscan_offsets_kernel(float* __restrict__ totals, int nch,
-                                                            int P, int nseg) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= nseg * P) return;
-  const int bg = idx / P, p = idx % P;
-  float run = 0.f;
-  for (int c = nch - 1; c >= 0; --c) {
-    float* x = totals + ((size_t)bg * nch + c) * P + p;
-    const float tot = *x;
-    *x = run;
-    run += tot;
-  }
-}
-
+// In-chunk suffix sums plus the totals of every later chunk (read directly:
+// at most a few hundred coalesced loads per thread, no separate pass).
 template <int P>
 __global__ __launch_bounds__(256) void rscan_apply_kernel(const float* __restrict__ dtheta,
-                                                          const float* __restrict__ offsets,
+                                                          const float* __restrict__ totals,
                                                           float* __restrict__ dphi, int L, int H,
                                                           int Hphi, int nch, int exclusive) {
   constexpr int G = 256 / P, R = RCH / G;  // each thread: R consecutive tokens of one pair
@@ -566,9 +553,18 @@ __global__ __launch_bounds__(256) void rscan_apply_kernel(const float* __restric
   float tot = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) tot += x[r];
+  // chunks after this one: the G threads of a pair split them
+  float later = 0.f;
+  for (int c2 = c + 1 + rg; c2 < nch; c2 += G) later += totals[((size_t)bg * nch + c2) * P + p];
+  __syncthreads();
+  run_tot[rg][p] = later;
+  __syncthreads();
+  float off = 0.f;
+#pragma unroll
+  for (int r2 = 0; r2 < G; ++r2) off += run_tot[r2][p];
+  __syncthreads();
   run_tot[rg][p] = tot;
   __syncthreads();
-  float off = offsets[((size_t)bg * nch + c) * P + p];
   for (int r2 = rg + 1; r2 < G; ++r2) off += run_tot[r2][p];
   float* dst = dphi + ((size_t)bg * L) * P;
   float run = off;
@@ -632,8 +628,6 @@ hipError_t launch_rscan(const Geometry& g, const float* dtheta, float* totals, f
   const int nseg = g.B * g.Hphi;
   hipLaunchKernelGGL((rscan_totals_kernel<P>), dim3(nch, nseg), dim3(256), 0, stream, dtheta,
                      totals, g.L, g.H, g.Hphi, nch);
-  hipLaunchKernelGGL(rscan_offsets_kernel, dim3((nseg * P + 255) / 256), dim3(256), 0, stream,
-                     totals, nch, P, nseg);
   hipLaunchKernelGGL((rscan_apply_kernel<P>), dim3(nch, nseg), dim3(256), 0, stream, dtheta,
                      totals, dphi, g.L, g.H, g.Hphi, nch, (g.flags & ARP_SCAN_EXCLUSIVE) ? 1 : 0);
   return hipGetLastError();

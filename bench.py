@@ -158,6 +158,41 @@ def scan_gate(binding, torch, dev, steps: int = 30) -> dict:
             "us_per_launch": round(ms * 1e3, 2), "bytes_per_launch": nbytes}
 
 
+def backward_leg(binding, torch, dev, w, q, k, v, phi, alibi, steps: int = 20) -> dict:
+    """The training step's backward on the same workload: the training forward
+    (which also writes the per-row log-sum-exp) once, then the backward timed
+    alone (prep, dK/dV, dQ and the reverse angle scan: one C-ABI call) between
+    events on its stream.  Rate: the conventional 2.5x the forward's
+    algorithmic flops (the five products per causal pair: S recomputed, dP,
+    dV, dK, dQ) against the bf16 matrix-core peak."""
+    if w.dtype != "bf16":
+        return None
+    o, theta, lse, desc = binding.forward_train(q, k, v, phi, rotate_qk=True,
+                                                rotate_v=w.rotate_v, alibi=alibi)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    dout = torch.randn(q.shape, device=dev, generator=g).to(torch.bfloat16)
+    stream = torch.cuda.current_stream(dev)
+    ws = binding.backward_workspace(desc, dev)
+    for _ in range(5):
+        binding.backward(desc, q, k, v, phi, theta, o, lse, dout, alibi=alibi, ws=ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        binding.backward(desc, q, k, v, phi, theta, o, lse, dout, alibi=alibi, ws=ws)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+    flops = 2.5 * w.flops
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "ms": round(ms, 4), "algorithmic_flops": flops,
+            "bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "outputs": "dq, dk, dv (bf16), dtheta, dphi (fp32)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -278,6 +313,8 @@ def main():
                           "traffic": scan_traffic},
     }
     result["scan_hbm_gate"] = scan_gate(binding, torch, dev)
+    if not args.fused:
+        result["backward"] = backward_leg(binding, torch, dev, w, q, k, v, phi, alibi)
     if not args.no_cpu_baseline:
         import oracle
         of = (oracle.ROTATE_QK | (oracle.ROTATE_V if w.rotate_v else 0) |
