@@ -36,7 +36,7 @@ EXPORTS = ("arp_abi_version", "arp_status_string", "arp_check", "arp_scan_state_
            "arp_workspace_bytes",
            "arp_angle_scan", "arp_rotate_qkv", "arp_attn_rotated", "arp_attn_fwd",
            "arp_forward", "arp_rotate", "arp_forward_train", "arp_backward_workspace_bytes",
-           "arp_backward")
+           "arp_backward", "arp_decode_workspace_bytes", "arp_decode_prefill", "arp_decode_step")
 
 
 class ArpError(RuntimeError):
@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
                 "arp_forward_train": ([D, P, P, P, P, P, P, P, P, P, S, P, S, P], ctypes.c_int),
                 "arp_backward_workspace_bytes": ([D], S),
                 "arp_backward": ([D] + [P] * 14 + [S, P], ctypes.c_int),
+                "arp_decode_workspace_bytes": ([D], S),
+                "arp_decode_prefill": ([D, ctypes.c_int32] + [P] * 7 + [P], ctypes.c_int),
+                "arp_decode_step": ([D, ctypes.c_int32] + [P] * 11 + [S, P], ctypes.c_int),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -299,3 +302,45 @@ def backward(desc: Desc, q, k, v, phi, theta, o, lse, dout, alibi=None, ws=None)
         _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtheta), _ptr(dphi),
         _ptr(ws), ws.numel(), _stream(q.device)))
     return dq, dk, dv, dphi, dtheta
+
+
+class DecodeCache:
+    """Key/value cache (pre-rotated bf16 [B, H, capacity, d]), the angle state
+    (uint64 [B, Hphi, d/2]) and the step workspace of one decoding stream."""
+
+    def __init__(self, batch: int, heads: int, capacity: int, head_dim: int, *, phi_heads=None,
+                 rotate_qk: bool = True, rotate_v: bool = False, alibi: bool = False,
+                 exclusive: bool = False, scale: float | None = None,
+                 device: torch.device = torch.device("cuda:0")):
+        hphi = heads if phi_heads is None else phi_heads
+        flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi,
+                          shared_phi=hphi == 1 and heads != 1, exclusive=exclusive)
+        self.desc = make_desc(batch, heads, capacity, head_dim, torch.bfloat16, flags, scale)
+        self.device = device
+        self.kcache = torch.zeros(batch, heads, capacity, head_dim, dtype=torch.bfloat16, device=device)
+        self.vcache = torch.zeros_like(self.kcache)
+        self.state = torch.zeros(batch, hphi, head_dim // 2, dtype=torch.int64, device=device)
+        self.theta = torch.zeros(batch, hphi, head_dim // 2, dtype=torch.float32, device=device)
+        nbytes = max(int(lib().arp_decode_workspace_bytes(ctypes.byref(self.desc))), 256)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+    def prefill(self, k=None, v=None, phi=None, theta=None) -> None:
+        """Cache rows [0, len) and the state after the len prompt tokens
+        (k, v [B, H, len, d]; phi, theta [B, Hphi, len, d/2]); no arguments:
+        an empty prompt (state reset)."""
+        _require_gpu(k, v, phi, theta)
+        n = 0 if k is None else int(k.shape[2])
+        _check("arp_decode_prefill", lib().arp_decode_prefill(
+            ctypes.byref(self.desc), n, _ptr(k), _ptr(v), _ptr(phi), _ptr(theta),
+            _ptr(self.kcache), _ptr(self.vcache), _ptr(self.state), _stream(self.device)))
+
+    def step(self, pos: int, q, k, v, phi, alibi=None, out=None) -> torch.Tensor:
+        """One token at position pos: q, k, v [B, H, d]; phi [B, Hphi, d/2].
+        Returns o [B, H, d]; self.theta holds the token's angles."""
+        _require_gpu(q, k, v, phi, alibi, out)
+        out = torch.empty_like(q) if out is None else out
+        _check("arp_decode_step", lib().arp_decode_step(
+            ctypes.byref(self.desc), int(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(phi), _ptr(alibi),
+            _ptr(self.state), _ptr(self.theta), _ptr(self.kcache), _ptr(self.vcache), _ptr(out),
+            _ptr(self.ws), self.ws.numel(), _stream(self.device)))
+        return out

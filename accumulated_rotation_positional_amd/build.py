@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 TARGET = os.path.join(HERE, "libarp.so")
-SOURCES = ["api.hip", "angle_scan.hip", "rotate.hip", "attn_f32.hip", "attn_bf16.hip", "attn_bwd.hip"]
+SOURCES = ["api.hip", "angle_scan.hip", "rotate.hip", "attn_f32.hip", "attn_bf16.hip", "attn_bwd.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

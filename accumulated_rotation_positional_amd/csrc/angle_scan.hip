@@ -52,6 +52,7 @@
 // and records how many words it dirtied.  The next launch on the stream sees all of it at the kernel
 // boundary.  A buffer zero-filled once therefore serves any number of calls
 // of any size that fits it.
+#include "angle_fixed.hpp"
 #include "arp_device.hpp"
 #include "arp_internal.hpp"
 
@@ -63,9 +64,6 @@ constexpr int SCAN_THREADS = 256;
 constexpr int FALLBACK_POLLS = 256;  // polls of an unpublished word before reducing it here
 constexpr int GROUP = 16;            // workgroups per completion counter
 constexpr uint64_t ST_AGG = 1, ST_INC = 2, ST_MASK = 3;
-constexpr uint64_t MASK48 = (1ull << 48) - 1;
-constexpr double INV_2PI = 0.15915494309189533577;
-constexpr double TWO_PI = 6.28318530717958647693;
 
 // Header of the state buffer, padded to 256 bytes so that every 128-byte
 // cache line of the status words belongs to exactly one half (the halves are
@@ -84,30 +82,6 @@ static_assert(sizeof(ScanHeader) == 256, "header size");
 // a layout that does not depend on the problem's shape.
 __device__ __forceinline__ size_t phys_word(size_t w, uint32_t h) {
   return ((w >> 5) * 2 + h) * 32 + (w & 31);
-}
-
-// Radians (fp32) -> fixed-point turns, low 48 bits meaningful.
-// n is the nearest whole number of turns; fma(a, 1/(2 pi), 24 - n) rounds
-// a / (2 pi) - n + 24 once, to a multiple of 2^-48 (the result lies in
-// [23.5, 24.5], so its exponent is that of 16), and the low 48 mantissa bits
-// are the fraction of the turn.  Branch-free and exact in n for any finite
-// angle below 2^50 turns.
-__device__ __forceinline__ uint64_t to_fixed(float a) {
-#pragma clang fp contract(off)
-  const double x = (double)a;
-  const double n = __builtin_rint(x * INV_2PI);
-  const double y = __builtin_fma(x, INV_2PI, 24.0 - n);
-  return (uint64_t)__double_as_longlong(y) & MASK48;
-}
-
-// Fixed-point turns (already offset by 2^47) -> radians in [-pi, pi).
-// The 48 bits become the mantissa of a double in [16, 17); subtracting 16.5
-// is exact and yields the signed turn in [-1/2, 1/2).
-__device__ __forceinline__ float to_radians_offset(uint64_t u) {
-#pragma clang fp contract(off)
-  const uint64_t bits = (0x4030000000000000ull) | (u & MASK48);
-  const double z = __longlong_as_double((long long)bits) - 16.5;
-  return (float)(z * TWO_PI);
 }
 
 __device__ __forceinline__ uint64_t shfl_up64(uint64_t v, int delta) {
@@ -296,7 +270,7 @@ __global__ __launch_bounds__(SCAN_THREADS, MINB) void angle_scan_kernel(
       acc = look_back<P>(words, wbase, half, chunk, seg_phi, L, CH, lane);
       if (lane < P) publish(my, acc + agg, ST_INC);
     }
-    if (lane < P) s_carry[p] = acc + (1ull << 47);  // turns [0,1) into [-1/2,1/2) below
+    if (lane < P) s_carry[p] = acc + FIXED_ZERO;  // turns [0,1) into [-1/2,1/2) below
   }
   __syncthreads();
 

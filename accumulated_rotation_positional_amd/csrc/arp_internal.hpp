@@ -92,4 +92,21 @@ struct BwdWorkspaceLayout {
 BwdWorkspaceLayout bwd_workspace_layout(const Geometry& g);
 hipError_t launch_backward_bf16(const Geometry& g, const BwdArgs& a, hipStream_t stream);
 
+// ---- decode (bf16; Geometry.L is the cache capacity) ------------------------
+struct DecodeArgs {
+  int pos;                      // position of the new token (cache rows 0..pos attended)
+  const uint16_t *q, *k, *v;    // [B, H, D] the new token
+  const float *phi, *alibi;     // phi [B, Hphi, P] the new token's steps
+  uint64_t* state;              // [B, Hphi, P] angle sums, 48-bit turns + 2^47
+  float* theta;                 // [B, Hphi, P] out: the new token's angles
+  uint16_t *kcache, *vcache;    // [B, H, L, D] pre-rotated k~, v~
+  uint16_t* o;                  // [B, H, D]
+  float *qrot, *part;           // workspace: [B*H, D], [B*H, ceil(L/256), D + 2]
+};
+size_t decode_workspace_bytes(const Geometry& g);
+hipError_t launch_decode_prefill(const Geometry& g, int len, const uint16_t* k, const uint16_t* v,
+                                 const float* phi, const float* theta, uint16_t* kcache,
+                                 uint16_t* vcache, uint64_t* state, hipStream_t stream);
+hipError_t launch_decode_step(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
+
 }  // namespace arp

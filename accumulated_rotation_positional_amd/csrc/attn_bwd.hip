@@ -292,12 +292,16 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
     for (int r = 0; r < 16; ++r) dkt[db][r] = dvt[db][r] = 0.f;
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
 
-  if (first_tile <= last_tile) issue(first_tile, smem);
-  for (int t = first_tile; t <= last_tile; ++t) {
-    uint8_t* st = smem + ((t - first_tile) & 1) * STAGE;
+  // Query tiles from the last one down: the workgroups that run at the same
+  // time on an XCD (keys of the same heads) then stream the same query tiles
+  // together, which keeps them in L2 (from its own diagonal upwards, each
+  // workgroup would start at a different tile).
+  if (first_tile <= last_tile) issue(last_tile, smem);
+  for (int t = last_tile; t >= first_tile; --t) {
+    uint8_t* st = smem + ((last_tile - t) & 1) * STAGE;
     wait_loads<0>();
     __builtin_amdgcn_s_barrier();
-    if (t + 1 <= last_tile) issue(t + 1, smem + ((t + 1 - first_tile) & 1) * STAGE);
+    if (t - 1 >= first_tile) issue(t - 1, smem + ((last_tile - t + 1) & 1) * STAGE);
     const uint8_t* tq = st;
     const uint8_t* tdo = st + RT;
     const uint8_t* tqT = st + 2 * RT;

@@ -1,0 +1,352 @@
+// decode.hip -- token-by-token generation against a cache of pre-rotated
+// keys and values, with the accumulated angle carried as a streaming state.
+//
+// Why no history is ever rewritten: a key rotated by its own accumulated angle
+// Theta_j keeps that rotation forever; the route from j to a later query i is
+// R(Theta_j - Theta_i) ("Why Do Accumulated Transformations Extrapolate?"
+// Sec. 2.2 eq. (6)-(8) and Sec. 5), applied through the query's own rotation
+// at query time.  So a decode step only has to
+//   1. advance the angle state by the new token's steps phi_t (exact sums of
+//      48-bit fixed-point turns, the same arithmetic as the full-sequence
+//      scan, so Theta_t is bit-identical to the scan's),
+//   2. rotate the new q, k, v by R(Theta_t) and append k~, v~ to the cache,
+//   3. attend with q~_t over the cache positions 0..t (causal), and
+//   4. un-rotate the output by R(Theta_t)^T when values are transported.
+//
+// Kernels of a step:
+//   decode_append   one workgroup per (b, h), a thread per rotary pair
+//   decode_attn     split over the keys: one workgroup per (256 keys, b, h);
+//                   each wave reads its 64 keys and values in whole-row,
+//                   1 KB-per-instruction loads, scores them, takes its own
+//                   softmax maximum and sum and its P V; the four waves merge
+//                   in LDS into one partial (m, l, acc)
+//   decode_combine  one workgroup per (b, h): merges the partials, normalises,
+//                   un-rotates, writes o, and advances the angle state.
+// The attention pass is bound by HBM: it reads 2 * (t+1) * d bf16 per (b, h).
+#include "angle_fixed.hpp"
+#include "arp_device.hpp"
+#include "arp_internal.hpp"
+
+namespace arp {
+
+namespace {
+
+constexpr int DKC = 256;  // keys per workgroup of the attention pass
+
+// ---------------------------------------------------------------------------
+// prefill: cache rows [0, len) and the state after len tokens
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void decode_fill_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ theta,
+    uint16_t* __restrict__ kcache, uint16_t* __restrict__ vcache, int len, int Lmax, int H, int Hphi,
+    uint32_t flags) {
+  constexpr int P = D / 2, CPR = D / 8;
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh % H, g = (Hphi == 1) ? 0 : h;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int t = idx / CPR, c = idx % CPR;
+  if (t >= len) return;
+  const bool rqk = (flags & ARP_ROTATE_QK) != 0, rv = (flags & ARP_ROTATE_V) != 0;
+  const size_t in = ((size_t)bh * len + t) * D + 8 * c;
+  u32x4 wk = *reinterpret_cast<const u32x4*>(k + in);
+  u32x4 wv = *reinterpret_cast<const u32x4*>(v + in);
+  if (rqk || rv) {
+    const float4 th = *reinterpret_cast<const float4*>(theta + ((size_t)(b * Hphi + g) * len + t) * P + 4 * c);
+    const float ang[4] = {th.x, th.y, th.z, th.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float sn, cs;
+      sincosf(ang[e], &sn, &cs);
+      float k0 = lo_bf16(wk[e]), k1 = hi_bf16(wk[e]), v0 = lo_bf16(wv[e]), v1 = hi_bf16(wv[e]);
+      if (rqk) rotate_pair(k0, k1, cs, sn);
+      if (rv) rotate_pair(v0, v1, cs, sn);
+      wk[e] = pack_bf16x2(k0, k1);
+      wv[e] = pack_bf16x2(v0, v1);
+    }
+  }
+  const size_t out = ((size_t)bh * Lmax + t) * D + 8 * c;
+  *reinterpret_cast<u32x4*>(kcache + out) = wk;
+  *reinterpret_cast<u32x4*>(vcache + out) = wv;
+}
+
+// state[b, g, p] = 2^47 + sum_{s < len} fixed(phi[b, g, s, p])   (mod 2^48)
+template <int P>
+__global__ __launch_bounds__(256) void decode_state_kernel(const float* __restrict__ phi,
+                                                           uint64_t* __restrict__ state, int len) {
+  constexpr int G = 256 / P;
+  __shared__ uint64_t part[G][P];
+  const int bg = blockIdx.x;
+  const int p = threadIdx.x % P, rg = threadIdx.x / P;
+  uint64_t acc = 0;
+  for (int t = rg; t < len; t += G) acc += to_fixed(phi[((size_t)bg * len + t) * P + p]);
+  part[rg][p] = acc;
+  __syncthreads();
+  if (rg == 0) {
+    uint64_t s = FIXED_ZERO;
+#pragma unroll
+    for (int r = 0; r < G; ++r) s += part[r][p];
+    state[(size_t)bg * P + p] = s & MASK48;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// step
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(D / 2) void decode_append_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ phi, const uint64_t* __restrict__ state, float* __restrict__ theta,
+    uint16_t* __restrict__ kcache, uint16_t* __restrict__ vcache, float* __restrict__ qrot, int H,
+    int Hphi, int Lmax, int pos, uint32_t flags, float qscale) {
+  constexpr int P = D / 2;
+  const int bh = blockIdx.x;
+  const int b = bh / H, h = bh % H, g = (Hphi == 1) ? 0 : h;
+  const int p = threadIdx.x;
+  const size_t sidx = (size_t)(b * Hphi + g) * P + p;
+  const uint64_t cur = (flags & ARP_SCAN_EXCLUSIVE) ? state[sidx] : state[sidx] + to_fixed(phi[sidx]);
+  const float th = to_radians_offset(cur);
+  if (Hphi != 1 || h == 0) theta[sidx] = th;
+  float sn, cs;
+  sincosf(th, &sn, &cs);
+  const size_t in = (size_t)bh * D + 2 * p;
+  const uint32_t wq = *reinterpret_cast<const uint32_t*>(q + in);
+  const uint32_t wk = *reinterpret_cast<const uint32_t*>(k + in);
+  const uint32_t wv = *reinterpret_cast<const uint32_t*>(v + in);
+  float q0 = lo_bf16(wq), q1 = hi_bf16(wq), k0 = lo_bf16(wk), k1 = hi_bf16(wk);
+  float v0 = lo_bf16(wv), v1 = hi_bf16(wv);
+  if (flags & ARP_ROTATE_QK) {
+    rotate_pair(q0, q1, cs, sn);
+    rotate_pair(k0, k1, cs, sn);
+  }
+  if (flags & ARP_ROTATE_V) rotate_pair(v0, v1, cs, sn);
+  // the query as the attention pass multiplies it: bf16-rounded like a cached key
+  qrot[in] = lo_bf16(pack_bf16x2(q0 * qscale, q1 * qscale));
+  qrot[in + 1] = hi_bf16(pack_bf16x2(q0 * qscale, q1 * qscale));
+  const size_t out = ((size_t)bh * Lmax + pos) * D + 2 * p;
+  *reinterpret_cast<uint32_t*>(kcache + out) = pack_bf16x2(k0, k1);
+  *reinterpret_cast<uint32_t*>(vcache + out) = pack_bf16x2(v0, v1);
+}
+
+// One partial per (256 keys, b, h): part = [m, l, acc[0..D)] in base-2 logits.
+// Every load instruction of a wave reads whole consecutive cache rows (CPR
+// lanes of 16 bytes per row, 1 KB per instruction): lane (r, c) holds chunk c
+// of rows kw0 + RPI i + r.  Scores are reduced over the CPR lanes of a row;
+// P V accumulates per lane and is reduced over the RPI row groups at the end.
+template <int D, bool ALIBI>
+__global__ __launch_bounds__(256) void decode_attn_kernel(
+    const float* __restrict__ qrot, const uint16_t* __restrict__ kcache,
+    const uint16_t* __restrict__ vcache, const float* __restrict__ alibi, float* __restrict__ part,
+    int H, int Lmax, int pos, int nchunk) {
+  constexpr int CPR = D / 8;     // lanes per row
+  constexpr int RPI = 64 / CPR;  // rows per load instruction
+  constexpr int NI = 64 / RPI;   // instructions per 64 keys
+  __shared__ float s_m[4], s_l[4];
+  __shared__ float s_acc[4][D];
+  const int c = blockIdx.x, bh = blockIdx.y, h = bh % H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ch = lane % CPR, rg = lane / CPR;
+  const int n = pos + 1;                // keys 0..pos
+  const int kw0 = c * DKC + wave * 64;  // this wave's first key
+  const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
+  float qv[8];
+  {
+    const float4 a = *reinterpret_cast<const float4*>(qrot + (size_t)bh * D + 8 * ch);
+    const float4 b2 = *reinterpret_cast<const float4*>(qrot + (size_t)bh * D + 8 * ch + 4);
+    qv[0] = a.x; qv[1] = a.y; qv[2] = a.z; qv[3] = a.w;
+    qv[4] = b2.x; qv[5] = b2.y; qv[6] = b2.z; qv[7] = b2.w;
+  }
+  const uint16_t* kb = kcache + (size_t)bh * Lmax * D + 8 * ch;
+  const uint16_t* vb = vcache + (size_t)bh * Lmax * D + 8 * ch;
+  u32x4 kw[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = kw0 + RPI * i + rg;
+    kw[i] = (row < n) ? *reinterpret_cast<const u32x4*>(kb + (size_t)row * D) : u32x4{0, 0, 0, 0};
+  }
+  float sc[NI];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a = fmaf(lo_bf16(kw[i][e]), qv[2 * e], a);
+      a = fmaf(hi_bf16(kw[i][e]), qv[2 * e + 1], a);
+    }
+#pragma unroll
+    for (int mk = 1; mk < CPR; mk <<= 1) a += __shfl_xor(a, mk);
+    const int row = kw0 + RPI * i + rg;
+    if (ALIBI) a += slope2 * (float)(row - pos);
+    sc[i] = (row < n) ? a : -INFINITY;
+    m = fmaxf(m, sc[i]);
+  }
+#pragma unroll
+  for (int off = CPR; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+  // values of the same rows (issued before the exponentials)
+  u32x4 vw[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = kw0 + RPI * i + rg;
+    vw[i] = (row < n) ? *reinterpret_cast<const u32x4*>(vb + (size_t)row * D) : u32x4{0, 0, 0, 0};
+  }
+  float l = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const float pr = (sc[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[i] - m);
+    l += pr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(pr, lo_bf16(vw[i][e]), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(pr, hi_bf16(vw[i][e]), acc[2 * e + 1]);
+    }
+  }
+  // over the row groups (each row's probability sits in its CPR lanes once per group)
+#pragma unroll
+  for (int off = CPR; off < 64; off <<= 1) {
+    l += __shfl_xor(l, off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
+  }
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_l[wave] = l;
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_acc[wave][8 * ch + e] = acc[e];
+  }
+  __syncthreads();
+  if (tid < D) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w]);
+    float Ls = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (s_m[w] == -INFINITY) continue;
+      const float f = __builtin_amdgcn_exp2f(s_m[w] - M);
+      Ls = fmaf(s_l[w], f, Ls);
+      A = fmaf(s_acc[w][tid], f, A);
+    }
+    float* dst = part + ((size_t)bh * nchunk + c) * (D + 2);
+    if (tid == 0) {
+      dst[0] = M;
+      dst[1] = Ls;
+    }
+    dst[2 + tid] = A;
+  }
+}
+
+// One workgroup per (b, h): thread (pair p, group cg) merges every G-th chunk
+// of its pair, then the G groups are summed in LDS.
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const float* __restrict__ part, const float* __restrict__ theta, const float* __restrict__ phi,
+    uint64_t* __restrict__ state, uint16_t* __restrict__ o, int H, int Hphi, int nchunk,
+    uint32_t flags) {
+  constexpr int P = D / 2, G = 256 / P;
+  __shared__ float s_red[256];
+  __shared__ float s_sum[G][P][3];
+  const int bh = blockIdx.x;
+  const int b = bh / H, h = bh % H, g = (Hphi == 1) ? 0 : h;
+  const int tid = threadIdx.x;
+  const int p = tid % P, cg = tid / P;
+  const float* src = part + (size_t)bh * nchunk * (D + 2);
+  float M = -INFINITY;
+  for (int c = tid; c < nchunk; c += 256) M = fmaxf(M, src[(size_t)c * (D + 2)]);
+  s_red[tid] = M;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
+    __syncthreads();
+  }
+  M = s_red[0];
+  float Ls = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int c = cg; c < nchunk; c += G) {
+    const float* pc = src + (size_t)c * (D + 2);
+    const float mc = pc[0];
+    if (mc == -INFINITY) continue;
+    const float f = __builtin_amdgcn_exp2f(mc - M);
+    Ls = fmaf(pc[1], f, Ls);
+    a0 = fmaf(pc[2 + 2 * p], f, a0);
+    a1 = fmaf(pc[3 + 2 * p], f, a1);
+  }
+  s_sum[cg][p][0] = Ls;
+  s_sum[cg][p][1] = a0;
+  s_sum[cg][p][2] = a1;
+  __syncthreads();
+  if (cg != 0) return;
+#pragma unroll
+  for (int r = 1; r < G; ++r) {
+    Ls += s_sum[r][p][0];
+    a0 += s_sum[r][p][1];
+    a1 += s_sum[r][p][2];
+  }
+  const float inv = 1.f / Ls;
+  float x0 = a0 * inv, x1 = a1 * inv;
+  const size_t sidx = (size_t)(b * Hphi + g) * P + p;
+  if (flags & ARP_ROTATE_V) {
+    float sn, cs;
+    sincosf(theta[sidx], &sn, &cs);
+    rotate_pair(x0, x1, cs, -sn);
+  }
+  *reinterpret_cast<uint32_t*>(o + (size_t)bh * D + 2 * p) = pack_bf16x2(x0, x1);
+  // advance the state (one workgroup per angle stream; no other workgroup of
+  // this kernel reads it)
+  if (Hphi != 1 || h == 0) state[sidx] = (state[sidx] + to_fixed(phi[sidx])) & MASK48;
+}
+
+template <int D>
+hipError_t launch_step(const Geometry& g, const DecodeArgs& a, hipStream_t stream) {
+  const int BH = g.B * g.H;
+  hipLaunchKernelGGL((decode_append_kernel<D>), dim3(BH), dim3(D / 2), 0, stream, a.q, a.k, a.v,
+                     a.phi, a.state, a.theta, a.kcache, a.vcache, a.qrot, g.H, g.Hphi, g.L, a.pos,
+                     g.flags, g.scale * LOG2E);
+  const int nchunk = (a.pos + 1 + DKC - 1) / DKC;
+  if (g.flags & ARP_ALIBI)
+    hipLaunchKernelGGL((decode_attn_kernel<D, true>), dim3(nchunk, BH), dim3(256), 0, stream, a.qrot,
+                       a.kcache, a.vcache, a.alibi, a.part, g.H, g.L, a.pos, nchunk);
+  else
+    hipLaunchKernelGGL((decode_attn_kernel<D, false>), dim3(nchunk, BH), dim3(256), 0, stream,
+                       a.qrot, a.kcache, a.vcache, a.alibi, a.part, g.H, g.L, a.pos, nchunk);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(BH), dim3(256), 0, stream, a.part, a.theta,
+                     a.phi, a.state, a.o, g.H, g.Hphi, nchunk, g.flags);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(const Geometry& g) {
+  const size_t nchunk = ((size_t)g.L + DKC - 1) / DKC;
+  return (size_t)g.B * g.H * (nchunk * (g.D + 2) + g.D) * sizeof(float);
+}
+
+hipError_t launch_decode_prefill(const Geometry& g, int len, const uint16_t* k, const uint16_t* v,
+                                 const float* phi, const float* theta, uint16_t* kcache,
+                                 uint16_t* vcache, uint64_t* state, hipStream_t stream) {
+  if (len > 0) {
+    dim3 grid((unsigned)(((size_t)len * (g.D / 8) + 255) / 256), g.B * g.H);
+    if (g.D == 64)
+      hipLaunchKernelGGL((decode_fill_kernel<64>), grid, dim3(256), 0, stream, k, v, theta, kcache,
+                         vcache, len, g.L, g.H, g.Hphi, g.flags);
+    else
+      hipLaunchKernelGGL((decode_fill_kernel<128>), grid, dim3(256), 0, stream, k, v, theta, kcache,
+                         vcache, len, g.L, g.H, g.Hphi, g.flags);
+  }
+  if (g.P == 32)
+    hipLaunchKernelGGL((decode_state_kernel<32>), dim3(g.B * g.Hphi), dim3(256), 0, stream, phi, state,
+                       len);
+  else
+    hipLaunchKernelGGL((decode_state_kernel<64>), dim3(g.B * g.Hphi), dim3(256), 0, stream, phi, state,
+                       len);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step(const Geometry& g, const DecodeArgs& a, hipStream_t stream) {
+  return g.D == 64 ? launch_step<64>(g, a, stream) : launch_step<128>(g, a, stream);
+}
+
+}  // namespace arp

@@ -193,6 +193,53 @@ def backward_leg(binding, torch, dev, w, q, k, v, phi, alibi, steps: int = 20) -
             "outputs": "dq, dk, dv (bf16), dtheta, dphi (fp32)"}
 
 
+def decode_leg(binding, torch, dev, steps: int = 50) -> dict:
+    """Decode steps at a full context: the token at the last position attends
+    to every cached row.  Two cache shapes: extrap_16k's (B=2, H=8, 16384
+    tokens, d=64: 67 MB of keys and values, which the 256 MB Infinity Cache
+    can hold) and rope_8k_d128's (B=4, H=32, 8192 tokens, d=128: 537 MB, read
+    from HBM on every step).  Per step: the append, the split-key attention and
+    the combine; HBM roofline on the bytes the attention must read,
+    2 * tokens * d * 2 bytes per (b, h).  The caches hold seeded random bf16
+    (the cost does not depend on the values)."""
+    from accumulated_rotation_positional_amd import workloads as wl
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    for name in ("extrap_16k", "rope_8k_d128"):
+        spec = wl.SPECS[name]
+        B, H, L, d = spec.batch, spec.heads, spec.seqlen, spec.head_dim
+        cache = binding.DecodeCache(B, H, L, d, rotate_qk=True, rotate_v=True, device=dev)
+        cache.kcache.copy_(torch.randn(cache.kcache.shape, device=dev, generator=g) * d ** -0.5)
+        cache.vcache.copy_(torch.randn(cache.vcache.shape, device=dev, generator=g) * d ** -0.5)
+        cache.prefill()
+        q, k, v = (torch.randn(B, H, d, device=dev, generator=g).to(torch.bfloat16) * d ** -0.5
+                   for _ in range(3))
+        phi = torch.rand(B, H, d // 2, device=dev, generator=g) * 0.5
+        o = torch.empty_like(q)
+        for _ in range(5):
+            cache.step(L - 1, q, k, v, phi, out=o)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            cache.step(L - 1, q, k, v, phi, out=o)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+        nbytes = 2.0 * L * d * 2 * B * H
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"context": L, "batch": B, "heads": H, "head_dim": d, "us_per_step": round(us, 2),
+                     "tokens_per_s": round(B / (us * 1e-6), 1), "cache_bytes": nbytes,
+                     "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del cache
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -315,6 +362,7 @@ def main():
     result["scan_hbm_gate"] = scan_gate(binding, torch, dev)
     if not args.fused:
         result["backward"] = backward_leg(binding, torch, dev, w, q, k, v, phi, alibi)
+        result["decode"] = decode_leg(binding, torch, dev)
     if not args.no_cpu_baseline:
         import oracle
         of = (oracle.ROTATE_QK | (oracle.ROTATE_V if w.rotate_v else 0) |

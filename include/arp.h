@@ -185,6 +185,41 @@ arp_status arp_backward(const arp_desc* desc, const void* q, const void* k, cons
                         const void* dout, void* dq, void* dk, void* dv, float* dtheta,
                         float* dphi, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- decode: one new token per sequence against a key/value cache ----
+ * desc.seqlen is the cache capacity Lmax; bf16 only.  Caches hold the keys and
+ * values already rotated by their own accumulated angles, bf16
+ * [batch, heads, Lmax, head_dim]: a token's rotation never changes once it is
+ * written, since the route from j to i is R(Theta_j - Theta_i) (eq. (6)-(8),
+ * Sec. 5), applied through the query's rotation.  The angle state is
+ * uint64 [batch, phi_heads, head_dim/2]: the running sum of the steps in
+ * 48-bit fixed-point turns (plus half a turn), the arithmetic of
+ * arp_angle_scan, so decoded angles are bit-identical to a full scan's. */
+
+/* Bytes of the decode step's workspace (partial results of the split-key
+ * attention) for a cache of desc.seqlen tokens; 0 unless bf16. */
+size_t arp_decode_workspace_bytes(const arp_desc* desc);
+
+/* Fill cache rows [0, len) from a prompt and set the state after len tokens.
+ * k, v: [batch, heads, len, head_dim] (raw); phi, theta: [batch, phi_heads,
+ * len, head_dim/2], theta from arp_angle_scan (or arp_forward) over the same
+ * len tokens.  len = 0 only resets the state (k, v, phi, theta may be NULL). */
+arp_status arp_decode_prefill(const arp_desc* desc, int32_t len, const void* k, const void* v,
+                              const float* phi, const float* theta, void* kcache, void* vcache,
+                              uint64_t* state, void* stream);
+
+/* One decode step at position pos (0 <= pos < Lmax, the same for every
+ * sequence; rows 0..pos-1 of the caches filled): q, k, v [batch, heads,
+ * head_dim] and phi [batch, phi_heads, head_dim/2] are the new token's.
+ * Advances the state, writes the token's wrapped angles to theta
+ * [batch, phi_heads, head_dim/2], appends its rotated k, v at row pos, and
+ * writes o [batch, heads, head_dim]: causal attention of the token over rows
+ * 0..pos, with the flags' rotation, distance bias and value transport --
+ * the row pos of arp_forward over the whole sequence. */
+arp_status arp_decode_step(const arp_desc* desc, int32_t pos, const void* q, const void* k,
+                           const void* v, const float* phi, const float* alibi, uint64_t* state,
+                           float* theta, void* kcache, void* vcache, void* o, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Diagnostic: out = R(theta) x (or R(theta)^T x when inverse != 0) in fp32.
  * x has the desc's dtype and q's layout; out is float32 of the same shape. */
 arp_status arp_rotate(const arp_desc* desc, const void* x, const float* theta, float* out,
