@@ -37,6 +37,7 @@ ROTATE_QK = 1
 ROTATE_V = 2
 ALIBI = 4
 SCAN_EXCLUSIVE = 16
+FORGET = 64
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
@@ -57,6 +58,7 @@ class _Problem(ctypes.Structure):
         ("v", ctypes.c_void_p),
         ("phi", ctypes.c_void_p),
         ("alibi_slopes", ctypes.c_void_p),
+        ("logf", ctypes.c_void_p),
     ]
 
 
@@ -142,7 +144,8 @@ def rotate_rows(x: np.ndarray, angle: np.ndarray, inverse: bool = False) -> np.n
 class Problem:
     """Holds the arrays of one attention problem and the C descriptor pointing at them."""
 
-    def __init__(self, q, k, v, phi, flags: int, scale: float | None = None, alibi=None):
+    def __init__(self, q, k, v, phi, flags: int, scale: float | None = None, alibi=None,
+                 logf=None):
         self.q = np.ascontiguousarray(q)
         self.k = np.ascontiguousarray(k)
         self.v = np.ascontiguousarray(v)
@@ -157,13 +160,17 @@ class Problem:
         self.alibi = None if alibi is None else np.ascontiguousarray(alibi, dtype=np.float32)
         if flags & ALIBI and (self.alibi is None or self.alibi.shape != (H,)):
             raise ValueError("ALIBI needs one slope per head")
+        self.logf = None if logf is None else np.ascontiguousarray(logf, dtype=np.float32)
+        if flags & FORGET and (self.logf is None or self.logf.shape != (B, H, L)):
+            raise ValueError("FORGET needs log forget gates [B, H, L]")
         self.shape = (B, H, L, d)
         self.flags = int(flags)
         self.scale = float(1.0 / np.sqrt(d) if scale is None else scale)
         self.c = _Problem(B, H, L, d, self.phi.shape[1], _io_dtype(self.q), self.flags, self.scale,
                           self.q.ctypes.data, self.k.ctypes.data, self.v.ctypes.data,
                           self.phi.ctypes.data,
-                          None if self.alibi is None else self.alibi.ctypes.data)
+                          None if self.alibi is None else self.alibi.ctypes.data,
+                          None if self.logf is None else self.logf.ctypes.data)
 
     def theta(self) -> np.ndarray:
         B, H, L, d = self.shape
@@ -214,5 +221,6 @@ class Problem:
         return self.rows(np.arange(B * H * L, dtype=np.int64), nthreads).reshape(B, H, L, d)
 
 
-def attention(q, k, v, phi, flags: int, scale=None, alibi=None, nthreads: int = 0) -> np.ndarray:
-    return Problem(q, k, v, phi, flags, scale, alibi).output(nthreads)
+def attention(q, k, v, phi, flags: int, scale=None, alibi=None, nthreads: int = 0,
+              logf=None) -> np.ndarray:
+    return Problem(q, k, v, phi, flags, scale, alibi, logf).output(nthreads)

@@ -33,8 +33,13 @@
  *     the routed score of [ACC] eq. (7)-(8), with P_{j->i} a rotation by
  *     minus the summed angles of steps j+1..i ([ACC] App. B.8, position-only
  *     case; App. B.2 writes the step as e^{-i psi_t}).
- *  3. Scores s_ij = scale * <q~_i, k~_j> - m_h (i - j) [distance bias on],
- *     for the causal set j <= i ([ACC] eq. (2), (11); [ADA] eq. (5)).
+ *  3. Scores s_ij = scale * <q~_i, k~_j> - m_h (i - j) [distance bias on]
+ *     + sum_{s=j+1}^{i} log f_s [forget gate on], for the causal set j <= i
+ *     ([ACC] eq. (2), (11); [ADA] eq. (5); the forget gate is the logit term of
+ *     the PaTH reading notes' Sec. 2.5, one gate f_s per token and head, which
+ *     [ACC] Sec. 4 names beside the distance bias as far-mass control).  The
+ *     gate sum is accumulated here over s = j+1..i directly, not as a
+ *     difference of prefix sums.
  *  4. Softmax over j <= i, computed in two passes: the row maximum M, then
  *     w_ij = exp(s_ij - M) and l_i = sum_j w_ij ([ACC] eq. (2)).
  *  5. Aggregation c_i = sum_j (w_ij / l_i) P_{j->i} v_j ([ACC] eq. (4)); with
@@ -147,6 +152,7 @@ static int check_problem(const oracle_problem* p) {
   if (p->io_dtype != ORACLE_DTYPE_F32 && p->io_dtype != ORACLE_DTYPE_BF16) return ORACLE_ERR_ARG;
   if (!p->q || !p->k || !p->v || !p->phi) return ORACLE_ERR_ARG;
   if ((p->flags & ORACLE_ALIBI) && !p->alibi_slopes) return ORACLE_ERR_ARG;
+  if ((p->flags & ORACLE_FORGET) && !p->logf) return ORACLE_ERR_ARG;
   return ORACLE_OK;
 }
 
@@ -233,6 +239,15 @@ static void row_scores(const oracle_problem* p, const head_state* hs, int64_t b,
     double dot = 0.0;
     for (int64_t c = 0; c < d; ++c) dot += qrot[c] * kj[c];
     scores[j] = p->scale * dot - slope * (double)(i - j);
+  }
+  if (p->flags & ORACLE_FORGET) {
+    /* sum_{s=j+1}^{i} log f_s, from j = i (empty) down to 0 */
+    const float* lf = p->logf + (b * p->heads + h) * L;
+    double gate = 0.0;
+    for (int64_t j = i; j >= 0; --j) {
+      scores[j] += gate;
+      gate += (double)lf[j];
+    }
   }
 }
 
@@ -455,6 +470,7 @@ int oracle_backward(const oracle_problem* p, const void* dout, int nthreads, dou
   int rc = check_problem(p);
   if (rc) return rc;
   if (!dout || !dq || !dk || !dv || !dtheta || !dphi) return ORACLE_ERR_ARG;
+  if (p->flags & ORACLE_FORGET) return ORACLE_ERR_ARG; /* gradients of the gate are not derived here */
   const int64_t B = p->batch, H = p->heads, L = p->seqlen, P = p->head_dim / 2;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);

@@ -29,6 +29,7 @@ extern "C" {
 #define ORACLE_ROTATE_V 2u       /* transport values along the route (eq. (4))    */
 #define ORACLE_ALIBI 4u          /* add the distance bias -m_h (i - j)            */
 #define ORACLE_SCAN_EXCLUSIVE 16u /* Theta_t sums steps s < t instead of s <= t   */
+#define ORACLE_FORGET 64u        /* add the forget-gate bias sum_{s=j+1}^{i} log f_s */
 
 #define ORACLE_DTYPE_F32 0
 #define ORACLE_DTYPE_BF16 1
@@ -48,6 +49,7 @@ typedef struct oracle_problem {
   const void* v;
   const float* phi;
   const float* alibi_slopes; /* read only when ORACLE_ALIBI is set */
+  const float* logf;         /* [batch, heads, seqlen] log forget gates; read only with ORACLE_FORGET */
 } oracle_problem;
 
 /* Prefix sum of step angles along the sequence, one segment per (outer, pair).
@@ -81,7 +83,8 @@ int oracle_attention_rows(const oracle_problem* p, const int64_t* rows, int64_t 
  *   dq, dk, dv  [batch, heads, seqlen, head_dim]
  *   dtheta      [batch, heads, seqlen, head_dim/2]   dL/dTheta per head
  *   dphi        [batch, phi_heads, seqlen, head_dim/2]
- * O(seqlen^2 head_dim) per head; OpenMP over heads. */
+ * O(seqlen^2 head_dim) per head; OpenMP over heads.  ORACLE_ERR_ARG with
+ * ORACLE_FORGET (the gate's own gradient is not part of this oracle). */
 int oracle_backward(const oracle_problem* p, const void* dout, int nthreads, double* dq,
                     double* dk, double* dv, double* dtheta, double* dphi);
 

@@ -30,6 +30,9 @@ MUTANTS = [
     ("pair layout half-split", "double b = x[2 * p + 1];", "double b = x[p + npairs];"),
     ("bf16 decode shift", "<< 16;", "<< 15;"),
     ("softmax max not subtracted", "double w = exp(scores[j] - m);", "double w = exp(scores[j] - 1.0);"),
+    ("gate sum includes the key's own gate", "scores[j] += gate;\n      gate += (double)lf[j];",
+     "gate += (double)lf[j];\n      scores[j] += gate;"),
+    ("gate sign", "scores[j] += gate;", "scores[j] -= gate;"),
 ]
 
 
@@ -65,7 +68,8 @@ def _run_pins_against(old, new, name, tmp_path, pin_file):
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_fail_on_planted_mistake(name, old, new, tmp_path):
-    _run_pins_against(old, new, name, tmp_path, "test_oracle_pins.py")
+    pins = "test_oracle_forget.py" if "gate" in name else "test_oracle_pins.py"
+    _run_pins_against(old, new, name, tmp_path, pins)
 
 
 @pytest.mark.parametrize("name,old,new", BACKWARD_MUTANTS, ids=[m[0] for m in BACKWARD_MUTANTS])
