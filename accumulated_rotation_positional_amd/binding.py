@@ -30,13 +30,15 @@ ALIBI = 0x4
 PHI_SHARED_HEADS = 0x8
 SCAN_EXCLUSIVE = 0x10
 FUSED_ROTATION = 0x20
+FORGET_GATE = 0x40
 
 # Every function the header declares (tests check the library exports them all).
 EXPORTS = ("arp_abi_version", "arp_status_string", "arp_check", "arp_scan_state_bytes",
            "arp_workspace_bytes",
            "arp_angle_scan", "arp_rotate_qkv", "arp_attn_rotated", "arp_attn_fwd",
            "arp_forward", "arp_rotate", "arp_forward_train", "arp_backward_workspace_bytes",
-           "arp_backward", "arp_decode_workspace_bytes", "arp_decode_prefill", "arp_decode_step")
+           "arp_backward", "arp_decode_workspace_bytes", "arp_decode_prefill", "arp_decode_step",
+           "arp_forward_ex")
 
 
 class ArpError(RuntimeError):
@@ -83,6 +85,7 @@ def lib() -> ctypes.CDLL:
                 "arp_decode_workspace_bytes": ([D], S),
                 "arp_decode_prefill": ([D, ctypes.c_int32] + [P] * 7 + [P], ctypes.c_int),
                 "arp_decode_step": ([D, ctypes.c_int32] + [P] * 11 + [S, P], ctypes.c_int),
+                "arp_forward_ex": ([D] + [P] * 10 + [S, P, S, P], ctypes.c_int),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -128,10 +131,12 @@ def _stream(device: torch.device) -> int:
 
 
 def flags_for(*, rotate_qk: bool = True, rotate_v: bool = False, alibi: bool = False,
-              shared_phi: bool = False, exclusive: bool = False, fused: bool = False) -> int:
+              shared_phi: bool = False, exclusive: bool = False, fused: bool = False,
+              forget: bool = False) -> int:
     return ((ROTATE_QK if rotate_qk else 0) | (ROTATE_V if rotate_v else 0) |
             (ALIBI if alibi else 0) | (PHI_SHARED_HEADS if shared_phi else 0) |
-            (SCAN_EXCLUSIVE if exclusive else 0) | (FUSED_ROTATION if fused else 0))
+            (SCAN_EXCLUSIVE if exclusive else 0) | (FUSED_ROTATION if fused else 0) |
+            (FORGET_GATE if forget else 0))
 
 
 def desc_for(q: torch.Tensor, flags: int, scale: float | None = None) -> Desc:
@@ -344,3 +349,28 @@ class DecodeCache:
             _ptr(self.state), _ptr(self.theta), _ptr(self.kcache), _ptr(self.vcache), _ptr(out),
             _ptr(self.ws), self.ws.numel(), _stream(self.device)))
         return out
+
+
+def forward_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.Tensor, *,
+               rotate_qk: bool = True, rotate_v: bool = False, alibi: torch.Tensor | None = None,
+               logf: torch.Tensor | None = None, scale: float | None = None,
+               exclusive: bool = False, with_lse: bool = False):
+    """The forward with every option (arp_forward_ex): logf [B, H, L] log forget
+    gates (the gate bias is on when given), with_lse also returns the per-row
+    base-2 log-sum-exp.  Returns (o, theta, lse or None)."""
+    _require_gpu(q, k, v, phi, alibi, logf)
+    flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi is not None,
+                      shared_phi=phi.shape[1] == 1 and q.shape[1] != 1, exclusive=exclusive,
+                      forget=logf is not None)
+    desc = desc_for(q, flags, scale)
+    out = torch.empty_like(q)
+    theta = torch.empty_like(phi)
+    B, H, L, _ = q.shape
+    lse = torch.empty(B, H, L, dtype=torch.float32, device=q.device) if with_lse else None
+    state = scan_state(desc, q.device)
+    ws = workspace(desc, q.device)
+    _check("arp_forward_ex", lib().arp_forward_ex(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(phi), _ptr(alibi), _ptr(logf),
+        _ptr(theta), _ptr(out), _ptr(lse), _ptr(state), state.numel(), _ptr(ws), ws.numel(),
+        _stream(q.device)))
+    return out, theta, lse

@@ -66,6 +66,7 @@ arp_status fused_status(hipError_t e) {
 }
 
 bool rotates(const Geometry& g) { return (g.flags & (ARP_ROTATE_QK | ARP_ROTATE_V)) != 0; }
+bool gated(const Geometry& g) { return (g.flags & ARP_FORGET_GATE) != 0; }
 
 }  // namespace
 
@@ -80,6 +81,10 @@ WorkspaceLayout workspace_layout(const Geometry& g) {
     off += 3 * lay.operand_bytes;
     lay.kmax_off = off;
     off += align_up((size_t)g.B * g.H * (g.Lp / KEY_TILE) * sizeof(float));
+    if (g.flags & ARP_FORGET_GATE) {
+      lay.gate_off = off;
+      off += align_up((size_t)g.B * g.H * g.Lp * sizeof(float));
+    }
   }
   lay.total = off;
   return lay;
@@ -149,6 +154,7 @@ arp_status arp_rotate_qkv(const arp_desc* desc, const void* q, const void* k, co
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
+  if (gated(g)) return ARP_ERR_INVALID_ARG;  // the gate input: arp_forward_ex
   if (!needs_operands(g)) return ARP_ERR_UNSUPPORTED;
   if (q == nullptr || k == nullptr || v == nullptr || (rotates(g) && theta == nullptr))
     return ARP_ERR_INVALID_ARG;
@@ -169,6 +175,7 @@ arp_status arp_attn_rotated(const arp_desc* desc, const float* theta, const floa
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
+  if (gated(g)) return ARP_ERR_INVALID_ARG;  // the gate input: arp_forward_ex
   if (!needs_operands(g)) return ARP_ERR_UNSUPPORTED;
   if (o == nullptr || ((g.flags & ARP_ROTATE_V) && theta == nullptr) ||
       ((g.flags & ARP_ALIBI) && alibi == nullptr))
@@ -182,7 +189,7 @@ arp_status arp_attn_rotated(const arp_desc* desc, const float* theta, const floa
       g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
       reinterpret_cast<const uint16_t*>(ws + lay.k_off),
       reinterpret_cast<const uint16_t*>(ws + lay.vt_off),
-      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi,
+      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi, nullptr,
       static_cast<uint16_t*>(o), nullptr, (hipStream_t)stream));
 }
 
@@ -192,6 +199,7 @@ arp_status arp_attn_fwd(const arp_desc* desc, const void* q, const void* k, cons
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
+  if (gated(g)) return ARP_ERR_INVALID_ARG;  // the gate input: arp_forward_ex
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr ||
       (rotates(g) && theta == nullptr) || ((g.flags & ARP_ALIBI) && alibi == nullptr))
     return ARP_ERR_INVALID_ARG;
@@ -220,6 +228,7 @@ arp_status arp_forward(const arp_desc* desc, const void* q, const void* k, const
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
+  if (gated(g)) return ARP_ERR_INVALID_ARG;  // the gate input: arp_forward_ex
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || phi == nullptr ||
       theta == nullptr || ((g.flags & ARP_ALIBI) && alibi == nullptr))
     return ARP_ERR_INVALID_ARG;
@@ -240,6 +249,7 @@ arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k,
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
+  if (gated(g)) return ARP_ERR_INVALID_ARG;  // the gate input: arp_forward_ex
   if (!needs_operands(g)) return ARP_ERR_UNSUPPORTED;
   if (lse == nullptr) return ARP_ERR_INVALID_ARG;
   if (!aligned16(lse)) return ARP_ERR_ALIGNMENT;
@@ -261,8 +271,50 @@ arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k,
       g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
       reinterpret_cast<const uint16_t*>(ws + lay.k_off),
       reinterpret_cast<const uint16_t*>(ws + lay.vt_off),
-      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi,
+      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi, nullptr,
       static_cast<uint16_t*>(o), lse, (hipStream_t)stream));
+}
+
+arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, const void* v,
+                          const float* phi, const float* alibi, const float* logf, float* theta,
+                          void* o, float* lse, void* scan_state, size_t scan_state_bytes,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (!needs_operands(g)) {
+    // fp32 I/O or the fused rotation: neither the gate nor lse is built there
+    if (gated(g) || lse != nullptr) return ARP_ERR_UNSUPPORTED;
+    return arp_forward(desc, q, k, v, phi, alibi, theta, o, scan_state, scan_state_bytes,
+                       workspace, workspace_bytes, stream);
+  }
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || phi == nullptr ||
+      theta == nullptr || ((g.flags & ARP_ALIBI) && alibi == nullptr) || (gated(g) && logf == nullptr))
+    return ARP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(phi) ||
+      !aligned16(theta) || (alibi && !aligned16(alibi)) || (lse && !aligned16(lse)) ||
+      (gated(g) && !aligned16(logf)))
+    return ARP_ERR_ALIGNMENT;
+  if ((st = check_scan_state(g, scan_state, scan_state_bytes)) != ARP_OK) return st;
+  if ((st = check_ws(g, workspace, workspace_bytes)) != ARP_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const WorkspaceLayout lay = workspace_layout(g);
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = launch_angle_scan(g, phi, theta, scan_state, s);
+  if (e != hipSuccess) return ARP_ERR_HIP;
+  e = launch_rotate_qkv(g, q, k, v, theta, reinterpret_cast<uint16_t*>(ws + lay.q_off),
+                        reinterpret_cast<uint16_t*>(ws + lay.k_off),
+                        reinterpret_cast<uint16_t*>(ws + lay.vt_off),
+                        reinterpret_cast<float*>(ws + lay.kmax_off), s);
+  if (e != hipSuccess) return ARP_ERR_HIP;
+  float* gate2 = gated(g) ? reinterpret_cast<float*>(ws + lay.gate_off) : nullptr;
+  if (gated(g) && launch_gate_scan(g, logf, gate2, s) != hipSuccess) return ARP_ERR_HIP;
+  return hip_status(launch_attn_bf16_rotated(
+      g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
+      reinterpret_cast<const uint16_t*>(ws + lay.k_off),
+      reinterpret_cast<const uint16_t*>(ws + lay.vt_off),
+      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi, gate2,
+      static_cast<uint16_t*>(o), lse, s));
 }
 
 size_t arp_backward_workspace_bytes(const arp_desc* desc) {
@@ -278,6 +330,7 @@ arp_status arp_backward(const arp_desc* desc, const void* q, const void* k, cons
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
+  if (gated(g)) return ARP_ERR_UNSUPPORTED;
   if (g.dtype != ARP_DTYPE_BF16) return ARP_ERR_UNSUPPORTED;
   const void* in[] = {q, k, v, o, lse, dout, dq, dk, dv, dtheta, dphi};
   for (const void* p : in)
@@ -323,6 +376,7 @@ arp_status arp_decode_prefill(const arp_desc* desc, int32_t len, const void* k, 
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
+  if (gated(g)) return ARP_ERR_UNSUPPORTED;
   if (g.dtype != ARP_DTYPE_BF16) return ARP_ERR_UNSUPPORTED;
   if (len < 0 || len > g.L || kcache == nullptr || vcache == nullptr || state == nullptr)
     return ARP_ERR_INVALID_ARG;
@@ -345,6 +399,7 @@ arp_status arp_decode_step(const arp_desc* desc, int32_t pos, const void* q, con
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
+  if (gated(g)) return ARP_ERR_UNSUPPORTED;
   if (g.dtype != ARP_DTYPE_BF16) return ARP_ERR_UNSUPPORTED;
   if (pos < 0 || pos >= g.L) return ARP_ERR_INVALID_ARG;
   const void* req[] = {q, k, v, phi, state, theta, kcache, vcache, o};

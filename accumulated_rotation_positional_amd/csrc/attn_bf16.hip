@@ -54,13 +54,19 @@ constexpr float TAU = 8.0f;   // lazy-rescale threshold (base-2 logits)
 // and scaled in the prologue, and each K/V tile is rotated while it is staged
 // through registers into LDS (sin/cos once per (key, pair), shared by k and
 // v); row maxima are always taken exactly.
-template <int D, int QPW, int NW, int NST, int MINB, bool FUSED, bool ALIBI, bool ROTV>
+// BIAS: bit 0 the distance bias -m_h (i - j), bit 1 the forget-gate bias
+// G_i - G_j, with G = log2 e * (prefix sums of log f) from the gate pass
+// ([B*H, Lp] in gate2; non-increasing, so the bias never raises a score).
+template <int D, int QPW, int NW, int NST, int MINB, bool FUSED, int BIAS, bool ROTV>
 __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
-    const float* __restrict__ theta, const float* __restrict__ alibi, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int L, int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk,
-    float qscale) {
+    const float* __restrict__ theta, const float* __restrict__ alibi,
+    const float* __restrict__ gate2, uint16_t* __restrict__ o, float* __restrict__ lse, int L,
+    int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk, float qscale) {
+  constexpr bool ALIBI = (BIAS & 1) != 0;
+  constexpr bool FORGET = (BIAS & 2) != 0;
+  static_assert(!(FUSED && FORGET), "the gate bias needs the pre-rotation path");
   constexpr int BM = QPW * NW;
   constexpr int QB = QPW / 32;         // 32-query blocks per wave
   constexpr int KS = D / 16;           // k-steps of S^T (16 of D each)
@@ -82,7 +88,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
   constexpr int IPT = P * (BN / 4) / NT;  // fused staging: (pair, 4-key group) items per thread
   static_assert(!FUSED || IPT * NT == P * (BN / 4), "fused staging split");
 
-  constexpr int STAGE = KTILE + VTILE;
+  constexpr int GTILE = FORGET ? BN * 4 : 0;  // the tile's 64 key gates (fp32)
+  constexpr int STAGE = KTILE + VTILE + GTILE;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
   // ---- which tile: XCD-aware, heads grouped per XCD, longest tiles first ----
@@ -124,6 +131,11 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
       const uint16_t* src = vbase + (size_t)row * Lp + j0 + 8 * c;
       __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + KTILE + p0), 16,
                                        0, 0);
+    }
+    if constexpr (FORGET) {
+      if (wave == 0 && lane < BN / 4)
+        __builtin_amdgcn_global_load_lds((global_void_ptr)(gate2 + (size_t)bh * Lp + j0 + 4 * lane),
+                                         (lds_void_ptr)(stage + KTILE + VTILE), 16, 0, 0);
     }
   };
   // ---- fused staging: raw k, v and angles of one tile -> registers -> rotated into LDS ----
@@ -255,6 +267,10 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     for (int r = 0; r < 16; ++r) cneg[qb][r] = 0.f;
   }
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
+  float gq[QB];  // the forget-gate prefix of this lane's queries
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+    gq[qb] = FORGET ? gate2[(size_t)bh * Lp + min(qw + 32 * qb + ln, Lp - 1)] : 0.f;
 
   // ---- the three parts of one key tile of this wave's queries ----
   f32x16 s[KB][QB];      // logits of the tile in flight
@@ -285,7 +301,24 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     // Element r of s[kb][qb] on this lane is key j0 + koff(kb, r) + 8 hf,
     // koff = 32 kb + 16 (r>>3) + 4 ((r>>2)&1) + (r&3); query qw + 32 qb + ln.
     const bool diag = (n == last_w);
-    if (ALIBI || diag) {
+    if (ALIBI || FORGET || diag) {
+      // the tile's key gates for this lane's elements: keys koff + 8 hf
+      float gk[KB][16];
+      if constexpr (FORGET) {
+        const float* gt = reinterpret_cast<const float*>(smem + (n % NST) * STAGE + KTILE + VTILE);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(gt + 32 * kb + 16 * h2 + 8 * hf);
+            const f32x4 c = *reinterpret_cast<const f32x4*>(gt + 32 * kb + 16 * h2 + 8 * hf + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              gk[kb][8 * h2 + e] = a[e];
+              gk[kb][8 * h2 + 4 + e] = c[e];
+            }
+          }
+      }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int base = j0 + 8 * hf - (qw + 32 * qb + ln);  // key - query minus koff
@@ -297,6 +330,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
             const int koff = 32 * kb + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
             float x = s[kb][qb][r];
             if (ALIBI) x += fmaf(slope2, (float)koff, fb);
+            if (FORGET) x += gq[qb] - gk[kb][r];
             if (diag && koff + base > 0) x = -INFINITY;
             s[kb][qb][r] = x;
           }
@@ -457,23 +491,36 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
 template <int D, int QPW, int NW, int NST, int MINB, bool FUSED>
 hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                            const uint16_t* vt, const float* kmax, const float* theta,
-                           const float* alibi, uint16_t* o, float* lse, hipStream_t stream) {
+                           const float* alibi, const float* gate2, uint16_t* o, float* lse,
+                           hipStream_t stream) {
   constexpr int BM = QPW * NW;
   const int nqt = (g.L + BM - 1) / BM;
   const int total = g.B * g.H * nqt;
   const int grid = ((total + 7) / 8) * 8;
-  const bool al = g.flags & ARP_ALIBI, rv = g.flags & ARP_ROTATE_V;
+  const bool rv = g.flags & ARP_ROTATE_V;
+  const int bias = ((g.flags & ARP_ALIBI) ? 1 : 0) | ((g.flags & ARP_FORGET_GATE) ? 2 : 0);
   const int rqk = (g.flags & ARP_ROTATE_QK) ? 1 : 0;
   const float qscale = g.scale * LOG2E;
 #define ARP_BF16_LAUNCH(A, R)                                                                  \
   hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, MINB, FUSED, A, R>), dim3(grid),      \
-                     dim3(NW * 64), 0, stream, qr, kr, vt, kmax, theta, alibi, o, lse, g.L, g.Lp, \
-                     g.H, g.Hphi, nqt, total, rqk, qscale)
-  if (al) {
-    if (rv) ARP_BF16_LAUNCH(true, true); else ARP_BF16_LAUNCH(true, false);
+                     dim3(NW * 64), 0, stream, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,   \
+                     g.L, g.Lp, g.H, g.Hphi, nqt, total, rqk, qscale)
+#define ARP_BF16_LAUNCH_R(A) \
+  do {                       \
+    if (rv) ARP_BF16_LAUNCH(A, true); else ARP_BF16_LAUNCH(A, false); \
+  } while (0)
+  if constexpr (FUSED) {
+    if (bias & 2) return hipErrorNotSupported;
+    if (bias & 1) ARP_BF16_LAUNCH_R(1); else ARP_BF16_LAUNCH_R(0);
   } else {
-    if (rv) ARP_BF16_LAUNCH(false, true); else ARP_BF16_LAUNCH(false, false);
+    switch (bias) {
+      case 0: ARP_BF16_LAUNCH_R(0); break;
+      case 1: ARP_BF16_LAUNCH_R(1); break;
+      case 2: ARP_BF16_LAUNCH_R(2); break;
+      default: ARP_BF16_LAUNCH_R(3); break;
+    }
   }
+#undef ARP_BF16_LAUNCH_R
 #undef ARP_BF16_LAUNCH
   return hipGetLastError();
 }
@@ -482,19 +529,21 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
 
 hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                                     const uint16_t* vt, const float* kmax, const float* theta,
-                                    const float* alibi, uint16_t* o, float* lse,
-                                    hipStream_t stream) {
+                                    const float* alibi, const float* gate2, uint16_t* o,
+                                    float* lse, hipStream_t stream) {
   if (g.D == 64)
-    return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, o, lse, stream);
-  return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, o, lse, stream);
+    return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,
+                                                   stream);
+  return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,
+                                                  stream);
 }
 
 hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const float* theta, const float* alibi,
                                   uint16_t* o, hipStream_t stream) {
   if (g.D == 64)
-    return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, o, nullptr, stream);
-  return launch_bf16_cfg<128, 32, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, o, nullptr, stream);
+    return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, nullptr, o, nullptr, stream);
+  return launch_bf16_cfg<128, 32, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, nullptr, o, nullptr, stream);
 }
 
 }  // namespace arp

@@ -147,7 +147,41 @@ __global__ __launch_bounds__(256) void rotate_diag_kernel(const TIn* __restrict_
   out[2 * i + 1] = bb;
 }
 
+// Forget-gate prefix per (b, h): one workgroup per head, each thread a
+// contiguous run of tokens; fp64 run sums, an fp64 exclusive scan of the runs
+// in LDS, then the running sums (times log2 e, fp32) written out.  Padded to
+// Lp with the last value (padded keys only meet masked scores).
+__global__ __launch_bounds__(256) void gate_scan_kernel(const float* __restrict__ logf,
+                                                        float* __restrict__ gate2, int L, int Lp) {
+  __shared__ double s_run[256];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int seg = (Lp + 255) / 256;
+  const int t0 = tid * seg;
+  const float* src = logf + (size_t)bh * L;
+  double tot = 0.0;
+  for (int t = t0; t < min(t0 + seg, L); ++t) tot += (double)fminf(src[t], 0.f);
+  s_run[tid] = tot;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of the runs (Hillis-Steele)
+    const double x = (tid >= off) ? s_run[tid - off] : 0.0;
+    __syncthreads();
+    s_run[tid] += x;
+    __syncthreads();
+  }
+  double run = s_run[tid] - tot;  // exclusive prefix of this run
+  float* dst = gate2 + (size_t)bh * Lp;
+  for (int t = t0; t < min(t0 + seg, Lp); ++t) {
+    if (t < L) run += (double)fminf(src[t], 0.f);
+    dst[t] = (float)(run * 1.4426950408889634);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gate_scan(const Geometry& g, const float* logf, float* gate2, hipStream_t stream) {
+  hipLaunchKernelGGL(gate_scan_kernel, dim3(g.B * g.H), dim3(256), 0, stream, logf, gate2, g.L, g.Lp);
+  return hipGetLastError();
+}
 
 hipError_t launch_rotate_qkv(const Geometry& g, const void* q, const void* k, const void* v,
                              const float* theta, uint16_t* qr, uint16_t* kr, uint16_t* vt,

@@ -193,6 +193,37 @@ def backward_leg(binding, torch, dev, w, q, k, v, phi, alibi, steps: int = 20) -
             "outputs": "dq, dk, dv (bf16), dtheta, dphi (fp32)"}
 
 
+def forget_leg(binding, torch, dev, w, q, k, v, phi, steps: int = 20) -> dict:
+    """The same forward with the forget-gate bias (arp_forward_ex: scan, rotation
+    pass, gate prefix pass, attention) against the same call without gates,
+    each timed whole between events.  Gates log sigmoid(z), z ~ N(2, 1),
+    seeded."""
+    if w.dtype != "bf16":
+        return None
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    z = torch.randn(w.batch, w.heads, w.seqlen, device=dev, generator=g) + 2.0
+    logf = torch.nn.functional.logsigmoid(z).contiguous()
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(gates):
+        for _ in range(5):
+            binding.forward_ex(q, k, v, phi, rotate_v=w.rotate_v, logf=gates)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            binding.forward_ex(q, k, v, phi, rotate_v=w.rotate_v, logf=gates)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    with_g, without = timed(logf), timed(None)
+    return {"workload": w.name, "ms_with_gate": round(with_g, 4), "ms_without": round(without, 4),
+            "tflops_with_gate": round(w.flops / (with_g * 1e-3) / 1e12, 2)}
+
+
 def decode_leg(binding, torch, dev, steps: int = 50) -> dict:
     """Decode steps at a full context: the token at the last position attends
     to every cached row.  Two cache shapes: extrap_16k's (B=2, H=8, 16384
@@ -363,6 +394,7 @@ def main():
     if not args.fused:
         result["backward"] = backward_leg(binding, torch, dev, w, q, k, v, phi, alibi)
         result["decode"] = decode_leg(binding, torch, dev)
+        result["forget_gate"] = forget_leg(binding, torch, dev, w, q, k, v, phi)
     if not args.no_cpu_baseline:
         import oracle
         of = (oracle.ROTATE_QK | (oracle.ROTATE_V if w.rotate_v else 0) |

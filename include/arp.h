@@ -82,7 +82,9 @@ typedef enum arp_dtype {
 #define ARP_SCAN_EXCLUSIVE 0x10u  /* Theta_t = sum_{s<t} phi_s (route steps j..i-1) */
 #define ARP_FUSED_ROTATION 0x20u  /* bf16: rotate k/v while staging tiles in LDS
                                      instead of a separate pre-rotation pass */
-#define ARP_ALL_FLAGS 0x3Fu
+#define ARP_FORGET_GATE 0x40u     /* add the forget-gate bias sum_{s=j+1}^{i} log f_s (bf16,
+                                     pre-rotation path, arp_forward_ex only) */
+#define ARP_ALL_FLAGS 0x7Fu
 
 typedef struct arp_desc {
   int32_t batch;
@@ -161,6 +163,21 @@ arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k,
                              const float* phi, const float* alibi, float* theta, void* o,
                              float* lse, void* scan_state, size_t scan_state_bytes,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole forward with every option: arp_forward plus
+ *  - lse (NULL, or float32 [batch, heads, seqlen]: as in arp_forward_train),
+ *  - logf (required with ARP_FORGET_GATE, else ignored): float32
+ *    [batch, heads, seqlen] log forget gates log f_t; score (i, j) gets
+ *    sum_{s=j+1}^{i} log f_s, the route's product of gates outside the
+ *    exponential (the PaTH reading notes' Sec. 2.5; named as far-mass control
+ *    beside the distance bias in Sec. 4 of the method paper).  Gates are at
+ *    most 1: values log f_t > 0 are taken as 0.
+ * bf16 with the pre-rotation path only (ARP_ERR_UNSUPPORTED otherwise); every
+ * other entry point returns ARP_ERR_INVALID_ARG when ARP_FORGET_GATE is set. */
+arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, const void* v,
+                          const float* phi, const float* alibi, const float* logf, float* theta,
+                          void* o, float* lse, void* scan_state, size_t scan_state_bytes,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of the backward workspace for desc (bf16 only; 0 otherwise): the bf16
  * operands of the gradient kernels (rotated q scaled by scale*log2(e), k, v

@@ -52,7 +52,7 @@ def _desc(**kw):
     (dict(head_dim=63), b.ERR_INVALID_ARG),
     (dict(head_dim=96), b.ERR_UNSUPPORTED),
     (dict(head_dim=32), b.ERR_UNSUPPORTED),
-    (dict(flags=0x40), b.ERR_INVALID_ARG),
+    (dict(flags=0x80), b.ERR_INVALID_ARG),
     (dict(seqlen=(1 << 24) + 1), b.ERR_INVALID_ARG),
 ])
 def test_check_descriptor(kw, status):

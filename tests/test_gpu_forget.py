@@ -1,0 +1,85 @@
+"""GPU parity of the forget-gate bias (arp_forward_ex with ARP_FORGET_GATE)
+against the fp64 oracle.  Gates: log f_t = log sigmoid(z), z ~ N(2, 1) per
+(b, h, t), seeded (open on average, with some tokens strongly forgetting).
+Bar: the forward's bf16 bar, max |err| <= 2e-2."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from accumulated_rotation_positional_amd import binding
+from accumulated_rotation_positional_amd import workloads as wl
+from gpu_util import assert_close, oracle_flags, sample_rows, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _gates(w, seed=21, mean=2.0):
+    z = np.random.default_rng(seed).normal(mean, 1.0, size=(w.batch, w.heads, w.seqlen))
+    return (-np.logaddexp(0.0, -z)).astype(np.float32)  # log sigmoid(z)
+
+
+def _run(w, logf, *, rotate_v=False, alibi=False, with_lse=False):
+    say(f"[gpu] forget {w.name} B={w.batch} H={w.heads} L={w.seqlen} d={w.head_dim} v={rotate_v} "
+        f"alibi={alibi}")
+    al = to_dev(wl.alibi_slopes(w.heads)) if alibi else None
+    o, theta, lse = binding.forward_ex(to_dev(w.q), to_dev(w.k), to_dev(w.v), to_dev(w.phi),
+                                       rotate_qk=True, rotate_v=rotate_v, alibi=al,
+                                       logf=to_dev(logf), with_lse=with_lse)
+    torch.cuda.synchronize()
+    return to_host(o), None if lse is None else lse.cpu().numpy()
+
+
+def _oracle(w, logf, rotate_v, alibi):
+    return oracle.Problem(w.q, w.k, w.v, w.phi,
+                          oracle_flags(True, rotate_v, alibi) | oracle.FORGET,
+                          alibi=wl.alibi_slopes(w.heads) if alibi else None, logf=logf)
+
+
+@pytest.mark.parametrize("alibi", [False, True])
+@pytest.mark.parametrize("rotate_v", [False, True])
+@pytest.mark.parametrize("name,L", [("train_1k", 333), ("rope_8k_d128", 200)])
+def test_forget_gate_small(name, L, rotate_v, alibi):
+    w = wl.make(name, batch=2, heads=3, seqlen=L)
+    logf = _gates(w)
+    got, _ = _run(w, logf, rotate_v=rotate_v, alibi=alibi)
+    assert_close(got, _oracle(w, logf, rotate_v, alibi).output(), "bf16",
+                 f"forget {name} L={L} v={rotate_v} alibi={alibi}")
+
+
+@pytest.mark.parametrize("L", [1, 65, 257, 700])
+def test_forget_gate_ragged_and_strong(L):
+    """Strong forgetting (z ~ N(0, 1)): attention is nearly local, which the
+    bound on the scores must still get right."""
+    w = wl.make("train_1k", batch=1, heads=2, seqlen=L)
+    logf = _gates(w, seed=22, mean=0.0)
+    got, _ = _run(w, logf, rotate_v=True)
+    assert_close(got, _oracle(w, logf, True, False).output(), "bf16", f"forget strong L={L}")
+
+
+def test_forget_gate_open_equals_plain_forward():
+    w = wl.make("train_1k", batch=1, heads=2, seqlen=300)
+    logf = np.zeros((1, 2, 300), dtype=np.float32)
+    got, _ = _run(w, logf, rotate_v=True)
+    ref, _ = binding.forward(to_dev(w.q), to_dev(w.k), to_dev(w.v), to_dev(w.phi), rotate_v=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(got, to_host(ref))
+
+
+def test_forget_gate_full_size_sampled_rows():
+    w = wl.make("extrap_16k")
+    logf = _gates(w)
+    got, _ = _run(w, logf, rotate_v=True)
+    rows = sample_rows(w)
+    want = _oracle(w, logf, True, False).rows(rows)
+    assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", "forget extrap_16k sampled rows")
+
+
+def test_forget_gate_rejected_elsewhere():
+    w = wl.make("train_1k", batch=1, heads=1, seqlen=64)
+    flags = binding.flags_for(forget=True)
+    desc = binding.make_desc(1, 1, 64, 64, "bf16", flags)
+    q = to_dev(w.q)
+    with pytest.raises(binding.ArpError) as e:
+        binding.attn_fwd(q, q, q, to_dev(w.phi), desc)
+    assert e.value.status == binding.ERR_INVALID_ARG
