@@ -10,9 +10,11 @@
 //
 // Work decomposition
 //  * A workgroup owns BM = NW * QPW consecutive queries of one (batch, head)
-//    and walks the key tiles j0 = 0, BN, 2BN, ... up to its last query.
-//    Each of its NW waves owns QPW queries; a wave skips the tiles past its
-//    own last query and masks only the tile that holds its diagonal.
+//    and walks the key tiles j0 = 0, BN, 2BN, ... up to its last query (with
+//    a distance or gate bias: from its last query back to key 0, stopping
+//    once every remaining probability is exactly zero).  Each of its NW
+//    waves owns QPW queries; a wave skips the tiles past its own last query
+//    and masks only the tile that holds its diagonal.
 //  * Both products put the query on the matrix-core N axis, so one lane owns
 //    one query and the softmax row statistics are per lane:
 //      S^T [keys x queries] = K~ [keys x D] . Q~^T          (v_mfma_f32_32x32x16_bf16)
@@ -46,6 +48,10 @@ namespace {
 
 constexpr int BN = KEY_TILE;  // keys per tile
 constexpr float TAU = 8.0f;   // lazy-rescale threshold (base-2 logits)
+// A tile whose logits all lie more than ZGAP below the running maximum has
+// probabilities 2^(s - m) < 2^-160, below fp32's smallest subnormal (2^-149):
+// every one of them is exactly zero, so skipping the tile changes no bit.
+constexpr float ZGAP = 160.0f;
 
 // FUSED = false: q~, k~ (L padded to Lp) and v~^T come pre-rotated from the
 // rotation pass, K/V tiles load straight into LDS, and the per-tile key-norm
@@ -107,6 +113,14 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
   const int qw = q0 + wave * QPW;  // first query of this wave
   const int last_tile = min(q0 + BM - 1, L - 1) / BN;
   const int last_w = (qw < L) ? min(qw + QPW - 1, L - 1) / BN : -1;
+  // With a bias the key tiles are walked from the diagonal back to key 0:
+  // both biases only fall with the distance (the gate prefix never rises), so
+  // the first tile holds every row's largest biases, later tiles rarely raise
+  // the running maximum, and once a bound on every remaining logit is ZGAP
+  // below it the wave is done.  Unbiased attention walks forward, so the
+  // workgroups of a head stream the same tiles through L2 together.
+  constexpr bool DESC = (BIAS != 0) && !FUSED;
+  auto tile_at = [&](int step) { return DESC ? last_tile - step : step; };
 
   // ---- direct global -> LDS loads of one K~ / V~^T tile ----
   const uint16_t* kbase = kr + (size_t)bh * Lp * D;
@@ -243,7 +257,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
   if constexpr (!FUSED) {
 #pragma unroll
     for (int t = 0; t < NST - 1; ++t)
-      if (t <= last_tile) issue(t, smem + t * STAGE);
+      if (t <= last_tile) issue(tile_at(t), smem + t * STAGE);
   } else {
     fetch(0);
     commit(smem);
@@ -272,6 +286,24 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
   for (int qb = 0; qb < QB; ++qb)
     gq[qb] = FORGET ? gate2[(size_t)bh * Lp + min(qw + 32 * qb + ln, Lp - 1)] : 0.f;
 
+  // Biased walk: a bound on the logits of the tile in flight (tb), the
+  // largest key norm of the wave's tiles (kglob), and per-wave "done" flags,
+  // kept per step parity so that a flag set in step n is read in step n+1
+  // after the barrier and no wave writes that parity before every wave has
+  // read it.  A wave with no query below L is done from the start.
+  float tb[QB];
+  float kglob = 0.f;
+  __shared__ int wdone[2][DESC ? NW : 1];
+  bool wave_done = false;
+  if constexpr (DESC) {
+    for (int c = lane; c <= last_w; c += 64) kglob = fmaxf(kglob, kmax_bh[c]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) kglob = fmaxf(kglob, __shfl_xor(kglob, off));
+    wave_done = last_w < 0;
+    if (lane == 0) wdone[0][wave] = wdone[1][wave] = wave_done ? 1 : 0;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  }
+
   // ---- the three parts of one key tile of this wave's queries ----
   f32x16 s[KB][QB];      // logits of the tile in flight
   bf16x8 pop[KS2][QB];   // its probabilities, P^T operand layout
@@ -296,60 +328,58 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
 
   };
 
-  auto soft = [&](int n) __attribute__((always_inline)) {
-    const int j0 = n * BN;
+  // n: step (ring stage n % NST), t: key tile, first: the wave's first tile.
+  auto soft = [&](int n, int t, bool first) __attribute__((always_inline)) {
+    const int j0 = t * BN;
     // Element r of s[kb][qb] on this lane is key j0 + koff(kb, r) + 8 hf,
     // koff = 32 kb + 16 (r>>3) + 4 ((r>>2)&1) + (r&3); query qw + 32 qb + ln.
-    const bool diag = (n == last_w);
+    const bool diag = (t == last_w);
     if (ALIBI || FORGET || diag) {
-      // the tile's key gates for this lane's elements: keys koff + 8 hf
-      float gk[KB][16];
-      if constexpr (FORGET) {
-        const float* gt = reinterpret_cast<const float*>(smem + (n % NST) * STAGE + KTILE + VTILE);
+      const float* gt = reinterpret_cast<const float*>(smem + (n % NST) * STAGE + KTILE + VTILE);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(gt + 32 * kb + 16 * h2 + 8 * hf);
-            const f32x4 c = *reinterpret_cast<const f32x4*>(gt + 32 * kb + 16 * h2 + 8 * hf + 4);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          // elements r = 8 h2 + e: keys koff + 8 hf, koff = 32 kb + 16 h2 + e (+4 for e >= 4)
+          f32x4 ga = {}, gc = {};
+          if constexpr (FORGET) {
+            ga = *reinterpret_cast<const f32x4*>(gt + 32 * kb + 16 * h2 + 8 * hf);
+            gc = *reinterpret_cast<const f32x4*>(gt + 32 * kb + 16 * h2 + 8 * hf + 4);
+          }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              gk[kb][8 * h2 + e] = a[e];
-              gk[kb][8 * h2 + 4 + e] = c[e];
+          for (int qb = 0; qb < QB; ++qb) {
+            const int base = j0 + 8 * hf - (qw + 32 * qb + ln);  // key - query minus koff
+            const float fb = slope2 * (float)base;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * h2 + e;
+              const int koff = 32 * kb + 16 * h2 + 4 * (e >> 2) + (e & 3);
+              float x = s[kb][qb][r];
+              if (ALIBI) x += fmaf(slope2, (float)koff, fb);
+              if (FORGET) x += gq[qb] - (e < 4 ? ga[e] : gc[e - 4]);
+              if (diag && koff + base > 0) x = -INFINITY;
+              s[kb][qb][r] = x;
             }
           }
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int base = j0 + 8 * hf - (qw + 32 * qb + ln);  // key - query minus koff
-        const float fb = slope2 * (float)base;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int koff = 32 * kb + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
-            float x = s[kb][qb][r];
-            if (ALIBI) x += fmaf(slope2, (float)koff, fb);
-            if (FORGET) x += gq[qb] - gk[kb][r];
-            if (diag && koff + base > 0) x = -INFINITY;
-            s[kb][qb][r] = x;
-          }
-      }
+        }
     }
 
     // Row maxima of the shifted logits (both half-waves) -- only when the
-    // tile might need them: s_ij <= |q~_i| max_j |k~_j| (Cauchy-Schwarz; the
-    // distance bias and the mask only lower scores), so while that bound
-    // stays within TAU of the running maximum no rescale can be due.
-    bool check = FUSED || (n == 0);
-    if constexpr (!FUSED) {
-      const float km = kmax_bh[n];
+    // tile might need them: s_ij <= |q~_i| max_j |k~_j| (Cauchy-Schwarz) plus
+    // the tile's largest bias (the mask only lowers scores), so while that
+    // bound stays within TAU of the running maximum no rescale can be due.
+    bool check = FUSED || first;
+    if constexpr (DESC) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) check |= (tb[qb] > mrun[qb] + TAU);
+    } else if constexpr (!FUSED) {
+      const float km = kmax_bh[t];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) check |= (qn[qb] * km > mrun[qb] + TAU);
     }
     if (__any(check)) {
     float mx[QB];
-    bool need = (n == 0);
+    bool need = first;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // a chain of three-input maxima (v_max3_f32), two new values per step
@@ -365,12 +395,12 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     if (__any(need)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float delta = (n == 0) ? mx[qb] : fmaxf(mx[qb], 0.f);
+        const float delta = first ? mx[qb] : fmaxf(mx[qb], 0.f);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[kb][qb][r] -= delta;
-        if (n != 0) {
+        if (!first) {
           const float alpha = __builtin_amdgcn_exp2f(-delta);
           lsum[qb] *= alpha;
 #pragma unroll
@@ -425,21 +455,68 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     // ---- key loop: NST-stage ring; tile n+NST-1 is loaded while n is computed ----
     constexpr int LOADS = KLD + VLD;  // direct loads per wave per tile
     for (int n = 0; n <= last_tile; ++n) {
-      // tile n has landed once at most the loads of the tiles after it are pending
+      const int t = tile_at(n);
+      // step n's tile has landed once at most the loads of the steps after it are pending
       if (n + NST - 2 <= last_tile) wait_loads<(NST - 2) * LOADS>();
       else wait_loads<0>();
-      // Every wave's share of tile n is in place and every wave is done with
-      // tile n-1 (whose stage the next issue overwrites).  A bare s_barrier:
-      // the wait above already covers this wave's loads, and a fenced barrier
-      // would also wait for the loads of the tiles still in flight.
+      // Every wave's share of step n's tile is in place and every wave is
+      // done with step n-1 (whose stage the next issue overwrites).  A bare
+      // s_barrier: the wait above already covers this wave's loads, and a
+      // fenced barrier would also wait for the loads of the tiles still in
+      // flight.
       __builtin_amdgcn_s_barrier();
-      if (n + NST - 1 <= last_tile) issue(n + NST - 1, smem + ((n + NST - 1) % NST) * STAGE);
-      if (n <= last_w) {
+      if constexpr (DESC) {
+        if (n > 0) {  // the flags of step n-1, the same for every wave
+          bool all = true;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) all &= wdone[(n - 1) & 1][w] != 0;
+          if (all) break;
+        }
+      }
+      if (n + NST - 1 <= last_tile) issue(tile_at(n + NST - 1), smem + ((n + NST - 1) % NST) * STAGE);
+      if constexpr (DESC) {
+        if (t <= last_w && !wave_done) {
+          // Bound the tile's logits per row: the key-norm bound plus the
+          // tile's largest bias (distance bias at the tile end nearer the
+          // query -- the far end for a negative slope -- and the gate bias
+          // at its last key, where the non-increasing prefix is lowest).
+          // With the wave-wide key-norm maximum and a non-negative slope the
+          // same bound covers every tile not yet walked.
+          const bool first = (t == last_w);
+          const float km = kmax_bh[t];
+          const float gl = FORGET ? reinterpret_cast<const float*>(
+                                        smem + (n % NST) * STAGE + KTILE + VTILE)[BN - 1]
+                                  : 0.f;
+          bool dead = !first && !(ALIBI && slope2 < 0.f);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const int i = qw + 32 * qb + ln;
+            float bb = 0.f;
+            if (ALIBI)
+              bb = fmaxf(slope2 * (float)(t * BN - i), slope2 * (float)(t * BN + BN - 1 - i));
+            if (FORGET) bb += gq[qb] - gl;
+            tb[qb] = fmaf(qn[qb], km, bb);
+            dead &= (i >= L) || (fmaf(qn[qb], kglob, bb) < mrun[qb] - ZGAP);
+          }
+          if (__all(dead)) {
+            wave_done = true;
+          } else {
+            qk(n);
+            soft(n, t, first);
+            pv(n);
+          }
+        }
+        if (wave_done && lane == 0) {
+          wdone[n & 1][wave] = 1;
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the flag is in LDS before the next barrier
+        }
+      } else if (n <= last_w) {
         qk(n);
-        soft(n);
+        soft(n, t, n == 0);
         pv(n);
       }
     }
+    if constexpr (DESC) wait_loads<0>();  // no load into LDS outlives an early exit
   } else {
     // ---- key loop, fused rotation: tile n+1 is fetched into registers while
     // n is computed, then rotated into the other stage ----
@@ -447,7 +524,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
       if (n + 1 <= last_tile) fetch(n + 1);
       if (n <= last_w) {
         qk(n);
-        soft(n);
+        soft(n, n, n == 0);
         pv(n);
       }
       if (n + 1 <= last_tile) commit(smem + ((n + 1) & 1) * STAGE);
