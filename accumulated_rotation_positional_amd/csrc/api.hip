@@ -84,6 +84,8 @@ WorkspaceLayout workspace_layout(const Geometry& g) {
     if (g.flags & ARP_FORGET_GATE) {
       lay.gate_off = off;
       off += align_up((size_t)g.B * g.H * g.Lp * sizeof(float));
+      lay.gate_tot_off = off;
+      off += align_up((size_t)g.B * g.H * gate_chunks(g) * sizeof(double));
     }
   }
   lay.total = off;
@@ -308,7 +310,9 @@ arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, co
                         reinterpret_cast<float*>(ws + lay.kmax_off), s);
   if (e != hipSuccess) return ARP_ERR_HIP;
   float* gate2 = gated(g) ? reinterpret_cast<float*>(ws + lay.gate_off) : nullptr;
-  if (gated(g) && launch_gate_scan(g, logf, gate2, s) != hipSuccess) return ARP_ERR_HIP;
+  if (gated(g) && launch_gate_scan(g, logf, gate2, reinterpret_cast<double*>(ws + lay.gate_tot_off),
+                                   s) != hipSuccess)
+    return ARP_ERR_HIP;
   return hip_status(launch_attn_bf16_rotated(
       g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
       reinterpret_cast<const uint16_t*>(ws + lay.k_off),

@@ -38,6 +38,7 @@ struct WorkspaceLayout {
   size_t q_off, k_off, vt_off, operand_bytes;  // each operand block
   size_t kmax_off;                             // float [B*H][Lp/64]: max |k~| per key tile
   size_t gate_off;                             // float [B*H][Lp]: gate prefix (ARP_FORGET_GATE)
+  size_t gate_tot_off;                         // double [B*H][gate_chunks]: chunk totals
   size_t total;
 };
 constexpr int KEY_TILE = 64;  // keys per tile of the attention kernel (and per kmax entry)
@@ -54,8 +55,12 @@ hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const
                                     const float* alibi, const float* gate2, uint16_t* o,
                                     float* lse, hipStream_t stream);
 // Forget gates: gate2[b*H + h][t] = log2 e * sum_{s <= t} min(logf[b, h, s], 0), fp64
-// accumulation, padded to Lp with the last value.
-hipError_t launch_gate_scan(const Geometry& g, const float* logf, float* gate2, hipStream_t stream);
+// accumulation, padded to Lp with the last value; totals holds one double per
+// (b*H + h, chunk of GATE_CHUNK tokens).
+constexpr int GATE_CHUNK = 1024;
+inline int gate_chunks(const Geometry& g) { return (g.Lp + GATE_CHUNK - 1) / GATE_CHUNK; }
+hipError_t launch_gate_scan(const Geometry& g, const float* logf, float* gate2, double* totals,
+                            hipStream_t stream);
 hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const float* theta, const float* alibi,
                                   uint16_t* o, hipStream_t stream);

@@ -147,39 +147,94 @@ __global__ __launch_bounds__(256) void rotate_diag_kernel(const TIn* __restrict_
   out[2 * i + 1] = bb;
 }
 
-// Forget-gate prefix per (b, h): one workgroup per head, each thread a
-// contiguous run of tokens; fp64 run sums, an fp64 exclusive scan of the runs
-// in LDS, then the running sums (times log2 e, fp32) written out.  Padded to
-// Lp with the last value (padded keys only meet masked scores).
-__global__ __launch_bounds__(256) void gate_scan_kernel(const float* __restrict__ logf,
-                                                        float* __restrict__ gate2, int L, int Lp) {
-  __shared__ double s_run[256];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int seg = (Lp + 255) / 256;
-  const int t0 = tid * seg;
-  const float* src = logf + (size_t)bh * L;
-  double tot = 0.0;
-  for (int t = t0; t < min(t0 + seg, L); ++t) tot += (double)fminf(src[t], 0.f);
-  s_run[tid] = tot;
+// Forget-gate prefix G_t = log2 e * sum_{s<=t} min(log f_s, 0) per (b, h), in
+// chunks of GATE_CHUNK tokens: gate_totals sums each chunk (fp64), then
+// gate_apply adds the totals of the earlier chunks to an in-chunk scan (fp64)
+// and writes G (fp32).  Padded to Lp with the last value (padded keys only
+// meet masked scores).  Loads are coalesced; each thread then scans four
+// consecutive tokens from LDS.
+constexpr int GATE_THREADS = 256;
+constexpr int GATE_PER_THREAD = GATE_CHUNK / GATE_THREADS;
+static_assert(GATE_PER_THREAD == 4, "four consecutive tokens per thread");
+
+__device__ __forceinline__ double block_sum_256(double x, double* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of the runs (Hillis-Steele)
-    const double x = (tid >= off) ? s_run[tid - off] : 0.0;
-    __syncthreads();
-    s_run[tid] += x;
-    __syncthreads();
+  const double t = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return t;
+}
+
+__global__ __launch_bounds__(GATE_THREADS) void gate_totals_kernel(const float* __restrict__ logf,
+                                                                   double* __restrict__ tot, int L,
+                                                                   int nch) {
+  __shared__ double red[4];
+  const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const float* src = logf + (size_t)bh * L;
+  double x = 0.0;
+#pragma unroll
+  for (int e = 0; e < GATE_PER_THREAD; ++e) {
+    const int t = c * GATE_CHUNK + e * GATE_THREADS + tid;
+    if (t < L) x += (double)fminf(src[t], 0.f);
   }
-  double run = s_run[tid] - tot;  // exclusive prefix of this run
-  float* dst = gate2 + (size_t)bh * Lp;
-  for (int t = t0; t < min(t0 + seg, Lp); ++t) {
-    if (t < L) run += (double)fminf(src[t], 0.f);
-    dst[t] = (float)(run * 1.4426950408889634);
+  x = block_sum_256(x, red);
+  if (tid == 0) tot[(size_t)bh * nch + c] = x;
+}
+
+__global__ __launch_bounds__(GATE_THREADS) void gate_apply_kernel(const float* __restrict__ logf,
+                                                                  const double* __restrict__ tot,
+                                                                  float* __restrict__ gate2, int L,
+                                                                  int Lp, int nch) {
+  __shared__ float sv[GATE_CHUNK];
+  __shared__ double red[4], wsum[4];
+  const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  double carry = 0.0;  // the earlier chunks
+  for (int i = tid; i < c; i += GATE_THREADS) carry += tot[(size_t)bh * nch + i];
+  carry = block_sum_256(carry, red);
+  const float* src = logf + (size_t)bh * L;
+#pragma unroll
+  for (int e = 0; e < GATE_PER_THREAD; ++e) {
+    const int t = c * GATE_CHUNK + e * GATE_THREADS + tid;
+    sv[e * GATE_THREADS + tid] = (t < L) ? fminf(src[t], 0.f) : 0.f;
+  }
+  __syncthreads();
+  const float4 mine = *reinterpret_cast<const float4*>(sv + GATE_PER_THREAD * tid);
+  double run[GATE_PER_THREAD];
+  run[0] = (double)mine.x;
+  run[1] = run[0] + (double)mine.y;
+  run[2] = run[1] + (double)mine.z;
+  run[3] = run[2] + (double)mine.w;
+  double x = run[3];  // inclusive scan of the thread totals within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  double pre = carry + (x - run[3]);
+  for (int i = 0; i < w; ++i) pre += wsum[i];
+  const int t0 = c * GATE_CHUNK + GATE_PER_THREAD * tid;
+  if (t0 < Lp) {  // Lp is a multiple of 256, so all four tokens are below it
+    constexpr double LOG2E_D = 1.4426950408889634;
+    const float4 out = make_float4((float)((pre + run[0]) * LOG2E_D), (float)((pre + run[1]) * LOG2E_D),
+                                   (float)((pre + run[2]) * LOG2E_D), (float)((pre + run[3]) * LOG2E_D));
+    *reinterpret_cast<float4*>(gate2 + (size_t)bh * Lp + t0) = out;
   }
 }
 
 }  // namespace
 
-hipError_t launch_gate_scan(const Geometry& g, const float* logf, float* gate2, hipStream_t stream) {
-  hipLaunchKernelGGL(gate_scan_kernel, dim3(g.B * g.H), dim3(256), 0, stream, logf, gate2, g.L, g.Lp);
+hipError_t launch_gate_scan(const Geometry& g, const float* logf, float* gate2, double* totals,
+                            hipStream_t stream) {
+  const int nch = gate_chunks(g);
+  const dim3 grid(nch, g.B * g.H);
+  hipLaunchKernelGGL(gate_totals_kernel, grid, dim3(GATE_THREADS), 0, stream, logf, totals, g.L, nch);
+  hipLaunchKernelGGL(gate_apply_kernel, grid, dim3(GATE_THREADS), 0, stream, logf, totals, gate2,
+                     g.L, g.Lp, nch);
   return hipGetLastError();
 }
 

@@ -111,8 +111,9 @@ arp_status arp_check(const arp_desc* desc);
 size_t arp_scan_state_bytes(const arp_desc* desc);
 
 /* Bytes of the operand workspace for desc: the rotated bf16 q~, k~, v~^T of
- * the pre-rotation path; 0 for fp32 I/O or ARP_FUSED_ROTATION (and when desc is
- * invalid). */
+ * the pre-rotation path, per-tile key-norm maxima, and with ARP_FORGET_GATE the
+ * gate prefix and its chunk totals; 0 for fp32 I/O or ARP_FUSED_ROTATION (and
+ * when desc is invalid). */
 size_t arp_workspace_bytes(const arp_desc* desc);
 
 /* a1. Accumulated angles: theta[b,g,t,p] = wrap(sum_{s<=t} phi[b,g,s,p]) in
