@@ -50,6 +50,14 @@ def alibi_slopes(heads: int) -> np.ndarray:
     return np.power(2.0, -8.0 * h / heads).astype(np.float32)
 
 
+def rope_frequencies(head_dim: int, base: float = None) -> np.ndarray:
+    """RoPE's log-spaced per-pair frequencies base^(-2p/d), p = 0..d/2-1, as fp32
+    (also the bounds f_b of the random-angle variant)."""
+    base = ROPE_BASE if base is None else base
+    p = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(base, -2.0 * p / head_dim).astype(np.float32)
+
+
 def causal_pairs(seqlen: int) -> int:
     """(query, key) pairs with key <= query in one head."""
     return seqlen * (seqlen + 1) // 2

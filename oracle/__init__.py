@@ -18,7 +18,11 @@ score of the method paper's App. B.6, and the RoPE post's worked numbers);
 the gradients by ``tests/test_oracle_backward.py`` (central differences of
 the forward, the one-token closed form, invariance under a common angle
 shift, the column-sum identities of softmax attention, and the textbook
-attention gradient of a library autodiff).
+attention gradient of a library autodiff); the forget-gate bias by
+``tests/test_oracle_forget.py``; the on-the-fly step angles by
+``tests/test_oracle_generators.py`` (Philox4x64-10 against numpy's independent
+Philox generator, the counter layout with numpy's words, uniformity, the token
+and constant sources against explicit loops).
 """
 from __future__ import annotations
 
@@ -94,6 +98,13 @@ def _lib() -> ctypes.CDLL:
         lib.oracle_backward.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_int,
                                         dp, dp, dp, dp, dp]
         lib.oracle_backward.restype = ctypes.c_int
+        u64p = ctypes.POINTER(ctypes.c_uint64)
+        lib.oracle_philox4x64_10.argtypes = [u64p, u64p, u64p]
+        lib.oracle_philox4x64_10.restype = None
+        lib.oracle_random_phi.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint64,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_random_phi.restype = None
         _LIB = lib
     return _LIB
 
@@ -139,6 +150,49 @@ def rotate_rows(x: np.ndarray, angle: np.ndarray, inverse: bool = False) -> np.n
     _lib().oracle_rotate_rows(x.ctypes.data, _io_dtype(x), _dptr(ang), nrows, d, int(inverse),
                               _dptr(out))
     return out
+
+
+def philox4x64_10(counter, key) -> np.ndarray:
+    """The four 64-bit words of the Philox4x64-10 block for a 4-word counter and
+    a 2-word key (Salmon et al., SC 2011)."""
+    c = np.ascontiguousarray(counter, dtype=np.uint64)
+    k = np.ascontiguousarray(key, dtype=np.uint64)
+    assert c.shape == (4,) and k.shape == (2,)
+    out = np.empty(4, dtype=np.uint64)
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    _lib().oracle_philox4x64_10(c.ctypes.data_as(u64p), k.ctypes.data_as(u64p),
+                                out.ctypes.data_as(u64p))
+    return out
+
+
+def random_phi(batch: int, phi_heads: int, seqlen: int, npairs: int, seed: int, step: int,
+               bound) -> np.ndarray:
+    """Random step angles [B, Hphi, L, P] (fp32) of the method paper's random
+    variant: uniform on (-bound[g, p], bound[g, p]), one Philox word per
+    element (see arp_oracle.h for the counter layout)."""
+    bound = np.ascontiguousarray(bound, dtype=np.float32)
+    assert bound.shape == (phi_heads, npairs)
+    out = np.empty((batch, phi_heads, seqlen, npairs), dtype=np.float32)
+    _lib().oracle_random_phi(batch, phi_heads, seqlen, npairs, int(seed), int(step),
+                             bound.ctypes.data, out.ctypes.data)
+    return out
+
+
+def token_phi(tokens, table) -> np.ndarray:
+    """Step angles of the learned token-rotation variant: phi[b, g, t, p] =
+    table[tokens[b, t], g, p] (tokens [B, L] integers in [0, V), table
+    [V, Hphi, P] fp32)."""
+    tokens = np.asarray(tokens)
+    table = np.asarray(table, dtype=np.float32)
+    return np.ascontiguousarray(table[tokens].transpose(0, 2, 1, 3))
+
+
+def constant_phi(batch: int, seqlen: int, freq) -> np.ndarray:
+    """Position-independent step angles (RoPE, or per-head learned frequencies):
+    phi[b, g, t, p] = freq[g, p]."""
+    freq = np.asarray(freq, dtype=np.float32)
+    return np.ascontiguousarray(np.broadcast_to(freq[None, :, None, :],
+                                                (batch, freq.shape[0], seqlen, freq.shape[1])))
 
 
 class Problem:

@@ -106,6 +106,62 @@ void oracle_angle_scan(const float* phi, int64_t nseg, int64_t seqlen, int64_t n
   }
 }
 
+/* ---- Step angles drawn on the fly ----------------------------------------
+ * Philox4x64-10, the counter-based generator of Salmon, Moraes, Dror and Shaw
+ * ("Parallel random numbers: as easy as 1, 2, 3", SC 2011).  A block of four
+ * 64-bit words is a pure function of a 256-bit counter and a 128-bit key: ten
+ * rounds, each multiplying words 0 and 2 by two fixed odd constants; the low
+ * halves of the products become words 3 and 1, the high halves xor'd with
+ * the other two words and the key become words 2 and 0; between rounds the
+ * key grows by two Weyl increments (the golden ratio and sqrt(3) - 1 in
+ * 64-bit fixed point). */
+__extension__ typedef unsigned __int128 oracle_u128;
+
+void oracle_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
+  const uint64_t m0 = 0xD2E7470EE14C6C93ull, m1 = 0xCA5A826395121157ull;
+  const uint64_t w0 = 0x9E3779B97F4A7C15ull, w1 = 0xBB67AE8584CAA73Bull;
+  uint64_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+  uint64_t k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += w0;
+      k1 += w1;
+    }
+    const oracle_u128 p0 = (oracle_u128)m0 * c[0];
+    const oracle_u128 p1 = (oracle_u128)m1 * c[2];
+    const uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+    const uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+  for (int i = 0; i < 4; ++i) out[i] = c[i];
+}
+
+/* The random variant's step angles ("Why Do Accumulated Transformations
+ * Extrapolate?", App. D "Model variants": independent per position and pair,
+ * uniform on (-f_b, f_b), redrawn every forward pass).  Element
+ * n = ((b * phi_heads + g) * seqlen + t) * npairs + p takes word n mod 4 of
+ * the Philox block at counter (n / 4, step, 0, 0) under key (seed, 0); its top
+ * 53 bits give u in [0, 1), and phi = bound[g][p] * (2u - 1), formed in fp64
+ * and rounded once to fp32.  step numbers the draws (one per forward pass). */
+void oracle_random_phi(int64_t batch, int64_t phi_heads, int64_t seqlen, int64_t npairs,
+                       uint64_t seed, uint64_t step, const float* bound, float* phi) {
+  const uint64_t key[2] = {seed, 0};
+  const int64_t n_all = batch * phi_heads * seqlen * npairs;
+  for (int64_t n = 0; n < n_all; ++n) {
+    const uint64_t ctr[4] = {(uint64_t)n / 4, step, 0, 0};
+    uint64_t words[4];
+    oracle_philox4x64_10(ctr, key, words);
+    const double u = (double)(words[n % 4] >> 11) * (1.0 / 9007199254740992.0); /* 2^-53 */
+    const int64_t p = n % npairs;
+    const int64_t g = (n / (npairs * seqlen)) % phi_heads;
+    phi[n] = (float)((double)bound[g * npairs + p] * (2.0 * u - 1.0));
+  }
+}
+
 /* x - 2 pi k with k chosen so the result lies in [-pi, pi). */
 double oracle_wrap(double x) {
   const double two_pi = 2.0 * ORACLE_PI;

@@ -49,6 +49,18 @@ BACKWARD_MUTANTS = [
 ]
 
 
+# Mistakes in the on-the-fly step angles, caught by the generator pins.
+GENERATOR_MUTANTS = [
+    ("philox round dropped", "for (int r = 0; r < 10; ++r) {", "for (int r = 0; r < 9; ++r) {"),
+    ("philox halves swapped", "c[1] = lo1;\n    c[2] = n2;\n    c[3] = lo0;",
+     "c[1] = lo0;\n    c[2] = n2;\n    c[3] = lo1;"),
+    ("philox key not bumped", "k1 += w1;", "(void)w1;"),
+    ("counter per element", "const uint64_t ctr[4] = {(uint64_t)n / 4, step, 0, 0};",
+     "const uint64_t ctr[4] = {(uint64_t)n, step, 0, 0};"),
+    ("uniform on [0, f_b)", "(2.0 * u - 1.0)", "u"),
+]
+
+
 def _run_pins_against(old, new, name, tmp_path, pin_file):
     src = open(SRC).read()
     assert src.count(old) >= 1, f"mutation site for {name!r} not found"
@@ -75,3 +87,8 @@ def test_pins_fail_on_planted_mistake(name, old, new, tmp_path):
 @pytest.mark.parametrize("name,old,new", BACKWARD_MUTANTS, ids=[m[0] for m in BACKWARD_MUTANTS])
 def test_backward_pins_fail_on_planted_mistake(name, old, new, tmp_path):
     _run_pins_against(old, new, name, tmp_path, "test_oracle_backward.py")
+
+
+@pytest.mark.parametrize("name,old,new", GENERATOR_MUTANTS, ids=[m[0] for m in GENERATOR_MUTANTS])
+def test_generator_pins_fail_on_planted_mistake(name, old, new, tmp_path):
+    _run_pins_against(old, new, name, tmp_path, "test_oracle_generators.py")
