@@ -168,8 +168,8 @@ def philox4x64_10(counter, key) -> np.ndarray:
 def random_phi(batch: int, phi_heads: int, seqlen: int, npairs: int, seed: int, step: int,
                bound) -> np.ndarray:
     """Random step angles [B, Hphi, L, P] (fp32) of the method paper's random
-    variant: uniform on (-bound[g, p], bound[g, p]), one Philox word per
-    element (see arp_oracle.h for the counter layout)."""
+    variant: uniform on (-bound[g, p], bound[g, p]), 32 Philox bits per element,
+    one block per two positions of four pairs (arp_oracle.c gives the layout)."""
     bound = np.ascontiguousarray(bound, dtype=np.float32)
     assert bound.shape == (phi_heads, npairs)
     out = np.empty((batch, phi_heads, seqlen, npairs), dtype=np.float32)

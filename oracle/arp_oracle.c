@@ -142,23 +142,33 @@ void oracle_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t
 
 /* The random variant's step angles ("Why Do Accumulated Transformations
  * Extrapolate?", App. D "Model variants": independent per position and pair,
- * uniform on (-f_b, f_b), redrawn every forward pass).  Element
- * n = ((b * phi_heads + g) * seqlen + t) * npairs + p takes word n mod 4 of
- * the Philox block at counter (n / 4, step, 0, 0) under key (seed, 0); its top
- * 53 bits give u in [0, 1), and phi = bound[g][p] * (2u - 1), formed in fp64
- * and rounded once to fp32.  step numbers the draws (one per forward pass). */
+ * uniform on (-f_b, f_b), redrawn every forward pass).  One Philox block
+ * serves two consecutive positions (t even and odd) of four consecutive pairs:
+ * the block for (b, g, t, p) sits at counter (c, step, 0, 0), key (seed, 0),
+ * with c = ((b * phi_heads + g) * ceil(seqlen / 2) + t / 2) * (npairs / 4) +
+ * p / 4; word p mod 4 holds the pair, its low 32 bits for even t and high 32
+ * bits for odd t.  Those 32 bits w give u = w * 2^-32 in [0, 1), and
+ * phi = bound[g][p] * (2u - 1), formed in fp64 (exactly, but for the final
+ * product) and rounded once to fp32.  step numbers the draws (one per
+ * forward pass).  npairs must be a multiple of 4. */
 void oracle_random_phi(int64_t batch, int64_t phi_heads, int64_t seqlen, int64_t npairs,
                        uint64_t seed, uint64_t step, const float* bound, float* phi) {
   const uint64_t key[2] = {seed, 0};
-  const int64_t n_all = batch * phi_heads * seqlen * npairs;
-  for (int64_t n = 0; n < n_all; ++n) {
-    const uint64_t ctr[4] = {(uint64_t)n / 4, step, 0, 0};
-    uint64_t words[4];
-    oracle_philox4x64_10(ctr, key, words);
-    const double u = (double)(words[n % 4] >> 11) * (1.0 / 9007199254740992.0); /* 2^-53 */
-    const int64_t p = n % npairs;
-    const int64_t g = (n / (npairs * seqlen)) % phi_heads;
-    phi[n] = (float)((double)bound[g * npairs + p] * (2.0 * u - 1.0));
+  const int64_t half_len = (seqlen + 1) / 2, groups = npairs / 4;
+  for (int64_t s = 0; s < batch * phi_heads; ++s) {
+    const int64_t g = s % phi_heads;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      for (int64_t p = 0; p < npairs; ++p) {
+        const uint64_t c = (uint64_t)((s * half_len + t / 2) * groups + p / 4);
+        const uint64_t ctr[4] = {c, step, 0, 0};
+        uint64_t words[4];
+        oracle_philox4x64_10(ctr, key, words);
+        const uint64_t w = words[p % 4];
+        const uint32_t bits = (t % 2 == 0) ? (uint32_t)w : (uint32_t)(w >> 32);
+        const double u = (double)bits * (1.0 / 4294967296.0); /* 2^-32 */
+        phi[(s * seqlen + t) * npairs + p] = (float)((double)bound[g * npairs + p] * (2.0 * u - 1.0));
+      }
+    }
   }
 }
 

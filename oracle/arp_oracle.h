@@ -60,10 +60,11 @@ void oracle_angle_scan(const float* phi, int64_t nseg, int64_t seqlen, int64_t n
 /* Philox4x64-10 block for counter ctr and key (Salmon et al., SC 2011). */
 void oracle_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]);
 
-/* Random step angles phi [batch, phi_heads, seqlen, npairs] (fp32): element n
- * (flat index) is bound[g][p] * (2u - 1), u = (word n%4 of the Philox block at
- * counter (n/4, step, 0, 0), key (seed, 0)) >> 11, times 2^-53.  bound is
- * [phi_heads, npairs] fp32. */
+/* Random step angles phi [batch, phi_heads, seqlen, npairs] (fp32), uniform
+ * on (-bound[g][p], bound[g][p]); bound is [phi_heads, npairs] fp32 and npairs
+ * a multiple of 4.  One Philox block (key (seed, 0), counter (c, step, 0, 0))
+ * covers positions 2m, 2m+1 of pairs 4j..4j+3 of one (b, g); the arp_oracle.c
+ * definition gives c and which 32 bits each element takes. */
 void oracle_random_phi(int64_t batch, int64_t phi_heads, int64_t seqlen, int64_t npairs,
                        uint64_t seed, uint64_t step, const float* bound, float* phi);
 

@@ -3,10 +3,11 @@
 * Philox4x64-10 against numpy's Philox bit generator, an independent
   implementation of the same published generator (numpy advances its 256-bit
   counter by one before each block), across keys, counters and carries.
-* The random variant's angles: element n takes word n mod 4 of the block at
-  counter (n / 4, step, 0, 0) -- checked with numpy's generator as the source
-  of the words -- and the draws are uniform on (-f_b, f_b): bounds, first two
-  moments, no correlation between neighbours or between steps, zero bound.
+* The random variant's angles: the counter layout (a block per two positions
+  of four pairs, 32 bits per element) checked with numpy's generator as the
+  source of the words, and the draws are uniform on (-f_b, f_b): bounds,
+  first two moments, no correlation between neighbours or between steps, zero
+  bound.
 * The token-table and constant sources against explicit loops.
 """
 import numpy as np
@@ -35,17 +36,19 @@ def test_philox_matches_numpy(counter, key):
     assert np.array_equal(got, _numpy_block(counter, key))
 
 
-def test_random_phi_layout_matches_numpy_words():
-    B, G, L, P = 2, 3, 5, 8
+@pytest.mark.parametrize("L", [5, 6])
+def test_random_phi_layout_matches_numpy_words(L):
+    B, G, P = 2, 3, 8
     seed, step = 0xC0FFEE, 11
     bound = np.abs(np.random.default_rng(0).standard_normal((G, P))).astype(np.float32) + 0.1
     got = oracle.random_phi(B, G, L, P, seed, step, bound)
     want = np.empty_like(got)
-    for n in range(B * G * L * P):
-        w = _numpy_block((step << 64) | (n // 4), (seed, 0))[n % 4]
-        u = float(int(w) >> 11) * 2.0 ** -53
-        b, g, t, p = np.unravel_index(n, (B, G, L, P))
-        want[b, g, t, p] = np.float32(float(bound[g, p]) * (2.0 * u - 1.0))
+    half = (L + 1) // 2
+    for b, g, t, p in np.ndindex(B, G, L, P):
+        c = ((b * G + g) * half + t // 2) * (P // 4) + p // 4
+        w = int(_numpy_block((step << 64) | c, (seed, 0))[p % 4])
+        bits = (w & 0xFFFFFFFF) if t % 2 == 0 else (w >> 32)
+        want[b, g, t, p] = np.float32(float(bound[g, p]) * (2.0 * bits * 2.0 ** -32 - 1.0))
     assert np.array_equal(got, want)
 
 

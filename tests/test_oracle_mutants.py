@@ -55,8 +55,10 @@ GENERATOR_MUTANTS = [
     ("philox halves swapped", "c[1] = lo1;\n    c[2] = n2;\n    c[3] = lo0;",
      "c[1] = lo0;\n    c[2] = n2;\n    c[3] = lo1;"),
     ("philox key not bumped", "k1 += w1;", "(void)w1;"),
-    ("counter per element", "const uint64_t ctr[4] = {(uint64_t)n / 4, step, 0, 0};",
-     "const uint64_t ctr[4] = {(uint64_t)n, step, 0, 0};"),
+    ("counter per pair", "const uint64_t ctr[4] = {c, step, 0, 0};",
+     "const uint64_t ctr[4] = {c + (uint64_t)(p % 4), step, 0, 0};"),
+    ("halves of a word swapped", "(t % 2 == 0) ? (uint32_t)w : (uint32_t)(w >> 32)",
+     "(t % 2 == 1) ? (uint32_t)w : (uint32_t)(w >> 32)"),
     ("uniform on [0, f_b)", "(2.0 * u - 1.0)", "u"),
 ]
 
