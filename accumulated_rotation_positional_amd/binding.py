@@ -38,7 +38,8 @@ EXPORTS = ("arp_abi_version", "arp_status_string", "arp_check", "arp_scan_state_
            "arp_angle_scan", "arp_rotate_qkv", "arp_attn_rotated", "arp_attn_fwd",
            "arp_forward", "arp_rotate", "arp_forward_train", "arp_backward_workspace_bytes",
            "arp_backward", "arp_decode_workspace_bytes", "arp_decode_prefill", "arp_decode_step",
-           "arp_forward_ex")
+           "arp_forward_ex", "arp_angle_scan_random", "arp_angle_scan_tokens",
+           "arp_angle_scan_const", "arp_random_phi")
 
 
 class ArpError(RuntimeError):
@@ -67,6 +68,7 @@ def lib() -> ctypes.CDLL:
                                    "`python -c 'import __graft_entry__ as g; g.build()'`")
             L = ctypes.CDLL(LIB_PATH)
             P, S, D = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Desc)
+            U64 = ctypes.c_uint64
             sig = {
                 "arp_abi_version": ([], ctypes.c_int),
                 "arp_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -86,6 +88,10 @@ def lib() -> ctypes.CDLL:
                 "arp_decode_prefill": ([D, ctypes.c_int32] + [P] * 7 + [P], ctypes.c_int),
                 "arp_decode_step": ([D, ctypes.c_int32] + [P] * 11 + [S, P], ctypes.c_int),
                 "arp_forward_ex": ([D] + [P] * 10 + [S, P, S, P], ctypes.c_int),
+                "arp_angle_scan_random": ([D, U64, U64, P, P, P, S, P], ctypes.c_int),
+                "arp_angle_scan_tokens": ([D, P, P, ctypes.c_int64, P, P, S, P], ctypes.c_int),
+                "arp_angle_scan_const": ([D, P, P, P, S, P], ctypes.c_int),
+                "arp_random_phi": ([D, U64, U64, P, P, P], ctypes.c_int),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -193,6 +199,68 @@ def angle_scan(phi: torch.Tensor, desc: Desc, theta: torch.Tensor | None = None,
     _check("arp_angle_scan", lib().arp_angle_scan(ctypes.byref(desc), _ptr(phi), _ptr(theta),
                                                   _ptr(state), state.numel(), _stream(phi.device)))
     return theta
+
+
+def _phi_shape(desc: Desc):
+    hphi = 1 if desc.flags & PHI_SHARED_HEADS else desc.heads
+    return (desc.batch, hphi, desc.seqlen, desc.head_dim // 2)
+
+
+def angle_scan_random(desc: Desc, seed: int, step: int, bound: torch.Tensor,
+                      theta: torch.Tensor | None = None,
+                      state: torch.Tensor | None = None) -> torch.Tensor:
+    """Accumulated angles of the random variant, drawn inside the scan; bound is
+    float32 [angle heads, d/2] on the device."""
+    _require_gpu(bound, theta, state)
+    dev = bound.device
+    theta = torch.empty(_phi_shape(desc), dtype=torch.float32, device=dev) if theta is None else theta
+    state = scan_state(desc, dev) if state is None else state
+    _check("arp_angle_scan_random",
+           lib().arp_angle_scan_random(ctypes.byref(desc), seed, step, _ptr(bound), _ptr(theta),
+                                       _ptr(state), state.numel(), _stream(dev)))
+    return theta
+
+
+def angle_scan_tokens(desc: Desc, tokens: torch.Tensor, table: torch.Tensor,
+                      theta: torch.Tensor | None = None,
+                      state: torch.Tensor | None = None) -> torch.Tensor:
+    """Accumulated angles of a per-token angle table; tokens int32 [B, L], table
+    float32 [vocab, angle heads, d/2], both on the device."""
+    _require_gpu(tokens, table, theta, state)
+    if tokens.dtype != torch.int32:
+        raise TypeError("tokens must be int32")
+    dev = table.device
+    theta = torch.empty(_phi_shape(desc), dtype=torch.float32, device=dev) if theta is None else theta
+    state = scan_state(desc, dev) if state is None else state
+    _check("arp_angle_scan_tokens",
+           lib().arp_angle_scan_tokens(ctypes.byref(desc), _ptr(tokens), _ptr(table),
+                                       table.shape[0], _ptr(theta), _ptr(state), state.numel(),
+                                       _stream(dev)))
+    return theta
+
+
+def angle_scan_const(desc: Desc, freq: torch.Tensor, theta: torch.Tensor | None = None,
+                     state: torch.Tensor | None = None) -> torch.Tensor:
+    """Accumulated angles of constant per-pair steps; freq float32 [angle heads, d/2]."""
+    _require_gpu(freq, theta, state)
+    dev = freq.device
+    theta = torch.empty(_phi_shape(desc), dtype=torch.float32, device=dev) if theta is None else theta
+    state = scan_state(desc, dev) if state is None else state
+    _check("arp_angle_scan_const",
+           lib().arp_angle_scan_const(ctypes.byref(desc), _ptr(freq), _ptr(theta), _ptr(state),
+                                      state.numel(), _stream(dev)))
+    return theta
+
+
+def random_phi(desc: Desc, seed: int, step: int, bound: torch.Tensor,
+               phi: torch.Tensor | None = None) -> torch.Tensor:
+    """The random variant's step angles written out (float32 [B, angle heads, L, d/2])."""
+    _require_gpu(bound, phi)
+    dev = bound.device
+    phi = torch.empty(_phi_shape(desc), dtype=torch.float32, device=dev) if phi is None else phi
+    _check("arp_random_phi", lib().arp_random_phi(ctypes.byref(desc), seed, step, _ptr(bound),
+                                                  _ptr(phi), _stream(dev)))
+    return phi
 
 
 def rotate_qkv(q, k, v, theta, desc: Desc, ws: torch.Tensor | None = None) -> torch.Tensor:

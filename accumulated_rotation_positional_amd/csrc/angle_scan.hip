@@ -97,13 +97,142 @@ __device__ __forceinline__ void publish(uint64_t* p, uint64_t value, uint64_t st
   __hip_atomic_store(p, (value << 16) | status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- where the step angles come from --------------------------------------
+// A source gives the angle of (segment s = b * Hphi + g, token, pair) one at a
+// time (at), or T consecutive tokens x 4 pairs at once (rows; tbase is even,
+// tokens past L may hold anything, the kernel zeroes them).
+
+// phi [B * Hphi, L, P] in memory.
+template <int P>
+struct PhiTensor {
+  const float* __restrict__ phi;
+  int L;
+  __device__ float at(int s, int tok, int p) const { return phi[((size_t)s * L + tok) * P + p]; }
+  template <int T>
+  __device__ void rows(int s, int tbase, int cq, float4 (&x)[T]) const {
+    const float* sp = phi + (size_t)s * L * P;
+    // Loads are unconditional (rows clamped into the segment) so that all T
+    // of them are in flight at once.
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int tok = min(tbase + t, L - 1);
+      x[t] = *reinterpret_cast<const float4*>(sp + (size_t)tok * P + cq * 4);
+    }
+  }
+};
+
+// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): the block of four 64-bit words for counter c and
+// key (k0, k1), in place.
+__device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
+    const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+}
+
+// The random variant's steps ("Why Do Accumulated Transformations
+// Extrapolate?", App. D "Model variants": independent per position and pair,
+// uniform on (-f_b, f_b), redrawn every forward pass), generated where they
+// are used.  One Philox block (key (seed, 0), counter (c, step, 0, 0)) covers
+// tokens 2m, 2m+1 of pairs 4j..4j+3 of segment s, c = (s * ceil(L/2) + m) *
+// P/4 + j; word p%4 serves pair p, its low 32 bits the even token and its high
+// 32 bits the odd one; 32 bits w give phi = bound[g][p] * (2 w 2^-32 - 1),
+// formed in fp64 and rounded once to fp32.
+template <int P>
+struct RandomAngles {
+  const float* __restrict__ bound;  // [Hphi, P]
+  uint64_t seed, step;
+  int L, Hphi;
+  __device__ void block(int s, int m, int j, uint64_t (&w)[4]) const {
+    w[0] = ((uint64_t)s * (uint64_t)((L + 1) >> 1) + (uint64_t)m) * (uint64_t)(P / 4) + (uint64_t)j;
+    w[1] = step;
+    w[2] = 0;
+    w[3] = 0;
+    philox4x64_10(w, seed, 0);
+  }
+  __device__ static float draw(float b, uint32_t bits) {
+#pragma clang fp contract(off)
+    const double u = (double)bits * 0x1p-32;
+    return (float)((double)b * (2.0 * u - 1.0));
+  }
+  __device__ float at(int s, int tok, int p) const {
+    uint64_t w[4];
+    block(s, tok >> 1, p >> 2, w);
+    const uint64_t x = w[p & 3];
+    return draw(bound[(s % Hphi) * P + p], (tok & 1) ? (uint32_t)(x >> 32) : (uint32_t)x);
+  }
+  template <int T>
+  __device__ void rows(int s, int tbase, int cq, float4 (&x)[T]) const {
+    static_assert(T % 2 == 0, "token pairs");
+    const float4 b = *reinterpret_cast<const float4*>(bound + (s % Hphi) * P + cq * 4);
+#pragma unroll
+    for (int i = 0; i < T / 2; ++i) {
+      uint64_t w[4];
+      block(s, (tbase >> 1) + i, cq, w);
+      x[2 * i] = make_float4(draw(b.x, (uint32_t)w[0]), draw(b.y, (uint32_t)w[1]),
+                             draw(b.z, (uint32_t)w[2]), draw(b.w, (uint32_t)w[3]));
+      x[2 * i + 1] = make_float4(draw(b.x, (uint32_t)(w[0] >> 32)), draw(b.y, (uint32_t)(w[1] >> 32)),
+                                 draw(b.z, (uint32_t)(w[2] >> 32)), draw(b.w, (uint32_t)(w[3] >> 32)));
+    }
+  }
+};
+
+// The learned token-rotation variant's steps (same section: one angle vector
+// per token identity): phi[b, g, t, p] = table[tokens[b, t], g, p], ids
+// clamped into [0, V).
+template <int P>
+struct TokenTable {
+  const int32_t* __restrict__ tokens;  // [B, L]
+  const float* __restrict__ table;     // [V, Hphi, P]
+  int L, Hphi, V;
+  __device__ const float* entry(int s, int tok) const {
+    const int v = tokens[(size_t)(s / Hphi) * L + tok];
+    return table + ((size_t)min(max(v, 0), V - 1) * Hphi + (s % Hphi)) * P;
+  }
+  __device__ float at(int s, int tok, int p) const { return entry(s, tok)[p]; }
+  template <int T>
+  __device__ void rows(int s, int tbase, int cq, float4 (&x)[T]) const {
+    const float* e[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) e[t] = entry(s, min(tbase + t, L - 1));
+#pragma unroll
+    for (int t = 0; t < T; ++t) x[t] = *reinterpret_cast<const float4*>(e[t] + cq * 4);
+  }
+};
+
+// Position-independent steps (RoPE's frequencies, or per-head learned ones):
+// phi[b, g, t, p] = freq[g, p].
+template <int P>
+struct ConstAngles {
+  const float* __restrict__ freq;  // [Hphi, P]
+  int Hphi;
+  __device__ float at(int s, int, int p) const { return freq[(s % Hphi) * P + p]; }
+  template <int T>
+  __device__ void rows(int s, int, int cq, float4 (&x)[T]) const {
+    const float4 f = *reinterpret_cast<const float4*>(freq + (s % Hphi) * P + cq * 4);
+#pragma unroll
+    for (int t = 0; t < T; ++t) x[t] = f;
+  }
+};
+
 // Sum of the converted angles of pair p over tokens t0, t0 + step, ... < t1,
-// read directly from phi (the fallback when a predecessor's aggregate is not
+// taken from the source (the fallback when a predecessor's aggregate is not
 // yet published).
-__device__ uint64_t reduce_pair(const float* __restrict__ seg_phi, int P, int p, int t0, int t1,
-                                int step) {
+template <class Src>
+__device__ uint64_t reduce_pair(const Src& src, int s, int p, int t0, int t1, int step) {
   uint64_t acc = 0;
-  for (int t = t0; t < t1; t += step) acc += to_fixed(seg_phi[(size_t)t * P + p]);
+  for (int t = t0; t < t1; t += step) acc += to_fixed(src.at(s, t, p));
   return acc;
 }
 
@@ -112,10 +241,9 @@ __device__ uint64_t reduce_pair(const float* __restrict__ seg_phi, int P, int p,
 // pass, so a pass reads K * W predecessors of every pair at once.  Returns
 // the sum of the aggregates of chunks 0 .. chunk-1 of the segment for pair p
 // (the same value on the K lanes of a pair).
-template <int P>
+template <int P, class Src>
 __device__ uint64_t look_back(const uint64_t* __restrict__ wh, size_t wbase, uint32_t half,
-                              int chunk, const float* __restrict__ seg_phi, int L, int CH,
-                              int lane) {
+                              int chunk, const Src& src, int seg, int L, int CH, int lane) {
   constexpr int K = 64 / P;
   constexpr int W = 8;
   constexpr int SPAN = K * W;  // predecessors per pass
@@ -168,7 +296,7 @@ __device__ uint64_t look_back(const uint64_t* __restrict__ wh, size_t wbase, uin
     if (stop > 0) polls = 0;
     if (++polls > FALLBACK_POLLS) {
       const int t0 = d * CH, t1 = min(t0 + CH, L);
-      uint64_t r = reduce_pair(seg_phi, P, p, t0 + k0, t1, K);
+      uint64_t r = reduce_pair(src, seg, p, t0 + k0, t1, K);
       if (K == 2) {
         const uint32_t lo = __shfl_xor((uint32_t)r, 32), hi = __shfl_xor((uint32_t)(r >> 32), 32);
         r += ((uint64_t)hi << 32) | lo;
@@ -184,9 +312,9 @@ __device__ uint64_t look_back(const uint64_t* __restrict__ wh, size_t wbase, uin
   return acc;
 }
 
-template <int P, int T, int MINB>
+template <int P, int T, int MINB, class Src>
 __global__ __launch_bounds__(SCAN_THREADS, MINB) void angle_scan_kernel(
-    const float* __restrict__ phi, float* __restrict__ theta, ScanHeader* __restrict__ hdr,
+    Src src, float* __restrict__ theta, ScanHeader* __restrict__ hdr,
     uint64_t* __restrict__ words, int L, int nchunks, int exclusive) {
   constexpr int CPT = P / 4;              // threads per token row (4 pairs each)
   constexpr int RG = SCAN_THREADS / CPT;  // row groups per chunk
@@ -213,16 +341,10 @@ __global__ __launch_bounds__(SCAN_THREADS, MINB) void angle_scan_kernel(
   const uint64_t stale = hdr->used[half ^ 1u];
   const int ngroups = (nblocks + GROUP - 1) / GROUP;
 
-  // ---- load T rows x 4 pairs; thread totals of the converted angles ----
-  const float* seg_phi = phi + (size_t)seg * L * P;
-  // Loads are unconditional (rows clamped into the segment) so that all T of
-  // them are in flight at once; rows past the end then count as zero.
+  // ---- T rows x 4 pairs of steps; thread totals of the converted angles ----
+  // Rows past the end of the segment count as zero.
   float4 x[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int tok = min(tbase + t, L - 1);
-    x[t] = *reinterpret_cast<const float4*>(seg_phi + (size_t)tok * P + cq * 4);
-  }
+  src.template rows<T>(seg, tbase, cq, x);
 #pragma unroll
   for (int t = 0; t < T; ++t)
     if (tbase + t >= L) x[t] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -267,7 +389,7 @@ __global__ __launch_bounds__(SCAN_THREADS, MINB) void angle_scan_kernel(
     if (lane < P) publish(my, agg, chunk == 0 ? ST_INC : ST_AGG);
     uint64_t acc = 0;
     if (chunk > 0) {
-      acc = look_back<P>(words, wbase, half, chunk, seg_phi, L, CH, lane);
+      acc = look_back<P>(words, wbase, half, chunk, src, seg, L, CH, lane);
       if (lane < P) publish(my, acc + agg, ST_INC);
     }
     if (lane < P) s_carry[p] = acc + FIXED_ZERO;  // turns [0,1) into [-1/2,1/2) below
@@ -385,8 +507,11 @@ size_t scan_state_bytes(const Geometry& g) {
   return (bytes + 255) & ~(size_t)255;
 }
 
-hipError_t launch_angle_scan(const Geometry& g, const float* phi, float* theta, void* scan_state,
-                             hipStream_t stream) {
+namespace {
+
+template <int P, class Src>
+hipError_t launch_scan(const Geometry& g, const Src& src, float* theta, void* scan_state,
+                       hipStream_t stream) {
   const ScanPlan sp = scan_plan(g);
   const long nblocks = (long)g.B * g.Hphi * sp.nchunks;
   auto* hdr = reinterpret_cast<ScanHeader*>(scan_state);
@@ -395,21 +520,86 @@ hipError_t launch_angle_scan(const Geometry& g, const float* phi, float* theta, 
   if (nblocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)nblocks);
   dim3 block(SCAN_THREADS);
-#define ARP_SCAN_LAUNCH(PP, TT, MB)                                                             \
-  hipLaunchKernelGGL((angle_scan_kernel<PP, TT, MB>), grid, block, 0, stream, phi, theta, hdr,    \
+#define ARP_SCAN_LAUNCH(TT, MB)                                                               \
+  hipLaunchKernelGGL((angle_scan_kernel<P, TT, MB, Src>), grid, block, 0, stream, src, theta, hdr, \
                      words, g.L, sp.nchunks, excl)
-  if (g.P == 32) {
-    if (sp.rows_per_thread == 16) {
-      if (sp.min_blocks == 4) ARP_SCAN_LAUNCH(32, 16, 4); else ARP_SCAN_LAUNCH(32, 16, 1);
-    } else if (sp.rows_per_thread == 8) ARP_SCAN_LAUNCH(32, 8, 1);
-    else ARP_SCAN_LAUNCH(32, 4, 1);
+  if (sp.rows_per_thread == 16) {
+    if (sp.min_blocks == 4) ARP_SCAN_LAUNCH(16, 4); else ARP_SCAN_LAUNCH(16, 1);
+  } else if (sp.rows_per_thread == 8) {
+    ARP_SCAN_LAUNCH(8, 1);
   } else {
-    if (sp.rows_per_thread == 16) {
-      if (sp.min_blocks == 4) ARP_SCAN_LAUNCH(64, 16, 4); else ARP_SCAN_LAUNCH(64, 16, 1);
-    } else if (sp.rows_per_thread == 8) ARP_SCAN_LAUNCH(64, 8, 1);
-    else ARP_SCAN_LAUNCH(64, 4, 1);
+    ARP_SCAN_LAUNCH(4, 1);
   }
 #undef ARP_SCAN_LAUNCH
+  return hipGetLastError();
+}
+
+// phi of the random variant written out: one thread per Philox block (two
+// tokens x four pairs; consecutive threads take consecutive pair groups).
+template <int P>
+__global__ __launch_bounds__(256) void random_phi_kernel(RandomAngles<P> src, float* __restrict__ phi,
+                                                         long nseg) {
+  constexpr int J = P / 4;
+  const long half = (src.L + 1) >> 1;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nseg * half * J) return;
+  const int j = (int)(i % J);
+  const long sm = i / J;
+  const int m = (int)(sm % half);
+  const int seg = (int)(sm / half);
+  float4 x[2];
+  src.template rows<2>(seg, 2 * m, j, x);
+  float* row = phi + ((size_t)seg * src.L + 2 * m) * P + 4 * j;
+  *reinterpret_cast<float4*>(row) = x[0];
+  if (2 * m + 1 < src.L) *reinterpret_cast<float4*>(row + P) = x[1];
+}
+
+}  // namespace
+
+hipError_t launch_angle_scan(const Geometry& g, const float* phi, float* theta, void* scan_state,
+                             hipStream_t stream) {
+  if (g.P == 32) return launch_scan<32>(g, PhiTensor<32>{phi, g.L}, theta, scan_state, stream);
+  return launch_scan<64>(g, PhiTensor<64>{phi, g.L}, theta, scan_state, stream);
+}
+
+hipError_t launch_angle_scan_random(const Geometry& g, uint64_t seed, uint64_t step,
+                                    const float* bound, float* theta, void* scan_state,
+                                    hipStream_t stream) {
+  if (g.P == 32)
+    return launch_scan<32>(g, RandomAngles<32>{bound, seed, step, g.L, g.Hphi}, theta, scan_state,
+                           stream);
+  return launch_scan<64>(g, RandomAngles<64>{bound, seed, step, g.L, g.Hphi}, theta, scan_state,
+                         stream);
+}
+
+hipError_t launch_angle_scan_tokens(const Geometry& g, const int32_t* tokens, const float* table,
+                                    int vocab, float* theta, void* scan_state, hipStream_t stream) {
+  if (g.P == 32)
+    return launch_scan<32>(g, TokenTable<32>{tokens, table, g.L, g.Hphi, vocab}, theta, scan_state,
+                           stream);
+  return launch_scan<64>(g, TokenTable<64>{tokens, table, g.L, g.Hphi, vocab}, theta, scan_state,
+                         stream);
+}
+
+hipError_t launch_angle_scan_const(const Geometry& g, const float* freq, float* theta,
+                                   void* scan_state, hipStream_t stream) {
+  if (g.P == 32) return launch_scan<32>(g, ConstAngles<32>{freq, g.Hphi}, theta, scan_state, stream);
+  return launch_scan<64>(g, ConstAngles<64>{freq, g.Hphi}, theta, scan_state, stream);
+}
+
+hipError_t launch_random_phi(const Geometry& g, uint64_t seed, uint64_t step, const float* bound,
+                             float* phi, hipStream_t stream) {
+  const long nseg = (long)g.B * g.Hphi;
+  const long n = nseg * ((g.L + 1) / 2) * (g.P / 4);
+  if (n == 0) return hipSuccess;
+  const long blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  if (g.P == 32)
+    hipLaunchKernelGGL(random_phi_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       RandomAngles<32>{bound, seed, step, g.L, g.Hphi}, phi, nseg);
+  else
+    hipLaunchKernelGGL(random_phi_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       RandomAngles<64>{bound, seed, step, g.L, g.Hphi}, phi, nseg);
   return hipGetLastError();
 }
 

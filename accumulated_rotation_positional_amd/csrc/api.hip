@@ -150,6 +150,55 @@ arp_status arp_angle_scan(const arp_desc* desc, const float* phi, float* theta, 
   return hip_status(launch_angle_scan(g, phi, theta, scan_state, (hipStream_t)stream));
 }
 
+arp_status arp_angle_scan_random(const arp_desc* desc, uint64_t seed, uint64_t step,
+                                 const float* bound, float* theta, void* scan_state,
+                                 size_t scan_state_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (bound == nullptr || theta == nullptr) return ARP_ERR_INVALID_ARG;
+  if (!aligned16(bound) || !aligned16(theta)) return ARP_ERR_ALIGNMENT;
+  if ((st = check_scan_state(g, scan_state, scan_state_bytes)) != ARP_OK) return st;
+  return hip_status(
+      launch_angle_scan_random(g, seed, step, bound, theta, scan_state, (hipStream_t)stream));
+}
+
+arp_status arp_angle_scan_tokens(const arp_desc* desc, const int32_t* tokens, const float* table,
+                                 int64_t vocab, float* theta, void* scan_state,
+                                 size_t scan_state_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (tokens == nullptr || table == nullptr || theta == nullptr || vocab < 1 || vocab > INT32_MAX)
+    return ARP_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(tokens) & 3) != 0 || !aligned16(table) || !aligned16(theta))
+    return ARP_ERR_ALIGNMENT;
+  if ((st = check_scan_state(g, scan_state, scan_state_bytes)) != ARP_OK) return st;
+  return hip_status(launch_angle_scan_tokens(g, tokens, table, (int)vocab, theta, scan_state,
+                                             (hipStream_t)stream));
+}
+
+arp_status arp_angle_scan_const(const arp_desc* desc, const float* freq, float* theta,
+                                void* scan_state, size_t scan_state_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (freq == nullptr || theta == nullptr) return ARP_ERR_INVALID_ARG;
+  if (!aligned16(freq) || !aligned16(theta)) return ARP_ERR_ALIGNMENT;
+  if ((st = check_scan_state(g, scan_state, scan_state_bytes)) != ARP_OK) return st;
+  return hip_status(launch_angle_scan_const(g, freq, theta, scan_state, (hipStream_t)stream));
+}
+
+arp_status arp_random_phi(const arp_desc* desc, uint64_t seed, uint64_t step, const float* bound,
+                          float* phi, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (bound == nullptr || phi == nullptr) return ARP_ERR_INVALID_ARG;
+  if (!aligned16(bound) || !aligned16(phi)) return ARP_ERR_ALIGNMENT;
+  return hip_status(launch_random_phi(g, seed, step, bound, phi, (hipStream_t)stream));
+}
+
 arp_status arp_rotate_qkv(const arp_desc* desc, const void* q, const void* k, const void* v,
                           const float* theta, void* workspace, size_t workspace_bytes,
                           void* stream) {

@@ -126,6 +126,47 @@ size_t arp_workspace_bytes(const arp_desc* desc);
 arp_status arp_angle_scan(const arp_desc* desc, const float* phi, float* theta, void* scan_state,
                           size_t scan_state_bytes, void* stream);
 
+/* a1 with the step angles generated inside the scan instead of read from a
+ * phi tensor (the theta it writes is bit-identical to arp_angle_scan's on the
+ * phi the generator defines; same scan state, flags and errors as
+ * arp_angle_scan).  Angle heads: 1 with ARP_PHI_SHARED_HEADS, else heads.
+ *
+ * arp_angle_scan_random: the method paper's random variant (App. D "Model
+ *   variants": steps independent per position and pair, uniform on
+ *   (-f_b, f_b), redrawn every forward pass, shared by the heads of a layer).
+ *   bound: float32 [angle heads, head_dim/2] device, the f_b (RoPE's
+ *   10000^(-2b/d) in the paper).  seed keys the draws, step numbers them (pass
+ *   a new step per forward pass).  Definition: one Philox4x64-10 block
+ *   (Salmon et al., SC 2011; key (seed, 0), counter (c, step, 0, 0)) per two
+ *   positions 2m, 2m+1 and four pairs 4j..4j+3 of one (b, g), with
+ *   c = ((b * angle_heads + g) * ceil(seqlen / 2) + m) * (head_dim / 8) + j;
+ *   word p % 4 serves pair p, its low 32 bits position 2m and its high 32 bits
+ *   position 2m+1; bits w give phi = bound[g][p] * (2 w 2^-32 - 1), in fp64,
+ *   rounded once to fp32.
+ * arp_angle_scan_tokens: the learned token-rotation variant (same section: an
+ *   angle vector per token identity), phi[b, g, t, p] = table[tokens[b, t], g, p].
+ *   tokens: int32 [batch, seqlen] device (4-byte aligned), ids outside
+ *   [0, vocab) are clamped into it; table: float32 [vocab, angle heads,
+ *   head_dim/2] device.
+ * arp_angle_scan_const: position-independent steps, phi[b, g, t, p] =
+ *   freq[g, p] (RoPE: 10000^(-2p/d); AdaRoPE's per-head learned frequencies,
+ *   AdaRoPE Sec. 3.3, AdaFreq): theta_t = (t + 1) freq, wrapped.  freq: float32
+ *   [angle heads, head_dim/2] device. */
+arp_status arp_angle_scan_random(const arp_desc* desc, uint64_t seed, uint64_t step,
+                                 const float* bound, float* theta, void* scan_state,
+                                 size_t scan_state_bytes, void* stream);
+arp_status arp_angle_scan_tokens(const arp_desc* desc, const int32_t* tokens, const float* table,
+                                 int64_t vocab, float* theta, void* scan_state,
+                                 size_t scan_state_bytes, void* stream);
+arp_status arp_angle_scan_const(const arp_desc* desc, const float* freq, float* theta,
+                                void* scan_state, size_t scan_state_bytes, void* stream);
+
+/* The random variant's steps written out: phi float32 [batch, angle heads,
+ * seqlen, head_dim/2] device, exactly the phi arp_angle_scan_random scans
+ * (same seed, step, bound).  For callers that need the draws themselves. */
+arp_status arp_random_phi(const arp_desc* desc, uint64_t seed, uint64_t step, const float* bound,
+                          float* phi, void* stream);
+
 /* a2. Pre-rotation pass (bf16): writes R(Theta_t) q_t (times scale*log2(e)),
  * R(Theta_t) k_t and R(Theta_t) v_t (or the unrotated tensors, per the flags)
  * as bf16 into the workspace, in the layout arp_attn_rotated reads.
