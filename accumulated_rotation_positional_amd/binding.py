@@ -90,7 +90,7 @@ def lib() -> ctypes.CDLL:
                 "arp_forward_ex": ([D] + [P] * 10 + [S, P, S, P], ctypes.c_int),
                 "arp_angle_scan_random": ([D, U64, U64, P, P, P, S, P], ctypes.c_int),
                 "arp_angle_scan_tokens": ([D, P, P, ctypes.c_int64, P, P, S, P], ctypes.c_int),
-                "arp_angle_scan_const": ([D, P, P, P, S, P], ctypes.c_int),
+                "arp_angle_scan_const": ([D, P, P, P], ctypes.c_int),
                 "arp_random_phi": ([D, U64, U64, P, P, P], ctypes.c_int),
             }
             for name, (args, res) in sig.items():
@@ -239,16 +239,14 @@ def angle_scan_tokens(desc: Desc, tokens: torch.Tensor, table: torch.Tensor,
     return theta
 
 
-def angle_scan_const(desc: Desc, freq: torch.Tensor, theta: torch.Tensor | None = None,
-                     state: torch.Tensor | None = None) -> torch.Tensor:
-    """Accumulated angles of constant per-pair steps; freq float32 [angle heads, d/2]."""
-    _require_gpu(freq, theta, state)
+def angle_scan_const(desc: Desc, freq: torch.Tensor, theta: torch.Tensor | None = None) -> torch.Tensor:
+    """Accumulated angles of constant per-pair steps (closed form); freq float32
+    [angle heads, d/2]."""
+    _require_gpu(freq, theta)
     dev = freq.device
     theta = torch.empty(_phi_shape(desc), dtype=torch.float32, device=dev) if theta is None else theta
-    state = scan_state(desc, dev) if state is None else state
     _check("arp_angle_scan_const",
-           lib().arp_angle_scan_const(ctypes.byref(desc), _ptr(freq), _ptr(theta), _ptr(state),
-                                      state.numel(), _stream(dev)))
+           lib().arp_angle_scan_const(ctypes.byref(desc), _ptr(freq), _ptr(theta), _stream(dev)))
     return theta
 
 

@@ -124,13 +124,28 @@ struct PhiTensor {
 // Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC 2011): the block of four 64-bit words for counter c and
 // key (k0, k1), in place.
+// The 128-bit product of a and b from four 32 x 32 + 64 multiply-adds
+// (v_mad_u64_u32), the partial products shared between the two halves:
+// a b = a1 b1 2^64 + (a1 b0 + a0 b1) 2^32 + a0 b0.  No sum overflows 64 bits:
+// (2^32 - 1)^2 + 2 (2^32 - 1) < 2^64.
+__device__ __forceinline__ void mulhilo64(uint64_t a, uint64_t b, uint64_t& lo, uint64_t& hi) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
+  const uint32_t b0 = (uint32_t)b, b1 = (uint32_t)(b >> 32);
+  const uint64_t p00 = (uint64_t)a0 * b0;
+  const uint64_t t = (uint64_t)a1 * b0 + (p00 >> 32);
+  const uint64_t u = (uint64_t)a0 * b1 + (uint32_t)t;
+  hi = (uint64_t)a1 * b1 + ((t >> 32) + (u >> 32));
+  lo = (u << 32) | (uint32_t)p00;
+}
+
 __device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
   constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
-    const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
+    uint64_t lo0, hi0, lo1, hi1;
+    mulhilo64(M0, c[0], lo0, hi0);
+    mulhilo64(M1, c[2], lo1, hi1);
     const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
     c[0] = n0;
     c[1] = lo1;
@@ -208,21 +223,6 @@ struct TokenTable {
     for (int t = 0; t < T; ++t) e[t] = entry(s, min(tbase + t, L - 1));
 #pragma unroll
     for (int t = 0; t < T; ++t) x[t] = *reinterpret_cast<const float4*>(e[t] + cq * 4);
-  }
-};
-
-// Position-independent steps (RoPE's frequencies, or per-head learned ones):
-// phi[b, g, t, p] = freq[g, p].
-template <int P>
-struct ConstAngles {
-  const float* __restrict__ freq;  // [Hphi, P]
-  int Hphi;
-  __device__ float at(int s, int, int p) const { return freq[(s % Hphi) * P + p]; }
-  template <int T>
-  __device__ void rows(int s, int, int cq, float4 (&x)[T]) const {
-    const float4 f = *reinterpret_cast<const float4*>(freq + (s % Hphi) * P + cq * 4);
-#pragma unroll
-    for (int t = 0; t < T; ++t) x[t] = f;
   }
 };
 
@@ -554,6 +554,31 @@ __global__ __launch_bounds__(256) void random_phi_kernel(RandomAngles<P> src, fl
   if (2 * m + 1 < src.L) *reinterpret_cast<float4*>(row + P) = x[1];
 }
 
+// Constant steps need no scan: the sum of n copies of one fixed-point step is
+// n times it, mod 2^48 -- the very integer the scan would reach, so the result
+// is bit-identical to scanning the broadcast steps.  One thread per token and
+// four pairs, consecutive threads along the row.
+template <int P>
+__global__ __launch_bounds__(256) void const_angles_kernel(const float* __restrict__ freq,
+                                                           float* __restrict__ theta, long n, int L,
+                                                           int Hphi, int exclusive) {
+  constexpr int J = P / 4;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int j = (int)(i % J);
+  const long st = i / J;  // segment * L + token
+  const int t = (int)(st % L);
+  const int g = (int)((st / L) % Hphi);
+  const float4 f = *reinterpret_cast<const float4*>(freq + g * P + 4 * j);
+  const uint64_t count = (uint64_t)(exclusive ? t : t + 1);
+  const float fx[4] = {f.x, f.y, f.z, f.w};
+  float out[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) out[c] = to_radians_offset(FIXED_ZERO + count * to_fixed(fx[c]));
+  __builtin_nontemporal_store(f32x4{out[0], out[1], out[2], out[3]},
+                              reinterpret_cast<f32x4*>(theta + st * P + 4 * j));
+}
+
 }  // namespace
 
 hipError_t launch_angle_scan(const Geometry& g, const float* phi, float* theta, void* scan_state,
@@ -582,9 +607,19 @@ hipError_t launch_angle_scan_tokens(const Geometry& g, const int32_t* tokens, co
 }
 
 hipError_t launch_angle_scan_const(const Geometry& g, const float* freq, float* theta,
-                                   void* scan_state, hipStream_t stream) {
-  if (g.P == 32) return launch_scan<32>(g, ConstAngles<32>{freq, g.Hphi}, theta, scan_state, stream);
-  return launch_scan<64>(g, ConstAngles<64>{freq, g.Hphi}, theta, scan_state, stream);
+                                   hipStream_t stream) {
+  const long n = (long)g.B * g.Hphi * g.L * (g.P / 4);
+  if (n == 0) return hipSuccess;
+  const long blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const int excl = (g.flags & ARP_SCAN_EXCLUSIVE) ? 1 : 0;
+  if (g.P == 32)
+    hipLaunchKernelGGL(const_angles_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, freq,
+                       theta, n, g.L, g.Hphi, excl);
+  else
+    hipLaunchKernelGGL(const_angles_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, freq,
+                       theta, n, g.L, g.Hphi, excl);
+  return hipGetLastError();
 }
 
 hipError_t launch_random_phi(const Geometry& g, uint64_t seed, uint64_t step, const float* bound,

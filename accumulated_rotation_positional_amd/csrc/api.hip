@@ -179,14 +179,13 @@ arp_status arp_angle_scan_tokens(const arp_desc* desc, const int32_t* tokens, co
 }
 
 arp_status arp_angle_scan_const(const arp_desc* desc, const float* freq, float* theta,
-                                void* scan_state, size_t scan_state_bytes, void* stream) {
+                                void* stream) {
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
   if (freq == nullptr || theta == nullptr) return ARP_ERR_INVALID_ARG;
   if (!aligned16(freq) || !aligned16(theta)) return ARP_ERR_ALIGNMENT;
-  if ((st = check_scan_state(g, scan_state, scan_state_bytes)) != ARP_OK) return st;
-  return hip_status(launch_angle_scan_const(g, freq, theta, scan_state, (hipStream_t)stream));
+  return hip_status(launch_angle_scan_const(g, freq, theta, (hipStream_t)stream));
 }
 
 arp_status arp_random_phi(const arp_desc* desc, uint64_t seed, uint64_t step, const float* bound,

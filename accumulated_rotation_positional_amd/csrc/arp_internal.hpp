@@ -49,15 +49,16 @@ hipError_t launch_angle_scan(const Geometry& g, const float* phi, float* theta, 
                              hipStream_t stream);
 // The scan with its step angles generated in the kernel: the random
 // variant's uniform draws (Philox4x64-10 keyed by seed, draw number step;
-// bound [Hphi, P]), a learned per-token table (tokens [B, L], table
-// [vocab, Hphi, P]), or constant per-pair frequencies (freq [Hphi, P]).
+// bound [Hphi, P]) or a learned per-token table (tokens [B, L], table
+// [vocab, Hphi, P]); constant per-pair frequencies (freq [Hphi, P]) in
+// closed form, without a scan.
 hipError_t launch_angle_scan_random(const Geometry& g, uint64_t seed, uint64_t step,
                                     const float* bound, float* theta, void* scan_state,
                                     hipStream_t stream);
 hipError_t launch_angle_scan_tokens(const Geometry& g, const int32_t* tokens, const float* table,
                                     int vocab, float* theta, void* scan_state, hipStream_t stream);
 hipError_t launch_angle_scan_const(const Geometry& g, const float* freq, float* theta,
-                                   void* scan_state, hipStream_t stream);
+                                   hipStream_t stream);
 // The random draws written out as phi [B, Hphi, L, P].
 hipError_t launch_random_phi(const Geometry& g, uint64_t seed, uint64_t step, const float* bound,
                              float* phi, hipStream_t stream);

@@ -237,6 +237,54 @@ def forget_leg(binding, torch, dev, w, q, k, v, phi, steps: int = 20) -> dict:
             "speedup_vs_ungated": round(without / with_g, 3)}
 
 
+def generator_leg(binding, torch, dev, steps: int = 30) -> dict:
+    """The scans that generate their step angles in the kernel, on the largest
+    workload's angle shape (B=4, 32 angle heads, L=8192, 64 pairs; theta is
+    268 MB): the random variant's draws (Philox), a per-token table (vocab
+    256), constant frequencies.  Each writes theta only (plus 32 KB of token
+    ids and the table), so the HBM roofline is on 4 bytes per element.  The
+    Infinity Cache is evicted by a 512 MB read before each timed launch, as in
+    the scan gate; median of the launches, each bracketed by its own events."""
+    from accumulated_rotation_positional_amd import workloads as wl
+    B, H, L, P = 4, 32, 8192, 64
+    desc = binding.make_desc(B, H, L, 2 * P, "bf16", binding.flags_for())
+    g = torch.Generator(device=dev)
+    g.manual_seed(6)
+    bound = torch.from_numpy(np.broadcast_to(wl.rope_frequencies(2 * P), (H, P)).copy()).to(dev)
+    tokens = torch.randint(0, 256, (B, L), device=dev, generator=g, dtype=torch.int32)
+    table = torch.rand(256, H, P, device=dev, generator=g) * 6.0 - 3.0
+    theta = torch.empty(B, H, L, P, device=dev)
+    state = binding.scan_state(desc, dev)
+    calls = {
+        "random": lambda i: binding.angle_scan_random(desc, 1234, i, bound, theta=theta, state=state),
+        "token_table": lambda i: binding.angle_scan_tokens(desc, tokens, table, theta=theta, state=state),
+        "constant": lambda i: binding.angle_scan_const(desc, bound, theta=theta),
+    }
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    nbytes = 4.0 * theta.numel()
+    out = {"workload": "rope_8k_d128 angles", "bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "bytes_per_launch": nbytes}
+    for name, f in calls.items():
+        for i in range(5):
+            f(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i, (e0, e1) in enumerate(evs):
+            flush.sum()
+            e0.record(stream)
+            f(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"us_per_launch": round(ms * 1e3, 2), "achieved": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del flush
+    return out
+
+
 def decode_leg(binding, torch, dev, steps: int = 50) -> dict:
     """Decode steps at a full context: the token at the last position attends
     to every cached row.  Two cache shapes: extrap_16k's (B=2, H=8, 16384
@@ -404,6 +452,7 @@ def main():
                           "traffic": scan_traffic},
     }
     result["scan_hbm_gate"] = scan_gate(binding, torch, dev)
+    result["angle_generators"] = generator_leg(binding, torch, dev)
     if not args.fused:
         result["backward"] = backward_leg(binding, torch, dev, w, q, k, v, phi, alibi)
         result["decode"] = decode_leg(binding, torch, dev)

@@ -126,10 +126,11 @@ size_t arp_workspace_bytes(const arp_desc* desc);
 arp_status arp_angle_scan(const arp_desc* desc, const float* phi, float* theta, void* scan_state,
                           size_t scan_state_bytes, void* stream);
 
-/* a1 with the step angles generated inside the scan instead of read from a
- * phi tensor (the theta it writes is bit-identical to arp_angle_scan's on the
- * phi the generator defines; same scan state, flags and errors as
- * arp_angle_scan).  Angle heads: 1 with ARP_PHI_SHARED_HEADS, else heads.
+/* a1 with the step angles generated inside the kernel instead of read from a
+ * phi tensor (the theta written is bit-identical to arp_angle_scan's on the
+ * phi the generator defines; same flags and errors as arp_angle_scan, and the
+ * same scan state where one is taken).  Angle heads: 1 with
+ * ARP_PHI_SHARED_HEADS, else heads.
  *
  * arp_angle_scan_random: the method paper's random variant (App. D "Model
  *   variants": steps independent per position and pair, uniform on
@@ -150,7 +151,9 @@ arp_status arp_angle_scan(const arp_desc* desc, const float* phi, float* theta, 
  *   head_dim/2] device.
  * arp_angle_scan_const: position-independent steps, phi[b, g, t, p] =
  *   freq[g, p] (RoPE: 10000^(-2p/d); AdaRoPE's per-head learned frequencies,
- *   AdaRoPE Sec. 3.3, AdaFreq): theta_t = (t + 1) freq, wrapped.  freq: float32
+ *   AdaRoPE Sec. 3.3, AdaFreq): theta_t = (t + 1) freq, wrapped (t freq with
+ *   ARP_SCAN_EXCLUSIVE), formed directly as an integer multiple of the
+ *   fixed-point step, without a scan or its state.  freq: float32
  *   [angle heads, head_dim/2] device. */
 arp_status arp_angle_scan_random(const arp_desc* desc, uint64_t seed, uint64_t step,
                                  const float* bound, float* theta, void* scan_state,
@@ -159,7 +162,7 @@ arp_status arp_angle_scan_tokens(const arp_desc* desc, const int32_t* tokens, co
                                  int64_t vocab, float* theta, void* scan_state,
                                  size_t scan_state_bytes, void* stream);
 arp_status arp_angle_scan_const(const arp_desc* desc, const float* freq, float* theta,
-                                void* scan_state, size_t scan_state_bytes, void* stream);
+                                void* stream);
 
 /* The random variant's steps written out: phi float32 [batch, angle heads,
  * seqlen, head_dim/2] device, exactly the phi arp_angle_scan_random scans

@@ -103,21 +103,23 @@ def test_token_table_scan(L, P, shared):
     assert circular_err(got, oracle.angle_scan(phi)) <= F32_TOL
 
 
-@pytest.mark.parametrize("L,P,shared", [(1, 64, False), (1500, 32, False), (9000, 64, True)])
-def test_constant_scan(L, P, shared):
+@pytest.mark.parametrize("L,P,shared,excl", [(1, 64, False, False), (1500, 32, False, False),
+                                              (9000, 64, True, False), (777, 32, False, True)])
+def test_constant_steps_closed_form(L, P, shared, excl):
     B, H = 2, 4
     G = 1 if shared else H
     rng = np.random.default_rng(L)
     freq = (wl.rope_frequencies(2 * P)[None, :] * rng.uniform(0.5, 3.0, size=(G, P))).astype(np.float32)
-    desc = _desc(B, H, L, P, shared)
-    say(f"[gpu] constant angles L={L} P={P} shared={shared}")
+    freq[0, :3] = (5.5, -2.0, 0.0)  # a step above pi, a negative one, none
+    desc = _desc(B, H, L, P, shared, exclusive=excl)
+    say(f"[gpu] constant angles L={L} P={P} shared={shared} excl={excl}")
     theta = binding.angle_scan_const(desc, to_dev(freq))
     phi = oracle.constant_phi(B, L, freq)
     ref = binding.angle_scan(to_dev(phi), desc)
     torch.cuda.synchronize()
     got = theta.cpu().numpy()
     assert np.array_equal(got, ref.cpu().numpy())
-    t = np.arange(1, L + 1, dtype=np.float64)[None, None, :, None]
+    t = np.arange(0 if excl else 1, L + (0 if excl else 1), dtype=np.float64)[None, None, :, None]
     closed = np.broadcast_to(t * freq.astype(np.float64)[None, :, None, :], got.shape)
     assert circular_err(got, closed) <= F32_TOL
 
