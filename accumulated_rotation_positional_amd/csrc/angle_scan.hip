@@ -472,18 +472,22 @@ constexpr int rows_per_group(int P) { return SCAN_THREADS / (P / 4); }
 }  // namespace
 
 ScanPlan scan_plan(const Geometry& g) {
-  // Rows per thread: 16 (64 KB of phi per workgroup) amortises the look-back
-  // latency best once the grid has a workgroup per SIMD; smaller problems
-  // take smaller chunks so that the grid still covers the chip.  A grid of at
-  // most 1024 workgroups of 16 rows is built for four workgroups per CU, so
-  // that all of it is resident at once.
+  // Rows per thread on large grids: 10, built for four workgroups per CU
+  // (120 registers, no spills), so that three other workgroups stream while
+  // one waits in its look-back.  Measured on 4 x 32 x 8192 x 64 (537 MB):
+  // 10 rows 106 us, 12 rows 106 us (2 spilled registers), 16 rows at three
+  // workgroups per CU 113 us, 16 rows at four (17 spilled) slower still,
+  // 8 rows 114 us, 32 rows 124 us, 4 rows 142 us; 4 x 32 x 16384 x 32:
+  // 10 rows 105 us, 8 rows 109 us.  Grids of at most 1024 16-row chunks take
+  // 8 rows (2 x 8 x 16384 x 32: 21.6 us), smaller problems 4 rows so that the
+  // grid still covers the chip.
   const long nseg = (long)g.B * g.Hphi;
   const int rg = rows_per_group(g.P);
   auto blocks = [&](int T) { return nseg * ((g.L + (long)rg * T - 1) / ((long)rg * T)); };
   int T = 4, minb = 1;
-  if (blocks(16) >= 512) {
-    T = 16;
-    minb = blocks(16) <= 1024 ? 4 : 1;
+  if (blocks(16) > 1024) {
+    T = 10;
+    minb = 4;
   } else if (blocks(8) >= 512) {
     T = 8;
   }
@@ -523,8 +527,8 @@ hipError_t launch_scan(const Geometry& g, const Src& src, float* theta, void* sc
 #define ARP_SCAN_LAUNCH(TT, MB)                                                               \
   hipLaunchKernelGGL((angle_scan_kernel<P, TT, MB, Src>), grid, block, 0, stream, src, theta, hdr, \
                      words, g.L, sp.nchunks, excl)
-  if (sp.rows_per_thread == 16) {
-    if (sp.min_blocks == 4) ARP_SCAN_LAUNCH(16, 4); else ARP_SCAN_LAUNCH(16, 1);
+  if (sp.rows_per_thread == 10) {
+    ARP_SCAN_LAUNCH(10, 4);
   } else if (sp.rows_per_thread == 8) {
     ARP_SCAN_LAUNCH(8, 1);
   } else {
