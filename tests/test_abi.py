@@ -150,3 +150,50 @@ def test_binding_refuses_cpu_tensors():
     phi = torch.zeros(1, 1, 8, 32)
     with pytest.raises(ValueError):
         b.forward(q, q, q, phi)
+
+
+def test_generated_angle_entry_points_validate_arguments():
+    L = b.lib()
+    d = _desc()
+    by = ctypes.byref(d)
+    st = L.arp_scan_state_bytes(by)
+    # random draws: bound and theta required and 16-byte aligned, state checked
+    assert L.arp_angle_scan_random(by, 1, 0, None, A, A, st, None) == b.ERR_INVALID_ARG
+    assert L.arp_angle_scan_random(by, 1, 0, A, None, A, st, None) == b.ERR_INVALID_ARG
+    assert L.arp_angle_scan_random(by, 1, 0, M, A, A, st, None) == b.ERR_ALIGNMENT
+    assert L.arp_angle_scan_random(by, 1, 0, A, A, None, st, None) == b.ERR_WORKSPACE
+    assert L.arp_angle_scan_random(by, 1, 0, A, A, A, 16, None) == b.ERR_WORKSPACE
+    assert L.arp_random_phi(by, 1, 0, None, A, None) == b.ERR_INVALID_ARG
+    assert L.arp_random_phi(by, 1, 0, A, M, None) == b.ERR_ALIGNMENT
+    # token table: ids 4-byte aligned, table 16-byte aligned, vocab in [1, 2^31)
+    assert L.arp_angle_scan_tokens(by, A, A, 0, A, A, st, None) == b.ERR_INVALID_ARG
+    assert L.arp_angle_scan_tokens(by, A, A, 1 << 31, A, A, st, None) == b.ERR_INVALID_ARG
+    assert L.arp_angle_scan_tokens(by, None, A, 10, A, A, st, None) == b.ERR_INVALID_ARG
+    assert L.arp_angle_scan_tokens(by, A + 2, A, 10, A, A, st, None) == b.ERR_ALIGNMENT
+    assert L.arp_angle_scan_tokens(by, A + 4, M, 10, A, A, st, None) == b.ERR_ALIGNMENT
+    assert L.arp_angle_scan_tokens(by, A + 4, A, 10, A, A, 8, None) == b.ERR_WORKSPACE
+    # constant steps take no scan state
+    assert L.arp_angle_scan_const(by, None, A, None) == b.ERR_INVALID_ARG
+    assert L.arp_angle_scan_const(by, A, M, None) == b.ERR_ALIGNMENT
+    bad = _desc(head_dim=63)
+    assert L.arp_angle_scan_const(ctypes.byref(bad), A, A, None) == b.ERR_INVALID_ARG
+    assert L.arp_random_phi(ctypes.byref(bad), 1, 0, A, A, None) == b.ERR_INVALID_ARG
+
+
+def test_forget_gate_flag_is_refused_outside_the_gated_forward():
+    L = b.lib()
+    d = _desc(flags=b.ROTATE_QK | b.FORGET_GATE)
+    by = ctypes.byref(d)
+    big = L.arp_workspace_bytes(by)
+    st = L.arp_scan_state_bytes(by)
+    assert L.arp_forward(by, A, A, A, A, None, A, A, A, st, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_fwd(by, A, A, A, A, None, A, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_rotate_qkv(by, A, A, A, A, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_rotated(by, A, None, A, A, big, None) == b.ERR_INVALID_ARG
+    # the gated forward needs the gates
+    assert L.arp_forward_ex(by, A, A, A, A, None, None, A, A, None, A, st, A, big,
+                            None) == b.ERR_INVALID_ARG
+    # fp32 I/O has no gated path
+    df = _desc(dtype="f32", flags=b.ROTATE_QK | b.FORGET_GATE)
+    assert L.arp_forward_ex(ctypes.byref(df), A, A, A, A, None, A, A, A, None, A, st, A, big,
+                            None) == b.ERR_UNSUPPORTED
