@@ -88,8 +88,9 @@ hipError_t launch_rotate_diag(const Geometry& g, const void* x, const float* the
 // Operands the gradient kernels read, in the backward workspace (per head):
 //   qs, k, v, dout   bf16 [B*H, Lp, D]: q~ * scale * log2 e, k~, v~, do~
 //   qsT, kT, doutT   bf16 [B*H, D, Lp]: transposes of qs, k, dout
-//   stats            fp32 [B*H, Lp/64, 128]: per 64-row tile, lse (+inf past L)
-//                    then D = <do~, o~> (0 past L)
+//   stats            fp32 [B*H, Lp/64, 128]: per 64-row tile, -lse (-inf past L)
+//                    then -D = -<do~, o~> (0 past L), negated for the MFMA
+//                    accumulator input
 struct BwdOperands {
   uint16_t* qs;
   uint16_t* qsT;

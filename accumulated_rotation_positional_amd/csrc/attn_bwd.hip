@@ -18,8 +18,8 @@
 // Kernels, in stream order:
 //  1. bwd_prep: one pass over q, k, v, o, dO and Theta per 64-token tile:
 //     the bf16 operands (q~ scaled by scale log2 e, k~, v~, do~ row-major;
-//     q~^T, k~^T, do~^T transposed through LDS), per-row lse (padded with
-//     +inf) and D, and dTheta initialised with the value-transport term.
+//     q~^T, k~^T, do~^T transposed through LDS), per-row -lse (padded with
+//     -inf) and -D, and dTheta initialised with the value-transport term.
 //  2. bwd_dkdv: key-stationary; a lane owns one key.  Per 32-query block:
 //       S    = Q~ K~^T   - lse   (A: q~ rows from LDS, B: k~ row in registers)
 //       dP'  = dO~ V~^T  - D     (A: do~ rows from LDS, B: v~ row in registers)
@@ -131,8 +131,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
 #pragma unroll
     for (int m = 1; m < CPR; m <<= 1) dsum += __shfl_xor(dsum, m);
     if (c == 0) {
-      stats[r] = (tok < L) ? lse[(size_t)bh * L + tok] : INFINITY;
-      stats[TILE + r] = (tok < L) ? dsum : 0.f;
+      stats[r] = (tok < L) ? -lse[(size_t)bh * L + tok] : -INFINITY;
+      stats[TILE + r] = (tok < L) ? -dsum : 0.f;
     }
     const u32x4* src[3] = {&wq, &wk, &wd};
 #pragma unroll
@@ -322,10 +322,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
         const f32x4 d1 = *reinterpret_cast<const f32x4*>(sl + TILE + ro + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          cl[8 * h2 + e] = -l0[e];
-          cl[8 * h2 + 4 + e] = -l1[e];
-          cd[8 * h2 + e] = -d0[e];
-          cd[8 * h2 + 4 + e] = -d1[e];
+          cl[8 * h2 + e] = l0[e];
+          cl[8 * h2 + 4 + e] = l1[e];
+          cd[8 * h2 + e] = d0[e];
+          cd[8 * h2 + 4 + e] = d1[e];
         }
       }
       f32x16 s = cl, dp = cd;
@@ -334,7 +334,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
         s = mfma32(lds_op<ROWB>(tq, 32 * qb + ln, 2 * ks + hf), kop[ks], s);
         dp = mfma32(lds_op<ROWB>(tdo, 32 * qb + ln, 2 * ks + hf), vop[ks], dp);
       }
-      const bool diag = (qbase == kw);
+      if (ALIBI || qbase == kw) {  // distance bias; the causal mask on the diagonal block
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = qbase + 16 * (r >> 3) + 8 * hf + (r & 7);  // query of element r
+          if (ALIBI) s[r] += slope2 * (float)(j - i);
+          if (qbase == kw && j > i) s[r] = -INFINITY;
+        }
+      }
       bf16x8 pop[2], dsop[2];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
@@ -343,14 +350,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
         for (int e = 0; e < 4; ++e) {
           float x[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = 8 * h2 + 2 * e + u;
-            const int i = qbase + 16 * h2 + 8 * hf + 2 * e + u;  // query of element r
-            float sv = s[r];
-            if (ALIBI) sv += slope2 * (float)(j - i);
-            if (diag && j > i) sv = -INFINITY;
-            x[u] = __builtin_amdgcn_exp2f(sv);
-          }
+          for (int u = 0; u < 2; ++u) x[u] = __builtin_amdgcn_exp2f(s[8 * h2 + 2 * e + u]);
           wp[e] = pack_bf16x2(x[0], x[1]);
           wd[e] = pack_bf16x2(x[0] * dp[8 * h2 + 2 * e], x[1] * dp[8 * h2 + 2 * e + 1]);
         }
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
     doop[ks] = *reinterpret_cast<const bf16x8*>(ops.dout + off);
   }
   const float* srow = ops.stats + ((size_t)bh * (Lp / TILE) + ic / TILE) * (2 * TILE);
-  const float nl = -srow[ic % TILE], nd = -srow[TILE + ic % TILE];
+  const float nl = srow[ic % TILE], nd = srow[TILE + ic % TILE];
   f32x16 cl, cd, dqt[DB];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -461,6 +461,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
         s = mfma32(lds_op<ROWB>(tk, 32 * kb + ln, 2 * ks + hf), qop[ks], s);
         dp = mfma32(lds_op<ROWB>(tv, 32 * kb + ln, 2 * ks + hf), doop[ks], dp);
       }
+      if (ALIBI || diag) {  // distance bias; the causal mask on the diagonal tile
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jj = n * TILE + 32 * kb + 16 * (r >> 3) + 8 * hf + (r & 7);  // key of element r
+          if (ALIBI) s[r] += slope2 * (float)(jj - i);
+          if (diag && jj > i) s[r] = -INFINITY;
+        }
+      }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         uint32_t wd[4];
@@ -470,11 +478,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int r = 8 * h2 + 2 * e + u;
-            const int jj = n * TILE + 32 * kb + 16 * h2 + 8 * hf + 2 * e + u;  // key of element r
-            float sv = s[r];
-            if (ALIBI) sv += slope2 * (float)(jj - i);
-            if (diag && jj > i) sv = -INFINITY;
-            x[u] = __builtin_amdgcn_exp2f(sv) * dp[r];
+            x[u] = __builtin_amdgcn_exp2f(s[r]) * dp[r];
           }
           wd[e] = pack_bf16x2(x[0], x[1]);
         }
