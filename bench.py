@@ -110,10 +110,11 @@ def run_cpu_baseline(w, flags: int, alibi, target_s: float) -> dict:
         want_rows = w.batch * w.heads * w.seqlen
     stride = int(max(1, min(512, round(w.batch * w.heads * w.seqlen / want_rows))))
     rows = _strided_rows(w, stride, 5)
-    # When even every row is quicker than the target, the whole workload is
-    # run again until about target_s / 2 of CPU work has been timed.
+    # The calibration can misjudge the per-row cost (small samples carry the
+    # thread pool's start-up), so the sample is run again until at least
+    # 10 s of CPU work (or eight runs) has been timed.
     reps, dt = 0, 0.0
-    while reps == 0 or (stride == 1 and dt < 0.5 * target_s and reps < 8):
+    while reps == 0 or (dt < min(10.0, target_s) and reps < 8):
         t0 = time.perf_counter()
         prob.rows(rows, nthreads)
         dt += time.perf_counter() - t0
