@@ -37,7 +37,9 @@
 //    most tiles need no rescale of the output accumulator.  Row sums are
 //    formed from the bf16 probabilities with v_dot2_f32_bf16.
 //  * Workgroups are numbered so that each XCD (blockIdx % 8) gets whole
-//    heads (its L2 then holds that head's K/V), longest query tiles first.
+//    heads (its L2 then holds that head's K/V), longest query tiles first;
+//    with a bias, whose early stop makes the work per head uneven, they are
+//    spread across the XCDs instead.
 #include "arp_device.hpp"
 #include "arp_internal.hpp"
 #include "mfma_tile.hpp"
@@ -98,12 +100,23 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
   constexpr int STAGE = KTILE + VTILE + GTILE;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
-  // ---- which tile: XCD-aware, heads grouped per XCD, longest tiles first ----
+  // ---- which tile: longest tiles first; without a bias, heads grouped per
+  // XCD (blockIdx % 8) so that its L2 holds their K/V.  A biased walk stops
+  // early by an amount that differs from head to head (the slope, the gates),
+  // so there the tiles are dealt out across the XCDs, the last query tile of
+  // every head first: grouping would leave the XCD with the gentlest heads
+  // doing several times the average work, and the longest tiles of the last
+  // heads would start last.
+  constexpr bool SPREAD = (BIAS != 0) && !FUSED;
   const int per = (total_tiles + 7) / 8;
-  const int logical = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  const int logical = SPREAD ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (logical >= total_tiles) return;
-  const int bh = logical / nqt;
-  const int qt = nqt - 1 - logical % nqt;
+  const int nbh = total_tiles / nqt;
+  // spread: round r deals query tile nqt-1-r of every head, rotated by r so
+  // that a head does not stay on one XCD (blockIdx % 8) from round to round
+  const int rnd = logical / nbh;
+  const int bh = SPREAD ? (logical % nbh + rnd) % nbh : logical / nqt;
+  const int qt = nqt - 1 - (SPREAD ? rnd : logical % nqt);
   const int q0 = qt * BM;
   const int b = bh / H, h = bh % H;
 
