@@ -151,3 +151,17 @@ def test_fused_rotation_full_size_sampled_rows(name):
     d = float(np.abs(got - ref).max())
     say(f"[gpu] fused vs pre-rotated {name}: max |diff| = {d:.3e}")
     assert d <= 2e-2
+
+
+@pytest.mark.parametrize("alibi", [False, True])
+def test_million_token_sequence_sampled_rows(alibi):
+    """2^20 tokens in one head (64x the longest workload): every index product
+    the kernels form past 2^31 elements-times-bytes is exercised; sampled rows
+    (tile edges, the last rows) against the oracle.  The distance bias takes
+    one gentle slope so the walk is long."""
+    w = wl.make("farmass_32k", batch=1, heads=1, seqlen=1 << 20)
+    w.alibi = np.array([2.0 ** -12], dtype=np.float32)
+    got, _ = run_forward(w, rotate_v=True, alibi=alibi)
+    rows = sample_rows(w, per_head=16)
+    want = oracle_problem(w, rotate_v=True, alibi=alibi).rows(rows)
+    assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", f"2^20 tokens alibi={alibi}")
