@@ -617,13 +617,37 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
 
 }  // namespace
 
+// Compute units of the current device (256 on an MI355X), cached per device.
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                                     const uint16_t* vt, const float* kmax, const float* theta,
                                     const float* alibi, const float* gate2, uint16_t* o,
                                     float* lse, hipStream_t stream) {
-  if (g.D == 64)
+  if (g.D == 64) {
+    // 512-query workgroups (one per CU) unless that leaves compute units
+    // idle: then 256-query workgroups, two per CU, so that short sequences
+    // and few heads still spread over the whole chip (8 x 8 heads at 1024
+    // tokens: 128 workgroups of 512 queries, 40 -> 33 us).  Both shapes
+    // compute every row the same way, so the results are bit-identical.
+    const long wg512 = (long)g.B * g.H * ((g.L + 511) / 512);
+    if (wg512 < device_cus())
+      return launch_bf16_cfg<64, 64, 4, 2, 2, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o,
+                                                     lse, stream);
     return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,
                                                    stream);
+  }
   return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,
                                                   stream);
 }

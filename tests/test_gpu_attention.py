@@ -6,6 +6,8 @@ fp32 I/O max |error| <= 1e-4.  Small problems are compared element by element
 on every output; the five full-size workloads are compared on sampled rows
 (tile edges, the first and last rows, random rows of every head), in the same
 launch configuration the benchmark times."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -165,3 +167,22 @@ def test_million_token_sequence_sampled_rows(alibi):
     rows = sample_rows(w, per_head=16)
     want = oracle_problem(w, rotate_v=True, alibi=alibi).rows(rows)
     assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", f"2^20 tokens alibi={alibi}")
+
+
+def test_workgroup_shapes_agree_on_a_ragged_length():
+    """The d=64 attention takes 512-query workgroups (8 waves) on grids that
+    fill the chip and 256-query workgroups (4 waves, two per CU) on smaller
+    ones.  72 heads at 1800 tokens (1800 = 3*512 + 264, a ragged 8-key tail)
+    take the 8-wave shape (288 workgroups); three of those heads alone take
+    the 4-wave shape.  Every row is computed the same way in both, so the
+    three heads must agree bit for bit; the big run is also checked against
+    the oracle on sampled rows."""
+    w = wl.make("train_1k", batch=1, heads=72, seqlen=1800)
+    got, _ = run_forward(w, rotate_v=True)
+    rows = sample_rows(w, per_head=4)
+    want = oracle_problem(w, rotate_v=True).rows(rows)
+    assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", "8-wave shape, L=1800")
+    part = dataclasses.replace(w, heads=3, **{n: np.ascontiguousarray(getattr(w, n)[:, :3])
+                                              for n in ("q", "k", "v", "phi")})
+    small, _ = run_forward(part, rotate_v=True)
+    assert np.array_equal(small, got[:, :3]), float(np.abs(small - got[:, :3]).max())
