@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     uint64_t* __restrict__ state, uint16_t* __restrict__ o, int H, int Hphi, int nchunk,
     uint32_t flags) {
   constexpr int P = D / 2, G = 256 / P;
-  __shared__ float s_red[256];
+  __shared__ float s_red[4];
   __shared__ float s_sum[G][P][3];
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh % H, g = (Hphi == 1) ? 0 : h;
@@ -257,22 +257,33 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   const float* src = part + (size_t)bh * nchunk * (D + 2);
   float M = -INFINITY;
   for (int c = tid; c < nchunk; c += 256) M = fmaxf(M, src[(size_t)c * (D + 2)]);
-  s_red[tid] = M;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((tid & 63) == 0) s_red[tid >> 6] = M;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
-    __syncthreads();
-  }
-  M = s_red[0];
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   float Ls = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int c = cg; c < nchunk; c += G) {
-    const float* pc = src + (size_t)c * (D + 2);
-    const float mc = pc[0];
-    if (mc == -INFINITY) continue;
-    const float f = __builtin_amdgcn_exp2f(mc - M);
-    Ls = fmaf(pc[1], f, Ls);
-    a0 = fmaf(pc[2 + 2 * p], f, a0);
-    a1 = fmaf(pc[3 + 2 * p], f, a1);
+  // four chunks per trip, all their loads issued before any is used (every
+  // chunk holds at least one key, so its maximum is finite)
+  constexpr int U = 4;
+  for (int c0 = cg; c0 < nchunk; c0 += U * G) {
+    float mc[U], lc[U], x0[U], x1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float* pc = src + (size_t)min(c0 + u * G, nchunk - 1) * (D + 2);
+      mc[u] = pc[0];
+      lc[u] = pc[1];
+      x0[u] = pc[2 + 2 * p];
+      x1[u] = pc[3 + 2 * p];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u * G >= nchunk) break;
+      const float f = __builtin_amdgcn_exp2f(mc[u] - M);
+      Ls = fmaf(lc[u], f, Ls);
+      a0 = fmaf(x0[u], f, a0);
+      a1 = fmaf(x1[u], f, a1);
+    }
   }
   s_sum[cg][p][0] = Ls;
   s_sum[cg][p][1] = a0;
