@@ -10,9 +10,12 @@ import dataclasses
 
 import numpy as np
 import pytest
+import torch
 
+from accumulated_rotation_positional_amd import binding
 from accumulated_rotation_positional_amd import workloads as wl
-from gpu_util import (assert_close, circular_err, oracle_problem, run_forward, sample_rows, say)
+from gpu_util import (assert_close, circular_err, oracle_flags, oracle_problem, run_forward,
+                      sample_rows, say, to_dev, to_host)
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -169,20 +172,40 @@ def test_million_token_sequence_sampled_rows(alibi):
     assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", f"2^20 tokens alibi={alibi}")
 
 
-def test_workgroup_shapes_agree_on_a_ragged_length():
+@pytest.mark.parametrize("bias", ["none", "alibi", "gate", "gate+alibi"])
+@pytest.mark.parametrize("rotate_v", [False, True])
+def test_workgroup_shapes_agree_on_a_ragged_length(bias, rotate_v):
     """The d=64 attention takes 512-query workgroups (8 waves) on grids that
     fill the chip and 256-query workgroups (4 waves, two per CU) on smaller
     ones.  72 heads at 1800 tokens (1800 = 3*512 + 264, a ragged 8-key tail)
     take the 8-wave shape (288 workgroups); three of those heads alone take
-    the 4-wave shape.  Every row is computed the same way in both, so the
-    three heads must agree bit for bit; the big run is also checked against
-    the oracle on sampled rows."""
+    the 4-wave shape.  Every row is computed the same way in both (the biased
+    walk included), so the three heads must agree bit for bit, log-sum-exp
+    too; the big run is also checked against the oracle on sampled rows."""
+    from test_gpu_forget import _gates
+    alibi, gate = "alibi" in bias, "gate" in bias
     w = wl.make("train_1k", batch=1, heads=72, seqlen=1800)
-    got, _ = run_forward(w, rotate_v=True)
+    logf = _gates(w) if gate else None
+
+    slopes = wl.alibi_slopes(w.heads)  # the subset keeps its heads' slopes
+
+    def run(x, lf):
+        al = to_dev(np.ascontiguousarray(slopes[:x.heads])) if alibi else None
+        say(f"[gpu] shapes H={x.heads} L={x.seqlen} bias={bias} v={rotate_v}")
+        o, _, lse = binding.forward_ex(to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.phi),
+                                       rotate_v=rotate_v, alibi=al,
+                                       logf=None if lf is None else to_dev(lf), with_lse=True)
+        torch.cuda.synchronize()
+        return to_host(o), lse.cpu().numpy()
+
+    got, lse = run(w, logf)
     rows = sample_rows(w, per_head=4)
-    want = oracle_problem(w, rotate_v=True).rows(rows)
-    assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", "8-wave shape, L=1800")
+    flags = oracle_flags(True, rotate_v, alibi) | (oracle.FORGET if gate else 0)
+    want = oracle.Problem(w.q, w.k, w.v, w.phi, flags,
+                          alibi=slopes if alibi else None, logf=logf).rows(rows)
+    assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", f"8-wave shape, {bias}")
     part = dataclasses.replace(w, heads=3, **{n: np.ascontiguousarray(getattr(w, n)[:, :3])
                                               for n in ("q", "k", "v", "phi")})
-    small, _ = run_forward(part, rotate_v=True)
+    small, lse_small = run(part, None if logf is None else np.ascontiguousarray(logf[:, :3]))
     assert np.array_equal(small, got[:, :3]), float(np.abs(small - got[:, :3]).max())
+    assert np.array_equal(lse_small, lse[:, :3])
