@@ -58,6 +58,16 @@ def test_small_all_flags(name, L, flags):
     assert circular_err(theta, th_ref) <= 1e-4
 
 
+@pytest.mark.parametrize("L", [1, 2, 3, 33, 65, 130])
+def test_fp32_ragged_lengths(L):
+    """fp32 I/O at lengths that leave some of a query's four key lanes
+    without keys (query 0 has one key) and tiles part-filled."""
+    w = wl.make("tiny_f32", batch=1, heads=2, seqlen=L)
+    flags = dict(rotate_qk=True, rotate_v=True, alibi=True)
+    got, _ = run_forward(w, **flags)
+    assert_close(got, oracle_problem(w, **flags).output(), "f32", f"fp32 L={L}")
+
+
 @pytest.mark.parametrize("flags", FLAG_SETS[:3], ids=[_ids(f) for f in FLAG_SETS[:3]])
 def test_fp32_head_dim_128(flags):
     w = _as_f32(wl.make("rope_8k_d128", batch=1, heads=2, seqlen=150))
