@@ -475,8 +475,7 @@ arp_status arp_decode_step(const arp_desc* desc, int32_t pos, const void* q, con
   a.kcache = static_cast<uint16_t*>(kcache);
   a.vcache = static_cast<uint16_t*>(vcache);
   a.o = static_cast<uint16_t*>(o);
-  a.qrot = static_cast<float*>(workspace);
-  a.part = a.qrot + (size_t)g.B * g.H * g.D;
+  a.part = static_cast<float*>(workspace);
   return hip_status(launch_decode_step(g, a, (hipStream_t)stream));
 }
 

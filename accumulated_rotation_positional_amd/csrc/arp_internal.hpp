@@ -126,7 +126,7 @@ struct DecodeArgs {
   float* theta;                 // [B, Hphi, P] out: the new token's angles
   uint16_t *kcache, *vcache;    // [B, H, L, D] pre-rotated k~, v~
   uint16_t* o;                  // [B, H, D]
-  float *qrot, *part;           // workspace: [B*H, D], [B*H, ceil(L/256), D + 2]
+  float* part;                  // workspace: [B*H, ceil(L/256), D + 2] partial results
 };
 size_t decode_workspace_bytes(const Geometry& g);
 hipError_t launch_decode_prefill(const Geometry& g, int len, const uint16_t* k, const uint16_t* v,

@@ -14,9 +14,13 @@
 //   4. un-rotate the output by R(Theta_t)^T when values are transported.
 //
 // Kernels of a step:
-//   decode_append   one workgroup per (b, h), a thread per rotary pair
 //   decode_attn     split over the keys: one workgroup per (256 keys, b, h);
-//                   each wave reads its 64 keys and values in whole-row,
+//                   every workgroup forms the new token's angles (state +
+//                   steps) and rotated query itself; the lanes holding row
+//                   pos rotate the new key and value, use them from
+//                   registers and append them to the caches; one lane group
+//                   writes the angles out.  Each wave reads its 64 keys and
+//                   values in whole-row,
 //                   1 KB-per-instruction loads, scores them, takes its own
 //                   softmax maximum and sum and its P V; the four waves merge
 //                   in LDS into one partial (m, l, acc)
@@ -93,41 +97,6 @@ __global__ __launch_bounds__(256) void decode_state_kernel(const float* __restri
 // ---------------------------------------------------------------------------
 // step
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(D / 2) void decode_append_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ phi, const uint64_t* __restrict__ state, float* __restrict__ theta,
-    uint16_t* __restrict__ kcache, uint16_t* __restrict__ vcache, float* __restrict__ qrot, int H,
-    int Hphi, int Lmax, int pos, uint32_t flags, float qscale) {
-  constexpr int P = D / 2;
-  const int bh = blockIdx.x;
-  const int b = bh / H, h = bh % H, g = (Hphi == 1) ? 0 : h;
-  const int p = threadIdx.x;
-  const size_t sidx = (size_t)(b * Hphi + g) * P + p;
-  const uint64_t cur = (flags & ARP_SCAN_EXCLUSIVE) ? state[sidx] : state[sidx] + to_fixed(phi[sidx]);
-  const float th = to_radians_offset(cur);
-  if (Hphi != 1 || h == 0) theta[sidx] = th;
-  float sn, cs;
-  sincosf(th, &sn, &cs);
-  const size_t in = (size_t)bh * D + 2 * p;
-  const uint32_t wq = *reinterpret_cast<const uint32_t*>(q + in);
-  const uint32_t wk = *reinterpret_cast<const uint32_t*>(k + in);
-  const uint32_t wv = *reinterpret_cast<const uint32_t*>(v + in);
-  float q0 = lo_bf16(wq), q1 = hi_bf16(wq), k0 = lo_bf16(wk), k1 = hi_bf16(wk);
-  float v0 = lo_bf16(wv), v1 = hi_bf16(wv);
-  if (flags & ARP_ROTATE_QK) {
-    rotate_pair(q0, q1, cs, sn);
-    rotate_pair(k0, k1, cs, sn);
-  }
-  if (flags & ARP_ROTATE_V) rotate_pair(v0, v1, cs, sn);
-  // the query as the attention pass multiplies it: bf16-rounded like a cached key
-  qrot[in] = lo_bf16(pack_bf16x2(q0 * qscale, q1 * qscale));
-  qrot[in + 1] = hi_bf16(pack_bf16x2(q0 * qscale, q1 * qscale));
-  const size_t out = ((size_t)bh * Lmax + pos) * D + 2 * p;
-  *reinterpret_cast<uint32_t*>(kcache + out) = pack_bf16x2(k0, k1);
-  *reinterpret_cast<uint32_t*>(vcache + out) = pack_bf16x2(v0, v1);
-}
-
 // One partial per (256 keys, b, h): part = [m, l, acc[0..D)] in base-2 logits.
 // Every load instruction of a wave reads whole consecutive cache rows (CPR
 // lanes of 16 bytes per row, 1 KB per instruction): lane (r, c) holds chunk c
@@ -135,26 +104,69 @@ __global__ __launch_bounds__(D / 2) void decode_append_kernel(
 // P V accumulates per lane and is reduced over the RPI row groups at the end.
 template <int D, bool ALIBI>
 __global__ __launch_bounds__(256) void decode_attn_kernel(
-    const float* __restrict__ qrot, const uint16_t* __restrict__ kcache,
-    const uint16_t* __restrict__ vcache, const float* __restrict__ alibi, float* __restrict__ part,
-    int H, int Lmax, int pos, int nchunk) {
+    const uint16_t* __restrict__ qin, const uint16_t* __restrict__ kin,
+    const uint16_t* __restrict__ vin, const float* __restrict__ phi,
+    const uint64_t* __restrict__ state, float* __restrict__ theta, uint16_t* __restrict__ kcache,
+    uint16_t* __restrict__ vcache, const float* __restrict__ alibi, float* __restrict__ part,
+    int H, int Hphi, int Lmax, int pos, int nchunk, uint32_t flags, float qscale) {
   constexpr int CPR = D / 8;     // lanes per row
   constexpr int RPI = 64 / CPR;  // rows per load instruction
   constexpr int NI = 64 / RPI;   // instructions per 64 keys
   __shared__ float s_m[4], s_l[4];
   __shared__ float s_acc[4][D];
-  const int c = blockIdx.x, bh = blockIdx.y, h = bh % H;
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / H, h = bh % H, g = (Hphi == 1) ? 0 : h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ch = lane % CPR, rg = lane / CPR;
   const int n = pos + 1;                // keys 0..pos
   const int kw0 = c * DKC + wave * 64;  // this wave's first key
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
+
+  // The new token's angles for this lane's four pairs 4 ch .. 4 ch + 3: the
+  // state plus its steps (the scan's arithmetic, so bit-identical to it).
+  float sn[4], cs[4];
+  const size_t sbase = (size_t)(b * Hphi + g) * (D / 2) + 4 * ch;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint64_t cur = (flags & ARP_SCAN_EXCLUSIVE) ? state[sbase + e]
+                                                      : state[sbase + e] + to_fixed(phi[sbase + e]);
+    const float th = to_radians_offset(cur);
+    // one writer per angle stream: the first chunk's row group 0 of wave 0
+    if (c == 0 && wave == 0 && rg == 0 && (Hphi != 1 || h == 0)) theta[sbase + e] = th;
+    sincosf(th, &sn[e], &cs[e]);
+  }
+  const bool rqk = (flags & ARP_ROTATE_QK) != 0, rv = (flags & ARP_ROTATE_V) != 0;
+  // q~ as the products use it: rotated, scaled, rounded to bf16 like a cached key
   float qv[8];
   {
-    const float4 a = *reinterpret_cast<const float4*>(qrot + (size_t)bh * D + 8 * ch);
-    const float4 b2 = *reinterpret_cast<const float4*>(qrot + (size_t)bh * D + 8 * ch + 4);
-    qv[0] = a.x; qv[1] = a.y; qv[2] = a.z; qv[3] = a.w;
-    qv[4] = b2.x; qv[5] = b2.y; qv[6] = b2.z; qv[7] = b2.w;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(qin + (size_t)bh * D + 8 * ch);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float q0 = lo_bf16(w[e]), q1 = hi_bf16(w[e]);
+      if (rqk) rotate_pair(q0, q1, cs[e], sn[e]);
+      const uint32_t r = pack_bf16x2(q0 * qscale, q1 * qscale);
+      qv[2 * e] = lo_bf16(r);
+      qv[2 * e + 1] = hi_bf16(r);
+    }
+  }
+  // The new key and value, rotated, in the lanes that hold row pos: they
+  // take part in this step from registers and are appended to the caches.
+  const bool owner = (pos >= kw0) && (pos < kw0 + 64) && ((pos - kw0) % RPI == rg);
+  u32x4 knew = {0, 0, 0, 0}, vnew = {0, 0, 0, 0};
+  if (owner) {
+    const u32x4 wk = *reinterpret_cast<const u32x4*>(kin + (size_t)bh * D + 8 * ch);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(vin + (size_t)bh * D + 8 * ch);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float k0 = lo_bf16(wk[e]), k1 = hi_bf16(wk[e]), v0 = lo_bf16(wv[e]), v1 = hi_bf16(wv[e]);
+      if (rqk) rotate_pair(k0, k1, cs[e], sn[e]);
+      if (rv) rotate_pair(v0, v1, cs[e], sn[e]);
+      knew[e] = pack_bf16x2(k0, k1);
+      vnew[e] = pack_bf16x2(v0, v1);
+    }
+    const size_t out = ((size_t)bh * Lmax + pos) * D + 8 * ch;
+    *reinterpret_cast<u32x4*>(kcache + out) = knew;
+    *reinterpret_cast<u32x4*>(vcache + out) = vnew;
   }
   const uint16_t* kb = kcache + (size_t)bh * Lmax * D + 8 * ch;
   const uint16_t* vb = vcache + (size_t)bh * Lmax * D + 8 * ch;
@@ -162,7 +174,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int row = kw0 + RPI * i + rg;
-    kw[i] = (row < n) ? *reinterpret_cast<const u32x4*>(kb + (size_t)row * D) : u32x4{0, 0, 0, 0};
+    kw[i] = (row < pos) ? *reinterpret_cast<const u32x4*>(kb + (size_t)row * D)
+                        : (row == pos ? knew : u32x4{0, 0, 0, 0});
   }
   float sc[NI];
   float m = -INFINITY;
@@ -188,7 +201,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int row = kw0 + RPI * i + rg;
-    vw[i] = (row < n) ? *reinterpret_cast<const u32x4*>(vb + (size_t)row * D) : u32x4{0, 0, 0, 0};
+    vw[i] = (row < pos) ? *reinterpret_cast<const u32x4*>(vb + (size_t)row * D)
+                        : (row == pos ? vnew : u32x4{0, 0, 0, 0});
   }
   float l = 0.f, acc[8];
 #pragma unroll
@@ -313,16 +327,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 template <int D>
 hipError_t launch_step(const Geometry& g, const DecodeArgs& a, hipStream_t stream) {
   const int BH = g.B * g.H;
-  hipLaunchKernelGGL((decode_append_kernel<D>), dim3(BH), dim3(D / 2), 0, stream, a.q, a.k, a.v,
-                     a.phi, a.state, a.theta, a.kcache, a.vcache, a.qrot, g.H, g.Hphi, g.L, a.pos,
-                     g.flags, g.scale * LOG2E);
   const int nchunk = (a.pos + 1 + DKC - 1) / DKC;
+  const float qscale = g.scale * LOG2E;
   if (g.flags & ARP_ALIBI)
-    hipLaunchKernelGGL((decode_attn_kernel<D, true>), dim3(nchunk, BH), dim3(256), 0, stream, a.qrot,
-                       a.kcache, a.vcache, a.alibi, a.part, g.H, g.L, a.pos, nchunk);
+    hipLaunchKernelGGL((decode_attn_kernel<D, true>), dim3(nchunk, BH), dim3(256), 0, stream, a.q,
+                       a.k, a.v, a.phi, a.state, a.theta, a.kcache, a.vcache, a.alibi, a.part, g.H,
+                       g.Hphi, g.L, a.pos, nchunk, g.flags, qscale);
   else
-    hipLaunchKernelGGL((decode_attn_kernel<D, false>), dim3(nchunk, BH), dim3(256), 0, stream,
-                       a.qrot, a.kcache, a.vcache, a.alibi, a.part, g.H, g.L, a.pos, nchunk);
+    hipLaunchKernelGGL((decode_attn_kernel<D, false>), dim3(nchunk, BH), dim3(256), 0, stream, a.q,
+                       a.k, a.v, a.phi, a.state, a.theta, a.kcache, a.vcache, a.alibi, a.part, g.H,
+                       g.Hphi, g.L, a.pos, nchunk, g.flags, qscale);
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(BH), dim3(256), 0, stream, a.part, a.theta,
                      a.phi, a.state, a.o, g.H, g.Hphi, nchunk, g.flags);
   return hipGetLastError();
@@ -332,7 +346,7 @@ hipError_t launch_step(const Geometry& g, const DecodeArgs& a, hipStream_t strea
 
 size_t decode_workspace_bytes(const Geometry& g) {
   const size_t nchunk = ((size_t)g.L + DKC - 1) / DKC;
-  return (size_t)g.B * g.H * (nchunk * (g.D + 2) + g.D) * sizeof(float);
+  return (size_t)g.B * g.H * nchunk * (g.D + 2) * sizeof(float);
 }
 
 hipError_t launch_decode_prefill(const Geometry& g, int len, const uint16_t* k, const uint16_t* v,
