@@ -636,19 +636,35 @@ hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const
                                     const float* alibi, const float* gate2, uint16_t* o,
                                     float* lse, hipStream_t stream) {
   if (g.D == 64) {
-    // 512-query workgroups (one per CU) unless that leaves compute units
-    // idle: then 256-query workgroups, two per CU, so that short sequences
-    // and few heads still spread over the whole chip (8 x 8 heads at 1024
-    // tokens: 128 workgroups of 512 queries, 40 -> 33 us).  Both shapes
-    // compute every row the same way, so the results are bit-identical.
+    // Two shapes, every row computed the same way in both (bit-identical
+    // results):
+    //  * 512-query workgroups of 8 waves x 64 queries, one per CU: the most
+    //    matrix-core work per LDS operand read; best on long, deep grids
+    //    (2 x 8 heads at 16384 tokens: 0.51 ms against 0.60 ms);
+    //  * 128-query workgroups of 4 waves x 32 queries, two per CU: finer
+    //    grains, so a grid's causal tail and a biased walk's uneven early
+    //    stops cost less (8 x 8 heads at 1024 tokens 28.5 -> 24.2 us, 1 x 8 at
+    //    16384 408 -> 291 us, ALiBi on 1 x 16 at 32768 1.34 -> 1.02 ms).
+    // The first is taken for an unbiased walk over at least 16384 tokens
+    // whose 512-query grid fills every CU twice, the second otherwise.
     const long wg512 = (long)g.B * g.H * ((g.L + 511) / 512);
-    if (wg512 < device_cus())
-      return launch_bf16_cfg<64, 64, 4, 2, 2, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o,
+    const bool biased = (g.flags & (ARP_ALIBI | ARP_FORGET_GATE)) != 0;
+    if (!biased && g.L >= 16384 && wg512 >= 2L * device_cus())
+      return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o,
                                                      lse, stream);
-    return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,
+    return launch_bf16_cfg<64, 32, 4, 2, 2, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,
                                                    stream);
   }
-  return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,
+  // d = 128: 256-query workgroups of 8 waves x 32 queries for unbiased grids
+  // of at least four per CU (4 x 32 heads at 8192 tokens: 2.06 ms against
+  // 2.12 ms), else 128-query workgroups of 4 waves x 32 queries, two per CU
+  // (1 x 8 heads at 8192 tokens 213 -> 201 us, 2 x 8 at 2048 63 -> 51 us).
+  const long wg256 = (long)g.B * g.H * ((g.L + 255) / 256);
+  const bool biased = (g.flags & (ARP_ALIBI | ARP_FORGET_GATE)) != 0;
+  if (!biased && wg256 >= 4L * device_cus())
+    return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o,
+                                                    lse, stream);
+  return launch_bf16_cfg<128, 32, 4, 2, 2, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,
                                                   stream);
 }
 

@@ -182,40 +182,35 @@ def test_million_token_sequence_sampled_rows(alibi):
     assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", f"2^20 tokens alibi={alibi}")
 
 
-@pytest.mark.parametrize("bias", ["none", "alibi", "gate", "gate+alibi"])
-@pytest.mark.parametrize("rotate_v", [False, True])
-def test_workgroup_shapes_agree_on_a_ragged_length(bias, rotate_v):
-    """The d=64 attention takes 512-query workgroups (8 waves) on grids that
-    fill the chip and 256-query workgroups (4 waves, two per CU) on smaller
-    ones.  72 heads at 1800 tokens (1800 = 3*512 + 264, a ragged 8-key tail)
-    take the 8-wave shape (288 workgroups); three of those heads alone take
-    the 4-wave shape.  Every row is computed the same way in both (the biased
-    walk included), so the three heads must agree bit for bit, log-sum-exp
-    too; the big run is also checked against the oracle on sampled rows."""
-    from test_gpu_forget import _gates
-    alibi, gate = "alibi" in bias, "gate" in bias
-    w = wl.make("train_1k", batch=1, heads=72, seqlen=1800)
-    logf = _gates(w) if gate else None
+@pytest.mark.parametrize("name,heads,L,rotate_v", [("train_1k", 16, 16400, False),
+                                                   ("train_1k", 16, 16400, True),
+                                                   ("rope_8k_d128", 32, 8200, False)])
+def test_workgroup_shapes_agree_on_a_ragged_length(name, heads, L, rotate_v):
+    """The d=64 attention takes 512-query workgroups (8 waves x 64 queries)
+    for unbiased walks over at least 16384 tokens whose 512-query grid fills
+    every CU twice, and 128-query workgroups (4 waves x 32 queries, two per
+    CU) otherwise.  16 heads at 16400 tokens (16400 = 256*64 + 16, a ragged
+    16-key tail; 528 workgroups of 512) take the first; three of those heads
+    alone take the second.  Every row is computed the same way in both, so
+    the three heads must agree bit for bit, log-sum-exp too; the big run is
+    also checked against the oracle on sampled rows.  At d=128 the shapes are
+    8 waves x 32 queries (unbiased grids of at least four 256-query
+    workgroups per CU: 32 heads at 8200 tokens make 1056) and 4 waves x 32."""
+    w = wl.make(name, batch=1, heads=heads, seqlen=L)
 
-    slopes = wl.alibi_slopes(w.heads)  # the subset keeps its heads' slopes
-
-    def run(x, lf):
-        al = to_dev(np.ascontiguousarray(slopes[:x.heads])) if alibi else None
-        say(f"[gpu] shapes H={x.heads} L={x.seqlen} bias={bias} v={rotate_v}")
+    def run(x):
+        say(f"[gpu] shapes H={x.heads} L={x.seqlen} v={rotate_v}")
         o, _, lse = binding.forward_ex(to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.phi),
-                                       rotate_v=rotate_v, alibi=al,
-                                       logf=None if lf is None else to_dev(lf), with_lse=True)
+                                       rotate_v=rotate_v, with_lse=True)
         torch.cuda.synchronize()
         return to_host(o), lse.cpu().numpy()
 
-    got, lse = run(w, logf)
-    rows = sample_rows(w, per_head=4)
-    flags = oracle_flags(True, rotate_v, alibi) | (oracle.FORGET if gate else 0)
-    want = oracle.Problem(w.q, w.k, w.v, w.phi, flags,
-                          alibi=slopes if alibi else None, logf=logf).rows(rows)
-    assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", f"8-wave shape, {bias}")
+    got, lse = run(w)
+    rows = sample_rows(w, per_head=6)
+    want = oracle.Problem(w.q, w.k, w.v, w.phi, oracle_flags(True, rotate_v, False)).rows(rows)
+    assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", f"8-wave shape, {name} L={L}")
     part = dataclasses.replace(w, heads=3, **{n: np.ascontiguousarray(getattr(w, n)[:, :3])
                                               for n in ("q", "k", "v", "phi")})
-    small, lse_small = run(part, None if logf is None else np.ascontiguousarray(logf[:, :3]))
+    small, lse_small = run(part)
     assert np.array_equal(small, got[:, :3]), float(np.abs(small - got[:, :3]).max())
     assert np.array_equal(lse_small, lse[:, :3])
