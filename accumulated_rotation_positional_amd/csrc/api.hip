@@ -96,7 +96,8 @@ BwdWorkspaceLayout bwd_workspace_layout(const Geometry& g) {
   BwdWorkspaceLayout lay{};
   lay.operand_bytes = align_up((size_t)g.B * g.H * g.Lp * g.D * sizeof(uint16_t));
   lay.stats_off = 7 * lay.operand_bytes;
-  lay.totals_off = lay.stats_off + align_up((size_t)g.B * g.H * g.Lp * 2 * sizeof(float));
+  lay.tstat_off = lay.stats_off + align_up((size_t)g.B * g.H * g.Lp * 2 * sizeof(float));
+  lay.totals_off = lay.tstat_off + align_up((size_t)g.B * g.H * (g.Lp / KEY_TILE) * 4 * sizeof(float));
   const size_t nch = ((size_t)g.L + 255) / 256;
   lay.total = lay.totals_off + align_up((size_t)g.B * g.Hphi * nch * g.P * sizeof(float));
   return lay;
@@ -412,7 +413,8 @@ arp_status arp_backward(const arp_desc* desc, const void* q, const void* k, cons
   a.dphi = dphi;
   a.totals = reinterpret_cast<float*>(ws + lay.totals_off);
   a.ops = BwdOperands{blk(0), blk(1), blk(2), blk(3), blk(4), blk(5), blk(6),
-                      reinterpret_cast<float*>(ws + lay.stats_off)};
+                      reinterpret_cast<float*>(ws + lay.stats_off),
+                      reinterpret_cast<float*>(ws + lay.tstat_off)};
   return hip_status(launch_backward_bf16(g, a, (hipStream_t)stream));
 }
 

@@ -100,6 +100,7 @@ struct BwdOperands {
   uint16_t* dout;
   uint16_t* doutT;
   float* stats;
+  float* tstat;  // per 64-token tile: max |q~ scale log2 e|, max |k~|, max_i (-lse_i - slope2 i), 0
 };
 struct BwdArgs {
   const uint16_t *q, *k, *v, *o, *dout;  // caller tensors [B, H, L, D]
@@ -112,7 +113,7 @@ struct BwdArgs {
 };
 struct BwdWorkspaceLayout {
   size_t operand_bytes;  // one bf16 [B*H, Lp, D] block
-  size_t stats_off, totals_off, total;
+  size_t stats_off, tstat_off, totals_off, total;
 };
 BwdWorkspaceLayout bwd_workspace_layout(const Geometry& g);
 hipError_t launch_backward_bf16(const Geometry& g, const BwdArgs& a, hipStream_t stream);

@@ -45,6 +45,15 @@ namespace arp {
 namespace {
 
 constexpr int TILE = 64;  // tokens per tile (queries or keys)
+// With a distance bias, a (query tile, key range) block whose base-2
+// log-probabilities s_ij - lse_i are all below -ZGAP_B has probabilities
+// 2^(s - lse) < 2^-160, below fp32's smallest subnormal: all exactly zero, so
+// P, dS and every contribution of the block to dK, dV and dQ are exactly
+// zero and the block can be left out without changing a bit.  The bound is
+//   |q~s_i| |k~_j| + slope2 (j - i) - lse_i
+//     <= max_i |q~s_i| * max_j |k~_j| + max_j slope2 j + max_i (-lse_i - slope2 i)
+// (Cauchy-Schwarz; the per-tile maxima come from the prep pass).
+constexpr float ZGAP_B = 160.0f;
 
 // ---------------------------------------------------------------------------
 // 1. prep
@@ -53,13 +62,17 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-    const float* __restrict__ theta, const float* __restrict__ lse, BwdOperands ops,
-    float* __restrict__ dtheta, int L, int Lp, int H, int Hphi, uint32_t flags, float qscale) {
+    const float* __restrict__ theta, const float* __restrict__ lse, const float* __restrict__ alibi,
+    BwdOperands ops, float* __restrict__ dtheta, int L, int Lp, int H, int Hphi, uint32_t flags,
+    float qscale) {
   constexpr int P = D / 2;
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   constexpr int ITER = TILE * CPR / 256;
   constexpr int TS = TILE + 8;  // padded LDS row of a transposed tile (elements)
   __shared__ __attribute__((aligned(16))) uint16_t s_t[3][D * TS];
+  // tile maxima of |q~s|^2, |k~|^2 (bits of non-negative floats) and of -lse_i - slope2 i
+  __shared__ uint32_t s_n2[2];
+  __shared__ float s_c[TILE];
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh % H;
   const int g = (Hphi == 1) ? 0 : h;
@@ -68,6 +81,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   const bool rqk = (flags & ARP_ROTATE_QK) != 0, rv = (flags & ARP_ROTATE_V) != 0;
   const size_t rm = (size_t)bh * Lp * D;  // row-major block of this head
   float* stats = ops.stats + ((size_t)bh * (Lp / TILE) + blockIdx.x) * (2 * TILE);
+  const float slope2 = (flags & ARP_ALIBI) ? alibi[h] * LOG2E : 0.f;
+  if (tid < 2) s_n2[tid] = 0u;
+  __syncthreads();
 
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
@@ -127,12 +143,27 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     *reinterpret_cast<u32x4*>(ops.k + roff) = wk;
     *reinterpret_cast<u32x4*>(ops.v + roff) = wv;
     *reinterpret_cast<u32x4*>(ops.dout + roff) = wd;
-    // D_i: the CPR threads of a row are consecutive lanes
+    // D_i and the row norms of the bf16 operands: the CPR threads of a row
+    // are consecutive lanes
+    float qn2 = 0.f, kn2 = 0.f;
 #pragma unroll
-    for (int m = 1; m < CPR; m <<= 1) dsum += __shfl_xor(dsum, m);
+    for (int e = 0; e < 4; ++e) {
+      qn2 = fmaf(lo_bf16(wq[e]), lo_bf16(wq[e]), fmaf(hi_bf16(wq[e]), hi_bf16(wq[e]), qn2));
+      kn2 = fmaf(lo_bf16(wk[e]), lo_bf16(wk[e]), fmaf(hi_bf16(wk[e]), hi_bf16(wk[e]), kn2));
+    }
+#pragma unroll
+    for (int m = 1; m < CPR; m <<= 1) {
+      dsum += __shfl_xor(dsum, m);
+      qn2 += __shfl_xor(qn2, m);
+      kn2 += __shfl_xor(kn2, m);
+    }
     if (c == 0) {
-      stats[r] = (tok < L) ? -lse[(size_t)bh * L + tok] : -INFINITY;
+      const float nl = (tok < L) ? -lse[(size_t)bh * L + tok] : -INFINITY;
+      stats[r] = nl;
       stats[TILE + r] = (tok < L) ? -dsum : 0.f;
+      s_c[r] = nl - slope2 * (float)tok;
+      atomicMax(&s_n2[0], __float_as_uint(qn2));
+      atomicMax(&s_n2[1], __float_as_uint(kn2));
     }
     const u32x4* src[3] = {&wq, &wk, &wd};
 #pragma unroll
@@ -144,6 +175,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
       }
   }
   __syncthreads();
+  // The tile's bound statistics (used by the gradient kernels to start their
+  // walks at the first tile that can hold a nonzero probability).  The norms
+  // carry a margin for the fp32 accumulation of the products they bound.
+  if (tid < 64) {
+    float cm = s_c[tid];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+    if (tid == 0) {
+      const f32x4 ts = {sqrtf(__uint_as_float(s_n2[0])) * (1.f + 1e-3f),
+                        sqrtf(__uint_as_float(s_n2[1])) * (1.f + 1e-3f), cm, 0.f};
+      *reinterpret_cast<f32x4*>(ops.tstat + ((size_t)bh * (Lp / TILE) + blockIdx.x) * 4) = ts;
+    }
+  }
   uint16_t* dstT[3] = {ops.qsT, ops.kT, ops.doutT};
   const size_t tb = (size_t)bh * D * Lp;
 #pragma unroll
@@ -249,11 +293,19 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
   constexpr int STAGE = 2 * RT + 2 * CT + 2 * TILE * 4;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
+  // Unbiased: each XCD (blockIdx % 8) gets whole heads, so their key
+  // workgroups share the streamed query tiles in its L2.  With a distance
+  // bias the work per head differs widely (a steep slope leaves most query
+  // tiles out), so the key blocks are dealt out across the XCDs instead: key
+  // block kt of every head, then kt + 1, ..., the heads rotated by kt so
+  // that a head does not stay on one XCD (blockIdx % 8) from round to round.
+  // Either way the longest query ranges (small kt) start first.
   const int per = (total_tiles + 7) / 8;
-  const int logical = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  const int logical = ALIBI ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (logical >= total_tiles) return;
-  const int bh = logical / nkt;
-  const int kt = logical % nkt;  // ascending: the longest query ranges first
+  const int nbh = total_tiles / nkt;
+  const int kt = ALIBI ? logical / nbh : logical % nkt;
+  const int bh = ALIBI ? (logical % nbh + kt) % nbh : logical / nkt;
   const int K0 = kt * BK;
   const int b = bh / H, h = bh % H;
   const int g = (Hphi == 1) ? 0 : h;
@@ -295,13 +347,37 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
   // Query tiles from the last one down: the workgroups that run at the same
   // time on an XCD (keys of the same heads) then stream the same query tiles
   // together, which keeps them in L2 (from its own diagonal upwards, each
-  // workgroup would start at a different tile).
-  if (first_tile <= last_tile) issue(last_tile, smem);
-  for (int t = last_tile; t >= first_tile; --t) {
-    uint8_t* st = smem + ((last_tile - t) & 1) * STAGE;
+  // workgroup would start at a different tile).  With a distance bias the
+  // walk starts at the last query tile that can hold a nonzero probability
+  // for these keys (every wave finds the same tile).
+  int t_hi = last_tile;
+  if constexpr (ALIBI) {
+    const float* ts = ops.tstat + (size_t)bh * (Lp / TILE) * 4;
+    const int j_hi = min(K0 + BK, L) - 1;
+    float kwn = 0.f;
+    for (int u = K0 / TILE; u <= j_hi / TILE; ++u) kwn = fmaxf(kwn, ts[4 * u + 1]);
+    const float jb = fmaxf(slope2 * (float)K0, slope2 * (float)j_hi);
+    t_hi = first_tile - 1;
+    for (int base = last_tile; base >= first_tile; base -= 64) {
+      const int t = base - lane;
+      bool alive = false;
+      if (t >= first_tile) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ts + 4 * t);
+        alive = fmaf(v[0], kwn, jb + v[2]) >= -ZGAP_B;
+      }
+      const uint64_t m = __ballot(alive);
+      if (m != 0) {
+        t_hi = base - (__ffsll((unsigned long long)m) - 1);
+        break;
+      }
+    }
+  }
+  if (first_tile <= t_hi) issue(t_hi, smem);
+  for (int t = t_hi; t >= first_tile; --t) {
+    uint8_t* st = smem + ((t_hi - t) & 1) * STAGE;
     wait_loads<0>();
     __builtin_amdgcn_s_barrier();
-    if (t - 1 >= first_tile) issue(t - 1, smem + ((last_tile - t + 1) & 1) * STAGE);
+    if (t - 1 >= first_tile) issue(t - 1, smem + ((t_hi - t + 1) & 1) * STAGE);
     const uint8_t* tq = st;
     const uint8_t* tdo = st + RT;
     const uint8_t* tqT = st + 2 * RT;
@@ -396,11 +472,16 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
   constexpr int STAGE = 2 * RT + CT;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
+  // Workgroup order as in the dK/dV pass: whole heads per XCD unbiased,
+  // query blocks dealt out across the XCDs with a distance bias (heads
+  // rotated from round to round); longest first.
   const int per = (total_tiles + 7) / 8;
-  const int logical = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  const int logical = ALIBI ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (logical >= total_tiles) return;
-  const int bh = logical / nqt;
-  const int qt = nqt - 1 - logical % nqt;  // longest first
+  const int nbh = total_tiles / nqt;
+  const int rnd = ALIBI ? logical / nbh : 0;
+  const int bh = ALIBI ? (logical % nbh + rnd) % nbh : logical / nqt;
+  const int qt = nqt - 1 - (ALIBI ? rnd : logical % nqt);
   const int q0 = qt * BM;
   const int b = bh / H, h = bh % H;
   const int g = (Hphi == 1) ? 0 : h;
@@ -441,12 +522,38 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
     for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
 
-  issue(0, smem);
-  for (int n = 0; n <= last_tile; ++n) {
-    uint8_t* st = smem + (n & 1) * STAGE;
+  // With a distance bias the walk starts at the first key tile that can
+  // hold a nonzero probability for these queries (every wave finds the same
+  // tile).
+  int n_lo = 0;
+  if constexpr (ALIBI) {
+    const float* ts = ops.tstat + (size_t)bh * (Lp / TILE) * 4;
+    float qwn = 0.f, cw = -INFINITY;
+    for (int u = q0 / TILE; u <= last_tile; ++u) {
+      qwn = fmaxf(qwn, ts[4 * u]);
+      cw = fmaxf(cw, ts[4 * u + 2]);
+    }
+    n_lo = last_tile + 1;
+    for (int base = 0; base <= last_tile; base += 64) {
+      const int n = base + lane;
+      bool alive = false;
+      if (n <= last_tile) {
+        const float jb = fmaxf(slope2 * (float)(n * TILE), slope2 * (float)(n * TILE + TILE - 1));
+        alive = fmaf(qwn, ts[4 * n + 1], jb + cw) >= -ZGAP_B;
+      }
+      const uint64_t m = __ballot(alive);
+      if (m != 0) {
+        n_lo = base + (__ffsll((unsigned long long)m) - 1);
+        break;
+      }
+    }
+  }
+  if (n_lo <= last_tile) issue(n_lo, smem);
+  for (int n = n_lo; n <= last_tile; ++n) {
+    uint8_t* st = smem + ((n - n_lo) & 1) * STAGE;
     wait_loads<0>();
     __builtin_amdgcn_s_barrier();
-    if (n + 1 <= last_tile) issue(n + 1, smem + ((n + 1) & 1) * STAGE);
+    if (n + 1 <= last_tile) issue(n + 1, smem + ((n - n_lo + 1) & 1) * STAGE);
     if (n > last_w) continue;
     const uint8_t* tk = st;
     const uint8_t* tv = st + RT;
@@ -592,7 +699,8 @@ hipError_t launch_bwd_d(const Geometry& g, const BwdArgs& a, hipStream_t stream)
   {
     dim3 grid(g.Lp / TILE, g.B * g.H);
     hipLaunchKernelGGL((bwd_prep_kernel<D>), grid, dim3(256), 0, stream, a.q, a.k, a.v, a.o, a.dout,
-                       a.theta, a.lse, a.ops, a.dtheta, g.L, g.Lp, g.H, g.Hphi, fl, g.scale * LOG2E);
+                       a.theta, a.lse, a.alibi, a.ops, a.dtheta, g.L, g.Lp, g.H, g.Hphi, fl,
+                       g.scale * LOG2E);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
