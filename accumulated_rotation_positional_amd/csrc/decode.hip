@@ -20,10 +20,9 @@
 //                   pos rotate the new key and value, use them from
 //                   registers and append them to the caches; one lane group
 //                   writes the angles out.  Each wave reads its 64 keys and
-//                   values in whole-row,
-//                   1 KB-per-instruction loads, scores them, takes its own
-//                   softmax maximum and sum and its P V; the four waves merge
-//                   in LDS into one partial (m, l, acc)
+//                   values in whole-row, 1 KB-per-instruction loads, scores
+//                   them, takes its own softmax maximum and sum and its P V;
+//                   the four waves merge in LDS into one partial (m, l, acc)
 //   decode_combine  one workgroup per (b, h): merges the partials, normalises,
 //                   un-rotates, writes o, and advances the angle state.
 // The attention pass is bound by HBM: it reads 2 * (t+1) * d bf16 per (b, h).
