@@ -284,6 +284,13 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][qb][r] = 0.f;
+  const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
+  float gq[QB];  // the forget-gate prefix of this lane's queries
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+    gq[qb] = FORGET ? gate2[(size_t)bh * Lp + min(qw + 32 * qb + ln, Lp - 1)] : 0.f;
+  // The accumulator input of Q K^T: -m, plus the query's gate prefix G_i
+  // with a gate bias (so only -G_j is left to add per logit).
   float mrun[QB], lsum[QB];
   f32x16 cneg[QB];
 #pragma unroll
@@ -291,13 +298,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     mrun[qb] = 0.f;
     lsum[qb] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) cneg[qb][r] = 0.f;
+    for (int r = 0; r < 16; ++r) cneg[qb][r] = gq[qb];
   }
-  const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
-  float gq[QB];  // the forget-gate prefix of this lane's queries
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-    gq[qb] = FORGET ? gate2[(size_t)bh * Lp + min(qw + 32 * qb + ln, Lp - 1)] : 0.f;
 
   // Biased walk: a bound on the logits of the tile in flight (tb), the
   // largest key norm of the wave's tiles (kglob), and per-wave "done" flags,
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
               const int koff = 32 * kb + 16 * h2 + 4 * (e >> 2) + (e & 3);
               float x = s[kb][qb][r];
               if (ALIBI) x += fmaf(slope2, (float)koff, fb);
-              if (FORGET) x += gq[qb] - (e < 4 ? ga[e] : gc[e - 4]);
+              if (FORGET) x -= (e < 4 ? ga[e] : gc[e - 4]);  // G_i rode in with the product
               if (diag && koff + base > 0) x = -INFINITY;
               s[kb][qb][r] = x;
             }
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
         }
         mrun[qb] += delta;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) cneg[qb][r] = -mrun[qb];
+        for (int r = 0; r < 16; ++r) cneg[qb][r] = FORGET ? gq[qb] - mrun[qb] : -mrun[qb];
       }
     }
     }
