@@ -333,6 +333,90 @@ def decode_leg(binding, torch, dev, steps: int = 50) -> dict:
     return out
 
 
+def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int = 20) -> dict:
+    """The forward step (scan, rotation pass, attention; fp32 I/O: scan and the
+    fp32 kernel) on every other workload, each at its full shape with seeded
+    inputs: step time, per-kernel event times on the stream, rates on the
+    algorithmic attention flops.  Secondary figures next to the headline
+    workload's."""
+    from accumulated_rotation_positional_amd import workloads as wl
+    out = {}
+    for name in wl.SPECS:
+        if name == skip:
+            continue
+        w = wl.make(name)
+
+        def to_dev(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+
+        q, k, v, phi = (to_dev(getattr(w, n)) for n in ("q", "k", "v", "phi"))
+        alibi = to_dev(w.alibi) if w.alibi is not None else None
+        flags = binding.flags_for(rotate_qk=True, rotate_v=w.rotate_v, alibi=w.use_alibi,
+                                  shared_phi=w.phi_heads == 1 and w.heads != 1)
+        desc = binding.desc_for(q, flags)
+        ws = binding.workspace(desc, dev)
+        state = binding.scan_state(desc, dev)
+        theta = torch.empty_like(phi)
+        o = torch.empty_like(q)
+        stream = torch.cuda.current_stream(dev)
+        fused = w.dtype == "f32"
+        n_ev = 2 if fused else 3
+
+        def step(evs=None):
+            if evs is not None:
+                evs[0].record(stream)
+            binding.angle_scan(phi, desc, theta=theta, state=state)
+            if evs is not None:
+                evs[1].record(stream)
+            if fused:
+                binding.attn_fwd(q, k, v, theta, desc, alibi=alibi, out=o, ws=ws)
+            else:
+                binding.rotate_qkv(q, k, v, theta, desc, ws=ws)
+                if evs is not None:
+                    evs[2].record(stream)
+                binding.attn_rotated(theta, alibi, o, desc, ws)
+            if evs is not None:
+                evs[n_ev].record(stream)
+
+        for _ in range(warmup):
+            step()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)]
+                  for _ in range(steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(steps):
+            step(events[i])
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_step = start.elapsed_time(end) / steps
+        seg = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(n_ev)] for e in events])
+        attn_ms = float(seg[:, -1].mean())
+        scan_ms = float(seg[:, 0].mean())
+        scan_gbs = 8.0 * w.batch * w.phi_heads * w.seqlen * (w.head_dim // 2) / (scan_ms * 1e-3) / 1e9
+        attn_tf = w.flops / (attn_ms * 1e-3) / 1e12
+        out[name] = {
+            "shape": [w.batch, w.heads, w.seqlen, w.head_dim], "dtype": w.dtype,
+            "rotate_v": w.rotate_v, "alibi": w.use_alibi, "ms_per_step": round(ms_step, 4),
+            "kernels_ms": {"angle_scan": round(scan_ms, 5),
+                           "rotate_qkv": round(float(seg[:, 1].mean()), 5) if n_ev == 3 else 0.0,
+                           "attn_fwd": round(attn_ms, 5)},
+            "tflops_step": round(w.flops / (ms_step * 1e-3) / 1e12, 2),
+            "tokens_per_s": round(w.batch * w.seqlen / (ms_step * 1e-3), 1),
+            "attn_tflops": round(attn_tf, 2),
+            "attn_frac_of_bf16_peak": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4) if not fused else None,
+            "scan_gbs": round(scan_gbs, 1),
+            "note": ("the distance-bias walk skips key tiles whose probabilities are all exactly "
+                     "zero, so the attention rate exceeds the matrix-core work done")
+            if w.use_alibi else None,
+        }
+        del q, k, v, phi, alibi, ws, state, theta, o
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -458,6 +542,7 @@ def main():
         result["backward"] = backward_leg(binding, torch, dev, w, q, k, v, phi, alibi)
         result["decode"] = decode_leg(binding, torch, dev)
         result["forget_gate"] = forget_leg(binding, torch, dev, w, q, k, v, phi)
+        result["workloads"] = workloads_leg(binding, torch, dev, w.name)
     if not args.no_cpu_baseline:
         import oracle
         of = (oracle.ROTATE_QK | (oracle.ROTATE_V if w.rotate_v else 0) |
