@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--workload", default="extrap_16k")
     p.add_argument("--fused", action="store_true", help="rotate k/v inside the attention kernel")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="skip the forward figures of the other workloads (profiling runs use "
+                        "this so that each kernel's counters come from the headline workload)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target duration of the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -542,7 +545,8 @@ def main():
         result["backward"] = backward_leg(binding, torch, dev, w, q, k, v, phi, alibi)
         result["decode"] = decode_leg(binding, torch, dev)
         result["forget_gate"] = forget_leg(binding, torch, dev, w, q, k, v, phi)
-        result["workloads"] = workloads_leg(binding, torch, dev, w.name)
+        if not args.no_workloads:
+            result["workloads"] = workloads_leg(binding, torch, dev, w.name)
     if not args.no_cpu_baseline:
         import oracle
         of = (oracle.ROTATE_QK | (oracle.ROTATE_V if w.rotate_v else 0) |
