@@ -96,7 +96,7 @@ def _lib() -> ctypes.CDLL:
                                               ctypes.c_int64, ctypes.c_int, dp]
         lib.oracle_attention_rows.restype = ctypes.c_int
         lib.oracle_backward.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_int,
-                                        dp, dp, dp, dp, dp]
+                                        dp, dp, dp, dp, dp, dp]
         lib.oracle_backward.restype = ctypes.c_int
         u64p = ctypes.POINTER(ctypes.c_uint64)
         lib.oracle_philox4x64_10.argtypes = [u64p, u64p, u64p]
@@ -254,7 +254,8 @@ class Problem:
     def backward(self, dout, nthreads: int = 0) -> dict:
         """Gradients for the upstream gradient dout ([B, H, L, d], the dtype of q):
         dict of fp64 arrays dq, dk, dv [B, H, L, d], dtheta [B, H, L, d/2]
-        (per head) and dphi (the shape of phi).  O(L^2 d) per head."""
+        (per head), dphi (the shape of phi) and, with the forget gate, dlogf
+        [B, H, L].  O(L^2 d) per head."""
         dout = np.ascontiguousarray(dout)
         if dout.shape != self.q.shape or dout.dtype != self.q.dtype:
             raise ValueError("dout must match q in shape and dtype")
@@ -262,9 +263,13 @@ class Problem:
         out = {n: np.empty(self.shape, dtype=np.float64) for n in ("dq", "dk", "dv")}
         out["dtheta"] = np.empty((B, H, L, d // 2), dtype=np.float64)
         out["dphi"] = np.empty(self.phi.shape, dtype=np.float64)
+        gated = (self.flags & FORGET) != 0
+        if gated:
+            out["dlogf"] = np.empty((B, H, L), dtype=np.float64)
         rc = _lib().oracle_backward(ctypes.byref(self.c), dout.ctypes.data, int(nthreads),
                                     _dptr(out["dq"]), _dptr(out["dk"]), _dptr(out["dv"]),
-                                    _dptr(out["dtheta"]), _dptr(out["dphi"]))
+                                    _dptr(out["dtheta"]), _dptr(out["dphi"]),
+                                    _dptr(out["dlogf"]) if gated else None)
         if rc:
             raise RuntimeError(f"oracle_backward failed: {rc}")
         return out

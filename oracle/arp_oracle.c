@@ -424,7 +424,7 @@ static double pair_cross(const double* x, const double* a) { return -x[0] * a[1]
 
 /* One (b, h): all gradients of the head, O(L^2 d). dtheta_h is [L, P]. */
 static int backward_head(const oracle_problem* p, const void* dout, int64_t b, int64_t h,
-                         double* dq, double* dk, double* dv, double* dtheta_h) {
+                         double* dq, double* dk, double* dv, double* dtheta_h, double* dlogf_h) {
   const int64_t d = p->head_dim, P = d / 2, L = p->seqlen;
   const int64_t base = ((b * p->heads + h) * L) * d;
   const int qk = (p->flags & ORACLE_ROTATE_QK) != 0, tv = (p->flags & ORACLE_ROTATE_V) != 0;
@@ -461,8 +461,18 @@ static int backward_head(const oracle_problem* p, const void* dout, int64_t b, i
       double dot = 0.0;
       for (int64_t c = 0; c < d; ++c) dot += qi[c] * kj[c];
       alpha[j] = p->scale * dot - slope * (double)(i - j);
-      if (alpha[j] > m) m = alpha[j];
     }
+    if (p->flags & ORACLE_FORGET) {
+      /* sum_{s=j+1}^{i} log f_s, from j = i (empty) down to 0 */
+      const float* lf = p->logf + (b * p->heads + h) * L;
+      double gate = 0.0;
+      for (int64_t j = i; j >= 0; --j) {
+        alpha[j] += gate;
+        gate += (double)lf[j];
+      }
+    }
+    for (int64_t j = 0; j <= i; ++j)
+      if (alpha[j] > m) m = alpha[j];
     double l = 0.0;
     for (int64_t j = 0; j <= i; ++j) {
       alpha[j] = exp(alpha[j] - m);
@@ -478,12 +488,19 @@ static int backward_head(const oracle_problem* p, const void* dout, int64_t b, i
     const double* gi = dorot + i * d;
     double Di = 0.0;
     for (int64_t c = 0; c < d; ++c) Di += gi[c] * oi[c];
+    /* gate gradient: the logit s_ij holds log f_s for j < s <= i, so
+       dlogf_s collects sum_{j < s} dS_ij from every row i >= s */
+    double pre = 0.0;
     for (int64_t j = 0; j <= i; ++j) {
       const double* vj = hs.vrot + j * d;
       const double* kj = hs.krot + j * d;
       double dp = 0.0;
       for (int64_t c = 0; c < d; ++c) dp += gi[c] * vj[c];
       const double ds = alpha[j] * (dp - Di);
+      if (dlogf_h && j + 1 <= i) {
+        pre += ds;                 /* sum_{j' <= j} dS_ij' = sum_{j' < s} for s = j + 1 */
+        dlogf_h[j + 1] += pre;
+      }
       for (int64_t c = 0; c < d; ++c) {
         dqt[i * d + c] += p->scale * ds * kj[c];
         dkt[j * d + c] += p->scale * ds * qi[c];
@@ -532,12 +549,14 @@ done:
 }
 
 int oracle_backward(const oracle_problem* p, const void* dout, int nthreads, double* dq,
-                    double* dk, double* dv, double* dtheta, double* dphi) {
+                    double* dk, double* dv, double* dtheta, double* dphi, double* dlogf) {
   int rc = check_problem(p);
   if (rc) return rc;
   if (!dout || !dq || !dk || !dv || !dtheta || !dphi) return ORACLE_ERR_ARG;
-  if (p->flags & ORACLE_FORGET) return ORACLE_ERR_ARG; /* gradients of the gate are not derived here */
+  if ((p->flags & ORACLE_FORGET) && !dlogf) return ORACLE_ERR_ARG;
   const int64_t B = p->batch, H = p->heads, L = p->seqlen, P = p->head_dim / 2;
+  const int gated = (p->flags & ORACLE_FORGET) != 0;
+  if (gated) memset(dlogf, 0, sizeof(double) * (size_t)(B * H * L));
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -546,7 +565,8 @@ int oracle_backward(const oracle_problem* p, const void* dout, int nthreads, dou
   int err = ORACLE_OK;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
   for (int64_t bh = 0; bh < B * H; ++bh)
-    err |= backward_head(p, dout, bh / H, bh % H, dq, dk, dv, dtheta + bh * L * P);
+    err |= backward_head(p, dout, bh / H, bh % H, dq, dk, dv, dtheta + bh * L * P,
+                         gated ? dlogf + bh * L : NULL);
   if (err) return err;
   /* dphi_s = sum over heads sharing the stream, and over t >= s (t > s exclusive). */
   const int excl = (p->flags & ORACLE_SCAN_EXCLUSIVE) != 0;

@@ -94,10 +94,12 @@ int oracle_attention_rows(const oracle_problem* p, const int64_t* rows, int64_t 
  *   dq, dk, dv  [batch, heads, seqlen, head_dim]
  *   dtheta      [batch, heads, seqlen, head_dim/2]   dL/dTheta per head
  *   dphi        [batch, phi_heads, seqlen, head_dim/2]
- * O(seqlen^2 head_dim) per head; OpenMP over heads.  ORACLE_ERR_ARG with
- * ORACLE_FORGET (the gate's own gradient is not part of this oracle). */
+ *   dlogf       [batch, heads, seqlen]  dL/d(log f_s), required with
+ *               ORACLE_FORGET (else may be NULL): the logit s_ij holds
+ *               log f_s for j < s <= i, so dlogf_s = sum_{i >= s} sum_{j < s} dS_ij
+ * O(seqlen^2 head_dim) per head; OpenMP over heads. */
 int oracle_backward(const oracle_problem* p, const void* dout, int nthreads, double* dq,
-                    double* dk, double* dv, double* dtheta, double* dphi);
+                    double* dk, double* dv, double* dtheta, double* dphi, double* dlogf);
 
 #ifdef __cplusplus
 }

@@ -131,3 +131,59 @@ def test_textbook_attention_gradients_match_autodiff():
     (o * torch.tensor(g, dtype=torch.float64)).sum().backward()
     for n, t in (("dq", Q), ("dk", K), ("dv", V)):
         np.testing.assert_allclose(got[n], t.grad.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("flags", [oracle.ROTATE_QK, oracle.ROTATE_QK | oracle.ROTATE_V | oracle.ALIBI],
+                         ids=["qk", "qk+v+alibi"])
+def test_gate_gradient_matches_central_differences(flags):
+    """With the forget gate the backward also returns dL/d(log f_s); it and the
+    other gradients against Richardson central differences of the forward
+    oracle (log f on the 2^-8 grid, negative, so the perturbed gates stay
+    valid log-probabilities)."""
+    flags |= oracle.FORGET
+    q, k, v, phi, alibi, g = _problem(13, 1, 2, 6, 4, flags)
+    rng = np.random.default_rng(14)
+    logf = (-np.round(rng.uniform(0.05, 1.5, size=(1, 2, 6)) * 256) / 256).astype(np.float32)
+
+    def loss(q_, k_, v_, phi_, lf_):
+        o = oracle.Problem(q_, k_, v_, phi_, flags, alibi=alibi, logf=lf_).output(nthreads=1)
+        return float((o * g.astype(np.float64)).sum())
+
+    got = oracle.Problem(q, k, v, phi, flags, alibi=alibi, logf=logf).backward(g, nthreads=1)
+    want = {
+        "dlogf": _numeric(lambda x: loss(q, k, v, phi, x), logf),
+        "dq": _numeric(lambda x: loss(x, k, v, phi, logf), q),
+        "dk": _numeric(lambda x: loss(q, x, v, phi, logf), k),
+        "dphi": _numeric(lambda x: loss(q, k, v, x, logf), phi),
+    }
+    for n, w in want.items():
+        err = np.abs(got[n] - w).max()
+        assert err <= 2e-8 * max(1.0, np.abs(w).max()), f"gate {n}: max err {err:.3e}"
+    # log f_0 enters no logit (the route j -> i holds steps j+1..i)
+    assert np.all(got["dlogf"][:, :, 0] == 0.0)
+
+
+def test_gate_gradient_equals_prefix_of_column_sums():
+    """Because every causal row of dS sums to zero, dL/d(log f_s) equals the
+    sum over t < s of the column sums sum_i dS_it.  Checked on the oracle's
+    own dS, rebuilt here from its public row scores (an identity of the
+    softmax gradient, independent of how the oracle accumulates dlogf)."""
+    flags = oracle.ROTATE_QK | oracle.FORGET
+    q, k, v, phi, alibi, g = _problem(15, 1, 1, 7, 4, flags)
+    logf = np.full((1, 1, 7), -0.25, dtype=np.float32)
+    prob = oracle.Problem(q, k, v, phi, flags, logf=logf)
+    got = prob.backward(g, nthreads=1)["dlogf"][0, 0]
+    # dS_ij = alpha_ij (<dO~_i, v~_j> - D_i); with no value transport dO~ = dO and
+    # v~ = v, and o_i = sum_j alpha_ij v_j
+    L = 7
+    dS = np.zeros((L, L))
+    for i in range(L):
+        s = np.array(prob.scores_row(0, 0, i))
+        a = np.exp(s - s.max()); a /= a.sum()
+        vv = v[0, 0, : i + 1].astype(np.float64)
+        gi = g[0, 0, i].astype(np.float64)
+        o = a @ vv
+        dS[i, : i + 1] = a * (vv @ gi - o @ gi)
+    colsum = dS.sum(axis=0)
+    want = np.concatenate([[0.0], np.cumsum(colsum)[:-1]])
+    assert np.abs(got - want).max() <= 1e-12 * max(1.0, np.abs(want).max())

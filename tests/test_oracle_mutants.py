@@ -46,6 +46,9 @@ BACKWARD_MUTANTS = [
     ("query gradient rotated forward", "rotate_vec(dqt + t * d, th, P, 1, oq);", "rotate_vec(dqt + t * d, th, P, 0, oq);"),
     ("upstream gradient rotated backward", "if (tv) rotate_vec(raw, hs.theta + t * P, P, 0, dorot + t * d);",
      "if (tv) rotate_vec(raw, hs.theta + t * P, P, 1, dorot + t * d);"),
+    ("gate gradient one step early", "dlogf_h[j + 1] += pre;", "dlogf_h[j] += pre;"),
+    ("gate gradient without the running sum", "pre += ds;", "pre = ds;"),
+    ("gate left out of the recomputed logits", "alpha[j] += gate;", "(void)alpha;"),
 ]
 
 
