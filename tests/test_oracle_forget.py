@@ -70,8 +70,21 @@ def test_brute_force_gate_products(flags):
     np.testing.assert_allclose(got[0, 0], want, rtol=0, atol=2e-6)
 
 
-def test_backward_refuses_forget_gate():
-    q, k, v, phi = _inputs(5, L=4)
-    logf = np.zeros(q.shape[:3], dtype=np.float32)
-    with pytest.raises(RuntimeError):
-        oracle.Problem(q, k, v, phi, QK | FG, logf=logf).backward(np.zeros_like(q))
+@pytest.mark.parametrize("kind", ["open", "constant"])
+def test_gated_backward_reduces_to_ungated(kind):
+    """Open gates leave every gradient of the ungated problem unchanged;
+    constant gates -m give the gradients of the distance bias with slope m."""
+    q, k, v, phi = _inputs(5, L=12)
+    B, H, L, _ = q.shape
+    dout = np.random.default_rng(6).standard_normal(q.shape).astype(np.float32)
+    slopes = np.array([0.5, 0.0625], dtype=np.float32)
+    if kind == "open":
+        logf = np.zeros((B, H, L), dtype=np.float32)
+        ref = oracle.Problem(q, k, v, phi, QK | V).backward(dout)
+    else:
+        logf = np.broadcast_to(-slopes[None, :, None], (B, H, L)).astype(np.float32)
+        ref = oracle.Problem(q, k, v, phi, QK | V | AL, alibi=slopes).backward(dout)
+    got = oracle.Problem(q, k, v, phi, QK | V | FG, logf=logf).backward(dout)
+    for n in ("dq", "dk", "dv", "dphi"):
+        np.testing.assert_allclose(got[n], ref[n], rtol=0, atol=1e-11, err_msg=n)
+    assert got["dlogf"].shape == (B, H, L)
