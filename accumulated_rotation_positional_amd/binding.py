@@ -39,7 +39,7 @@ EXPORTS = ("arp_abi_version", "arp_status_string", "arp_check", "arp_scan_state_
            "arp_forward", "arp_rotate", "arp_forward_train", "arp_backward_workspace_bytes",
            "arp_backward", "arp_decode_workspace_bytes", "arp_decode_prefill", "arp_decode_step",
            "arp_forward_ex", "arp_angle_scan_random", "arp_angle_scan_tokens",
-           "arp_angle_scan_const", "arp_random_phi")
+           "arp_angle_scan_const", "arp_random_phi", "arp_backward_ex")
 
 
 class ArpError(RuntimeError):
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
                 "arp_forward_train": ([D, P, P, P, P, P, P, P, P, P, S, P, S, P], ctypes.c_int),
                 "arp_backward_workspace_bytes": ([D], S),
                 "arp_backward": ([D] + [P] * 14 + [S, P], ctypes.c_int),
+                "arp_backward_ex": ([D] + [P] * 16 + [S, P], ctypes.c_int),
                 "arp_decode_workspace_bytes": ([D], S),
                 "arp_decode_prefill": ([D, ctypes.c_int32] + [P] * 7 + [P], ctypes.c_int),
                 "arp_decode_step": ([D, ctypes.c_int32] + [P] * 11 + [S, P], ctypes.c_int),
@@ -373,6 +374,24 @@ def backward(desc: Desc, q, k, v, phi, theta, o, lse, dout, alibi=None, ws=None)
         _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtheta), _ptr(dphi),
         _ptr(ws), ws.numel(), _stream(q.device)))
     return dq, dk, dv, dphi, dtheta
+
+
+def backward_ex(desc: Desc, q, k, v, phi, theta, o, lse, dout, alibi=None, logf=None, ws=None):
+    """arp_backward_ex: backward() plus, with the forget gates (desc has
+    FORGET_GATE; logf [B, H, L] as given to forward_ex), dlogf = dL/d(log f)
+    [B, H, L].  Returns (dq, dk, dv, dphi, dtheta, dlogf or None)."""
+    _require_gpu(q, k, v, phi, theta, o, lse, dout, alibi, logf, ws)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    B, H, L, d = q.shape
+    dtheta = torch.empty(B, H, L, d // 2, dtype=torch.float32, device=q.device)
+    dphi = torch.empty_like(phi)
+    dlogf = torch.empty(B, H, L, dtype=torch.float32, device=q.device) if logf is not None else None
+    ws = backward_workspace(desc, q.device) if ws is None else ws
+    _check("arp_backward_ex", lib().arp_backward_ex(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(alibi), _ptr(logf),
+        _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtheta), _ptr(dphi),
+        _ptr(dlogf), _ptr(ws), ws.numel(), _stream(q.device)))
+    return dq, dk, dv, dphi, dtheta, dlogf
 
 
 class DecodeCache:

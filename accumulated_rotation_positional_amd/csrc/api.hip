@@ -99,7 +99,17 @@ BwdWorkspaceLayout bwd_workspace_layout(const Geometry& g) {
   lay.tstat_off = lay.stats_off + align_up((size_t)g.B * g.H * g.Lp * 2 * sizeof(float));
   lay.totals_off = lay.tstat_off + align_up((size_t)g.B * g.H * (g.Lp / KEY_TILE) * 4 * sizeof(float));
   const size_t nch = ((size_t)g.L + 255) / 256;
-  lay.total = lay.totals_off + align_up((size_t)g.B * g.Hphi * nch * g.P * sizeof(float));
+  size_t off = lay.totals_off + align_up((size_t)g.B * g.Hphi * nch * g.P * sizeof(float));
+  if (g.flags & ARP_FORGET_GATE) {
+    const size_t per_token = align_up((size_t)g.B * g.H * g.Lp * sizeof(float));
+    lay.gate_off = off;
+    lay.gate_tot_off = off + per_token;
+    off = lay.gate_tot_off + align_up((size_t)g.B * g.H * gate_chunks(g) * sizeof(double));
+    lay.colsum_off = off;
+    lay.rowsum_off = off + per_token;
+    off += 2 * per_token;
+  }
+  lay.total = off;
   return lay;
 }
 
@@ -376,23 +386,25 @@ size_t arp_backward_workspace_bytes(const arp_desc* desc) {
   return bwd_workspace_layout(g).total;
 }
 
-arp_status arp_backward(const arp_desc* desc, const void* q, const void* k, const void* v,
-                        const float* theta, const float* alibi, const void* o, const float* lse,
-                        const void* dout, void* dq, void* dk, void* dv, float* dtheta,
-                        float* dphi, void* workspace, size_t workspace_bytes, void* stream) {
+arp_status arp_backward_ex(const arp_desc* desc, const void* q, const void* k, const void* v,
+                           const float* theta, const float* alibi, const float* logf, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* dtheta, float* dphi, float* dlogf, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
-  if (gated(g)) return ARP_ERR_UNSUPPORTED;
   if (g.dtype != ARP_DTYPE_BF16) return ARP_ERR_UNSUPPORTED;
   const void* in[] = {q, k, v, o, lse, dout, dq, dk, dv, dtheta, dphi};
   for (const void* p : in)
     if (p == nullptr) return ARP_ERR_INVALID_ARG;
-  if ((rotates(g) && theta == nullptr) || ((g.flags & ARP_ALIBI) && alibi == nullptr))
+  if ((rotates(g) && theta == nullptr) || ((g.flags & ARP_ALIBI) && alibi == nullptr) ||
+      (gated(g) && (logf == nullptr || dlogf == nullptr)))
     return ARP_ERR_INVALID_ARG;
   for (const void* p : in)
     if (!aligned16(p)) return ARP_ERR_ALIGNMENT;
   if ((theta && !aligned16(theta)) || (alibi && !aligned16(alibi))) return ARP_ERR_ALIGNMENT;
+  if (gated(g) && (!aligned16(logf) || !aligned16(dlogf))) return ARP_ERR_ALIGNMENT;
   const BwdWorkspaceLayout lay = bwd_workspace_layout(g);
   if ((st = check_buffer(workspace, workspace_bytes, lay.total)) != ARP_OK) return st;
   char* ws = static_cast<char*>(workspace);
@@ -414,8 +426,31 @@ arp_status arp_backward(const arp_desc* desc, const void* q, const void* k, cons
   a.totals = reinterpret_cast<float*>(ws + lay.totals_off);
   a.ops = BwdOperands{blk(0), blk(1), blk(2), blk(3), blk(4), blk(5), blk(6),
                       reinterpret_cast<float*>(ws + lay.stats_off),
-                      reinterpret_cast<float*>(ws + lay.tstat_off)};
-  return hip_status(launch_backward_bf16(g, a, (hipStream_t)stream));
+                      reinterpret_cast<float*>(ws + lay.tstat_off), nullptr, nullptr, nullptr};
+  hipStream_t s = (hipStream_t)stream;
+  if (gated(g)) {
+    float* gate2 = reinterpret_cast<float*>(ws + lay.gate_off);
+    a.logf = logf;
+    a.dlogf = dlogf;
+    a.gate_tot = reinterpret_cast<double*>(ws + lay.gate_tot_off);
+    a.ops.gate2 = gate2;
+    a.ops.colsum = reinterpret_cast<float*>(ws + lay.colsum_off);
+    a.ops.rowsum = reinterpret_cast<float*>(ws + lay.rowsum_off);
+    if ((st = hip_status(launch_gate_scan(g, logf, gate2, a.gate_tot, s))) != ARP_OK) return st;
+  }
+  return hip_status(launch_backward_bf16(g, a, s));
+}
+
+arp_status arp_backward(const arp_desc* desc, const void* q, const void* k, const void* v,
+                        const float* theta, const float* alibi, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, float* dtheta,
+                        float* dphi, void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (gated(g)) return ARP_ERR_INVALID_ARG;  // the gates' input and gradient: arp_backward_ex
+  return arp_backward_ex(desc, q, k, v, theta, alibi, nullptr, o, lse, dout, dq, dk, dv, dtheta,
+                         dphi, nullptr, workspace, workspace_bytes, stream);
 }
 
 size_t arp_decode_workspace_bytes(const arp_desc* desc) {

@@ -101,6 +101,12 @@ struct BwdOperands {
   uint16_t* doutT;
   float* stats;
   float* tstat;  // per 64-token tile: max |q~ scale log2 e|, max |k~|, max_i (-lse_i - slope2 i), 0
+  // forget gates only (else null), fp32 [B*H, Lp]: the gate prefix G (log2 e
+  // times the prefix sums of log f, as in the forward), and the sums of dS
+  // over each key's column and over each query's row
+  const float* gate2;
+  float* colsum;
+  float* rowsum;
 };
 struct BwdArgs {
   const uint16_t *q, *k, *v, *o, *dout;  // caller tensors [B, H, L, D]
@@ -109,11 +115,16 @@ struct BwdArgs {
   float* dtheta;                         // caller [B, H, L, P]
   float* dphi;                           // caller [B, Hphi, L, P]
   float* totals;                         // workspace [B*Hphi, ceil(L/256), P]
+  const float* logf;                     // caller [B, H, L] log forget gates (gated only)
+  float* dlogf;                          // caller [B, H, L] out: dL/d(log f) (gated only)
+  double* gate_tot;                      // workspace [B*H, gate_chunks] (gated only)
   BwdOperands ops;
 };
 struct BwdWorkspaceLayout {
   size_t operand_bytes;  // one bf16 [B*H, Lp, D] block
-  size_t stats_off, tstat_off, totals_off, total;
+  size_t stats_off, tstat_off, totals_off;
+  size_t gate_off, gate_tot_off, colsum_off, rowsum_off;  // gated only
+  size_t total;
 };
 BwdWorkspaceLayout bwd_workspace_layout(const Geometry& g);
 hipError_t launch_backward_bf16(const Geometry& g, const BwdArgs& a, hipStream_t stream);

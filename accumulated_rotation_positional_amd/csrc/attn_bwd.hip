@@ -34,6 +34,12 @@
 //  <dx~, J x~> terms to dTheta (each (t, p) owned by one lane).
 //  4. reverse scan of dTheta into dphi: chunk totals, then the in-chunk
 //     suffix sums plus the totals of the later chunks.
+// With forget gates the logits carry G_i - G_j (G = log2 e times the prefix
+// sums of log f, from the forward's gate pass): G_i rides in the -lse
+// statistic, -G_j is added per key.  The dK/dV pass sums each key's column
+// of dS and the dQ pass each query's row, and
+//  5. dlogf_s = sum_{t < s} (column sum_t - row sum_t), the sum of dS over
+//     the rectangle j < s <= i (the rows of dS sum to zero).
 #include <type_traits>
 
 #include "arp_device.hpp"
@@ -159,7 +165,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     }
     if (c == 0) {
       const float nl = (tok < L) ? -lse[(size_t)bh * L + tok] : -INFINITY;
-      stats[r] = nl;
+      // the gate prefix G_i joins -lse_i (the walk bounds below leave it
+      // out: G_i - G_j <= 0 for j <= i, so they stay upper bounds)
+      stats[r] = (ops.gate2 != nullptr && tok < L) ? nl + ops.gate2[(size_t)bh * Lp + tok] : nl;
       stats[TILE + r] = (tok < L) ? -dsum : 0.f;
       s_c[r] = nl - slope2 * (float)tok;
       atomicMax(&s_n2[0], __float_as_uint(qn2));
@@ -280,7 +288,7 @@ __device__ __forceinline__ void grad_rows(const f32x16 (&acc)[DB], float mul, co
 // ---------------------------------------------------------------------------
 // 2. dK, dV (key-stationary)
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool ALIBI>
+template <int D, int NW, bool ALIBI, bool GATE>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
     BwdOperands ops, const float* __restrict__ theta, const float* __restrict__ alibi,
     uint16_t* __restrict__ dk,
@@ -343,6 +351,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dkt[db][r] = dvt[db][r] = 0.f;
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
+  // the key's gate prefix G_j, subtracted from every logit of its column
+  const float gj = GATE ? ops.gate2[(size_t)bh * Lp + min(j, Lp - 1)] : 0.f;
+  float csum = 0.f;  // sum of dS over this lane's part of the key's column
 
   // Query tiles from the last one down: the workgroups that run at the same
   // time on an XCD (keys of the same heads) then stream the same query tiles
@@ -404,6 +415,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
           cd[8 * h2 + 4 + e] = d1[e];
         }
       }
+      if constexpr (GATE) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cl[r] -= gj;
+      }
       f32x16 s = cl, dp = cd;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -428,7 +443,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
 #pragma unroll
           for (int u = 0; u < 2; ++u) x[u] = __builtin_amdgcn_exp2f(s[8 * h2 + 2 * e + u]);
           wp[e] = pack_bf16x2(x[0], x[1]);
-          wd[e] = pack_bf16x2(x[0] * dp[8 * h2 + 2 * e], x[1] * dp[8 * h2 + 2 * e + 1]);
+          const float ds0 = x[0] * dp[8 * h2 + 2 * e], ds1 = x[1] * dp[8 * h2 + 2 * e + 1];
+          wd[e] = pack_bf16x2(ds0, ds1);
+          if (GATE) csum += ds0 + ds1;
         }
         u32x4 a = {wp[0], wp[1], wp[2], wp[3]}, c = {wd[0], wd[1], wd[2], wd[3]};
         pop[h2] = __builtin_bit_cast(bf16x8, a);
@@ -445,6 +462,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
     }
   }
 
+  if constexpr (GATE) {  // lanes ln and ln + 32 hold the two halves of the column
+    csum += __shfl_xor(csum, 32);
+    if (hf == 0 && j < L) ops.colsum[(size_t)bh * Lp + j] = csum;
+  }
   if (j >= L) return;
   const size_t row = ((size_t)bh * L + j) * D;
   const uint16_t* oprow = ops.k + rm + (size_t)j * D;
@@ -460,7 +481,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // 3. dQ (query-stationary)
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool ALIBI>
+template <int D, int NW, bool ALIBI, bool GATE>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
     BwdOperands ops, const float* __restrict__ theta, const float* __restrict__ alibi,
     uint16_t* __restrict__ dq, float* __restrict__ dtheta, int L, int Lp, int H, int Hphi, int nqt,
@@ -469,7 +490,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
   constexpr int KS = D / 16, DB = D / 32, KB = 2, KS2 = 4;
   constexpr int ROWB = D * 2, RT = TILE * ROWB;
   constexpr int COLB = TILE * 2, CT = D * COLB;
-  constexpr int STAGE = 2 * RT + CT;
+  constexpr int STAGE = 2 * RT + CT + (GATE ? TILE * 4 : 0);  // + the tile's key gates
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   // Workgroup order as in the dK/dV pass: whole heads per XCD unbiased,
@@ -498,6 +519,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
     load_rows_tile<D, NW>(ops.k + rm, t * TILE, st, wave, lane);
     load_rows_tile<D, NW>(ops.v + rm, t * TILE, st + RT, wave, lane);
     load_cols_tile<D, NW>(ops.kT + tb, Lp, t * TILE, st + 2 * RT, wave, lane);
+    if (GATE && wave == 0 && lane < TILE / 4)
+      __builtin_amdgcn_global_load_lds(
+          (global_void_ptr)(ops.gate2 + (size_t)bh * Lp + (size_t)t * TILE + 4 * lane),
+          (lds_void_ptr)(st + 2 * RT + CT), 16, 0, 0);
   };
 
   bf16x8 qop[KS], doop[KS];
@@ -521,6 +546,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
+  float rsum = 0.f;  // sum of dS over this lane's part of the query's row
 
   // With a distance bias the walk starts at the first key tile that can
   // hold a nonzero probability for these queries (every wave finds the same
@@ -563,6 +589,19 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       f32x16 s = cl, dp = cd;
+      if constexpr (GATE) {  // -G_j of the key of each element
+        const float* gp = reinterpret_cast<const float*>(st + 2 * RT + CT) + 32 * kb + 8 * hf;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const f32x4 ga = *reinterpret_cast<const f32x4*>(gp + 16 * h2);
+          const f32x4 gb = *reinterpret_cast<const f32x4*>(gp + 16 * h2 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[8 * h2 + e] -= ga[e];
+            s[8 * h2 + 4 + e] -= gb[e];
+          }
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = mfma32(lds_op<ROWB>(tk, 32 * kb + ln, 2 * ks + hf), qop[ks], s);
@@ -587,6 +626,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
             const int r = 8 * h2 + 2 * e + u;
             x[u] = __builtin_amdgcn_exp2f(s[r]) * dp[r];
           }
+          if (GATE) rsum += x[0] + x[1];
           wd[e] = pack_bf16x2(x[0], x[1]);
         }
         u32x4 c = {wd[0], wd[1], wd[2], wd[3]};
@@ -600,6 +640,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
         dqt[db] = mfma32(lds_op<COLB>(tkT, 32 * db + ln, 2 * ks2 + hf), dsop[ks2], dqt[db]);
   }
 
+  if constexpr (GATE) {  // lanes ln and ln + 32 hold the two halves of the row
+    rsum += __shfl_xor(rsum, 32);
+    if (hf == 0 && i < L) ops.rowsum[(size_t)bh * Lp + i] = rsum;
+  }
   if (i >= L) return;
   const size_t row = ((size_t)bh * L + i) * D;
   const float* th = theta + ((size_t)(b * Hphi + g) * L + i) * (D / 2);
@@ -692,6 +736,125 @@ __global__ __launch_bounds__(256) void rscan_apply_kernel(const float* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// 5. gate gradient: dlogf[bh, s] = sum_{t < s} (colsum_t - rowsum_t) (fp64
+// sums), 0 where log f_s > 0 (the forward takes such gates as 1).  Chunks of
+// 1024 tokens, four consecutive tokens per thread: the first kernel sums each
+// chunk, the second adds the sums of the earlier chunks to an in-chunk
+// exclusive scan.
+// ---------------------------------------------------------------------------
+constexpr int GG_THREADS = 256, GG_CHUNK = 4 * GG_THREADS;
+
+// The thread's four differences colsum - rowsum (0 past L).
+__device__ __forceinline__ void gate_diffs(const float* __restrict__ colsum,
+                                           const float* __restrict__ rowsum, int bh, int t0, int L,
+                                           int Lp, double (&x)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = 0.0;
+  if (t0 >= Lp) return;  // Lp is a multiple of 256: all four tokens are below it
+  const float4 cs = *reinterpret_cast<const float4*>(colsum + (size_t)bh * Lp + t0);
+  const float4 rs = *reinterpret_cast<const float4*>(rowsum + (size_t)bh * Lp + t0);
+  const float cv[4] = {cs.x, cs.y, cs.z, cs.w}, rv[4] = {rs.x, rs.y, rs.z, rs.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (t0 + e < L) x[e] = (double)cv[e] - (double)rv[e];
+}
+
+__device__ __forceinline__ double block_sum_gg(double x, double* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int u = 0; u < GG_THREADS / 64; ++u) t += red[u];
+  return t;
+}
+
+__global__ __launch_bounds__(GG_THREADS) void bwd_gate_tot_kernel(
+    const float* __restrict__ colsum, const float* __restrict__ rowsum, double* __restrict__ tot,
+    int L, int Lp, int nch) {
+  __shared__ double red[GG_THREADS / 64];
+  const int c = blockIdx.x, bh = blockIdx.y;
+  double x[4];
+  gate_diffs(colsum, rowsum, bh, c * GG_CHUNK + 4 * threadIdx.x, L, Lp, x);
+  const double t = block_sum_gg((x[0] + x[1]) + (x[2] + x[3]), red);
+  if (threadIdx.x == 0) tot[(size_t)bh * nch + c] = t;
+}
+
+__global__ __launch_bounds__(GG_THREADS) void bwd_gate_grad_kernel(
+    const float* __restrict__ colsum, const float* __restrict__ rowsum,
+    const double* __restrict__ tot, const float* __restrict__ logf, float* __restrict__ dlogf,
+    int L, int Lp, int nch) {
+  __shared__ double red[GG_THREADS / 64], wsum[GG_THREADS / 64];
+  const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  double carry = 0.0;  // the earlier chunks
+  for (int u = tid; u < c; u += GG_THREADS) carry += tot[(size_t)bh * nch + u];
+  carry = block_sum_gg(carry, red);
+  const int t0 = c * GG_CHUNK + 4 * tid;
+  double x[4];
+  gate_diffs(colsum, rowsum, bh, t0, L, Lp, x);
+  const double mine = (x[0] + x[1]) + (x[2] + x[3]);
+  double incl = mine;  // inclusive scan of the thread sums within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  double pre = carry + (incl - mine);
+  for (int u = 0; u < w; ++u) pre += wsum[u];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = t0 + e;
+    if (t < L) {
+      const float lf = logf[(size_t)bh * L + t];
+      dlogf[(size_t)bh * L + t] = (lf <= 0.f) ? (float)pre : 0.f;
+    }
+    pre += x[e];
+  }
+}
+
+template <int D, int NW, bool ALIBI, bool GATE>
+hipError_t launch_bwd_grads(const Geometry& g, const BwdArgs& a, hipStream_t stream) {
+  const uint32_t fl = g.flags;
+  {
+    const int nkt = (g.L + 32 * NW - 1) / (32 * NW);
+    const int total = g.B * g.H * nkt;
+    const int grid = ((total + 7) / 8) * 8;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, ALIBI, GATE>), dim3(grid), dim3(NW * 64), 0, stream,
+                       a.ops, a.theta, a.alibi, a.dk, a.dv, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nkt,
+                       total, fl);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int nqt = (g.L + 32 * NW - 1) / (32 * NW);
+    const int total = g.B * g.H * nqt;
+    const int grid = ((total + 7) / 8) * 8;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, ALIBI, GATE>), dim3(grid), dim3(NW * 64), 0, stream,
+                       a.ops, a.theta, a.alibi, a.dq, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nqt, total,
+                       fl, g.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if constexpr (GATE) {
+    // the chunk sums reuse the gate prefix's totals (read by then); both
+    // have ceil(Lp / 1024) chunks per (b, h)
+    static_assert(GG_CHUNK == GATE_CHUNK, "one chunk size for both gate scans");
+    const int nch = gate_chunks(g);
+    const dim3 grid(nch, g.B * g.H);
+    hipLaunchKernelGGL(bwd_gate_tot_kernel, grid, dim3(GG_THREADS), 0, stream, a.ops.colsum,
+                       a.ops.rowsum, a.gate_tot, g.L, g.Lp, nch);
+    hipLaunchKernelGGL(bwd_gate_grad_kernel, grid, dim3(GG_THREADS), 0, stream, a.ops.colsum,
+                       a.ops.rowsum, a.gate_tot, a.logf, a.dlogf, g.L, g.Lp, nch);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
 template <int D, int NW>
 hipError_t launch_bwd_d(const Geometry& g, const BwdArgs& a, hipStream_t stream) {
   const uint32_t fl = g.flags;
@@ -704,37 +867,11 @@ hipError_t launch_bwd_d(const Geometry& g, const BwdArgs& a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
-    const int nkt = (g.L + 32 * NW - 1) / (32 * NW);
-    const int total = g.B * g.H * nkt;
-    const int grid = ((total + 7) / 8) * 8;
-    if (al)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, true>), dim3(grid), dim3(NW * 64), 0, stream, a.ops,
-                         a.theta, a.alibi, a.dk, a.dv, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nkt, total,
-                         fl);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, false>), dim3(grid), dim3(NW * 64), 0, stream,
-                         a.ops, a.theta, a.alibi, a.dk, a.dv, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nkt,
-                         total, fl);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    const int nqt = (g.L + 32 * NW - 1) / (32 * NW);
-    const int total = g.B * g.H * nqt;
-    const int grid = ((total + 7) / 8) * 8;
-    if (al)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, NW, true>), dim3(grid), dim3(NW * 64), 0, stream, a.ops,
-                         a.theta, a.alibi, a.dq, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nqt, total, fl,
-                         g.scale);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, NW, false>), dim3(grid), dim3(NW * 64), 0, stream, a.ops,
-                         a.theta, a.alibi, a.dq, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nqt, total, fl,
-                         g.scale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  const bool gate = a.ops.gate2 != nullptr;
+  if (al) return gate ? launch_bwd_grads<D, NW, true, true>(g, a, stream)
+                      : launch_bwd_grads<D, NW, true, false>(g, a, stream);
+  return gate ? launch_bwd_grads<D, NW, false, true>(g, a, stream)
+              : launch_bwd_grads<D, NW, false, false>(g, a, stream);
 }
 
 template <int P>

@@ -83,7 +83,8 @@ typedef enum arp_dtype {
 #define ARP_FUSED_ROTATION 0x20u  /* bf16: rotate k/v while staging tiles in LDS
                                      instead of a separate pre-rotation pass */
 #define ARP_FORGET_GATE 0x40u     /* add the forget-gate bias sum_{s=j+1}^{i} log f_s (bf16,
-                                     pre-rotation path, arp_forward_ex only) */
+                                     pre-rotation path; arp_forward_ex and
+                                     arp_backward_ex only) */
 #define ARP_ALL_FLAGS 0x7Fu
 
 typedef struct arp_desc {
@@ -218,7 +219,8 @@ arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k,
  *    beside the distance bias in Sec. 4 of the method paper).  Gates are at
  *    most 1: values log f_t > 0 are taken as 0.
  * bf16 with the pre-rotation path only (ARP_ERR_UNSUPPORTED otherwise); every
- * other entry point returns ARP_ERR_INVALID_ARG when ARP_FORGET_GATE is set. */
+ * other entry point but arp_backward_ex returns ARP_ERR_INVALID_ARG when
+ * ARP_FORGET_GATE is set. */
 arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, const void* v,
                           const float* phi, const float* alibi, const float* logf, float* theta,
                           void* o, float* lse, void* scan_state, size_t scan_state_bytes,
@@ -246,6 +248,24 @@ arp_status arp_backward(const arp_desc* desc, const void* q, const void* k, cons
                         const float* theta, const float* alibi, const void* o, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, float* dtheta,
                         float* dphi, void* workspace, size_t workspace_bytes, void* stream);
+
+/* arp_backward with the forget gates (ARP_FORGET_GATE; logf and dlogf are
+ * then required, else ignored): o and lse from arp_forward_ex with the same
+ * desc and logf (float32 [batch, heads, seqlen]); additionally writes
+ *   dlogf       float32 [batch, heads, seqlen]: dL/d(log f_s).
+ * Score (i, j) holds log f_s for j < s <= i (the PaTH reading notes' Sec. 2.5),
+ * so dlogf_s = sum_{i >= s} sum_{j < s} dS_ij with dS_ij = dL/ds_ij.  It is
+ * formed as sum_{t < s} (c_t - r_t) from the column sums c_t = sum_i dS_it and
+ * the row sums r_t = sum_j dS_tj of the computed dS, an identity for any
+ * lower-triangular matrix (the rows of the exact dS also sum to zero).  Gates
+ * above 1 are taken as 1 by the forward, so dlogf_s = 0 where log f_s > 0.
+ * The workspace (arp_backward_workspace_bytes with the flag set) also holds
+ * the gate prefix and the dS sums.  Without the flag this is arp_backward. */
+arp_status arp_backward_ex(const arp_desc* desc, const void* q, const void* k, const void* v,
+                           const float* theta, const float* alibi, const float* logf, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* dtheta, float* dphi, float* dlogf, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* ---- decode: one new token per sequence against a key/value cache ----
  * desc.seqlen is the cache capacity Lmax; bf16 only.  Caches hold the keys and

@@ -197,3 +197,33 @@ def test_forget_gate_flag_is_refused_outside_the_gated_forward():
     df = _desc(dtype="f32", flags=b.ROTATE_QK | b.FORGET_GATE)
     assert L.arp_forward_ex(ctypes.byref(df), A, A, A, A, None, A, A, A, None, A, st, A, big,
                             None) == b.ERR_UNSUPPORTED
+
+
+def test_gated_backward_validates_gates_and_workspace():
+    """arp_backward refuses the gate flag (arp_backward_ex takes it); the gated
+    backward needs logf and dlogf, and a workspace that also holds the gate
+    prefix, its chunk totals and the two dS sums."""
+    L = b.lib()
+    d = _desc(batch=2, heads=8, seqlen=16384, flags=b.ROTATE_QK | b.FORGET_GATE)
+    plain = _desc(batch=2, heads=8, seqlen=16384, flags=b.ROTATE_QK)
+    by = ctypes.byref(d)
+    ws, ws0 = L.arp_backward_workspace_bytes(by), L.arp_backward_workspace_bytes(ctypes.byref(plain))
+    extra = 3 * 2 * 8 * 16384 * 4 + 2 * 8 * (16384 // 1024) * 8  # G, colsum, rowsum; fp64 totals
+    assert ws0 + extra <= ws < ws0 + extra + 4 * 256 and ws % 256 == 0
+    p14 = [A] * 14
+    assert L.arp_backward(by, *p14, ws, None) == b.ERR_INVALID_ARG
+    # q k v theta alibi logf o lse dout dq dk dv dtheta dphi dlogf workspace
+    args = [A, A, A, A, None, A, A, A, A, A, A, A, A, A, A, A]
+    no_logf = list(args)
+    no_logf[5] = None
+    assert L.arp_backward_ex(by, *no_logf, ws, None) == b.ERR_INVALID_ARG
+    no_dlogf = list(args)
+    no_dlogf[14] = None
+    assert L.arp_backward_ex(by, *no_dlogf, ws, None) == b.ERR_INVALID_ARG
+    bad_logf = list(args)
+    bad_logf[5] = M
+    assert L.arp_backward_ex(by, *bad_logf, ws, None) == b.ERR_ALIGNMENT
+    assert L.arp_backward_ex(by, *args, ws - 256, None) == b.ERR_WORKSPACE
+    # without the flag the gate arguments are ignored
+    assert L.arp_backward_ex(ctypes.byref(plain), *no_logf[:14], None, A, ws0 - 256,
+                             None) == b.ERR_WORKSPACE
