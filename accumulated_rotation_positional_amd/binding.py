@@ -39,7 +39,8 @@ EXPORTS = ("arp_abi_version", "arp_status_string", "arp_check", "arp_scan_state_
            "arp_forward", "arp_rotate", "arp_forward_train", "arp_backward_workspace_bytes",
            "arp_backward", "arp_decode_workspace_bytes", "arp_decode_prefill", "arp_decode_step",
            "arp_forward_ex", "arp_angle_scan_random", "arp_angle_scan_tokens",
-           "arp_angle_scan_const", "arp_random_phi", "arp_backward_ex")
+           "arp_angle_scan_const", "arp_random_phi", "arp_backward_ex", "arp_decode_prefill_ex",
+           "arp_decode_step_ex")
 
 
 class ArpError(RuntimeError):
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
                 "arp_backward_workspace_bytes": ([D], S),
                 "arp_backward": ([D] + [P] * 14 + [S, P], ctypes.c_int),
                 "arp_backward_ex": ([D] + [P] * 16 + [S, P], ctypes.c_int),
+                "arp_decode_prefill_ex": ([D, ctypes.c_int32] + [P] * 10 + [P], ctypes.c_int),
+                "arp_decode_step_ex": ([D, ctypes.c_int32] + [P] * 14 + [S, P], ctypes.c_int),
                 "arp_decode_workspace_bytes": ([D], S),
                 "arp_decode_prefill": ([D, ctypes.c_int32] + [P] * 7 + [P], ctypes.c_int),
                 "arp_decode_step": ([D, ctypes.c_int32] + [P] * 11 + [S, P], ctypes.c_int),
@@ -396,15 +399,21 @@ def backward_ex(desc: Desc, q, k, v, phi, theta, o, lse, dout, alibi=None, logf=
 
 class DecodeCache:
     """Key/value cache (pre-rotated bf16 [B, H, capacity, d]), the angle state
-    (uint64 [B, Hphi, d/2]) and the step workspace of one decoding stream."""
+    (uint64 [B, Hphi, d/2]) and the step workspace of one decoding stream;
+    with forget=True also the gate-prefix cache (fp32 [B, H, capacity]) and the
+    gate state (fp64 [B, H])."""
 
     def __init__(self, batch: int, heads: int, capacity: int, head_dim: int, *, phi_heads=None,
                  rotate_qk: bool = True, rotate_v: bool = False, alibi: bool = False,
-                 exclusive: bool = False, scale: float | None = None,
+                 exclusive: bool = False, forget: bool = False, scale: float | None = None,
                  device: torch.device = torch.device("cuda:0")):
         hphi = heads if phi_heads is None else phi_heads
         flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi,
-                          shared_phi=hphi == 1 and heads != 1, exclusive=exclusive)
+                          shared_phi=hphi == 1 and heads != 1, exclusive=exclusive, forget=forget)
+        self.forget = forget
+        self.gcache = (torch.zeros(batch, heads, capacity, dtype=torch.float32, device=device)
+                       if forget else None)
+        self.gstate = torch.zeros(batch, heads, dtype=torch.float64, device=device) if forget else None
         self.desc = make_desc(batch, heads, capacity, head_dim, torch.bfloat16, flags, scale)
         self.device = device
         self.kcache = torch.zeros(batch, heads, capacity, head_dim, dtype=torch.bfloat16, device=device)
@@ -414,21 +423,35 @@ class DecodeCache:
         nbytes = max(int(lib().arp_decode_workspace_bytes(ctypes.byref(self.desc))), 256)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
-    def prefill(self, k=None, v=None, phi=None, theta=None) -> None:
+    def prefill(self, k=None, v=None, phi=None, theta=None, logf=None) -> None:
         """Cache rows [0, len) and the state after the len prompt tokens
-        (k, v [B, H, len, d]; phi, theta [B, Hphi, len, d/2]); no arguments:
-        an empty prompt (state reset)."""
-        _require_gpu(k, v, phi, theta)
+        (k, v [B, H, len, d]; phi, theta [B, Hphi, len, d/2]; with gates logf
+        [B, H, len]); no arguments: an empty prompt (state reset)."""
+        _require_gpu(k, v, phi, theta, logf)
         n = 0 if k is None else int(k.shape[2])
+        if self.forget:
+            _check("arp_decode_prefill_ex", lib().arp_decode_prefill_ex(
+                ctypes.byref(self.desc), n, _ptr(k), _ptr(v), _ptr(phi), _ptr(theta), _ptr(logf),
+                _ptr(self.kcache), _ptr(self.vcache), _ptr(self.state), _ptr(self.gcache),
+                _ptr(self.gstate), _stream(self.device)))
+            return
         _check("arp_decode_prefill", lib().arp_decode_prefill(
             ctypes.byref(self.desc), n, _ptr(k), _ptr(v), _ptr(phi), _ptr(theta),
             _ptr(self.kcache), _ptr(self.vcache), _ptr(self.state), _stream(self.device)))
 
-    def step(self, pos: int, q, k, v, phi, alibi=None, out=None) -> torch.Tensor:
-        """One token at position pos: q, k, v [B, H, d]; phi [B, Hphi, d/2].
-        Returns o [B, H, d]; self.theta holds the token's angles."""
-        _require_gpu(q, k, v, phi, alibi, out)
+    def step(self, pos: int, q, k, v, phi, alibi=None, out=None, logf=None) -> torch.Tensor:
+        """One token at position pos: q, k, v [B, H, d]; phi [B, Hphi, d/2];
+        with gates logf [B, H].  Returns o [B, H, d]; self.theta holds the
+        token's angles."""
+        _require_gpu(q, k, v, phi, alibi, out, logf)
         out = torch.empty_like(q) if out is None else out
+        if self.forget:
+            _check("arp_decode_step_ex", lib().arp_decode_step_ex(
+                ctypes.byref(self.desc), int(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(phi),
+                _ptr(alibi), _ptr(logf), _ptr(self.state), _ptr(self.theta), _ptr(self.kcache),
+                _ptr(self.vcache), _ptr(self.gcache), _ptr(self.gstate), _ptr(out), _ptr(self.ws),
+                self.ws.numel(), _stream(self.device)))
+            return out
         _check("arp_decode_step", lib().arp_decode_step(
             ctypes.byref(self.desc), int(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(phi), _ptr(alibi),
             _ptr(self.state), _ptr(self.theta), _ptr(self.kcache), _ptr(self.vcache), _ptr(out),

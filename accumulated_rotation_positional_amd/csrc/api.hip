@@ -459,45 +459,64 @@ size_t arp_decode_workspace_bytes(const arp_desc* desc) {
   return align_up(decode_workspace_bytes(g));
 }
 
+arp_status arp_decode_prefill_ex(const arp_desc* desc, int32_t len, const void* k, const void* v,
+                                 const float* phi, const float* theta, const float* logf,
+                                 void* kcache, void* vcache, uint64_t* state, float* gcache,
+                                 double* gstate, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (g.dtype != ARP_DTYPE_BF16) return ARP_ERR_UNSUPPORTED;
+  if (len < 0 || len > g.L || kcache == nullptr || vcache == nullptr || state == nullptr)
+    return ARP_ERR_INVALID_ARG;
+  if (len > 0 && (k == nullptr || v == nullptr || phi == nullptr || (rotates(g) && theta == nullptr)))
+    return ARP_ERR_INVALID_ARG;
+  if (gated(g) && (gcache == nullptr || gstate == nullptr || (len > 0 && logf == nullptr)))
+    return ARP_ERR_INVALID_ARG;
+  if (!aligned16(kcache) || !aligned16(vcache) || !aligned16(state)) return ARP_ERR_ALIGNMENT;
+  if (len > 0 && (!aligned16(k) || !aligned16(v) || !aligned16(phi) || (theta && !aligned16(theta))))
+    return ARP_ERR_ALIGNMENT;
+  if (gated(g) && (!aligned16(gcache) || !aligned16(gstate) || (len > 0 && !aligned16(logf))))
+    return ARP_ERR_ALIGNMENT;
+  return hip_status(launch_decode_prefill(
+      g, len, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), phi, theta,
+      static_cast<uint16_t*>(kcache), static_cast<uint16_t*>(vcache), state,
+      gated(g) ? logf : nullptr, gated(g) ? gcache : nullptr, gated(g) ? gstate : nullptr,
+      (hipStream_t)stream));
+}
+
 arp_status arp_decode_prefill(const arp_desc* desc, int32_t len, const void* k, const void* v,
                               const float* phi, const float* theta, void* kcache, void* vcache,
                               uint64_t* state, void* stream) {
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
-  if (gated(g)) return ARP_ERR_UNSUPPORTED;
-  if (g.dtype != ARP_DTYPE_BF16) return ARP_ERR_UNSUPPORTED;
-  if (len < 0 || len > g.L || kcache == nullptr || vcache == nullptr || state == nullptr)
-    return ARP_ERR_INVALID_ARG;
-  if (len > 0 && (k == nullptr || v == nullptr || phi == nullptr || (rotates(g) && theta == nullptr)))
-    return ARP_ERR_INVALID_ARG;
-  if (!aligned16(kcache) || !aligned16(vcache) || !aligned16(state)) return ARP_ERR_ALIGNMENT;
-  if (len > 0 && (!aligned16(k) || !aligned16(v) || !aligned16(phi) || (theta && !aligned16(theta))))
-    return ARP_ERR_ALIGNMENT;
-  return hip_status(launch_decode_prefill(g, len, static_cast<const uint16_t*>(k),
-                                          static_cast<const uint16_t*>(v), phi, theta,
-                                          static_cast<uint16_t*>(kcache),
-                                          static_cast<uint16_t*>(vcache), state,
-                                          (hipStream_t)stream));
+  if (gated(g)) return ARP_ERR_INVALID_ARG;  // the gates: arp_decode_prefill_ex
+  return arp_decode_prefill_ex(desc, len, k, v, phi, theta, nullptr, kcache, vcache, state,
+                               nullptr, nullptr, stream);
 }
 
-arp_status arp_decode_step(const arp_desc* desc, int32_t pos, const void* q, const void* k,
-                           const void* v, const float* phi, const float* alibi, uint64_t* state,
-                           float* theta, void* kcache, void* vcache, void* o, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+arp_status arp_decode_step_ex(const arp_desc* desc, int32_t pos, const void* q, const void* k,
+                              const void* v, const float* phi, const float* alibi,
+                              const float* logf, uint64_t* state, float* theta, void* kcache,
+                              void* vcache, float* gcache, double* gstate, void* o,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
-  if (gated(g)) return ARP_ERR_UNSUPPORTED;
   if (g.dtype != ARP_DTYPE_BF16) return ARP_ERR_UNSUPPORTED;
   if (pos < 0 || pos >= g.L) return ARP_ERR_INVALID_ARG;
   const void* req[] = {q, k, v, phi, state, theta, kcache, vcache, o};
   for (const void* p : req)
     if (p == nullptr) return ARP_ERR_INVALID_ARG;
   if ((g.flags & ARP_ALIBI) && alibi == nullptr) return ARP_ERR_INVALID_ARG;
+  if (gated(g) && (logf == nullptr || gcache == nullptr || gstate == nullptr))
+    return ARP_ERR_INVALID_ARG;
   for (const void* p : req)
     if (!aligned16(p)) return ARP_ERR_ALIGNMENT;
   if (alibi && !aligned16(alibi)) return ARP_ERR_ALIGNMENT;
+  if (gated(g) && (!aligned16(logf) || !aligned16(gcache) || !aligned16(gstate)))
+    return ARP_ERR_ALIGNMENT;
   if ((st = check_buffer(workspace, workspace_bytes, align_up(decode_workspace_bytes(g)))) != ARP_OK)
     return st;
   DecodeArgs a{};
@@ -513,7 +532,24 @@ arp_status arp_decode_step(const arp_desc* desc, int32_t pos, const void* q, con
   a.vcache = static_cast<uint16_t*>(vcache);
   a.o = static_cast<uint16_t*>(o);
   a.part = static_cast<float*>(workspace);
+  if (gated(g)) {
+    a.logf = logf;
+    a.gcache = gcache;
+    a.gstate = gstate;
+  }
   return hip_status(launch_decode_step(g, a, (hipStream_t)stream));
+}
+
+arp_status arp_decode_step(const arp_desc* desc, int32_t pos, const void* q, const void* k,
+                           const void* v, const float* phi, const float* alibi, uint64_t* state,
+                           float* theta, void* kcache, void* vcache, void* o, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (gated(g)) return ARP_ERR_INVALID_ARG;  // the gates: arp_decode_step_ex
+  return arp_decode_step_ex(desc, pos, q, k, v, phi, alibi, nullptr, state, theta, kcache, vcache,
+                            nullptr, nullptr, o, workspace, workspace_bytes, stream);
 }
 
 arp_status arp_rotate(const arp_desc* desc, const void* x, const float* theta, float* out,

@@ -139,11 +139,15 @@ struct DecodeArgs {
   uint16_t *kcache, *vcache;    // [B, H, L, D] pre-rotated k~, v~
   uint16_t* o;                  // [B, H, D]
   float* part;                  // workspace: [B*H, ceil(L/256), D + 2] partial results
+  const float* logf;            // [B, H] the new token's log forget gate (gated only)
+  float* gcache;                // [B, H, L] gate prefixes G_j of the cached keys (gated only)
+  double* gstate;               // [B, H] running sum of min(log f, 0) (gated only)
 };
 size_t decode_workspace_bytes(const Geometry& g);
 hipError_t launch_decode_prefill(const Geometry& g, int len, const uint16_t* k, const uint16_t* v,
                                  const float* phi, const float* theta, uint16_t* kcache,
-                                 uint16_t* vcache, uint64_t* state, hipStream_t stream);
+                                 uint16_t* vcache, uint64_t* state, const float* logf,
+                                 float* gcache, double* gstate, hipStream_t stream);
 hipError_t launch_decode_step(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace arp

@@ -26,6 +26,13 @@
 //   decode_combine  one workgroup per (b, h): merges the partials, normalises,
 //                   un-rotates, writes o, and advances the angle state.
 // The attention pass is bound by HBM: it reads 2 * (t+1) * d bf16 per (b, h).
+//
+// Forget gates (ARP_FORGET_GATE): a third cache holds each key's gate prefix
+// G_j = log2 e * sum_{s <= j} min(log f_s, 0) (fp32, the forward's G), and a
+// per-(b, h) state the running sum of min(log f, 0) in fp64.  A step forms
+// G_t from the state and the new token's gate, adds G_t - G_j to each score
+// (the route's product of gates, PaTH reading notes Sec. 2.5), appends G_t
+// to the gate cache, and the combine pass advances the state.
 #include "angle_fixed.hpp"
 #include "arp_device.hpp"
 #include "arp_internal.hpp"
@@ -93,6 +100,47 @@ __global__ __launch_bounds__(256) void decode_state_kernel(const float* __restri
   }
 }
 
+// Gate prefix of the prompt: gcache[bh][t] = fp32(log2 e * sum_{s <= t} min(logf[bh][s], 0))
+// for t < len and gstate[bh] = the fp64 sum over the whole prompt.  One
+// workgroup per (b, h) walks the prompt in chunks of 1024 tokens (four
+// consecutive tokens per thread, an in-chunk scan in fp64 plus the carry).
+__global__ __launch_bounds__(256) void decode_gate_fill_kernel(const float* __restrict__ logf,
+                                                               float* __restrict__ gcache,
+                                                               double* __restrict__ gstate, int len,
+                                                               int Lmax) {
+  __shared__ double wsum[4];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  constexpr double LOG2E_D = 1.4426950408889634;
+  double carry = 0.0;
+  for (int c0 = 0; c0 < len; c0 += 1024) {
+    const int t0 = c0 + 4 * tid;
+    double run[4];
+    double acc = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (t0 + e < len) acc += (double)fminf(logf[(size_t)bh * len + t0 + e], 0.f);
+      run[e] = acc;
+    }
+    double incl = acc;  // inclusive scan of the thread sums within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    double pre = carry + (incl - acc);
+    for (int u = 0; u < w; ++u) pre += wsum[u];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (t0 + e < len) gcache[(size_t)bh * Lmax + t0 + e] = (float)((pre + run[e]) * LOG2E_D);
+    carry += (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    __syncthreads();  // wsum is rewritten by the next chunk
+  }
+  if (tid == 0) gstate[bh] = carry;
+}
+
 // ---------------------------------------------------------------------------
 // step
 // ---------------------------------------------------------------------------
@@ -101,13 +149,14 @@ __global__ __launch_bounds__(256) void decode_state_kernel(const float* __restri
 // lanes of 16 bytes per row, 1 KB per instruction): lane (r, c) holds chunk c
 // of rows kw0 + RPI i + r.  Scores are reduced over the CPR lanes of a row;
 // P V accumulates per lane and is reduced over the RPI row groups at the end.
-template <int D, bool ALIBI>
+template <int D, bool ALIBI, bool GATE>
 __global__ __launch_bounds__(256) void decode_attn_kernel(
     const uint16_t* __restrict__ qin, const uint16_t* __restrict__ kin,
     const uint16_t* __restrict__ vin, const float* __restrict__ phi,
     const uint64_t* __restrict__ state, float* __restrict__ theta, uint16_t* __restrict__ kcache,
-    uint16_t* __restrict__ vcache, const float* __restrict__ alibi, float* __restrict__ part,
-    int H, int Hphi, int Lmax, int pos, int nchunk, uint32_t flags, float qscale) {
+    uint16_t* __restrict__ vcache, const float* __restrict__ alibi, const float* __restrict__ logf,
+    float* __restrict__ gcache, const double* __restrict__ gstate, float* __restrict__ part, int H,
+    int Hphi, int Lmax, int pos, int nchunk, uint32_t flags, float qscale) {
   constexpr int CPR = D / 8;     // lanes per row
   constexpr int RPI = 64 / CPR;  // rows per load instruction
   constexpr int NI = 64 / RPI;   // instructions per 64 keys
@@ -120,6 +169,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   const int n = pos + 1;                // keys 0..pos
   const int kw0 = c * DKC + wave * 64;  // this wave's first key
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
+  // The new token's gate prefix G_t (every workgroup forms the same value;
+  // the first one appends it to the gate cache).
+  float gt = 0.f;
+  if constexpr (GATE) {
+    gt = (float)((gstate[bh] + (double)fminf(logf[bh], 0.f)) * 1.4426950408889634);
+    if (c == 0 && tid == 0) gcache[(size_t)bh * Lmax + pos] = gt;
+  }
 
   // The new token's angles for this lane's four pairs 4 ch .. 4 ch + 3: the
   // state plus its steps (the scan's arithmetic, so bit-identical to it).
@@ -190,6 +246,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     for (int mk = 1; mk < CPR; mk <<= 1) a += __shfl_xor(a, mk);
     const int row = kw0 + RPI * i + rg;
     if (ALIBI) a += slope2 * (float)(row - pos);
+    if (GATE && row < pos) a += gt - gcache[(size_t)bh * Lmax + row];
     sc[i] = (row < n) ? a : -INFINITY;
     m = fmaxf(m, sc[i]);
   }
@@ -258,8 +315,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ part, const float* __restrict__ theta, const float* __restrict__ phi,
-    uint64_t* __restrict__ state, uint16_t* __restrict__ o, int H, int Hphi, int nchunk,
-    uint32_t flags) {
+    uint64_t* __restrict__ state, const float* __restrict__ logf, double* __restrict__ gstate,
+    uint16_t* __restrict__ o, int H, int Hphi, int nchunk, uint32_t flags) {
   constexpr int P = D / 2, G = 256 / P;
   __shared__ float s_red[4];
   __shared__ float s_sum[G][P][3];
@@ -321,23 +378,33 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   // advance the state (one workgroup per angle stream; no other workgroup of
   // this kernel reads it)
   if (Hphi != 1 || h == 0) state[sidx] = (state[sidx] + to_fixed(phi[sidx])) & MASK48;
+  // and the gate state (one workgroup per (b, h))
+  if (gstate != nullptr && tid == 0) gstate[bh] += (double)fminf(logf[bh], 0.f);
+}
+
+template <int D, bool ALIBI, bool GATE>
+void launch_attn_step(const Geometry& g, const DecodeArgs& a, int nchunk, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_attn_kernel<D, ALIBI, GATE>), dim3(nchunk, g.B * g.H), dim3(256), 0,
+                     stream, a.q, a.k, a.v, a.phi, a.state, a.theta, a.kcache, a.vcache, a.alibi,
+                     a.logf, a.gcache, a.gstate, a.part, g.H, g.Hphi, g.L, a.pos, nchunk, g.flags,
+                     g.scale * LOG2E);
 }
 
 template <int D>
 hipError_t launch_step(const Geometry& g, const DecodeArgs& a, hipStream_t stream) {
   const int BH = g.B * g.H;
   const int nchunk = (a.pos + 1 + DKC - 1) / DKC;
-  const float qscale = g.scale * LOG2E;
-  if (g.flags & ARP_ALIBI)
-    hipLaunchKernelGGL((decode_attn_kernel<D, true>), dim3(nchunk, BH), dim3(256), 0, stream, a.q,
-                       a.k, a.v, a.phi, a.state, a.theta, a.kcache, a.vcache, a.alibi, a.part, g.H,
-                       g.Hphi, g.L, a.pos, nchunk, g.flags, qscale);
-  else
-    hipLaunchKernelGGL((decode_attn_kernel<D, false>), dim3(nchunk, BH), dim3(256), 0, stream, a.q,
-                       a.k, a.v, a.phi, a.state, a.theta, a.kcache, a.vcache, a.alibi, a.part, g.H,
-                       g.Hphi, g.L, a.pos, nchunk, g.flags, qscale);
+  const bool al = (g.flags & ARP_ALIBI) != 0, gate = (g.flags & ARP_FORGET_GATE) != 0;
+  if (al) {
+    if (gate) launch_attn_step<D, true, true>(g, a, nchunk, stream);
+    else launch_attn_step<D, true, false>(g, a, nchunk, stream);
+  } else {
+    if (gate) launch_attn_step<D, false, true>(g, a, nchunk, stream);
+    else launch_attn_step<D, false, false>(g, a, nchunk, stream);
+  }
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(BH), dim3(256), 0, stream, a.part, a.theta,
-                     a.phi, a.state, a.o, g.H, g.Hphi, nchunk, g.flags);
+                     a.phi, a.state, gate ? a.logf : nullptr, gate ? a.gstate : nullptr, a.o, g.H,
+                     g.Hphi, nchunk, g.flags);
   return hipGetLastError();
 }
 
@@ -350,7 +417,8 @@ size_t decode_workspace_bytes(const Geometry& g) {
 
 hipError_t launch_decode_prefill(const Geometry& g, int len, const uint16_t* k, const uint16_t* v,
                                  const float* phi, const float* theta, uint16_t* kcache,
-                                 uint16_t* vcache, uint64_t* state, hipStream_t stream) {
+                                 uint16_t* vcache, uint64_t* state, const float* logf,
+                                 float* gcache, double* gstate, hipStream_t stream) {
   if (len > 0) {
     dim3 grid((unsigned)(((size_t)len * (g.D / 8) + 255) / 256), g.B * g.H);
     if (g.D == 64)
@@ -366,6 +434,9 @@ hipError_t launch_decode_prefill(const Geometry& g, int len, const uint16_t* k, 
   else
     hipLaunchKernelGGL((decode_state_kernel<64>), dim3(g.B * g.Hphi), dim3(256), 0, stream, phi, state,
                        len);
+  if (g.flags & ARP_FORGET_GATE)
+    hipLaunchKernelGGL(decode_gate_fill_kernel, dim3(g.B * g.H), dim3(256), 0, stream, logf, gcache,
+                       gstate, len, g.L);
   return hipGetLastError();
 }
 

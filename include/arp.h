@@ -83,8 +83,8 @@ typedef enum arp_dtype {
 #define ARP_FUSED_ROTATION 0x20u  /* bf16: rotate k/v while staging tiles in LDS
                                      instead of a separate pre-rotation pass */
 #define ARP_FORGET_GATE 0x40u     /* add the forget-gate bias sum_{s=j+1}^{i} log f_s (bf16,
-                                     pre-rotation path; arp_forward_ex and
-                                     arp_backward_ex only) */
+                                     pre-rotation path; arp_forward_ex,
+                                     arp_backward_ex and the _ex decode calls) */
 #define ARP_ALL_FLAGS 0x7Fu
 
 typedef struct arp_desc {
@@ -219,8 +219,8 @@ arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k,
  *    beside the distance bias in Sec. 4 of the method paper).  Gates are at
  *    most 1: values log f_t > 0 are taken as 0.
  * bf16 with the pre-rotation path only (ARP_ERR_UNSUPPORTED otherwise); every
- * other entry point but arp_backward_ex returns ARP_ERR_INVALID_ARG when
- * ARP_FORGET_GATE is set. */
+ * other entry point but arp_backward_ex, arp_decode_prefill_ex and
+ * arp_decode_step_ex returns ARP_ERR_INVALID_ARG when ARP_FORGET_GATE is set. */
 arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, const void* v,
                           const float* phi, const float* alibi, const float* logf, float* theta,
                           void* o, float* lse, void* scan_state, size_t scan_state_bytes,
@@ -301,6 +301,30 @@ arp_status arp_decode_step(const arp_desc* desc, int32_t pos, const void* q, con
                            const void* v, const float* phi, const float* alibi, uint64_t* state,
                            float* theta, void* kcache, void* vcache, void* o, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* Decode with forget gates (ARP_FORGET_GATE; without it these are
+ * arp_decode_prefill and arp_decode_step).  Two more caller-owned buffers:
+ *   gcache  float32 [batch, heads, Lmax]: G_j = log2(e) * sum_{s<=j} min(log f_s, 0)
+ *           of each cached key (the forward's gate prefix),
+ *   gstate  double [batch, heads]: sum_{s<t} min(log f_s, 0) of the tokens so
+ *           far, in fp64.
+ * prefill_ex takes the prompt's gates logf float32 [batch, heads, len] (NULL
+ * when len = 0) and sets gcache rows [0, len) and gstate; step_ex takes the
+ * new token's logf float32 [batch, heads], adds G_t - G_j to the score of
+ * every cached key j (the route's product of gates outside the exponential,
+ * the PaTH reading notes' Sec. 2.5), appends G_t and advances gstate: the
+ * row pos of arp_forward_ex over the whole sequence with the same gates.
+ * Gates above 1 are taken as 1.  With the flag, logf, gcache and gstate are
+ * required (ARP_ERR_INVALID_ARG) and 16-byte aligned (ARP_ERR_ALIGNMENT). */
+arp_status arp_decode_prefill_ex(const arp_desc* desc, int32_t len, const void* k, const void* v,
+                                 const float* phi, const float* theta, const float* logf,
+                                 void* kcache, void* vcache, uint64_t* state, float* gcache,
+                                 double* gstate, void* stream);
+arp_status arp_decode_step_ex(const arp_desc* desc, int32_t pos, const void* q, const void* k,
+                              const void* v, const float* phi, const float* alibi,
+                              const float* logf, uint64_t* state, float* theta, void* kcache,
+                              void* vcache, float* gcache, double* gstate, void* o,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Diagnostic: out = R(theta) x (or R(theta)^T x when inverse != 0) in fp32.
  * x has the desc's dtype and q's layout; out is float32 of the same shape. */

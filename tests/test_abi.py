@@ -227,3 +227,33 @@ def test_gated_backward_validates_gates_and_workspace():
     # without the flag the gate arguments are ignored
     assert L.arp_backward_ex(ctypes.byref(plain), *no_logf[:14], None, A, ws0 - 256,
                              None) == b.ERR_WORKSPACE
+
+
+def test_gated_decode_validates_gate_buffers():
+    """The plain decode calls refuse the gate flag; the _ex calls need the
+    gates, the gate cache and the gate state (every call here fails
+    validation: nothing is launched)."""
+    L = b.lib()
+    d = _desc(seqlen=512, flags=b.ROTATE_QK | b.FORGET_GATE)
+    by = ctypes.byref(d)
+    ws = L.arp_decode_workspace_bytes(by)
+    # prefill: len k v phi theta [logf] kcache vcache state [gcache gstate]
+    assert L.arp_decode_prefill(by, 0, None, None, None, None, A, A, A, None) == b.ERR_INVALID_ARG
+    assert L.arp_decode_prefill_ex(by, 0, None, None, None, None, None, A, A, A, None, A,
+                                   None) == b.ERR_INVALID_ARG
+    assert L.arp_decode_prefill_ex(by, 0, None, None, None, None, None, A, A, A, A, None,
+                                   None) == b.ERR_INVALID_ARG
+    assert L.arp_decode_prefill_ex(by, 4, A, A, A, A, None, A, A, A, A, A,
+                                   None) == b.ERR_INVALID_ARG  # gates of the prompt missing
+    assert L.arp_decode_prefill_ex(by, 0, None, None, None, None, None, A, A, A, M, A,
+                                   None) == b.ERR_ALIGNMENT
+    # step: pos q k v phi alibi [logf] state theta kcache vcache [gcache gstate] o workspace
+    assert L.arp_decode_step(by, 0, A, A, A, A, None, A, A, A, A, A, A, ws, None) == b.ERR_INVALID_ARG
+    assert L.arp_decode_step_ex(by, 0, A, A, A, A, None, None, A, A, A, A, A, A, A, A, ws,
+                                None) == b.ERR_INVALID_ARG
+    assert L.arp_decode_step_ex(by, 0, A, A, A, A, None, A, A, A, A, A, None, A, A, A, ws,
+                                None) == b.ERR_INVALID_ARG
+    assert L.arp_decode_step_ex(by, 0, A, A, A, A, None, M, A, A, A, A, A, A, A, A, ws,
+                                None) == b.ERR_ALIGNMENT
+    assert L.arp_decode_step_ex(by, 0, A, A, A, A, None, A, A, A, A, A, A, A, A, A, ws - 256,
+                                None) == b.ERR_WORKSPACE
