@@ -232,6 +232,16 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     kw[i] = (row < pos) ? *reinterpret_cast<const u32x4*>(kb + (size_t)row * D)
                         : (row == pos ? knew : u32x4{0, 0, 0, 0});
   }
+  // the rows' gate biases G_t - G_j (0 for row pos and beyond): lane l loads
+  // the gate of the wave's row kw0 + l, and each lane takes its rows' gates
+  // from the lanes that hold them
+  float gb[NI];
+  if constexpr (GATE) {
+    const int mine = kw0 + lane;
+    const float gl = (mine < pos) ? gcache[(size_t)bh * Lmax + mine] : gt;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) gb[i] = gt - __shfl(gl, RPI * i + rg);
+  }
   float sc[NI];
   float m = -INFINITY;
 #pragma unroll
@@ -246,7 +256,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     for (int mk = 1; mk < CPR; mk <<= 1) a += __shfl_xor(a, mk);
     const int row = kw0 + RPI * i + rg;
     if (ALIBI) a += slope2 * (float)(row - pos);
-    if (GATE && row < pos) a += gt - gcache[(size_t)bh * Lmax + row];
+    if (GATE) a += gb[i];
     sc[i] = (row < n) ? a : -INFINITY;
     m = fmaxf(m, sc[i]);
   }
