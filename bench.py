@@ -233,12 +233,33 @@ def forget_leg(binding, torch, dev, w, q, k, v, phi, steps: int = 20) -> dict:
         return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
 
     with_g, without = timed(logf), timed(None)
+
+    # The gated backward (arp_backward_ex: gate prefix, prep, dK/dV and dQ with
+    # the gate terms and the dS sums, the two gate-gradient scans, the reverse
+    # angle scan) on the gated forward's o and lse.
+    o, theta, lse = binding.forward_ex(q, k, v, phi, rotate_v=w.rotate_v, logf=logf, with_lse=True)
+    desc = binding.desc_for(q, binding.flags_for(rotate_v=w.rotate_v, forget=True))
+    g.manual_seed(7)
+    dout = torch.randn(q.shape, device=dev, generator=g).to(torch.bfloat16)
+    ws = binding.backward_workspace(desc, dev)
+    for _ in range(5):
+        binding.backward_ex(desc, q, k, v, phi, theta, o, lse, dout, logf=logf, ws=ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        binding.backward_ex(desc, q, k, v, phi, theta, o, lse, dout, logf=logf, ws=ws)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    bwd = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
     # The gated kernel stops walking a row's keys once every remaining
     # probability is exactly zero, so dense causal flops over its time would
     # overstate its rate: report the two times and their ratio.
     return {"workload": w.name, "gates": "log sigmoid(z), z ~ N(2, 1)",
             "ms_with_gate": round(with_g, 4), "ms_without": round(without, 4),
-            "speedup_vs_ungated": round(without / with_g, 3)}
+            "speedup_vs_ungated": round(without / with_g, 3),
+            "backward_ms_with_gate": round(bwd, 4)}
 
 
 def generator_leg(binding, torch, dev, steps: int = 30) -> dict:
@@ -297,7 +318,8 @@ def decode_leg(binding, torch, dev, steps: int = 50) -> dict:
     from HBM on every step).  Per step: the append, the split-key attention and
     the combine; HBM roofline on the bytes the attention must read,
     2 * tokens * d * 2 bytes per (b, h).  The caches hold seeded random bf16
-    (the cost does not depend on the values)."""
+    (the cost does not depend on the values).  The same step with forget gates
+    (arp_decode_step_ex, seeded log sigmoid(z) gates) is timed next to it."""
     from accumulated_rotation_positional_amd import workloads as wl
     out = {}
     g = torch.Generator(device=dev)
@@ -325,13 +347,30 @@ def decode_leg(binding, torch, dev, steps: int = 50) -> dict:
             e1.record(stream)
         torch.cuda.synchronize()
         us = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+        # the same step with forget gates (the gate-prefix cache adds 4 bytes per key)
+        gated = binding.DecodeCache(B, H, L, d, rotate_qk=True, rotate_v=True, forget=True,
+                                    device=dev)
+        gated.kcache.copy_(cache.kcache)
+        gated.vcache.copy_(cache.vcache)
+        gated.prefill()
+        logf = torch.nn.functional.logsigmoid(
+            torch.randn(B, H, device=dev, generator=g) + 2.0).contiguous()
+        for _ in range(5):
+            gated.step(L - 1, q, k, v, phi, out=o, logf=logf)
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record(stream)
+            gated.step(L - 1, q, k, v, phi, out=o, logf=logf)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us_g = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
         nbytes = 2.0 * L * d * 2 * B * H
         gbs = nbytes / (us * 1e-6) / 1e9
         out[name] = {"context": L, "batch": B, "heads": H, "head_dim": d, "us_per_step": round(us, 2),
                      "tokens_per_s": round(B / (us * 1e-6), 1), "cache_bytes": nbytes,
                      "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
-        del cache
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "us_per_step_with_gate": round(us_g, 2)}
+        del cache, gated
         torch.cuda.empty_cache()
     return out
 
