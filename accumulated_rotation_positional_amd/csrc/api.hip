@@ -94,6 +94,16 @@ WorkspaceLayout workspace_layout(const Geometry& g) {
 
 BwdWorkspaceLayout bwd_workspace_layout(const Geometry& g) {
   BwdWorkspaceLayout lay{};
+  if (g.dtype == ARP_DTYPE_F32) {
+    // four fp32 operand blocks [B*H, L, D], then -lse and -D, then the reverse scan's totals
+    lay.operand_bytes = align_up((size_t)g.B * g.H * g.L * g.D * sizeof(float));
+    lay.stats_off = 4 * lay.operand_bytes;
+    lay.tstat_off = lay.stats_off + align_up((size_t)g.B * g.H * g.L * 2 * sizeof(float));
+    lay.totals_off = lay.tstat_off;
+    const size_t nch = ((size_t)g.L + 255) / 256;
+    lay.total = lay.totals_off + align_up((size_t)g.B * g.Hphi * nch * g.P * sizeof(float));
+    return lay;
+  }
   lay.operand_bytes = align_up((size_t)g.B * g.H * g.Lp * g.D * sizeof(uint16_t));
   lay.stats_off = 7 * lay.operand_bytes;
   lay.tstat_off = lay.stats_off + align_up((size_t)g.B * g.H * g.Lp * 2 * sizeof(float));
@@ -272,7 +282,7 @@ arp_status arp_attn_fwd(const arp_desc* desc, const void* q, const void* k, cons
   if (g.dtype == ARP_DTYPE_F32)
     return hip_status(launch_attn_f32(g, static_cast<const float*>(q), static_cast<const float*>(k),
                                       static_cast<const float*>(v), theta, alibi,
-                                      static_cast<float*>(o), s));
+                                      static_cast<float*>(o), nullptr, s));
   if (g.flags & ARP_FUSED_ROTATION)
     return fused_status(launch_attn_bf16_fused(
         g, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
@@ -311,7 +321,8 @@ arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k,
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
   if (gated(g)) return ARP_ERR_INVALID_ARG;  // the gate input: arp_forward_ex
-  if (!needs_operands(g)) return ARP_ERR_UNSUPPORTED;
+  const bool f32 = g.dtype == ARP_DTYPE_F32;
+  if (!needs_operands(g) && !f32) return ARP_ERR_UNSUPPORTED;  // the fused rotation
   if (lse == nullptr) return ARP_ERR_INVALID_ARG;
   if (!aligned16(lse)) return ARP_ERR_ALIGNMENT;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || phi == nullptr ||
@@ -324,6 +335,10 @@ arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k,
   if ((st = check_ws(g, workspace, workspace_bytes)) != ARP_OK) return st;
   st = arp_angle_scan(desc, phi, theta, scan_state, scan_state_bytes, stream);
   if (st != ARP_OK) return st;
+  if (f32)
+    return hip_status(launch_attn_f32(g, static_cast<const float*>(q), static_cast<const float*>(k),
+                                      static_cast<const float*>(v), theta, alibi,
+                                      static_cast<float*>(o), lse, (hipStream_t)stream));
   st = arp_rotate_qkv(desc, q, k, v, theta, workspace, workspace_bytes, stream);
   if (st != ARP_OK) return st;
   const WorkspaceLayout lay = workspace_layout(g);
@@ -344,8 +359,13 @@ arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, co
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
   if (!needs_operands(g)) {
-    // fp32 I/O or the fused rotation: neither the gate nor lse is built there
-    if (gated(g) || lse != nullptr) return ARP_ERR_UNSUPPORTED;
+    // fp32 I/O or the fused rotation: no gate there; lse from the fp32 kernel only
+    if (gated(g)) return ARP_ERR_UNSUPPORTED;
+    if (lse != nullptr)
+      return g.dtype == ARP_DTYPE_F32
+                 ? arp_forward_train(desc, q, k, v, phi, alibi, theta, o, lse, scan_state,
+                                     scan_state_bytes, workspace, workspace_bytes, stream)
+                 : ARP_ERR_UNSUPPORTED;
     return arp_forward(desc, q, k, v, phi, alibi, theta, o, scan_state, scan_state_bytes,
                        workspace, workspace_bytes, stream);
   }
@@ -382,7 +402,8 @@ arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, co
 
 size_t arp_backward_workspace_bytes(const arp_desc* desc) {
   Geometry g;
-  if (make_geometry(desc, &g) != ARP_OK || g.dtype != ARP_DTYPE_BF16) return 0;
+  if (make_geometry(desc, &g) != ARP_OK) return 0;
+  if (g.dtype == ARP_DTYPE_F32 && gated(g)) return 0;
   return bwd_workspace_layout(g).total;
 }
 
@@ -394,7 +415,8 @@ arp_status arp_backward_ex(const arp_desc* desc, const void* q, const void* k, c
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
-  if (g.dtype != ARP_DTYPE_BF16) return ARP_ERR_UNSUPPORTED;
+  const bool f32 = g.dtype == ARP_DTYPE_F32;
+  if (f32 && gated(g)) return ARP_ERR_UNSUPPORTED;  // gates: bf16 only
   const void* in[] = {q, k, v, o, lse, dout, dq, dk, dv, dtheta, dphi};
   for (const void* p : in)
     if (p == nullptr) return ARP_ERR_INVALID_ARG;
@@ -408,6 +430,31 @@ arp_status arp_backward_ex(const arp_desc* desc, const void* q, const void* k, c
   const BwdWorkspaceLayout lay = bwd_workspace_layout(g);
   if ((st = check_buffer(workspace, workspace_bytes, lay.total)) != ARP_OK) return st;
   char* ws = static_cast<char*>(workspace);
+  if (f32) {
+    auto fblk = [&](int i) { return reinterpret_cast<float*>(ws + i * lay.operand_bytes); };
+    BwdF32Args f{};
+    f.q = static_cast<const float*>(q);
+    f.k = static_cast<const float*>(k);
+    f.v = static_cast<const float*>(v);
+    f.o = static_cast<const float*>(o);
+    f.dout = static_cast<const float*>(dout);
+    f.theta = theta;
+    f.lse = lse;
+    f.alibi = alibi;
+    f.dq = static_cast<float*>(dq);
+    f.dk = static_cast<float*>(dk);
+    f.dv = static_cast<float*>(dv);
+    f.dtheta = dtheta;
+    f.dphi = dphi;
+    f.totals = reinterpret_cast<float*>(ws + lay.totals_off);
+    f.qs = fblk(0);
+    f.kr = fblk(1);
+    f.vr = fblk(2);
+    f.dor = fblk(3);
+    f.nl = reinterpret_cast<float*>(ws + lay.stats_off);
+    f.nd = f.nl + (size_t)g.B * g.H * g.L;
+    return hip_status(launch_backward_f32(g, f, (hipStream_t)stream));
+  }
   auto blk = [&](int i) { return reinterpret_cast<uint16_t*>(ws + i * lay.operand_bytes); };
   BwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);

@@ -79,8 +79,10 @@ hipError_t launch_gate_scan(const Geometry& g, const float* logf, float* gate2, 
 hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const float* theta, const float* alibi,
                                   uint16_t* o, hipStream_t stream);
+// lse (nullable): [B, H, L] base-2 log-sum-exp of each row's scaled logits
 hipError_t launch_attn_f32(const Geometry& g, const float* q, const float* k, const float* v,
-                           const float* theta, const float* alibi, float* o, hipStream_t stream);
+                           const float* theta, const float* alibi, float* o, float* lse,
+                           hipStream_t stream);
 hipError_t launch_rotate_diag(const Geometry& g, const void* x, const float* theta, float* out,
                               int inverse, hipStream_t stream);
 
@@ -128,6 +130,19 @@ struct BwdWorkspaceLayout {
 };
 BwdWorkspaceLayout bwd_workspace_layout(const Geometry& g);
 hipError_t launch_backward_bf16(const Geometry& g, const BwdArgs& a, hipStream_t stream);
+
+// fp32 I/O backward (plain FMAs; no forget gates)
+struct BwdF32Args {
+  const float *q, *k, *v, *o, *dout;  // caller tensors [B, H, L, D]
+  const float *theta, *lse, *alibi;
+  float *dq, *dk, *dv;                 // caller gradients [B, H, L, D]
+  float* dtheta;                       // caller [B, H, L, P]
+  float* dphi;                         // caller [B, Hphi, L, P]
+  float* totals;                       // workspace [B*Hphi, ceil(L/256), P]
+  float *qs, *kr, *vr, *dor;           // workspace [B*H, L, D]: q~ scale log2 e, k~, v~, do~
+  float *nl, *nd;                      // workspace [B*H, L]: -lse, -D
+};
+hipError_t launch_backward_f32(const Geometry& g, const BwdF32Args& a, hipStream_t stream);
 
 // ---- decode (bf16; Geometry.L is the cache capacity) ------------------------
 struct DecodeArgs {

@@ -886,7 +886,244 @@ hipError_t launch_rscan(const Geometry& g, const float* dtheta, float* totals, f
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// 6. fp32 I/O: the same gradients with plain FMAs (no matrix cores), for the
+// small fp32 problems.  Four lanes per row, each holding a quarter of the
+// head dimension; dot products are reduced over the four lanes.
+// ---------------------------------------------------------------------------
+constexpr int F32B_ROWS = 64;  // rows (queries or keys) per workgroup
+constexpr int F32B_T = 32;     // rows per staged LDS tile
+
+// Rotated operands, -lse, -D and dTheta's transport term: one thread per
+// (token, pair); the P threads of a token are consecutive lanes.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_f32_prep_kernel(BwdF32Args a, int L, int H, int Hphi,
+                                                           uint32_t flags, float qscale) {
+  constexpr int P = D / 2;
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh % H, g = (Hphi == 1) ? 0 : h;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int t = idx / P, p = idx % P;
+  const bool ok = t < L;
+  const bool rqk = (flags & ARP_ROTATE_QK) != 0, rv = (flags & ARP_ROTATE_V) != 0;
+  float dsum = 0.f;
+  if (ok) {
+    const size_t off = ((size_t)bh * L + t) * D + 2 * p;
+    float q0 = a.q[off], q1 = a.q[off + 1], k0 = a.k[off], k1 = a.k[off + 1];
+    float v0 = a.v[off], v1 = a.v[off + 1], o0 = a.o[off], o1 = a.o[off + 1];
+    float d0 = a.dout[off], d1 = a.dout[off + 1];
+    if (rqk || rv) {
+      float sn, cs;
+      sincosf(a.theta[((size_t)(b * Hphi + g) * L + t) * P + p], &sn, &cs);
+      if (rqk) {
+        rotate_pair(q0, q1, cs, sn);
+        rotate_pair(k0, k1, cs, sn);
+      }
+      if (rv) {
+        rotate_pair(v0, v1, cs, sn);
+        rotate_pair(o0, o1, cs, sn);
+        rotate_pair(d0, d1, cs, sn);
+      }
+    }
+    a.qs[off] = q0 * qscale;
+    a.qs[off + 1] = q1 * qscale;
+    a.kr[off] = k0;
+    a.kr[off + 1] = k1;
+    a.vr[off] = v0;
+    a.vr[off + 1] = v1;
+    a.dor[off] = d0;
+    a.dor[off + 1] = d1;
+    dsum = fmaf(d0, o0, d1 * o1);
+    // value transport: -<do~, J o~> = d0 o1 - d1 o0
+    a.dtheta[((size_t)bh * L + t) * P + p] = rv ? (d0 * o1 - d1 * o0) : 0.f;
+  }
+#pragma unroll
+  for (int m = 1; m < P; m <<= 1) dsum += __shfl_xor(dsum, m);
+  if (ok && p == 0) {
+    a.nd[(size_t)bh * L + t] = -dsum;
+    a.nl[(size_t)bh * L + t] = -a.lse[(size_t)bh * L + t];
+  }
+}
+
+// <a, J x> per pair for this lane's dims, added to dth; then g <- R(theta)^T g.
+template <int DQ>
+__device__ __forceinline__ void f32_grad_out(float (&gr)[DQ], const float (&x)[DQ], float xmul,
+                                             const float* th, bool rot, float* dth, float* out) {
+#pragma unroll
+  for (int e = 0; e < DQ; e += 2) {
+    float g0 = gr[e], g1 = gr[e + 1];
+    if (rot) {
+      const float x0 = x[e] * xmul, x1 = x[e + 1] * xmul;
+      dth[e / 2] += -g0 * x1 + g1 * x0;
+      float sn, cs;
+      sincosf(th[e / 2], &sn, &cs);
+      rotate_pair(g0, g1, cs, -sn);
+    }
+    out[e] = g0;
+    out[e + 1] = g1;
+  }
+}
+
+// dK, dV: a workgroup owns 64 keys and walks the query tiles from its first
+// key to the end.
+template <int D, bool ALIBI>
+__global__ __launch_bounds__(256) void bwd_f32_dkdv_kernel(BwdF32Args a, int L, int H, int Hphi,
+                                                           uint32_t flags) {
+  constexpr int DQ = D / 4, P = D / 2;
+  __shared__ float sq[F32B_T][D], sdo[F32B_T][D], snl[F32B_T], snd[F32B_T];
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh % H, g = (Hphi == 1) ? 0 : h;
+  const int tid = threadIdx.x, sp = tid & 3;
+  const int j = blockIdx.x * F32B_ROWS + tid / 4;
+  const int jc = min(j, L - 1);
+  const int d0 = sp * DQ;
+  float kv[DQ], vv[DQ], dk[DQ], dv[DQ];
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) {
+    kv[e] = a.kr[((size_t)bh * L + jc) * D + d0 + e];
+    vv[e] = a.vr[((size_t)bh * L + jc) * D + d0 + e];
+    dk[e] = dv[e] = 0.f;
+  }
+  const float slope2 = ALIBI ? a.alibi[h] * LOG2E : 0.f;
+  const int jfirst = blockIdx.x * F32B_ROWS;
+  for (int i0 = (jfirst / F32B_T) * F32B_T; i0 < L; i0 += F32B_T) {
+    __syncthreads();
+    for (int e = tid; e < F32B_T * D; e += 256) {
+      const int r = e / D, c = e % D, i = i0 + r;
+      sq[r][c] = (i < L) ? a.qs[((size_t)bh * L + i) * D + c] : 0.f;
+      sdo[r][c] = (i < L) ? a.dor[((size_t)bh * L + i) * D + c] : 0.f;
+    }
+    if (tid < F32B_T) {
+      const int i = i0 + tid;
+      snl[tid] = (i < L) ? a.nl[(size_t)bh * L + i] : -INFINITY;
+      snd[tid] = (i < L) ? a.nd[(size_t)bh * L + i] : 0.f;
+    }
+    __syncthreads();
+    // queries i >= j of the tile (the four lanes of a key share the bounds)
+    const int ibeg = max(0, j - i0), iend = min(F32B_T, L - i0);
+    for (int r = ibeg; r < iend; ++r) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) {
+        s = fmaf(kv[e], sq[r][d0 + e], s);
+        dp = fmaf(vv[e], sdo[r][d0 + e], dp);
+      }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      dp += __shfl_xor(dp, 1);
+      dp += __shfl_xor(dp, 2);
+      s += snl[r];
+      if (ALIBI) s += slope2 * (float)(j - (i0 + r));
+      const float pr = exp2f(s);
+      const float ds = pr * (dp + snd[r]);
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) {
+        dk[e] = fmaf(ds, sq[r][d0 + e], dk[e]);
+        dv[e] = fmaf(pr, sdo[r][d0 + e], dv[e]);
+      }
+    }
+  }
+  if (j >= L) return;
+  // dk~ = scale sum dS q~ = ln 2 sum dS q~s (q~s carries scale log2 e)
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) dk[e] *= 0.69314718055994531f;
+  const float* th = a.theta + ((size_t)(b * Hphi + g) * L + j) * P + d0 / 2;
+  float* dth = a.dtheta + ((size_t)bh * L + j) * P + d0 / 2;
+  const size_t row = ((size_t)bh * L + j) * D + d0;
+  f32_grad_out<DQ>(dk, kv, 1.f, th, (flags & ARP_ROTATE_QK) != 0, dth, a.dk + row);
+  f32_grad_out<DQ>(dv, vv, 1.f, th, (flags & ARP_ROTATE_V) != 0, dth, a.dv + row);
+}
+
+// dQ: a workgroup owns 64 queries and walks the key tiles up to its last query.
+template <int D, bool ALIBI>
+__global__ __launch_bounds__(256) void bwd_f32_dq_kernel(BwdF32Args a, int L, int H, int Hphi,
+                                                         uint32_t flags, float scale) {
+  constexpr int DQ = D / 4, P = D / 2;
+  __shared__ float sk[F32B_T][D], sv[F32B_T][D];
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh % H, g = (Hphi == 1) ? 0 : h;
+  const int tid = threadIdx.x, sp = tid & 3;
+  const int i = blockIdx.x * F32B_ROWS + tid / 4;
+  const int ic = min(i, L - 1);
+  const int d0 = sp * DQ;
+  float qv[DQ], dov[DQ], dq[DQ];
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) {
+    qv[e] = a.qs[((size_t)bh * L + ic) * D + d0 + e];
+    dov[e] = a.dor[((size_t)bh * L + ic) * D + d0 + e];
+    dq[e] = 0.f;
+  }
+  const float nl = a.nl[(size_t)bh * L + ic], nd = a.nd[(size_t)bh * L + ic];
+  const float slope2 = ALIBI ? a.alibi[h] * LOG2E : 0.f;
+  const int i_last = min(L - 1, blockIdx.x * F32B_ROWS + F32B_ROWS - 1);
+  for (int j0 = 0; j0 <= i_last; j0 += F32B_T) {
+    __syncthreads();
+    for (int e = tid; e < F32B_T * D; e += 256) {
+      const int r = e / D, c = e % D, jj = j0 + r;
+      sk[r][c] = (jj < L) ? a.kr[((size_t)bh * L + jj) * D + c] : 0.f;
+      sv[r][c] = (jj < L) ? a.vr[((size_t)bh * L + jj) * D + c] : 0.f;
+    }
+    __syncthreads();
+    // keys j <= i of the tile (the four lanes of a query share the bound)
+    const int jn = min(F32B_T, ic + 1 - j0);
+    for (int r = 0; r < jn; ++r) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) {
+        s = fmaf(qv[e], sk[r][d0 + e], s);
+        dp = fmaf(dov[e], sv[r][d0 + e], dp);
+      }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      dp += __shfl_xor(dp, 1);
+      dp += __shfl_xor(dp, 2);
+      s += nl;
+      if (ALIBI) s += slope2 * (float)((j0 + r) - ic);
+      const float ds = exp2f(s) * (dp + nd);
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) dq[e] = fmaf(ds, sk[r][d0 + e], dq[e]);
+    }
+  }
+  if (i >= L) return;
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) dq[e] *= scale;  // dq~ = scale sum dS k~
+  const float* th = a.theta + ((size_t)(b * Hphi + g) * L + i) * P + d0 / 2;
+  float* dth = a.dtheta + ((size_t)bh * L + i) * P + d0 / 2;
+  // q~ = q~s / (scale log2 e)
+  f32_grad_out<DQ>(dq, qv, 1.f / (scale * LOG2E), th, (flags & ARP_ROTATE_QK) != 0, dth,
+                   a.dq + ((size_t)bh * L + i) * D + d0);
+}
+
+template <int D>
+hipError_t launch_bwd_f32_d(const Geometry& g, const BwdF32Args& a, hipStream_t stream) {
+  constexpr int P = D / 2;
+  const int BH = g.B * g.H;
+  const bool al = (g.flags & ARP_ALIBI) != 0;
+  hipLaunchKernelGGL((bwd_f32_prep_kernel<D>), dim3((g.L * P + 255) / 256, BH), dim3(256), 0,
+                     stream, a, g.L, g.H, g.Hphi, g.flags, g.scale * LOG2E);
+  const dim3 grid((g.L + F32B_ROWS - 1) / F32B_ROWS, BH);
+  if (al) {
+    hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, true>), grid, dim3(256), 0, stream, a, g.L, g.H,
+                       g.Hphi, g.flags);
+    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, true>), grid, dim3(256), 0, stream, a, g.L, g.H,
+                       g.Hphi, g.flags, g.scale);
+  } else {
+    hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, false>), grid, dim3(256), 0, stream, a, g.L, g.H,
+                       g.Hphi, g.flags);
+    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, false>), grid, dim3(256), 0, stream, a, g.L, g.H,
+                       g.Hphi, g.flags, g.scale);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_backward_f32(const Geometry& g, const BwdF32Args& a, hipStream_t stream) {
+  hipError_t e = (g.D == 64) ? launch_bwd_f32_d<64>(g, a, stream) : launch_bwd_f32_d<128>(g, a, stream);
+  if (e != hipSuccess) return e;
+  return (g.P == 32) ? launch_rscan<32>(g, a.dtheta, a.totals, a.dphi, stream)
+                     : launch_rscan<64>(g, a.dtheta, a.totals, a.dphi, stream);
+}
 
 hipError_t launch_backward_bf16(const Geometry& g, const BwdArgs& a, hipStream_t stream) {
   hipError_t e = (g.D == 64) ? launch_bwd_d<64, 8>(g, a, stream) : launch_bwd_d<128, 4>(g, a, stream);

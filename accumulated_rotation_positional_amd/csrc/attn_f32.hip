@@ -29,8 +29,8 @@ constexpr int F32_K = 32;   // keys per staged tile
 template <int D, bool ROT_QK, bool ROT_V, bool ALIBI>
 __global__ __launch_bounds__(F32_T) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ theta, const float* __restrict__ alibi, float* __restrict__ o, int L,
-    int H, int Hphi, float qscale) {
+    const float* __restrict__ theta, const float* __restrict__ alibi, float* __restrict__ o,
+    float* __restrict__ lse, int L, int H, int Hphi, float qscale) {
   constexpr int P = D / 2;
   __shared__ float sk[F32_K][D];
   __shared__ float sv[F32_K][D];
@@ -128,6 +128,8 @@ __global__ __launch_bounds__(F32_T) void attn_f32_kernel(
     m = mm;
   }
   if (!valid) return;
+  // base-2 log-sum-exp of the row's scaled logits (the backward's statistic)
+  if (lse != nullptr && sp == 0) lse[(size_t)bh * L + i] = m + log2f(l);
   const float inv = 1.f / l;
   float* orow = o + ((size_t)bh * L + i) * D;
   // each of the query's lanes writes P / F32_S of its pairs
@@ -147,13 +149,14 @@ __global__ __launch_bounds__(F32_T) void attn_f32_kernel(
 
 template <int D>
 hipError_t launch_f32_d(const Geometry& g, const float* q, const float* k, const float* v,
-                        const float* theta, const float* alibi, float* o, hipStream_t stream) {
+                        const float* theta, const float* alibi, float* o, float* lse,
+                        hipStream_t stream) {
   dim3 grid((g.L + F32_Q - 1) / F32_Q, g.B * g.H);
   const float qscale = g.scale * LOG2E;
   const bool rqk = g.flags & ARP_ROTATE_QK, rv = g.flags & ARP_ROTATE_V, al = g.flags & ARP_ALIBI;
 #define ARP_F32_LAUNCH(A, B, C)                                                                \
   hipLaunchKernelGGL((attn_f32_kernel<D, A, B, C>), grid, dim3(F32_T), 0, stream, q, k, v,    \
-                     theta, alibi, o, g.L, g.H, g.Hphi, qscale)
+                     theta, alibi, o, lse, g.L, g.H, g.Hphi, qscale)
   if (rqk) {
     if (rv) {
       if (al) ARP_F32_LAUNCH(true, true, true); else ARP_F32_LAUNCH(true, true, false);
@@ -174,9 +177,10 @@ hipError_t launch_f32_d(const Geometry& g, const float* q, const float* k, const
 }  // namespace
 
 hipError_t launch_attn_f32(const Geometry& g, const float* q, const float* k, const float* v,
-                           const float* theta, const float* alibi, float* o, hipStream_t stream) {
-  if (g.D == 64) return launch_f32_d<64>(g, q, k, v, theta, alibi, o, stream);
-  return launch_f32_d<128>(g, q, k, v, theta, alibi, o, stream);
+                           const float* theta, const float* alibi, float* o, float* lse,
+                           hipStream_t stream) {
+  if (g.D == 64) return launch_f32_d<64>(g, q, k, v, theta, alibi, o, lse, stream);
+  return launch_f32_d<128>(g, q, k, v, theta, alibi, o, lse, stream);
 }
 
 }  // namespace arp

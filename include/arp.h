@@ -200,11 +200,11 @@ arp_status arp_forward(const arp_desc* desc, const void* q, const void* k, const
                        void* scan_state, size_t scan_state_bytes, void* workspace,
                        size_t workspace_bytes, void* stream);
 
-/* Training forward (bf16, pre-rotation path): arp_forward that also writes
- * lse[b,h,i] (float32 [batch, heads, seqlen]), the base-2 log-sum-exp of row
- * i's scaled logits: log2 sum_{j<=i} 2^(log2(e) s_ij).  The backward pass
- * recomputes the softmax from it.  ARP_ERR_UNSUPPORTED for fp32 I/O or
- * ARP_FUSED_ROTATION. */
+/* Training forward (bf16 pre-rotation path, or fp32 I/O): arp_forward that
+ * also writes lse[b,h,i] (float32 [batch, heads, seqlen]), the base-2
+ * log-sum-exp of row i's scaled logits: log2 sum_{j<=i} 2^(log2(e) s_ij).
+ * The backward pass recomputes the softmax from it.  ARP_ERR_UNSUPPORTED
+ * for bf16 with ARP_FUSED_ROTATION. */
 arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k, const void* v,
                              const float* phi, const float* alibi, float* theta, void* o,
                              float* lse, void* scan_state, size_t scan_state_bytes,
@@ -232,10 +232,10 @@ arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, co
  * statistics, and the reverse scan's chunk totals.  No initialisation needed. */
 size_t arp_backward_workspace_bytes(const arp_desc* desc);
 
-/* Gradients (bf16): given the forward's inputs, theta, o and lse (from
+/* Gradients: given the forward's inputs, theta, o and lse (from
  * arp_forward_train, same desc) and the upstream gradient dout = dL/do
- * ([batch, heads, seqlen, head_dim], bf16), writes
- *   dq, dk, dv  bf16 [batch, heads, seqlen, head_dim]
+ * ([batch, heads, seqlen, head_dim], the dtype of q), writes
+ *   dq, dk, dv  [batch, heads, seqlen, head_dim], the dtype of q
  *   dtheta      float32 [batch, heads, seqlen, head_dim/2]: dL/dTheta per head
  *   dphi        float32, phi's layout: dL/dphi_s = sum over t >= s (t > s with
  *               ARP_SCAN_EXCLUSIVE) of dL/dTheta_t, summed over the heads that
@@ -243,7 +243,8 @@ size_t arp_backward_workspace_bytes(const arp_desc* desc);
  * The chain rule through eq. (2)-(4), (6)-(8) and the rotation AdaRoPE
  * Sec. 2.1 eq. (1) defines (dR/da = R J, J = [[0,-1],[1,0]]); the wrap into
  * [-pi, pi) has derivative 1.  The ALiBi slopes and the scale are constants.
- * ARP_ERR_UNSUPPORTED for fp32 I/O; ARP_FUSED_ROTATION is ignored. */
+ * bf16: matrix-core kernels; fp32 I/O: fp32 FMAs throughout (the workspace
+ * then holds fp32 operands).  ARP_FUSED_ROTATION is ignored. */
 arp_status arp_backward(const arp_desc* desc, const void* q, const void* k, const void* v,
                         const float* theta, const float* alibi, const void* o, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, float* dtheta,
@@ -260,7 +261,8 @@ arp_status arp_backward(const arp_desc* desc, const void* q, const void* k, cons
  * lower-triangular matrix (the rows of the exact dS also sum to zero).  Gates
  * above 1 are taken as 1 by the forward, so dlogf_s = 0 where log f_s > 0.
  * The workspace (arp_backward_workspace_bytes with the flag set) also holds
- * the gate prefix and the dS sums.  Without the flag this is arp_backward. */
+ * the gate prefix and the dS sums.  Gates are bf16 only (ARP_ERR_UNSUPPORTED
+ * for fp32 I/O).  Without the flag this is arp_backward. */
 arp_status arp_backward_ex(const arp_desc* desc, const void* q, const void* k, const void* v,
                            const float* theta, const float* alibi, const float* logf, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
