@@ -65,9 +65,11 @@ constexpr float ZGAP = 160.0f;
 // BIAS: bit 0 the distance bias -m_h (i - j), bit 1 the forget-gate bias
 // G_i - G_j, with G = log2 e * (prefix sums of log f) from the gate pass
 // ([B*H, Lp] in gate2; non-increasing, so the bias never raises a score).
+// One query tile (logical index `logical`, mapped to (head, query tile) below)
+// with the workgroup's LDS ring smem.
 template <int D, int QPW, int NW, int NST, int MINB, bool FUSED, int BIAS, bool ROTV>
-__global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
-    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
+__device__ __forceinline__ void attn_tile(
+    int logical, uint8_t* smem, const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
     const float* __restrict__ theta, const float* __restrict__ alibi,
     const float* __restrict__ gate2, uint16_t* __restrict__ o, float* __restrict__ lse, int L,
@@ -98,18 +100,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
 
   constexpr int GTILE = FORGET ? BN * 4 : 0;  // the tile's 64 key gates (fp32)
   constexpr int STAGE = KTILE + VTILE + GTILE;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
-  // ---- which tile: longest tiles first; without a bias, heads grouped per
-  // XCD (blockIdx % 8) so that its L2 holds their K/V.  A biased walk stops
-  // early by an amount that differs from head to head (the slope, the gates),
-  // so there the tiles are dealt out across the XCDs, the last query tile of
-  // every head first: grouping would leave the XCD with the gentlest heads
-  // doing several times the average work, and the longest tiles of the last
-  // heads would start last.
+  // ---- which tile (the logical order is set by the kernel below) ----
   constexpr bool SPREAD = (BIAS != 0) && !FUSED;
-  const int per = (total_tiles + 7) / 8;
-  const int logical = SPREAD ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (logical >= total_tiles) return;
   const int nbh = total_tiles / nqt;
   // spread: round r deals query tile nqt-1-r of every head, rotated by r so
@@ -580,6 +573,46 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
   }
 }
 
+// Logical tile order: longest tiles first; without a bias, heads grouped per
+// XCD (blockIdx % 8) so that its L2 holds their K/V.  A biased walk stops
+// early by an amount that differs from head to head (the slope, the gates),
+// so there the tiles are dealt out across the XCDs, the last query tile of
+// every head first: grouping would leave the XCD with the gentlest heads
+// doing several times the average work, and the longest tiles of the last
+// heads would start last.
+// paired (the unbiased 512-query shape, total_tiles a multiple of 16): half
+// as many workgroups, each taking the c-th longest and the c-th shortest
+// tile of its XCD's share one after the other, so every workgroup has the
+// same work and no CU waits for a second dispatch.
+template <int D, int QPW, int NW, int NST, int MINB, bool FUSED, int BIAS, bool ROTV>
+__global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
+    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
+    const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
+    const float* __restrict__ theta, const float* __restrict__ alibi,
+    const float* __restrict__ gate2, uint16_t* __restrict__ o, float* __restrict__ lse, int L,
+    int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk, float qscale, int paired) {
+  constexpr int STAGE = BN * D * 2 + D * BN * 2 + (((BIAS & 2) != 0) ? BN * 4 : 0);  // as in attn_tile
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
+  constexpr bool SPREAD = (BIAS != 0) && !FUSED;
+  constexpr bool PAIRABLE = QPW == 64 && NW == 8 && BIAS == 0 && !FUSED;
+  const int per = (total_tiles + 7) / 8;
+  if (PAIRABLE && paired) {
+    const int x = (int)(blockIdx.x % 8), c = (int)(blockIdx.x / 8);
+    attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(x * per + c, smem, qr, kr, vt, kmax, theta,
+                                                        alibi, gate2, o, lse, L, Lp, H, Hphi, nqt,
+                                                        total_tiles, rot_qk, qscale);
+    __syncthreads();  // every wave is done with the LDS ring before it is refilled
+    attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(x * per + per - 1 - c, smem, qr, kr, vt,
+                                                        kmax, theta, alibi, gate2, o, lse, L, Lp, H,
+                                                        Hphi, nqt, total_tiles, rot_qk, qscale);
+    return;
+  }
+  const int logical = SPREAD ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(logical, smem, qr, kr, vt, kmax, theta, alibi,
+                                                      gate2, o, lse, L, Lp, H, Hphi, nqt,
+                                                      total_tiles, rot_qk, qscale);
+}
+
 template <int D, int QPW, int NW, int NST, int MINB, bool FUSED>
 hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                            const uint16_t* vt, const float* kmax, const float* theta,
@@ -588,15 +621,16 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
   constexpr int BM = QPW * NW;
   const int nqt = (g.L + BM - 1) / BM;
   const int total = g.B * g.H * nqt;
-  const int grid = ((total + 7) / 8) * 8;
   const bool rv = g.flags & ARP_ROTATE_V;
   const int bias = ((g.flags & ARP_ALIBI) ? 1 : 0) | ((g.flags & ARP_FORGET_GATE) ? 2 : 0);
+  const int paired = (QPW == 64 && NW == 8 && !FUSED && bias == 0 && total % 16 == 0) ? 1 : 0;
+  const int grid = paired ? total / 2 : ((total + 7) / 8) * 8;
   const int rqk = (g.flags & ARP_ROTATE_QK) ? 1 : 0;
   const float qscale = g.scale * LOG2E;
 #define ARP_BF16_LAUNCH(A, R)                                                                  \
   hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, MINB, FUSED, A, R>), dim3(grid),      \
                      dim3(NW * 64), 0, stream, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,   \
-                     g.L, g.Lp, g.H, g.Hphi, nqt, total, rqk, qscale)
+                     g.L, g.Lp, g.H, g.Hphi, nqt, total, rqk, qscale, paired)
 #define ARP_BF16_LAUNCH_R(A) \
   do {                       \
     if (rv) ARP_BF16_LAUNCH(A, true); else ARP_BF16_LAUNCH(A, false); \
