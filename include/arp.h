@@ -226,10 +226,12 @@ arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, co
                           void* o, float* lse, void* scan_state, size_t scan_state_bytes,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of the backward workspace for desc (bf16 only; 0 otherwise): the bf16
- * operands of the gradient kernels (rotated q scaled by scale*log2(e), k, v
- * and the rotated upstream gradient, row-major and transposed), per-row
- * statistics, and the reverse scan's chunk totals.  No initialisation needed. */
+/* Bytes of the backward workspace for desc (0 for an invalid desc or fp32
+ * with forget gates): the operands of the gradient kernels (rotated q scaled
+ * by scale*log2(e), k, v and the rotated upstream gradient; bf16 row-major
+ * and transposed, or fp32 row-major for fp32 I/O), per-row statistics, the
+ * reverse scan's chunk totals and, with forget gates, the gate prefix and
+ * the dS sums.  No initialisation needed. */
 size_t arp_backward_workspace_bytes(const arp_desc* desc);
 
 /* Gradients: given the forward's inputs, theta, o and lse (from
