@@ -184,6 +184,7 @@ def test_million_token_sequence_sampled_rows(alibi):
 
 @pytest.mark.parametrize("name,heads,L,rotate_v", [("train_1k", 16, 16400, False),
                                                    ("train_1k", 16, 16400, True),
+                                                   ("train_1k", 17, 16896, True),
                                                    ("rope_8k_d128", 32, 8200, False)])
 def test_workgroup_shapes_agree_on_a_ragged_length(name, heads, L, rotate_v):
     """The d=64 attention takes 512-query workgroups (8 waves x 64 queries)
@@ -193,7 +194,10 @@ def test_workgroup_shapes_agree_on_a_ragged_length(name, heads, L, rotate_v):
     16-key tail; 528 workgroups of 512) take the first; three of those heads
     alone take the second.  Every row is computed the same way in both, so
     the three heads must agree bit for bit, log-sum-exp too; the big run is
-    also checked against the oracle on sampled rows.  At d=128 the shapes are
+    also checked against the oracle on sampled rows.  The 512-query shape
+    pairs the c-th longest and c-th shortest query tiles in one workgroup
+    when the tile count is a multiple of 16 (16 x 33 = 528 tiles); 17 heads
+    at 16896 tokens make 561 tiles, the unpaired launch.  At d=128 the shapes are
     8 waves x 32 queries (unbiased grids of at least four 256-query
     workgroups per CU: 32 heads at 8200 tokens make 1056) and 4 waves x 32."""
     w = wl.make(name, batch=1, heads=heads, seqlen=L)
