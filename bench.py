@@ -91,10 +91,12 @@ def _strided_rows(w, stride: int, offset: int = 0) -> np.ndarray:
     return np.concatenate([bh * L + i for bh in range(w.batch * w.heads)])
 
 
-def run_cpu_baseline(w, flags: int, alibi, target_s: float) -> dict:
+def run_cpu_baseline(w, flags: int, alibi, target_s: float, got=None) -> dict:
     """Time the oracle on strided query rows.  Its cost is a fixed part per
     head (angle scan and key/value rotation) plus a part per row, so two
-    calibration runs fix both before the timed sample is sized."""
+    calibration runs fix both before the timed sample is sized.  got (the
+    GPU step's output rows, fp32 [B*H*L, d]) is compared with the oracle's
+    rows of the timed sample: the step's parity at full size."""
     import oracle
 
     nthreads = min(len(os.sched_getaffinity(0)), 16)
@@ -119,7 +121,7 @@ def run_cpu_baseline(w, flags: int, alibi, target_s: float) -> dict:
     reps, dt = 0, 0.0
     while reps == 0 or (dt < min(10.0, target_s) and reps < 8):
         t0 = time.perf_counter()
-        prob.rows(rows, nthreads)
+        ref = prob.rows(rows, nthreads)
         dt += time.perf_counter() - t0
         reps += 1
     per = dt / reps
@@ -130,7 +132,18 @@ def run_cpu_baseline(w, flags: int, alibi, target_s: float) -> dict:
             "sample": f"{rows.size} query rows ({which} of each of the {w.batch * w.heads} heads, "
                       f"with the angle scan and key/value rotation of each head), fp64, "
                       f"{reps} run(s), {dt:.1f} s in all",
-            "seconds": round(per, 3), "tokens_per_s": rows.size / per}
+            "seconds": round(per, 3), "tokens_per_s": rows.size / per,
+            "parity": None if got is None else _parity(got[rows], ref,
+                                                       2e-2 if w.dtype == "bf16" else 1e-4)}
+
+
+def _parity(got, ref, bar: float) -> dict:
+    """The GPU rows against the oracle's: max |error| (the tests' bar beside
+    it) and the rms error relative to the rms output."""
+    err = np.abs(got.astype(np.float64) - ref)
+    return {"rows": int(ref.shape[0]), "max_abs_err": float(err.max()),
+            "rms_err_over_rms": float(np.sqrt((err ** 2).mean() / max((ref ** 2).mean(), 1e-300))),
+            "bar_max_abs": bar, "within_bar": bool(err.max() <= bar)}
 
 
 def scan_gate(binding, torch, dev, steps: int = 30) -> dict:
@@ -590,7 +603,8 @@ def main():
         import oracle
         of = (oracle.ROTATE_QK | (oracle.ROTATE_V if w.rotate_v else 0) |
               (oracle.ALIBI if w.use_alibi else 0))
-        result["cpu_baseline"] = run_cpu_baseline(w, of, w.alibi, args.cpu_seconds)
+        got = o.float().cpu().numpy().reshape(-1, w.head_dim)
+        result["cpu_baseline"] = run_cpu_baseline(w, of, w.alibi, args.cpu_seconds, got)
     print(json.dumps(result), flush=True)
 
 
