@@ -294,19 +294,27 @@ __device__ __forceinline__ void attn_tile(
     for (int r = 0; r < 16; ++r) cneg[qb][r] = gq[qb];
   }
 
-  // Biased walk: a bound on the logits of the tile in flight (tb), the
-  // largest key norm of the wave's tiles (kglob), and per-wave "done" flags,
-  // kept per step parity so that a flag set in step n is read in step n+1
-  // after the barrier and no wave writes that parity before every wave has
-  // read it.  A wave with no query below L is done from the start.
+  // The largest key norm of the wave's tiles (kglob).  Unbiased walk: once
+  // |q~_i| kglob lies within TAU of every row's running maximum (after the
+  // first tile, on typical inputs), no later tile can need a rescale, since
+  // the running maximum never falls: the per-tile bound (a load of that tile's
+  // norm, waited on between Q K^T and the softmax) is then skipped for good.
+  // Biased walk: a bound on the logits of the tile in flight (tb), and
+  // per-wave "done" flags, kept per step parity so that a flag set in step n
+  // is read in step n+1 after the barrier and no wave writes that parity
+  // before every wave has read it.  A wave with no query below L is done from
+  // the start.
   float tb[QB];
   float kglob = 0.f;
+  bool nb_safe = false;  // wave-uniform
   __shared__ int wdone[2][DESC ? NW : 1];
   bool wave_done = false;
-  if constexpr (DESC) {
+  if constexpr (!FUSED) {
     for (int c = lane; c <= last_w; c += 64) kglob = fmaxf(kglob, kmax_bh[c]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) kglob = fmaxf(kglob, __shfl_xor(kglob, off));
+  }
+  if constexpr (DESC) {
     wave_done = last_w < 0;
     if (lane == 0) wdone[0][wave] = wdone[1][wave] = wave_done ? 1 : 0;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -381,9 +389,11 @@ __device__ __forceinline__ void attn_tile(
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) check |= (tb[qb] > mrun[qb] + TAU);
     } else if constexpr (!FUSED) {
-      const float km = kmax_bh[t];
+      if (!nb_safe) {
+        const float km = kmax_bh[t];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) check |= (qn[qb] * km > mrun[qb] + TAU);
+        for (int qb = 0; qb < QB; ++qb) check |= (qn[qb] * km > mrun[qb] + TAU);
+      }
     }
     if (__any(check)) {
     float mx[QB];
@@ -420,6 +430,12 @@ __device__ __forceinline__ void attn_tile(
 #pragma unroll
         for (int r = 0; r < 16; ++r) cneg[qb][r] = FORGET ? gq[qb] - mrun[qb] : -mrun[qb];
       }
+    }
+    if constexpr (!DESC && !FUSED) {
+      bool ok = true;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) ok &= (qn[qb] * kglob <= mrun[qb] + TAU);
+      nb_safe = __all(ok);
     }
     }
 

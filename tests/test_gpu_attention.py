@@ -109,6 +109,32 @@ def test_large_logits_bf16():
     assert max_abs <= 2e-2 * max(1.0, float(np.abs(want).max()))
 
 
+@pytest.mark.parametrize("heads,L", [(2, 2000), (16, 16384)])
+def test_growing_key_norms_rescale_on_late_tiles(heads, L):
+    """Keys whose norm grows along the sequence (x1 at key 0 to x12 at the
+    end) and queries scaled by 16: each row's largest logits sit near its own
+    position, so the running maximum must be raised on late key tiles, and a
+    bound from the largest key norm never clears the rescale threshold after
+    the first tile -- the per-tile bound has to keep running.  2 heads at 2000
+    tokens take the 128-query workgroups; 16 heads at 16384 the 512-query ones
+    (sampled rows)."""
+    w = wl.make("train_1k", batch=1, heads=heads, seqlen=L)
+    grow = (1.0 + 11.0 * np.arange(L, dtype=np.float32) / L)[None, None, :, None]
+    w.k = wl.to_bf16_bits(wl.from_bf16_bits(w.k) * grow)
+    w.q = wl.to_bf16_bits(wl.from_bf16_bits(w.q) * np.float32(16.0))
+    got, _ = run_forward(w, rotate_v=True)
+    prob = oracle_problem(w, rotate_v=True)
+    if heads * L > 100_000:
+        rows = sample_rows(w, per_head=8)
+        got, want = got.reshape(-1, w.head_dim)[rows], prob.rows(rows)
+    else:
+        want = prob.output()
+    max_abs = float(np.abs(got - want).max())
+    say(f"[gpu] growing key norms H={heads} L={L}: max_abs={max_abs:.3e}")
+    assert np.all(np.isfinite(got))
+    assert max_abs <= 2e-2 * max(1.0, float(np.abs(want).max()))
+
+
 @pytest.mark.parametrize("name", list(wl.SPECS))
 def test_full_size_workload_sampled_rows(name):
     w = wl.make(name)
