@@ -136,6 +136,69 @@ def _require_gpu(*ts) -> None:
             _ptr(t)
 
 
+# ---- argument validation --------------------------------------------------
+# The C ABI sees plain pointers and cannot tell a buffer's size, so a tensor of
+# the wrong shape or dtype would become an out-of-bounds device access.  Every
+# call below checks its tensors against the descriptor first and raises
+# ValueError (shape, size) or TypeError (dtype) before anything is launched.
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _expect(t: torch.Tensor | None, name: str, shape, dtype) -> None:
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _io_dtype(desc: Desc):
+    return torch.float32 if desc.dtype == DTYPE_F32 else torch.bfloat16
+
+
+def _angle_heads(desc: Desc) -> int:
+    return 1 if desc.flags & PHI_SHARED_HEADS else desc.heads
+
+
+def _check_qkv(desc: Desc, **ts) -> None:
+    shape = (desc.batch, desc.heads, desc.seqlen, desc.head_dim)
+    for name, t in ts.items():
+        _expect(t, name, shape, _io_dtype(desc))
+
+
+def _check_angles(desc: Desc, **ts) -> None:
+    shape = (desc.batch, _angle_heads(desc), desc.seqlen, desc.head_dim // 2)
+    for name, t in ts.items():
+        _expect(t, name, shape, torch.float32)
+
+
+def _check_rows(desc: Desc, **ts) -> None:
+    """Per-row fp32 tensors [B, H, L] (lse, log gates and their gradient)."""
+    for name, t in ts.items():
+        _expect(t, name, (desc.batch, desc.heads, desc.seqlen), torch.float32)
+
+
+def _check_alibi(desc: Desc, alibi) -> None:
+    if alibi is not None:
+        _expect(alibi, "alibi", (desc.heads,), torch.float32)
+
+
+def _check_buffer(t: torch.Tensor | None, name: str, need: int) -> None:
+    if t is not None and _nbytes(t) < need:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes, the call needs {need}")
+
+
+def _check_phi_heads(q: torch.Tensor, phi: torch.Tensor) -> None:
+    if q.dim() != 4 or phi.dim() != 4:
+        raise ValueError("q must be [B, H, L, d] and phi [B, Hphi, L, d/2]")
+    if phi.shape[1] not in (1, q.shape[1]):
+        raise ValueError(f"phi has {phi.shape[1]} angle heads; expected 1 (shared) or "
+                         f"{q.shape[1]} (one per head)")
+
+
 def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -197,11 +260,13 @@ def workspace(desc: Desc, device: torch.device) -> torch.Tensor:
 
 def angle_scan(phi: torch.Tensor, desc: Desc, theta: torch.Tensor | None = None,
                state: torch.Tensor | None = None) -> torch.Tensor:
+    _check_angles(desc, phi=phi, theta=theta)
+    _check_buffer(state, "state", scan_state_bytes(desc))
     _require_gpu(phi, theta, state)
     theta = torch.empty_like(phi) if theta is None else theta
     state = scan_state(desc, phi.device) if state is None else state
     _check("arp_angle_scan", lib().arp_angle_scan(ctypes.byref(desc), _ptr(phi), _ptr(theta),
-                                                  _ptr(state), state.numel(), _stream(phi.device)))
+                                                  _ptr(state), _nbytes(state), _stream(phi.device)))
     return theta
 
 
@@ -215,13 +280,16 @@ def angle_scan_random(desc: Desc, seed: int, step: int, bound: torch.Tensor,
                       state: torch.Tensor | None = None) -> torch.Tensor:
     """Accumulated angles of the random variant, drawn inside the scan; bound is
     float32 [angle heads, d/2] on the device."""
+    _expect(bound, "bound", (_angle_heads(desc), desc.head_dim // 2), torch.float32)
+    _check_angles(desc, theta=theta)
+    _check_buffer(state, "state", scan_state_bytes(desc))
     _require_gpu(bound, theta, state)
     dev = bound.device
     theta = torch.empty(_phi_shape(desc), dtype=torch.float32, device=dev) if theta is None else theta
     state = scan_state(desc, dev) if state is None else state
     _check("arp_angle_scan_random",
            lib().arp_angle_scan_random(ctypes.byref(desc), seed, step, _ptr(bound), _ptr(theta),
-                                       _ptr(state), state.numel(), _stream(dev)))
+                                       _ptr(state), _nbytes(state), _stream(dev)))
     return theta
 
 
@@ -230,15 +298,19 @@ def angle_scan_tokens(desc: Desc, tokens: torch.Tensor, table: torch.Tensor,
                       state: torch.Tensor | None = None) -> torch.Tensor:
     """Accumulated angles of a per-token angle table; tokens int32 [B, L], table
     float32 [vocab, angle heads, d/2], both on the device."""
+    _expect(tokens, "tokens", (desc.batch, desc.seqlen), torch.int32)
+    if table.dim() != 3 or table.shape[0] < 1:
+        raise ValueError("table must be [vocab, angle heads, d/2] with vocab >= 1")
+    _expect(table, "table", (table.shape[0], _angle_heads(desc), desc.head_dim // 2), torch.float32)
+    _check_angles(desc, theta=theta)
+    _check_buffer(state, "state", scan_state_bytes(desc))
     _require_gpu(tokens, table, theta, state)
-    if tokens.dtype != torch.int32:
-        raise TypeError("tokens must be int32")
     dev = table.device
     theta = torch.empty(_phi_shape(desc), dtype=torch.float32, device=dev) if theta is None else theta
     state = scan_state(desc, dev) if state is None else state
     _check("arp_angle_scan_tokens",
            lib().arp_angle_scan_tokens(ctypes.byref(desc), _ptr(tokens), _ptr(table),
-                                       table.shape[0], _ptr(theta), _ptr(state), state.numel(),
+                                       table.shape[0], _ptr(theta), _ptr(state), _nbytes(state),
                                        _stream(dev)))
     return theta
 
@@ -246,6 +318,8 @@ def angle_scan_tokens(desc: Desc, tokens: torch.Tensor, table: torch.Tensor,
 def angle_scan_const(desc: Desc, freq: torch.Tensor, theta: torch.Tensor | None = None) -> torch.Tensor:
     """Accumulated angles of constant per-pair steps (closed form); freq float32
     [angle heads, d/2]."""
+    _expect(freq, "freq", (_angle_heads(desc), desc.head_dim // 2), torch.float32)
+    _check_angles(desc, theta=theta)
     _require_gpu(freq, theta)
     dev = freq.device
     theta = torch.empty(_phi_shape(desc), dtype=torch.float32, device=dev) if theta is None else theta
@@ -257,6 +331,8 @@ def angle_scan_const(desc: Desc, freq: torch.Tensor, theta: torch.Tensor | None 
 def random_phi(desc: Desc, seed: int, step: int, bound: torch.Tensor,
                phi: torch.Tensor | None = None) -> torch.Tensor:
     """The random variant's step angles written out (float32 [B, angle heads, L, d/2])."""
+    _expect(bound, "bound", (_angle_heads(desc), desc.head_dim // 2), torch.float32)
+    _check_angles(desc, phi=phi)
     _require_gpu(bound, phi)
     dev = bound.device
     phi = torch.empty(_phi_shape(desc), dtype=torch.float32, device=dev) if phi is None else phi
@@ -266,29 +342,40 @@ def random_phi(desc: Desc, seed: int, step: int, bound: torch.Tensor,
 
 
 def rotate_qkv(q, k, v, theta, desc: Desc, ws: torch.Tensor | None = None) -> torch.Tensor:
+    _check_qkv(desc, q=q, k=k, v=v)
+    _check_angles(desc, theta=theta)
+    _check_buffer(ws, "ws", workspace_bytes(desc))
     _require_gpu(q, k, v, theta, ws)
     ws = workspace(desc, q.device) if ws is None else ws
     _check("arp_rotate_qkv", lib().arp_rotate_qkv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
-                                                  _ptr(theta), _ptr(ws), ws.numel(),
+                                                  _ptr(theta), _ptr(ws), _nbytes(ws),
                                                   _stream(q.device)))
     return ws
 
 
 def attn_rotated(theta, alibi, out, desc: Desc, ws: torch.Tensor) -> torch.Tensor:
+    _check_angles(desc, theta=theta)
+    _check_alibi(desc, alibi)
+    _check_qkv(desc, out=out)
+    _check_buffer(ws, "ws", workspace_bytes(desc))
     _require_gpu(theta, alibi, out, ws)
     _check("arp_attn_rotated", lib().arp_attn_rotated(ctypes.byref(desc), _ptr(theta), _ptr(alibi),
-                                                      _ptr(out), _ptr(ws), ws.numel(),
+                                                      _ptr(out), _ptr(ws), _nbytes(ws),
                                                       _stream(out.device)))
     return out
 
 
 def attn_fwd(q, k, v, theta, desc: Desc, alibi=None, out=None, ws=None) -> torch.Tensor:
+    _check_qkv(desc, q=q, k=k, v=v, out=out)
+    _check_angles(desc, theta=theta)
+    _check_alibi(desc, alibi)
+    _check_buffer(ws, "ws", workspace_bytes(desc))
     _require_gpu(q, k, v, theta, alibi, out, ws)
     out = torch.empty_like(q) if out is None else out
     ws = workspace(desc, q.device) if ws is None else ws
     _check("arp_attn_fwd", lib().arp_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                               _ptr(theta), _ptr(alibi), _ptr(out), _ptr(ws),
-                                              ws.numel(), _stream(q.device)))
+                                              _nbytes(ws), _stream(q.device)))
     return out
 
 
@@ -298,23 +385,32 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.Tensor
             out: torch.Tensor | None = None, theta: torch.Tensor | None = None,
             state: torch.Tensor | None = None, ws: torch.Tensor | None = None):
     """(q, k, v, phi, flags) -> (o, theta): the whole forward pass on the GPU."""
-    _require_gpu(q, k, v, phi, alibi, out, theta, state, ws)
+    _check_phi_heads(q, phi)
     flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi is not None,
                       shared_phi=phi.shape[1] == 1 and q.shape[1] != 1, exclusive=exclusive,
                       fused=fused)
     desc = desc_for(q, flags, scale)
+    _check_qkv(desc, q=q, k=k, v=v, out=out)
+    _check_angles(desc, phi=phi, theta=theta)
+    _check_alibi(desc, alibi)
+    _check_buffer(state, "state", scan_state_bytes(desc))
+    _check_buffer(ws, "ws", workspace_bytes(desc))
+    _require_gpu(q, k, v, phi, alibi, out, theta, state, ws)
     out = torch.empty_like(q) if out is None else out
     theta = torch.empty_like(phi) if theta is None else theta
     state = scan_state(desc, q.device) if state is None else state
     ws = workspace(desc, q.device) if ws is None else ws
     _check("arp_forward", lib().arp_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                             _ptr(phi), _ptr(alibi), _ptr(theta), _ptr(out),
-                                            _ptr(state), state.numel(), _ptr(ws), ws.numel(),
+                                            _ptr(state), _nbytes(state), _ptr(ws), _nbytes(ws),
                                             _stream(q.device)))
     return out, theta
 
 
 def rotate(x: torch.Tensor, theta: torch.Tensor, desc: Desc, inverse: bool = False) -> torch.Tensor:
+    _check_qkv(desc, x=x)
+    _check_angles(desc, theta=theta)
+    _require_gpu(x, theta)
     out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     _check("arp_rotate", lib().arp_rotate(ctypes.byref(desc), _ptr(x), _ptr(theta), _ptr(out),
                                           int(inverse), _stream(x.device)))
@@ -327,10 +423,14 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.
                   exclusive: bool = False):
     """Forward pass that also returns the per-row base-2 log-sum-exp (bf16,
     pre-rotation path): (o, theta, lse, desc), everything the backward needs."""
-    _require_gpu(q, k, v, phi, alibi)
+    _check_phi_heads(q, phi)
     flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi is not None,
                       shared_phi=phi.shape[1] == 1 and q.shape[1] != 1, exclusive=exclusive)
     desc = desc_for(q, flags, scale)
+    _check_qkv(desc, q=q, k=k, v=v)
+    _check_angles(desc, phi=phi)
+    _check_alibi(desc, alibi)
+    _require_gpu(q, k, v, phi, alibi)
     out = torch.empty_like(q)
     theta = torch.empty_like(phi)
     B, H, L, _ = q.shape
@@ -339,7 +439,7 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.
     ws = workspace(desc, q.device)
     _check("arp_forward_train", lib().arp_forward_train(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(phi), _ptr(alibi), _ptr(theta),
-        _ptr(out), _ptr(lse), _ptr(state), state.numel(), _ptr(ws), ws.numel(),
+        _ptr(out), _ptr(lse), _ptr(state), _nbytes(state), _ptr(ws), _nbytes(ws),
         _stream(q.device)))
     return out, theta, lse, desc
 
@@ -363,9 +463,18 @@ def backward_workspace(desc: Desc, device: torch.device) -> torch.Tensor:
     return ws
 
 
+def _check_backward_args(desc: Desc, q, k, v, phi, theta, o, lse, dout, alibi, logf, ws) -> None:
+    _check_qkv(desc, q=q, k=k, v=v, o=o, dout=dout)
+    _check_angles(desc, phi=phi, theta=theta)
+    _check_rows(desc, lse=lse, logf=logf)
+    _check_alibi(desc, alibi)
+    _check_buffer(ws, "ws", backward_workspace_bytes(desc))
+
+
 def backward(desc: Desc, q, k, v, phi, theta, o, lse, dout, alibi=None, ws=None):
     """Gradients for dout = dL/do: (dq, dk, dv, dphi, dtheta), with dtheta the
     per-head dL/dTheta ([B, H, L, d/2])."""
+    _check_backward_args(desc, q, k, v, phi, theta, o, lse, dout, alibi, None, ws)
     _require_gpu(q, k, v, phi, theta, o, lse, dout, alibi, ws)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     B, H, L, d = q.shape
@@ -375,7 +484,7 @@ def backward(desc: Desc, q, k, v, phi, theta, o, lse, dout, alibi=None, ws=None)
     _check("arp_backward", lib().arp_backward(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(alibi), _ptr(o),
         _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtheta), _ptr(dphi),
-        _ptr(ws), ws.numel(), _stream(q.device)))
+        _ptr(ws), _nbytes(ws), _stream(q.device)))
     return dq, dk, dv, dphi, dtheta
 
 
@@ -383,6 +492,7 @@ def backward_ex(desc: Desc, q, k, v, phi, theta, o, lse, dout, alibi=None, logf=
     """arp_backward_ex: backward() plus, with the forget gates (desc has
     FORGET_GATE; logf [B, H, L] as given to forward_ex), dlogf = dL/d(log f)
     [B, H, L].  Returns (dq, dk, dv, dphi, dtheta, dlogf or None)."""
+    _check_backward_args(desc, q, k, v, phi, theta, o, lse, dout, alibi, logf, ws)
     _require_gpu(q, k, v, phi, theta, o, lse, dout, alibi, logf, ws)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     B, H, L, d = q.shape
@@ -393,7 +503,7 @@ def backward_ex(desc: Desc, q, k, v, phi, theta, o, lse, dout, alibi=None, logf=
     _check("arp_backward_ex", lib().arp_backward_ex(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(alibi), _ptr(logf),
         _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtheta), _ptr(dphi),
-        _ptr(dlogf), _ptr(ws), ws.numel(), _stream(q.device)))
+        _ptr(dlogf), _ptr(ws), _nbytes(ws), _stream(q.device)))
     return dq, dk, dv, dphi, dtheta, dlogf
 
 
@@ -427,8 +537,22 @@ class DecodeCache:
         """Cache rows [0, len) and the state after the len prompt tokens
         (k, v [B, H, len, d]; phi, theta [B, Hphi, len, d/2]; with gates logf
         [B, H, len]); no arguments: an empty prompt (state reset)."""
-        _require_gpu(k, v, phi, theta, logf)
         n = 0 if k is None else int(k.shape[2])
+        d = self.desc
+        if n > d.seqlen:
+            raise ValueError(f"a prompt of {n} tokens does not fit a cache of {d.seqlen}")
+        if n > 0:
+            io = (d.batch, d.heads, n, d.head_dim)
+            _expect(k, "k", io, torch.bfloat16)
+            _expect(v, "v", io, torch.bfloat16)
+            ang = (d.batch, _angle_heads(d), n, d.head_dim // 2)
+            _expect(phi, "phi", ang, torch.float32)
+            _expect(theta, "theta", ang, torch.float32)
+            if self.forget:
+                if logf is None:
+                    raise ValueError("a gated cache needs the prompt's logf")
+                _expect(logf, "logf", (d.batch, d.heads, n), torch.float32)
+        _require_gpu(k, v, phi, theta, logf)
         if self.forget:
             _check("arp_decode_prefill_ex", lib().arp_decode_prefill_ex(
                 ctypes.byref(self.desc), n, _ptr(k), _ptr(v), _ptr(phi), _ptr(theta), _ptr(logf),
@@ -443,6 +567,18 @@ class DecodeCache:
         """One token at position pos: q, k, v [B, H, d]; phi [B, Hphi, d/2];
         with gates logf [B, H].  Returns o [B, H, d]; self.theta holds the
         token's angles."""
+        d = self.desc
+        if not 0 <= int(pos) < d.seqlen:
+            raise ValueError(f"position {pos} outside the cache of {d.seqlen} tokens")
+        tok = (d.batch, d.heads, d.head_dim)
+        for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+            _expect(t, name, tok, torch.bfloat16)
+        _expect(phi, "phi", (d.batch, _angle_heads(d), d.head_dim // 2), torch.float32)
+        _check_alibi(d, alibi)
+        if self.forget:
+            if logf is None:
+                raise ValueError("a gated cache needs the token's logf")
+            _expect(logf, "logf", (d.batch, d.heads), torch.float32)
         _require_gpu(q, k, v, phi, alibi, out, logf)
         out = torch.empty_like(q) if out is None else out
         if self.forget:
@@ -450,12 +586,12 @@ class DecodeCache:
                 ctypes.byref(self.desc), int(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(phi),
                 _ptr(alibi), _ptr(logf), _ptr(self.state), _ptr(self.theta), _ptr(self.kcache),
                 _ptr(self.vcache), _ptr(self.gcache), _ptr(self.gstate), _ptr(out), _ptr(self.ws),
-                self.ws.numel(), _stream(self.device)))
+                _nbytes(self.ws), _stream(self.device)))
             return out
         _check("arp_decode_step", lib().arp_decode_step(
             ctypes.byref(self.desc), int(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(phi), _ptr(alibi),
             _ptr(self.state), _ptr(self.theta), _ptr(self.kcache), _ptr(self.vcache), _ptr(out),
-            _ptr(self.ws), self.ws.numel(), _stream(self.device)))
+            _ptr(self.ws), _nbytes(self.ws), _stream(self.device)))
         return out
 
 
@@ -466,11 +602,16 @@ def forward_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.Ten
     """The forward with every option (arp_forward_ex): logf [B, H, L] log forget
     gates (the gate bias is on when given), with_lse also returns the per-row
     base-2 log-sum-exp.  Returns (o, theta, lse or None)."""
-    _require_gpu(q, k, v, phi, alibi, logf)
+    _check_phi_heads(q, phi)
     flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi is not None,
                       shared_phi=phi.shape[1] == 1 and q.shape[1] != 1, exclusive=exclusive,
                       forget=logf is not None)
     desc = desc_for(q, flags, scale)
+    _check_qkv(desc, q=q, k=k, v=v)
+    _check_angles(desc, phi=phi)
+    _check_alibi(desc, alibi)
+    _check_rows(desc, logf=logf)
+    _require_gpu(q, k, v, phi, alibi, logf)
     out = torch.empty_like(q)
     theta = torch.empty_like(phi)
     B, H, L, _ = q.shape
@@ -479,6 +620,6 @@ def forward_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.Ten
     ws = workspace(desc, q.device)
     _check("arp_forward_ex", lib().arp_forward_ex(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(phi), _ptr(alibi), _ptr(logf),
-        _ptr(theta), _ptr(out), _ptr(lse), _ptr(state), state.numel(), _ptr(ws), ws.numel(),
+        _ptr(theta), _ptr(out), _ptr(lse), _ptr(state), _nbytes(state), _ptr(ws), _nbytes(ws),
         _stream(q.device)))
     return out, theta, lse

@@ -136,7 +136,8 @@ const char* arp_status_string(int status) {
     case ARP_OK: return "ok";
     case ARP_ERR_INVALID_ARG: return "invalid argument";
     case ARP_ERR_UNSUPPORTED: return "unsupported configuration";
-    case ARP_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case ARP_ERR_ALIGNMENT:
+      return "pointer misaligned (tensors: 16 bytes; scan state and workspaces: 256 bytes)";
     case ARP_ERR_WORKSPACE: return "workspace missing or too small";
     case ARP_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";

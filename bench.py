@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--clock-warmup-s", type=float, default=1.0,
+                   help="fixed untimed phase of whole steps run before the --warmup steps, "
+                        "so that the timed steps see the clocks the GPU holds under this load")
     p.add_argument("--workload", default="extrap_16k")
     p.add_argument("--fused", action="store_true", help="rotate k/v inside the attention kernel")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -99,7 +102,7 @@ def run_cpu_baseline(w, flags: int, alibi, target_s: float, got=None) -> dict:
     rows of the timed sample: the step's parity at full size."""
     import oracle
 
-    nthreads = min(len(os.sched_getaffinity(0)), 16)
+    nthreads = host_threads()
     prob = oracle.Problem(w.q, w.k, w.v, w.phi, flags, alibi=alibi)
     samples = []
     for stride in (2048, 512):
@@ -129,12 +132,60 @@ def run_cpu_baseline(w, flags: int, alibi, target_s: float, got=None) -> dict:
     flops = float(4.0 * w.head_dim * (i + 1).sum())
     which = "every query row" if stride == 1 else f"every {stride}-th query row"
     return {"value": flops / per / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
             "sample": f"{rows.size} query rows ({which} of each of the {w.batch * w.heads} heads, "
                       f"with the angle scan and key/value rotation of each head), fp64, "
                       f"{reps} run(s), {dt:.1f} s in all",
             "seconds": round(per, 3), "tokens_per_s": rows.size / per,
             "parity": None if got is None else _parity(got[rows], ref,
                                                        2e-2 if w.dtype == "bf16" else 1e-4)}
+
+
+def host_threads() -> int:
+    """Threads for the oracle: the host's CPU share as the environment states it
+    (OMP_NUM_THREADS, which the GPU hosts set to the share one GPU's jobs may
+    use), else every core this process may run on."""
+    aff = len(os.sched_getaffinity(0))
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        share = 0
+    return min(aff, share) if share > 0 else aff
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_cpu_single_thread(target_s: float = 4.0) -> dict:
+    """The oracle on one thread, on strided query rows of the small decoder
+    training shape (8 x 8 heads, 1024 tokens, d=64, rotation of q and k): a
+    per-core reference next to the multi-threaded baseline."""
+    import oracle
+    from accumulated_rotation_positional_amd import workloads as wl
+    w = wl.make("train_1k")
+    prob = oracle.Problem(w.q, w.k, w.v, w.phi, oracle.ROTATE_QK)
+    rows = _strided_rows(w, 64, 3)
+    t0 = time.perf_counter()
+    prob.rows(rows, 1)
+    dt = time.perf_counter() - t0
+    stride = int(max(1, min(64, round(64 * dt / target_s))))
+    rows = _strided_rows(w, stride, 3)
+    t0 = time.perf_counter()
+    prob.rows(rows, 1)
+    dt = time.perf_counter() - t0
+    flops = float(4.0 * w.head_dim * ((rows % w.seqlen) + 1).sum())
+    return {"workload": w.name, "value": flops / dt / 1e9, "unit": "GFLOP/s", "cores": 1,
+            "sample": f"{rows.size} query rows (every {stride}-th of each of the "
+                      f"{w.batch * w.heads} heads, with each head's angle scan and key/value "
+                      f"rotation), fp64, {dt:.1f} s", "tokens_per_s": rows.size / dt}
 
 
 def _parity(got, ref, bar: float) -> dict:
@@ -460,11 +511,15 @@ def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int =
                            "attn_fwd": round(attn_ms, 5)},
             "tflops_step": round(w.flops / (ms_step * 1e-3) / 1e12, 2),
             "tokens_per_s": round(w.batch * w.seqlen / (ms_step * 1e-3), 1),
-            "attn_tflops": round(attn_tf, 2),
-            "attn_frac_of_bf16_peak": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4) if not fused else None,
+            **({"attn_dense_equivalent_tflops": round(attn_tf, 2)} if w.use_alibi else
+               {"attn_tflops": round(attn_tf, 2),
+                "attn_frac_of_bf16_peak": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4)
+                if not fused else None}),
             "scan_gbs": round(scan_gbs, 1),
-            "note": ("the distance-bias walk skips key tiles whose probabilities are all exactly "
-                     "zero, so the attention rate exceeds the matrix-core work done")
+            "note": ("dense-equivalent: the algorithmic flops of every causal pair over the "
+                     "kernel time, while the distance-bias walk skips key tiles whose "
+                     "probabilities are all exactly zero; the matrix-core utilisation is "
+                     "the counted flops over the time (profiles/)")
             if w.use_alibi else None,
         }
         del q, k, v, phi, alibi, ws, state, theta, o
@@ -523,6 +578,18 @@ def main():
         if evs is not None:
             evs[n_ev].record(stream)
 
+    # Clock warm-up: an idle GPU starts below the clock it holds under a long
+    # matrix-core load (the attention kernel reads ~15% slower over the first
+    # few steps).  Whole steps are run for a fixed wall time, untimed and
+    # reported as their own field; the --warmup steps and the timed --steps
+    # steps follow unchanged.
+    warm_steps, t_warm = 0, time.perf_counter()
+    while time.perf_counter() - t_warm < args.clock_warmup_s:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        warm_steps += 20
+    t_warm = time.perf_counter() - t_warm
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -572,6 +639,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_warmup": {"seconds": round(t_warm, 3), "steps": warm_steps,
+                         "note": "untimed whole steps before the --warmup steps"},
         "ms_per_step": round(ms_step, 4),
         "wall_s_timed": round(t_wall, 4),
         "higher_is_better": True,
@@ -605,6 +674,7 @@ def main():
               (oracle.ALIBI if w.use_alibi else 0))
         got = o.float().cpu().numpy().reshape(-1, w.head_dim)
         result["cpu_baseline"] = run_cpu_baseline(w, of, w.alibi, args.cpu_seconds, got)
+        result["cpu_baseline"]["single_thread"] = run_cpu_single_thread()
     print(json.dumps(result), flush=True)
 
 

@@ -31,7 +31,9 @@
  *                   phi_heads = 1 with ARP_PHI_SHARED_HEADS, else heads
  *      alibi      : [heads] float32 slopes m_h (ARP_ALIBI only)
  *    Rotary pair p is elements (2p, 2p+1) of the last axis.
- *  - Every pointer must be 16-byte aligned.
+ *  - Every tensor pointer must be 16-byte aligned (token ids: 4 bytes); the
+ *    scan state and every workspace must be 256-byte aligned.  A misaligned
+ *    pointer returns ARP_ERR_ALIGNMENT with nothing launched.
  *  - stream is a hipStream_t (NULL: the default stream).  Work is enqueued
  *    asynchronously; nothing is synchronised; no host memory is touched.
  *  - The library allocates nothing.  It uses two caller-provided buffers:
@@ -64,7 +66,8 @@ typedef enum arp_status {
   ARP_OK = 0,
   ARP_ERR_INVALID_ARG = 1, /* null desc/pointer, bad size, odd head_dim, unknown flag or dtype */
   ARP_ERR_UNSUPPORTED = 2, /* well-formed but not built: head_dim other than 64 or 128 */
-  ARP_ERR_ALIGNMENT = 3,   /* a pointer is not 16-byte aligned */
+  ARP_ERR_ALIGNMENT = 3,   /* a tensor pointer is not 16-byte aligned, or a scan
+                              state or workspace not 256-byte aligned */
   ARP_ERR_WORKSPACE = 4,   /* scan state or workspace null or smaller than required */
   ARP_ERR_HIP = 5          /* a kernel launch failed */
 } arp_status;

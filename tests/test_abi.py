@@ -257,3 +257,117 @@ def test_gated_decode_validates_gate_buffers():
                                 None) == b.ERR_ALIGNMENT
     assert L.arp_decode_step_ex(by, 0, A, A, A, A, None, A, A, A, A, A, A, A, A, A, ws - 256,
                                 None) == b.ERR_WORKSPACE
+
+
+def test_scan_state_and_workspace_need_256_byte_alignment():
+    """Tensor pointers need 16 bytes; the scan state and the workspaces 256
+    (A + 16 is 16-byte aligned, not 256-byte aligned)."""
+    L = b.lib()
+    d = _desc()
+    by = ctypes.byref(d)
+    big = L.arp_workspace_bytes(by)
+    st = L.arp_scan_state_bytes(by)
+    assert A % 256 == 0
+    assert L.arp_angle_scan(by, A, A, A + 16, st, None) == b.ERR_ALIGNMENT
+    assert L.arp_attn_rotated(by, A, None, A, A + 16, big, None) == b.ERR_ALIGNMENT
+    assert L.arp_rotate_qkv(by, A, A, A, A, A + 16, big, None) == b.ERR_ALIGNMENT
+    assert L.arp_forward(by, A, A, A, A, None, A, A, A + 16, st, A, big, None) == b.ERR_ALIGNMENT
+    assert L.arp_forward(by, A, A, A, A, None, A, A, A, st, A + 16, big, None) == b.ERR_ALIGNMENT
+    bw = L.arp_backward_workspace_bytes(by)
+    assert L.arp_backward(by, *([A] * 13), A + 16, bw, None) == b.ERR_ALIGNMENT
+    msg = L.arp_status_string(b.ERR_ALIGNMENT).decode()
+    assert "16" in msg and "256" in msg
+
+
+# ---- the Python binding checks shapes, dtypes and buffer sizes before any call ----
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_rejects_mismatched_forward_arguments():
+    import torch
+    B, H, L, d = 1, 4, 16, 64
+    q = _cpu(B, H, L, d)
+    phi = _cpu(B, H, L, d // 2, dtype=torch.float32)
+    with pytest.raises(ValueError, match="k has shape"):
+        b.forward(q, _cpu(B, H, L + 1, d), q, phi)
+    with pytest.raises(TypeError, match="v has dtype"):
+        b.forward(q, q, _cpu(B, H, L, d, dtype=torch.float32), phi)
+    with pytest.raises(ValueError, match="angle heads"):
+        b.forward(q, q, q, _cpu(B, 3, L, d // 2, dtype=torch.float32))
+    with pytest.raises(ValueError, match="phi has shape"):
+        b.forward(q, q, q, _cpu(B, H, L, d // 4, dtype=torch.float32))
+    with pytest.raises(TypeError, match="phi has dtype"):
+        b.forward(q, q, q, _cpu(B, H, L, d // 2))
+    with pytest.raises(ValueError, match="alibi has shape"):
+        b.forward(q, q, q, phi, alibi=_cpu(H + 1, dtype=torch.float32))
+    with pytest.raises(TypeError, match="alibi has dtype"):
+        b.forward(q, q, q, phi, alibi=_cpu(H, dtype=torch.float64))
+    with pytest.raises(ValueError, match="out has shape"):
+        b.forward(q, q, q, phi, out=_cpu(B, H, L, d + 2))
+    with pytest.raises(ValueError, match="theta has shape"):
+        b.forward(q, q, q, phi, theta=_cpu(B, 1, L, d // 2, dtype=torch.float32))
+    with pytest.raises(ValueError, match="ws holds"):
+        b.forward(q, q, q, phi, ws=_cpu(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="state holds"):
+        b.forward(q, q, q, phi, state=_cpu(8, dtype=torch.uint8))
+    # a buffer of another dtype is sized by its bytes, not its element count
+    need = b.workspace_bytes(b.desc_for(q, b.flags_for()))
+    with pytest.raises(ValueError, match="ws holds"):
+        b.forward(q, q, q, phi, ws=_cpu(need // 8, dtype=torch.float32))
+    # well-formed CPU tensors pass validation and then fail the device check
+    with pytest.raises(ValueError, match="GPU"):
+        b.forward(q, q, q, phi)
+
+
+def test_binding_rejects_mismatched_gates_angles_and_gradients():
+    import torch
+    B, H, L, d = 2, 2, 8, 64
+    q = _cpu(B, H, L, d)
+    phi = _cpu(B, 1, L, d // 2, dtype=torch.float32)
+    with pytest.raises(ValueError, match="logf has shape"):
+        b.forward_ex(q, q, q, phi, logf=_cpu(B, H, L + 1, dtype=torch.float32))
+    with pytest.raises(TypeError, match="logf has dtype"):
+        b.forward_ex(q, q, q, phi, logf=_cpu(B, H, L))
+    desc = b.desc_for(q, b.flags_for(shared_phi=True))
+    with pytest.raises(ValueError, match="theta has shape"):
+        b.angle_scan(phi, desc, theta=_cpu(B, H, L, d // 2, dtype=torch.float32))
+    with pytest.raises(TypeError, match="tokens has dtype"):
+        b.angle_scan_tokens(desc, _cpu(B, L, dtype=torch.int64), _cpu(7, 1, d // 2, dtype=torch.float32))
+    with pytest.raises(ValueError, match="table has shape"):
+        b.angle_scan_tokens(desc, _cpu(B, L, dtype=torch.int32), _cpu(7, 2, d // 2, dtype=torch.float32))
+    with pytest.raises(ValueError, match="bound has shape"):
+        b.angle_scan_random(desc, 1, 0, _cpu(2, d // 2, dtype=torch.float32))
+    with pytest.raises(ValueError, match="freq has shape"):
+        b.angle_scan_const(desc, _cpu(1, d, dtype=torch.float32))
+    lse = _cpu(B, H, L, dtype=torch.float32)
+    with pytest.raises(ValueError, match="lse has shape"):
+        b.backward(desc, q, q, q, phi, phi, q, _cpu(B, H, L - 1, dtype=torch.float32), q)
+    with pytest.raises(ValueError, match="dout has shape"):
+        b.backward(desc, q, q, q, phi, phi, q, lse, _cpu(B, H, L, d // 2))
+    with pytest.raises(ValueError, match="ws holds"):
+        b.backward(desc, q, q, q, phi, phi, q, lse, q, ws=_cpu(256, dtype=torch.uint8))
+
+
+def test_decode_cache_checks_token_and_prompt_shapes():
+    import torch
+    cache = b.DecodeCache(1, 2, 64, 64, device=torch.device("cpu"))
+    tok = _cpu(1, 2, 64)
+    phi = _cpu(1, 2, 32, dtype=torch.float32)
+    with pytest.raises(ValueError, match="position"):
+        cache.step(64, tok, tok, tok, phi)
+    with pytest.raises(ValueError, match="q has shape"):
+        cache.step(0, _cpu(1, 2, 32), tok, tok, phi)
+    with pytest.raises(TypeError, match="phi has dtype"):
+        cache.step(0, tok, tok, tok, _cpu(1, 2, 32))
+    with pytest.raises(ValueError, match="does not fit"):
+        cache.prefill(_cpu(1, 2, 65, 64), _cpu(1, 2, 65, 64), _cpu(1, 2, 65, 32, dtype=torch.float32),
+                      _cpu(1, 2, 65, 32, dtype=torch.float32))
+    with pytest.raises(ValueError, match="theta has shape"):
+        cache.prefill(_cpu(1, 2, 4, 64), _cpu(1, 2, 4, 64), _cpu(1, 2, 4, 32, dtype=torch.float32),
+                      _cpu(1, 2, 5, 32, dtype=torch.float32))
+    gated = b.DecodeCache(1, 2, 64, 64, forget=True, device=torch.device("cpu"))
+    with pytest.raises(ValueError, match="logf"):
+        gated.step(0, tok, tok, tok, phi)
