@@ -63,6 +63,7 @@ class _Problem(ctypes.Structure):
         ("phi", ctypes.c_void_p),
         ("alibi_slopes", ctypes.c_void_p),
         ("logf", ctypes.c_void_p),
+        ("head_scale", ctypes.c_void_p),
     ]
 
 
@@ -105,6 +106,9 @@ def _lib() -> ctypes.CDLL:
                                           ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint64,
                                           ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_random_phi.restype = None
+        lib.oracle_adascale_lambda.argtypes = [dp, dp, ctypes.c_int64, ctypes.c_double,
+                                               ctypes.c_double, dp]
+        lib.oracle_adascale_lambda.restype = None
         _LIB = lib
     return _LIB
 
@@ -199,7 +203,7 @@ class Problem:
     """Holds the arrays of one attention problem and the C descriptor pointing at them."""
 
     def __init__(self, q, k, v, phi, flags: int, scale: float | None = None, alibi=None,
-                 logf=None):
+                 logf=None, head_scale=None):
         self.q = np.ascontiguousarray(q)
         self.k = np.ascontiguousarray(k)
         self.v = np.ascontiguousarray(v)
@@ -217,6 +221,10 @@ class Problem:
         self.logf = None if logf is None else np.ascontiguousarray(logf, dtype=np.float32)
         if flags & FORGET and (self.logf is None or self.logf.shape != (B, H, L)):
             raise ValueError("FORGET needs log forget gates [B, H, L]")
+        self.head_scale = (None if head_scale is None
+                           else np.ascontiguousarray(head_scale, dtype=np.float32))
+        if self.head_scale is not None and self.head_scale.shape != (H,):
+            raise ValueError("head_scale needs one multiplier per head")
         self.shape = (B, H, L, d)
         self.flags = int(flags)
         self.scale = float(1.0 / np.sqrt(d) if scale is None else scale)
@@ -224,7 +232,8 @@ class Problem:
                           self.q.ctypes.data, self.k.ctypes.data, self.v.ctypes.data,
                           self.phi.ctypes.data,
                           None if self.alibi is None else self.alibi.ctypes.data,
-                          None if self.logf is None else self.logf.ctypes.data)
+                          None if self.logf is None else self.logf.ctypes.data,
+                          None if self.head_scale is None else self.head_scale.ctypes.data)
 
     def theta(self) -> np.ndarray:
         B, H, L, d = self.shape
@@ -281,5 +290,18 @@ class Problem:
 
 
 def attention(q, k, v, phi, flags: int, scale=None, alibi=None, nthreads: int = 0,
-              logf=None) -> np.ndarray:
-    return Problem(q, k, v, phi, flags, scale, alibi, logf).output(nthreads)
+              logf=None, head_scale=None) -> np.ndarray:
+    return Problem(q, k, v, phi, flags, scale, alibi, logf, head_scale).output(nthreads)
+
+
+def adascale_lambda(tau, gamma, L: float, L_ref: float) -> np.ndarray:
+    """AdaScale's inverse temperatures lambda_h(L) = (1/tau_h) [ln(1 + max(L, L_ref)/L_ref)]^gamma_h
+    (AdaRoPE Sec. 3.3), fp64, one per head."""
+    tau = np.ascontiguousarray(tau, dtype=np.float64)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float64)
+    if tau.shape != gamma.shape or tau.ndim != 1:
+        raise ValueError("tau and gamma must be [heads]")
+    out = np.empty_like(tau)
+    _lib().oracle_adascale_lambda(_dptr(tau), _dptr(gamma), tau.size, ctypes.c_double(L),
+                                  ctypes.c_double(L_ref), _dptr(out))
+    return out

@@ -33,6 +33,11 @@
  *     the routed score of [ACC] eq. (7)-(8), with P_{j->i} a rotation by
  *     minus the summed angles of steps j+1..i ([ACC] App. B.8, position-only
  *     case; App. B.2 writes the step as e^{-i psi_t}).
+ *  2b. Per-head query scale (AdaScale, [ADA] Sec. 3.3): each head's query is
+ *     multiplied by its inverse temperature lambda_h before anything else,
+ *     q_i <- lambda_h q_i, so the logit becomes lambda_h scale <q~_i, k~_j>;
+ *     keys and values are untouched (the page applies it to the query only).
+ *     Without a head scale lambda_h = 1.
  *  3. Scores s_ij = scale * <q~_i, k~_j> - m_h (i - j) [distance bias on]
  *     + sum_{s=j+1}^{i} log f_s [forget gate on], for the causal set j <= i
  *     ([ACC] eq. (2), (11); [ADA] eq. (5); the forget gate is the logit term of
@@ -54,6 +59,7 @@
  *  - value transport: c_i = R(Theta_i)^T o~_i, so dL/do~_i = R(Theta_i) g_i;
  *  - softmax: with alpha_ij = w_ij / l_i and D_i = <dL/do~_i, o~_i>,
  *    dL/ds_ij = alpha_ij (<dL/do~_i, v~_j> - D_i);
+ *  - head scale: q_i = lambda_h q_raw_i, so dL/dq_raw_i = lambda_h dL/dq_i;
  *  - scores: dL/dq~_i = scale sum_j dL/ds_ij k~_j, dL/dk~_j = scale
  *    sum_i dL/ds_ij q~_i, dL/dv~_j = sum_i alpha_ij dL/do~_i;
  *  - rotation: x~ = R(a) x gives dL/dx = R(a)^T dL/dx~ and, per pair,
@@ -287,13 +293,25 @@ static int head_build(const oracle_problem* p, int64_t b, int64_t h, int64_t ima
   return ORACLE_OK;
 }
 
+/* Step 2b: the query multiplier of head h (1 without a head scale). */
+static double head_lambda(const oracle_problem* p, int64_t h) {
+  return p->head_scale ? (double)p->head_scale[h] : 1.0;
+}
+
+void oracle_adascale_lambda(const double* tau, const double* gamma, int64_t heads, double L,
+                            double L_ref, double* lambda) {
+  const double len = L > L_ref ? L : L_ref;
+  for (int64_t h = 0; h < heads; ++h) lambda[h] = pow(log(1.0 + len / L_ref), gamma[h]) / tau[h];
+}
+
 /* Step 3 for row i: scores[j] for j = 0..i.  qrot is scratch of length d. */
 static void row_scores(const oracle_problem* p, const head_state* hs, int64_t b, int64_t h,
                        int64_t i, double* qrot, double* scores) {
   const int64_t d = p->head_dim, P = d / 2, L = p->seqlen;
   const int64_t base = ((b * p->heads + h) * L) * d;
   double* qraw = qrot + d; /* caller gives 2*d doubles */
-  for (int64_t c = 0; c < d; ++c) qraw[c] = load_elem(p->q, p->io_dtype, base + i * d + c);
+  const double lam = head_lambda(p, h);
+  for (int64_t c = 0; c < d; ++c) qraw[c] = lam * load_elem(p->q, p->io_dtype, base + i * d + c);
   if (p->flags & ORACLE_ROTATE_QK) {
     rotate_vec(qraw, hs->theta + i * P, P, 0, qrot);
   } else {
@@ -444,8 +462,9 @@ static int backward_head(const oracle_problem* p, const void* dout, int64_t b, i
     rc = ORACLE_ERR_NOMEM;
     goto done;
   }
+  const double lam = head_lambda(p, h);
   for (int64_t t = 0; t < L; ++t) {
-    for (int64_t c = 0; c < d; ++c) raw[c] = load_elem(p->q, p->io_dtype, base + t * d + c);
+    for (int64_t c = 0; c < d; ++c) raw[c] = lam * load_elem(p->q, p->io_dtype, base + t * d + c);
     if (qk) rotate_vec(raw, hs.theta + t * P, P, 0, qrot + t * d);
     else memcpy(qrot + t * d, raw, sizeof(double) * (size_t)d);
     for (int64_t c = 0; c < d; ++c) raw[c] = load_elem(dout, p->io_dtype, base + t * d + c);
@@ -534,6 +553,7 @@ static int backward_head(const oracle_problem* p, const void* dout, int64_t b, i
     }
     if (tv) rotate_vec(dvt + t * d, th, P, 1, ov);
     else memcpy(ov, dvt + t * d, sizeof(double) * (size_t)d);
+    for (int64_t c = 0; c < d; ++c) oq[c] *= lam;  /* through q = lambda_h q_raw */
   }
 done:
   free(qrot);

@@ -50,6 +50,7 @@ typedef struct oracle_problem {
   const float* phi;
   const float* alibi_slopes; /* read only when ORACLE_ALIBI is set */
   const float* logf;         /* [batch, heads, seqlen] log forget gates; read only with ORACLE_FORGET */
+  const float* head_scale;   /* NULL, or [heads]: per-head query multipliers lambda_h (AdaScale) */
 } oracle_problem;
 
 /* Prefix sum of step angles along the sequence, one segment per (outer, pair).
@@ -67,6 +68,13 @@ void oracle_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t
  * definition gives c and which 32 bits each element takes. */
 void oracle_random_phi(int64_t batch, int64_t phi_heads, int64_t seqlen, int64_t npairs,
                        uint64_t seed, uint64_t step, const float* bound, float* phi);
+
+/* AdaScale's per-head, length-aware inverse temperature ("AdaRoPE: Not All
+ * Attention Heads Should Rotate and Scale Equally", Sec. 3.3, AdaScale):
+ *   lambda_h(L) = (1 / tau_h) * [ln(1 + max(L, L_ref) / L_ref)]^gamma_h
+ * for heads h = 0..heads-1, in fp64. */
+void oracle_adascale_lambda(const double* tau, const double* gamma, int64_t heads, double L,
+                            double L_ref, double* lambda);
 
 /* Reduce an angle into [-pi, pi). */
 double oracle_wrap(double x);

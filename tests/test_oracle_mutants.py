@@ -66,6 +66,20 @@ GENERATOR_MUTANTS = [
 ]
 
 
+# Mistakes in AdaScale (the per-head query scale and its schedule).
+ADASCALE_MUTANTS = [
+    ("head scale chain factor dropped", "for (int64_t c = 0; c < d; ++c) oq[c] *= lam;", "(void)oq;"),
+    ("head scale of the next head", "return p->head_scale ? (double)p->head_scale[h] : 1.0;",
+     "return p->head_scale ? (double)p->head_scale[(h + 1) % p->heads] : 1.0;"),
+    ("head scale squared in the scores", "qraw[c] = lam * load_elem(", "qraw[c] = lam * lam * load_elem("),
+    ("schedule takes min(L, L_ref)", "const double len = L > L_ref ? L : L_ref;",
+     "const double len = L < L_ref ? L : L_ref;"),
+    ("schedule in log10", "pow(log(1.0 + len / L_ref), gamma[h])", "pow(log10(1.0 + len / L_ref), gamma[h])"),
+    ("schedule without the 1 +", "pow(log(1.0 + len / L_ref), gamma[h])", "pow(log(len / L_ref), gamma[h])"),
+    ("schedule multiplies by tau", "gamma[h]) / tau[h];", "gamma[h]) * tau[h];"),
+]
+
+
 def _run_pins_against(old, new, name, tmp_path, pin_file):
     src = open(SRC).read()
     assert src.count(old) >= 1, f"mutation site for {name!r} not found"
@@ -97,3 +111,8 @@ def test_backward_pins_fail_on_planted_mistake(name, old, new, tmp_path):
 @pytest.mark.parametrize("name,old,new", GENERATOR_MUTANTS, ids=[m[0] for m in GENERATOR_MUTANTS])
 def test_generator_pins_fail_on_planted_mistake(name, old, new, tmp_path):
     _run_pins_against(old, new, name, tmp_path, "test_oracle_generators.py")
+
+
+@pytest.mark.parametrize("name,old,new", ADASCALE_MUTANTS, ids=[m[0] for m in ADASCALE_MUTANTS])
+def test_adascale_pins_fail_on_planted_mistake(name, old, new, tmp_path):
+    _run_pins_against(old, new, name, tmp_path, "test_oracle_adascale.py")
