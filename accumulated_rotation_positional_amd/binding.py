@@ -31,6 +31,8 @@ PHI_SHARED_HEADS = 0x8
 SCAN_EXCLUSIVE = 0x10
 FUSED_ROTATION = 0x20
 FORGET_GATE = 0x40
+HEAD_SCALE = 0x80
+ABI_VERSION = 2
 
 # Every function the header declares (tests check the library exports them all).
 EXPORTS = ("arp_abi_version", "arp_status_string", "arp_check", "arp_scan_state_bytes",
@@ -40,7 +42,7 @@ EXPORTS = ("arp_abi_version", "arp_status_string", "arp_check", "arp_scan_state_
            "arp_backward", "arp_decode_workspace_bytes", "arp_decode_prefill", "arp_decode_step",
            "arp_forward_ex", "arp_angle_scan_random", "arp_angle_scan_tokens",
            "arp_angle_scan_const", "arp_random_phi", "arp_backward_ex", "arp_decode_prefill_ex",
-           "arp_decode_step_ex")
+           "arp_decode_step_ex", "arp_adascale_lambda")
 
 
 class ArpError(RuntimeError):
@@ -52,7 +54,8 @@ class ArpError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seqlen", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
-                ("scale", ctypes.c_float), ("reserved", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("head_scale", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -96,6 +99,8 @@ def lib() -> ctypes.CDLL:
                 "arp_angle_scan_tokens": ([D, P, P, ctypes.c_int64, P, P, S, P], ctypes.c_int),
                 "arp_angle_scan_const": ([D, P, P, P], ctypes.c_int),
                 "arp_random_phi": ([D, U64, U64, P, P, P], ctypes.c_int),
+                "arp_adascale_lambda": ([ctypes.c_int32, P, P, ctypes.c_int64, ctypes.c_int64, P],
+                                        ctypes.c_int),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -110,14 +115,38 @@ def _check(fn: str, status: int) -> None:
 
 
 def make_desc(batch: int, heads: int, seqlen: int, head_dim: int, dtype, flags: int,
-              scale: float | None = None) -> Desc:
+              scale: float | None = None, head_scale: torch.Tensor | None = None) -> Desc:
+    """A descriptor; head_scale (float32 [heads] on the GPU: AdaScale's per-head
+    query multipliers) sets HEAD_SCALE and is kept alive with the descriptor."""
     if dtype in (torch.float32, "f32", DTYPE_F32):
         code = DTYPE_F32
     elif dtype in (torch.bfloat16, "bf16", DTYPE_BF16):
         code = DTYPE_BF16
     else:
         raise TypeError(f"unsupported dtype {dtype}")
-    return Desc(batch, heads, seqlen, head_dim, code, flags, 0.0 if scale is None else scale, 0)
+    ptr = None
+    if head_scale is not None:
+        _expect(head_scale, "head_scale", (heads,), torch.float32)
+        ptr = _ptr(head_scale)
+        flags |= HEAD_SCALE
+    d = Desc(batch, heads, seqlen, head_dim, code, flags, 0.0 if scale is None else scale, 0, ptr)
+    d._head_scale = head_scale  # the device array the pointer refers to
+    return d
+
+
+def adascale_lambda(tau, gamma, L: int, L_ref: int) -> torch.Tensor:
+    """AdaScale's inverse temperatures lambda_h(L) = (1/tau_h) [ln(1 + max(L, L_ref)/L_ref)]^gamma_h
+    computed by the library's host routine (fp64, rounded to fp32); returns a
+    CPU float32 tensor [heads] (move it to the GPU for head_scale)."""
+    tau = torch.as_tensor(tau, dtype=torch.float32).contiguous().cpu()
+    gamma = torch.as_tensor(gamma, dtype=torch.float32).contiguous().cpu()
+    if tau.dim() != 1 or tau.shape != gamma.shape:
+        raise ValueError("tau and gamma must be [heads]")
+    out = torch.empty_like(tau)
+    _check("arp_adascale_lambda", lib().arp_adascale_lambda(tau.numel(), tau.data_ptr(),
+                                                            gamma.data_ptr(), int(L), int(L_ref),
+                                                            out.data_ptr()))
+    return out
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
@@ -212,11 +241,12 @@ def flags_for(*, rotate_qk: bool = True, rotate_v: bool = False, alibi: bool = F
             (FORGET_GATE if forget else 0))
 
 
-def desc_for(q: torch.Tensor, flags: int, scale: float | None = None) -> Desc:
+def desc_for(q: torch.Tensor, flags: int, scale: float | None = None,
+             head_scale: torch.Tensor | None = None) -> Desc:
     if q.dim() != 4:
         raise ValueError("q must be [B, H, L, d]")
     B, H, L, d = q.shape
-    return make_desc(B, H, L, d, q.dtype, flags, scale)
+    return make_desc(B, H, L, d, q.dtype, flags, scale, head_scale)
 
 
 def workspace_bytes(desc: Desc) -> int:
@@ -383,13 +413,15 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.Tensor
             rotate_qk: bool = True, rotate_v: bool = False, alibi: torch.Tensor | None = None,
             scale: float | None = None, exclusive: bool = False, fused: bool = False,
             out: torch.Tensor | None = None, theta: torch.Tensor | None = None,
-            state: torch.Tensor | None = None, ws: torch.Tensor | None = None):
-    """(q, k, v, phi, flags) -> (o, theta): the whole forward pass on the GPU."""
+            state: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+            head_scale: torch.Tensor | None = None):
+    """(q, k, v, phi, flags) -> (o, theta): the whole forward pass on the GPU.
+    head_scale: float32 [H] per-head query multipliers (AdaScale), or None."""
     _check_phi_heads(q, phi)
     flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi is not None,
                       shared_phi=phi.shape[1] == 1 and q.shape[1] != 1, exclusive=exclusive,
                       fused=fused)
-    desc = desc_for(q, flags, scale)
+    desc = desc_for(q, flags, scale, head_scale)
     _check_qkv(desc, q=q, k=k, v=v, out=out)
     _check_angles(desc, phi=phi, theta=theta)
     _check_alibi(desc, alibi)
@@ -420,13 +452,14 @@ def rotate(x: torch.Tensor, theta: torch.Tensor, desc: Desc, inverse: bool = Fal
 def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.Tensor, *,
                   rotate_qk: bool = True, rotate_v: bool = False,
                   alibi: torch.Tensor | None = None, scale: float | None = None,
-                  exclusive: bool = False):
+                  exclusive: bool = False, head_scale: torch.Tensor | None = None):
     """Forward pass that also returns the per-row base-2 log-sum-exp (bf16,
-    pre-rotation path): (o, theta, lse, desc), everything the backward needs."""
+    pre-rotation path): (o, theta, lse, desc), everything the backward needs
+    (desc carries the head scale, if any, into the backward)."""
     _check_phi_heads(q, phi)
     flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi is not None,
                       shared_phi=phi.shape[1] == 1 and q.shape[1] != 1, exclusive=exclusive)
-    desc = desc_for(q, flags, scale)
+    desc = desc_for(q, flags, scale, head_scale)
     _check_qkv(desc, q=q, k=k, v=v)
     _check_angles(desc, phi=phi)
     _check_alibi(desc, alibi)
@@ -516,6 +549,7 @@ class DecodeCache:
     def __init__(self, batch: int, heads: int, capacity: int, head_dim: int, *, phi_heads=None,
                  rotate_qk: bool = True, rotate_v: bool = False, alibi: bool = False,
                  exclusive: bool = False, forget: bool = False, scale: float | None = None,
+                 head_scale: torch.Tensor | None = None,
                  device: torch.device = torch.device("cuda:0")):
         hphi = heads if phi_heads is None else phi_heads
         flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi,
@@ -524,7 +558,8 @@ class DecodeCache:
         self.gcache = (torch.zeros(batch, heads, capacity, dtype=torch.float32, device=device)
                        if forget else None)
         self.gstate = torch.zeros(batch, heads, dtype=torch.float64, device=device) if forget else None
-        self.desc = make_desc(batch, heads, capacity, head_dim, torch.bfloat16, flags, scale)
+        self.desc = make_desc(batch, heads, capacity, head_dim, torch.bfloat16, flags, scale,
+                              head_scale)
         self.device = device
         self.kcache = torch.zeros(batch, heads, capacity, head_dim, dtype=torch.bfloat16, device=device)
         self.vcache = torch.zeros_like(self.kcache)
@@ -598,7 +633,8 @@ class DecodeCache:
 def forward_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.Tensor, *,
                rotate_qk: bool = True, rotate_v: bool = False, alibi: torch.Tensor | None = None,
                logf: torch.Tensor | None = None, scale: float | None = None,
-               exclusive: bool = False, with_lse: bool = False):
+               exclusive: bool = False, with_lse: bool = False,
+               head_scale: torch.Tensor | None = None):
     """The forward with every option (arp_forward_ex): logf [B, H, L] log forget
     gates (the gate bias is on when given), with_lse also returns the per-row
     base-2 log-sum-exp.  Returns (o, theta, lse or None)."""
@@ -606,7 +642,7 @@ def forward_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.Ten
     flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi is not None,
                       shared_phi=phi.shape[1] == 1 and q.shape[1] != 1, exclusive=exclusive,
                       forget=logf is not None)
-    desc = desc_for(q, flags, scale)
+    desc = desc_for(q, flags, scale, head_scale)
     _check_qkv(desc, q=q, k=k, v=v)
     _check_angles(desc, phi=phi)
     _check_alibi(desc, alibi)

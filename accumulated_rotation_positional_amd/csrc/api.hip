@@ -29,6 +29,8 @@ arp_status make_geometry(const arp_desc* d, Geometry* g) {
   // Sizes: every tensor index must fit comfortably in 64 bits and the grids in
   // their limits; the sequence is capped at 2^24 tokens.
   if (d->seqlen > (1 << 24) || (long long)d->batch * d->heads > 65535) return ARP_ERR_INVALID_ARG;
+  if (((d->flags & ARP_HEAD_SCALE) != 0) != (d->head_scale != nullptr)) return ARP_ERR_INVALID_ARG;
+  if (d->head_scale != nullptr && ((uintptr_t)d->head_scale & 15u) != 0) return ARP_ERR_ALIGNMENT;
   if (d->head_dim != 64 && d->head_dim != 128) return ARP_ERR_UNSUPPORTED;
   g->B = d->batch;
   g->H = d->heads;
@@ -40,6 +42,7 @@ arp_status make_geometry(const arp_desc* d, Geometry* g) {
   g->flags = d->flags;
   g->scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->head_dim);
   g->Lp = (int)(((long long)d->seqlen + 255) / 256 * 256);
+  g->hscale = d->head_scale;
   return ARP_OK;
 }
 
@@ -147,6 +150,20 @@ const char* arp_status_string(int status) {
 arp_status arp_check(const arp_desc* desc) {
   Geometry g;
   return make_geometry(desc, &g);
+}
+
+arp_status arp_adascale_lambda(int32_t heads, const float* tau, const float* gamma, int64_t L,
+                               int64_t L_ref, float* lambda) {
+  if (heads < 1 || L < 1 || L_ref < 1 || tau == nullptr || gamma == nullptr || lambda == nullptr)
+    return ARP_ERR_INVALID_ARG;
+  for (int32_t h = 0; h < heads; ++h)
+    if (!(tau[h] > 0.f) || isinf(tau[h]) || !(gamma[h] == gamma[h]) || isinf(gamma[h]))
+      return ARP_ERR_INVALID_ARG;
+  const double len = (double)(L > L_ref ? L : L_ref);
+  const double growth = log(1.0 + len / (double)L_ref);
+  for (int32_t h = 0; h < heads; ++h)
+    lambda[h] = (float)(pow(growth, (double)gamma[h]) / (double)tau[h]);
+  return ARP_OK;
 }
 
 size_t arp_scan_state_bytes(const arp_desc* desc) {

@@ -18,6 +18,7 @@ struct Geometry {
   uint32_t flags;
   float scale;         // resolved logit scale
   int Lp;              // seqlen padded for the pre-rotated operands (multiple of 256)
+  const float* hscale; // device [H] per-head query multipliers (ARP_HEAD_SCALE), else null
 };
 
 // ---- buffers ----------------------------------------------------------------

@@ -73,7 +73,8 @@ __device__ __forceinline__ void attn_tile(
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
     const float* __restrict__ theta, const float* __restrict__ alibi,
     const float* __restrict__ gate2, uint16_t* __restrict__ o, float* __restrict__ lse, int L,
-    int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk, float qscale) {
+    int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk, float qscale0,
+    const float* __restrict__ hscale) {
   constexpr bool ALIBI = (BIAS & 1) != 0;
   constexpr bool FORGET = (BIAS & 2) != 0;
   static_assert(!(FUSED && FORGET), "the gate bias needs the pre-rotation path");
@@ -212,6 +213,9 @@ __device__ __forceinline__ void attn_tile(
   };
 
   // ---- Q~ operand: lane (ln, hf) holds query qw+32qb+ln, d = 16ks+8hf..+7 ----
+  // (fused: rotated and multiplied by scale * log2 e and the head's query
+  // multiplier here; the pre-rotated operand already carries both)
+  const float qscale = (FUSED && hscale != nullptr) ? qscale0 * hscale[h] : qscale0;
   bf16x8 qop[QB][KS];
   if constexpr (!FUSED) {
 #pragma unroll
@@ -606,7 +610,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
     const float* __restrict__ theta, const float* __restrict__ alibi,
     const float* __restrict__ gate2, uint16_t* __restrict__ o, float* __restrict__ lse, int L,
-    int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk, float qscale, int paired) {
+    int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk, float qscale, int paired,
+    const float* __restrict__ hscale) {
   constexpr int STAGE = BN * D * 2 + D * BN * 2 + (((BIAS & 2) != 0) ? BN * 4 : 0);  // as in attn_tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
   constexpr bool SPREAD = (BIAS != 0) && !FUSED;
@@ -616,17 +621,17 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     const int x = (int)(blockIdx.x % 8), c = (int)(blockIdx.x / 8);
     attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(x * per + c, smem, qr, kr, vt, kmax, theta,
                                                         alibi, gate2, o, lse, L, Lp, H, Hphi, nqt,
-                                                        total_tiles, rot_qk, qscale);
+                                                        total_tiles, rot_qk, qscale, hscale);
     __syncthreads();  // every wave is done with the LDS ring before it is refilled
     attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(x * per + per - 1 - c, smem, qr, kr, vt,
                                                         kmax, theta, alibi, gate2, o, lse, L, Lp, H,
-                                                        Hphi, nqt, total_tiles, rot_qk, qscale);
+                                                        Hphi, nqt, total_tiles, rot_qk, qscale, hscale);
     return;
   }
   const int logical = SPREAD ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(logical, smem, qr, kr, vt, kmax, theta, alibi,
                                                       gate2, o, lse, L, Lp, H, Hphi, nqt,
-                                                      total_tiles, rot_qk, qscale);
+                                                      total_tiles, rot_qk, qscale, hscale);
 }
 
 template <int D, int QPW, int NW, int NST, int MINB, bool FUSED>
@@ -646,7 +651,7 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
 #define ARP_BF16_LAUNCH(A, R)                                                                  \
   hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, MINB, FUSED, A, R>), dim3(grid),      \
                      dim3(NW * 64), 0, stream, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,   \
-                     g.L, g.Lp, g.H, g.Hphi, nqt, total, rqk, qscale, paired)
+                     g.L, g.Lp, g.H, g.Hphi, nqt, total, rqk, qscale, paired, g.hscale)
 #define ARP_BF16_LAUNCH_R(A) \
   do {                       \
     if (rv) ARP_BF16_LAUNCH(A, true); else ARP_BF16_LAUNCH(A, false); \

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
     const float* __restrict__ theta, const float* __restrict__ lse, const float* __restrict__ alibi,
     BwdOperands ops, float* __restrict__ dtheta, int L, int Lp, int H, int Hphi, uint32_t flags,
-    float qscale) {
+    float qscale0, const float* __restrict__ hscale) {
   constexpr int P = D / 2;
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   constexpr int ITER = TILE * CPR / 256;
@@ -88,6 +88,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   const size_t rm = (size_t)bh * Lp * D;  // row-major block of this head
   float* stats = ops.stats + ((size_t)bh * (Lp / TILE) + blockIdx.x) * (2 * TILE);
   const float slope2 = (flags & ARP_ALIBI) ? alibi[h] * LOG2E : 0.f;
+  // q~s = q~ scale log2 e, times the head's query multiplier (AdaScale)
+  const float qscale = hscale != nullptr ? qscale0 * hscale[h] : qscale0;
   if (tid < 2) s_n2[tid] = 0u;
   __syncthreads();
 
@@ -485,7 +487,7 @@ template <int D, int NW, bool ALIBI, bool GATE>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
     BwdOperands ops, const float* __restrict__ theta, const float* __restrict__ alibi,
     uint16_t* __restrict__ dq, float* __restrict__ dtheta, int L, int Lp, int H, int Hphi, int nqt,
-    int total_tiles, uint32_t flags, float scale) {
+    int total_tiles, uint32_t flags, float scale0, const float* __restrict__ hscale) {
   constexpr int BM = 32 * NW;
   constexpr int KS = D / 16, DB = D / 32, KB = 2, KS2 = 4;
   constexpr int ROWB = D * 2, RT = TILE * ROWB;
@@ -506,6 +508,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
   const int q0 = qt * BM;
   const int b = bh / H, h = bh % H;
   const int g = (Hphi == 1) ? 0 : h;
+  // the logit scale of this head: scale times its query multiplier (AdaScale),
+  // so dq = lambda_h dq' where q' = lambda_h q
+  const float scale = hscale != nullptr ? scale0 * hscale[h] : scale0;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, hf = lane >> 5;
@@ -648,7 +653,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
   const size_t row = ((size_t)bh * L + i) * D;
   const float* th = theta + ((size_t)(b * Hphi + g) * L + i) * (D / 2);
   float* dth = dtheta + ((size_t)bh * L + i) * (D / 2);
-  // q~ = q~s / (scale log2 e)
+  // dq~ = scale lambda_h sum dS k~ (the gradient of the unscaled q~), and
+  // q~ = q~s / (scale lambda_h log2 e): their product, the dTheta term, is
+  // that of the scaled query
   grad_rows<DB>(dqt, scale, ops.qs + rm + (size_t)i * D, 1.f / (scale * LOG2E), th,
                 (flags & ARP_ROTATE_QK) != 0, dq + row, dth, hf);
 }
@@ -836,7 +843,7 @@ hipError_t launch_bwd_grads(const Geometry& g, const BwdArgs& a, hipStream_t str
     const int grid = ((total + 7) / 8) * 8;
     hipLaunchKernelGGL((bwd_dq_kernel<D, NW, ALIBI, GATE>), dim3(grid), dim3(NW * 64), 0, stream,
                        a.ops, a.theta, a.alibi, a.dq, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nqt, total,
-                       fl, g.scale);
+                       fl, g.scale, g.hscale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -863,7 +870,7 @@ hipError_t launch_bwd_d(const Geometry& g, const BwdArgs& a, hipStream_t stream)
     dim3 grid(g.Lp / TILE, g.B * g.H);
     hipLaunchKernelGGL((bwd_prep_kernel<D>), grid, dim3(256), 0, stream, a.q, a.k, a.v, a.o, a.dout,
                        a.theta, a.lse, a.alibi, a.ops, a.dtheta, g.L, g.Lp, g.H, g.Hphi, fl,
-                       g.scale * LOG2E);
+                       g.scale * LOG2E, g.hscale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -898,10 +905,12 @@ constexpr int F32B_T = 32;     // rows per staged LDS tile
 // (token, pair); the P threads of a token are consecutive lanes.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_f32_prep_kernel(BwdF32Args a, int L, int H, int Hphi,
-                                                           uint32_t flags, float qscale) {
+                                                           uint32_t flags, float qscale0,
+                                                           const float* __restrict__ hscale) {
   constexpr int P = D / 2;
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh % H, g = (Hphi == 1) ? 0 : h;
+  const float qscale = hscale != nullptr ? qscale0 * hscale[h] : qscale0;  // AdaScale
   const int idx = blockIdx.x * 256 + threadIdx.x;
   const int t = idx / P, p = idx % P;
   const bool ok = t < L;
@@ -1037,11 +1046,14 @@ __global__ __launch_bounds__(256) void bwd_f32_dkdv_kernel(BwdF32Args a, int L, 
 // dQ: a workgroup owns 64 queries and walks the key tiles up to its last query.
 template <int D, bool ALIBI>
 __global__ __launch_bounds__(256) void bwd_f32_dq_kernel(BwdF32Args a, int L, int H, int Hphi,
-                                                         uint32_t flags, float scale) {
+                                                         uint32_t flags, float scale0,
+                                                         const float* __restrict__ hscale) {
   constexpr int DQ = D / 4, P = D / 2;
   __shared__ float sk[F32B_T][D], sv[F32B_T][D];
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh % H, g = (Hphi == 1) ? 0 : h;
+  // scale times the head's query multiplier (AdaScale): dq = lambda_h dq'
+  const float scale = hscale != nullptr ? scale0 * hscale[h] : scale0;
   const int tid = threadIdx.x, sp = tid & 3;
   const int i = blockIdx.x * F32B_ROWS + tid / 4;
   const int ic = min(i, L - 1);
@@ -1100,18 +1112,18 @@ hipError_t launch_bwd_f32_d(const Geometry& g, const BwdF32Args& a, hipStream_t 
   const int BH = g.B * g.H;
   const bool al = (g.flags & ARP_ALIBI) != 0;
   hipLaunchKernelGGL((bwd_f32_prep_kernel<D>), dim3((g.L * P + 255) / 256, BH), dim3(256), 0,
-                     stream, a, g.L, g.H, g.Hphi, g.flags, g.scale * LOG2E);
+                     stream, a, g.L, g.H, g.Hphi, g.flags, g.scale * LOG2E, g.hscale);
   const dim3 grid((g.L + F32B_ROWS - 1) / F32B_ROWS, BH);
   if (al) {
     hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, true>), grid, dim3(256), 0, stream, a, g.L, g.H,
                        g.Hphi, g.flags);
     hipLaunchKernelGGL((bwd_f32_dq_kernel<D, true>), grid, dim3(256), 0, stream, a, g.L, g.H,
-                       g.Hphi, g.flags, g.scale);
+                       g.Hphi, g.flags, g.scale, g.hscale);
   } else {
     hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, false>), grid, dim3(256), 0, stream, a, g.L, g.H,
                        g.Hphi, g.flags);
     hipLaunchKernelGGL((bwd_f32_dq_kernel<D, false>), grid, dim3(256), 0, stream, a, g.L, g.H,
-                       g.Hphi, g.flags, g.scale);
+                       g.Hphi, g.flags, g.scale, g.hscale);
   }
   return hipGetLastError();
 }

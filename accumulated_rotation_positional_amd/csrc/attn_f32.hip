@@ -30,7 +30,8 @@ template <int D, bool ROT_QK, bool ROT_V, bool ALIBI>
 __global__ __launch_bounds__(F32_T) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ theta, const float* __restrict__ alibi, float* __restrict__ o,
-    float* __restrict__ lse, int L, int H, int Hphi, float qscale) {
+    float* __restrict__ lse, int L, int H, int Hphi, float qscale0,
+    const float* __restrict__ hscale) {
   constexpr int P = D / 2;
   __shared__ float sk[F32_K][D];
   __shared__ float sv[F32_K][D];
@@ -44,6 +45,8 @@ __global__ __launch_bounds__(F32_T) void attn_f32_kernel(
   const bool valid = i < L;
   const int irow = valid ? i : L - 1;
   const float* th_base = theta + (size_t)(b * Hphi + g) * L * P;
+  // scale * log2 e, times the head's query multiplier (AdaScale)
+  const float qscale = hscale != nullptr ? qscale0 * hscale[h] : qscale0;
 
   float qv[D];
   const float* qrow = q + ((size_t)bh * L + irow) * D;
@@ -156,7 +159,7 @@ hipError_t launch_f32_d(const Geometry& g, const float* q, const float* k, const
   const bool rqk = g.flags & ARP_ROTATE_QK, rv = g.flags & ARP_ROTATE_V, al = g.flags & ARP_ALIBI;
 #define ARP_F32_LAUNCH(A, B, C)                                                                \
   hipLaunchKernelGGL((attn_f32_kernel<D, A, B, C>), grid, dim3(F32_T), 0, stream, q, k, v,    \
-                     theta, alibi, o, lse, g.L, g.H, g.Hphi, qscale)
+                     theta, alibi, o, lse, g.L, g.H, g.Hphi, qscale, g.hscale)
   if (rqk) {
     if (rv) {
       if (al) ARP_F32_LAUNCH(true, true, true); else ARP_F32_LAUNCH(true, true, false);

@@ -156,7 +156,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     const uint64_t* __restrict__ state, float* __restrict__ theta, uint16_t* __restrict__ kcache,
     uint16_t* __restrict__ vcache, const float* __restrict__ alibi, const float* __restrict__ logf,
     float* __restrict__ gcache, const double* __restrict__ gstate, float* __restrict__ part, int H,
-    int Hphi, int Lmax, int pos, int nchunk, uint32_t flags, float qscale) {
+    int Hphi, int Lmax, int pos, int nchunk, uint32_t flags, float qscale0,
+    const float* __restrict__ hscale) {
   constexpr int CPR = D / 8;     // lanes per row
   constexpr int RPI = 64 / CPR;  // rows per load instruction
   constexpr int NI = 64 / RPI;   // instructions per 64 keys
@@ -169,6 +170,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   const int n = pos + 1;                // keys 0..pos
   const int kw0 = c * DKC + wave * 64;  // this wave's first key
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
+  // scale * log2 e, times the head's query multiplier (AdaScale)
+  const float qscale = hscale != nullptr ? qscale0 * hscale[h] : qscale0;
   // The new token's gate prefix G_t (every workgroup forms the same value;
   // the first one appends it to the gate cache).
   float gt = 0.f;
@@ -397,7 +400,7 @@ void launch_attn_step(const Geometry& g, const DecodeArgs& a, int nchunk, hipStr
   hipLaunchKernelGGL((decode_attn_kernel<D, ALIBI, GATE>), dim3(nchunk, g.B * g.H), dim3(256), 0,
                      stream, a.q, a.k, a.v, a.phi, a.state, a.theta, a.kcache, a.vcache, a.alibi,
                      a.logf, a.gcache, a.gstate, a.part, g.H, g.Hphi, g.L, a.pos, nchunk, g.flags,
-                     g.scale * LOG2E);
+                     g.scale * LOG2E, g.hscale);
 }
 
 template <int D>

@@ -12,8 +12,9 @@
 //    elements = 4 pairs per thread, with the matching float4 of angles);
 //  * sin/cos of the wrapped angle are computed once per (token, pair) and
 //    shared by q, k and v;
-//  * q~ is pre-multiplied by scale * log2(e) so the attention kernel's
-//    matrix-core products are already base-2 logits;
+//  * q~ is pre-multiplied by scale * log2(e) (and by the head's query
+//    multiplier with ARP_HEAD_SCALE) so the attention kernel's matrix-core
+//    products are already base-2 logits;
 //  * q~ and k~ are written row-major [Lp, D]; v~ is transposed through LDS and
 //    written [D, Lp], the layout the P V product reads (keys contiguous);
 //  * tokens in [L, Lp) are written as zeros (the attention kernel reads whole
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(256) void rotate_qkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ theta, uint16_t* __restrict__ qr, uint16_t* __restrict__ kr,
     uint16_t* __restrict__ vt, float* __restrict__ kmax, int L, int Lp, int H, int Hphi,
-    uint32_t flags, float qscale) {
+    uint32_t flags, float qscale0, const float* __restrict__ hscale) {
   constexpr int P = D / 2;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int ITER = ROT_TOKENS * CPR / 256;
@@ -50,6 +51,8 @@ __global__ __launch_bounds__(256) void rotate_qkv_kernel(
   const int tid = threadIdx.x;
   const bool rot_qk = (flags & ARP_ROTATE_QK) != 0;
   const bool rot_v = (flags & ARP_ROTATE_V) != 0;
+  // the head's query multiplier (AdaScale) rides with scale * log2 e
+  const float qscale = hscale != nullptr ? qscale0 * hscale[h] : qscale0;
   if (tid == 0) s_kmax2 = 0u;
   __syncthreads();
 
@@ -248,10 +251,10 @@ hipError_t launch_rotate_qkv(const Geometry& g, const void* q, const void* k, co
   const auto* vb = static_cast<const uint16_t*>(v);
   if (g.D == 64)
     hipLaunchKernelGGL((rotate_qkv_kernel<64>), grid, dim3(256), 0, stream, qb, kb, vb, theta, qr,
-                       kr, vt, kmax, g.L, g.Lp, g.H, g.Hphi, g.flags, qscale);
+                       kr, vt, kmax, g.L, g.Lp, g.H, g.Hphi, g.flags, qscale, g.hscale);
   else
     hipLaunchKernelGGL((rotate_qkv_kernel<128>), grid, dim3(256), 0, stream, qb, kb, vb, theta,
-                       qr, kr, vt, kmax, g.L, g.Lp, g.H, g.Hphi, g.flags, qscale);
+                       qr, kr, vt, kmax, g.L, g.Lp, g.H, g.Hphi, g.flags, qscale, g.hscale);
   return hipGetLastError();
 }
 

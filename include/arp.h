@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define ARP_ABI_VERSION 1
+#define ARP_ABI_VERSION 2
 
 typedef enum arp_status {
   ARP_OK = 0,
@@ -88,7 +88,8 @@ typedef enum arp_dtype {
 #define ARP_FORGET_GATE 0x40u     /* add the forget-gate bias sum_{s=j+1}^{i} log f_s (bf16,
                                      pre-rotation path; arp_forward_ex,
                                      arp_backward_ex and the _ex decode calls) */
-#define ARP_ALL_FLAGS 0x7Fu
+#define ARP_HEAD_SCALE 0x80u      /* multiply head h's queries by head_scale[h] (AdaScale) */
+#define ARP_ALL_FLAGS 0xFFu
 
 typedef struct arp_desc {
   int32_t batch;
@@ -99,6 +100,16 @@ typedef struct arp_desc {
   uint32_t flags;    /* ARP_* flags above */
   float scale;       /* logit scale; <= 0 selects 1/sqrt(head_dim) */
   int32_t reserved;  /* must be 0 */
+  /* With ARP_HEAD_SCALE: device float32 [heads], 16-byte aligned, each head's
+   * query multiplier lambda_h -- AdaScale's per-head, length-aware inverse
+   * temperature ("AdaRoPE: Not All Attention Heads Should Rotate and Scale
+   * Equally", Sec. 3.3; arp_adascale_lambda computes it), applied to the
+   * query only (q_i <- lambda_h q_i, same section and Sec. 3.4), so the logit
+   * is lambda_h * scale * <q~_i, k~_j>; keys, values and caches are
+   * unchanged.  Every attention entry point honours it (forward, training,
+   * backward, decode; arp_rotate and the angle scans do not read it).
+   * Without the flag it must be NULL (ARP_ERR_INVALID_ARG otherwise). */
+  const float* head_scale;
 } arp_desc;
 
 /* ARP_ABI_VERSION of the loaded library. */
@@ -107,8 +118,22 @@ int arp_abi_version(void);
 /* Static, never-NULL description of a status code. */
 const char* arp_status_string(int status);
 
-/* Host-only validation of a descriptor (no pointers, no launch). */
+/* Host-only validation of a descriptor (no launch; head_scale is checked for
+ * presence and alignment only, never dereferenced). */
 arp_status arp_check(const arp_desc* desc);
+
+/* Host-only: AdaScale's inverse temperatures ("AdaRoPE", Sec. 3.3)
+ *   lambda[h] = (1 / tau[h]) * [ln(1 + max(L, L_ref) / L_ref)]^gamma[h]
+ * for h < heads, evaluated in fp64 and rounded once to fp32; L is the context
+ * length the queries attend over (seqlen for a whole-sequence pass), L_ref the
+ * reference length.  tau, gamma, lambda are HOST arrays of heads floats.
+ * ARP_ERR_INVALID_ARG for heads < 1, L < 1, L_ref < 1, a NULL array, or a
+ * tau that is not finite and positive.  Copy the result to the device and
+ * pass it as arp_desc.head_scale.  The scale is a constant of the library's
+ * calls: a caller training tau and gamma gets dL/dlambda_h =
+ * (1 / lambda_h) sum_{b,i} <dL/dq_{b,h,i}, q_{b,h,i}> from arp_backward's dq. */
+arp_status arp_adascale_lambda(int32_t heads, const float* tau, const float* gamma, int64_t L,
+                               int64_t L_ref, float* lambda);
 
 /* Bytes of the angle scan's look-back state for desc (0 when desc is invalid).
  * The state must be zero before first use; every call leaves it ready for the next. */

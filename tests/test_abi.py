@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = b.lib()
-    assert L.arp_abi_version() == 1
+    assert L.arp_abi_version() == 2
     for s in range(6):
         assert L.arp_status_string(s)
     assert L.arp_status_string(99) == b"unknown status"
@@ -371,3 +371,45 @@ def test_decode_cache_checks_token_and_prompt_shapes():
     gated = b.DecodeCache(1, 2, 64, 64, forget=True, device=torch.device("cpu"))
     with pytest.raises(ValueError, match="logf"):
         gated.step(0, tok, tok, tok, phi)
+
+
+def test_head_scale_flag_and_pointer_must_agree():
+    L = b.lib()
+    d = _desc()
+    d.flags |= b.HEAD_SCALE
+    assert L.arp_check(ctypes.byref(d)) == b.ERR_INVALID_ARG      # flag without the array
+    d.head_scale = A
+    assert L.arp_check(ctypes.byref(d)) == b.OK
+    d.head_scale = M
+    assert L.arp_check(ctypes.byref(d)) == b.ERR_ALIGNMENT
+    d = _desc()
+    d.head_scale = A
+    assert L.arp_check(ctypes.byref(d)) == b.ERR_INVALID_ARG      # array without the flag
+    assert ctypes.sizeof(b.Desc) == 40 and b.ABI_VERSION == L.arp_abi_version() == 2
+
+
+def test_adascale_lambda_host_routine_matches_the_oracle():
+    """The library's host routine for AdaScale's schedule against the oracle's
+    fp64 evaluation (both written from AdaRoPE Sec. 3.3), rounded once to fp32."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(3)
+    tau = rng.uniform(0.5, 2.0, 16).astype(np.float32)
+    gamma = rng.uniform(-1.0, 3.0, 16).astype(np.float32)
+    for L_, ref in ((1024, 4096), (16384, 1024), (1 << 20, 2048), (4096, 4096)):
+        got = b.adascale_lambda(tau, gamma, L_, ref).numpy()
+        want = oracle.adascale_lambda(tau.astype(np.float64), gamma.astype(np.float64), L_, ref)
+        np.testing.assert_array_equal(got, want.astype(np.float32))
+    lib = b.lib()
+    f = (ctypes.c_float * 2)(1.0, 1.0)
+    out = (ctypes.c_float * 2)()
+    assert lib.arp_adascale_lambda(0, f, f, 10, 10, out) == b.ERR_INVALID_ARG
+    assert lib.arp_adascale_lambda(2, f, f, 0, 10, out) == b.ERR_INVALID_ARG
+    assert lib.arp_adascale_lambda(2, f, f, 10, 0, out) == b.ERR_INVALID_ARG
+    assert lib.arp_adascale_lambda(2, None, f, 10, 10, out) == b.ERR_INVALID_ARG
+    bad = (ctypes.c_float * 2)(1.0, 0.0)
+    assert lib.arp_adascale_lambda(2, bad, f, 10, 10, out) == b.ERR_INVALID_ARG   # tau = 0
+    bad = (ctypes.c_float * 2)(1.0, float("nan"))
+    assert lib.arp_adascale_lambda(2, f, bad, 10, 10, out) == b.ERR_INVALID_ARG   # gamma NaN
+    assert lib.arp_adascale_lambda(2, f, f, 10, 10, out) == b.OK
+    assert abs(out[0] - 0.6931472) < 1e-6
