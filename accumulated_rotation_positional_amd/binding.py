@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libarp.so")
 
 # Status codes and flags of include/arp.h.
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_WORKSPACE, ERR_HIP = range(6)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = range(7)
 DTYPE_F32, DTYPE_BF16 = 0, 1
 ROTATE_QK = 0x1
 ROTATE_V = 0x2
@@ -42,7 +42,7 @@ EXPORTS = ("arp_abi_version", "arp_status_string", "arp_check", "arp_scan_state_
            "arp_backward", "arp_decode_workspace_bytes", "arp_decode_prefill", "arp_decode_step",
            "arp_forward_ex", "arp_angle_scan_random", "arp_angle_scan_tokens",
            "arp_angle_scan_const", "arp_random_phi", "arp_backward_ex", "arp_decode_prefill_ex",
-           "arp_decode_step_ex", "arp_adascale_lambda")
+           "arp_decode_step_ex", "arp_adascale_lambda", "arp_forward_noalloc")
 
 
 class ArpError(RuntimeError):
@@ -101,6 +101,7 @@ def lib() -> ctypes.CDLL:
                 "arp_random_phi": ([D, U64, U64, P, P, P], ctypes.c_int),
                 "arp_adascale_lambda": ([ctypes.c_int32, P, P, ctypes.c_int64, ctypes.c_int64, P],
                                         ctypes.c_int),
+                "arp_forward_noalloc": ([D, P, P, P, P, P, P, P, P], ctypes.c_int),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -436,6 +437,31 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.Tensor
                                             _ptr(phi), _ptr(alibi), _ptr(theta), _ptr(out),
                                             _ptr(state), _nbytes(state), _ptr(ws), _nbytes(ws),
                                             _stream(q.device)))
+    return out, theta
+
+
+def forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: torch.Tensor, *,
+                    rotate_qk: bool = True, rotate_v: bool = False,
+                    alibi: torch.Tensor | None = None, scale: float | None = None,
+                    exclusive: bool = False, fused: bool = False, out: torch.Tensor | None = None,
+                    theta: torch.Tensor | None = None, head_scale: torch.Tensor | None = None):
+    """forward() through arp_forward_noalloc: no scan state or workspace from
+    the caller (the library's own device scratch).  Allocates only the outputs
+    it is not given; pass out and theta to allocate nothing."""
+    _check_phi_heads(q, phi)
+    flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi is not None,
+                      shared_phi=phi.shape[1] == 1 and q.shape[1] != 1, exclusive=exclusive,
+                      fused=fused)
+    desc = desc_for(q, flags, scale, head_scale)
+    _check_qkv(desc, q=q, k=k, v=v, out=out)
+    _check_angles(desc, phi=phi, theta=theta)
+    _check_alibi(desc, alibi)
+    _require_gpu(q, k, v, phi, alibi, out, theta)
+    out = torch.empty_like(q) if out is None else out
+    theta = torch.empty_like(phi) if theta is None else theta
+    _check("arp_forward_noalloc", lib().arp_forward_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(phi), _ptr(alibi), _ptr(theta),
+        _ptr(out), _stream(q.device)))
     return out, theta
 
 

@@ -7,6 +7,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "arp_internal.hpp"
 
 namespace arp {
@@ -143,6 +145,8 @@ const char* arp_status_string(int status) {
       return "pointer misaligned (tensors: 16 bytes; scan state and workspaces: 256 bytes)";
     case ARP_ERR_WORKSPACE: return "workspace missing or too small";
     case ARP_ERR_HIP: return "HIP launch failed";
+    case ARP_ERR_SCRATCH:
+      return "problem exceeds the no-alloc scratch (24 MiB scan state, 40 MiB operands)";
     default: return "unknown status";
   }
 }
@@ -628,3 +632,82 @@ arp_status arp_rotate(const arp_desc* desc, const void* x, const float* theta, f
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The no-alloc forward: arp_forward with its scan state and operand workspace
+// in a library-owned device array instead of caller buffers, for callers that
+// cannot allocate.  Host code never uses the array's name as an address: per
+// device, the first call takes its device address with hipGetSymbolAddress
+// and every later call uses that pointer.
+// ---------------------------------------------------------------------------
+namespace arp {
+namespace {
+
+constexpr size_t NOALLOC_STATE_BYTES = size_t(24) << 20;  // look-back status words
+constexpr size_t NOALLOC_WS_BYTES = size_t(40) << 20;     // rotated bf16 operands
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
+// One copy per GPU the library runs on, held until the process ends.
+__device__ __align__(256) uint8_t scratch[NOALLOC_STATE_BYTES + NOALLOC_WS_BYTES];
+
+// Zero fill of the scan-state region (a kernel, not a memset, so that a
+// first call made under graph capture records a kernel node).
+__global__ __launch_bounds__(256) void noalloc_clear_kernel(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct ScratchSlot {
+  std::once_flag once;
+  uint8_t* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[NOALLOC_MAX_DEVICES];
+
+// The current device's scratch address; on the first call on a device, also
+// clears the scan-state region on the caller's stream (the scan leaves the
+// state ready for the next call from then on).
+hipError_t scratch_on_device(hipStream_t stream, uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hipErrorInvalidDevice;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&] {
+    void* p = nullptr;
+    slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (slot.err != hipSuccess) return;
+    slot.ptr = static_cast<uint8_t*>(p);
+    hipLaunchKernelGGL(noalloc_clear_kernel, dim3(1024), dim3(256), 0, stream,
+                       reinterpret_cast<uint4*>(slot.ptr), NOALLOC_STATE_BYTES / 16);
+    slot.err = hipGetLastError();
+  });
+  if (slot.err != hipSuccess) return slot.err;
+  *out = slot.ptr;
+  return hipSuccess;
+}
+
+}  // namespace
+}  // namespace arp
+
+extern "C" arp_status arp_forward_noalloc(const arp_desc* desc, const void* q, const void* k,
+                                          const void* v, const float* phi, const float* alibi,
+                                          float* theta, void* o, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (gated(g)) return ARP_ERR_INVALID_ARG;  // as arp_forward
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || phi == nullptr ||
+      theta == nullptr || ((g.flags & ARP_ALIBI) && alibi == nullptr))
+    return ARP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(phi) ||
+      !aligned16(theta) || (alibi && !aligned16(alibi)))
+    return ARP_ERR_ALIGNMENT;
+  if (align_up(scan_state_bytes(g)) > NOALLOC_STATE_BYTES ||
+      workspace_layout(g).total > NOALLOC_WS_BYTES)
+    return ARP_ERR_SCRATCH;
+  uint8_t* base = nullptr;
+  if (scratch_on_device((hipStream_t)stream, &base) != hipSuccess) return ARP_ERR_HIP;
+  return arp_forward(desc, q, k, v, phi, alibi, theta, o, base, NOALLOC_STATE_BYTES,
+                     base + NOALLOC_STATE_BYTES, NOALLOC_WS_BYTES, stream);
+}

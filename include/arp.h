@@ -69,7 +69,8 @@ typedef enum arp_status {
   ARP_ERR_ALIGNMENT = 3,   /* a tensor pointer is not 16-byte aligned, or a scan
                               state or workspace not 256-byte aligned */
   ARP_ERR_WORKSPACE = 4,   /* scan state or workspace null or smaller than required */
-  ARP_ERR_HIP = 5          /* a kernel launch failed */
+  ARP_ERR_HIP = 5,         /* a kernel launch failed */
+  ARP_ERR_SCRATCH = 6      /* arp_forward_noalloc: the problem exceeds its scratch */
 } arp_status;
 
 typedef enum arp_dtype {
@@ -227,6 +228,23 @@ arp_status arp_forward(const arp_desc* desc, const void* q, const void* k, const
                        const float* phi, const float* alibi, float* theta, void* o,
                        void* scan_state, size_t scan_state_bytes, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate or pass buffers -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: arp_forward
+ * with the scan state and the operand workspace in a device array the library
+ * owns (one per GPU, 64 MiB, held until the process ends), so the call needs
+ * nothing but the inputs and outputs and allocates nothing.  Same arguments,
+ * flags, kernels and results as arp_forward (ARP_FUSED_ROTATION included).
+ * Limits: arp_scan_state_bytes(desc) <= 24 MiB and arp_workspace_bytes(desc)
+ * <= 40 MiB, else ARP_ERR_SCRATCH with nothing launched (the pre-rotation
+ * path's operands take 6 head_dim bytes per token and head: ~109 thousand
+ * tokens x heads fit at head_dim 64, e.g. 8 x 8 heads at 1024 tokens, half
+ * that at 128; ARP_FUSED_ROTATION and fp32 I/O need no operand workspace).  The first call on a device clears the scan-state region with a
+ * kernel on its stream; every call on that GPU shares the array, so calls that
+ * overlap on one GPU (different streams or threads without ordering) race. */
+arp_status arp_forward_noalloc(const arp_desc* desc, const void* q, const void* k, const void* v,
+                               const float* phi, const float* alibi, float* theta, void* o,
+                               void* stream);
 
 /* Training forward (bf16 pre-rotation path, or fp32 I/O): arp_forward that
  * also writes lse[b,h,i] (float32 [batch, heads, seqlen]), the base-2

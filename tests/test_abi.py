@@ -30,8 +30,8 @@ def test_library_exports_every_declared_function():
 def test_abi_version_and_status_strings():
     L = b.lib()
     assert L.arp_abi_version() == 2
-    for s in range(6):
-        assert L.arp_status_string(s)
+    for s in range(7):
+        assert L.arp_status_string(s) != b"unknown status"
     assert L.arp_status_string(99) == b"unknown status"
 
 
@@ -413,3 +413,21 @@ def test_adascale_lambda_host_routine_matches_the_oracle():
     assert lib.arp_adascale_lambda(2, f, bad, 10, 10, out) == b.ERR_INVALID_ARG   # gamma NaN
     assert lib.arp_adascale_lambda(2, f, f, 10, 10, out) == b.OK
     assert abs(out[0] - 0.6931472) < 1e-6
+
+
+def test_noalloc_forward_validates_before_touching_the_device():
+    """arp_forward_noalloc checks its arguments and its scratch limits on the
+    host (fake addresses: nothing is launched, no device is touched)."""
+    L = b.lib()
+    d = _desc(batch=2, heads=8, seqlen=16384)
+    by = ctypes.byref(d)
+    assert L.arp_forward_noalloc(by, A, A, A, None, None, A, A, None) == b.ERR_INVALID_ARG
+    assert L.arp_forward_noalloc(by, A, A, A, A, None, A, M, None) == b.ERR_ALIGNMENT
+    # 96 MiB of pre-rotated operands exceed the 40 MiB operand scratch
+    assert L.arp_forward_noalloc(by, A, A, A, A, None, A, A, None) == b.ERR_SCRATCH
+    # 4 x 32 heads at 32768 tokens (d = 128): a scan state beyond 24 MiB, even fused
+    big = _desc(batch=4, heads=32, seqlen=32768, head_dim=128, flags=b.ROTATE_QK | b.FUSED_ROTATION)
+    assert L.arp_scan_state_bytes(ctypes.byref(big)) > (24 << 20)
+    assert L.arp_forward_noalloc(ctypes.byref(big), A, A, A, A, None, A, A, None) == b.ERR_SCRATCH
+    gated = _desc(flags=b.ROTATE_QK | b.FORGET_GATE)
+    assert L.arp_forward_noalloc(ctypes.byref(gated), A, A, A, A, None, A, A, None) == b.ERR_INVALID_ARG
