@@ -569,7 +569,7 @@ def backward_ex(desc: Desc, q, k, v, phi, theta, o, lse, dout, alibi=None, logf=
 class DecodeCache:
     """Key/value cache (pre-rotated bf16 [B, H, capacity, d]), the angle state
     (uint64 [B, Hphi, d/2]) and the step workspace of one decoding stream;
-    with forget=True also the gate-prefix cache (fp32 [B, H, capacity]) and the
+    with forget=True also the gate-prefix cache (fp64 [B, H, capacity]) and the
     gate state (fp64 [B, H])."""
 
     def __init__(self, batch: int, heads: int, capacity: int, head_dim: int, *, phi_heads=None,
@@ -581,7 +581,7 @@ class DecodeCache:
         flags = flags_for(rotate_qk=rotate_qk, rotate_v=rotate_v, alibi=alibi,
                           shared_phi=hphi == 1 and heads != 1, exclusive=exclusive, forget=forget)
         self.forget = forget
-        self.gcache = (torch.zeros(batch, heads, capacity, dtype=torch.float32, device=device)
+        self.gcache = (torch.zeros(batch, heads, capacity, dtype=torch.float64, device=device)
                        if forget else None)
         self.gstate = torch.zeros(batch, heads, dtype=torch.float64, device=device) if forget else None
         self.desc = make_desc(batch, heads, capacity, head_dim, torch.bfloat16, flags, scale,

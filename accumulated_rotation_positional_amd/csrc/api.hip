@@ -89,6 +89,8 @@ WorkspaceLayout workspace_layout(const Geometry& g) {
     if (g.flags & ARP_FORGET_GATE) {
       lay.gate_off = off;
       off += align_up((size_t)g.B * g.H * g.Lp * sizeof(float));
+      lay.gate_base_off = off;
+      off += align_up((size_t)g.B * g.H * (g.Lp / GATE_TILE) * sizeof(double));
       lay.gate_tot_off = off;
       off += align_up((size_t)g.B * g.H * gate_chunks(g) * sizeof(double));
     }
@@ -118,7 +120,9 @@ BwdWorkspaceLayout bwd_workspace_layout(const Geometry& g) {
   if (g.flags & ARP_FORGET_GATE) {
     const size_t per_token = align_up((size_t)g.B * g.H * g.Lp * sizeof(float));
     lay.gate_off = off;
-    lay.gate_tot_off = off + per_token;
+    lay.gate_base_off = off + per_token;
+    lay.gate_tot_off =
+        lay.gate_base_off + align_up((size_t)g.B * g.H * (g.Lp / GATE_TILE) * sizeof(double));
     off = lay.gate_tot_off + align_up((size_t)g.B * g.H * gate_chunks(g) * sizeof(double));
     lay.colsum_off = off;
     lay.rowsum_off = off + per_token;
@@ -282,7 +286,7 @@ arp_status arp_attn_rotated(const arp_desc* desc, const float* theta, const floa
       g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
       reinterpret_cast<const uint16_t*>(ws + lay.k_off),
       reinterpret_cast<const uint16_t*>(ws + lay.vt_off),
-      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi, nullptr,
+      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi, nullptr, nullptr,
       static_cast<uint16_t*>(o), nullptr, (hipStream_t)stream));
 }
 
@@ -369,7 +373,7 @@ arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k,
       g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
       reinterpret_cast<const uint16_t*>(ws + lay.k_off),
       reinterpret_cast<const uint16_t*>(ws + lay.vt_off),
-      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi, nullptr,
+      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi, nullptr, nullptr,
       static_cast<uint16_t*>(o), lse, (hipStream_t)stream));
 }
 
@@ -411,14 +415,15 @@ arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, co
                         reinterpret_cast<float*>(ws + lay.kmax_off), s);
   if (e != hipSuccess) return ARP_ERR_HIP;
   float* gate2 = gated(g) ? reinterpret_cast<float*>(ws + lay.gate_off) : nullptr;
-  if (gated(g) && launch_gate_scan(g, logf, gate2, reinterpret_cast<double*>(ws + lay.gate_tot_off),
-                                   s) != hipSuccess)
+  double* gbase = gated(g) ? reinterpret_cast<double*>(ws + lay.gate_base_off) : nullptr;
+  if (gated(g) && launch_gate_scan(g, logf, gate2, gbase,
+                                   reinterpret_cast<double*>(ws + lay.gate_tot_off), s) != hipSuccess)
     return ARP_ERR_HIP;
   return hip_status(launch_attn_bf16_rotated(
       g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
       reinterpret_cast<const uint16_t*>(ws + lay.k_off),
       reinterpret_cast<const uint16_t*>(ws + lay.vt_off),
-      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi, gate2,
+      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi, gate2, gbase,
       static_cast<uint16_t*>(o), lse, s));
 }
 
@@ -495,17 +500,21 @@ arp_status arp_backward_ex(const arp_desc* desc, const void* q, const void* k, c
   a.totals = reinterpret_cast<float*>(ws + lay.totals_off);
   a.ops = BwdOperands{blk(0), blk(1), blk(2), blk(3), blk(4), blk(5), blk(6),
                       reinterpret_cast<float*>(ws + lay.stats_off),
-                      reinterpret_cast<float*>(ws + lay.tstat_off), nullptr, nullptr, nullptr};
+                      reinterpret_cast<float*>(ws + lay.tstat_off), nullptr, nullptr, nullptr,
+                      nullptr};
   hipStream_t s = (hipStream_t)stream;
   if (gated(g)) {
     float* gate2 = reinterpret_cast<float*>(ws + lay.gate_off);
     a.logf = logf;
     a.dlogf = dlogf;
     a.gate_tot = reinterpret_cast<double*>(ws + lay.gate_tot_off);
+    double* gbase = reinterpret_cast<double*>(ws + lay.gate_base_off);
     a.ops.gate2 = gate2;
+    a.ops.gbase = gbase;
     a.ops.colsum = reinterpret_cast<float*>(ws + lay.colsum_off);
     a.ops.rowsum = reinterpret_cast<float*>(ws + lay.rowsum_off);
-    if ((st = hip_status(launch_gate_scan(g, logf, gate2, a.gate_tot, s))) != ARP_OK) return st;
+    if ((st = hip_status(launch_gate_scan(g, logf, gate2, gbase, a.gate_tot, s))) != ARP_OK)
+      return st;
   }
   return hip_status(launch_backward_bf16(g, a, s));
 }
@@ -530,7 +539,7 @@ size_t arp_decode_workspace_bytes(const arp_desc* desc) {
 
 arp_status arp_decode_prefill_ex(const arp_desc* desc, int32_t len, const void* k, const void* v,
                                  const float* phi, const float* theta, const float* logf,
-                                 void* kcache, void* vcache, uint64_t* state, float* gcache,
+                                 void* kcache, void* vcache, uint64_t* state, double* gcache,
                                  double* gstate, void* stream) {
   Geometry g;
   arp_status st = make_geometry(desc, &g);
@@ -568,7 +577,7 @@ arp_status arp_decode_prefill(const arp_desc* desc, int32_t len, const void* k, 
 arp_status arp_decode_step_ex(const arp_desc* desc, int32_t pos, const void* q, const void* k,
                               const void* v, const float* phi, const float* alibi,
                               const float* logf, uint64_t* state, float* theta, void* kcache,
-                              void* vcache, float* gcache, double* gstate, void* o,
+                              void* vcache, double* gcache, double* gstate, void* o,
                               void* workspace, size_t workspace_bytes, void* stream) {
   Geometry g;
   arp_status st = make_geometry(desc, &g);

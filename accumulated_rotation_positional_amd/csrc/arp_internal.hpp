@@ -38,7 +38,9 @@ size_t scan_state_bytes(const Geometry& g);  // upper bound over every plan
 struct WorkspaceLayout {
   size_t q_off, k_off, vt_off, operand_bytes;  // each operand block
   size_t kmax_off;                             // float [B*H][Lp/64]: max |k~| per key tile
-  size_t gate_off;                             // float [B*H][Lp]: gate prefix (ARP_FORGET_GATE)
+  size_t gate_off;                             // float [B*H][Lp]: gate prefix within its
+                                               //   64-token tile (ARP_FORGET_GATE)
+  size_t gate_base_off;                        // double [B*H][Lp/64]: the prefix before each tile
   size_t gate_tot_off;                         // double [B*H][gate_chunks]: chunk totals
   size_t total;
 };
@@ -68,15 +70,21 @@ hipError_t launch_rotate_qkv(const Geometry& g, const void* q, const void* k, co
                              float* kmax, hipStream_t stream);
 hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                                     const uint16_t* vt, const float* kmax, const float* theta,
-                                    const float* alibi, const float* gate2, uint16_t* o,
-                                    float* lse, hipStream_t stream);
-// Forget gates: gate2[b*H + h][t] = log2 e * sum_{s <= t} min(logf[b, h, s], 0), fp64
-// accumulation, padded to Lp with the last value; totals holds one double per
+                                    const float* alibi, const float* gate2, const double* gbase,
+                                    uint16_t* o, float* lse, hipStream_t stream);
+// Forget gates: with G_t = log2 e * sum_{s <= t} min(logf[b, h, s], 0) (fp64
+// accumulation; padded to Lp with the last value), the prefix is kept relative
+// to 64-token tiles so that it stays exact however long the sequence:
+//   gbase[b*H + h][c] = G_{64c - 1} (0 for c = 0), double
+//   gate2[b*H + h][t] = fp32(G_t - gbase[t / 64])   (|.| <= 64 max|log f| log2 e)
+// and a logit's bias G_i - G_j = fp32(gbase[i/64] - gbase[j/64]) + gate2[i] -
+// gate2[j], the tile difference rounded once.  totals holds one double per
 // (b*H + h, chunk of GATE_CHUNK tokens).
 constexpr int GATE_CHUNK = 1024;
+constexpr int GATE_TILE = 64;
 inline int gate_chunks(const Geometry& g) { return (g.Lp + GATE_CHUNK - 1) / GATE_CHUNK; }
-hipError_t launch_gate_scan(const Geometry& g, const float* logf, float* gate2, double* totals,
-                            hipStream_t stream);
+hipError_t launch_gate_scan(const Geometry& g, const float* logf, float* gate2, double* gbase,
+                            double* totals, hipStream_t stream);
 hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const float* theta, const float* alibi,
                                   uint16_t* o, hipStream_t stream);
@@ -104,12 +112,14 @@ struct BwdOperands {
   uint16_t* doutT;
   float* stats;
   float* tstat;  // per 64-token tile: max |q~ scale log2 e|, max |k~|, max_i (-lse_i - slope2 i), 0
-  // forget gates only (else null), fp32 [B*H, Lp]: the gate prefix G (log2 e
-  // times the prefix sums of log f, as in the forward), and the sums of dS
-  // over each key's column and over each query's row
+  // forget gates only (else null): the gate prefix in the forward's tiled
+  // form (gate2 fp32 [B*H, Lp] within each 64-token tile, gbase double
+  // [B*H, Lp/64] the prefix before each tile), and fp32 [B*H, Lp] the sums of
+  // dS over each key's column and over each query's row
   const float* gate2;
   float* colsum;
   float* rowsum;
+  const double* gbase;
 };
 struct BwdArgs {
   const uint16_t *q, *k, *v, *o, *dout;  // caller tensors [B, H, L, D]
@@ -126,7 +136,7 @@ struct BwdArgs {
 struct BwdWorkspaceLayout {
   size_t operand_bytes;  // one bf16 [B*H, Lp, D] block
   size_t stats_off, tstat_off, totals_off;
-  size_t gate_off, gate_tot_off, colsum_off, rowsum_off;  // gated only
+  size_t gate_off, gate_base_off, gate_tot_off, colsum_off, rowsum_off;  // gated only
   size_t total;
 };
 BwdWorkspaceLayout bwd_workspace_layout(const Geometry& g);
@@ -156,14 +166,14 @@ struct DecodeArgs {
   uint16_t* o;                  // [B, H, D]
   float* part;                  // workspace: [B*H, ceil(L/256), D + 2] partial results
   const float* logf;            // [B, H] the new token's log forget gate (gated only)
-  float* gcache;                // [B, H, L] gate prefixes G_j of the cached keys (gated only)
+  double* gcache;               // [B, H, L] gate prefixes G_j of the cached keys (gated only)
   double* gstate;               // [B, H] running sum of min(log f, 0) (gated only)
 };
 size_t decode_workspace_bytes(const Geometry& g);
 hipError_t launch_decode_prefill(const Geometry& g, int len, const uint16_t* k, const uint16_t* v,
                                  const float* phi, const float* theta, uint16_t* kcache,
                                  uint16_t* vcache, uint64_t* state, const float* logf,
-                                 float* gcache, double* gstate, hipStream_t stream);
+                                 double* gcache, double* gstate, hipStream_t stream);
 hipError_t launch_decode_step(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace arp

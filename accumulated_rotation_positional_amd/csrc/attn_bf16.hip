@@ -64,7 +64,11 @@ constexpr float ZGAP = 160.0f;
 // v); row maxima are always taken exactly.
 // BIAS: bit 0 the distance bias -m_h (i - j), bit 1 the forget-gate bias
 // G_i - G_j, with G = log2 e * (prefix sums of log f) from the gate pass
-// ([B*H, Lp] in gate2; non-increasing, so the bias never raises a score).
+// (non-increasing, so the bias never raises a score), read in its tiled
+// form: gate2 [B*H, Lp] the offset of G_t within its 64-token tile, gbase
+// [B*H, Lp/64] (fp64) the prefix before each tile, so G_i - G_j =
+// D + gate2[i] - gate2[j] with D = fp32(gbase[i/64] - gbase[j/64]) formed once
+// per (wave, key tile).
 // One query tile (logical index `logical`, mapped to (head, query tile) below)
 // with the workgroup's LDS ring smem.
 template <int D, int QPW, int NW, int NST, int MINB, bool FUSED, int BIAS, bool ROTV>
@@ -72,9 +76,9 @@ __device__ __forceinline__ void attn_tile(
     int logical, uint8_t* smem, const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
     const float* __restrict__ theta, const float* __restrict__ alibi,
-    const float* __restrict__ gate2, uint16_t* __restrict__ o, float* __restrict__ lse, int L,
-    int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk, float qscale0,
-    const float* __restrict__ hscale) {
+    const float* __restrict__ gate2, const double* __restrict__ gbase, uint16_t* __restrict__ o,
+    float* __restrict__ lse, int L, int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk,
+    float qscale0, const float* __restrict__ hscale) {
   constexpr bool ALIBI = (BIAS & 1) != 0;
   constexpr bool FORGET = (BIAS & 2) != 0;
   static_assert(!(FUSED && FORGET), "the gate bias needs the pre-rotation path");
@@ -286,8 +290,9 @@ __device__ __forceinline__ void attn_tile(
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
     gq[qb] = FORGET ? gate2[(size_t)bh * Lp + min(qw + 32 * qb + ln, Lp - 1)] : 0.f;
-  // The accumulator input of Q K^T: -m, plus the query's gate prefix G_i
-  // with a gate bias (so only -G_j is left to add per logit).
+  // The accumulator input of Q K^T: -m, plus with a gate bias the query's
+  // gate offset and the tile base difference D (so only the key's offset is
+  // left to subtract per logit; set per key tile in the walk below).
   float mrun[QB], lsum[QB];
   f32x16 cneg[QB];
 #pragma unroll
@@ -376,7 +381,7 @@ __device__ __forceinline__ void attn_tile(
               const int koff = 32 * kb + 16 * h2 + 4 * (e >> 2) + (e & 3);
               float x = s[kb][qb][r];
               if (ALIBI) x += fmaf(slope2, (float)koff, fb);
-              if (FORGET) x -= (e < 4 ? ga[e] : gc[e - 4]);  // G_i rode in with the product
+              if (FORGET) x -= (e < 4 ? ga[e] : gc[e - 4]);  // G_i - G_j's other terms rode in
               if (diag && koff + base > 0) x = -INFINITY;
               s[kb][qb][r] = x;
             }
@@ -522,7 +527,15 @@ __device__ __forceinline__ void attn_tile(
             float bb = 0.f;
             if (ALIBI)
               bb = fmaxf(slope2 * (float)(t * BN - i), slope2 * (float)(t * BN + BN - 1 - i));
-            if (FORGET) bb += gq[qb] - gl;
+            if (FORGET) {
+              // the tile base difference, rounded once; the query rows of
+              // block qb share one 64-token tile
+              const double* gb = gbase + (size_t)bh * (Lp / BN);
+              const float dt = (float)(gb[min((qw + 32 * qb) / BN, Lp / BN - 1)] - gb[t]);
+              bb += gq[qb] + dt - gl;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) cneg[qb][r] = gq[qb] + dt - mrun[qb];
+            }
             tb[qb] = fmaf(qn[qb], km, bb);
             dead &= (i >= L) || (fmaf(qn[qb], kglob, bb) < mrun[qb] - ZGAP);
           }
@@ -609,9 +622,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
     const float* __restrict__ theta, const float* __restrict__ alibi,
-    const float* __restrict__ gate2, uint16_t* __restrict__ o, float* __restrict__ lse, int L,
-    int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk, float qscale, int paired,
-    const float* __restrict__ hscale) {
+    const float* __restrict__ gate2, const double* __restrict__ gbase, uint16_t* __restrict__ o,
+    float* __restrict__ lse, int L, int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk,
+    float qscale, int paired, const float* __restrict__ hscale) {
   constexpr int STAGE = BN * D * 2 + D * BN * 2 + (((BIAS & 2) != 0) ? BN * 4 : 0);  // as in attn_tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
   constexpr bool SPREAD = (BIAS != 0) && !FUSED;
@@ -620,25 +633,25 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
   if (PAIRABLE && paired) {
     const int x = (int)(blockIdx.x % 8), c = (int)(blockIdx.x / 8);
     attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(x * per + c, smem, qr, kr, vt, kmax, theta,
-                                                        alibi, gate2, o, lse, L, Lp, H, Hphi, nqt,
+                                                        alibi, gate2, gbase, o, lse, L, Lp, H, Hphi, nqt,
                                                         total_tiles, rot_qk, qscale, hscale);
     __syncthreads();  // every wave is done with the LDS ring before it is refilled
     attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(x * per + per - 1 - c, smem, qr, kr, vt,
-                                                        kmax, theta, alibi, gate2, o, lse, L, Lp, H,
+                                                        kmax, theta, alibi, gate2, gbase, o, lse, L, Lp, H,
                                                         Hphi, nqt, total_tiles, rot_qk, qscale, hscale);
     return;
   }
   const int logical = SPREAD ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(logical, smem, qr, kr, vt, kmax, theta, alibi,
-                                                      gate2, o, lse, L, Lp, H, Hphi, nqt,
+                                                      gate2, gbase, o, lse, L, Lp, H, Hphi, nqt,
                                                       total_tiles, rot_qk, qscale, hscale);
 }
 
 template <int D, int QPW, int NW, int NST, int MINB, bool FUSED>
 hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                            const uint16_t* vt, const float* kmax, const float* theta,
-                           const float* alibi, const float* gate2, uint16_t* o, float* lse,
-                           hipStream_t stream) {
+                           const float* alibi, const float* gate2, const double* gbase, uint16_t* o,
+                           float* lse, hipStream_t stream) {
   constexpr int BM = QPW * NW;
   const int nqt = (g.L + BM - 1) / BM;
   const int total = g.B * g.H * nqt;
@@ -650,7 +663,8 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
   const float qscale = g.scale * LOG2E;
 #define ARP_BF16_LAUNCH(A, R)                                                                  \
   hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, MINB, FUSED, A, R>), dim3(grid),      \
-                     dim3(NW * 64), 0, stream, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,   \
+                     dim3(NW * 64), 0, stream, qr, kr, vt, kmax, theta, alibi, gate2, gbase, o, \
+                     lse,                                                                       \
                      g.L, g.Lp, g.H, g.Hphi, nqt, total, rqk, qscale, paired, g.hscale)
 #define ARP_BF16_LAUNCH_R(A) \
   do {                       \
@@ -686,8 +700,8 @@ static int device_cus() {
 
 hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
                                     const uint16_t* vt, const float* kmax, const float* theta,
-                                    const float* alibi, const float* gate2, uint16_t* o,
-                                    float* lse, hipStream_t stream) {
+                                    const float* alibi, const float* gate2, const double* gbase,
+                                    uint16_t* o, float* lse, hipStream_t stream) {
   if (g.D == 64) {
     // Two shapes, every row computed the same way in both (bit-identical
     // results):
@@ -703,9 +717,9 @@ hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const
     const long wg512 = (long)g.B * g.H * ((g.L + 511) / 512);
     const bool biased = (g.flags & (ARP_ALIBI | ARP_FORGET_GATE)) != 0;
     if (!biased && g.L >= 16384 && wg512 >= 2L * device_cus())
-      return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o,
+      return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, gbase, o,
                                                      lse, stream);
-    return launch_bf16_cfg<64, 32, 4, 2, 2, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,
+    return launch_bf16_cfg<64, 32, 4, 2, 2, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, gbase, o, lse,
                                                    stream);
   }
   // d = 128: 256-query workgroups of 8 waves x 32 queries for unbiased grids
@@ -715,9 +729,9 @@ hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const
   const long wg256 = (long)g.B * g.H * ((g.L + 255) / 256);
   const bool biased = (g.flags & (ARP_ALIBI | ARP_FORGET_GATE)) != 0;
   if (!biased && wg256 >= 4L * device_cus())
-    return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o,
+    return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, gbase, o,
                                                     lse, stream);
-  return launch_bf16_cfg<128, 32, 4, 2, 2, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, o, lse,
+  return launch_bf16_cfg<128, 32, 4, 2, 2, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, gbase, o, lse,
                                                   stream);
 }
 
@@ -725,8 +739,8 @@ hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const ui
                                   const uint16_t* v, const float* theta, const float* alibi,
                                   uint16_t* o, hipStream_t stream) {
   if (g.D == 64)
-    return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, nullptr, o, nullptr, stream);
-  return launch_bf16_cfg<128, 32, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, nullptr, o, nullptr, stream);
+    return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
+  return launch_bf16_cfg<128, 32, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
 }
 
 }  // namespace arp

@@ -167,8 +167,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     }
     if (c == 0) {
       const float nl = (tok < L) ? -lse[(size_t)bh * L + tok] : -INFINITY;
-      // the gate prefix G_i joins -lse_i (the walk bounds below leave it
-      // out: G_i - G_j <= 0 for j <= i, so they stay upper bounds)
+      // the query's gate offset within its 64-token tile joins -lse_i (the
+      // tile base difference is added per block; the walk bounds below leave
+      // the gates out: G_i - G_j <= 0 for j <= i, so they stay upper bounds)
       stats[r] = (ops.gate2 != nullptr && tok < L) ? nl + ops.gate2[(size_t)bh * Lp + tok] : nl;
       stats[TILE + r] = (tok < L) ? -dsum : 0.f;
       s_c[r] = nl - slope2 * (float)tok;
@@ -353,8 +354,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dkt[db][r] = dvt[db][r] = 0.f;
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
-  // the key's gate prefix G_j, subtracted from every logit of its column
+  // the key's gate offset within its 64-token tile, subtracted from every
+  // logit of its column with the (query tile, key tile) base difference
   const float gj = GATE ? ops.gate2[(size_t)bh * Lp + min(j, Lp - 1)] : 0.f;
+  const double* gbase_bh = GATE ? ops.gbase + (size_t)bh * (Lp / TILE) : nullptr;
+  const double gbase_k = GATE ? gbase_bh[kw / TILE] : 0.0;  // the wave's keys share a tile
   float csum = 0.f;  // sum of dS over this lane's part of the key's column
 
   // Query tiles from the last one down: the workgroups that run at the same
@@ -396,6 +400,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
     const uint8_t* tqT = st + 2 * RT;
     const uint8_t* tdoT = st + 2 * RT + CT;
     const float* sl = reinterpret_cast<const float*>(st + 2 * RT + 2 * CT);
+    // G_i - G_j = fp32(gbase[t] - gbase[key tile]) + offset_i - offset_j
+    const float dg = GATE ? (float)(gbase_bh[t] - gbase_k) - gj : 0.f;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qbase = t * TILE + 32 * qb;
@@ -419,7 +425,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
       }
       if constexpr (GATE) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) cl[r] -= gj;
+        for (int r = 0; r < 16; ++r) cl[r] += dg;
       }
       f32x16 s = cl, dp = cd;
 #pragma unroll
@@ -590,11 +596,20 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
     const uint8_t* tv = st + RT;
     const uint8_t* tkT = st + 2 * RT;
     const bool diag = (n == last_w);
+    // with gates: the (query tile, key tile) base difference joins -lse_i +
+    // the query's offset; the key offsets are subtracted per element below
+    f32x16 clt = cl;
+    if constexpr (GATE) {
+      const double* gb = ops.gbase + (size_t)bh * (Lp / TILE);
+      const float dt = (float)(gb[qw / TILE] - gb[n]);  // the wave's queries share a tile
+#pragma unroll
+      for (int r = 0; r < 16; ++r) clt[r] += dt;
+    }
     bf16x8 dsop[KS2];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      f32x16 s = cl, dp = cd;
-      if constexpr (GATE) {  // -G_j of the key of each element
+      f32x16 s = clt, dp = cd;
+      if constexpr (GATE) {  // minus the offset of the key of each element
         const float* gp = reinterpret_cast<const float*>(st + 2 * RT + CT) + 32 * kb + 8 * hf;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {

@@ -28,9 +28,10 @@
 // The attention pass is bound by HBM: it reads 2 * (t+1) * d bf16 per (b, h).
 //
 // Forget gates (ARP_FORGET_GATE): a third cache holds each key's gate prefix
-// G_j = log2 e * sum_{s <= j} min(log f_s, 0) (fp32, the forward's G), and a
-// per-(b, h) state the running sum of min(log f, 0) in fp64.  A step forms
-// G_t from the state and the new token's gate, adds G_t - G_j to each score
+// G_j = log2 e * sum_{s <= j} min(log f_s, 0) in fp64 (so G_t - G_j keeps fp32
+// precision at any context length), and a per-(b, h) state the running sum of
+// min(log f, 0) in fp64.  A step forms G_t from the state and the new token's
+// gate, adds G_t - G_j (rounded once to fp32) to each score
 // (the route's product of gates, PaTH reading notes Sec. 2.5), appends G_t
 // to the gate cache, and the combine pass advances the state.
 #include "angle_fixed.hpp"
@@ -100,12 +101,12 @@ __global__ __launch_bounds__(256) void decode_state_kernel(const float* __restri
   }
 }
 
-// Gate prefix of the prompt: gcache[bh][t] = fp32(log2 e * sum_{s <= t} min(logf[bh][s], 0))
-// for t < len and gstate[bh] = the fp64 sum over the whole prompt.  One
+// Gate prefix of the prompt: gcache[bh][t] = log2 e * sum_{s <= t} min(logf[bh][s], 0)
+// (fp64) for t < len and gstate[bh] = the fp64 sum over the whole prompt.  One
 // workgroup per (b, h) walks the prompt in chunks of 1024 tokens (four
 // consecutive tokens per thread, an in-chunk scan in fp64 plus the carry).
 __global__ __launch_bounds__(256) void decode_gate_fill_kernel(const float* __restrict__ logf,
-                                                               float* __restrict__ gcache,
+                                                               double* __restrict__ gcache,
                                                                double* __restrict__ gstate, int len,
                                                                int Lmax) {
   __shared__ double wsum[4];
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(256) void decode_gate_fill_kernel(const float* __re
     for (int u = 0; u < w; ++u) pre += wsum[u];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (t0 + e < len) gcache[(size_t)bh * Lmax + t0 + e] = (float)((pre + run[e]) * LOG2E_D);
+      if (t0 + e < len) gcache[(size_t)bh * Lmax + t0 + e] = (pre + run[e]) * LOG2E_D;
     carry += (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
     __syncthreads();  // wsum is rewritten by the next chunk
   }
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     const uint16_t* __restrict__ vin, const float* __restrict__ phi,
     const uint64_t* __restrict__ state, float* __restrict__ theta, uint16_t* __restrict__ kcache,
     uint16_t* __restrict__ vcache, const float* __restrict__ alibi, const float* __restrict__ logf,
-    float* __restrict__ gcache, const double* __restrict__ gstate, float* __restrict__ part, int H,
+    double* __restrict__ gcache, const double* __restrict__ gstate, float* __restrict__ part, int H,
     int Hphi, int Lmax, int pos, int nchunk, uint32_t flags, float qscale0,
     const float* __restrict__ hscale) {
   constexpr int CPR = D / 8;     // lanes per row
@@ -174,9 +175,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   const float qscale = hscale != nullptr ? qscale0 * hscale[h] : qscale0;
   // The new token's gate prefix G_t (every workgroup forms the same value;
   // the first one appends it to the gate cache).
-  float gt = 0.f;
+  double gt = 0.0;
   if constexpr (GATE) {
-    gt = (float)((gstate[bh] + (double)fminf(logf[bh], 0.f)) * 1.4426950408889634);
+    gt = (gstate[bh] + (double)fminf(logf[bh], 0.f)) * 1.4426950408889634;
     if (c == 0 && tid == 0) gcache[(size_t)bh * Lmax + pos] = gt;
   }
 
@@ -238,12 +239,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   // the rows' gate biases G_t - G_j (0 for row pos and beyond): lane l loads
   // the gate of the wave's row kw0 + l, and each lane takes its rows' gates
   // from the lanes that hold them
+  // (G in fp64, its difference rounded once to fp32)
   float gb[NI];
   if constexpr (GATE) {
     const int mine = kw0 + lane;
-    const float gl = (mine < pos) ? gcache[(size_t)bh * Lmax + mine] : gt;
+    const double gl = (mine < pos) ? gcache[(size_t)bh * Lmax + mine] : gt;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) gb[i] = gt - __shfl(gl, RPI * i + rg);
+    for (int i = 0; i < NI; ++i) gb[i] = (float)(gt - __shfl(gl, RPI * i + rg));
   }
   float sc[NI];
   float m = -INFINITY;
@@ -431,7 +433,7 @@ size_t decode_workspace_bytes(const Geometry& g) {
 hipError_t launch_decode_prefill(const Geometry& g, int len, const uint16_t* k, const uint16_t* v,
                                  const float* phi, const float* theta, uint16_t* kcache,
                                  uint16_t* vcache, uint64_t* state, const float* logf,
-                                 float* gcache, double* gstate, hipStream_t stream) {
+                                 double* gcache, double* gstate, hipStream_t stream) {
   if (len > 0) {
     dim3 grid((unsigned)(((size_t)len * (g.D / 8) + 255) / 256), g.B * g.H);
     if (g.D == 64)

@@ -153,9 +153,12 @@ __global__ __launch_bounds__(256) void rotate_diag_kernel(const TIn* __restrict_
 // Forget-gate prefix G_t = log2 e * sum_{s<=t} min(log f_s, 0) per (b, h), in
 // chunks of GATE_CHUNK tokens: gate_totals sums each chunk (fp64), then
 // gate_apply adds the totals of the earlier chunks to an in-chunk scan (fp64)
-// and writes G (fp32).  Padded to Lp with the last value (padded keys only
-// meet masked scores).  Loads are coalesced; each thread then scans four
-// consecutive tokens from LDS.
+// and writes G in the tiled form the attention kernels read: per 64-token
+// tile the fp64 prefix before it (gbase) and each token's fp32 offset from it
+// (gate2), so G_i - G_j keeps its fp32 precision at any sequence length.
+// Padded to Lp with the last value (padded keys only meet masked scores).
+// Loads are coalesced; each thread then scans four consecutive tokens from
+// LDS, and the 16 threads of a tile take its base from the first of them.
 constexpr int GATE_THREADS = 256;
 constexpr int GATE_PER_THREAD = GATE_CHUNK / GATE_THREADS;
 static_assert(GATE_PER_THREAD == 4, "four consecutive tokens per thread");
@@ -188,8 +191,10 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_totals_kernel(const float* 
 
 __global__ __launch_bounds__(GATE_THREADS) void gate_apply_kernel(const float* __restrict__ logf,
                                                                   const double* __restrict__ tot,
-                                                                  float* __restrict__ gate2, int L,
+                                                                  float* __restrict__ gate2,
+                                                                  double* __restrict__ gbase, int L,
                                                                   int Lp, int nch) {
+  static_assert(GATE_TILE == 16 * GATE_PER_THREAD, "a tile is 16 consecutive threads of a wave");
   __shared__ float sv[GATE_CHUNK];
   __shared__ double red[4], wsum[4];
   const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
@@ -221,23 +226,30 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_apply_kernel(const float* _
   double pre = carry + (x - run[3]);
   for (int i = 0; i < w; ++i) pre += wsum[i];
   const int t0 = c * GATE_CHUNK + GATE_PER_THREAD * tid;
+  // the prefix before this thread's 64-token tile: the exclusive prefix of
+  // the tile's first thread (lane 16 k of the wave)
+  const double tile_pre = __shfl(pre, lane & ~15);
   if (t0 < Lp) {  // Lp is a multiple of 256, so all four tokens are below it
     constexpr double LOG2E_D = 1.4426950408889634;
-    const float4 out = make_float4((float)((pre + run[0]) * LOG2E_D), (float)((pre + run[1]) * LOG2E_D),
-                                   (float)((pre + run[2]) * LOG2E_D), (float)((pre + run[3]) * LOG2E_D));
+    const double base = tile_pre * LOG2E_D;
+    const float4 out = make_float4((float)((pre + run[0]) * LOG2E_D - base),
+                                   (float)((pre + run[1]) * LOG2E_D - base),
+                                   (float)((pre + run[2]) * LOG2E_D - base),
+                                   (float)((pre + run[3]) * LOG2E_D - base));
     *reinterpret_cast<float4*>(gate2 + (size_t)bh * Lp + t0) = out;
+    if ((lane & 15) == 0) gbase[(size_t)bh * (Lp / GATE_TILE) + t0 / GATE_TILE] = base;
   }
 }
 
 }  // namespace
 
-hipError_t launch_gate_scan(const Geometry& g, const float* logf, float* gate2, double* totals,
-                            hipStream_t stream) {
+hipError_t launch_gate_scan(const Geometry& g, const float* logf, float* gate2, double* gbase,
+                            double* totals, hipStream_t stream) {
   const int nch = gate_chunks(g);
   const dim3 grid(nch, g.B * g.H);
   hipLaunchKernelGGL(gate_totals_kernel, grid, dim3(GATE_THREADS), 0, stream, logf, totals, g.L, nch);
   hipLaunchKernelGGL(gate_apply_kernel, grid, dim3(GATE_THREADS), 0, stream, logf, totals, gate2,
-                     g.L, g.Lp, nch);
+                     gbase, g.L, g.Lp, nch);
   return hipGetLastError();
 }
 

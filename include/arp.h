@@ -354,8 +354,9 @@ arp_status arp_decode_step(const arp_desc* desc, int32_t pos, const void* q, con
 
 /* Decode with forget gates (ARP_FORGET_GATE; without it these are
  * arp_decode_prefill and arp_decode_step).  Two more caller-owned buffers:
- *   gcache  float32 [batch, heads, Lmax]: G_j = log2(e) * sum_{s<=j} min(log f_s, 0)
- *           of each cached key (the forward's gate prefix),
+ *   gcache  double [batch, heads, Lmax]: G_j = log2(e) * sum_{s<=j} min(log f_s, 0)
+ *           of each cached key (the gate prefix, in fp64 so that G_t - G_j stays
+ *           exact to fp32 rounding however long the context),
  *   gstate  double [batch, heads]: sum_{s<t} min(log f_s, 0) of the tokens so
  *           far, in fp64.
  * prefill_ex takes the prompt's gates logf float32 [batch, heads, len] (NULL
@@ -368,12 +369,12 @@ arp_status arp_decode_step(const arp_desc* desc, int32_t pos, const void* q, con
  * required (ARP_ERR_INVALID_ARG) and 16-byte aligned (ARP_ERR_ALIGNMENT). */
 arp_status arp_decode_prefill_ex(const arp_desc* desc, int32_t len, const void* k, const void* v,
                                  const float* phi, const float* theta, const float* logf,
-                                 void* kcache, void* vcache, uint64_t* state, float* gcache,
+                                 void* kcache, void* vcache, uint64_t* state, double* gcache,
                                  double* gstate, void* stream);
 arp_status arp_decode_step_ex(const arp_desc* desc, int32_t pos, const void* q, const void* k,
                               const void* v, const float* phi, const float* alibi,
                               const float* logf, uint64_t* state, float* theta, void* kcache,
-                              void* vcache, float* gcache, double* gstate, void* o,
+                              void* vcache, double* gcache, double* gstate, void* o,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Diagnostic: out = R(theta) x (or R(theta)^T x when inverse != 0) in fp32.

@@ -53,9 +53,10 @@ def _decode(w, logf, t0, t1, *, rotate_v=False, alibi=False):
 
 def _check(w, logf, t0, t1, **flags):
     got, gc, gs = _decode(w, logf, t0, t1, **flags)
-    # the gate cache and state against the fp64 prefix sums of min(log f, 0)
+    # the gate cache (fp64) and state against the fp64 prefix sums of min(log f, 0)
     pre = np.cumsum(np.minimum(logf.astype(np.float64), 0.0), axis=2)[:, :, :t1]
-    assert np.all(np.abs(gc - pre * np.log2(np.e)) <= 1e-6 * np.maximum(1.0, np.abs(pre) * 1.45))
+    assert gc.dtype == np.float64
+    assert np.all(np.abs(gc - pre * np.log2(np.e)) <= 1e-12 * np.maximum(1.0, np.abs(pre) * 1.45))
     assert np.all(np.abs(gs - pre[:, :, -1]) <= 1e-9 * np.maximum(1.0, np.abs(pre[:, :, -1])))
     rv, al = flags.get("rotate_v", False), flags.get("alibi", False)
     prob = oracle.Problem(w.q, w.k, w.v, w.phi, oracle_flags(True, rv, al) | oracle.FORGET,
