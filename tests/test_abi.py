@@ -208,7 +208,8 @@ def test_gated_backward_validates_gates_and_workspace():
     plain = _desc(batch=2, heads=8, seqlen=16384, flags=b.ROTATE_QK)
     by = ctypes.byref(d)
     ws, ws0 = L.arp_backward_workspace_bytes(by), L.arp_backward_workspace_bytes(ctypes.byref(plain))
-    extra = 3 * 2 * 8 * 16384 * 4 + 2 * 8 * (16384 // 1024) * 8  # G, colsum, rowsum; fp64 totals
+    # G offsets, colsum, rowsum (fp32 per token); fp64 base per 64-token tile; fp64 chunk totals
+    extra = 3 * 2 * 8 * 16384 * 4 + 2 * 8 * (16384 // 64) * 8 + 2 * 8 * (16384 // 1024) * 8
     assert ws0 + extra <= ws < ws0 + extra + 4 * 256 and ws % 256 == 0
     p14 = [A] * 14
     assert L.arp_backward(by, *p14, ws, None) == b.ERR_INVALID_ARG
