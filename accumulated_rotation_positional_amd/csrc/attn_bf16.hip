@@ -103,7 +103,9 @@ __device__ __forceinline__ void attn_tile(
   constexpr int IPT = P * (BN / 4) / NT;  // fused staging: (pair, 4-key group) items per thread
   static_assert(!FUSED || IPT * NT == P * (BN / 4), "fused staging split");
 
-  constexpr int GTILE = FORGET ? BN * 4 : 0;  // the tile's 64 key gates (fp32)
+  // the tile's 64 key gate offsets (fp32) and its fp64 gate base, padded so
+  // that every stage starts on a 256-byte boundary (the LDS bank period)
+  constexpr int GTILE = FORGET ? BN * 4 + 256 : 0;
   constexpr int STAGE = KTILE + VTILE + GTILE;
 
   // ---- which tile (the logical order is set by the kernel below) ----
@@ -161,6 +163,12 @@ __device__ __forceinline__ void attn_tile(
       if (wave == 0 && lane < BN / 4)
         __builtin_amdgcn_global_load_lds((global_void_ptr)(gate2 + (size_t)bh * Lp + j0 + 4 * lane),
                                          (lds_void_ptr)(stage + KTILE + VTILE), 16, 0, 0);
+      // the tile's base, one 4-byte half per lane (lane l lands at 4 l)
+      if (wave == 0 && lane < 2)
+        __builtin_amdgcn_global_load_lds(
+            (global_void_ptr)(reinterpret_cast<const uint32_t*>(gbase + (size_t)bh * (Lp / BN) + tile) +
+                              lane),
+            (lds_void_ptr)(stage + KTILE + VTILE + BN * 4), 4, 0, 0);
     }
   };
   // ---- fused staging: raw k, v and angles of one tile -> registers -> rotated into LDS ----
@@ -286,10 +294,13 @@ __device__ __forceinline__ void attn_tile(
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][qb][r] = 0.f;
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
-  float gq[QB];  // the forget-gate prefix of this lane's queries
+  float gq[QB];    // the forget-gate offset of this lane's queries within their tile
+  double gqb[QB];  // and that tile's base (the rows of block qb share one tile)
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int qb = 0; qb < QB; ++qb) {
     gq[qb] = FORGET ? gate2[(size_t)bh * Lp + min(qw + 32 * qb + ln, Lp - 1)] : 0.f;
+    gqb[qb] = FORGET ? gbase[(size_t)bh * (Lp / BN) + min((qw + 32 * qb) / BN, Lp / BN - 1)] : 0.0;
+  }
   // The accumulator input of Q K^T: -m, plus with a gate bias the query's
   // gate offset and the tile base difference D (so only the key's offset is
   // left to subtract per logit; set per key tile in the walk below).
@@ -528,10 +539,11 @@ __device__ __forceinline__ void attn_tile(
             if (ALIBI)
               bb = fmaxf(slope2 * (float)(t * BN - i), slope2 * (float)(t * BN + BN - 1 - i));
             if (FORGET) {
-              // the tile base difference, rounded once; the query rows of
-              // block qb share one 64-token tile
-              const double* gb = gbase + (size_t)bh * (Lp / BN);
-              const float dt = (float)(gb[min((qw + 32 * qb) / BN, Lp / BN - 1)] - gb[t]);
+              // the tile base difference, rounded once (the key tile's base
+              // came into LDS with its gates)
+              const double gkt = *reinterpret_cast<const double*>(smem + (n % NST) * STAGE + KTILE +
+                                                                  VTILE + BN * 4);
+              const float dt = (float)(gqb[qb] - gkt);
               bb += gq[qb] + dt - gl;
 #pragma unroll
               for (int r = 0; r < 16; ++r) cneg[qb][r] = gq[qb] + dt - mrun[qb];
@@ -625,7 +637,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     const float* __restrict__ gate2, const double* __restrict__ gbase, uint16_t* __restrict__ o,
     float* __restrict__ lse, int L, int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk,
     float qscale, int paired, const float* __restrict__ hscale) {
-  constexpr int STAGE = BN * D * 2 + D * BN * 2 + (((BIAS & 2) != 0) ? BN * 4 : 0);  // as in attn_tile
+  constexpr int STAGE = BN * D * 2 + D * BN * 2 + (((BIAS & 2) != 0) ? BN * 4 + 256 : 0);  // as in attn_tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
   constexpr bool SPREAD = (BIAS != 0) && !FUSED;
   constexpr bool PAIRABLE = QPW == 64 && NW == 8 && BIAS == 0 && !FUSED;

@@ -301,7 +301,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int ROWB = D * 2, RT = TILE * ROWB;     // row tile bytes
   constexpr int COLB = TILE * 2, CT = D * COLB;     // column tile bytes
-  constexpr int STAGE = 2 * RT + 2 * CT + 2 * TILE * 4;
+  // + with gates the query tile's fp64 gate base (padded to keep stages on
+  // 256-byte boundaries, the LDS bank period)
+  constexpr int STAGE = 2 * RT + 2 * CT + 2 * TILE * 4 + (GATE ? 256 : 0);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   // Unbiased: each XCD (blockIdx % 8) gets whole heads, so their key
@@ -338,6 +340,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
     if (wave == 0 && lane < 32)
       __builtin_amdgcn_global_load_lds((global_void_ptr)(stats_bh + (size_t)t * 2 * TILE + 4 * lane),
                                        (lds_void_ptr)(st + 2 * RT + 2 * CT), 16, 0, 0);
+    if (GATE && wave == 0 && lane < 2)  // one 4-byte half per lane (lane l lands at 4 l)
+      __builtin_amdgcn_global_load_lds(
+          (global_void_ptr)(reinterpret_cast<const uint32_t*>(ops.gbase + (size_t)bh * (Lp / TILE) + t) +
+                            lane),
+          (lds_void_ptr)(st + 2 * RT + 2 * CT + 2 * TILE * 4), 4, 0, 0);
   };
 
   // B operands: this lane's key row of k~ and v~ (d = 16 ks + 8 hf .. +7)
@@ -357,8 +364,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
   // the key's gate offset within its 64-token tile, subtracted from every
   // logit of its column with the (query tile, key tile) base difference
   const float gj = GATE ? ops.gate2[(size_t)bh * Lp + min(j, Lp - 1)] : 0.f;
-  const double* gbase_bh = GATE ? ops.gbase + (size_t)bh * (Lp / TILE) : nullptr;
-  const double gbase_k = GATE ? gbase_bh[kw / TILE] : 0.0;  // the wave's keys share a tile
+  // the wave's keys share a tile
+  const double gbase_k = GATE ? ops.gbase[(size_t)bh * (Lp / TILE) + min(kw / TILE, Lp / TILE - 1)]
+                              : 0.0;
   float csum = 0.f;  // sum of dS over this lane's part of the key's column
 
   // Query tiles from the last one down: the workgroups that run at the same
@@ -401,7 +409,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
     const uint8_t* tdoT = st + 2 * RT + CT;
     const float* sl = reinterpret_cast<const float*>(st + 2 * RT + 2 * CT);
     // G_i - G_j = fp32(gbase[t] - gbase[key tile]) + offset_i - offset_j
-    const float dg = GATE ? (float)(gbase_bh[t] - gbase_k) - gj : 0.f;
+    // (the query tile's base came into LDS with its statistics)
+    const float dg =
+        GATE ? (float)(*reinterpret_cast<const double*>(st + 2 * RT + 2 * CT + 2 * TILE * 4) - gbase_k) - gj
+             : 0.f;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qbase = t * TILE + 32 * qb;
@@ -498,7 +509,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
   constexpr int KS = D / 16, DB = D / 32, KB = 2, KS2 = 4;
   constexpr int ROWB = D * 2, RT = TILE * ROWB;
   constexpr int COLB = TILE * 2, CT = D * COLB;
-  constexpr int STAGE = 2 * RT + CT + (GATE ? TILE * 4 : 0);  // + the tile's key gates
+  // + the tile's key gates and base (padded to a 256-byte multiple)
+  constexpr int STAGE = 2 * RT + CT + (GATE ? TILE * 4 + 256 : 0);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   // Workgroup order as in the dK/dV pass: whole heads per XCD unbiased,
@@ -534,6 +546,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
       __builtin_amdgcn_global_load_lds(
           (global_void_ptr)(ops.gate2 + (size_t)bh * Lp + (size_t)t * TILE + 4 * lane),
           (lds_void_ptr)(st + 2 * RT + CT), 16, 0, 0);
+    if (GATE && wave == 0 && lane < 2)  // the key tile's base, one 4-byte half per lane
+      __builtin_amdgcn_global_load_lds(
+          (global_void_ptr)(reinterpret_cast<const uint32_t*>(ops.gbase + (size_t)bh * (Lp / TILE) + t) +
+                            lane),
+          (lds_void_ptr)(st + 2 * RT + CT + TILE * 4), 4, 0, 0);
   };
 
   bf16x8 qop[KS], doop[KS];
@@ -558,6 +575,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
     for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
   const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
   float rsum = 0.f;  // sum of dS over this lane's part of the query's row
+  // the gate base of the wave's query tile (its 32 queries share one)
+  const double gbase_q = GATE ? ops.gbase[(size_t)bh * (Lp / TILE) + min(qw / TILE, Lp / TILE - 1)]
+                              : 0.0;
 
   // With a distance bias the walk starts at the first key tile that can
   // hold a nonzero probability for these queries (every wave finds the same
@@ -600,8 +620,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
     // the query's offset; the key offsets are subtracted per element below
     f32x16 clt = cl;
     if constexpr (GATE) {
-      const double* gb = ops.gbase + (size_t)bh * (Lp / TILE);
-      const float dt = (float)(gb[qw / TILE] - gb[n]);  // the wave's queries share a tile
+      const float dt =
+          (float)(gbase_q - *reinterpret_cast<const double*>(st + 2 * RT + CT + TILE * 4));
 #pragma unroll
       for (int r = 0; r < 16; ++r) clt[r] += dt;
     }
