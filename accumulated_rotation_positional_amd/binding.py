@@ -37,7 +37,7 @@ ABI_VERSION = 2
 # Every function the header declares (tests check the library exports them all).
 EXPORTS = ("arp_abi_version", "arp_status_string", "arp_check", "arp_scan_state_bytes",
            "arp_workspace_bytes",
-           "arp_angle_scan", "arp_rotate_qkv", "arp_attn_rotated", "arp_attn_fwd",
+           "arp_angle_scan", "arp_rotate_kv", "arp_attn_rotated", "arp_attn_fwd",
            "arp_forward", "arp_rotate", "arp_forward_train", "arp_backward_workspace_bytes",
            "arp_backward", "arp_decode_workspace_bytes", "arp_decode_prefill", "arp_decode_step",
            "arp_forward_ex", "arp_angle_scan_random", "arp_angle_scan_tokens",
@@ -80,8 +80,8 @@ def lib() -> ctypes.CDLL:
                 "arp_scan_state_bytes": ([D], S),
                 "arp_workspace_bytes": ([D], S),
                 "arp_angle_scan": ([D, P, P, P, S, P], ctypes.c_int),
-                "arp_rotate_qkv": ([D, P, P, P, P, P, S, P], ctypes.c_int),
-                "arp_attn_rotated": ([D, P, P, P, P, S, P], ctypes.c_int),
+                "arp_rotate_kv": ([D, P, P, P, P, S, P], ctypes.c_int),
+                "arp_attn_rotated": ([D, P, P, P, P, P, P, S, P], ctypes.c_int),
                 "arp_attn_fwd": ([D, P, P, P, P, P, P, P, S, P], ctypes.c_int),
                 "arp_forward": ([D, P, P, P, P, P, P, P, P, S, P, S, P], ctypes.c_int),
                 "arp_rotate": ([D, P, P, P, ctypes.c_int, P], ctypes.c_int),
@@ -372,27 +372,30 @@ def random_phi(desc: Desc, seed: int, step: int, bound: torch.Tensor,
     return phi
 
 
-def rotate_qkv(q, k, v, theta, desc: Desc, ws: torch.Tensor | None = None) -> torch.Tensor:
-    _check_qkv(desc, q=q, k=k, v=v)
+def rotate_kv(k, v, theta, desc: Desc, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """The pre-rotation pass: k~ (and v~ with value transport) into the
+    workspace, which it returns."""
+    _check_qkv(desc, k=k, v=v)
     _check_angles(desc, theta=theta)
     _check_buffer(ws, "ws", workspace_bytes(desc))
-    _require_gpu(q, k, v, theta, ws)
-    ws = workspace(desc, q.device) if ws is None else ws
-    _check("arp_rotate_qkv", lib().arp_rotate_qkv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
-                                                  _ptr(theta), _ptr(ws), _nbytes(ws),
-                                                  _stream(q.device)))
+    _require_gpu(k, v, theta, ws)
+    ws = workspace(desc, k.device) if ws is None else ws
+    _check("arp_rotate_kv", lib().arp_rotate_kv(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(theta),
+                                                _ptr(ws), _nbytes(ws), _stream(k.device)))
     return ws
 
 
-def attn_rotated(theta, alibi, out, desc: Desc, ws: torch.Tensor) -> torch.Tensor:
+def attn_rotated(q, v, theta, alibi, out, desc: Desc, ws: torch.Tensor) -> torch.Tensor:
+    """Attention over the pass's keys (and values): q is rotated inside the
+    kernel; v is the caller's values (read without value transport)."""
+    _check_qkv(desc, q=q, v=v, out=out)
     _check_angles(desc, theta=theta)
     _check_alibi(desc, alibi)
-    _check_qkv(desc, out=out)
     _check_buffer(ws, "ws", workspace_bytes(desc))
-    _require_gpu(theta, alibi, out, ws)
-    _check("arp_attn_rotated", lib().arp_attn_rotated(ctypes.byref(desc), _ptr(theta), _ptr(alibi),
-                                                      _ptr(out), _ptr(ws), _nbytes(ws),
-                                                      _stream(out.device)))
+    _require_gpu(q, v, theta, alibi, out, ws)
+    _check("arp_attn_rotated", lib().arp_attn_rotated(ctypes.byref(desc), _ptr(q), _ptr(v),
+                                                      _ptr(theta), _ptr(alibi), _ptr(out),
+                                                      _ptr(ws), _nbytes(ws), _stream(out.device)))
     return out
 
 

@@ -75,15 +75,46 @@ bool gated(const Geometry& g) { return (g.flags & ARP_FORGET_GATE) != 0; }
 
 }  // namespace
 
+namespace {
+
+// The pre-rotation path's two launches over a carved workspace: k~ (and v~
+// with value transport), then the attention kernel, which rotates q itself
+// and reads V rows from v~ or, without value transport, the caller's v.
+hipError_t launch_rotation_pass(const Geometry& g, const void* k, const void* v,
+                                const float* theta, char* ws, hipStream_t s) {
+  const WorkspaceLayout lay = workspace_layout(g);
+  return launch_rotate_kv(g, k, v, theta, reinterpret_cast<uint16_t*>(ws + lay.k_off),
+                          (g.flags & ARP_ROTATE_V) ? reinterpret_cast<uint16_t*>(ws + lay.v_off)
+                                                   : nullptr,
+                          reinterpret_cast<float*>(ws + lay.kmax_off), s);
+}
+
+hipError_t launch_attention(const Geometry& g, const void* q, const void* v, const float* theta,
+                            const float* alibi, const float* gate2, const double* gbase, void* o,
+                            float* lse, const char* ws, hipStream_t s) {
+  const WorkspaceLayout lay = workspace_layout(g);
+  const bool rv = (g.flags & ARP_ROTATE_V) != 0;
+  const uint16_t* vrows = rv ? reinterpret_cast<const uint16_t*>(ws + lay.v_off)
+                             : static_cast<const uint16_t*>(v);
+  return launch_attn_bf16_rotated(g, static_cast<const uint16_t*>(q),
+                                  reinterpret_cast<const uint16_t*>(ws + lay.k_off), vrows,
+                                  rv ? g.Lp : g.L, reinterpret_cast<const float*>(ws + lay.kmax_off),
+                                  theta, alibi, gate2, gbase, static_cast<uint16_t*>(o), lse, s);
+}
+
+}  // namespace
+
 WorkspaceLayout workspace_layout(const Geometry& g) {
   WorkspaceLayout lay{};
   size_t off = 0;
   if (needs_operands(g)) {
     lay.operand_bytes = align_up((size_t)g.B * g.H * g.Lp * g.D * sizeof(uint16_t));
-    lay.q_off = off;
-    lay.k_off = off + lay.operand_bytes;
-    lay.vt_off = off + 2 * lay.operand_bytes;
-    off += 3 * lay.operand_bytes;
+    lay.k_off = off;
+    off += lay.operand_bytes;
+    if (g.flags & ARP_ROTATE_V) {  // v~; without value transport the caller's v is read
+      lay.v_off = off;
+      off += lay.operand_bytes;
+    }
     lay.kmax_off = off;
     off += align_up((size_t)g.B * g.H * (g.Lp / KEY_TILE) * sizeof(float));
     if (g.flags & ARP_FORGET_GATE) {
@@ -245,49 +276,40 @@ arp_status arp_random_phi(const arp_desc* desc, uint64_t seed, uint64_t step, co
   return hip_status(launch_random_phi(g, seed, step, bound, phi, (hipStream_t)stream));
 }
 
-arp_status arp_rotate_qkv(const arp_desc* desc, const void* q, const void* k, const void* v,
-                          const float* theta, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+arp_status arp_rotate_kv(const arp_desc* desc, const void* k, const void* v, const float* theta,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
   if (gated(g)) return ARP_ERR_INVALID_ARG;  // the gate input: arp_forward_ex
   if (!needs_operands(g)) return ARP_ERR_UNSUPPORTED;
-  if (q == nullptr || k == nullptr || v == nullptr || (rotates(g) && theta == nullptr))
+  const bool rv = (g.flags & ARP_ROTATE_V) != 0;
+  if (k == nullptr || (rv && v == nullptr) || (rotates(g) && theta == nullptr))
     return ARP_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (theta && !aligned16(theta)))
-    return ARP_ERR_ALIGNMENT;
+  if (!aligned16(k) || (v && !aligned16(v)) || (theta && !aligned16(theta))) return ARP_ERR_ALIGNMENT;
   if ((st = check_ws(g, workspace, workspace_bytes)) != ARP_OK) return st;
-  const WorkspaceLayout lay = workspace_layout(g);
-  char* ws = static_cast<char*>(workspace);
-  return hip_status(launch_rotate_qkv(g, q, k, v, theta, reinterpret_cast<uint16_t*>(ws + lay.q_off),
-                                      reinterpret_cast<uint16_t*>(ws + lay.k_off),
-                                      reinterpret_cast<uint16_t*>(ws + lay.vt_off),
-                                      reinterpret_cast<float*>(ws + lay.kmax_off),
-                                      (hipStream_t)stream));
+  return hip_status(launch_rotation_pass(g, k, v, theta, static_cast<char*>(workspace),
+                                         (hipStream_t)stream));
 }
 
-arp_status arp_attn_rotated(const arp_desc* desc, const float* theta, const float* alibi, void* o,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+arp_status arp_attn_rotated(const arp_desc* desc, const void* q, const void* v, const float* theta,
+                            const float* alibi, void* o, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   Geometry g;
   arp_status st = make_geometry(desc, &g);
   if (st != ARP_OK) return st;
   if (gated(g)) return ARP_ERR_INVALID_ARG;  // the gate input: arp_forward_ex
   if (!needs_operands(g)) return ARP_ERR_UNSUPPORTED;
-  if (o == nullptr || ((g.flags & ARP_ROTATE_V) && theta == nullptr) ||
+  const bool rv = (g.flags & ARP_ROTATE_V) != 0;
+  if (q == nullptr || o == nullptr || (!rv && v == nullptr) || (rotates(g) && theta == nullptr) ||
       ((g.flags & ARP_ALIBI) && alibi == nullptr))
     return ARP_ERR_INVALID_ARG;
-  if (!aligned16(o) || (theta && !aligned16(theta)) || (alibi && !aligned16(alibi)))
+  if (!aligned16(q) || !aligned16(o) || (v && !aligned16(v)) || (theta && !aligned16(theta)) ||
+      (alibi && !aligned16(alibi)))
     return ARP_ERR_ALIGNMENT;
   if ((st = check_ws(g, workspace, workspace_bytes)) != ARP_OK) return st;
-  const WorkspaceLayout lay = workspace_layout(g);
-  char* ws = static_cast<char*>(workspace);
-  return hip_status(launch_attn_bf16_rotated(
-      g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
-      reinterpret_cast<const uint16_t*>(ws + lay.k_off),
-      reinterpret_cast<const uint16_t*>(ws + lay.vt_off),
-      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi, nullptr, nullptr,
-      static_cast<uint16_t*>(o), nullptr, (hipStream_t)stream));
+  return hip_status(launch_attention(g, q, v, theta, alibi, nullptr, nullptr, o, nullptr,
+                                     static_cast<const char*>(workspace), (hipStream_t)stream));
 }
 
 arp_status arp_attn_fwd(const arp_desc* desc, const void* q, const void* k, const void* v,
@@ -313,9 +335,9 @@ arp_status arp_attn_fwd(const arp_desc* desc, const void* q, const void* k, cons
     return fused_status(launch_attn_bf16_fused(
         g, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
         static_cast<const uint16_t*>(v), theta, alibi, static_cast<uint16_t*>(o), s));
-  st = arp_rotate_qkv(desc, q, k, v, theta, workspace, workspace_bytes, stream);
+  st = arp_rotate_kv(desc, k, v, theta, workspace, workspace_bytes, stream);
   if (st != ARP_OK) return st;
-  return arp_attn_rotated(desc, theta, alibi, o, workspace, workspace_bytes, stream);
+  return arp_attn_rotated(desc, q, v, theta, alibi, o, workspace, workspace_bytes, stream);
 }
 
 arp_status arp_forward(const arp_desc* desc, const void* q, const void* k, const void* v,
@@ -365,16 +387,10 @@ arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k,
     return hip_status(launch_attn_f32(g, static_cast<const float*>(q), static_cast<const float*>(k),
                                       static_cast<const float*>(v), theta, alibi,
                                       static_cast<float*>(o), lse, (hipStream_t)stream));
-  st = arp_rotate_qkv(desc, q, k, v, theta, workspace, workspace_bytes, stream);
+  st = arp_rotate_kv(desc, k, v, theta, workspace, workspace_bytes, stream);
   if (st != ARP_OK) return st;
-  const WorkspaceLayout lay = workspace_layout(g);
-  char* ws = static_cast<char*>(workspace);
-  return hip_status(launch_attn_bf16_rotated(
-      g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
-      reinterpret_cast<const uint16_t*>(ws + lay.k_off),
-      reinterpret_cast<const uint16_t*>(ws + lay.vt_off),
-      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi, nullptr, nullptr,
-      static_cast<uint16_t*>(o), lse, (hipStream_t)stream));
+  return hip_status(launch_attention(g, q, v, theta, alibi, nullptr, nullptr, o, lse,
+                                     static_cast<const char*>(workspace), (hipStream_t)stream));
 }
 
 arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, const void* v,
@@ -409,22 +425,14 @@ arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, co
   char* ws = static_cast<char*>(workspace);
   hipError_t e = launch_angle_scan(g, phi, theta, scan_state, s);
   if (e != hipSuccess) return ARP_ERR_HIP;
-  e = launch_rotate_qkv(g, q, k, v, theta, reinterpret_cast<uint16_t*>(ws + lay.q_off),
-                        reinterpret_cast<uint16_t*>(ws + lay.k_off),
-                        reinterpret_cast<uint16_t*>(ws + lay.vt_off),
-                        reinterpret_cast<float*>(ws + lay.kmax_off), s);
+  e = launch_rotation_pass(g, k, v, theta, ws, s);
   if (e != hipSuccess) return ARP_ERR_HIP;
   float* gate2 = gated(g) ? reinterpret_cast<float*>(ws + lay.gate_off) : nullptr;
   double* gbase = gated(g) ? reinterpret_cast<double*>(ws + lay.gate_base_off) : nullptr;
   if (gated(g) && launch_gate_scan(g, logf, gate2, gbase,
                                    reinterpret_cast<double*>(ws + lay.gate_tot_off), s) != hipSuccess)
     return ARP_ERR_HIP;
-  return hip_status(launch_attn_bf16_rotated(
-      g, reinterpret_cast<const uint16_t*>(ws + lay.q_off),
-      reinterpret_cast<const uint16_t*>(ws + lay.k_off),
-      reinterpret_cast<const uint16_t*>(ws + lay.vt_off),
-      reinterpret_cast<const float*>(ws + lay.kmax_off), theta, alibi, gate2, gbase,
-      static_cast<uint16_t*>(o), lse, s));
+  return hip_status(launch_attention(g, q, v, theta, alibi, gate2, gbase, o, lse, ws, s));
 }
 
 size_t arp_backward_workspace_bytes(const arp_desc* desc) {

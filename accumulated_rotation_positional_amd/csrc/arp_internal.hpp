@@ -24,8 +24,8 @@ struct Geometry {
 // ---- buffers ----------------------------------------------------------------
 // scan state: a 256-byte header and two interleaved halves of 64-bit
 //   look-back status words, [B*Hphi][nchunks][P] per half (angle_scan.hip).
-// workspace:  [ q~ (bf16, [B*H, Lp, D]) | k~ (bf16, [B*H, Lp, D]) | v~^T (bf16, [B*H, D, Lp])
-//               | kmax (fp32, [B*H, Lp/64]) ]
+// workspace:  [ k~ (bf16, [B*H, Lp, D]) | v~ (bf16, [B*H, Lp, D], with ARP_ROTATE_V only)
+//               | kmax (fp32, [B*H, Lp/64]) | gate prefix (ARP_FORGET_GATE) ]
 //   for bf16 without ARP_FUSED_ROTATION; empty otherwise.
 struct ScanPlan {
   int rows_per_thread;  // tokens each thread scans serially (T)
@@ -36,7 +36,7 @@ struct ScanPlan {
 ScanPlan scan_plan(const Geometry& g);
 size_t scan_state_bytes(const Geometry& g);  // upper bound over every plan
 struct WorkspaceLayout {
-  size_t q_off, k_off, vt_off, operand_bytes;  // each operand block
+  size_t k_off, v_off, operand_bytes;          // each operand block (v~ only with ARP_ROTATE_V)
   size_t kmax_off;                             // float [B*H][Lp/64]: max |k~| per key tile
   size_t gate_off;                             // float [B*H][Lp]: gate prefix within its
                                                //   64-token tile (ARP_FORGET_GATE)
@@ -65,13 +65,16 @@ hipError_t launch_angle_scan_const(const Geometry& g, const float* freq, float* 
 // The random draws written out as phi [B, Hphi, L, P].
 hipError_t launch_random_phi(const Geometry& g, uint64_t seed, uint64_t step, const float* bound,
                              float* phi, hipStream_t stream);
-hipError_t launch_rotate_qkv(const Geometry& g, const void* q, const void* k, const void* v,
-                             const float* theta, uint16_t* qr, uint16_t* kr, uint16_t* vt,
-                             float* kmax, hipStream_t stream);
-hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
-                                    const uint16_t* vt, const float* kmax, const float* theta,
-                                    const float* alibi, const float* gate2, const double* gbase,
-                                    uint16_t* o, float* lse, hipStream_t stream);
+// k~ (and v~ with ARP_ROTATE_V) into the workspace, with the key-norm maxima
+hipError_t launch_rotate_kv(const Geometry& g, const void* k, const void* v, const float* theta,
+                            uint16_t* kr, uint16_t* vr, float* kmax, hipStream_t stream);
+// q: the caller's raw q (rotated in the kernel's prologue); v: V rows, vrows
+// per head (the workspace's v~ with vrows = Lp, or the caller's v with L)
+hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* q, const uint16_t* kr,
+                                    const uint16_t* v, int vrows, const float* kmax,
+                                    const float* theta, const float* alibi, const float* gate2,
+                                    const double* gbase, uint16_t* o, float* lse,
+                                    hipStream_t stream);
 // Forget gates: with G_t = log2 e * sum_{s <= t} min(logf[b, h, s], 0) (fp64
 // accumulation; padded to Lp with the last value), the prefix is kept relative
 // to 64-token tiles so that it stays exact however long the sequence:

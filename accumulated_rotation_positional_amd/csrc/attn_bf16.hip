@@ -24,13 +24,23 @@
 //    that makes the S^T accumulator layout coincide with the P^T operand
 //    layout: a lane's 8 consecutive accumulator values are its 8 consecutive
 //    keys, so P^T is built in registers with no data movement.
-//  * K~ and V~^T tiles go from global memory straight into LDS
+//  * K~ and V tiles go from global memory straight into LDS
 //    (global_load_lds_dwordx4, no staging registers) through a ring of NST
 //    stages: the loads of the next NST-1 tiles are in flight while a tile is
 //    computed; one barrier per tile.  The LDS layout XOR-swizzles 16-byte chunks (no bank
 //    conflicts on the 128-bit operand reads); since a direct load writes lane
 //    l's 16 bytes to position 16 l, the swizzle is applied to the global
-//    addresses instead.
+//    addresses instead.  V rows stay in their natural [key, d] layout (the
+//    caller's v, or the rotation pass's v~ with value transport); the P V
+//    product's V^T operand is read from them with LDS transpose reads
+//    (ds_read_b64_tr_b16: each group of 16 lanes names a 16 x 4 block of
+//    16-bit elements, four consecutive d of four keys per lane, and lane i
+//    receives d = i of the four keys).
+//  * q is rotated, scaled by scale * log2 e (and the head's query multiplier)
+//    and rounded to bf16 in the prologue; the rotation pass only writes k~
+//    (and v~ with value transport).  Every sin/cos here (q, the fused
+//    staging, the value-transport epilogue) is the hardware sine and cosine
+//    of turns (__sincosf), absolute error below 3e-7 on the scan's [-pi, pi).
 //  * The running maximum is subtracted inside the matrix-core product (the
 //    accumulator input is -m, kept in registers), and it is only raised when
 //    a row's tile maximum exceeds it by more than TAU = 8 (so 2^(s-m) <= 256):
@@ -55,13 +65,16 @@ constexpr float TAU = 8.0f;   // lazy-rescale threshold (base-2 logits)
 // every one of them is exactly zero, so skipping the tile changes no bit.
 constexpr float ZGAP = 160.0f;
 
-// FUSED = false: q~, k~ (L padded to Lp) and v~^T come pre-rotated from the
-// rotation pass, K/V tiles load straight into LDS, and the per-tile key-norm
-// maxima kmax bound the logits.
-// FUSED = true: qr, kr, vt are the raw q, k, v ([B, H, L, D]); q is rotated
-// and scaled in the prologue, and each K/V tile is rotated while it is staged
-// through registers into LDS (sin/cos once per (key, pair), shared by k and
-// v); row maxima are always taken exactly.
+// qr is the raw q ([B, H, L, D]), rotated and scaled in the prologue.
+// FUSED = false: k~ (L padded to Lp) comes pre-rotated from the rotation pass,
+// V rows come from vt ([B*H, vrows, D]: the pass's v~ with vrows = Lp, or the
+// caller's v with vrows = L, rows past vrows - 1 read as row vrows - 1 -- their
+// probabilities are zero), both tiles load straight into LDS, and the per-tile
+// key-norm maxima kmax bound the logits.
+// FUSED = true: kr, vt are the raw k, v ([B, H, L, D]); each K/V tile is
+// rotated while it is staged through registers into LDS (sin/cos once per
+// (key, pair), shared by k and v; V transposed); row maxima are always taken
+// exactly.
 // BIAS: bit 0 the distance bias -m_h (i - j), bit 1 the forget-gate bias
 // G_i - G_j, with G = log2 e * (prefix sums of log f) from the gate pass
 // (non-increasing, so the bias never raises a score), read in its tiled
@@ -77,8 +90,8 @@ __device__ __forceinline__ void attn_tile(
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
     const float* __restrict__ theta, const float* __restrict__ alibi,
     const float* __restrict__ gate2, const double* __restrict__ gbase, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int L, int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk,
-    float qscale0, const float* __restrict__ hscale) {
+    float* __restrict__ lse, int L, int Lp, int vrows, int H, int Hphi, int nqt, int total_tiles,
+    int rot_qk, float qscale0, const float* __restrict__ hscale) {
   constexpr bool ALIBI = (BIAS & 1) != 0;
   constexpr bool FORGET = (BIAS & 2) != 0;
   static_assert(!(FUSED && FORGET), "the gate bias needs the pre-rotation path");
@@ -90,8 +103,8 @@ __device__ __forceinline__ void attn_tile(
   constexpr int KS2 = BN / 16;         // k-steps of O^T (16 keys each)
   constexpr int KROW = D * 2;          // bytes per K~ row in LDS
   constexpr int KTILE = BN * KROW;
-  constexpr int VROW = BN * 2;         // bytes per V~^T row in LDS
-  constexpr int VTILE = D * VROW;
+  constexpr int VROW = BN * 2;         // bytes per V~^T row in LDS (fused staging)
+  constexpr int VTILE = D * VROW;      // = BN * KROW: the natural V rows take the same space
   constexpr int KLD = KTILE / (1024 * NW);  // 1 KB direct loads per wave per tile
   constexpr int VLD = VTILE / (1024 * NW);
   static_assert(KLD * 1024 * NW == KTILE && VLD * 1024 * NW == VTILE, "staging split");
@@ -135,9 +148,9 @@ __device__ __forceinline__ void attn_tile(
   constexpr bool DESC = (BIAS != 0) && !FUSED;
   auto tile_at = [&](int step) { return DESC ? last_tile - step : step; };
 
-  // ---- direct global -> LDS loads of one K~ / V~^T tile ----
+  // ---- direct global -> LDS loads of one K~ / V tile ----
   const uint16_t* kbase = kr + (size_t)bh * Lp * D;
-  const uint16_t* vbase = vt + (size_t)bh * D * Lp;
+  const uint16_t* vbase = vt + (size_t)bh * vrows * D;
   auto issue = [&](int tile, uint8_t* stage) __attribute__((always_inline)) {
     const int j0 = tile * BN;
 #pragma unroll
@@ -149,13 +162,14 @@ __device__ __forceinline__ void attn_tile(
       const uint16_t* src = kbase + (size_t)(j0 + swap_bits23(row)) * D + 8 * c;
       __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + p0), 16, 0, 0);
     }
+    // V rows in key order (rows past the source are clamped)
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int p0 = (wave * VLD + i) * 1024;
       const int p = p0 + 16 * lane;
-      const int row = p / VROW, cs = (p % VROW) / 16;
-      const int c = cs ^ swz<VROW>(row);
-      const uint16_t* src = vbase + (size_t)row * Lp + j0 + 8 * c;
+      const int row = p / KROW, cs = (p % KROW) / 16;
+      const int c = cs ^ swzv<KROW>(row);
+      const uint16_t* src = vbase + (size_t)min(j0 + row, vrows - 1) * D + 8 * c;
       __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + KTILE + p0), 16,
                                        0, 0);
     }
@@ -224,19 +238,12 @@ __device__ __forceinline__ void attn_tile(
     }
   };
 
-  // ---- Q~ operand: lane (ln, hf) holds query qw+32qb+ln, d = 16ks+8hf..+7 ----
-  // (fused: rotated and multiplied by scale * log2 e and the head's query
-  // multiplier here; the pre-rotated operand already carries both)
-  const float qscale = (FUSED && hscale != nullptr) ? qscale0 * hscale[h] : qscale0;
+  // ---- Q~ operand: lane (ln, hf) holds query qw+32qb+ln, d = 16ks+8hf..+7,
+  // rotated and multiplied by scale * log2 e and the head's query multiplier
+  // here, then rounded to bf16 ----
+  const float qscale = hscale != nullptr ? qscale0 * hscale[h] : qscale0;
   bf16x8 qop[QB][KS];
-  if constexpr (!FUSED) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qop[qb][ks] = *reinterpret_cast<const bf16x8*>(
-            qr + ((size_t)bh * Lp + min(qw + 32 * qb + ln, Lp - 1)) * D + 16 * ks + 8 * hf);
-  } else {
+  {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int i = min(qw + 32 * qb + ln, L - 1);
@@ -251,7 +258,7 @@ __device__ __forceinline__ void attn_tile(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float sn, cs;
-          sincosf(ang[e], &sn, &cs);
+          __sincosf(ang[e], &sn, &cs);
           float x0 = lo_bf16(w[e]), x1 = hi_bf16(w[e]);
           if (rot_qk) rotate_pair(x0, x1, cs, sn);
           r[e] = pack_bf16x2(x0 * qscale, x1 * qscale);
@@ -480,15 +487,34 @@ __device__ __forceinline__ void attn_tile(
       }
   };
 
+  // The V^T operand A[m = d][k = keys 8 hf .. 8 hf + 7] of the P V product:
+  // from the natural V rows, two transpose reads of four keys each.  Source
+  // lane j = lane % 16 of group g = lane / 16 names keys 16 ks2 + 8 (g / 2) +
+  // 4 u + j / 4 and d = 32 db + 16 (g % 2) + 4 (j % 4) .. + 3.
+  const int trj = lane & 15, trg = (lane >> 4) & 1;
   auto pv = [&](int n) __attribute__((always_inline)) {
     const uint8_t* vtile = smem + (n % NST) * STAGE + KTILE;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int row = 32 * db + ln;
 #pragma unroll
       for (int ks2 = 0; ks2 < KS2; ++ks2) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-            vtile + row * VROW + (((2 * ks2 + hf) ^ swz<VROW>(row)) << 4));
+        bf16x8 va;
+        if constexpr (!FUSED) {
+          const int colb = 64 * db + 32 * trg + 8 * (trj & 3);  // byte offset in the row
+          u32x2 t[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int row = 16 * ks2 + 8 * hf + 4 * u + (trj >> 2);
+            t[u] = lds_read_tr16(vtile + row * KROW + (((colb >> 4) ^ swzv<KROW>(row)) << 4) +
+                                 (colb & 15));
+          }
+          const u32x4 w = {t[0][0], t[0][1], t[1][0], t[1][1]};
+          va = __builtin_bit_cast(bf16x8, w);
+        } else {
+          const int row = 32 * db + ln;
+          va = *reinterpret_cast<const bf16x8*>(
+              vtile + row * VROW + (((2 * ks2 + hf) ^ swz<VROW>(row)) << 4));
+        }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma32(va, pop[ks2][qb], oacc[db][qb]);
       }
@@ -607,8 +633,8 @@ __device__ __forceinline__ void attn_tile(
         if (ROTV) {
           const float2 a = *reinterpret_cast<const float2*>(th + d0 / 2);
           float s0, c0, s1, c1;
-          sincosf(a.x, &s0, &c0);
-          sincosf(a.y, &s1, &c1);
+          __sincosf(a.x, &s0, &c0);
+          __sincosf(a.y, &s1, &c1);
           rotate_pair(x0, x1, c0, -s0);
           rotate_pair(x2, x3, c1, -s1);
         }
@@ -635,8 +661,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
     const float* __restrict__ theta, const float* __restrict__ alibi,
     const float* __restrict__ gate2, const double* __restrict__ gbase, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int L, int Lp, int H, int Hphi, int nqt, int total_tiles, int rot_qk,
-    float qscale, int paired, const float* __restrict__ hscale) {
+    float* __restrict__ lse, int L, int Lp, int vrows, int H, int Hphi, int nqt, int total_tiles,
+    int rot_qk, float qscale, int paired, const float* __restrict__ hscale) {
   constexpr int STAGE = BN * D * 2 + D * BN * 2 + (((BIAS & 2) != 0) ? BN * 4 + 256 : 0);  // as in attn_tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
   constexpr bool SPREAD = (BIAS != 0) && !FUSED;
@@ -645,23 +671,24 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
   if (PAIRABLE && paired) {
     const int x = (int)(blockIdx.x % 8), c = (int)(blockIdx.x / 8);
     attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(x * per + c, smem, qr, kr, vt, kmax, theta,
-                                                        alibi, gate2, gbase, o, lse, L, Lp, H, Hphi, nqt,
+                                                        alibi, gate2, gbase, o, lse, L, Lp, vrows, H, Hphi, nqt,
                                                         total_tiles, rot_qk, qscale, hscale);
     __syncthreads();  // every wave is done with the LDS ring before it is refilled
     attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(x * per + per - 1 - c, smem, qr, kr, vt,
-                                                        kmax, theta, alibi, gate2, gbase, o, lse, L, Lp, H,
-                                                        Hphi, nqt, total_tiles, rot_qk, qscale, hscale);
+                                                        kmax, theta, alibi, gate2, gbase, o, lse, L, Lp,
+                                                        vrows, H, Hphi, nqt, total_tiles, rot_qk,
+                                                        qscale, hscale);
     return;
   }
   const int logical = SPREAD ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(logical, smem, qr, kr, vt, kmax, theta, alibi,
-                                                      gate2, gbase, o, lse, L, Lp, H, Hphi, nqt,
+                                                      gate2, gbase, o, lse, L, Lp, vrows, H, Hphi, nqt,
                                                       total_tiles, rot_qk, qscale, hscale);
 }
 
 template <int D, int QPW, int NW, int NST, int MINB, bool FUSED>
 hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
-                           const uint16_t* vt, const float* kmax, const float* theta,
+                           const uint16_t* vt, int vrows, const float* kmax, const float* theta,
                            const float* alibi, const float* gate2, const double* gbase, uint16_t* o,
                            float* lse, hipStream_t stream) {
   constexpr int BM = QPW * NW;
@@ -677,7 +704,7 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
   hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, MINB, FUSED, A, R>), dim3(grid),      \
                      dim3(NW * 64), 0, stream, qr, kr, vt, kmax, theta, alibi, gate2, gbase, o, \
                      lse,                                                                       \
-                     g.L, g.Lp, g.H, g.Hphi, nqt, total, rqk, qscale, paired, g.hscale)
+                     g.L, g.Lp, vrows, g.H, g.Hphi, nqt, total, rqk, qscale, paired, g.hscale)
 #define ARP_BF16_LAUNCH_R(A) \
   do {                       \
     if (rv) ARP_BF16_LAUNCH(A, true); else ARP_BF16_LAUNCH(A, false); \
@@ -710,10 +737,11 @@ static int device_cus() {
   return n;
 }
 
-hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const uint16_t* kr,
-                                    const uint16_t* vt, const float* kmax, const float* theta,
-                                    const float* alibi, const float* gate2, const double* gbase,
-                                    uint16_t* o, float* lse, hipStream_t stream) {
+hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* q, const uint16_t* kr,
+                                    const uint16_t* v, int vrows, const float* kmax,
+                                    const float* theta, const float* alibi, const float* gate2,
+                                    const double* gbase, uint16_t* o, float* lse,
+                                    hipStream_t stream) {
   if (g.D == 64) {
     // Two shapes, every row computed the same way in both (bit-identical
     // results):
@@ -729,9 +757,9 @@ hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const
     const long wg512 = (long)g.B * g.H * ((g.L + 511) / 512);
     const bool biased = (g.flags & (ARP_ALIBI | ARP_FORGET_GATE)) != 0;
     if (!biased && g.L >= 16384 && wg512 >= 2L * device_cus())
-      return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, gbase, o,
+      return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, q, kr, v, vrows, kmax, theta, alibi, gate2, gbase, o,
                                                      lse, stream);
-    return launch_bf16_cfg<64, 32, 4, 2, 2, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, gbase, o, lse,
+    return launch_bf16_cfg<64, 32, 4, 2, 2, false>(g, q, kr, v, vrows, kmax, theta, alibi, gate2, gbase, o, lse,
                                                    stream);
   }
   // d = 128: 256-query workgroups of 8 waves x 32 queries for unbiased grids
@@ -741,9 +769,9 @@ hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* qr, const
   const long wg256 = (long)g.B * g.H * ((g.L + 255) / 256);
   const bool biased = (g.flags & (ARP_ALIBI | ARP_FORGET_GATE)) != 0;
   if (!biased && wg256 >= 4L * device_cus())
-    return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, gbase, o,
+    return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, q, kr, v, vrows, kmax, theta, alibi, gate2, gbase, o,
                                                     lse, stream);
-  return launch_bf16_cfg<128, 32, 4, 2, 2, false>(g, qr, kr, vt, kmax, theta, alibi, gate2, gbase, o, lse,
+  return launch_bf16_cfg<128, 32, 4, 2, 2, false>(g, q, kr, v, vrows, kmax, theta, alibi, gate2, gbase, o, lse,
                                                   stream);
 }
 
@@ -751,8 +779,8 @@ hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const ui
                                   const uint16_t* v, const float* theta, const float* alibi,
                                   uint16_t* o, hipStream_t stream) {
   if (g.D == 64)
-    return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
-  return launch_bf16_cfg<128, 32, 8, 2, 1, true>(g, q, k, v, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
+    return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, g.L, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
+  return launch_bf16_cfg<128, 32, 8, 2, 1, true>(g, q, k, v, g.L, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
 }
 
 }  // namespace arp

@@ -19,6 +19,19 @@ namespace arp {
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef const __attribute__((address_space(1))) void* global_void_ptr;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+// LDS transpose read (ds_read_b64_tr_b16): each group of 16 lanes names a
+// 16 x 4 block of 16-bit elements (lane j of the group: four consecutive
+// elements at p); lane i of the group receives element i % 4 of the rows named
+// by lanes 4 e + i / 4, e = 0..3.
+// The four elements come back packed in two dwords (element 0 in the low
+// half of the first).
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(const_cast<void*>(p))));
+}
 
 // Row order of K~ in LDS: bits 2 and 3 of the key index swapped (an involution).
 __device__ __forceinline__ int swap_bits23(int x) {
@@ -34,6 +47,18 @@ template <int ROWB>
 __device__ __forceinline__ int swz(int row) {
   static_assert(ROWB == 64 || ROWB == 128 || ROWB == 256, "row size");
   return ROWB == 64 ? ((row >> 2) & 3) : ROWB == 128 ? ((row >> 1) & 7) : (row & 15);
+}
+
+// LDS swizzle of the natural V rows (64-bit transpose reads): one read
+// instruction of 32 lanes covers 4 consecutive rows x 64 bytes (four 16-byte
+// chunks, 4b .. 4b + 3), which must land in the four distinct 64-byte quarters
+// of the 256-byte bank period.  128-byte rows: consecutive rows already sit
+// in opposite halves, so rows r and r + 2 swap the 64-byte blocks of their
+// half (chunk bit 2 from row bit 1); 256-byte rows: row r % 4 picks the block.
+template <int ROWB>
+__device__ __forceinline__ int swzv(int row) {
+  static_assert(ROWB == 128 || ROWB == 256, "row size");
+  return ROWB == 128 ? ((row >> 1) & 1) << 2 : (row & 3) << 2;
 }
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {

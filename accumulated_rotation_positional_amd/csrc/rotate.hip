@@ -6,17 +6,20 @@
 // Sec. 2.1 eq. (1); the RoPE decay-curve post's rope(): adjacent pairs, sine
 // term negative in the first component.)
 //
-// rotate_qkv_kernel: the pre-rotation pass in front of the bf16 attention
-// kernel.  One workgroup handles 64 tokens x head_dim of one (batch, head):
-//  * q, k, v and theta are read with 16-byte coalesced loads (one chunk of 8
-//    elements = 4 pairs per thread, with the matching float4 of angles);
+// rotate_kv_kernel: the pre-rotation pass in front of the bf16 attention
+// kernel (which rotates q itself, in its prologue).  One workgroup handles
+// 64 tokens x head_dim of one (batch, head):
+//  * k (and v with value transport) and theta are read with 16-byte coalesced
+//    loads (one chunk of 8 elements = 4 pairs per thread, with the matching
+//    float4 of angles);
 //  * sin/cos of the wrapped angle are computed once per (token, pair) and
-//    shared by q, k and v;
-//  * q~ is pre-multiplied by scale * log2(e) (and by the head's query
-//    multiplier with ARP_HEAD_SCALE) so the attention kernel's matrix-core
-//    products are already base-2 logits;
-//  * q~ and k~ are written row-major [Lp, D]; v~ is transposed through LDS and
-//    written [D, Lp], the layout the P V product reads (keys contiguous);
+//    shared by k and v, from the hardware sine and cosine of turns
+//    (__sincosf: v_sin_f32 / v_cos_f32 of theta / 2 pi; absolute error below
+//    3e-7 for angles in [-pi, pi), far below the bf16 rounding of k~);
+//  * k~ and v~ are written row-major [Lp, D], the layout the attention
+//    kernel stages into LDS (it reads the V^T operand with transpose reads);
+//    without value transport v is not touched: the attention kernel reads
+//    the caller's v;
 //  * tokens in [L, Lp) are written as zeros (the attention kernel reads whole
 //    tiles without bounds checks);
 //  * the largest |k~| of the 64 keys (one attention key tile) is recorded, from
@@ -31,16 +34,13 @@ namespace {
 constexpr int ROT_TOKENS = 64;
 
 template <int D>
-__global__ __launch_bounds__(256) void rotate_qkv_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ theta, uint16_t* __restrict__ qr, uint16_t* __restrict__ kr,
-    uint16_t* __restrict__ vt, float* __restrict__ kmax, int L, int Lp, int H, int Hphi,
-    uint32_t flags, float qscale0, const float* __restrict__ hscale) {
+__global__ __launch_bounds__(256) void rotate_kv_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ theta, uint16_t* __restrict__ kr, uint16_t* __restrict__ vr,
+    float* __restrict__ kmax, int L, int Lp, int H, int Hphi, uint32_t flags) {
   constexpr int P = D / 2;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int ITER = ROT_TOKENS * CPR / 256;
-  constexpr int VT_STRIDE = ROT_TOKENS + 8;  // padded LDS row (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VT_STRIDE];
   __shared__ uint32_t s_kmax2;  // max |k~|^2 of the tile, as the bits of a non-negative float
   static_assert(ROT_TOKENS == KEY_TILE, "one workgroup per attention key tile");
 
@@ -51,8 +51,6 @@ __global__ __launch_bounds__(256) void rotate_qkv_kernel(
   const int tid = threadIdx.x;
   const bool rot_qk = (flags & ARP_ROTATE_QK) != 0;
   const bool rot_v = (flags & ARP_ROTATE_V) != 0;
-  // the head's query multiplier (AdaScale) rides with scale * log2 e
-  const float qscale = hscale != nullptr ? qscale0 * hscale[h] : qscale0;
   if (tid == 0) s_kmax2 = 0u;
   __syncthreads();
 
@@ -61,12 +59,11 @@ __global__ __launch_bounds__(256) void rotate_qkv_kernel(
     const int idx = it * 256 + tid;
     const int r = idx / CPR, c = idx % CPR;
     const int tok = t0 + r;
-    u32x4 qa = {0, 0, 0, 0}, ka = {0, 0, 0, 0}, va = {0, 0, 0, 0};
+    u32x4 ka = {0, 0, 0, 0}, va = {0, 0, 0, 0};
     if (tok < L) {
       const size_t off = ((size_t)bh * L + tok) * D + c * 8;
-      qa = *reinterpret_cast<const u32x4*>(q + off);
       ka = *reinterpret_cast<const u32x4*>(k + off);
-      va = *reinterpret_cast<const u32x4*>(v + off);
+      if (rot_v) va = *reinterpret_cast<const u32x4*>(v + off);
       float4 th = make_float4(0.f, 0.f, 0.f, 0.f);
       if (rot_qk || rot_v)
         th = *reinterpret_cast<const float4*>(theta + ((size_t)(b * Hphi + g) * L + tok) * P + c * 4);
@@ -74,23 +71,20 @@ __global__ __launch_bounds__(256) void rotate_qkv_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float sn, cs;
-        sincosf(ang[e], &sn, &cs);
-        float q0 = lo_bf16(qa[e]), q1 = hi_bf16(qa[e]);
+        __sincosf(ang[e], &sn, &cs);
         float k0 = lo_bf16(ka[e]), k1 = hi_bf16(ka[e]);
-        float v0 = lo_bf16(va[e]), v1 = hi_bf16(va[e]);
-        if (rot_qk) {
-          rotate_pair(q0, q1, cs, sn);
-          rotate_pair(k0, k1, cs, sn);
-        }
-        if (rot_v) rotate_pair(v0, v1, cs, sn);
-        qa[e] = pack_bf16x2(q0 * qscale, q1 * qscale);
+        if (rot_qk) rotate_pair(k0, k1, cs, sn);
         ka[e] = pack_bf16x2(k0, k1);
-        va[e] = pack_bf16x2(v0, v1);
+        if (rot_v) {
+          float v0 = lo_bf16(va[e]), v1 = hi_bf16(va[e]);
+          rotate_pair(v0, v1, cs, sn);
+          va[e] = pack_bf16x2(v0, v1);
+        }
       }
     }
     const size_t roff = ((size_t)bh * Lp + tok) * D + c * 8;
-    *reinterpret_cast<u32x4*>(qr + roff) = qa;
     *reinterpret_cast<u32x4*>(kr + roff) = ka;
+    if (rot_v) *reinterpret_cast<u32x4*>(vr + roff) = va;
     // |k~|^2 of this row from the stored bf16 values (the CPR threads of a
     // row are consecutive lanes), then the tile maximum.
     float n2 = 0.f;
@@ -102,22 +96,9 @@ __global__ __launch_bounds__(256) void rotate_qkv_kernel(
 #pragma unroll
     for (int m = 1; m < CPR; m <<= 1) n2 += __shfl_xor(n2, m);
     if (c == 0) atomicMax(&s_kmax2, __float_as_uint(n2));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s_vt[(c * 8 + 2 * e) * VT_STRIDE + r] = (uint16_t)(va[e] & 0xFFFFu);
-      s_vt[(c * 8 + 2 * e + 1) * VT_STRIDE + r] = (uint16_t)(va[e] >> 16);
-    }
   }
   __syncthreads();
   if (tid == 0) kmax[(size_t)bh * (Lp / ROT_TOKENS) + blockIdx.x] = sqrtf(__uint_as_float(s_kmax2));
-  // v~^T rows: D rows x 64 tokens = 8 chunks of 16 bytes per row.
-#pragma unroll
-  for (int it = 0; it < D * 8 / 256; ++it) {
-    const int idx = it * 256 + tid;
-    const int drow = idx / 8, cc = idx % 8;
-    const u32x4 w = *reinterpret_cast<const u32x4*>(&s_vt[drow * VT_STRIDE + cc * 8]);
-    *reinterpret_cast<u32x4*>(vt + ((size_t)bh * D + drow) * Lp + t0 + cc * 8) = w;
-  }
 }
 
 // Diagnostic rotation with fp32 output: one thread per (row, pair).
@@ -253,20 +234,17 @@ hipError_t launch_gate_scan(const Geometry& g, const float* logf, float* gate2, 
   return hipGetLastError();
 }
 
-hipError_t launch_rotate_qkv(const Geometry& g, const void* q, const void* k, const void* v,
-                             const float* theta, uint16_t* qr, uint16_t* kr, uint16_t* vt,
-                             float* kmax, hipStream_t stream) {
+hipError_t launch_rotate_kv(const Geometry& g, const void* k, const void* v, const float* theta,
+                            uint16_t* kr, uint16_t* vr, float* kmax, hipStream_t stream) {
   dim3 grid(g.Lp / ROT_TOKENS, g.B * g.H);
-  const float qscale = g.scale * LOG2E;
-  const auto* qb = static_cast<const uint16_t*>(q);
   const auto* kb = static_cast<const uint16_t*>(k);
   const auto* vb = static_cast<const uint16_t*>(v);
   if (g.D == 64)
-    hipLaunchKernelGGL((rotate_qkv_kernel<64>), grid, dim3(256), 0, stream, qb, kb, vb, theta, qr,
-                       kr, vt, kmax, g.L, g.Lp, g.H, g.Hphi, g.flags, qscale, g.hscale);
+    hipLaunchKernelGGL((rotate_kv_kernel<64>), grid, dim3(256), 0, stream, kb, vb, theta, kr, vr,
+                       kmax, g.L, g.Lp, g.H, g.Hphi, g.flags);
   else
-    hipLaunchKernelGGL((rotate_qkv_kernel<128>), grid, dim3(256), 0, stream, qb, kb, vb, theta,
-                       qr, kr, vt, kmax, g.L, g.Lp, g.H, g.Hphi, g.flags, qscale, g.hscale);
+    hipLaunchKernelGGL((rotate_kv_kernel<128>), grid, dim3(256), 0, stream, kb, vb, theta, kr, vr,
+                       kmax, g.L, g.Lp, g.H, g.Hphi, g.flags);
   return hipGetLastError();
 }
 

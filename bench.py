@@ -479,10 +479,10 @@ def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int =
             if fused:
                 binding.attn_fwd(q, k, v, theta, desc, alibi=alibi, out=o, ws=ws)
             else:
-                binding.rotate_qkv(q, k, v, theta, desc, ws=ws)
+                binding.rotate_kv(k, v, theta, desc, ws=ws)
                 if evs is not None:
                     evs[2].record(stream)
-                binding.attn_rotated(theta, alibi, o, desc, ws)
+                binding.attn_rotated(q, v, theta, alibi, o, desc, ws)
             if evs is not None:
                 evs[n_ev].record(stream)
 
@@ -507,7 +507,7 @@ def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int =
             "shape": [w.batch, w.heads, w.seqlen, w.head_dim], "dtype": w.dtype,
             "rotate_v": w.rotate_v, "alibi": w.use_alibi, "ms_per_step": round(ms_step, 4),
             "kernels_ms": {"angle_scan": round(scan_ms, 5),
-                           "rotate_qkv": round(float(seg[:, 1].mean()), 5) if n_ev == 3 else 0.0,
+                           "rotate_kv": round(float(seg[:, 1].mean()), 5) if n_ev == 3 else 0.0,
                            "attn_fwd": round(attn_ms, 5)},
             "tflops_step": round(w.flops / (ms_step * 1e-3) / 1e12, 2),
             "tokens_per_s": round(w.batch * w.seqlen / (ms_step * 1e-3), 1),
@@ -571,10 +571,10 @@ def main():
         if fused:
             binding.attn_fwd(q, k, v, theta, desc, alibi=alibi, out=o, ws=ws)
         else:
-            binding.rotate_qkv(q, k, v, theta, desc, ws=ws)
+            binding.rotate_kv(k, v, theta, desc, ws=ws)
             if evs is not None:
                 evs[2].record(stream)
-            binding.attn_rotated(theta, alibi, o, desc, ws)
+            binding.attn_rotated(q, v, theta, alibi, o, desc, ws)
         if evs is not None:
             evs[n_ev].record(stream)
 
@@ -651,7 +651,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seqlen,
                    "head_dim": w.head_dim, "rotate_v": w.rotate_v, "alibi": w.use_alibi,
                    "rotation": "fused-in-staging" if fused else "pre-rotation pass"},
-        "kernels_ms": {"angle_scan": round(scan_ms, 5), "rotate_qkv": round(rot_ms, 5),
+        "kernels_ms": {"angle_scan": round(scan_ms, 5), "rotate_kv": round(rot_ms, 5),
                        "attn_fwd": round(attn_ms, 5)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -43,8 +43,8 @@
  *        keeps two halves and alternates between them), so one buffer serves
  *        any number of calls and problem sizes, as long as each call's
  *        arp_scan_state_bytes fits in it.
- *      workspace (arp_workspace_bytes): the rotated bf16 operands of the
- *        pre-rotation path; no initialisation needed.
+ *      workspace (arp_workspace_bytes): the rotated bf16 keys (and values)
+ *        of the pre-rotation path; no initialisation needed.
  *    Calls that share a buffer must be ordered (same stream).
  *  - Arguments are validated on the host before anything is enqueued; an
  *    error code means nothing was launched.  ARP_ERR_HIP reports a failed
@@ -140,10 +140,10 @@ arp_status arp_adascale_lambda(int32_t heads, const float* tau, const float* gam
  * The state must be zero before first use; every call leaves it ready for the next. */
 size_t arp_scan_state_bytes(const arp_desc* desc);
 
-/* Bytes of the operand workspace for desc: the rotated bf16 q~, k~, v~^T of
- * the pre-rotation path, per-tile key-norm maxima, and with ARP_FORGET_GATE the
- * gate prefix and its chunk totals; 0 for fp32 I/O or ARP_FUSED_ROTATION (and
- * when desc is invalid). */
+/* Bytes of the operand workspace for desc: the rotated bf16 k~ (and v~ with
+ * ARP_ROTATE_V) of the pre-rotation path, per-tile key-norm maxima, and with
+ * ARP_FORGET_GATE the gate prefix and its tile bases and chunk totals; 0 for
+ * fp32 I/O or ARP_FUSED_ROTATION (and when desc is invalid). */
 size_t arp_workspace_bytes(const arp_desc* desc);
 
 /* a1. Accumulated angles: theta[b,g,t,p] = wrap(sum_{s<=t} phi[b,g,s,p]) in
@@ -200,22 +200,31 @@ arp_status arp_angle_scan_const(const arp_desc* desc, const float* freq, float* 
 arp_status arp_random_phi(const arp_desc* desc, uint64_t seed, uint64_t step, const float* bound,
                           float* phi, void* stream);
 
-/* a2. Pre-rotation pass (bf16): writes R(Theta_t) q_t (times scale*log2(e)),
- * R(Theta_t) k_t and R(Theta_t) v_t (or the unrotated tensors, per the flags)
- * as bf16 into the workspace, in the layout arp_attn_rotated reads.
+/* a2 for keys and values (bf16 pre-rotation pass): writes R(Theta_t) k_t (or
+ * k_t without ARP_ROTATE_QK) and, with ARP_ROTATE_V, R(Theta_t) v_t as bf16
+ * into the workspace, with each 64-key tile's largest |k~|, in the layout
+ * arp_attn_rotated reads.  v is read (and required) only with ARP_ROTATE_V.
+ * The queries are rotated by arp_attn_rotated itself.
  * Method: AdaRoPE Sec. 2.1 eq. (1); RoPE post, rope(). */
-arp_status arp_rotate_qkv(const arp_desc* desc, const void* q, const void* k, const void* v,
-                          const float* theta, void* workspace, size_t workspace_bytes,
-                          void* stream);
+arp_status arp_rotate_kv(const arp_desc* desc, const void* k, const void* v, const float* theta,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* a3-a6 over operands already in the workspace (bf16, after arp_rotate_qkv):
- * scores, causal mask, distance bias, online softmax, P V, and the
- * value-transport epilogue o_i = R(Theta_i)^T o~_i.  Method: eq. (2)-(4),
- * (8), (11).  theta is read only with ARP_ROTATE_V, alibi only with ARP_ALIBI. */
-arp_status arp_attn_rotated(const arp_desc* desc, const float* theta, const float* alibi,
-                            void* o, void* workspace, size_t workspace_bytes, void* stream);
+/* a2 for the queries, then a3-a6, over the keys (and transported values) that
+ * arp_rotate_kv left in the workspace (bf16): q (the caller's, [batch, heads,
+ * seqlen, head_dim]) rotated by R(Theta_i) and multiplied by the logit scale
+ * in the kernel's prologue; scores, causal mask, distance bias, online
+ * softmax, P V, and the value-transport epilogue o_i = R(Theta_i)^T o~_i.
+ * Without ARP_ROTATE_V the values are the caller's v, read here (and
+ * required); with it, v~ from the workspace (v may be NULL).  Method: eq.
+ * (2)-(4), (8), (11).  theta is read with ARP_ROTATE_QK or ARP_ROTATE_V,
+ * alibi with ARP_ALIBI.  The bf16 kernels take sin/cos from the hardware's
+ * sine and cosine of turns: angles are expected as the scan writes them, in
+ * [-pi, pi) (absolute error below 3e-7 there; it grows with |theta|). */
+arp_status arp_attn_rotated(const arp_desc* desc, const void* q, const void* v, const float* theta,
+                            const float* alibi, void* o, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
-/* a2-a6: attention given accumulated angles.  bf16: arp_rotate_qkv then
+/* a2-a6: attention given accumulated angles.  bf16: arp_rotate_kv then
  * arp_attn_rotated, or one kernel that rotates while staging with
  * ARP_FUSED_ROTATION.  fp32: one kernel, rotation fused into staging. */
 arp_status arp_attn_fwd(const arp_desc* desc, const void* q, const void* k, const void* v,
@@ -237,9 +246,9 @@ arp_status arp_forward(const arp_desc* desc, const void* q, const void* k, const
  * flags, kernels and results as arp_forward (ARP_FUSED_ROTATION included).
  * Limits: arp_scan_state_bytes(desc) <= 24 MiB and arp_workspace_bytes(desc)
  * <= 40 MiB, else ARP_ERR_SCRATCH with nothing launched (the pre-rotation
- * path's operands take 6 head_dim bytes per token and head: ~109 thousand
- * tokens x heads fit at head_dim 64, e.g. 8 x 8 heads at 1024 tokens, half
- * that at 128; ARP_FUSED_ROTATION and fp32 I/O need no operand workspace).  The first call on a device clears the scan-state region with a
+ * path's operands take 2 head_dim bytes per token and head, 4 with
+ * ARP_ROTATE_V: ~327 (164) thousand tokens x heads at head_dim 64, half that
+ * at 128; ARP_FUSED_ROTATION and fp32 I/O need no operand workspace).  The first call on a device clears the scan-state region with a
  * kernel on its stream; every call on that GPU shares the array, so calls that
  * overlap on one GPU (different streams or threads without ordering) race. */
 arp_status arp_forward_noalloc(const arp_desc* desc, const void* q, const void* k, const void* v,

@@ -80,9 +80,11 @@ def test_workspace_and_scan_state_bytes():
     L = b.lib()
     d = _desc(batch=2, heads=8, seqlen=16384)
     ws = L.arp_workspace_bytes(ctypes.byref(d))
-    operands = 3 * 2 * 8 * 16384 * 64 * 2
+    operands = 2 * 8 * 16384 * 64 * 2   # k~ only: q is rotated by the attention kernel, v read there
     kmax = 2 * 8 * (16384 // 64) * 4  # max |k~| per 64-key tile, fp32
     assert operands + kmax <= ws < operands + kmax + 4096 and ws % 256 == 0
+    transported = _desc(batch=2, heads=8, seqlen=16384, flags=b.ROTATE_QK | b.ROTATE_V)
+    assert L.arp_workspace_bytes(ctypes.byref(transported)) == ws + operands  # + v~
     st = L.arp_scan_state_bytes(ctypes.byref(d))
     assert 0 < st < (16 << 20) and st % 256 == 0
     fused = _desc(batch=2, heads=8, seqlen=16384, flags=b.ROTATE_QK | b.FUSED_ROTATION)
@@ -112,11 +114,14 @@ def test_entry_points_reject_null_and_misaligned_pointers():
     assert L.arp_angle_scan(by, A, A, None, st, None) == b.ERR_WORKSPACE
     assert L.arp_angle_scan(by, A, A, A, 16, None) == b.ERR_WORKSPACE
     assert L.arp_angle_scan(by, A, A, A + 16, st, None) == b.ERR_ALIGNMENT
-    assert L.arp_rotate_qkv(by, A, None, A, A, A, big, None) == b.ERR_INVALID_ARG
-    assert L.arp_rotate_qkv(by, A, A, M, A, A, big, None) == b.ERR_ALIGNMENT
-    assert L.arp_rotate_qkv(by, A, A, A, None, A, big, None) == b.ERR_INVALID_ARG
-    assert L.arp_attn_rotated(by, A, A, None, A, big, None) == b.ERR_INVALID_ARG
-    assert L.arp_attn_rotated(by, A, A, A, A, 8, None) == b.ERR_WORKSPACE
+    assert L.arp_rotate_kv(by, None, A, A, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_rotate_kv(by, A, M, A, A, big, None) == b.ERR_ALIGNMENT
+    assert L.arp_rotate_kv(by, A, A, None, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_rotated(by, A, A, A, None, None, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_rotated(by, A, A, A, None, A, A, 8, None) == b.ERR_WORKSPACE
+    # without value transport the attention reads the caller's v: required
+    assert L.arp_attn_rotated(by, A, None, A, None, A, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_rotated(by, None, A, A, None, A, A, big, None) == b.ERR_INVALID_ARG
     assert L.arp_attn_fwd(by, A, A, A, A, None, None, A, big, None) == b.ERR_INVALID_ARG
     assert L.arp_attn_fwd(by, A, A, A, A, None, M, A, big, None) == b.ERR_ALIGNMENT
     assert L.arp_forward(by, A, A, A, None, None, A, A, A, st, A, big, None) == b.ERR_INVALID_ARG
@@ -135,13 +140,15 @@ def test_alibi_requires_slopes_and_rotation_requires_theta():
     by = ctypes.byref(d)
     assert L.arp_forward(by, A, A, A, A, None, A, A, A, st, A, big, None) == b.ERR_INVALID_ARG
     assert L.arp_attn_fwd(by, A, A, A, A, None, A, A, big, None) == b.ERR_INVALID_ARG
-    assert L.arp_attn_rotated(by, A, None, A, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_rotated(by, A, A, A, None, A, A, big, None) == b.ERR_INVALID_ARG
     dv = _desc(flags=b.ROTATE_V)
-    assert L.arp_attn_rotated(ctypes.byref(dv), None, None, A, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_rotated(ctypes.byref(dv), A, None, None, None, A, A, big, None) == b.ERR_INVALID_ARG
+    # with value transport the pass needs v
+    assert L.arp_rotate_kv(ctypes.byref(dv), A, None, A, A, big, None) == b.ERR_INVALID_ARG
     df32 = _desc(dtype="f32")
     # the pre-rotation pass and its attention kernel exist for bf16 only
-    assert L.arp_rotate_qkv(ctypes.byref(df32), A, A, A, A, A, big, None) == b.ERR_UNSUPPORTED
-    assert L.arp_attn_rotated(ctypes.byref(df32), A, None, A, A, big, None) == b.ERR_UNSUPPORTED
+    assert L.arp_rotate_kv(ctypes.byref(df32), A, A, A, A, big, None) == b.ERR_UNSUPPORTED
+    assert L.arp_attn_rotated(ctypes.byref(df32), A, A, A, None, A, A, big, None) == b.ERR_UNSUPPORTED
 
 
 def test_binding_refuses_cpu_tensors():
@@ -188,8 +195,8 @@ def test_forget_gate_flag_is_refused_outside_the_gated_forward():
     st = L.arp_scan_state_bytes(by)
     assert L.arp_forward(by, A, A, A, A, None, A, A, A, st, A, big, None) == b.ERR_INVALID_ARG
     assert L.arp_attn_fwd(by, A, A, A, A, None, A, A, big, None) == b.ERR_INVALID_ARG
-    assert L.arp_rotate_qkv(by, A, A, A, A, A, big, None) == b.ERR_INVALID_ARG
-    assert L.arp_attn_rotated(by, A, None, A, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_rotate_kv(by, A, A, A, A, big, None) == b.ERR_INVALID_ARG
+    assert L.arp_attn_rotated(by, A, A, A, None, A, A, big, None) == b.ERR_INVALID_ARG
     # the gated forward needs the gates
     assert L.arp_forward_ex(by, A, A, A, A, None, None, A, A, None, A, st, A, big,
                             None) == b.ERR_INVALID_ARG
@@ -270,8 +277,8 @@ def test_scan_state_and_workspace_need_256_byte_alignment():
     st = L.arp_scan_state_bytes(by)
     assert A % 256 == 0
     assert L.arp_angle_scan(by, A, A, A + 16, st, None) == b.ERR_ALIGNMENT
-    assert L.arp_attn_rotated(by, A, None, A, A + 16, big, None) == b.ERR_ALIGNMENT
-    assert L.arp_rotate_qkv(by, A, A, A, A, A + 16, big, None) == b.ERR_ALIGNMENT
+    assert L.arp_attn_rotated(by, A, A, A, None, A, A + 16, big, None) == b.ERR_ALIGNMENT
+    assert L.arp_rotate_kv(by, A, A, A, A + 16, big, None) == b.ERR_ALIGNMENT
     assert L.arp_forward(by, A, A, A, A, None, A, A, A + 16, st, A, big, None) == b.ERR_ALIGNMENT
     assert L.arp_forward(by, A, A, A, A, None, A, A, A, st, A + 16, big, None) == b.ERR_ALIGNMENT
     bw = L.arp_backward_workspace_bytes(by)
@@ -420,11 +427,11 @@ def test_noalloc_forward_validates_before_touching_the_device():
     """arp_forward_noalloc checks its arguments and its scratch limits on the
     host (fake addresses: nothing is launched, no device is touched)."""
     L = b.lib()
-    d = _desc(batch=2, heads=8, seqlen=16384)
+    d = _desc(batch=2, heads=8, seqlen=16384, flags=b.ROTATE_QK | b.ROTATE_V)
     by = ctypes.byref(d)
     assert L.arp_forward_noalloc(by, A, A, A, None, None, A, A, None) == b.ERR_INVALID_ARG
     assert L.arp_forward_noalloc(by, A, A, A, A, None, A, M, None) == b.ERR_ALIGNMENT
-    # 96 MiB of pre-rotated operands exceed the 40 MiB operand scratch
+    # 64 MiB of pre-rotated operands (k~ and v~) exceed the 40 MiB operand scratch
     assert L.arp_forward_noalloc(by, A, A, A, A, None, A, A, None) == b.ERR_SCRATCH
     # 4 x 32 heads at 32768 tokens (d = 128): a scan state beyond 24 MiB, even fused
     big = _desc(batch=4, heads=32, seqlen=32768, head_dim=128, flags=b.ROTATE_QK | b.FUSED_ROTATION)

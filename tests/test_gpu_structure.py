@@ -66,18 +66,21 @@ def test_deterministic(name):
 
 
 def test_step_entry_points_compose_to_forward():
-    """arp_angle_scan -> arp_rotate_qkv -> arp_attn_rotated gives exactly
-    arp_forward's output (the benchmark times the steps separately)."""
+    """arp_angle_scan -> arp_rotate_kv -> arp_attn_rotated gives exactly
+    arp_forward's output (the benchmark times the steps separately), with
+    value transport (v~ from the pass) and without (the caller's v read by the
+    attention kernel)."""
     w = wl.make("extrap_16k", seqlen=2048)
     q, k, v, phi = (to_dev(getattr(w, n)) for n in ("q", "k", "v", "phi"))
-    say("[gpu] step entry points")
-    o_fwd, th_fwd = binding.forward(q, k, v, phi, rotate_v=True)
-    desc = binding.desc_for(q, binding.flags_for(rotate_v=True))
-    ws = binding.workspace(desc, DEV)
-    theta = binding.angle_scan(phi, desc)
-    binding.rotate_qkv(q, k, v, theta, desc, ws=ws)
-    o = torch.empty_like(q)
-    binding.attn_rotated(theta, None, o, desc, ws)
-    torch.cuda.synchronize()
-    assert torch.equal(theta, th_fwd)
-    assert torch.equal(o, o_fwd)
+    for rv in (True, False):
+        say(f"[gpu] step entry points rotate_v={rv}")
+        o_fwd, th_fwd = binding.forward(q, k, v, phi, rotate_v=rv)
+        desc = binding.desc_for(q, binding.flags_for(rotate_v=rv))
+        ws = binding.workspace(desc, DEV)
+        theta = binding.angle_scan(phi, desc)
+        binding.rotate_kv(k, v, theta, desc, ws=ws)
+        o = torch.empty_like(q)
+        binding.attn_rotated(q, v, theta, None, o, desc, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(theta, th_fwd)
+        assert torch.equal(o, o_fwd)
