@@ -92,6 +92,16 @@ hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const ui
                                   const uint16_t* v, const float* theta, const float* alibi,
                                   uint16_t* o, hipStream_t stream);
 // lse (nullable): [B, H, L] base-2 log-sum-exp of each row's scaled logits
+// Compute units of the current device (queried on every call: launches size
+// their grids by it; 256 if the query fails).
+inline int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
 hipError_t launch_attn_f32(const Geometry& g, const float* q, const float* k, const float* v,
                            const float* theta, const float* alibi, float* o, float* lse,
                            hipStream_t stream);

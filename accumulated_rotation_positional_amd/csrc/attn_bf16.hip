@@ -729,14 +729,6 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
 
 // Compute units of the current device (256 on an MI355X), queried on every
 // call (a host-side attribute lookup; the library keeps no mutable state).
-static int device_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
-  return n;
-}
-
 hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* q, const uint16_t* kr,
                                     const uint16_t* v, int vrows, const float* kmax,
                                     const float* theta, const float* alibi, const float* gate2,

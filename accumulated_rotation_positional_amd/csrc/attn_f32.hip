@@ -1,11 +1,15 @@
 // attn_f32.hip -- fp32 causal attention with accumulated rotations (gfx950).
 //
 // The fp32-I/O path: every product and sum in fp32, so outputs stay within
-// ~1e-6 of the exact result.  A workgroup of 256 threads owns 64 queries;
-// four adjacent lanes share one query and take every fourth key of each
+// ~1e-6 of the exact result.  A workgroup of 256 threads owns 256 / S
+// queries; S adjacent lanes share one query and take every S-th key of each
 // staged tile, each with its own online-softmax state (running maximum, sum,
-// output accumulator), and the four states are merged with lane shuffles at
-// the end.  32-key tiles of k and v are staged in LDS, each (key, pair)
+// output accumulator), and the S states are merged with lane shuffles at the
+// end.  S = 4 (64 queries per workgroup: each staged key serves 64 queries);
+// grids of fewer 64-query workgroups than compute units take S = 32 (8
+// queries per workgroup, eight times the workgroups, an eighth of the keys
+// per lane): such launches are bound by the serial key walk of one lane, not
+// by throughput.  64-key tiles of k and v are staged in LDS, each (key, pair)
 // rotated by R(Theta_j) while staged (one sin/cos shared by k and v).  Dot
 // products use four partial sums.  Online softmax in base 2 with an exact
 // running maximum.
@@ -21,20 +25,25 @@ namespace arp {
 
 namespace {
 
-constexpr int F32_Q = 64;   // queries per workgroup: each staged key is used by 64 queries
-constexpr int F32_S = 4;    // lanes (key subsets) per query
-constexpr int F32_T = F32_Q * F32_S;
-constexpr int F32_K = 32;   // keys per staged tile
+constexpr int F32_T = 256;  // threads per workgroup
+constexpr int F32_K = 64;   // keys per staged tile
 
-template <int D, bool ROT_QK, bool ROT_V, bool ALIBI>
+// F32_S: lanes (key subsets) per query; F32_T / F32_S queries per workgroup.
+template <int D, int F32_S, bool ROT_QK, bool ROT_V, bool ALIBI>
 __global__ __launch_bounds__(F32_T) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ theta, const float* __restrict__ alibi, float* __restrict__ o,
     float* __restrict__ lse, int L, int H, int Hphi, float qscale0,
     const float* __restrict__ hscale) {
   constexpr int P = D / 2;
-  __shared__ float sk[F32_K][D];
-  __shared__ float sv[F32_K][D];
+  constexpr int F32_Q = F32_T / F32_S;
+  static_assert(P % F32_S == 0, "each lane writes whole pairs");
+  // Rows padded by 16 bytes: the F32_S lanes of a query read F32_S different
+  // keys at once, and unpadded rows (256 or 512 bytes, a multiple of the bank
+  // period) would put all of them in the same LDS banks.
+  constexpr int ROW = D + 4;
+  __shared__ __attribute__((aligned(16))) float sk[F32_K][ROW];
+  __shared__ __attribute__((aligned(16))) float sv[F32_K][ROW];
 
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh % H;
@@ -68,33 +77,53 @@ __global__ __launch_bounds__(F32_T) void attn_f32_kernel(
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  const int i_last = min(L - 1, blockIdx.x * F32_Q + F32_Q - 1);
-  for (int j0 = 0; j0 <= i_last; j0 += F32_K) {
-    __syncthreads();
-    // Stage and rotate keys/values j0 .. j0+F32_K-1 (one sin/cos per (key, pair)).
-    for (int e = tid; e < F32_K * P; e += F32_T) {
-      const int jj = e / P, p = e % P;
-      const int j = j0 + jj;
-      float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
+  // Key/value staging, software-pipelined: the raw k, v and angles of tile
+  // n + 1 are loaded into registers (each thread IT (key, pair) items, pairs
+  // fastest, so a wave reads whole rows) before tile n is computed; they are
+  // rotated into LDS after it (one sin/cos per (key, pair), shared by k, v).
+  constexpr int IT = F32_K * P / F32_T;
+  static_assert(IT * F32_T == F32_K * P, "staging split");
+  float2 rk[IT], rv[IT];
+  float rt[IT];
+  auto fetch = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int e = tid + it * F32_T;
+      const int j = j0 + e / P, p = e % P;
+      rk[it] = rv[it] = make_float2(0.f, 0.f);
+      rt[it] = 0.f;
       if (j < L) {
         const size_t off = ((size_t)bh * L + j) * D + 2 * p;
-        k0 = k[off];
-        k1 = k[off + 1];
-        v0 = v[off];
-        v1 = v[off + 1];
-        if (ROT_QK || ROT_V) {
-          float sn, cs;
-          sincosf(th_base[(size_t)j * P + p], &sn, &cs);
-          if (ROT_QK) rotate_pair(k0, k1, cs, sn);
-          if (ROT_V) rotate_pair(v0, v1, cs, sn);
-        }
+        rk[it] = *reinterpret_cast<const float2*>(k + off);
+        rv[it] = *reinterpret_cast<const float2*>(v + off);
+        if (ROT_QK || ROT_V) rt[it] = th_base[(size_t)j * P + p];
       }
-      sk[jj][2 * p] = k0;
-      sk[jj][2 * p + 1] = k1;
-      sv[jj][2 * p] = v0;
-      sv[jj][2 * p + 1] = v1;
     }
+  };
+  auto commit = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int e = tid + it * F32_T;
+      const int jj = e / P, p = e % P;
+      float k0 = rk[it].x, k1 = rk[it].y, v0 = rv[it].x, v1 = rv[it].y;
+      if (ROT_QK || ROT_V) {
+        float sn, cs;
+        sincosf(rt[it], &sn, &cs);
+        if (ROT_QK) rotate_pair(k0, k1, cs, sn);
+        if (ROT_V) rotate_pair(v0, v1, cs, sn);
+      }
+      *reinterpret_cast<float2*>(&sk[jj][2 * p]) = make_float2(k0, k1);
+      *reinterpret_cast<float2*>(&sv[jj][2 * p]) = make_float2(v0, v1);
+    }
+  };
+
+  const int i_last = min(L - 1, blockIdx.x * F32_Q + F32_Q - 1);
+  fetch(0);
+  for (int j0 = 0; j0 <= i_last; j0 += F32_K) {
+    __syncthreads();  // every lane is done with the previous tile
+    commit();
     __syncthreads();
+    if (j0 + F32_K <= i_last) fetch(j0 + F32_K);
     const int jn = min(F32_K, i + 1 - j0);  // keys j <= i in this tile
     for (int jj = sp; jj < jn; jj += F32_S) {
       float s4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -150,15 +179,16 @@ __global__ __launch_bounds__(F32_T) void attn_f32_kernel(
   }
 }
 
-template <int D>
+template <int D, int S>
 hipError_t launch_f32_d(const Geometry& g, const float* q, const float* k, const float* v,
                         const float* theta, const float* alibi, float* o, float* lse,
                         hipStream_t stream) {
-  dim3 grid((g.L + F32_Q - 1) / F32_Q, g.B * g.H);
+  constexpr int QPB = F32_T / S;
+  dim3 grid((g.L + QPB - 1) / QPB, g.B * g.H);
   const float qscale = g.scale * LOG2E;
   const bool rqk = g.flags & ARP_ROTATE_QK, rv = g.flags & ARP_ROTATE_V, al = g.flags & ARP_ALIBI;
 #define ARP_F32_LAUNCH(A, B, C)                                                                \
-  hipLaunchKernelGGL((attn_f32_kernel<D, A, B, C>), grid, dim3(F32_T), 0, stream, q, k, v,    \
+  hipLaunchKernelGGL((attn_f32_kernel<D, S, A, B, C>), grid, dim3(F32_T), 0, stream, q, k, v, \
                      theta, alibi, o, lse, g.L, g.H, g.Hphi, qscale, g.hscale)
   if (rqk) {
     if (rv) {
@@ -182,8 +212,13 @@ hipError_t launch_f32_d(const Geometry& g, const float* q, const float* k, const
 hipError_t launch_attn_f32(const Geometry& g, const float* q, const float* k, const float* v,
                            const float* theta, const float* alibi, float* o, float* lse,
                            hipStream_t stream) {
-  if (g.D == 64) return launch_f32_d<64>(g, q, k, v, theta, alibi, o, lse, stream);
-  return launch_f32_d<128>(g, q, k, v, theta, alibi, o, lse, stream);
+  const long wg64 = (long)g.B * g.H * ((g.L + 63) / 64);
+  if (wg64 < device_cus()) {
+    if (g.D == 64) return launch_f32_d<64, 32>(g, q, k, v, theta, alibi, o, lse, stream);
+    return launch_f32_d<128, 32>(g, q, k, v, theta, alibi, o, lse, stream);
+  }
+  if (g.D == 64) return launch_f32_d<64, 4>(g, q, k, v, theta, alibi, o, lse, stream);
+  return launch_f32_d<128, 4>(g, q, k, v, theta, alibi, o, lse, stream);
 }
 
 }  // namespace arp

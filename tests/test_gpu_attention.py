@@ -60,12 +60,26 @@ def test_small_all_flags(name, L, flags):
 
 @pytest.mark.parametrize("L", [1, 2, 3, 33, 65, 130])
 def test_fp32_ragged_lengths(L):
-    """fp32 I/O at lengths that leave some of a query's four key lanes
+    """fp32 I/O at lengths that leave some of a query's key lanes
     without keys (query 0 has one key) and tiles part-filled."""
     w = wl.make("tiny_f32", batch=1, heads=2, seqlen=L)
     flags = dict(rotate_qk=True, rotate_v=True, alibi=True)
     got, _ = run_forward(w, **flags)
     assert_close(got, oracle_problem(w, **flags).output(), "f32", f"fp32 L={L}")
+
+
+@pytest.mark.parametrize("heads,L", [(8, 1100), (2, 1100)])
+def test_fp32_lane_splits(heads, L):
+    """The fp32 kernel splits each query's keys over 4 lanes on grids of at
+    least one 64-query workgroup per compute unit (2 x 8 heads x 18 tiles =
+    288 here) and over 32 lanes below that (2 x 2 x 18 = 72): both against the
+    oracle, ragged length, every flag that changes the kernel."""
+    w = wl.make("tiny_f32", batch=2, heads=heads, seqlen=L)
+    flags = dict(rotate_qk=True, rotate_v=True, alibi=True)
+    got, _ = run_forward(w, **flags)
+    rows = sample_rows(w, per_head=24)
+    want = oracle_problem(w, **flags).rows(rows)
+    assert_close(got.reshape(-1, w.head_dim)[rows], want, "f32", f"fp32 lane split H={heads} L={L}")
 
 
 @pytest.mark.parametrize("flags", FLAG_SETS[:3], ids=[_ids(f) for f in FLAG_SETS[:3]])
