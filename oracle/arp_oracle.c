@@ -180,10 +180,15 @@ void oracle_random_phi(int64_t batch, int64_t phi_heads, int64_t seqlen, int64_t
 
 /* x - 2 pi k with k chosen so the result lies in [-pi, pi). */
 double oracle_wrap(double x) {
+  /* fmod's remainder is exact, and the one correction step is exact too (a
+   * difference of two doubles within a factor of two of each other), so the
+   * result is x - k 2pi with no rounding at all, in [-pi, pi) for every
+   * finite x.  (A quotient-and-multiply reduction rounds twice and leaves the
+   * range once |x| passes ~2^53.) */
   const double two_pi = 2.0 * ORACLE_PI;
-  double r = x - two_pi * floor((x + ORACLE_PI) / two_pi);
-  if (r < -ORACLE_PI) r += two_pi;
+  double r = fmod(x, two_pi);
   if (r >= ORACLE_PI) r -= two_pi;
+  else if (r < -ORACLE_PI) r += two_pi;
   return r;
 }
 

@@ -157,6 +157,23 @@ def test_wrap_range_and_congruence():
     assert w[4] == pytest.approx(math.pi / 2, abs=1e-15)
 
 
+def test_wrap_is_exact_and_in_range_at_any_magnitude():
+    """wrap(x) = x - k * two_pi exactly (two_pi the double nearest 2 pi, k an
+    integer), checked in exact rational arithmetic, and inside [-pi, pi) up to
+    the largest doubles."""
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    xs = np.concatenate([rng.uniform(-1e6, 1e6, 200), rng.standard_normal(50) * 10.0 ** 12,
+                         [1e30, -1e30, 1.7e308, -1.7e308, 2.0 ** 60 + 3.0, -(2.0 ** 53) - 2.0,
+                          math.nextafter(math.pi, 0), -math.pi, 5e-324]])
+    w = oracle.wrap(xs)
+    assert np.all(w >= -math.pi) and np.all(w < math.pi)
+    two_pi = Fraction(2.0 * math.pi)
+    for x, r in zip(xs, w):
+        k = (Fraction(float(x)) - Fraction(float(r))) / two_pi
+        assert k.denominator == 1, (x, r)
+
+
 # ---------------------------------------------------------------------------
 # Attention: brute-force route products, textbook reductions, closed forms
 # ---------------------------------------------------------------------------
