@@ -67,47 +67,53 @@ def lib() -> ctypes.CDLL:
     global _LIB
     with _LOCK:
         if _LIB is None:
-            if not os.path.exists(LIB_PATH):
-                raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                                   "`python -c 'import __graft_entry__ as g; g.build()'`")
-            L = ctypes.CDLL(LIB_PATH)
-            P, S, D = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Desc)
-            U64 = ctypes.c_uint64
-            sig = {
-                "arp_abi_version": ([], ctypes.c_int),
-                "arp_status_string": ([ctypes.c_int], ctypes.c_char_p),
-                "arp_check": ([D], ctypes.c_int),
-                "arp_scan_state_bytes": ([D], S),
-                "arp_workspace_bytes": ([D], S),
-                "arp_angle_scan": ([D, P, P, P, S, P], ctypes.c_int),
-                "arp_rotate_kv": ([D, P, P, P, P, S, P], ctypes.c_int),
-                "arp_attn_rotated": ([D, P, P, P, P, P, P, S, P], ctypes.c_int),
-                "arp_attn_fwd": ([D, P, P, P, P, P, P, P, S, P], ctypes.c_int),
-                "arp_forward": ([D, P, P, P, P, P, P, P, P, S, P, S, P], ctypes.c_int),
-                "arp_rotate": ([D, P, P, P, ctypes.c_int, P], ctypes.c_int),
-                "arp_forward_train": ([D, P, P, P, P, P, P, P, P, P, S, P, S, P], ctypes.c_int),
-                "arp_backward_workspace_bytes": ([D], S),
-                "arp_backward": ([D] + [P] * 14 + [S, P], ctypes.c_int),
-                "arp_backward_ex": ([D] + [P] * 16 + [S, P], ctypes.c_int),
-                "arp_decode_prefill_ex": ([D, ctypes.c_int32] + [P] * 10 + [P], ctypes.c_int),
-                "arp_decode_step_ex": ([D, ctypes.c_int32] + [P] * 14 + [S, P], ctypes.c_int),
-                "arp_decode_workspace_bytes": ([D], S),
-                "arp_decode_prefill": ([D, ctypes.c_int32] + [P] * 7 + [P], ctypes.c_int),
-                "arp_decode_step": ([D, ctypes.c_int32] + [P] * 11 + [S, P], ctypes.c_int),
-                "arp_forward_ex": ([D] + [P] * 10 + [S, P, S, P], ctypes.c_int),
-                "arp_angle_scan_random": ([D, U64, U64, P, P, P, S, P], ctypes.c_int),
-                "arp_angle_scan_tokens": ([D, P, P, ctypes.c_int64, P, P, S, P], ctypes.c_int),
-                "arp_angle_scan_const": ([D, P, P, P], ctypes.c_int),
-                "arp_random_phi": ([D, U64, U64, P, P, P], ctypes.c_int),
-                "arp_adascale_lambda": ([ctypes.c_int32, P, P, ctypes.c_int64, ctypes.c_int64, P],
-                                        ctypes.c_int),
-                "arp_forward_noalloc": ([D, P, P, P, P, P, P, P, P], ctypes.c_int),
-            }
-            for name, (args, res) in sig.items():
-                f = getattr(L, name)
-                f.argtypes, f.restype = args, res
-            _LIB = L
+            _LIB = open_library(LIB_PATH)
     return _LIB
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Load a build of the library at path with every entry point's prototype
+    (lib() uses it for libarp.so; tests use it for the scan test variant)."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(path)
+    P, S, D = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Desc)
+    U64 = ctypes.c_uint64
+    sig = {
+        "arp_abi_version": ([], ctypes.c_int),
+        "arp_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "arp_check": ([D], ctypes.c_int),
+        "arp_scan_state_bytes": ([D], S),
+        "arp_workspace_bytes": ([D], S),
+        "arp_angle_scan": ([D, P, P, P, S, P], ctypes.c_int),
+        "arp_rotate_kv": ([D, P, P, P, P, S, P], ctypes.c_int),
+        "arp_attn_rotated": ([D, P, P, P, P, P, P, S, P], ctypes.c_int),
+        "arp_attn_fwd": ([D, P, P, P, P, P, P, P, S, P], ctypes.c_int),
+        "arp_forward": ([D, P, P, P, P, P, P, P, P, S, P, S, P], ctypes.c_int),
+        "arp_rotate": ([D, P, P, P, ctypes.c_int, P], ctypes.c_int),
+        "arp_forward_train": ([D, P, P, P, P, P, P, P, P, P, S, P, S, P], ctypes.c_int),
+        "arp_backward_workspace_bytes": ([D], S),
+        "arp_backward": ([D] + [P] * 14 + [S, P], ctypes.c_int),
+        "arp_backward_ex": ([D] + [P] * 16 + [S, P], ctypes.c_int),
+        "arp_decode_prefill_ex": ([D, ctypes.c_int32] + [P] * 10 + [P], ctypes.c_int),
+        "arp_decode_step_ex": ([D, ctypes.c_int32] + [P] * 14 + [S, P], ctypes.c_int),
+        "arp_decode_workspace_bytes": ([D], S),
+        "arp_decode_prefill": ([D, ctypes.c_int32] + [P] * 7 + [P], ctypes.c_int),
+        "arp_decode_step": ([D, ctypes.c_int32] + [P] * 11 + [S, P], ctypes.c_int),
+        "arp_forward_ex": ([D] + [P] * 10 + [S, P, S, P], ctypes.c_int),
+        "arp_angle_scan_random": ([D, U64, U64, P, P, P, S, P], ctypes.c_int),
+        "arp_angle_scan_tokens": ([D, P, P, ctypes.c_int64, P, P, S, P], ctypes.c_int),
+        "arp_angle_scan_const": ([D, P, P, P], ctypes.c_int),
+        "arp_random_phi": ([D, U64, U64, P, P, P], ctypes.c_int),
+        "arp_adascale_lambda": ([ctypes.c_int32, P, P, ctypes.c_int64, ctypes.c_int64, P],
+                                ctypes.c_int),
+        "arp_forward_noalloc": ([D, P, P, P, P, P, P, P, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes, f.restype = args, res
+    return L
 
 
 def _check(fn: str, status: int) -> None:

@@ -61,7 +61,16 @@ namespace arp {
 namespace {
 
 constexpr int SCAN_THREADS = 256;
-constexpr int FALLBACK_POLLS = 256;  // polls of an unpublished word before reducing it here
+// Polls of an unpublished word before its chunk is reduced from the source
+// here.  A build with ARP_SCAN_FALLBACK_POLLS=0 is a test variant: it ignores
+// every published word and reduces each predecessor chunk from the source, so
+// that the fallback path (reduce_pair and its lane combine) produces every
+// prefix; its angles must equal the normal build's bit for bit.
+#ifndef ARP_SCAN_FALLBACK_POLLS
+#define ARP_SCAN_FALLBACK_POLLS 256
+#endif
+constexpr int FALLBACK_POLLS = ARP_SCAN_FALLBACK_POLLS;
+constexpr bool FROM_SOURCE = FALLBACK_POLLS == 0;
 constexpr int GROUP = 16;            // workgroups per completion counter
 constexpr uint64_t ST_AGG = 1, ST_INC = 2, ST_MASK = 3;
 
@@ -270,11 +279,12 @@ __device__ uint64_t look_back(const uint64_t* __restrict__ wh, size_t wbase, uin
     for (int i = W - 1; i >= 0; --i)
       if ((wv[i] & ST_MASK) != ST_AGG) stop = k0 + K * i;
     if (K == 2) stop = min(stop, __shfl_xor(stop, 32));
+    if (FROM_SOURCE) stop = 0;
     uint64_t part = 0;
 #pragma unroll
     for (int i = 0; i < W; ++i)
       if (k0 + K * i < stop) part += wv[i] >> 16;
-    if (stop < SPAN && (stop % K) == k0) {
+    if (!FROM_SOURCE && stop < SPAN && (stop % K) == k0) {
       const uint64_t w = wv[stop / K];
       if ((w & ST_MASK) == ST_INC) part += (w >> 16) | (1ull << 62);  // mark: found final prefix
     }
