@@ -64,6 +64,9 @@ constexpr float TAU = 8.0f;   // lazy-rescale threshold (base-2 logits)
 // probabilities 2^(s - m) < 2^-160, below fp32's smallest subnormal (2^-149):
 // every one of them is exactly zero, so skipping the tile changes no bit.
 constexpr float ZGAP = 160.0f;
+// Adjacent query tiles of one head that a biased launch places on one XCD at
+// the same time (they share key/value tiles in its L2).
+constexpr int SPREAD_GROUP = 8;
 
 // qr is the raw q ([B, H, L, D]), rotated and scaled in the prologue.
 // FUSED = false: k~ (L padded to Lp) comes pre-rotated from the rotation pass,
@@ -123,13 +126,27 @@ __device__ __forceinline__ void attn_tile(
 
   // ---- which tile (the logical order is set by the kernel below) ----
   constexpr bool SPREAD = (BIAS != 0) && !FUSED;
-  if (logical >= total_tiles) return;
   const int nbh = total_tiles / nqt;
-  // spread: round r deals query tile nqt-1-r of every head, rotated by r so
-  // that a head does not stay on one XCD (blockIdx % 8) from round to round
-  const int rnd = logical / nbh;
-  const int bh = SPREAD ? (logical % nbh + rnd) % nbh : logical / nqt;
-  const int qt = nqt - 1 - (SPREAD ? rnd : logical % nqt);
+  int bh, qt;
+  if constexpr (SPREAD) {
+    // Spread: groups of SPREAD_GROUP adjacent query tiles of one head, dealt
+    // round-robin over the XCDs (blockIdx % 8) in dispatch order, so that a
+    // group's workgroups run at the same time on one XCD and share the key
+    // and value tiles of their overlapping walks in its L2, while the heads
+    // (whose walks stop at different depths) are spread over the XCDs.  Round
+    // r deals the r-th group from the end of every head, rotated by r so that
+    // a head does not stay on one XCD from round to round.
+    const int x = logical % 8, m = logical / 8;
+    const int gi = (m / SPREAD_GROUP) * 8 + x;
+    const int rnd = gi / nbh;
+    bh = (gi % nbh + rnd) % nbh;
+    qt = nqt - 1 - (rnd * SPREAD_GROUP + m % SPREAD_GROUP);
+    if (qt < 0) return;
+  } else {
+    if (logical >= total_tiles) return;
+    bh = logical / nqt;
+    qt = nqt - 1 - logical % nqt;
+  }
   const int q0 = qt * BM;
   const int b = bh / H, h = bh % H;
 
@@ -697,7 +714,12 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
   const bool rv = g.flags & ARP_ROTATE_V;
   const int bias = ((g.flags & ARP_ALIBI) ? 1 : 0) | ((g.flags & ARP_FORGET_GATE) ? 2 : 0);
   const int paired = (QPW == 64 && NW == 8 && !FUSED && bias == 0 && total % 16 == 0) ? 1 : 0;
-  const int grid = paired ? total / 2 : ((total + 7) / 8) * 8;
+  // spread (biased, pre-rotation): every head's groups of SPREAD_GROUP query
+  // tiles, a whole number of rounds over the 8 XCDs
+  const long groups = (long)g.B * g.H * ((nqt + SPREAD_GROUP - 1) / SPREAD_GROUP);
+  const int grid = paired ? total / 2
+                   : (bias != 0 && !FUSED) ? (int)(((groups + 7) / 8) * 8 * SPREAD_GROUP)
+                                           : ((total + 7) / 8) * 8;
   const int rqk = (g.flags & ARP_ROTATE_QK) ? 1 : 0;
   const float qscale = g.scale * LOG2E;
 #define ARP_BF16_LAUNCH(A, R)                                                                  \

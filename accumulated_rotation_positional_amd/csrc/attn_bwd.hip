@@ -291,12 +291,15 @@ __device__ __forceinline__ void grad_rows(const f32x16 (&acc)[DB], float mul, co
 // ---------------------------------------------------------------------------
 // 2. dK, dV (key-stationary)
 // ---------------------------------------------------------------------------
+// The dK/dV of one block of BK = 32 NW keys (kt) of head bh, walking the
+// query tiles from the last one down (ascending = false) or from the block's
+// diagonal up (ascending = true).
 template <int D, int NW, bool ALIBI, bool GATE>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
-    BwdOperands ops, const float* __restrict__ theta, const float* __restrict__ alibi,
-    uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, float* __restrict__ dtheta, int L, int Lp, int H, int Hphi, int nkt,
-    int total_tiles, uint32_t flags) {
+__device__ __forceinline__ void dkdv_block(
+    uint8_t* smem, const BwdOperands& ops, const float* __restrict__ theta,
+    const float* __restrict__ alibi, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    float* __restrict__ dtheta, int L, int Lp, int H, int Hphi, uint32_t flags, int kt, int bh,
+    bool ascending) {
   constexpr int BK = 32 * NW;  // keys per workgroup
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int ROWB = D * 2, RT = TILE * ROWB;     // row tile bytes
@@ -304,21 +307,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
   // + with gates the query tile's fp64 gate base (padded to keep stages on
   // 256-byte boundaries, the LDS bank period)
   constexpr int STAGE = 2 * RT + 2 * CT + 2 * TILE * 4 + (GATE ? 256 : 0);
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
-
-  // Unbiased: each XCD (blockIdx % 8) gets whole heads, so their key
-  // workgroups share the streamed query tiles in its L2.  With a distance
-  // bias the work per head differs widely (a steep slope leaves most query
-  // tiles out), so the key blocks are dealt out across the XCDs instead: key
-  // block kt of every head, then kt + 1, ..., the heads rotated by kt so
-  // that a head does not stay on one XCD (blockIdx % 8) from round to round.
-  // Either way the longest query ranges (small kt) start first.
-  const int per = (total_tiles + 7) / 8;
-  const int logical = ALIBI ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-  if (logical >= total_tiles) return;
-  const int nbh = total_tiles / nkt;
-  const int kt = ALIBI ? logical / nbh : logical % nkt;
-  const int bh = ALIBI ? (logical % nbh + kt) % nbh : logical / nkt;
   const int K0 = kt * BK;
   const int b = bh / H, h = bh % H;
   const int g = (Hphi == 1) ? 0 : h;
@@ -397,12 +385,15 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
       }
     }
   }
-  if (first_tile <= t_hi) issue(t_hi, smem);
-  for (int t = t_hi; t >= first_tile; --t) {
-    uint8_t* st = smem + ((t_hi - t) & 1) * STAGE;
+  const int nsteps = t_hi - first_tile + 1;
+  auto tile_of = [&](int n) { return ascending ? first_tile + n : t_hi - n; };
+  if (nsteps > 0) issue(tile_of(0), smem);
+  for (int n = 0; n < nsteps; ++n) {
+    const int t = tile_of(n);
+    uint8_t* st = smem + (n & 1) * STAGE;
     wait_loads<0>();
     __builtin_amdgcn_s_barrier();
-    if (t - 1 >= first_tile) issue(t - 1, smem + ((t_hi - t + 1) & 1) * STAGE);
+    if (n + 1 < nsteps) issue(tile_of(n + 1), smem + ((n + 1) & 1) * STAGE);
     const uint8_t* tq = st;
     const uint8_t* tdo = st + RT;
     const uint8_t* tqT = st + 2 * RT;
@@ -495,6 +486,53 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
                 dk + row, dth, hf);
   grad_rows<DB>(dvt, 1.f, ops.v + rm + (size_t)j * D, 1.f, th, (flags & ARP_ROTATE_V) != 0,
                 dv + row, dth, hf);
+}
+
+template <int D, int NW, bool ALIBI, bool GATE>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
+    BwdOperands ops, const float* __restrict__ theta, const float* __restrict__ alibi,
+    uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, float* __restrict__ dtheta, int L, int Lp, int H, int Hphi, int nkt,
+    int total_tiles, uint32_t flags, int paired) {
+  constexpr int ROWB = D * 2, RT = TILE * ROWB, COLB = TILE * 2, CT = D * COLB;
+  constexpr int STAGE = 2 * RT + 2 * CT + 2 * TILE * 4 + (GATE ? 256 : 0);  // as in dkdv_block
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  // Unbiased: each XCD (blockIdx % 8) gets whole heads, so their key
+  // workgroups share the streamed query tiles in its L2.  Paired (grids that
+  // still fill the chip with half the workgroups): workgroup c of a head
+  // takes key block c, walking the query tiles down from the last, then key
+  // block nkt - 1 - c, walking up from its diagonal.  Every workgroup then
+  // does the same work (nkt + 1 tiles' worth), and at any moment the
+  // workgroups of a head are on one of only two query tiles (the last tile
+  // minus the steps taken, or the steps taken minus the offset of the second
+  // block), so each tile streams through the XCD's L2 about twice instead of
+  // once per key block.  With a distance bias the work per head differs
+  // widely (a steep slope leaves most query tiles out), so the key blocks are
+  // dealt out across the XCDs instead: key block kt of every head, then
+  // kt + 1, ..., the heads rotated by kt so that a head does not stay on one
+  // XCD (blockIdx % 8) from round to round; the longest query ranges (small
+  // kt) start first.
+  const int per = (total_tiles + 7) / 8;
+  const int logical = ALIBI ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (logical >= total_tiles) return;
+  if (!ALIBI && paired) {
+    const int npk = (nkt + 1) / 2;  // workgroups per head
+    const int bh = logical / npk, c = logical % npk;
+    dkdv_block<D, NW, ALIBI, GATE>(smem, ops, theta, alibi, dk, dv, dtheta, L, Lp, H, Hphi, flags,
+                                   c, bh, false);
+    if (nkt - 1 - c != c) {
+      __syncthreads();  // every wave is done with the LDS stages before they are refilled
+      dkdv_block<D, NW, ALIBI, GATE>(smem, ops, theta, alibi, dk, dv, dtheta, L, Lp, H, Hphi,
+                                     flags, nkt - 1 - c, bh, true);
+    }
+    return;
+  }
+  const int nbh = total_tiles / nkt;
+  const int kt = ALIBI ? logical / nbh : logical % nkt;
+  const int bh = ALIBI ? (logical % nbh + kt) % nbh : logical / nkt;
+  dkdv_block<D, NW, ALIBI, GATE>(smem, ops, theta, alibi, dk, dv, dtheta, L, Lp, H, Hphi, flags, kt,
+                                 bh, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -864,11 +902,14 @@ hipError_t launch_bwd_grads(const Geometry& g, const BwdArgs& a, hipStream_t str
   const uint32_t fl = g.flags;
   {
     const int nkt = (g.L + 32 * NW - 1) / (32 * NW);
-    const int total = g.B * g.H * nkt;
+    // key blocks paired when half as many workgroups still fill every CU
+    const long pairs = (long)g.B * g.H * ((nkt + 1) / 2);
+    const int paired = (!ALIBI && pairs >= device_cus()) ? 1 : 0;
+    const int total = paired ? (int)pairs : g.B * g.H * nkt;
     const int grid = ((total + 7) / 8) * 8;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, ALIBI, GATE>), dim3(grid), dim3(NW * 64), 0, stream,
                        a.ops, a.theta, a.alibi, a.dk, a.dv, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nkt,
-                       total, fl);
+                       total, fl, paired);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
