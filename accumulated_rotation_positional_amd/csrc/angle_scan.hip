@@ -322,10 +322,22 @@ __device__ uint64_t look_back(const uint64_t* __restrict__ wh, size_t wbase, uin
   return acc;
 }
 
+// The key rotation of the fused epilogue (kr == nullptr: none): the bf16
+// k (and v) rows of the chunk's tokens for every head of the segment.
+struct RotEpilogue {
+  const uint16_t* __restrict__ k;
+  const uint16_t* __restrict__ v;
+  uint16_t* __restrict__ kr;
+  uint16_t* __restrict__ vr;
+  float* __restrict__ kmax;
+  int H, Hphi, Lp;
+  int rot_qk, rot_v;
+};
+
 template <int P, int T, int MINB, class Src>
 __global__ __launch_bounds__(SCAN_THREADS, MINB) void angle_scan_kernel(
     Src src, float* __restrict__ theta, ScanHeader* __restrict__ hdr,
-    uint64_t* __restrict__ words, int L, int nchunks, int exclusive) {
+    uint64_t* __restrict__ words, int L, int nchunks, int exclusive, RotEpilogue rot) {
   constexpr int CPT = P / 4;              // threads per token row (4 pairs each)
   constexpr int RG = SCAN_THREADS / CPT;  // row groups per chunk
   constexpr int CH = RG * T;              // tokens per chunk
@@ -335,6 +347,7 @@ __global__ __launch_bounds__(SCAN_THREADS, MINB) void angle_scan_kernel(
 
   __shared__ uint64_t s_wtot[NWAVE][P];  // per-wave totals
   __shared__ uint64_t s_carry[P];        // exclusive prefix of this chunk (+ 2^47)
+  __shared__ uint32_t s_kmax2[4];        // fused rotation: max |k~|^2 per key tile of the chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -418,6 +431,7 @@ __global__ __launch_bounds__(SCAN_THREADS, MINB) void angle_scan_kernel(
   uint64_t run[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) run[c] = pre[c] + s_carry[cq * 4 + c];
+  float ang[T][4];  // the thread's angles, for the fused key rotation
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const float xs[4] = {x[t].x, x[t].y, x[t].z, x[t].w};
@@ -432,6 +446,7 @@ __global__ __launch_bounds__(SCAN_THREADS, MINB) void angle_scan_kernel(
         run[c] += step;
         out[c] = to_radians_offset(run[c]);
       }
+      ang[t][c] = out[c];
     }
     const int tok = tbase + t;
     if (tok < L)
@@ -439,6 +454,69 @@ __global__ __launch_bounds__(SCAN_THREADS, MINB) void angle_scan_kernel(
       // it out of the caches measured 5-15% faster than a plain store.
       __builtin_nontemporal_store(f32x4{out[0], out[1], out[2], out[3]},
                                   reinterpret_cast<f32x4*>(seg_theta + (size_t)tok * P + cq * 4));
+  }
+
+  // ---- fused key rotation: the pre-rotation pass of these tokens ----
+  // Thread (row group rg, chunk cq) owns 16 bytes (4 pairs) of T consecutive
+  // rows, which lie in one 64-key tile (T divides 64); the arithmetic is the
+  // pass's (rotate.hip), operation for operation, so k~, v~ and the tile
+  // maxima are bit-identical to it: hardware sin/cos of the angle, fp32
+  // rotation rounded to bf16, |k~|^2 from the stored values summed over the
+  // row's lanes in the same butterfly order.
+  if constexpr (64 % T == 0 && CH % 64 == 0 && CH / 64 <= 4) {  // plans of whole key tiles
+   if (rot.kr != nullptr) {
+    constexpr int D = 2 * P;
+    const int nh = rot.Hphi == 1 ? rot.H : 1;
+    const int bh0 = (seg / rot.Hphi) * rot.H + (rot.Hphi == 1 ? 0 : seg % rot.Hphi);
+    const int tile = (rg * T) / 64;  // key tile of this thread's rows within the chunk
+    for (int hh = 0; hh < nh; ++hh) {
+      const int bh = bh0 + hh;
+      if (tid < 4) s_kmax2[tid] = 0u;
+      __syncthreads();
+      uint32_t n2max = 0u;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int tok = tbase + t;  // the same on the CPT lanes of a row
+        if (tok >= rot.Lp) break;
+        u32x4 ka = {0, 0, 0, 0}, va = {0, 0, 0, 0};
+        if (tok < L) {
+          const size_t off = ((size_t)bh * L + tok) * D + cq * 8;
+          ka = *reinterpret_cast<const u32x4*>(rot.k + off);
+          if (rot.rot_v) va = *reinterpret_cast<const u32x4*>(rot.v + off);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float sn, cs;
+            __sincosf(ang[t][e], &sn, &cs);
+            float k0 = lo_bf16(ka[e]), k1 = hi_bf16(ka[e]);
+            if (rot.rot_qk) rotate_pair(k0, k1, cs, sn);
+            ka[e] = pack_bf16x2(k0, k1);
+            if (rot.rot_v) {
+              float v0 = lo_bf16(va[e]), v1 = hi_bf16(va[e]);
+              rotate_pair(v0, v1, cs, sn);
+              va[e] = pack_bf16x2(v0, v1);
+            }
+          }
+        }
+        const size_t roff = ((size_t)bh * rot.Lp + tok) * D + cq * 8;
+        *reinterpret_cast<u32x4*>(rot.kr + roff) = ka;
+        if (rot.rot_v) *reinterpret_cast<u32x4*>(rot.vr + roff) = va;
+        float n2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float k0 = lo_bf16(ka[e]), k1 = hi_bf16(ka[e]);
+          n2 = fmaf(k0, k0, fmaf(k1, k1, n2));
+        }
+#pragma unroll
+        for (int m = 1; m < CPT; m <<= 1) n2 += __shfl_xor(n2, m);
+        n2max = max(n2max, __float_as_uint(n2));  // non-negative floats order as their bits
+      }
+      if (cq == 0 && n2max != 0u) atomicMax(&s_kmax2[tile], n2max);
+      __syncthreads();
+      const int t0 = chunk * CH / 64;  // the chunk's first key tile
+      if (tid < CH / 64 && t0 + tid < rot.Lp / 64)
+        rot.kmax[(size_t)bh * (rot.Lp / 64) + t0 + tid] = sqrtf(__uint_as_float(s_kmax2[tid]));
+    }
+   }
   }
 
   // ---- state upkeep: clear this block's share of the other half ----
@@ -481,7 +559,7 @@ constexpr int rows_per_group(int P) { return SCAN_THREADS / (P / 4); }
 
 }  // namespace
 
-ScanPlan scan_plan(const Geometry& g) {
+ScanPlan scan_plan(const Geometry& g, bool rotating) {
   // Rows per thread on large grids: 10, built for four workgroups per CU
   // (120 registers, no spills), so that three other workgroups stream while
   // one waits in its look-back.  Measured on 4 x 32 x 8192 x 64 (537 MB):
@@ -495,11 +573,11 @@ ScanPlan scan_plan(const Geometry& g) {
   const int rg = rows_per_group(g.P);
   auto blocks = [&](int T) { return nseg * ((g.L + (long)rg * T - 1) / ((long)rg * T)); };
   int T = 4, minb = 1;
-  if (blocks(16) > 1024) {
+  if (blocks(16) > 1024 && !rotating) {
     T = 10;
     minb = 4;
   } else if (blocks(8) >= 512) {
-    T = 8;
+    T = 8;  // (also where a rotating scan would take 10: its chunks hold whole key tiles)
   }
   ScanPlan sp;
   sp.rows_per_thread = T;
@@ -525,8 +603,8 @@ namespace {
 
 template <int P, class Src>
 hipError_t launch_scan(const Geometry& g, const Src& src, float* theta, void* scan_state,
-                       hipStream_t stream) {
-  const ScanPlan sp = scan_plan(g);
+                       hipStream_t stream, const RotEpilogue& rot = RotEpilogue{}) {
+  const ScanPlan sp = scan_plan(g, rot.kr != nullptr);
   const long nblocks = (long)g.B * g.Hphi * sp.nchunks;
   auto* hdr = reinterpret_cast<ScanHeader*>(scan_state);
   auto* words = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(scan_state) + sizeof(ScanHeader));
@@ -536,7 +614,7 @@ hipError_t launch_scan(const Geometry& g, const Src& src, float* theta, void* sc
   dim3 block(SCAN_THREADS);
 #define ARP_SCAN_LAUNCH(TT, MB)                                                               \
   hipLaunchKernelGGL((angle_scan_kernel<P, TT, MB, Src>), grid, block, 0, stream, src, theta, hdr, \
-                     words, g.L, sp.nchunks, excl)
+                     words, g.L, sp.nchunks, excl, rot)
   if (sp.rows_per_thread == 10) {
     ARP_SCAN_LAUNCH(10, 4);
   } else if (sp.rows_per_thread == 8) {
@@ -599,6 +677,21 @@ hipError_t launch_angle_scan(const Geometry& g, const float* phi, float* theta, 
                              hipStream_t stream) {
   if (g.P == 32) return launch_scan<32>(g, PhiTensor<32>{phi, g.L}, theta, scan_state, stream);
   return launch_scan<64>(g, PhiTensor<64>{phi, g.L}, theta, scan_state, stream);
+}
+
+hipError_t launch_angle_scan_rotate(const Geometry& g, const float* phi, float* theta,
+                                    void* scan_state, const KeyRotation& kr, hipStream_t stream) {
+  const ScanPlan sp = scan_plan(g, true);
+  if (sp.chunk % KEY_TILE != 0 || sp.chunk / KEY_TILE > 4 || KEY_TILE % sp.rows_per_thread != 0) {
+    const hipError_t e = launch_angle_scan(g, phi, theta, scan_state, stream);
+    if (e != hipSuccess) return e;
+    return launch_rotate_kv(g, kr.k, kr.v, theta, kr.kr, kr.vr, kr.kmax, stream);
+  }
+  const RotEpilogue rot{static_cast<const uint16_t*>(kr.k), static_cast<const uint16_t*>(kr.v),
+                        kr.kr, kr.vr, kr.kmax, g.H, g.Hphi, g.Lp,
+                        (g.flags & ARP_ROTATE_QK) ? 1 : 0, (g.flags & ARP_ROTATE_V) ? 1 : 0};
+  if (g.P == 32) return launch_scan<32>(g, PhiTensor<32>{phi, g.L}, theta, scan_state, stream, rot);
+  return launch_scan<64>(g, PhiTensor<64>{phi, g.L}, theta, scan_state, stream, rot);
 }
 
 hipError_t launch_angle_scan_random(const Geometry& g, uint64_t seed, uint64_t step,

@@ -89,6 +89,18 @@ hipError_t launch_rotation_pass(const Geometry& g, const void* k, const void* v,
                           reinterpret_cast<float*>(ws + lay.kmax_off), s);
 }
 
+// a1 and the pre-rotation pass in one launch (the bf16 pre-rotation path)
+hipError_t launch_scan_and_rotation(const Geometry& g, const float* phi, float* theta,
+                                    void* scan_state, const void* k, const void* v, char* ws,
+                                    hipStream_t s) {
+  const WorkspaceLayout lay = workspace_layout(g);
+  const KeyRotation kr{k, v, reinterpret_cast<uint16_t*>(ws + lay.k_off),
+                       (g.flags & ARP_ROTATE_V) ? reinterpret_cast<uint16_t*>(ws + lay.v_off)
+                                                : nullptr,
+                       reinterpret_cast<float*>(ws + lay.kmax_off)};
+  return launch_angle_scan_rotate(g, phi, theta, scan_state, kr, s);
+}
+
 hipError_t launch_attention(const Geometry& g, const void* q, const void* v, const float* theta,
                             const float* alibi, const float* gate2, const double* gbase, void* o,
                             float* lse, const char* ws, hipStream_t s) {
@@ -356,6 +368,13 @@ arp_status arp_forward(const arp_desc* desc, const void* q, const void* k, const
     return ARP_ERR_ALIGNMENT;
   if ((st = check_scan_state(g, scan_state, scan_state_bytes)) != ARP_OK) return st;
   if ((st = check_ws(g, workspace, workspace_bytes)) != ARP_OK) return st;
+  if (needs_operands(g)) {  // bf16 pre-rotation path: the scan rotates the keys too
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = static_cast<char*>(workspace);
+    if (launch_scan_and_rotation(g, phi, theta, scan_state, k, v, ws, s) != hipSuccess)
+      return ARP_ERR_HIP;
+    return hip_status(launch_attention(g, q, v, theta, alibi, nullptr, nullptr, o, nullptr, ws, s));
+  }
   st = arp_angle_scan(desc, phi, theta, scan_state, scan_state_bytes, stream);
   if (st != ARP_OK) return st;
   return arp_attn_fwd(desc, q, k, v, theta, alibi, o, workspace, workspace_bytes, stream);
@@ -381,16 +400,18 @@ arp_status arp_forward_train(const arp_desc* desc, const void* q, const void* k,
     return ARP_ERR_ALIGNMENT;
   if ((st = check_scan_state(g, scan_state, scan_state_bytes)) != ARP_OK) return st;
   if ((st = check_ws(g, workspace, workspace_bytes)) != ARP_OK) return st;
-  st = arp_angle_scan(desc, phi, theta, scan_state, scan_state_bytes, stream);
-  if (st != ARP_OK) return st;
-  if (f32)
+  if (f32) {
+    st = arp_angle_scan(desc, phi, theta, scan_state, scan_state_bytes, stream);
+    if (st != ARP_OK) return st;
     return hip_status(launch_attn_f32(g, static_cast<const float*>(q), static_cast<const float*>(k),
                                       static_cast<const float*>(v), theta, alibi,
                                       static_cast<float*>(o), lse, (hipStream_t)stream));
-  st = arp_rotate_kv(desc, k, v, theta, workspace, workspace_bytes, stream);
-  if (st != ARP_OK) return st;
-  return hip_status(launch_attention(g, q, v, theta, alibi, nullptr, nullptr, o, lse,
-                                     static_cast<const char*>(workspace), (hipStream_t)stream));
+  }
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  if (launch_scan_and_rotation(g, phi, theta, scan_state, k, v, ws, s) != hipSuccess)
+    return ARP_ERR_HIP;
+  return hip_status(launch_attention(g, q, v, theta, alibi, nullptr, nullptr, o, lse, ws, s));
 }
 
 arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, const void* v,
@@ -423,10 +444,8 @@ arp_status arp_forward_ex(const arp_desc* desc, const void* q, const void* k, co
   hipStream_t s = (hipStream_t)stream;
   const WorkspaceLayout lay = workspace_layout(g);
   char* ws = static_cast<char*>(workspace);
-  hipError_t e = launch_angle_scan(g, phi, theta, scan_state, s);
-  if (e != hipSuccess) return ARP_ERR_HIP;
-  e = launch_rotation_pass(g, k, v, theta, ws, s);
-  if (e != hipSuccess) return ARP_ERR_HIP;
+  if (launch_scan_and_rotation(g, phi, theta, scan_state, k, v, ws, s) != hipSuccess)
+    return ARP_ERR_HIP;
   float* gate2 = gated(g) ? reinterpret_cast<float*>(ws + lay.gate_off) : nullptr;
   double* gbase = gated(g) ? reinterpret_cast<double*>(ws + lay.gate_base_off) : nullptr;
   if (gated(g) && launch_gate_scan(g, logf, gate2, gbase,

@@ -33,7 +33,9 @@ struct ScanPlan {
   int chunk;            // tokens per workgroup
   int nchunks;          // chunks per (batch, angle head) segment
 };
-ScanPlan scan_plan(const Geometry& g);
+// rotating: the plan of the scan with the key rotation in its epilogue
+// (chunks that hold whole 64-key tiles)
+ScanPlan scan_plan(const Geometry& g, bool rotating = false);
 size_t scan_state_bytes(const Geometry& g);  // upper bound over every plan
 struct WorkspaceLayout {
   size_t k_off, v_off, operand_bytes;          // each operand block (v~ only with ARP_ROTATE_V)
@@ -65,6 +67,20 @@ hipError_t launch_angle_scan_const(const Geometry& g, const float* freq, float* 
 // The random draws written out as phi [B, Hphi, L, P].
 hipError_t launch_random_phi(const Geometry& g, uint64_t seed, uint64_t step, const float* bound,
                              float* phi, hipStream_t stream);
+// The angle scan with the pre-rotation pass in its epilogue: each scan
+// thread rotates the k (and v) rows of the angles it has just produced, so
+// the angles are not read back and one launch is saved.  Same outputs, bit
+// for bit, as launch_angle_scan then launch_rotate_kv (which it falls back to
+// when the scan's chunks do not cover whole 64-key tiles).
+struct KeyRotation {
+  const void* k;
+  const void* v;   // read with ARP_ROTATE_V only
+  uint16_t* kr;    // k~ [B*H, Lp, D] (rows past L written as zeros)
+  uint16_t* vr;    // v~ [B*H, Lp, D] with ARP_ROTATE_V, else NULL
+  float* kmax;     // [B*H, Lp/64]: the largest |k~| of each 64-key tile
+};
+hipError_t launch_angle_scan_rotate(const Geometry& g, const float* phi, float* theta,
+                                    void* scan_state, const KeyRotation& rot, hipStream_t stream);
 // k~ (and v~ with ARP_ROTATE_V) into the workspace, with the key-norm maxima
 hipError_t launch_rotate_kv(const Geometry& g, const void* k, const void* v, const float* theta,
                             uint16_t* kr, uint16_t* vr, float* kmax, hipStream_t stream);
