@@ -37,7 +37,7 @@ ABI_VERSION = 2
 # Every function the header declares (tests check the library exports them all).
 EXPORTS = ("arp_abi_version", "arp_status_string", "arp_check", "arp_scan_state_bytes",
            "arp_workspace_bytes",
-           "arp_angle_scan", "arp_rotate_kv", "arp_attn_rotated", "arp_attn_fwd",
+           "arp_angle_scan", "arp_rotate_kv", "arp_angle_scan_rotate_kv", "arp_attn_rotated", "arp_attn_fwd",
            "arp_forward", "arp_rotate", "arp_forward_train", "arp_backward_workspace_bytes",
            "arp_backward", "arp_decode_workspace_bytes", "arp_decode_prefill", "arp_decode_step",
            "arp_forward_ex", "arp_angle_scan_random", "arp_angle_scan_tokens",
@@ -88,6 +88,7 @@ def open_library(path: str) -> ctypes.CDLL:
         "arp_workspace_bytes": ([D], S),
         "arp_angle_scan": ([D, P, P, P, S, P], ctypes.c_int),
         "arp_rotate_kv": ([D, P, P, P, P, S, P], ctypes.c_int),
+        "arp_angle_scan_rotate_kv": ([D, P, P, P, P, P, S, P, S, P], ctypes.c_int),
         "arp_attn_rotated": ([D, P, P, P, P, P, P, S, P], ctypes.c_int),
         "arp_attn_fwd": ([D, P, P, P, P, P, P, P, S, P], ctypes.c_int),
         "arp_forward": ([D, P, P, P, P, P, P, P, P, S, P, S, P], ctypes.c_int),
@@ -389,6 +390,25 @@ def rotate_kv(k, v, theta, desc: Desc, ws: torch.Tensor | None = None) -> torch.
     _check("arp_rotate_kv", lib().arp_rotate_kv(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(theta),
                                                 _ptr(ws), _nbytes(ws), _stream(k.device)))
     return ws
+
+
+def angle_scan_rotate_kv(phi, k, v, desc: Desc, theta: torch.Tensor | None = None,
+                         state: torch.Tensor | None = None,
+                         ws: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """The angle scan with the key (and value) pre-rotation in its epilogue:
+    returns (theta, ws) as angle_scan then rotate_kv would leave them."""
+    _check_qkv(desc, k=k, v=v)
+    _check_angles(desc, phi=phi, theta=theta)
+    _check_buffer(state, "state", scan_state_bytes(desc))
+    _check_buffer(ws, "ws", workspace_bytes(desc))
+    _require_gpu(phi, k, v, theta, state, ws)
+    theta = torch.empty_like(phi) if theta is None else theta
+    state = scan_state(desc, phi.device) if state is None else state
+    ws = workspace(desc, phi.device) if ws is None else ws
+    _check("arp_angle_scan_rotate_kv", lib().arp_angle_scan_rotate_kv(
+        ctypes.byref(desc), _ptr(phi), _ptr(k), _ptr(v), _ptr(theta), _ptr(state), _nbytes(state),
+        _ptr(ws), _nbytes(ws), _stream(phi.device)))
+    return theta, ws
 
 
 def attn_rotated(q, v, theta, alibi, out, desc: Desc, ws: torch.Tensor) -> torch.Tensor:

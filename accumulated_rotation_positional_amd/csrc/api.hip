@@ -304,6 +304,26 @@ arp_status arp_rotate_kv(const arp_desc* desc, const void* k, const void* v, con
                                          (hipStream_t)stream));
 }
 
+arp_status arp_angle_scan_rotate_kv(const arp_desc* desc, const float* phi, const void* k,
+                                    const void* v, float* theta, void* scan_state,
+                                    size_t scan_state_bytes, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  Geometry g;
+  arp_status st = make_geometry(desc, &g);
+  if (st != ARP_OK) return st;
+  if (gated(g)) return ARP_ERR_INVALID_ARG;  // the gate input: arp_forward_ex
+  if (!needs_operands(g)) return ARP_ERR_UNSUPPORTED;
+  const bool rv = (g.flags & ARP_ROTATE_V) != 0;
+  if (phi == nullptr || theta == nullptr || k == nullptr || (rv && v == nullptr))
+    return ARP_ERR_INVALID_ARG;
+  if (!aligned16(phi) || !aligned16(theta) || !aligned16(k) || (v && !aligned16(v)))
+    return ARP_ERR_ALIGNMENT;
+  if ((st = check_scan_state(g, scan_state, scan_state_bytes)) != ARP_OK) return st;
+  if ((st = check_ws(g, workspace, workspace_bytes)) != ARP_OK) return st;
+  return hip_status(launch_scan_and_rotation(g, phi, theta, scan_state, k, v,
+                                             static_cast<char*>(workspace), (hipStream_t)stream));
+}
+
 arp_status arp_attn_rotated(const arp_desc* desc, const void* q, const void* v, const float* theta,
                             const float* alibi, void* o, void* workspace, size_t workspace_bytes,
                             void* stream) {

@@ -36,7 +36,7 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense)
 HBM_PEAK_GBS = 8000.0
 METRIC = "accum-rotation causal attention fwd TFLOP/s + tokens/s at L=16K, d=64"
 CSRC = os.path.join(ROOT, "accumulated_rotation_positional_amd", "csrc")
-ATTN_SOURCES = ("attn_bf16.hip", "arp_device.hpp")
+ATTN_SOURCES = ("attn_bf16.hip", "arp_device.hpp", "mfma_tile.hpp")
 SCAN_SOURCES = ("angle_scan.hip",)
 COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_extrap_16k_hbm_counters.json")
 
@@ -440,11 +440,14 @@ def decode_leg(binding, torch, dev, steps: int = 50) -> dict:
 
 
 def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int = 20) -> dict:
-    """The forward step (scan, rotation pass, attention; fp32 I/O: scan and the
-    fp32 kernel) on every other workload, each at its full shape with seeded
-    inputs: step time, per-kernel event times on the stream, rates on the
-    algorithmic attention flops.  Secondary figures next to the headline
-    workload's."""
+    """The forward on every other workload, each at its full shape with seeded
+    inputs.  ms_per_step: the whole forward through arp_forward (the scan with
+    the key rotation fused in, then attention; fp32 I/O: scan and the fp32
+    kernel), device time with the launches queued ahead; the same step
+    launched kernel by kernel from Python (ms_per_step_host_launched, host
+    bound on small grids) gives per-kernel event times on the stream; rates
+    on the algorithmic attention flops.  Secondary figures next to the
+    headline workload's."""
     from accumulated_rotation_positional_amd import workloads as wl
     out = {}
     for name in wl.SPECS:
@@ -497,8 +500,28 @@ def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int =
             step(events[i])
         end.record(stream)
         torch.cuda.synchronize()
-        ms_step = start.elapsed_time(end) / steps
+        ms_host = start.elapsed_time(end) / steps
         seg = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(n_ev)] for e in events])
+
+        # The whole forward through its one entry point (arp_forward: the angle
+        # scan with the key rotation fused in, then attention), one call per
+        # step back to back with no events in between: on small grids the
+        # kernel-by-kernel launches above are bound by the host, this one by
+        # the device as long as a call's host time is below its device time.
+        def forward():
+            binding.forward(q, k, v, phi, rotate_v=w.rotate_v, alibi=alibi, out=o, theta=theta,
+                            state=state, ws=ws)
+
+        for _ in range(warmup):
+            forward()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        f0.record(stream)
+        for _ in range(steps):
+            forward()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        ms_step = f0.elapsed_time(f1) / steps
         attn_ms = float(seg[:, -1].mean())
         scan_ms = float(seg[:, 0].mean())
         scan_gbs = 8.0 * w.batch * w.phi_heads * w.seqlen * (w.head_dim // 2) / (scan_ms * 1e-3) / 1e9
@@ -506,6 +529,7 @@ def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int =
         out[name] = {
             "shape": [w.batch, w.heads, w.seqlen, w.head_dim], "dtype": w.dtype,
             "rotate_v": w.rotate_v, "alibi": w.use_alibi, "ms_per_step": round(ms_step, 4),
+            "ms_per_step_host_launched": round(ms_host, 4),
             "kernels_ms": {"angle_scan": round(scan_ms, 5),
                            "rotate_kv": round(float(seg[:, 1].mean()), 5) if n_ev == 3 else 0.0,
                            "attn_fwd": round(attn_ms, 5)},
@@ -560,23 +584,27 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     fused = args.fused or w.dtype == "f32"
-    n_ev = 3 if not fused else 2
+    n_ev = 2
 
+    # One step = two launches through the step entry points: the angle scan
+    # with the key/value pre-rotation in its epilogue (arp_angle_scan_rotate_kv),
+    # then attention with the query rotation in its prologue (arp_attn_rotated);
+    # fp32 I/O or --fused: the scan, then attention rotating while it stages.
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
-        binding.angle_scan(phi, desc, theta=theta, state=state)
+        if fused:
+            binding.angle_scan(phi, desc, theta=theta, state=state)
+        else:
+            binding.angle_scan_rotate_kv(phi, k, v, desc, theta=theta, state=state, ws=ws)
         if evs is not None:
             evs[1].record(stream)
         if fused:
             binding.attn_fwd(q, k, v, theta, desc, alibi=alibi, out=o, ws=ws)
         else:
-            binding.rotate_kv(k, v, theta, desc, ws=ws)
-            if evs is not None:
-                evs[2].record(stream)
             binding.attn_rotated(q, v, theta, alibi, o, desc, ws)
         if evs is not None:
-            evs[n_ev].record(stream)
+            evs[2].record(stream)
 
     # Clock warm-up: an idle GPU starts below the clock it holds under a long
     # matrix-core load (the attention kernel reads ~15% slower over the first
@@ -619,13 +647,18 @@ def main():
     seg = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(n_ev)] for e in events])
     scan_ms = float(seg[:, 0].mean())
     attn_ms = float(seg[:, -1].mean())
-    rot_ms = float(seg[:, 1].mean()) if n_ev == 3 else 0.0
 
     flops = w.flops
     tflops = flops / (ms_step * 1e-3) / 1e12
     tokens = w.batch * w.seqlen / (ms_step * 1e-3)
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    # algorithmic bytes of the first launch: phi read and theta written (4 + 4
+    # bytes per token and pair of each angle stream); fused with the key
+    # rotation also k read and k~ written (2 + 2 bytes per element), and v /
+    # v~ likewise with value transport
     scan_bytes = 8.0 * w.batch * w.phi_heads * w.seqlen * (w.head_dim // 2)
+    if not fused:
+        scan_bytes += 4.0 * w.batch * w.heads * w.seqlen * w.head_dim * (2 if w.rotate_v else 1)
     scan_gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
     traffic, scan_traffic = measured_traffic(w.name)
     if fused:
@@ -651,14 +684,15 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seqlen,
                    "head_dim": w.head_dim, "rotate_v": w.rotate_v, "alibi": w.use_alibi,
                    "rotation": "fused-in-staging" if fused else "pre-rotation pass"},
-        "kernels_ms": {"angle_scan": round(scan_ms, 5), "rotate_kv": round(rot_ms, 5),
+        "kernels_ms": {("angle_scan" if fused else "angle_scan_rotate_kv"): round(scan_ms, 5),
                        "attn_fwd": round(attn_ms, 5)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
-        "scan_roofline": {"bound": "hbm", "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS,
+        "scan_roofline": {"kernel": "angle_scan" if fused else "angle_scan_rotate_kv",
+                          "bound": "hbm", "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
-                          "traffic": scan_traffic},
+                          "bytes_per_launch": scan_bytes, "traffic": scan_traffic},
     }
     result["scan_hbm_gate"] = scan_gate(binding, torch, dev)
     result["angle_generators"] = generator_leg(binding, torch, dev)

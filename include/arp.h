@@ -209,6 +209,20 @@ arp_status arp_random_phi(const arp_desc* desc, uint64_t seed, uint64_t step, co
 arp_status arp_rotate_kv(const arp_desc* desc, const void* k, const void* v, const float* theta,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* a1 and a2 for keys in one launch: the angle scan (as arp_angle_scan) with
+ * the pre-rotation pass of arp_rotate_kv in its epilogue -- the threads that
+ * produce a token's angles rotate that token's k (and v) rows for every head
+ * of the angle stream, so the angles are not read back.  theta and the
+ * workspace receive exactly what arp_angle_scan then arp_rotate_kv write (bit
+ * for bit).  bf16 pre-rotation path only (ARP_ERR_UNSUPPORTED for fp32 I/O or
+ * ARP_FUSED_ROTATION); v is read (and required) only with ARP_ROTATE_V.
+ * Method: AdaRoPE Sec. 2.1 eq. (1) applied to the accumulated angles of
+ * "Why Do Accumulated Transformations Extrapolate?" eq. (7). */
+arp_status arp_angle_scan_rotate_kv(const arp_desc* desc, const float* phi, const void* k,
+                                    const void* v, float* theta, void* scan_state,
+                                    size_t scan_state_bytes, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* a2 for the queries, then a3-a6, over the keys (and transported values) that
  * arp_rotate_kv left in the workspace (bf16): q (the caller's, [batch, heads,
  * seqlen, head_dim]) rotated by R(Theta_i) and multiplied by the logit scale

@@ -423,6 +423,28 @@ def test_adascale_lambda_host_routine_matches_the_oracle():
     assert abs(out[0] - 0.6931472) < 1e-6
 
 
+def test_scan_rotate_kv_validates_on_the_host():
+    L = b.lib()
+    d = _desc(flags=b.ROTATE_QK | b.ROTATE_V)
+    by = ctypes.byref(d)
+    st, ws = L.arp_scan_state_bytes(by), L.arp_workspace_bytes(by)
+    f = L.arp_angle_scan_rotate_kv
+    assert f(by, None, A, A, A, A, st, A, ws, None) == b.ERR_INVALID_ARG      # phi
+    assert f(by, A, None, A, A, A, st, A, ws, None) == b.ERR_INVALID_ARG      # k
+    assert f(by, A, A, None, A, A, st, A, ws, None) == b.ERR_INVALID_ARG      # v (transported)
+    assert f(by, A, A, A, None, A, st, A, ws, None) == b.ERR_INVALID_ARG      # theta
+    assert f(by, M, A, A, A, A, st, A, ws, None) == b.ERR_ALIGNMENT
+    assert f(by, A, A, A, A, A + 16, st, A, ws, None) == b.ERR_ALIGNMENT      # state: 256 bytes
+    assert f(by, A, A, A, A, A, st, A, ws - 1, None) == b.ERR_WORKSPACE
+    for flags in (b.ROTATE_QK | b.FUSED_ROTATION,):
+        x = _desc(flags=flags)
+        assert f(ctypes.byref(x), A, A, A, A, A, st, A, ws, None) == b.ERR_UNSUPPORTED
+    x = _desc(dtype="f32")
+    assert f(ctypes.byref(x), A, A, A, A, A, st, A, ws, None) == b.ERR_UNSUPPORTED
+    x = _desc(flags=b.ROTATE_QK | b.FORGET_GATE)
+    assert f(ctypes.byref(x), A, A, A, A, A, st, A, ws, None) == b.ERR_INVALID_ARG
+
+
 def test_noalloc_forward_validates_before_touching_the_device():
     """arp_forward_noalloc checks its arguments and its scratch limits on the
     host (fake addresses: nothing is launched, no device is touched)."""

@@ -122,3 +122,36 @@ def test_rotation_diagnostic_matches_oracle(dtype, inverse):
     xv = wl.from_bf16_bits(x) if dtype == "bf16" else x
     np.testing.assert_allclose(np.hypot(g[..., 0::2], g[..., 1::2]),
                                np.hypot(xv[..., 0::2], xv[..., 1::2]), rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("B,H,L,d,rotv,rotqk,shared", [
+    (2, 3, 333, 64, True, True, False),
+    (1, 4, 1000, 128, False, True, False),
+    (2, 4, 5000, 64, True, True, True),
+    (1, 2, 65, 128, True, False, False),
+    (1, 3, 1, 64, True, True, False),
+    (2, 8, 16384, 64, True, True, False),
+    (2, 8, 8191, 128, False, True, True),
+])
+def test_scan_with_fused_key_rotation_equals_scan_then_pass(B, H, L, d, rotv, rotqk, shared):
+    """arp_angle_scan_rotate_kv (the pass in the scan's epilogue) leaves theta
+    and the workspace (k~, v~, per-tile key norms) bit-identical to
+    arp_angle_scan followed by arp_rotate_kv, on ragged lengths, both head
+    dims, shared angle streams, with and without value transport."""
+    G = 1 if shared else H
+    rng = np.random.default_rng(L + d)
+    phi = to_dev((rng.standard_normal((B, G, L, d // 2)) * 0.5).astype(np.float32))
+    k, v = (to_dev(wl.to_bf16_bits(rng.standard_normal((B, H, L, d)).astype(np.float32) * 0.4))
+            for _ in range(2))
+    flags = binding.flags_for(rotate_qk=rotqk, rotate_v=rotv, shared_phi=shared)
+    desc = binding.make_desc(B, H, L, d, "bf16", flags)
+    say(f"[gpu] scan+rotation B={B} H={H} L={L} d={d} rotv={rotv} rotqk={rotqk} shared={shared}")
+    nbytes = binding.workspace_bytes(desc)
+    ws_a = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    ws_b = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    th_a = binding.angle_scan(phi, desc)
+    binding.rotate_kv(k, v, th_a, desc, ws=ws_a)
+    th_b, _ = binding.angle_scan_rotate_kv(phi, k, v, desc, ws=ws_b)
+    torch.cuda.synchronize()
+    assert torch.equal(th_a.view(torch.int32), th_b.view(torch.int32))
+    assert torch.equal(ws_a, ws_b)
