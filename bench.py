@@ -39,6 +39,11 @@ CSRC = os.path.join(ROOT, "accumulated_rotation_positional_amd", "csrc")
 ATTN_SOURCES = ("attn_bf16.hip", "arp_device.hpp", "mfma_tile.hpp")
 SCAN_SOURCES = ("angle_scan.hip",)
 COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_extrap_16k_hbm_counters.json")
+FWD_COUNTERS = os.path.join(ROOT, "profiles", "forward_counters.json")
+F32_SOURCES = ("attn_f32.hip", "arp_device.hpp")
+# One wave64 vector instruction occupies a SIMD for 4 cycles (16 lanes): 256 CUs x
+# 4 SIMDs x 2.4 GHz / 4 = 6.144e11 wave instructions per second.
+VALU_PEAK_INSTS = 256 * 4 * 2.4e9 / 4
 
 
 def parse():
@@ -55,6 +60,9 @@ def parse():
     p.add_argument("--no-workloads", action="store_true",
                    help="skip the forward figures of the other workloads (profiling runs use "
                         "this so that each kernel's counters come from the headline workload)")
+    p.add_argument("--forward-only", action="store_true",
+                   help="only the timed forward steps of --workload (profiling runs of one "
+                        "workload's forward kernels)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target duration of the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -86,6 +94,25 @@ def measured_traffic(workload: str):
     scan = (c.get("scan_hbm_bytes_per_launch")
             if c.get("scan_source_hash") == source_hash(SCAN_SOURCES) else None)
     return attn, scan
+
+
+def forward_counters(key: str):
+    """An entry of the committed per-workload counter summary, or None when it is
+    missing or older than the sources of the kernel it describes."""
+    try:
+        with open(FWD_COUNTERS) as f:
+            c = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if c is None:
+        return None
+    if "attn_source_hash" in c:
+        src = ATTN_SOURCES if "attn_bf16" in c["attn_kernel"] else F32_SOURCES
+        if c["attn_source_hash"] != source_hash(src):
+            return None
+    if "source_hash" in c and c["source_hash"] != source_hash(SCAN_SOURCES):
+        return None
+    return c
 
 
 def _strided_rows(w, stride: int, offset: int = 0) -> np.ndarray:
@@ -370,6 +397,18 @@ def generator_leg(binding, torch, dev, steps: int = 30) -> dict:
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[name] = {"us_per_launch": round(ms * 1e3, 2), "achieved": round(gbs, 1),
                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    # The random variant is bound by its Philox arithmetic, not by the 4 bytes
+    # it writes per angle: its vector-ALU roofline, on the wave instructions
+    # one launch executes (SQ_INSTS_VALU from the committed counter summary)
+    # over the measured launch time, against the chip's issue rate.
+    c = forward_counters("random_generator")
+    if c is not None:
+        rate = c["valu_insts_per_launch"] / (out["random"]["us_per_launch"] * 1e-6)
+        out["random"]["alu_roofline"] = {
+            "bound": "alu", "unit": "VALU wave-instr/s", "achieved": float(f"{rate:.4g}"),
+            "peak": VALU_PEAK_INSTS, "frac": round(rate / VALU_PEAK_INSTS, 4),
+            "valu_insts_per_launch": c["valu_insts_per_launch"],
+            "valu_busy_pct_counters": c["valu_busy_pct"]}
     del flush
     return out
 
@@ -437,6 +476,19 @@ def decode_leg(binding, torch, dev, steps: int = 50) -> dict:
         del cache, gated
         torch.cuda.empty_cache()
     return out
+
+
+def _executed(name: str, attn_ms: float) -> dict:
+    """Matrix-core utilisation of the attention kernel from the flops it executes
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per launch, committed counter summary)
+    over its measured time: with a distance bias the walk skips whole tiles, so
+    this, not the dense-equivalent rate, is what the matrix cores did."""
+    c = forward_counters(name)
+    if c is None or not c.get("attn_mfma_flops_executed"):
+        return {}
+    rate = c["attn_mfma_flops_executed"] / (attn_ms * 1e-3) / 1e12
+    return {"attn_executed_mfma_flops": c["attn_mfma_flops_executed"],
+            "attn_mfma_util": round(rate / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int = 20) -> dict:
@@ -540,10 +592,12 @@ def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int =
                 "attn_frac_of_bf16_peak": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4)
                 if not fused else None}),
             "scan_gbs": round(scan_gbs, 1),
+            **_executed(name, attn_ms),
             "note": ("dense-equivalent: the algorithmic flops of every causal pair over the "
                      "kernel time, while the distance-bias walk skips key tiles whose "
-                     "probabilities are all exactly zero; the matrix-core utilisation is "
-                     "the counted flops over the time (profiles/)")
+                     "probabilities are all exactly zero; attn_mfma_util is the "
+                     "matrix-core utilisation from the flops the kernel executes "
+                     "(profiles/forward_counters.json)")
             if w.use_alibi else None,
         }
         del q, k, v, phi, alibi, ws, state, theta, o
@@ -694,9 +748,10 @@ def main():
                           "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
                           "bytes_per_launch": scan_bytes, "traffic": scan_traffic},
     }
-    result["scan_hbm_gate"] = scan_gate(binding, torch, dev)
-    result["angle_generators"] = generator_leg(binding, torch, dev)
-    if not args.fused:
+    if not args.forward_only:
+        result["scan_hbm_gate"] = scan_gate(binding, torch, dev)
+        result["angle_generators"] = generator_leg(binding, torch, dev)
+    if not args.fused and not args.forward_only:
         result["backward"] = backward_leg(binding, torch, dev, w, q, k, v, phi, alibi)
         result["decode"] = decode_leg(binding, torch, dev)
         result["forget_gate"] = forget_leg(binding, torch, dev, w, q, k, v, phi)
