@@ -259,6 +259,50 @@ __device__ __forceinline__ void attn_tile(
   // rotated and multiplied by scale * log2 e and the head's query multiplier
   // here, then rounded to bf16 ----
   const float qscale = hscale != nullptr ? qscale0 * hscale[h] : qscale0;
+  // The angles of the wave's queries are staged through LDS (the space of the
+  // tile ring, before its first load): a lane needs 16 bytes every 32 of its
+  // query's angle row, and reading them straight from global memory touches
+  // QPW rows per instruction, which the L1 cannot hold across the KS
+  // instructions.  Rows are loaded whole and coalesced (C4 16-byte chunks per
+  // row, 64 / C4 rows per instruction), their chunks XOR-swizzled so that the
+  // column reads are conflict-free.
+  constexpr int TROW = P * 4;  // bytes per angle row
+  constexpr int C4 = P / 4;
+  // Where the LDS holds them both (one workgroup's share of the CU's 160 KB),
+  // the angle rows have their own region after the ring, and the first tiles
+  // are already in flight while they are staged; otherwise they use the
+  // ring's space first.
+  constexpr int RINGB = NST * STAGE, TSTAGEB = NW * QPW * TROW;
+  constexpr bool TSEP = !FUSED && RINGB + TSTAGEB <= 163840 / MINB;
+  uint8_t* const tw = smem + (TSEP ? RINGB : 0) + wave * QPW * TROW;
+  if constexpr (TSEP) {
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t)
+      if (t <= last_tile) issue(tile_at(t), smem + t * STAGE);
+  }
+  // the raw query words first, so that their loads and the angle rows' are in
+  // flight together
+  u32x4 qraw[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[qb][ks] = *reinterpret_cast<const u32x4*>(
+          qr + ((size_t)bh * L + min(qw + 32 * qb + ln, L - 1)) * D + 16 * ks + 8 * hf);
+  if constexpr (!FUSED) {
+    if (rot_qk) {
+#pragma unroll
+      for (int r0 = 0; r0 < QPW; r0 += 64 / C4) {
+        const int row = r0 + lane / C4, c = lane % C4;
+        const float4 x = *reinterpret_cast<const float4*>(th_bh + (size_t)min(qw + row, L - 1) * P + 4 * c);
+        *reinterpret_cast<float4*>(tw + row * TROW + ((c ^ swz<TROW>(row)) << 4)) = x;
+      }
+    }
+    // a wave reads only the rows it wrote (LDS operations of a wave complete
+    // in order); a shared region also waits for every wave before the ring
+    if constexpr (TSEP) __builtin_amdgcn_wave_barrier();
+    else __syncthreads();
+  }
   bf16x8 qop[QB][KS];
   {
 #pragma unroll
@@ -266,10 +310,13 @@ __device__ __forceinline__ void attn_tile(
       const int i = min(qw + 32 * qb + ln, L - 1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(qr + ((size_t)bh * L + i) * D + 16 * ks +
-                                                        8 * hf);
-        const float4 a = rot_qk ? *reinterpret_cast<const float4*>(th_bh + (size_t)i * P + 8 * ks + 4 * hf)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
+        const u32x4 w = qraw[qb][ks];
+        const int trow = 32 * qb + ln;
+        const float4 a =
+            !rot_qk ? make_float4(0.f, 0.f, 0.f, 0.f)
+            : FUSED ? *reinterpret_cast<const float4*>(th_bh + (size_t)i * P + 8 * ks + 4 * hf)
+                    : *reinterpret_cast<const float4*>(tw + trow * TROW +
+                                                       (((2 * ks + hf) ^ swz<TROW>(trow)) << 4));
         const float ang[4] = {a.x, a.y, a.z, a.w};
         u32x4 r;
 #pragma unroll
@@ -284,6 +331,8 @@ __device__ __forceinline__ void attn_tile(
       }
     }
   }
+
+  if constexpr (!FUSED && !TSEP) __syncthreads();  // every wave has its angles before the ring is loaded
 
   // |q~_i| of this lane's queries (both half-waves hold half of each row).
   float qn[QB];
@@ -301,9 +350,11 @@ __device__ __forceinline__ void attn_tile(
   // First tiles in flight before the loop: NST-1 direct loads, or tile 0
   // staged and rotated.
   if constexpr (!FUSED) {
+    if constexpr (!TSEP) {
 #pragma unroll
-    for (int t = 0; t < NST - 1; ++t)
-      if (t <= last_tile) issue(tile_at(t), smem + t * STAGE);
+      for (int t = 0; t < NST - 1; ++t)
+        if (t <= last_tile) issue(tile_at(t), smem + t * STAGE);
+    }
   } else {
     fetch(0);
     commit(smem);
@@ -681,7 +732,12 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     float* __restrict__ lse, int L, int Lp, int vrows, int H, int Hphi, int nqt, int total_tiles,
     int rot_qk, float qscale, int paired, const float* __restrict__ hscale) {
   constexpr int STAGE = BN * D * 2 + D * BN * 2 + (((BIAS & 2) != 0) ? BN * 4 + 256 : 0);  // as in attn_tile
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
+  // the tile ring and the waves' query angle rows (after the ring, or in its
+  // space before it is loaded; as in attn_tile)
+  constexpr int RING = NST * STAGE, TSTAGE = FUSED ? 0 : NW * QPW * D * 2;
+  constexpr int LDSB = (!FUSED && RING + TSTAGE <= 163840 / MINB) ? RING + TSTAGE
+                       : (RING > TSTAGE ? RING : TSTAGE);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDSB];
   constexpr bool SPREAD = (BIAS != 0) && !FUSED;
   constexpr bool PAIRABLE = QPW == 64 && NW == 8 && BIAS == 0 && !FUSED;
   const int per = (total_tiles + 7) / 8;
