@@ -291,6 +291,22 @@ __device__ __forceinline__ void grad_rows(const f32x16 (&acc)[DB], float mul, co
 // ---------------------------------------------------------------------------
 // 2. dK, dV (key-stationary)
 // ---------------------------------------------------------------------------
+// Biased launches: groups of BWD_GROUP adjacent blocks of one head, dealt
+// round-robin over the XCDs (blockIdx % 8) in dispatch order, the heads rotated
+// from round to round (the forward's spread order): a group runs together on
+// one XCD and shares its walks' operand tiles in L2, while heads whose walks
+// stop at different depths are spread over the XCDs.  r: the block's rank from
+// the longest walk; false for a slot past the last block.
+constexpr int BWD_GROUP = 8;
+__device__ __forceinline__ bool spread_slot(int slot, int nbh, int nblk, int& bh, int& r) {
+  const int x = slot % 8, m = slot / 8;
+  const int gi = (m / BWD_GROUP) * 8 + x;
+  const int rnd = gi / nbh;
+  bh = (gi % nbh + rnd) % nbh;
+  r = rnd * BWD_GROUP + m % BWD_GROUP;
+  return r < nblk;
+}
+
 // The dK/dV of one block of BK = 32 NW keys (kt) of head bh, walking the
 // query tiles from the last one down (ascending = false) or from the block's
 // diagonal up (ascending = true).
@@ -509,14 +525,19 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
   // block), so each tile streams through the XCD's L2 about twice instead of
   // once per key block.  With a distance bias the work per head differs
   // widely (a steep slope leaves most query tiles out), so the key blocks are
-  // dealt out across the XCDs instead: key block kt of every head, then
-  // kt + 1, ..., the heads rotated by kt so that a head does not stay on one
-  // XCD (blockIdx % 8) from round to round; the longest query ranges (small
-  // kt) start first.
+  // dealt out across the XCDs in groups instead (spread_slot), the longest
+  // query ranges (small kt) first.
+  if constexpr (ALIBI) {
+    int bh, kt;
+    if (!spread_slot((int)blockIdx.x, total_tiles / nkt, nkt, bh, kt)) return;
+    dkdv_block<D, NW, ALIBI, GATE>(smem, ops, theta, alibi, dk, dv, dtheta, L, Lp, H, Hphi, flags,
+                                   kt, bh, false);
+    return;
+  }
   const int per = (total_tiles + 7) / 8;
-  const int logical = ALIBI ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  const int logical = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (logical >= total_tiles) return;
-  if (!ALIBI && paired) {
+  if (paired) {
     const int npk = (nkt + 1) / 2;  // workgroups per head
     const int bh = logical / npk, c = logical % npk;
     dkdv_block<D, NW, ALIBI, GATE>(smem, ops, theta, alibi, dk, dv, dtheta, L, Lp, H, Hphi, flags,
@@ -528,11 +549,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
     }
     return;
   }
-  const int nbh = total_tiles / nkt;
-  const int kt = ALIBI ? logical / nbh : logical % nkt;
-  const int bh = ALIBI ? (logical % nbh + kt) % nbh : logical / nkt;
-  dkdv_block<D, NW, ALIBI, GATE>(smem, ops, theta, alibi, dk, dv, dtheta, L, Lp, H, Hphi, flags, kt,
-                                 bh, false);
+  dkdv_block<D, NW, ALIBI, GATE>(smem, ops, theta, alibi, dk, dv, dtheta, L, Lp, H, Hphi, flags,
+                                 logical % nkt, logical / nkt, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -552,15 +570,20 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   // Workgroup order as in the dK/dV pass: whole heads per XCD unbiased,
-  // query blocks dealt out across the XCDs with a distance bias (heads
-  // rotated from round to round); longest first.
-  const int per = (total_tiles + 7) / 8;
-  const int logical = ALIBI ? (int)blockIdx.x : (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-  if (logical >= total_tiles) return;
-  const int nbh = total_tiles / nqt;
-  const int rnd = ALIBI ? logical / nbh : 0;
-  const int bh = ALIBI ? (logical % nbh + rnd) % nbh : logical / nqt;
-  const int qt = nqt - 1 - (ALIBI ? rnd : logical % nqt);
+  // groups of query blocks dealt out across the XCDs with a distance bias
+  // (spread_slot); longest first.
+  int bh, qt;
+  if constexpr (ALIBI) {
+    int r;
+    if (!spread_slot((int)blockIdx.x, total_tiles / nqt, nqt, bh, r)) return;
+    qt = nqt - 1 - r;
+  } else {
+    const int per = (total_tiles + 7) / 8;
+    const int logical = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (logical >= total_tiles) return;
+    bh = logical / nqt;
+    qt = nqt - 1 - logical % nqt;
+  }
   const int q0 = qt * BM;
   const int b = bh / H, h = bh % H;
   const int g = (Hphi == 1) ? 0 : h;
@@ -906,7 +929,8 @@ hipError_t launch_bwd_grads(const Geometry& g, const BwdArgs& a, hipStream_t str
     const long pairs = (long)g.B * g.H * ((nkt + 1) / 2);
     const int paired = (!ALIBI && pairs >= device_cus()) ? 1 : 0;
     const int total = paired ? (int)pairs : g.B * g.H * nkt;
-    const int grid = ((total + 7) / 8) * 8;
+    const long groups = (long)g.B * g.H * ((nkt + BWD_GROUP - 1) / BWD_GROUP);
+    const int grid = ALIBI ? (int)(((groups + 7) / 8) * 8 * BWD_GROUP) : ((total + 7) / 8) * 8;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, ALIBI, GATE>), dim3(grid), dim3(NW * 64), 0, stream,
                        a.ops, a.theta, a.alibi, a.dk, a.dv, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nkt,
                        total, fl, paired);
@@ -916,7 +940,8 @@ hipError_t launch_bwd_grads(const Geometry& g, const BwdArgs& a, hipStream_t str
   {
     const int nqt = (g.L + 32 * NW - 1) / (32 * NW);
     const int total = g.B * g.H * nqt;
-    const int grid = ((total + 7) / 8) * 8;
+    const long groups = (long)g.B * g.H * ((nqt + BWD_GROUP - 1) / BWD_GROUP);
+    const int grid = ALIBI ? (int)(((groups + 7) / 8) * 8 * BWD_GROUP) : ((total + 7) / 8) * 8;
     hipLaunchKernelGGL((bwd_dq_kernel<D, NW, ALIBI, GATE>), dim3(grid), dim3(NW * 64), 0, stream,
                        a.ops, a.theta, a.alibi, a.dq, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nqt, total,
                        fl, g.scale, g.hscale);
