@@ -420,11 +420,10 @@ __device__ __forceinline__ void dkdv_block(
     const float dg =
         GATE ? (float)(*reinterpret_cast<const double*>(st + 2 * RT + 2 * CT + 2 * TILE * 4) - gbase_k) - gj
              : 0.f;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qbase = t * TILE + 32 * qb;
-      if (qbase + 31 < kw) continue;  // every query of the block precedes every key of the wave
-      // -lse and -D of the rows of this lane's accumulator elements
+    // The parts of one 32-query block qb of the tile: the accumulator inputs
+    // -lse and -D of this lane's rows, S and dP' (first products), P and dS
+    // (bf16 B operands), then dV and dK.
+    auto first_products = [&](int qb, f32x16& sv, f32x16& dpv) __attribute__((always_inline)) {
       f32x16 cl, cd;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
@@ -445,21 +444,16 @@ __device__ __forceinline__ void dkdv_block(
 #pragma unroll
         for (int r = 0; r < 16; ++r) cl[r] += dg;
       }
-      f32x16 s = cl, dp = cd;
+      sv = cl;
+      dpv = cd;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(lds_op<ROWB>(tq, 32 * qb + ln, 2 * ks + hf), kop[ks], s);
-        dp = mfma32(lds_op<ROWB>(tdo, 32 * qb + ln, 2 * ks + hf), vop[ks], dp);
+        sv = mfma32(lds_op<ROWB>(tq, 32 * qb + ln, 2 * ks + hf), kop[ks], sv);
+        dpv = mfma32(lds_op<ROWB>(tdo, 32 * qb + ln, 2 * ks + hf), vop[ks], dpv);
       }
-      if (ALIBI || qbase == kw) {  // distance bias; the causal mask on the diagonal block
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = qbase + 16 * (r >> 3) + 8 * hf + (r & 7);  // query of element r
-          if (ALIBI) s[r] += slope2 * (float)(j - i);
-          if (qbase == kw && j > i) s[r] = -INFINITY;
-        }
-      }
-      bf16x8 pop[2], dsop[2];
+    };
+    auto probabilities = [&](const f32x16& sv, const f32x16& dpv, bf16x8 (&pop)[2],
+                             bf16x8 (&dsop)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         uint32_t wp[4], wd[4];
@@ -467,9 +461,9 @@ __device__ __forceinline__ void dkdv_block(
         for (int e = 0; e < 4; ++e) {
           float x[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) x[u] = __builtin_amdgcn_exp2f(s[8 * h2 + 2 * e + u]);
+          for (int u = 0; u < 2; ++u) x[u] = __builtin_amdgcn_exp2f(sv[8 * h2 + 2 * e + u]);
           wp[e] = pack_bf16x2(x[0], x[1]);
-          const float ds0 = x[0] * dp[8 * h2 + 2 * e], ds1 = x[1] * dp[8 * h2 + 2 * e + 1];
+          const float ds0 = x[0] * dpv[8 * h2 + 2 * e], ds1 = x[1] * dpv[8 * h2 + 2 * e + 1];
           wd[e] = pack_bf16x2(ds0, ds1);
           if (GATE) csum += ds0 + ds1;
         }
@@ -477,6 +471,9 @@ __device__ __forceinline__ void dkdv_block(
         pop[h2] = __builtin_bit_cast(bf16x8, a);
         dsop[h2] = __builtin_bit_cast(bf16x8, c);
       }
+    };
+    auto second_products = [&](int qb, const bf16x8 (&pop)[2], const bf16x8 (&dsop)[2])
+        __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -485,6 +482,48 @@ __device__ __forceinline__ void dkdv_block(
           dvt[db] = mfma32(lds_op<COLB>(tdoT, 32 * db + ln, ch), pop[h2], dvt[db]);
           dkt[db] = mfma32(lds_op<COLB>(tqT, 32 * db + ln, ch), dsop[h2], dkt[db]);
         }
+    };
+    if (t * TILE >= kw + 32) {
+      // Every query of the tile follows every key of the wave: no block is
+      // skipped and none is masked.  Both blocks' first products come first,
+      // with no branch between them and the softmax, so that the second
+      // block's products can overlap the first block's exponentials (the
+      // same accumulation order as below: identical results).
+      f32x16 s0, dp0, s1, dp1;
+      bf16x8 p0[2], ds0[2], p1[2], ds1[2];
+      first_products(0, s0, dp0);
+      first_products(1, s1, dp1);
+      if (ALIBI) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i0 = t * TILE + 16 * (r >> 3) + 8 * hf + (r & 7);  // query of element r, block 0
+          s0[r] = fmaf(slope2, (float)(j - i0), s0[r]);
+          s1[r] = fmaf(slope2, (float)(j - (i0 + 32)), s1[r]);
+        }
+      }
+      probabilities(s0, dp0, p0, ds0);
+      second_products(0, p0, ds0);
+      probabilities(s1, dp1, p1, ds1);
+      second_products(1, p1, ds1);
+      continue;
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qbase = t * TILE + 32 * qb;
+      if (qbase + 31 < kw) continue;  // every query of the block precedes every key of the wave
+      f32x16 sv, dpv;
+      first_products(qb, sv, dpv);
+      if (ALIBI || qbase == kw) {  // distance bias; the causal mask on the diagonal block
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = qbase + 16 * (r >> 3) + 8 * hf + (r & 7);  // query of element r
+          if (ALIBI) sv[r] = fmaf(slope2, (float)(j - i), sv[r]);
+          if (qbase == kw && j > i) sv[r] = -INFINITY;
+        }
+      }
+      bf16x8 pop[2], dsop[2];
+      probabilities(sv, dpv, pop, dsop);
+      second_products(qb, pop, dsop);
     }
   }
 
@@ -686,10 +725,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) clt[r] += dt;
     }
-    bf16x8 dsop[KS2];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      f32x16 s = clt, dp = cd;
+    // S^T and dP'^T of the keys 32 kb .. 32 kb + 31 of the tile, then their
+    // dS^T (the B operands of dQ^T += K~^T dS^T)
+    auto first_products = [&](int kb, f32x16& sv, f32x16& dpv) __attribute__((always_inline)) {
+      sv = clt;
+      dpv = cd;
       if constexpr (GATE) {  // minus the offset of the key of each element
         const float* gp = reinterpret_cast<const float*>(st + 2 * RT + CT) + 32 * kb + 8 * hf;
 #pragma unroll
@@ -698,24 +738,28 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
           const f32x4 gb = *reinterpret_cast<const f32x4*>(gp + 16 * h2 + 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            s[8 * h2 + e] -= ga[e];
-            s[8 * h2 + 4 + e] -= gb[e];
+            sv[8 * h2 + e] -= ga[e];
+            sv[8 * h2 + 4 + e] -= gb[e];
           }
         }
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(lds_op<ROWB>(tk, 32 * kb + ln, 2 * ks + hf), qop[ks], s);
-        dp = mfma32(lds_op<ROWB>(tv, 32 * kb + ln, 2 * ks + hf), doop[ks], dp);
+        sv = mfma32(lds_op<ROWB>(tk, 32 * kb + ln, 2 * ks + hf), qop[ks], sv);
+        dpv = mfma32(lds_op<ROWB>(tv, 32 * kb + ln, 2 * ks + hf), doop[ks], dpv);
       }
-      if (ALIBI || diag) {  // distance bias; the causal mask on the diagonal tile
+    };
+    // the distance bias (and on the diagonal tile the causal mask)
+    auto bias = [&](int kb, f32x16& sv, bool mask) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jj = n * TILE + 32 * kb + 16 * (r >> 3) + 8 * hf + (r & 7);  // key of element r
-          if (ALIBI) s[r] += slope2 * (float)(jj - i);
-          if (diag && jj > i) s[r] = -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int jj = n * TILE + 32 * kb + 16 * (r >> 3) + 8 * hf + (r & 7);  // key of element r
+        if (ALIBI) sv[r] = fmaf(slope2, (float)(jj - i), sv[r]);
+        if (mask && jj > i) sv[r] = -INFINITY;
       }
+    };
+    bf16x8 dsop[KS2];
+    auto scores = [&](int kb, const f32x16& sv, const f32x16& dpv) __attribute__((always_inline)) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         uint32_t wd[4];
@@ -725,13 +769,35 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int r = 8 * h2 + 2 * e + u;
-            x[u] = __builtin_amdgcn_exp2f(s[r]) * dp[r];
+            x[u] = __builtin_amdgcn_exp2f(sv[r]) * dpv[r];
           }
           if (GATE) rsum += x[0] + x[1];
           wd[e] = pack_bf16x2(x[0], x[1]);
         }
         u32x4 c = {wd[0], wd[1], wd[2], wd[3]};
         dsop[2 * kb + h2] = __builtin_bit_cast(bf16x8, c);
+      }
+    };
+    if (!diag) {
+      // No mask: both key blocks' products first, with no branch before the
+      // exponentials, so that the second block's products can overlap the
+      // first block's (same accumulation order: identical results).
+      f32x16 s0, dp0, s1, dp1;
+      first_products(0, s0, dp0);
+      first_products(1, s1, dp1);
+      if (ALIBI) {
+        bias(0, s0, false);
+        bias(1, s1, false);
+      }
+      scores(0, s0, dp0);
+      scores(1, s1, dp1);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        f32x16 sv, dpv;
+        first_products(kb, sv, dpv);
+        bias(kb, sv, true);
+        scores(kb, sv, dpv);
       }
     }
 #pragma unroll
