@@ -121,6 +121,35 @@ def _strided_rows(w, stride: int, offset: int = 0) -> np.ndarray:
     return np.concatenate([bh * L + i for bh in range(w.batch * w.heads)])
 
 
+def _parity_rows(w, total: int = 1024) -> np.ndarray:
+    """About `total` query rows of a workload spread over all its heads: per
+    head, evenly spaced rows plus the head's last (longest) row."""
+    L, bh = w.seqlen, w.batch * w.heads
+    per = max(1, total // bh)
+    i = np.unique(np.concatenate([(np.arange(per, dtype=np.int64) * L) // per + (7 % max(L // per, 1)),
+                                  [L - 1]]))
+    i = i[i < L]
+    return np.concatenate([h * L + i for h in range(bh)])
+
+
+def run_workload_parity(samples: dict) -> dict:
+    """Each other workload's timed output against the oracle on sampled rows
+    (the oracle recomputes each head's angle scan and rotation at full
+    length): max |error| beside the bar and the relative rms error."""
+    import oracle
+    from accumulated_rotation_positional_amd import workloads as wl
+    out = {}
+    for name, (rows, got) in samples.items():
+        w = wl.make(name)
+        flags = (oracle.ROTATE_QK | (oracle.ROTATE_V if w.rotate_v else 0) |
+                 (oracle.ALIBI if w.use_alibi else 0))
+        t0 = time.perf_counter()
+        ref = oracle.Problem(w.q, w.k, w.v, w.phi, flags, alibi=w.alibi).rows(rows, host_threads())
+        out[name] = {**_parity(got, ref, 2e-2 if w.dtype == "bf16" else 1e-4),
+                     "oracle_seconds": round(time.perf_counter() - t0, 2)}
+    return out
+
+
 def run_cpu_baseline(w, flags: int, alibi, target_s: float, got=None) -> dict:
     """Time the oracle on strided query rows.  Its cost is a fixed part per
     head (angle scan and key/value rotation) plus a part per row, so two
@@ -491,7 +520,8 @@ def _executed(name: str, attn_ms: float) -> dict:
             "attn_mfma_util": round(rate / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
-def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int = 20) -> dict:
+def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int = 20,
+                  samples: dict | None = None) -> dict:
     """The forward on every other workload, each at its full shape with seeded
     inputs.  ms_per_step: the whole forward through arp_forward (the scan with
     the key rotation fused in, then attention; fp32 I/O: scan and the fp32
@@ -499,7 +529,8 @@ def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int =
     launched kernel by kernel from Python (ms_per_step_host_launched, host
     bound on small grids) gives per-kernel event times on the stream; rates
     on the algorithmic attention flops.  Secondary figures next to the
-    headline workload's."""
+    headline workload's.  samples (if given) receives each workload's sampled
+    output rows for the parity check of the oracle leg."""
     from accumulated_rotation_positional_amd import workloads as wl
     out = {}
     for name in wl.SPECS:
@@ -600,6 +631,10 @@ def workloads_leg(binding, torch, dev, skip: str, steps: int = 20, warmup: int =
                      "(profiles/forward_counters.json)")
             if w.use_alibi else None,
         }
+        if samples is not None:
+            rows = _parity_rows(w)
+            got = o.reshape(-1, w.head_dim)[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+            samples[name] = (rows, got)
         del q, k, v, phi, alibi, ws, state, theta, o
         torch.cuda.empty_cache()
     return out
@@ -751,12 +786,13 @@ def main():
     if not args.forward_only:
         result["scan_hbm_gate"] = scan_gate(binding, torch, dev)
         result["angle_generators"] = generator_leg(binding, torch, dev)
+    wl_samples = {}
     if not args.fused and not args.forward_only:
         result["backward"] = backward_leg(binding, torch, dev, w, q, k, v, phi, alibi)
         result["decode"] = decode_leg(binding, torch, dev)
         result["forget_gate"] = forget_leg(binding, torch, dev, w, q, k, v, phi)
         if not args.no_workloads:
-            result["workloads"] = workloads_leg(binding, torch, dev, w.name)
+            result["workloads"] = workloads_leg(binding, torch, dev, w.name, samples=wl_samples)
     if not args.no_cpu_baseline:
         import oracle
         of = (oracle.ROTATE_QK | (oracle.ROTATE_V if w.rotate_v else 0) |
@@ -764,6 +800,8 @@ def main():
         got = o.float().cpu().numpy().reshape(-1, w.head_dim)
         result["cpu_baseline"] = run_cpu_baseline(w, of, w.alibi, args.cpu_seconds, got)
         result["cpu_baseline"]["single_thread"] = run_cpu_single_thread()
+        if wl_samples:
+            result["cpu_baseline"]["parity_per_workload"] = run_workload_parity(wl_samples)
     print(json.dumps(result), flush=True)
 
 
