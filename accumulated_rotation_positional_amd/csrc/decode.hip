@@ -326,31 +326,25 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
 }
 
 // One workgroup per (b, h): thread (pair p, group cg) merges every G-th chunk
-// of its pair, then the G groups are summed in LDS.
+// of its pair in one pass, U chunks per trip with all their loads issued
+// before any is used and the running sums rescaled once per trip to the
+// trip's maximum; then the G groups are merged in LDS the same way.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ part, const float* __restrict__ theta, const float* __restrict__ phi,
     uint64_t* __restrict__ state, const float* __restrict__ logf, double* __restrict__ gstate,
     uint16_t* __restrict__ o, int H, int Hphi, int nchunk, uint32_t flags) {
   constexpr int P = D / 2, G = 256 / P;
-  __shared__ float s_red[4];
-  __shared__ float s_sum[G][P][3];
+  constexpr int U = 8;
+  __shared__ float s_sum[G][P][4];
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh % H, g = (Hphi == 1) ? 0 : h;
   const int tid = threadIdx.x;
   const int p = tid % P, cg = tid / P;
   const float* src = part + (size_t)bh * nchunk * (D + 2);
-  float M = -INFINITY;
-  for (int c = tid; c < nchunk; c += 256) M = fmaxf(M, src[(size_t)c * (D + 2)]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if ((tid & 63) == 0) s_red[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  float Ls = 0.f, a0 = 0.f, a1 = 0.f;
-  // four chunks per trip, all their loads issued before any is used (every
-  // chunk holds at least one key, so its maximum is finite)
-  constexpr int U = 4;
+  // every chunk holds at least one key, so its maximum is finite; a trip
+  // always holds its first chunk (c0 < nchunk)
+  float M = -INFINITY, Ls = 0.f, a0 = 0.f, a1 = 0.f;
   for (int c0 = cg; c0 < nchunk; c0 += U * G) {
     float mc[U], lc[U], x0[U], x1[U];
 #pragma unroll
@@ -361,25 +355,43 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
       x0[u] = pc[2 + 2 * p];
       x1[u] = pc[3 + 2 * p];
     }
+    float mt = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (c0 + u * G < nchunk) mt = fmaxf(mt, mc[u]);
+    const float f0 = __builtin_amdgcn_exp2f(M - mt);  // 0 on the first trip (M = -inf)
+    Ls *= f0;
+    a0 *= f0;
+    a1 *= f0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (c0 + u * G >= nchunk) break;
-      const float f = __builtin_amdgcn_exp2f(mc[u] - M);
+      const float f = __builtin_amdgcn_exp2f(mc[u] - mt);
       Ls = fmaf(lc[u], f, Ls);
       a0 = fmaf(x0[u], f, a0);
       a1 = fmaf(x1[u], f, a1);
     }
+    M = mt;
   }
-  s_sum[cg][p][0] = Ls;
-  s_sum[cg][p][1] = a0;
-  s_sum[cg][p][2] = a1;
+  s_sum[cg][p][0] = M;
+  s_sum[cg][p][1] = Ls;
+  s_sum[cg][p][2] = a0;
+  s_sum[cg][p][3] = a1;
   __syncthreads();
   if (cg != 0) return;
+  // group 0 holds chunk 0, so the merged maximum is finite; a group with no
+  // chunk (M = -inf) gets weight 0
 #pragma unroll
-  for (int r = 1; r < G; ++r) {
-    Ls += s_sum[r][p][0];
-    a0 += s_sum[r][p][1];
-    a1 += s_sum[r][p][2];
+  for (int r = 1; r < G; ++r) M = fmaxf(M, s_sum[r][p][0]);
+  Ls = 0.f;
+  a0 = 0.f;
+  a1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    const float f = __builtin_amdgcn_exp2f(s_sum[r][p][0] - M);
+    Ls = fmaf(s_sum[r][p][1], f, Ls);
+    a0 = fmaf(s_sum[r][p][2], f, a0);
+    a1 = fmaf(s_sum[r][p][3], f, a1);
   }
   const float inv = 1.f / Ls;
   float x0 = a0 * inv, x1 = a1 * inv;
