@@ -289,6 +289,16 @@ __device__ __forceinline__ void attn_tile(
     for (int ks = 0; ks < KS; ++ks)
       qraw[qb][ks] = *reinterpret_cast<const u32x4*>(
           qr + ((size_t)bh * L + min(qw + 32 * qb + ln, L - 1)) * D + 16 * ks + 8 * hf);
+  // the per-tile key-norm maxima of the wave's first 256 key tiles, loaded
+  // with the query words so that their latency overlaps (reduced to kglob
+  // below)
+  const float* kmax_bh = FUSED ? nullptr : kmax + (size_t)bh * (Lp / BN);
+  float kpre[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!FUSED) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (lane + 64 * u <= last_w) kpre[u] = kmax_bh[lane + 64 * u];
+  }
   if constexpr (!FUSED) {
     if (rot_qk) {
 #pragma unroll
@@ -345,7 +355,6 @@ __device__ __forceinline__ void attn_tile(
       for (int e = 0; e < 8; ++e) n2 = fmaf((float)qop[qb][ks][e], (float)qop[qb][ks][e], n2);
     qn[qb] = sqrtf(halves_sum(n2)) * (1.f + 1e-4f);  // margin for the fp32 accumulation
   }
-  const float* kmax_bh = FUSED ? nullptr : kmax + (size_t)bh * (Lp / BN);
 
   // First tiles in flight before the loop: NST-1 direct loads, or tile 0
   // staged and rotated.
@@ -405,7 +414,14 @@ __device__ __forceinline__ void attn_tile(
   __shared__ int wdone[2][DESC ? NW : 1];
   bool wave_done = false;
   if constexpr (!FUSED) {
-    for (int c = lane; c <= last_w; c += 64) kglob = fmaxf(kglob, kmax_bh[c]);
+    kglob = fmaxf(fmaxf(kpre[0], kpre[1]), fmaxf(kpre[2], kpre[3]));
+    // walks of more than 256 key tiles: four loads in flight per trip
+    for (int c0 = lane + 256; c0 <= last_w; c0 += 256) {
+      float km4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) km4[u] = kmax_bh[min(c0 + 64 * u, last_w)];
+      kglob = fmaxf(kglob, fmaxf(fmaxf(km4[0], km4[1]), fmaxf(km4[2], km4[3])));
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) kglob = fmaxf(kglob, __shfl_xor(kglob, off));
   }
