@@ -83,3 +83,26 @@ def test_rope_angles_and_shared_table():
 
 def test_flops_formula():
     assert wl.attn_flops(2, 8, 16384, 64) == 4 * 64 * (16384 * 16385 // 2) * 16
+
+
+def test_bench_parity_row_sampling():
+    """The benchmark's per-workload parity rows: valid flat row indices, each
+    head present with its last (longest) row, about the requested count."""
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location(
+        "bench_mod", os.path.join(os.path.dirname(os.path.dirname(__file__)), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    for name in ("tiny_f32", "train_1k", "farmass_32k", "rope_8k_d128"):
+        s = wl.SPECS[name]
+        w = wl.make(name, batch=s.batch, heads=min(s.heads, 4), seqlen=min(s.seqlen, 4096))
+        rows = bench._parity_rows(w, total=256)
+        L, bh = w.seqlen, w.batch * w.heads
+        assert rows.dtype == np.int64 and np.all(np.diff(rows) > 0)
+        assert rows.min() >= 0 and rows.max() < bh * L
+        heads = rows // L
+        assert set(heads.tolist()) == set(range(bh))
+        for h in range(bh):
+            assert h * L + L - 1 in rows
+        assert rows.size <= 256 + bh
