@@ -827,81 +827,105 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 constexpr int RCH = 256;  // tokens per chunk
 
+// Thread layout of both passes: lane group c4 (P / 4 lanes per token) holds
+// four consecutive pairs 4 c4 .. 4 c4 + 3 (16-byte loads and stores), row
+// group rg = tid / (P / 4) a set of the chunk's tokens.
+template <int P>
+struct RscanLayout {
+  static constexpr int C4 = P / 4;      // lanes per token
+  static constexpr int G = 256 / C4;    // row groups
+  static constexpr int R = RCH / G;     // tokens per thread in the apply pass
+};
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
 // chunk totals (summed over the heads of the stream)
 template <int P>
 __global__ __launch_bounds__(256) void rscan_totals_kernel(const float* __restrict__ dtheta,
                                                            float* __restrict__ totals, int L,
                                                            int H, int Hphi, int nch) {
-  constexpr int G = 256 / P;
-  __shared__ float part[G][P];
+  using Y = RscanLayout<P>;
+  __shared__ float4 part[Y::G][Y::C4];
   const int c = blockIdx.x, bg = blockIdx.y;
   const int b = bg / Hphi, gg = bg % Hphi;
-  const int p = threadIdx.x % P, rg = threadIdx.x / P;
+  const int c4 = threadIdx.x % Y::C4, rg = threadIdx.x / Y::C4;
   const int hn = (Hphi == 1) ? H : 1;
-  float acc = 0.f;
+  const int tend = min(L, (c + 1) * RCH);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int hh = 0; hh < hn; ++hh) {
     const int h = (Hphi == 1) ? hh : gg;
-    const float* src = dtheta + ((size_t)(b * H + h) * L) * P;
-    for (int t = c * RCH + rg; t < min(L, (c + 1) * RCH); t += G) acc += src[(size_t)t * P + p];
+    const float4* src = reinterpret_cast<const float4*>(dtheta + ((size_t)(b * H + h) * L) * P) + c4;
+    // the thread's tokens c RCH + rg + G u, all loads in flight together
+    float4 x[Y::R];
+#pragma unroll
+    for (int u = 0; u < Y::R; ++u) {
+      const int t = c * RCH + rg + Y::G * u;
+      x[u] = (t < tend) ? src[(size_t)t * Y::C4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < Y::R; ++u) acc = add4(acc, x[u]);
   }
-  part[rg][p] = acc;
+  part[rg][c4] = acc;
   __syncthreads();
   if (rg == 0) {
-    float s = 0.f;
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int r = 0; r < G; ++r) s += part[r][p];
-    totals[((size_t)bg * nch + c) * P + p] = s;
+    for (int r = 0; r < Y::G; ++r) t = add4(t, part[r][c4]);
+    reinterpret_cast<float4*>(totals + ((size_t)bg * nch + c) * P)[c4] = t;
   }
 }
 
 // In-chunk suffix sums plus the totals of every later chunk (read directly:
-// at most a few hundred coalesced loads per thread, no separate pass).
+// a few 16-byte loads per thread, no separate pass).
 template <int P>
 __global__ __launch_bounds__(256) void rscan_apply_kernel(const float* __restrict__ dtheta,
                                                           const float* __restrict__ totals,
                                                           float* __restrict__ dphi, int L, int H,
                                                           int Hphi, int nch, int exclusive) {
-  constexpr int G = 256 / P, R = RCH / G;  // each thread: R consecutive tokens of one pair
-  __shared__ float run_tot[G][P];
+  using Y = RscanLayout<P>;
+  constexpr int R = Y::R;  // each thread: R consecutive tokens of four pairs
+  __shared__ float4 run_tot[Y::G][Y::C4];
   const int c = blockIdx.x, bg = blockIdx.y;
   const int b = bg / Hphi, gg = bg % Hphi;
-  const int p = threadIdx.x % P, rg = threadIdx.x / P;
+  const int c4 = threadIdx.x % Y::C4, rg = threadIdx.x / Y::C4;
   const int hn = (Hphi == 1) ? H : 1;
   const int t0 = c * RCH + rg * R;
-  float x[R];
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 x[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) x[r] = 0.f;
+  for (int r = 0; r < R; ++r) x[r] = z;
   for (int hh = 0; hh < hn; ++hh) {
     const int h = (Hphi == 1) ? hh : gg;
-    const float* src = dtheta + ((size_t)(b * H + h) * L) * P;
+    const float4* src = reinterpret_cast<const float4*>(dtheta + ((size_t)(b * H + h) * L) * P) + c4;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (t0 + r < L) x[r] += src[(size_t)(t0 + r) * P + p];
+      if (t0 + r < L) x[r] = add4(x[r], src[(size_t)(t0 + r) * Y::C4]);
   }
-  float tot = 0.f;
+  float4 tot = z;
 #pragma unroll
-  for (int r = 0; r < R; ++r) tot += x[r];
-  // chunks after this one: the G threads of a pair split them
-  float later = 0.f;
-  for (int c2 = c + 1 + rg; c2 < nch; c2 += G) later += totals[((size_t)bg * nch + c2) * P + p];
+  for (int r = 0; r < R; ++r) tot = add4(tot, x[r]);
+  // chunks after this one: the G row groups of a pair set split them
+  float4 later = z;
+  const float4* tsrc = reinterpret_cast<const float4*>(totals + (size_t)bg * nch * P) + c4;
+  for (int c2 = c + 1 + rg; c2 < nch; c2 += Y::G) later = add4(later, tsrc[(size_t)c2 * Y::C4]);
+  run_tot[rg][c4] = later;
   __syncthreads();
-  run_tot[rg][p] = later;
-  __syncthreads();
-  float off = 0.f;
+  float4 off = z;
 #pragma unroll
-  for (int r2 = 0; r2 < G; ++r2) off += run_tot[r2][p];
+  for (int r2 = 0; r2 < Y::G; ++r2) off = add4(off, run_tot[r2][c4]);
   __syncthreads();
-  run_tot[rg][p] = tot;
+  run_tot[rg][c4] = tot;
   __syncthreads();
-  for (int r2 = rg + 1; r2 < G; ++r2) off += run_tot[r2][p];
-  float* dst = dphi + ((size_t)bg * L) * P;
-  float run = off;
+  for (int r2 = rg + 1; r2 < Y::G; ++r2) off = add4(off, run_tot[r2][c4]);
+  float4* dst = reinterpret_cast<float4*>(dphi + ((size_t)bg * L) * P) + c4;
+  float4 run = off;
 #pragma unroll
   for (int r = R - 1; r >= 0; --r) {
-    const float xr = x[r];
-    if (!exclusive) run += xr;
-    if (t0 + r < L) dst[(size_t)(t0 + r) * P + p] = run;
-    if (exclusive) run += xr;
+    if (!exclusive) run = add4(run, x[r]);
+    if (t0 + r < L) dst[(size_t)(t0 + r) * Y::C4] = run;
+    if (exclusive) run = add4(run, x[r]);
   }
 }
 
