@@ -778,10 +778,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
         dsop[2 * kb + h2] = __builtin_bit_cast(bf16x8, c);
       }
     };
-    if (!diag) {
+    if (!diag && D == 64) {
       // No mask: both key blocks' products first, with no branch before the
       // exponentials, so that the second block's products can overlap the
-      // first block's (same accumulation order: identical results).
+      // first block's (same accumulation order: identical results).  At
+      // d = 128 the two blocks' S and dP' would not fit beside the second
+      // wave of the SIMD.
       f32x16 s0, dp0, s1, dp1;
       first_products(0, s0, dp0);
       first_products(1, s1, dp1);
@@ -1028,11 +1030,16 @@ hipError_t launch_bwd_grads(const Geometry& g, const BwdArgs& a, hipStream_t str
     if (e != hipSuccess) return e;
   }
   {
-    const int nqt = (g.L + 32 * NW - 1) / (32 * NW);
+    // dQ runs 8 waves (two per SIMD) at both head dims: at d = 128 its
+    // registers fit two waves per SIMD when the key blocks are taken one at a
+    // time, which beats one wave per SIMD with both blocks in flight
+    // (rope_8k_d128 backward 10.87 -> 9.42 ms, gradients bit-identical)
+    constexpr int NQ = 8;
+    const int nqt = (g.L + 32 * NQ - 1) / (32 * NQ);
     const int total = g.B * g.H * nqt;
     const long groups = (long)g.B * g.H * ((nqt + BWD_GROUP - 1) / BWD_GROUP);
     const int grid = ALIBI ? (int)(((groups + 7) / 8) * 8 * BWD_GROUP) : ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, ALIBI, GATE>), dim3(grid), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NQ, ALIBI, GATE>), dim3(grid), dim3(NQ * 64), 0, stream,
                        a.ops, a.theta, a.alibi, a.dq, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nqt, total,
                        fl, g.scale, g.hscale);
     hipError_t e = hipGetLastError();
