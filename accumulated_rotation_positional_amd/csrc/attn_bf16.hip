@@ -76,8 +76,8 @@ constexpr int SPREAD_GROUP = 8;
 // key-norm maxima kmax bound the logits.
 // FUSED = true: kr, vt are the raw k, v ([B, H, L, D]); each K/V tile is
 // rotated while it is staged through registers into LDS (sin/cos once per
-// (key, pair), shared by k and v; V transposed); row maxima are always taken
-// exactly.
+// (key, pair), shared by k and v) in the layout the direct loads give the
+// pre-rotated rows; row maxima are always taken exactly.
 // BIAS: bit 0 the distance bias -m_h (i - j), bit 1 the forget-gate bias
 // G_i - G_j, with G = log2 e * (prefix sums of log f) from the gate pass
 // (non-increasing, so the bias never raises a score), read in its tiled
@@ -106,8 +106,7 @@ __device__ __forceinline__ void attn_tile(
   constexpr int KS2 = BN / 16;         // k-steps of O^T (16 keys each)
   constexpr int KROW = D * 2;          // bytes per K~ row in LDS
   constexpr int KTILE = BN * KROW;
-  constexpr int VROW = BN * 2;         // bytes per V~^T row in LDS (fused staging)
-  constexpr int VTILE = D * VROW;      // = BN * KROW: the natural V rows take the same space
+  constexpr int VTILE = BN * KROW;     // the natural V rows
   constexpr int KLD = KTILE / (1024 * NW);  // 1 KB direct loads per wave per tile
   constexpr int VLD = VTILE / (1024 * NW);
   static_assert(KLD * 1024 * NW == KTILE && VLD * 1024 * NW == VTILE, "staging split");
@@ -116,8 +115,9 @@ __device__ __forceinline__ void attn_tile(
   static_assert(!FUSED || NST == 2, "register staging uses two stages");
   constexpr int P = D / 2;
   constexpr int NT = NW * 64;
-  constexpr int IPT = P * (BN / 4) / NT;  // fused staging: (pair, 4-key group) items per thread
-  static_assert(!FUSED || IPT * NT == P * (BN / 4), "fused staging split");
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int IPT = BN * CPR / NT;      // fused staging: (key, chunk) items per thread
+  static_assert(!FUSED || IPT * NT == BN * CPR, "fused staging split");
 
   // the tile's 64 key gate offsets (fp32) and its fp64 gate base, padded so
   // that every stage starts on a 256-byte boundary (the LDS bank period)
@@ -206,55 +206,51 @@ __device__ __forceinline__ void attn_tile(
     }
   };
   // ---- fused staging: raw k, v and angles of one tile -> registers -> rotated into LDS ----
-  // Item it = (pair p, keys 4kg..4kg+3); lanes run over p, so each load
-  // instruction reads whole rows of k, v and theta.
+  // Item = (key kk of the tile, 16-byte chunk c of its row: four pairs); the
+  // CPR lanes of a key are adjacent, so each load instruction reads whole
+  // rows of k, v and theta.  The rotated rows land in the layout the direct
+  // loads give the pre-rotated operands (K~ rows in swap_bits23 order,
+  // chunks swizzled; natural V rows with the V swizzle), so the products
+  // are the same code.
   const int g = (Hphi == 1) ? 0 : h;
   const float* th_bh = theta + (size_t)(b * Hphi + g) * L * P;
-  uint32_t kreg[IPT > 0 ? IPT : 1][4], vreg[IPT > 0 ? IPT : 1][4];
-  float treg[IPT > 0 ? IPT : 1][4];
+  u32x4 kreg[IPT > 0 ? IPT : 1], vreg[IPT > 0 ? IPT : 1];
+  float4 treg[IPT > 0 ? IPT : 1];
   auto fetch = [&](int tile) __attribute__((always_inline)) {
     const uint16_t* kb = kr + (size_t)bh * L * D;
     const uint16_t* vb = vt + (size_t)bh * L * D;
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int it = tid + i * NT;
-      const int p = it % P, kg = it / P;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = min(tile * BN + 4 * kg + e, L - 1);  // rows past L are masked anyway
-        kreg[i][e] = *reinterpret_cast<const uint32_t*>(kb + (size_t)key * D + 2 * p);
-        vreg[i][e] = *reinterpret_cast<const uint32_t*>(vb + (size_t)key * D + 2 * p);
-        treg[i][e] = (rot_qk || ROTV) ? th_bh[(size_t)key * P + p] : 0.f;
-      }
+      const int kk = it / CPR, c = it % CPR;
+      const int key = min(tile * BN + kk, L - 1);  // rows past L are masked anyway
+      kreg[i] = *reinterpret_cast<const u32x4*>(kb + (size_t)key * D + 8 * c);
+      vreg[i] = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D + 8 * c);
+      treg[i] = (rot_qk || ROTV) ? *reinterpret_cast<const float4*>(th_bh + (size_t)key * P + 4 * c)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
   auto commit = [&](uint8_t* stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int it = tid + i * NT;
-      const int p = it % P, kg = it / P;
-      float v0[4], v1[4];
+      const int kk = it / CPR, c = it % CPR;
+      const float ang[4] = {treg[i].x, treg[i].y, treg[i].z, treg[i].w};
+      u32x4 kw, vw;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float sn, cs;
-        __sincosf(treg[i][e], &sn, &cs);
+        __sincosf(ang[e], &sn, &cs);
         float k0 = lo_bf16(kreg[i][e]), k1 = hi_bf16(kreg[i][e]);
-        v0[e] = lo_bf16(vreg[i][e]);
-        v1[e] = hi_bf16(vreg[i][e]);
+        float v0 = lo_bf16(vreg[i][e]), v1 = hi_bf16(vreg[i][e]);
         if (rot_qk) rotate_pair(k0, k1, cs, sn);
-        if (ROTV) rotate_pair(v0[e], v1[e], cs, sn);
-        const int row = swap_bits23(4 * kg + e);  // LDS row holding this key
-        *reinterpret_cast<uint32_t*>(stage + row * KROW + (((p >> 2) ^ swz<KROW>(row)) << 4) +
-                                     4 * (p & 3)) = pack_bf16x2(k0, k1);
+        if (ROTV) rotate_pair(v0, v1, cs, sn);
+        kw[e] = pack_bf16x2(k0, k1);
+        vw[e] = pack_bf16x2(v0, v1);
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int d = 2 * p + j;
-        const float* vv = j ? v1 : v0;
-        u32x2 w = {pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
-        *reinterpret_cast<u32x2*>(stage + KTILE + d * VROW + (((kg >> 1) ^ swz<VROW>(d)) << 4) +
-                                  8 * (kg & 1)) = w;
-      }
+      const int row = swap_bits23(kk);  // LDS row holding this key
+      *reinterpret_cast<u32x4*>(stage + row * KROW + ((c ^ swz<KROW>(row)) << 4)) = kw;
+      *reinterpret_cast<u32x4*>(stage + KTILE + kk * KROW + ((c ^ swzv<KROW>(kk)) << 4)) = vw;
     }
   };
 
@@ -587,23 +583,16 @@ __device__ __forceinline__ void attn_tile(
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int ks2 = 0; ks2 < KS2; ++ks2) {
-        bf16x8 va;
-        if constexpr (!FUSED) {
-          const int colb = 64 * db + 32 * trg + 8 * (trj & 3);  // byte offset in the row
-          u32x2 t[2];
+        const int colb = 64 * db + 32 * trg + 8 * (trj & 3);  // byte offset in the row
+        u32x2 t[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int row = 16 * ks2 + 8 * hf + 4 * u + (trj >> 2);
-            t[u] = lds_read_tr16(vtile + row * KROW + (((colb >> 4) ^ swzv<KROW>(row)) << 4) +
-                                 (colb & 15));
-          }
-          const u32x4 w = {t[0][0], t[0][1], t[1][0], t[1][1]};
-          va = __builtin_bit_cast(bf16x8, w);
-        } else {
-          const int row = 32 * db + ln;
-          va = *reinterpret_cast<const bf16x8*>(
-              vtile + row * VROW + (((2 * ks2 + hf) ^ swz<VROW>(row)) << 4));
+        for (int u = 0; u < 2; ++u) {
+          const int row = 16 * ks2 + 8 * hf + 4 * u + (trj >> 2);
+          t[u] = lds_read_tr16(vtile + row * KROW + (((colb >> 4) ^ swzv<KROW>(row)) << 4) +
+                               (colb & 15));
         }
+        const u32x4 w = {t[0][0], t[0][1], t[1][0], t[1][1]};
+        const bf16x8 va = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma32(va, pop[ks2][qb], oacc[db][qb]);
       }
