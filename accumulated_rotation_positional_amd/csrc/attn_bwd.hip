@@ -446,10 +446,21 @@ __device__ __forceinline__ void dkdv_block(
       }
       sv = cl;
       dpv = cd;
+      // every LDS operand of the block is read before its first product:
+      // left to itself the compiler reads each one just before its product
+      // and waits for it there, which at one wave per SIMD (d = 128) leaves
+      // the matrix core idle for the LDS latency at every product
+      bf16x8 qa[KS], da[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        sv = mfma32(lds_op<ROWB>(tq, 32 * qb + ln, 2 * ks + hf), kop[ks], sv);
-        dpv = mfma32(lds_op<ROWB>(tdo, 32 * qb + ln, 2 * ks + hf), vop[ks], dpv);
+        qa[ks] = lds_op<ROWB>(tq, 32 * qb + ln, 2 * ks + hf);
+        da[ks] = lds_op<ROWB>(tdo, 32 * qb + ln, 2 * ks + hf);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sv = mfma32(qa[ks], kop[ks], sv);
+        dpv = mfma32(da[ks], vop[ks], dpv);
       }
     };
     auto probabilities = [&](const f32x16& sv, const f32x16& dpv, bf16x8 (&pop)[2],
@@ -474,13 +485,22 @@ __device__ __forceinline__ void dkdv_block(
     };
     auto second_products = [&](int qb, const bf16x8 (&pop)[2], const bf16x8 (&dsop)[2])
         __attribute__((always_inline)) {
+      bf16x8 oa[DB][2], qa[DB][2];  // operands first, as in first_products
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int ch = 4 * qb + 2 * h2 + hf;
-          dvt[db] = mfma32(lds_op<COLB>(tdoT, 32 * db + ln, ch), pop[h2], dvt[db]);
-          dkt[db] = mfma32(lds_op<COLB>(tqT, 32 * db + ln, ch), dsop[h2], dkt[db]);
+          oa[db][h2] = lds_op<COLB>(tdoT, 32 * db + ln, ch);
+          qa[db][h2] = lds_op<COLB>(tqT, 32 * db + ln, ch);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          dvt[db] = mfma32(oa[db][h2], pop[h2], dvt[db]);
+          dkt[db] = mfma32(qa[db][h2], dsop[h2], dkt[db]);
         }
     };
     if (t * TILE >= kw + 32) {
