@@ -765,8 +765,8 @@ __device__ __forceinline__ void attn_tile(
 // every head first: grouping would leave the XCD with the gentlest heads
 // doing several times the average work, and the longest tiles of the last
 // heads would start last.
-// paired (the unbiased 512-query shape, total_tiles a multiple of 16): half
-// as many workgroups, each taking the c-th longest and the c-th shortest
+// paired (unbiased, total_tiles a multiple of 16; which grids is decided at
+// the launch below): half as many workgroups, each taking the c-th longest and the c-th shortest
 // tile of its XCD's share one after the other, so every workgroup has the
 // same work and no CU waits for a second dispatch.
 template <int D, int QPW, int NW, int NST, int MINB, bool FUSED, int BIAS, bool ROTV>
@@ -785,7 +785,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
                        : (RING > TSTAGE ? RING : TSTAGE);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDSB];
   constexpr bool SPREAD = (BIAS != 0) && !FUSED;
-  constexpr bool PAIRABLE = QPW == 64 && NW == 8 && BIAS == 0 && !FUSED;
+  constexpr bool PAIRABLE = ((QPW == 64 && NW == 8) || (QPW == 32 && NW == 4)) && BIAS == 0 && !FUSED;
   const int per = (total_tiles + 7) / 8;
   if (PAIRABLE && paired) {
     const int x = (int)(blockIdx.x % 8), c = (int)(blockIdx.x / 8);
@@ -815,7 +815,16 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
   const int total = g.B * g.H * nqt;
   const bool rv = g.flags & ARP_ROTATE_V;
   const int bias = ((g.flags & ARP_ALIBI) ? 1 : 0) | ((g.flags & ARP_FORGET_GATE) ? 2 : 0);
-  const int paired = (QPW == 64 && NW == 8 && !FUSED && bias == 0 && total % 16 == 0) ? 1 : 0;
+  // Paired query tiles (a workgroup takes tile c of a run of its XCD and then
+  // the tile as far from the end; every pair holds the same number of key
+  // tiles): always for the 512-query shape; for 4 waves x 32 queries where
+  // the pairs still fill every CU and a head's walks are at most 8192 keys
+  // long (2 x 8 heads at 8192 tokens, d = 64: 182 -> 157 us; 8 x 8 at 2048:
+  // 70 -> 56 us; at 16384 tokens the shorter unpaired walks keep a head's
+  // K/V tiles shared in L2 better: 292 against 306 us).
+  const bool pair_ok = (QPW == 64 && NW == 8) ||
+                       (QPW == 32 && NW == 4 && g.L <= 8192 && total / 2 >= device_cus());
+  const int paired = (pair_ok && !FUSED && bias == 0 && total % 16 == 0) ? 1 : 0;
   // spread (biased, pre-rotation): every head's groups of SPREAD_GROUP query
   // tiles, a whole number of rounds over the 8 XCDs
   const long groups = (long)g.B * g.H * ((nqt + SPREAD_GROUP - 1) / SPREAD_GROUP);

@@ -222,6 +222,38 @@ def test_million_token_sequence_sampled_rows(alibi):
     assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", f"2^20 tokens alibi={alibi}")
 
 
+@pytest.mark.parametrize("name,heads,L,rotate_v", [("train_1k", 32, 2000, False),
+                                                   ("train_1k", 32, 2000, True),
+                                                   ("rope_8k_d128", 32, 2000, False)])
+def test_paired_small_shape_matches_unpaired(name, heads, L, rotate_v):
+    """The 4 waves x 32 queries shape pairs the c-th longest and c-th
+    shortest query tiles in one workgroup when the pairs still fill every CU
+    (tiles / 2 >= 256 on an MI355X), the walks are at most 8192 keys and the
+    tile count is a multiple of 16: 32 heads at 2000 tokens make 32 x 16 = 512
+    tiles of 128 queries (ragged: the last tile holds 80).  Three of those
+    heads alone (48 tiles) take the unpaired launch.  Every row is computed
+    the same way in both, so they must agree bit for bit, log-sum-exp too;
+    the paired run is also checked against the oracle on sampled rows."""
+    w = wl.make(name, batch=1, heads=heads, seqlen=L)
+
+    def run(x):
+        say(f"[gpu] paired small shape {name} H={x.heads} L={x.seqlen} v={rotate_v}")
+        o, _, lse = binding.forward_ex(to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.phi),
+                                       rotate_v=rotate_v, with_lse=True)
+        torch.cuda.synchronize()
+        return to_host(o), lse.cpu().numpy()
+
+    got, lse = run(w)
+    rows = sample_rows(w, per_head=6)
+    want = oracle.Problem(w.q, w.k, w.v, w.phi, oracle_flags(True, rotate_v, False)).rows(rows)
+    assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", f"paired 4x32, {name} L={L}")
+    part = dataclasses.replace(w, heads=3, **{n: np.ascontiguousarray(getattr(w, n)[:, :3])
+                                              for n in ("q", "k", "v", "phi")})
+    small, lse_small = run(part)
+    assert np.array_equal(small, got[:, :3]), float(np.abs(small - got[:, :3]).max())
+    assert np.array_equal(lse_small, lse[:, :3])
+
+
 @pytest.mark.parametrize("name,heads,L,rotate_v", [("train_1k", 16, 16400, False),
                                                    ("train_1k", 16, 16400, True),
                                                    ("train_1k", 17, 16896, True),
