@@ -877,11 +877,14 @@ hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* q, const 
     //    grains, so a grid's causal tail and a biased walk's uneven early
     //    stops cost less (8 x 8 heads at 1024 tokens 28.5 -> 24.2 us, 1 x 8 at
     //    16384 408 -> 291 us, ALiBi on 1 x 16 at 32768 1.34 -> 1.02 ms).
-    // The first is taken for an unbiased walk over at least 16384 tokens
-    // whose 512-query grid fills every CU twice, the second otherwise.
+    // The first is taken for an unbiased walk over at least 4096 tokens
+    // whose 512-query grid fills every CU twice (4 x 16 heads at 8192: 553
+    // against 491 us; 8 x 8 at 4096: 168 against 152 us; at 2048 tokens the
+    // second is faster: 16 x 16 heads 184 against 197 us), the second
+    // otherwise.
     const long wg512 = (long)g.B * g.H * ((g.L + 511) / 512);
     const bool biased = (g.flags & (ARP_ALIBI | ARP_FORGET_GATE)) != 0;
-    if (!biased && g.L >= 16384 && wg512 >= 2L * device_cus())
+    if (!biased && g.L >= 4096 && wg512 >= 2L * device_cus())
       return launch_bf16_cfg<64, 64, 8, 2, 1, false>(g, q, kr, v, vrows, kmax, theta, alibi, gate2, gbase, o,
                                                      lse, stream);
     return launch_bf16_cfg<64, 32, 4, 2, 2, false>(g, q, kr, v, vrows, kmax, theta, alibi, gate2, gbase, o, lse,

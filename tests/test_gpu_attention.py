@@ -260,7 +260,7 @@ def test_paired_small_shape_matches_unpaired(name, heads, L, rotate_v):
                                                    ("rope_8k_d128", 32, 8200, False)])
 def test_workgroup_shapes_agree_on_a_ragged_length(name, heads, L, rotate_v):
     """The d=64 attention takes 512-query workgroups (8 waves x 64 queries)
-    for unbiased walks over at least 16384 tokens whose 512-query grid fills
+    for unbiased walks over at least 4096 tokens whose 512-query grid fills
     every CU twice, and 128-query workgroups (4 waves x 32 queries, two per
     CU) otherwise.  16 heads at 16400 tokens (16400 = 256*64 + 16, a ragged
     16-key tail; 528 workgroups of 512) take the first; three of those heads

@@ -1,8 +1,9 @@
 """Seeded random shapes and flag combinations against the fp64 oracle, on
 sampled rows (tile edges, the ends, random rows of every head).  The shapes
 straddle the attention kernel's workgroup-shape rule (512-query workgroups
-for unbiased walks over at least 16384 tokens on deep grids, 128-query
-workgroups otherwise, at d=64; the d=128 rule on 256-query grids), ragged
+for unbiased walks over at least 4096 tokens on deep grids, 128-query
+workgroups otherwise, paired where they fill the CUs, at d=64; the d=128
+rule on 256-query grids), ragged
 lengths, both head dims, shared angle heads, the exclusive scan, ALiBi and
 forget gates.  Bar: the forward's bf16 bar on the sampled rows."""
 import dataclasses
@@ -24,7 +25,7 @@ def _cases():
     cases = []
     # (B, H, L) chosen around the shape rule's edges, then random ones
     fixed = [(1, 16, 16384), (2, 8, 16385), (1, 32, 16383), (1, 8, 16400), (4, 8, 4097),
-             (1, 40, 8200), (2, 2, 513), (3, 5, 777)]
+             (1, 40, 8200), (2, 2, 513), (3, 5, 777), (8, 8, 4096), (4, 16, 4100), (8, 8, 4000)]
     for i, (B, H, L) in enumerate(fixed):
         cases.append(dict(B=B, H=H, L=L, d=64 if i % 3 else 128, rotate_v=bool(i % 2),
                           alibi=i % 4 == 3, gate=i % 5 == 4, exclusive=i % 6 == 5,
