@@ -891,12 +891,14 @@ hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* q, const 
                                                    stream);
   }
   // d = 128: 256-query workgroups of 8 waves x 32 queries for unbiased grids
-  // of at least four per CU (4 x 32 heads at 8192 tokens: 2.06 ms against
-  // 2.12 ms), else 128-query workgroups of 4 waves x 32 queries, two per CU
-  // (1 x 8 heads at 8192 tokens 213 -> 201 us, 2 x 8 at 2048 63 -> 51 us).
+  // of at least four per CU, or two per CU from 8192 tokens (4 x 32 heads at
+  // 8192 tokens: 2.06 ms against 2.12 ms; 1 x 16 at 8192: 249 against 261
+  // us), else 128-query workgroups of 4 waves x 32 queries, two per CU
+  // (1 x 8 heads at 8192 tokens 213 -> 201 us, 2 x 8 at 2048 63 -> 51 us; 2 x
+  // 16 at 4096, paired, 148 against 189 us for the larger workgroups).
   const long wg256 = (long)g.B * g.H * ((g.L + 255) / 256);
   const bool biased = (g.flags & (ARP_ALIBI | ARP_FORGET_GATE)) != 0;
-  if (!biased && wg256 >= 4L * device_cus())
+  if (!biased && wg256 >= (g.L >= 8192 ? 2L : 4L) * device_cus())
     return launch_bf16_cfg<128, 32, 8, 2, 1, false>(g, q, kr, v, vrows, kmax, theta, alibi, gate2, gbase, o,
                                                     lse, stream);
   return launch_bf16_cfg<128, 32, 4, 2, 2, false>(g, q, kr, v, vrows, kmax, theta, alibi, gate2, gbase, o, lse,

@@ -25,7 +25,7 @@ def _cases():
     cases = []
     # (B, H, L) chosen around the shape rule's edges, then random ones
     fixed = [(1, 16, 16384), (2, 8, 16385), (1, 32, 16383), (1, 8, 16400), (4, 8, 4097),
-             (1, 40, 8200), (2, 2, 513), (3, 5, 777), (8, 8, 4096), (4, 16, 4100), (8, 8, 4000)]
+             (1, 40, 8200), (2, 2, 513), (3, 5, 777), (8, 8, 4096), (4, 16, 4100), (8, 8, 4000), (2, 3, 300), (1, 16, 8192)]
     for i, (B, H, L) in enumerate(fixed):
         cases.append(dict(B=B, H=H, L=L, d=64 if i % 3 else 128, rotate_v=bool(i % 2),
                           alibi=i % 4 == 3, gate=i % 5 == 4, exclusive=i % 6 == 5,
