@@ -765,18 +765,21 @@ __device__ __forceinline__ void attn_tile(
 // every head first: grouping would leave the XCD with the gentlest heads
 // doing several times the average work, and the longest tiles of the last
 // heads would start last.
-// paired (unbiased, total_tiles a multiple of 16; which grids is decided at
-// the launch below): half as many workgroups, each taking the c-th longest and the c-th shortest
+// PAIR (unbiased, total_tiles a multiple of 16; which grids is decided at
+// the launch below, and the paired walk is an instantiation of its own so
+// that the unpaired one keeps its own register allocation): half as many
+// workgroups, each taking the c-th longest and the c-th shortest
 // tile of its XCD's share one after the other, so every workgroup has the
 // same work and no CU waits for a second dispatch.
-template <int D, int QPW, int NW, int NST, int MINB, bool FUSED, int BIAS, bool ROTV>
+template <int D, int QPW, int NW, int NST, int MINB, bool FUSED, int BIAS, bool ROTV, bool PAIR>
 __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
     const float* __restrict__ theta, const float* __restrict__ alibi,
     const float* __restrict__ gate2, const double* __restrict__ gbase, uint16_t* __restrict__ o,
     float* __restrict__ lse, int L, int Lp, int vrows, int H, int Hphi, int nqt, int total_tiles,
-    int rot_qk, float qscale, int paired, const float* __restrict__ hscale) {
+    int rot_qk, float qscale, const float* __restrict__ hscale) {
+  static_assert(!PAIR || BIAS == 0, "pairs are for unbiased walks");
   constexpr int STAGE = BN * D * 2 + D * BN * 2 + (((BIAS & 2) != 0) ? BN * 4 + 256 : 0);  // as in attn_tile
   // the tile ring and the waves' query angle rows (after the ring, or in its
   // space before it is loaded; as in attn_tile)
@@ -785,9 +788,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_bf16_kernel(
                        : (RING > TSTAGE ? RING : TSTAGE);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDSB];
   constexpr bool SPREAD = (BIAS != 0) && !FUSED;
-  constexpr bool PAIRABLE = ((QPW == 64 && NW == 8) || (QPW == 32 && NW == 4)) && BIAS == 0 && !FUSED;
   const int per = (total_tiles + 7) / 8;
-  if (PAIRABLE && paired) {
+  if constexpr (PAIR) {
     const int x = (int)(blockIdx.x % 8), c = (int)(blockIdx.x / 8);
     attn_tile<D, QPW, NW, NST, MINB, FUSED, BIAS, ROTV>(x * per + c, smem, qr, kr, vt, kmax, theta,
                                                         alibi, gate2, gbase, o, lse, L, Lp, vrows, H, Hphi, nqt,
@@ -822,9 +824,14 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
   // long (2 x 8 heads at 8192 tokens, d = 64: 182 -> 157 us; 8 x 8 at 2048:
   // 70 -> 56 us; at 16384 tokens the shorter unpaired walks keep a head's
   // K/V tiles shared in L2 better: 292 against 306 us).
+  // With the rotation fused into the staging the 4 x 32 shape pairs by the
+  // same rule (8 x 8 heads at 2048 tokens 93.6 -> 82.1 us, 2 x 8 at 4096
+  // 122.5 -> 95.7 us); the 512-query fused walk does not pair (2 x 8 heads
+  // at 16384 tokens: 610 against 766 us paired).
+  constexpr bool CAN_PAIR = (QPW == 64 && NW == 8 && !FUSED) || (QPW == 32 && NW == 4);
   const bool pair_ok = (QPW == 64 && NW == 8) ||
                        (QPW == 32 && NW == 4 && g.L <= 8192 && total / 2 >= device_cus());
-  const int paired = (pair_ok && !FUSED && bias == 0 && total % 16 == 0) ? 1 : 0;
+  const bool paired = CAN_PAIR && pair_ok && bias == 0 && total % 16 == 0;
   // spread (biased, pre-rotation): every head's groups of SPREAD_GROUP query
   // tiles, a whole number of rounds over the 8 XCDs
   const long groups = (long)g.B * g.H * ((nqt + SPREAD_GROUP - 1) / SPREAD_GROUP);
@@ -833,24 +840,33 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
                                            : ((total + 7) / 8) * 8;
   const int rqk = (g.flags & ARP_ROTATE_QK) ? 1 : 0;
   const float qscale = g.scale * LOG2E;
-#define ARP_BF16_LAUNCH(A, R)                                                                  \
-  hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, MINB, FUSED, A, R>), dim3(grid),      \
+#define ARP_BF16_LAUNCH(A, R, P)                                                               \
+  hipLaunchKernelGGL((attn_bf16_kernel<D, QPW, NW, NST, MINB, FUSED, A, R, P>), dim3(grid),   \
                      dim3(NW * 64), 0, stream, qr, kr, vt, kmax, theta, alibi, gate2, gbase, o, \
                      lse,                                                                       \
-                     g.L, g.Lp, vrows, g.H, g.Hphi, nqt, total, rqk, qscale, paired, g.hscale)
-#define ARP_BF16_LAUNCH_R(A) \
-  do {                       \
-    if (rv) ARP_BF16_LAUNCH(A, true); else ARP_BF16_LAUNCH(A, false); \
+                     g.L, g.Lp, vrows, g.H, g.Hphi, nqt, total, rqk, qscale, g.hscale)
+#define ARP_BF16_LAUNCH_R(A, P) \
+  do {                          \
+    if (rv) ARP_BF16_LAUNCH(A, true, P); else ARP_BF16_LAUNCH(A, false, P); \
   } while (0)
+  auto launch_unbiased = [&]() {
+    if constexpr (CAN_PAIR) {
+      if (paired) {
+        ARP_BF16_LAUNCH_R(0, true);
+        return;
+      }
+    }
+    ARP_BF16_LAUNCH_R(0, false);
+  };
   if constexpr (FUSED) {
     if (bias & 2) return hipErrorNotSupported;
-    if (bias & 1) ARP_BF16_LAUNCH_R(1); else ARP_BF16_LAUNCH_R(0);
+    if (bias & 1) ARP_BF16_LAUNCH_R(1, false); else launch_unbiased();
   } else {
     switch (bias) {
-      case 0: ARP_BF16_LAUNCH_R(0); break;
-      case 1: ARP_BF16_LAUNCH_R(1); break;
-      case 2: ARP_BF16_LAUNCH_R(2); break;
-      default: ARP_BF16_LAUNCH_R(3); break;
+      case 0: launch_unbiased(); break;
+      case 1: ARP_BF16_LAUNCH_R(1, false); break;
+      case 2: ARP_BF16_LAUNCH_R(2, false); break;
+      default: ARP_BF16_LAUNCH_R(3, false); break;
     }
   }
 #undef ARP_BF16_LAUNCH_R
@@ -908,8 +924,21 @@ hipError_t launch_attn_bf16_rotated(const Geometry& g, const uint16_t* q, const 
 hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const float* theta, const float* alibi,
                                   uint16_t* o, hipStream_t stream) {
-  if (g.D == 64)
-    return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, g.L, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
+  if (g.D == 64) {
+    // The 512-query shape on deep unbiased grids (the rule of the
+    // pre-rotation path) and with the distance bias (1 x 16 heads at 32768
+    // tokens: 3.50 against 4.30 ms for 4 waves x 32 queries, whose forward
+    // walk has no early stop here either); otherwise 4 waves x 32 queries
+    // (8 x 8 heads at 1024 tokens 51.2 -> 37.8 us, 1 x 8 at 16384 527 -> 452
+    // us).
+    const long wg512 = (long)g.B * g.H * ((g.L + 511) / 512);
+    const bool biased = (g.flags & ARP_ALIBI) != 0;
+    if (biased || (g.L >= 4096 && wg512 >= 2L * device_cus()))
+      return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, g.L, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
+    return launch_bf16_cfg<64, 32, 4, 2, 2, true>(g, q, k, v, g.L, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
+  }
+  // d = 128: one shape (the 4 x 32 one stages four 16-byte pieces per thread
+  // and was slower on 8 x 8 heads at 1024 tokens: 62.3 against 51.1 us)
   return launch_bf16_cfg<128, 32, 8, 2, 1, true>(g, q, k, v, g.L, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
 }
 

@@ -254,6 +254,24 @@ def test_paired_small_shape_matches_unpaired(name, heads, L, rotate_v):
     assert np.array_equal(lse_small, lse[:, :3])
 
 
+@pytest.mark.parametrize("rotate_v", [False, True])
+def test_fused_paired_small_shape_matches_unpaired(rotate_v):
+    """With the rotation fused into the staging, d=64 grids that miss the
+    512-query rule take 4 waves x 32 queries, paired by the same rule as the
+    pre-rotation path: 32 heads at 2000 tokens (512 tiles) pair, three of
+    those heads alone do not.  Rows are computed the same way in both: bit for
+    bit, and the paired run against the oracle on sampled rows."""
+    w = wl.make("train_1k", batch=1, heads=32, seqlen=2000)
+    got, _ = run_forward(w, rotate_v=rotate_v, fused=True)
+    rows = sample_rows(w, per_head=6)
+    want = oracle_problem(w, rotate_v=rotate_v).rows(rows)
+    assert_close(got.reshape(-1, w.head_dim)[rows], want, "bf16", "fused paired 4x32")
+    part = dataclasses.replace(w, heads=3, **{n: np.ascontiguousarray(getattr(w, n)[:, :3])
+                                              for n in ("q", "k", "v", "phi")})
+    small, _ = run_forward(part, rotate_v=rotate_v, fused=True)
+    assert np.array_equal(small, got[:, :3]), float(np.abs(small - got[:, :3]).max())
+
+
 @pytest.mark.parametrize("name,heads,L,rotate_v", [("train_1k", 16, 16400, False),
                                                    ("train_1k", 16, 16400, True),
                                                    ("train_1k", 17, 16896, True),
