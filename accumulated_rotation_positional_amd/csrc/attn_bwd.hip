@@ -615,11 +615,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // 3. dQ (query-stationary)
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool ALIBI, bool GATE>
+template <int D, int NW, bool ALIBI, bool GATE, bool PAIR>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
     BwdOperands ops, const float* __restrict__ theta, const float* __restrict__ alibi,
     uint16_t* __restrict__ dq, float* __restrict__ dtheta, int L, int Lp, int H, int Hphi, int nqt,
     int total_tiles, uint32_t flags, float scale0, const float* __restrict__ hscale) {
+  static_assert(!PAIR || !ALIBI, "pairs are for unbiased walks");
   constexpr int BM = 32 * NW;
   constexpr int KS = D / 16, DB = D / 32, KB = 2, KS2 = 4;
   constexpr int ROWB = D * 2, RT = TILE * ROWB;
@@ -630,218 +631,235 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
 
   // Workgroup order as in the dK/dV pass: whole heads per XCD unbiased,
   // groups of query blocks dealt out across the XCDs with a distance bias
-  // (spread_slot); longest first.
-  int bh, qt;
-  if constexpr (ALIBI) {
-    int r;
-    if (!spread_slot((int)blockIdx.x, total_tiles / nqt, nqt, bh, r)) return;
-    qt = nqt - 1 - r;
-  } else {
-    const int per = (total_tiles + 7) / 8;
-    const int logical = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (logical >= total_tiles) return;
-    bh = logical / nqt;
-    qt = nqt - 1 - logical % nqt;
-  }
-  const int q0 = qt * BM;
-  const int b = bh / H, h = bh % H;
-  const int g = (Hphi == 1) ? 0 : h;
-  // the logit scale of this head: scale times its query multiplier (AdaScale),
-  // so dq = lambda_h dq' where q' = lambda_h q
-  const float scale = hscale != nullptr ? scale0 * hscale[h] : scale0;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int ln = lane & 31, hf = lane >> 5;
-  const int qw = q0 + 32 * wave;
-  const int i = qw + ln;  // this lane's query
-  const int last_tile = min(q0 + BM - 1, L - 1) / TILE;
-  const int last_w = (qw < L) ? min(qw + 31, L - 1) / TILE : -1;
-  const size_t rm = (size_t)bh * Lp * D, tb = (size_t)bh * D * Lp;
+  // (spread_slot); longest first.  PAIR (unbiased grids whose pairs still
+  // fill every CU): a workgroup takes the c-th longest and the c-th shortest
+  // block of its XCD's share one after the other, so every workgroup has the
+  // same work (8 x 8 heads at 2048 tokens, d = 64: backward 0.269 -> 0.249
+  // ms; 2 x 16 at 4096, d = 128: 0.792 -> 0.738 ms; extrap_16k unchanged).
+  // It is an instantiation of its own, so the unpaired walk keeps its
+  // register allocation.
+  //
+  // One query block (bh, qt):
+  auto run = [&](int bh, int qt) __attribute__((always_inline)) {
+    const int q0 = qt * BM;
+    const int b = bh / H, h = bh % H;
+    const int g = (Hphi == 1) ? 0 : h;
+    // the logit scale of this head: scale times its query multiplier (AdaScale),
+    // so dq = lambda_h dq' where q' = lambda_h q
+    const float scale = hscale != nullptr ? scale0 * hscale[h] : scale0;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int ln = lane & 31, hf = lane >> 5;
+    const int qw = q0 + 32 * wave;
+    const int i = qw + ln;  // this lane's query
+    const int last_tile = min(q0 + BM - 1, L - 1) / TILE;
+    const int last_w = (qw < L) ? min(qw + 31, L - 1) / TILE : -1;
+    const size_t rm = (size_t)bh * Lp * D, tb = (size_t)bh * D * Lp;
 
-  auto issue = [&](int t, uint8_t* st) __attribute__((always_inline)) {
-    load_rows_tile<D, NW>(ops.k + rm, t * TILE, st, wave, lane);
-    load_rows_tile<D, NW>(ops.v + rm, t * TILE, st + RT, wave, lane);
-    load_cols_tile<D, NW>(ops.kT + tb, Lp, t * TILE, st + 2 * RT, wave, lane);
-    if (GATE && wave == 0 && lane < TILE / 4)
-      __builtin_amdgcn_global_load_lds(
-          (global_void_ptr)(ops.gate2 + (size_t)bh * Lp + (size_t)t * TILE + 4 * lane),
-          (lds_void_ptr)(st + 2 * RT + CT), 16, 0, 0);
-    if (GATE && wave == 0 && lane < 2)  // the key tile's base, one 4-byte half per lane
-      __builtin_amdgcn_global_load_lds(
-          (global_void_ptr)(reinterpret_cast<const uint32_t*>(ops.gbase + (size_t)bh * (Lp / TILE) + t) +
-                            lane),
-          (lds_void_ptr)(st + 2 * RT + CT + TILE * 4), 4, 0, 0);
-  };
+    auto issue = [&](int t, uint8_t* st) __attribute__((always_inline)) {
+      load_rows_tile<D, NW>(ops.k + rm, t * TILE, st, wave, lane);
+      load_rows_tile<D, NW>(ops.v + rm, t * TILE, st + RT, wave, lane);
+      load_cols_tile<D, NW>(ops.kT + tb, Lp, t * TILE, st + 2 * RT, wave, lane);
+      if (GATE && wave == 0 && lane < TILE / 4)
+        __builtin_amdgcn_global_load_lds(
+            (global_void_ptr)(ops.gate2 + (size_t)bh * Lp + (size_t)t * TILE + 4 * lane),
+            (lds_void_ptr)(st + 2 * RT + CT), 16, 0, 0);
+      if (GATE && wave == 0 && lane < 2)  // the key tile's base, one 4-byte half per lane
+        __builtin_amdgcn_global_load_lds(
+            (global_void_ptr)(reinterpret_cast<const uint32_t*>(ops.gbase + (size_t)bh * (Lp / TILE) + t) +
+                              lane),
+            (lds_void_ptr)(st + 2 * RT + CT + TILE * 4), 4, 0, 0);
+    };
 
-  bf16x8 qop[KS], doop[KS];
-  const int ic = min(i, Lp - 1);
+    bf16x8 qop[KS], doop[KS];
+    const int ic = min(i, Lp - 1);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const size_t off = rm + (size_t)ic * D + 16 * ks + 8 * hf;
-    qop[ks] = *reinterpret_cast<const bf16x8*>(ops.qs + off);
-    doop[ks] = *reinterpret_cast<const bf16x8*>(ops.dout + off);
-  }
-  const float* srow = ops.stats + ((size_t)bh * (Lp / TILE) + ic / TILE) * (2 * TILE);
-  const float nl = srow[ic % TILE], nd = srow[TILE + ic % TILE];
-  f32x16 cl, cd, dqt[DB];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    cl[r] = nl;
-    cd[r] = nd;
-  }
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
-  const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
-  float rsum = 0.f;  // sum of dS over this lane's part of the query's row
-  // the gate base of the wave's query tile (its 32 queries share one)
-  const double gbase_q = GATE ? ops.gbase[(size_t)bh * (Lp / TILE) + min(qw / TILE, Lp / TILE - 1)]
-                              : 0.0;
-
-  // With a distance bias the walk starts at the first key tile that can
-  // hold a nonzero probability for these queries (every wave finds the same
-  // tile).
-  int n_lo = 0;
-  if constexpr (ALIBI) {
-    const float* ts = ops.tstat + (size_t)bh * (Lp / TILE) * 4;
-    float qwn = 0.f, cw = -INFINITY;
-    for (int u = q0 / TILE; u <= last_tile; ++u) {
-      qwn = fmaxf(qwn, ts[4 * u]);
-      cw = fmaxf(cw, ts[4 * u + 2]);
+    for (int ks = 0; ks < KS; ++ks) {
+      const size_t off = rm + (size_t)ic * D + 16 * ks + 8 * hf;
+      qop[ks] = *reinterpret_cast<const bf16x8*>(ops.qs + off);
+      doop[ks] = *reinterpret_cast<const bf16x8*>(ops.dout + off);
     }
-    n_lo = last_tile + 1;
-    for (int base = 0; base <= last_tile; base += 64) {
-      const int n = base + lane;
-      bool alive = false;
-      if (n <= last_tile) {
-        const float jb = fmaxf(slope2 * (float)(n * TILE), slope2 * (float)(n * TILE + TILE - 1));
-        alive = fmaf(qwn, ts[4 * n + 1], jb + cw) >= -ZGAP_B;
-      }
-      const uint64_t m = __ballot(alive);
-      if (m != 0) {
-        n_lo = base + (__ffsll((unsigned long long)m) - 1);
-        break;
-      }
-    }
-  }
-  if (n_lo <= last_tile) issue(n_lo, smem);
-  for (int n = n_lo; n <= last_tile; ++n) {
-    uint8_t* st = smem + ((n - n_lo) & 1) * STAGE;
-    wait_loads<0>();
-    __builtin_amdgcn_s_barrier();
-    if (n + 1 <= last_tile) issue(n + 1, smem + ((n - n_lo + 1) & 1) * STAGE);
-    if (n > last_w) continue;
-    const uint8_t* tk = st;
-    const uint8_t* tv = st + RT;
-    const uint8_t* tkT = st + 2 * RT;
-    const bool diag = (n == last_w);
-    // with gates: the (query tile, key tile) base difference joins -lse_i +
-    // the query's offset; the key offsets are subtracted per element below
-    f32x16 clt = cl;
-    if constexpr (GATE) {
-      const float dt =
-          (float)(gbase_q - *reinterpret_cast<const double*>(st + 2 * RT + CT + TILE * 4));
+    const float* srow = ops.stats + ((size_t)bh * (Lp / TILE) + ic / TILE) * (2 * TILE);
+    const float nl = srow[ic % TILE], nd = srow[TILE + ic % TILE];
+    f32x16 cl, cd, dqt[DB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) clt[r] += dt;
-    }
-    // S^T and dP'^T of the keys 32 kb .. 32 kb + 31 of the tile, then their
-    // dS^T (the B operands of dQ^T += K~^T dS^T)
-    auto first_products = [&](int kb, f32x16& sv, f32x16& dpv) __attribute__((always_inline)) {
-      sv = clt;
-      dpv = cd;
-      if constexpr (GATE) {  // minus the offset of the key of each element
-        const float* gp = reinterpret_cast<const float*>(st + 2 * RT + CT) + 32 * kb + 8 * hf;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const f32x4 ga = *reinterpret_cast<const f32x4*>(gp + 16 * h2);
-          const f32x4 gb = *reinterpret_cast<const f32x4*>(gp + 16 * h2 + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sv[8 * h2 + e] -= ga[e];
-            sv[8 * h2 + 4 + e] -= gb[e];
-          }
-        }
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sv = mfma32(lds_op<ROWB>(tk, 32 * kb + ln, 2 * ks + hf), qop[ks], sv);
-        dpv = mfma32(lds_op<ROWB>(tv, 32 * kb + ln, 2 * ks + hf), doop[ks], dpv);
-      }
-    };
-    // the distance bias (and on the diagonal tile the causal mask)
-    auto bias = [&](int kb, f32x16& sv, bool mask) __attribute__((always_inline)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jj = n * TILE + 32 * kb + 16 * (r >> 3) + 8 * hf + (r & 7);  // key of element r
-        if (ALIBI) sv[r] = fmaf(slope2, (float)(jj - i), sv[r]);
-        if (mask && jj > i) sv[r] = -INFINITY;
-      }
-    };
-    bf16x8 dsop[KS2];
-    auto scores = [&](int kb, const f32x16& sv, const f32x16& dpv) __attribute__((always_inline)) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        uint32_t wd[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = 8 * h2 + 2 * e + u;
-            x[u] = __builtin_amdgcn_exp2f(sv[r]) * dpv[r];
-          }
-          if (GATE) rsum += x[0] + x[1];
-          wd[e] = pack_bf16x2(x[0], x[1]);
-        }
-        u32x4 c = {wd[0], wd[1], wd[2], wd[3]};
-        dsop[2 * kb + h2] = __builtin_bit_cast(bf16x8, c);
-      }
-    };
-    if (!diag && D == 64) {
-      // No mask: both key blocks' products first, with no branch before the
-      // exponentials, so that the second block's products can overlap the
-      // first block's (same accumulation order: identical results).  At
-      // d = 128 the two blocks' S and dP' would not fit beside the second
-      // wave of the SIMD.
-      f32x16 s0, dp0, s1, dp1;
-      first_products(0, s0, dp0);
-      first_products(1, s1, dp1);
-      if (ALIBI) {
-        bias(0, s0, false);
-        bias(1, s1, false);
-      }
-      scores(0, s0, dp0);
-      scores(1, s1, dp1);
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        f32x16 sv, dpv;
-        first_products(kb, sv, dpv);
-        bias(kb, sv, true);
-        scores(kb, sv, dpv);
-      }
+    for (int r = 0; r < 16; ++r) {
+      cl[r] = nl;
+      cd[r] = nd;
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int ks2 = 0; ks2 < KS2; ++ks2)
-        dqt[db] = mfma32(lds_op<COLB>(tkT, 32 * db + ln, 2 * ks2 + hf), dsop[ks2], dqt[db]);
-  }
+      for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
+    const float slope2 = ALIBI ? alibi[h] * LOG2E : 0.f;
+    float rsum = 0.f;  // sum of dS over this lane's part of the query's row
+    // the gate base of the wave's query tile (its 32 queries share one)
+    const double gbase_q = GATE ? ops.gbase[(size_t)bh * (Lp / TILE) + min(qw / TILE, Lp / TILE - 1)]
+                                : 0.0;
 
-  if constexpr (GATE) {  // lanes ln and ln + 32 hold the two halves of the row
-    rsum += __shfl_xor(rsum, 32);
-    if (hf == 0 && i < L) ops.rowsum[(size_t)bh * Lp + i] = rsum;
+    // With a distance bias the walk starts at the first key tile that can
+    // hold a nonzero probability for these queries (every wave finds the same
+    // tile).
+    int n_lo = 0;
+    if constexpr (ALIBI) {
+      const float* ts = ops.tstat + (size_t)bh * (Lp / TILE) * 4;
+      float qwn = 0.f, cw = -INFINITY;
+      for (int u = q0 / TILE; u <= last_tile; ++u) {
+        qwn = fmaxf(qwn, ts[4 * u]);
+        cw = fmaxf(cw, ts[4 * u + 2]);
+      }
+      n_lo = last_tile + 1;
+      for (int base = 0; base <= last_tile; base += 64) {
+        const int n = base + lane;
+        bool alive = false;
+        if (n <= last_tile) {
+          const float jb = fmaxf(slope2 * (float)(n * TILE), slope2 * (float)(n * TILE + TILE - 1));
+          alive = fmaf(qwn, ts[4 * n + 1], jb + cw) >= -ZGAP_B;
+        }
+        const uint64_t m = __ballot(alive);
+        if (m != 0) {
+          n_lo = base + (__ffsll((unsigned long long)m) - 1);
+          break;
+        }
+      }
+    }
+    if (n_lo <= last_tile) issue(n_lo, smem);
+    for (int n = n_lo; n <= last_tile; ++n) {
+      uint8_t* st = smem + ((n - n_lo) & 1) * STAGE;
+      wait_loads<0>();
+      __builtin_amdgcn_s_barrier();
+      if (n + 1 <= last_tile) issue(n + 1, smem + ((n - n_lo + 1) & 1) * STAGE);
+      if (n > last_w) continue;
+      const uint8_t* tk = st;
+      const uint8_t* tv = st + RT;
+      const uint8_t* tkT = st + 2 * RT;
+      const bool diag = (n == last_w);
+      // with gates: the (query tile, key tile) base difference joins -lse_i +
+      // the query's offset; the key offsets are subtracted per element below
+      f32x16 clt = cl;
+      if constexpr (GATE) {
+        const float dt =
+            (float)(gbase_q - *reinterpret_cast<const double*>(st + 2 * RT + CT + TILE * 4));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) clt[r] += dt;
+      }
+      // S^T and dP'^T of the keys 32 kb .. 32 kb + 31 of the tile, then their
+      // dS^T (the B operands of dQ^T += K~^T dS^T)
+      auto first_products = [&](int kb, f32x16& sv, f32x16& dpv) __attribute__((always_inline)) {
+        sv = clt;
+        dpv = cd;
+        if constexpr (GATE) {  // minus the offset of the key of each element
+          const float* gp = reinterpret_cast<const float*>(st + 2 * RT + CT) + 32 * kb + 8 * hf;
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const f32x4 ga = *reinterpret_cast<const f32x4*>(gp + 16 * h2);
+            const f32x4 gb = *reinterpret_cast<const f32x4*>(gp + 16 * h2 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sv[8 * h2 + e] -= ga[e];
+              sv[8 * h2 + 4 + e] -= gb[e];
+            }
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          sv = mfma32(lds_op<ROWB>(tk, 32 * kb + ln, 2 * ks + hf), qop[ks], sv);
+          dpv = mfma32(lds_op<ROWB>(tv, 32 * kb + ln, 2 * ks + hf), doop[ks], dpv);
+        }
+      };
+      // the distance bias (and on the diagonal tile the causal mask)
+      auto bias = [&](int kb, f32x16& sv, bool mask) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jj = n * TILE + 32 * kb + 16 * (r >> 3) + 8 * hf + (r & 7);  // key of element r
+          if (ALIBI) sv[r] = fmaf(slope2, (float)(jj - i), sv[r]);
+          if (mask && jj > i) sv[r] = -INFINITY;
+        }
+      };
+      bf16x8 dsop[KS2];
+      auto scores = [&](int kb, const f32x16& sv, const f32x16& dpv) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          uint32_t wd[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int r = 8 * h2 + 2 * e + u;
+              x[u] = __builtin_amdgcn_exp2f(sv[r]) * dpv[r];
+            }
+            if (GATE) rsum += x[0] + x[1];
+            wd[e] = pack_bf16x2(x[0], x[1]);
+          }
+          u32x4 c = {wd[0], wd[1], wd[2], wd[3]};
+          dsop[2 * kb + h2] = __builtin_bit_cast(bf16x8, c);
+        }
+      };
+      if (!diag && D == 64) {
+        // No mask: both key blocks' products first, with no branch before the
+        // exponentials, so that the second block's products can overlap the
+        // first block's (same accumulation order: identical results).  At
+        // d = 128 the two blocks' S and dP' would not fit beside the second
+        // wave of the SIMD.
+        f32x16 s0, dp0, s1, dp1;
+        first_products(0, s0, dp0);
+        first_products(1, s1, dp1);
+        if (ALIBI) {
+          bias(0, s0, false);
+          bias(1, s1, false);
+        }
+        scores(0, s0, dp0);
+        scores(1, s1, dp1);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          f32x16 sv, dpv;
+          first_products(kb, sv, dpv);
+          bias(kb, sv, true);
+          scores(kb, sv, dpv);
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int ks2 = 0; ks2 < KS2; ++ks2)
+          dqt[db] = mfma32(lds_op<COLB>(tkT, 32 * db + ln, 2 * ks2 + hf), dsop[ks2], dqt[db]);
+    }
+
+    if constexpr (GATE) {  // lanes ln and ln + 32 hold the two halves of the row
+      rsum += __shfl_xor(rsum, 32);
+      if (hf == 0 && i < L) ops.rowsum[(size_t)bh * Lp + i] = rsum;
+    }
+    if (i >= L) return;
+    const size_t row = ((size_t)bh * L + i) * D;
+    const float* th = theta + ((size_t)(b * Hphi + g) * L + i) * (D / 2);
+    float* dth = dtheta + ((size_t)bh * L + i) * (D / 2);
+    // dq~ = scale lambda_h sum dS k~ (the gradient of the unscaled q~), and
+    // q~ = q~s / (scale lambda_h log2 e): their product, the dTheta term, is
+    // that of the scaled query
+    grad_rows<DB>(dqt, scale, ops.qs + rm + (size_t)i * D, 1.f / (scale * LOG2E), th,
+                  (flags & ARP_ROTATE_QK) != 0, dq + row, dth, hf);
+  };
+  if constexpr (ALIBI) {
+    int bh, r;
+    if (!spread_slot((int)blockIdx.x, total_tiles / nqt, nqt, bh, r)) return;
+    run(bh, nqt - 1 - r);
+    return;
   }
-  if (i >= L) return;
-  const size_t row = ((size_t)bh * L + i) * D;
-  const float* th = theta + ((size_t)(b * Hphi + g) * L + i) * (D / 2);
-  float* dth = dtheta + ((size_t)bh * L + i) * (D / 2);
-  // dq~ = scale lambda_h sum dS k~ (the gradient of the unscaled q~), and
-  // q~ = q~s / (scale lambda_h log2 e): their product, the dTheta term, is
-  // that of the scaled query
-  grad_rows<DB>(dqt, scale, ops.qs + rm + (size_t)i * D, 1.f / (scale * LOG2E), th,
-                (flags & ARP_ROTATE_QK) != 0, dq + row, dth, hf);
+  const int per = (total_tiles + 7) / 8;
+  if constexpr (PAIR) {
+    // the c-th longest and the c-th shortest block of the XCD's share
+    const int x = (int)(blockIdx.x % 8), c = (int)(blockIdx.x / 8);
+    const int l1 = x * per + c, l2 = x * per + per - 1 - c;
+    run(l1 / nqt, nqt - 1 - l1 % nqt);
+    __syncthreads();  // every wave is done with the LDS stages before they are refilled
+    run(l2 / nqt, nqt - 1 - l2 % nqt);
+    return;
+  }
+  const int logical = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (logical >= total_tiles) return;
+  run(logical / nqt, nqt - 1 - logical % nqt);
 }
 
 // ---------------------------------------------------------------------------
@@ -1058,10 +1076,17 @@ hipError_t launch_bwd_grads(const Geometry& g, const BwdArgs& a, hipStream_t str
     const int nqt = (g.L + 32 * NQ - 1) / (32 * NQ);
     const int total = g.B * g.H * nqt;
     const long groups = (long)g.B * g.H * ((nqt + BWD_GROUP - 1) / BWD_GROUP);
-    const int grid = ALIBI ? (int)(((groups + 7) / 8) * 8 * BWD_GROUP) : ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NQ, ALIBI, GATE>), dim3(grid), dim3(NQ * 64), 0, stream,
-                       a.ops, a.theta, a.alibi, a.dq, a.dtheta, g.L, g.Lp, g.H, g.Hphi, nqt, total,
-                       fl, g.scale, g.hscale);
+    const bool paired = !ALIBI && total % 16 == 0 && total / 2 >= device_cus();
+    const int grid = ALIBI ? (int)(((groups + 7) / 8) * 8 * BWD_GROUP)
+                     : paired ? total / 2 : ((total + 7) / 8) * 8;
+    if (paired)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, NQ, ALIBI, GATE, !ALIBI>), dim3(grid), dim3(NQ * 64), 0,
+                         stream, a.ops, a.theta, a.alibi, a.dq, a.dtheta, g.L, g.Lp, g.H, g.Hphi,
+                         nqt, total, fl, g.scale, g.hscale);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, NQ, ALIBI, GATE, false>), dim3(grid), dim3(NQ * 64), 0,
+                         stream, a.ops, a.theta, a.alibi, a.dq, a.dtheta, g.L, g.Lp, g.H, g.Hphi,
+                         nqt, total, fl, g.scale, g.hscale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

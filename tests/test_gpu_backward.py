@@ -16,6 +16,8 @@ term summed; it is held to 2e-2 of its own scale for both the maximum and the
 rms error.  The forward's lse (fp32) is compared with the oracle's scores on
 sampled rows to 1e-3 (base-2 units: a 0.1% error in the softmax scale).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -150,6 +152,36 @@ def test_backward_two_thousand_tokens():
     w = wl.make("train_1k", batch=1, heads=2, seqlen=2048)
     flags = dict(rotate_qk=True, rotate_v=True)
     compare_all(w, flags, run_backward(w, _dout(w), **flags))
+
+
+@pytest.mark.parametrize("name", ["train_1k", "rope_8k_d128"])
+def test_backward_paired_blocks_match_unpaired(name):
+    """64 heads at 2000 tokens: the dQ pass pairs its 256-query blocks (64 x 8
+    = 512 blocks, half of them still fill the CUs) and the dK/dV pass its key
+    blocks; three of those heads alone pair neither.  A dQ block is computed
+    the same way in both, so dq (and the forward's lse) must agree bit for
+    bit.  A paired dK/dV workgroup walks its second key block up from the
+    diagonal instead of down from the last query tile, so dk, dv, dTheta and
+    dphi are the same fp32 sums in another order: each element within one
+    bf16 unit in the last place of itself plus 1e-6 of the largest element
+    (sums with cancellation)."""
+    w = wl.make(name, batch=1, heads=64, seqlen=2000)
+    dout = _dout(w)
+    flags = dict(rotate_qk=True, rotate_v=True)
+    big = run_backward(w, dout, **flags)
+    part = dataclasses.replace(w, heads=3, **{n: np.ascontiguousarray(getattr(w, n)[:, :3])
+                                              for n in ("q", "k", "v", "phi")})
+    small = run_backward(part, np.ascontiguousarray(dout[:, :3]), **flags)
+    for key in ("dq", "lse"):
+        assert np.array_equal(small[key].view(np.uint32), big[key][:, :3].view(np.uint32)), key
+    for key in ("dk", "dv", "dtheta", "dphi"):
+        a, b = small[key].astype(np.float64), big[key][:, :3].astype(np.float64)
+        m = float(np.abs(b).max())
+        excess = np.abs(a - b) - 2.0 ** -7 * np.abs(b)
+        say(f"[gpu] paired vs unpaired {key}: max |diff| {np.abs(a - b).max():.3e}, beyond 1 ulp "
+            f"{max(float(excess.max()), 0.0) / m:.3e} of max {m:.3e}")
+        # measured: at most 3e-8 of the largest element beyond one bf16 unit
+        assert float(excess.max()) <= 1e-6 * m, key
 
 
 @pytest.mark.parametrize("slopes", [(1.0, 0.25), (0.5, -0.002)], ids=["steep", "mixed-sign"])
