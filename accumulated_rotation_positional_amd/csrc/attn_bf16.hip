@@ -925,21 +925,24 @@ hipError_t launch_attn_bf16_fused(const Geometry& g, const uint16_t* q, const ui
                                   const uint16_t* v, const float* theta, const float* alibi,
                                   uint16_t* o, hipStream_t stream) {
   if (g.D == 64) {
-    // The 512-query shape on deep unbiased grids (the rule of the
-    // pre-rotation path) and with the distance bias (1 x 16 heads at 32768
-    // tokens: 3.50 against 4.30 ms for 4 waves x 32 queries, whose forward
-    // walk has no early stop here either); otherwise 4 waves x 32 queries
-    // (8 x 8 heads at 1024 tokens 51.2 -> 37.8 us, 1 x 8 at 16384 527 -> 452
-    // us).
+    // The 512-query shape on deep unbiased grids (the pre-rotation path's
+    // rule) and with the distance bias (1 x 16 heads at 32768 tokens: 3.50
+    // ms against 4.30 ms with 4 waves x 32 queries); otherwise 4 waves x 32
+    // queries (8 x 8 heads at 1024 tokens 51.2 -> 37.8 us, 1 x 8 at 16384
+    // tokens 527 -> 452 us).
     const long wg512 = (long)g.B * g.H * ((g.L + 511) / 512);
     const bool biased = (g.flags & ARP_ALIBI) != 0;
     if (biased || (g.L >= 4096 && wg512 >= 2L * device_cus()))
-      return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, g.L, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
-    return launch_bf16_cfg<64, 32, 4, 2, 2, true>(g, q, k, v, g.L, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
+      return launch_bf16_cfg<64, 64, 8, 2, 1, true>(g, q, k, v, g.L, nullptr, theta, alibi, nullptr,
+                                                    nullptr, o, nullptr, stream);
+    return launch_bf16_cfg<64, 32, 4, 2, 2, true>(g, q, k, v, g.L, nullptr, theta, alibi, nullptr,
+                                                  nullptr, o, nullptr, stream);
   }
-  // d = 128: one shape (the 4 x 32 one stages four 16-byte pieces per thread
-  // and was slower on 8 x 8 heads at 1024 tokens: 62.3 against 51.1 us)
-  return launch_bf16_cfg<128, 32, 8, 2, 1, true>(g, q, k, v, g.L, nullptr, theta, alibi, nullptr, nullptr, o, nullptr, stream);
+  // d = 128: one shape (4 waves x 32 queries stage four 16-byte pieces per
+  // thread and were slower on 8 x 8 heads at 1024 tokens: 62.3 against 51.1
+  // us)
+  return launch_bf16_cfg<128, 32, 8, 2, 1, true>(g, q, k, v, g.L, nullptr, theta, alibi, nullptr,
+                                                 nullptr, o, nullptr, stream);
 }
 
 }  // namespace arp
