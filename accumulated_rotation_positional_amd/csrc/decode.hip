@@ -342,6 +342,17 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   const int tid = threadIdx.x;
   const int p = tid % P, cg = tid / P;
   const float* src = part + (size_t)bh * nchunk * (D + 2);
+  // the epilogue's own operands, loaded before the partials so that their
+  // latency is not added after the merge (this workgroup is the only one that
+  // writes the state and the gate state of its stream)
+  const size_t sidx = (size_t)(b * Hphi + g) * P + p;
+  const bool advance = cg == 0 && (Hphi != 1 || h == 0);
+  const float th = (cg == 0 && (flags & ARP_ROTATE_V)) ? theta[sidx] : 0.f;
+  const float ph = advance ? phi[sidx] : 0.f;
+  const uint64_t st = advance ? state[sidx] : 0;
+  const bool gadv = gstate != nullptr && tid == 0;
+  const float lf = gadv ? logf[bh] : 0.f;
+  const double gs = gadv ? gstate[bh] : 0.0;
   // every chunk holds at least one key, so its maximum is finite; a trip
   // always holds its first chunk (c0 < nchunk)
   float M = -INFINITY, Ls = 0.f, a0 = 0.f, a1 = 0.f;
@@ -395,18 +406,17 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   }
   const float inv = 1.f / Ls;
   float x0 = a0 * inv, x1 = a1 * inv;
-  const size_t sidx = (size_t)(b * Hphi + g) * P + p;
   if (flags & ARP_ROTATE_V) {
     float sn, cs;
-    sincosf(theta[sidx], &sn, &cs);
+    sincosf(th, &sn, &cs);
     rotate_pair(x0, x1, cs, -sn);
   }
   *reinterpret_cast<uint32_t*>(o + (size_t)bh * D + 2 * p) = pack_bf16x2(x0, x1);
   // advance the state (one workgroup per angle stream; no other workgroup of
   // this kernel reads it)
-  if (Hphi != 1 || h == 0) state[sidx] = (state[sidx] + to_fixed(phi[sidx])) & MASK48;
+  if (advance) state[sidx] = (st + to_fixed(ph)) & MASK48;
   // and the gate state (one workgroup per (b, h))
-  if (gstate != nullptr && tid == 0) gstate[bh] += (double)fminf(logf[bh], 0.f);
+  if (gadv) gstate[bh] = gs + (double)fminf(lf, 0.f);
 }
 
 template <int D, bool ALIBI, bool GATE>
