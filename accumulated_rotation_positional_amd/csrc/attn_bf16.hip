@@ -42,7 +42,8 @@
 //    staging, the value-transport epilogue) is the hardware sine and cosine
 //    of turns (__sincosf), absolute error below 3e-7 on the scan's [-pi, pi).
 //  * The running maximum is subtracted inside the matrix-core product (the
-//    accumulator input is -m, kept in registers), and it is only raised when
+//    accumulator input is -m, kept in registers; on the biased walk it also
+//    carries each logit's distance bias), and it is only raised when
 //    a row's tile maximum exceeds it by more than TAU = 8 (so 2^(s-m) <= 256):
 //    most tiles need no rescale of the output accumulator.  Row sums are
 //    formed from the bf16 probabilities with v_dot2_f32_bf16.
@@ -434,6 +435,27 @@ __device__ __forceinline__ void attn_tile(
   f32x16 s[KB][QB];      // logits of the tile in flight
   bf16x8 pop[KS2][QB];   // its probabilities, P^T operand layout
 
+  // With the distance bias on the diagonal-first walk, the bias rides in the
+  // accumulator input of Q K^T with -m: one fused multiply-add per element
+  // before the products instead of two operations after them, and without
+  // gates the pass over the logits after the products (soft, below) is left
+  // to the diagonal tile's mask
+  f32x16 cb[(ALIBI && DESC) ? KB : 1][(ALIBI && DESC) ? QB : 1];
+  auto bias_init = [&](int t) __attribute__((always_inline)) {
+    const int j0 = t * BN;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int base = j0 + 8 * hf - (qw + 32 * qb + ln);  // key - query minus koff
+        const float fbm = fmaf(slope2, (float)base, cneg[qb][0]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int koff = 32 * kb + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
+          cb[kb][qb][r] = fmaf(slope2, (float)koff, fbm);
+        }
+      }
+  };
   auto qk = [&](int n) __attribute__((always_inline)) {
     const uint8_t* kt = smem + (n % NST) * STAGE;
     // S^T - m = K~ Q~^T + cneg
@@ -446,7 +468,7 @@ __device__ __forceinline__ void attn_tile(
         ka[ks] = *reinterpret_cast<const bf16x8*>(kt + row * KROW + (((2 * ks + hf) ^ swz<KROW>(row)) << 4));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        s[kb][qb] = mfma32(ka[0], qop[qb][0], cneg[qb]);
+        s[kb][qb] = mfma32(ka[0], qop[qb][0], (ALIBI && DESC) ? cb[kb][qb] : cneg[qb]);
 #pragma unroll
         for (int ks = 1; ks < KS; ++ks) s[kb][qb] = mfma32(ka[ks], qop[qb][ks], s[kb][qb]);
       }
@@ -462,7 +484,7 @@ __device__ __forceinline__ void attn_tile(
     // Element r of s[kb][qb] on this lane is key j0 + koff(kb, r) + 8 hf,
     // koff = 32 kb + 16 (r>>3) + 4 ((r>>2)&1) + (r&3); query qw + 32 qb + ln.
     const bool diag = (t == last_w);
-    if (ALIBI || FORGET || diag) {
+    if ((ALIBI && !DESC) || FORGET || diag) {
       const float* gt = reinterpret_cast<const float*>(smem + (n % NST) * STAGE + KTILE + VTILE);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -483,7 +505,7 @@ __device__ __forceinline__ void attn_tile(
               const int r = 8 * h2 + e;
               const int koff = 32 * kb + 16 * h2 + 4 * (e >> 2) + (e & 3);
               float x = s[kb][qb][r];
-              if (ALIBI) x += fmaf(slope2, (float)koff, fb);
+              if (ALIBI && !DESC) x += fmaf(slope2, (float)koff, fb);
               if (FORGET) x -= (e < 4 ? ga[e] : gc[e - 4]);  // G_i - G_j's other terms rode in
               if (diag && koff + base > 0) x = -INFINITY;
               s[kb][qb][r] = x;
@@ -694,6 +716,7 @@ __device__ __forceinline__ void attn_tile(
           if (__all(dead)) {
             wave_done = true;
           } else {
+            if constexpr (ALIBI) bias_init(t);
             qk(n);
             soft(n, t, first);
             pv(n);
