@@ -435,26 +435,37 @@ __device__ __forceinline__ void attn_tile(
   f32x16 s[KB][QB];      // logits of the tile in flight
   bf16x8 pop[KS2][QB];   // its probabilities, P^T operand layout
 
-  // With the distance bias on the diagonal-first walk, the bias rides in the
-  // accumulator input of Q K^T with -m: one fused multiply-add per element
-  // before the products instead of two operations after them, and without
-  // gates the pass over the logits after the products (soft, below) is left
-  // to the diagonal tile's mask
-  f32x16 cb[(ALIBI && DESC) ? KB : 1][(ALIBI && DESC) ? QB : 1];
-  auto bias_init = [&](int t) __attribute__((always_inline)) {
+  // On the diagonal-first (biased) walk the biases ride in the accumulator
+  // input of Q K^T with -m: per element the distance bias (one fused
+  // multiply-add) and minus the key's gate offset (one subtraction), formed
+  // before the products, so the pass over the logits after them (soft,
+  // below) is left to the diagonal tile's mask
+  f32x16 cb[DESC ? KB : 1][DESC ? QB : 1];
+  auto bias_init = [&](int n, int t) __attribute__((always_inline)) {
     const int j0 = t * BN;
+    const float* gt = reinterpret_cast<const float*>(smem + (n % NST) * STAGE + KTILE + VTILE);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb) {
+      // the gate offsets of this lane's keys: 16 h2 + 8 hf + e of the block
+      f32x4 gk[4] = {};
+      if constexpr (FORGET) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          gk[u] = *reinterpret_cast<const f32x4*>(gt + 32 * kb + 16 * (u >> 1) + 8 * hf + 4 * (u & 1));
+      }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int base = j0 + 8 * hf - (qw + 32 * qb + ln);  // key - query minus koff
-        const float fbm = fmaf(slope2, (float)base, cneg[qb][0]);
+        const float fbm = ALIBI ? fmaf(slope2, (float)base, cneg[qb][0]) : cneg[qb][0];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int koff = 32 * kb + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
-          cb[kb][qb][r] = fmaf(slope2, (float)koff, fbm);
+          float c = ALIBI ? fmaf(slope2, (float)koff, fbm) : fbm;
+          if (FORGET) c -= gk[r >> 2][r & 3];
+          cb[kb][qb][r] = c;
         }
       }
+    }
   };
   auto qk = [&](int n) __attribute__((always_inline)) {
     const uint8_t* kt = smem + (n % NST) * STAGE;
@@ -468,7 +479,7 @@ __device__ __forceinline__ void attn_tile(
         ka[ks] = *reinterpret_cast<const bf16x8*>(kt + row * KROW + (((2 * ks + hf) ^ swz<KROW>(row)) << 4));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        s[kb][qb] = mfma32(ka[0], qop[qb][0], (ALIBI && DESC) ? cb[kb][qb] : cneg[qb]);
+        s[kb][qb] = mfma32(ka[0], qop[qb][0], DESC ? cb[kb][qb] : cneg[qb]);
 #pragma unroll
         for (int ks = 1; ks < KS; ++ks) s[kb][qb] = mfma32(ka[ks], qop[qb][ks], s[kb][qb]);
       }
@@ -484,18 +495,12 @@ __device__ __forceinline__ void attn_tile(
     // Element r of s[kb][qb] on this lane is key j0 + koff(kb, r) + 8 hf,
     // koff = 32 kb + 16 (r>>3) + 4 ((r>>2)&1) + (r&3); query qw + 32 qb + ln.
     const bool diag = (t == last_w);
-    if ((ALIBI && !DESC) || FORGET || diag) {
-      const float* gt = reinterpret_cast<const float*>(smem + (n % NST) * STAGE + KTILE + VTILE);
+    if ((ALIBI && !DESC) || diag) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           // elements r = 8 h2 + e: keys koff + 8 hf, koff = 32 kb + 16 h2 + e (+4 for e >= 4)
-          f32x4 ga = {}, gc = {};
-          if constexpr (FORGET) {
-            ga = *reinterpret_cast<const f32x4*>(gt + 32 * kb + 16 * h2 + 8 * hf);
-            gc = *reinterpret_cast<const f32x4*>(gt + 32 * kb + 16 * h2 + 8 * hf + 4);
-          }
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             const int base = j0 + 8 * hf - (qw + 32 * qb + ln);  // key - query minus koff
@@ -506,7 +511,6 @@ __device__ __forceinline__ void attn_tile(
               const int koff = 32 * kb + 16 * h2 + 4 * (e >> 2) + (e & 3);
               float x = s[kb][qb][r];
               if (ALIBI && !DESC) x += fmaf(slope2, (float)koff, fb);
-              if (FORGET) x -= (e < 4 ? ga[e] : gc[e - 4]);  // G_i - G_j's other terms rode in
               if (diag && koff + base > 0) x = -INFINITY;
               s[kb][qb][r] = x;
             }
@@ -716,7 +720,7 @@ __device__ __forceinline__ void attn_tile(
           if (__all(dead)) {
             wave_done = true;
           } else {
-            if constexpr (ALIBI) bias_init(t);
+            bias_init(n, t);
             qk(n);
             soft(n, t, first);
             pv(n);
