@@ -66,8 +66,12 @@ constexpr float TAU = 8.0f;   // lazy-rescale threshold (base-2 logits)
 // every one of them is exactly zero, so skipping the tile changes no bit.
 constexpr float ZGAP = 160.0f;
 // Adjacent query tiles of one head that a biased launch places on one XCD at
-// the same time (they share key/value tiles in its L2).
-constexpr int SPREAD_GROUP = 8;
+// the same time (they share key/value tiles in its L2): 8 at d = 64, 4 at d =
+// 128, where a tile's K/V walk holds twice the bytes (4 x 8 heads at 8192
+// tokens with ALiBi: 436 us with groups of 8, 398 us with 4; at d = 64 groups
+// of 4 or 16 were no faster).
+template <int D>
+constexpr int spread_group() { return D == 64 ? 8 : 4; }
 
 // qr is the raw q ([B, H, L, D]), rotated and scaled in the prologue.
 // FUSED = false: k~ (L padded to Lp) comes pre-rotated from the rotation pass,
@@ -130,7 +134,7 @@ __device__ __forceinline__ void attn_tile(
   const int nbh = total_tiles / nqt;
   int bh, qt;
   if constexpr (SPREAD) {
-    // Spread: groups of SPREAD_GROUP adjacent query tiles of one head, dealt
+    // Spread: groups of SG adjacent query tiles of one head, dealt
     // round-robin over the XCDs (blockIdx % 8) in dispatch order, so that a
     // group's workgroups run at the same time on one XCD and share the key
     // and value tiles of their overlapping walks in its L2, while the heads
@@ -138,10 +142,11 @@ __device__ __forceinline__ void attn_tile(
     // r deals the r-th group from the end of every head, rotated by r so that
     // a head does not stay on one XCD from round to round.
     const int x = logical % 8, m = logical / 8;
-    const int gi = (m / SPREAD_GROUP) * 8 + x;
+    constexpr int SG = spread_group<D>();
+    const int gi = (m / SG) * 8 + x;
     const int rnd = gi / nbh;
     bh = (gi % nbh + rnd) % nbh;
-    qt = nqt - 1 - (rnd * SPREAD_GROUP + m % SPREAD_GROUP);
+    qt = nqt - 1 - (rnd * SG + m % SG);
     if (qt < 0) return;
   } else {
     if (logical >= total_tiles) return;
@@ -859,11 +864,12 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
   const bool pair_ok = (QPW == 64 && NW == 8) ||
                        (QPW == 32 && NW == 4 && g.L <= 8192 && total / 2 >= device_cus());
   const bool paired = CAN_PAIR && pair_ok && bias == 0 && total % 16 == 0;
-  // spread (biased, pre-rotation): every head's groups of SPREAD_GROUP query
+  // spread (biased, pre-rotation): every head's groups of SG query
   // tiles, a whole number of rounds over the 8 XCDs
-  const long groups = (long)g.B * g.H * ((nqt + SPREAD_GROUP - 1) / SPREAD_GROUP);
+  constexpr int SG = spread_group<D>();
+  const long groups = (long)g.B * g.H * ((nqt + SG - 1) / SG);
   const int grid = paired ? total / 2
-                   : (bias != 0 && !FUSED) ? (int)(((groups + 7) / 8) * 8 * SPREAD_GROUP)
+                   : (bias != 0 && !FUSED) ? (int)(((groups + 7) / 8) * 8 * SG)
                                            : ((total + 7) / 8) * 8;
   const int rqk = (g.flags & ARP_ROTATE_QK) ? 1 : 0;
   const float qscale = g.scale * LOG2E;
