@@ -297,7 +297,7 @@ __device__ __forceinline__ void grad_rows(const f32x16 (&acc)[DB], float mul, co
 // one XCD and shares its walks' operand tiles in L2, while heads whose walks
 // stop at different depths are spread over the XCDs.  r: the block's rank from
 // the longest walk; false for a slot past the last block.
-constexpr int BWD_GROUP = 8;
+constexpr int BWD_GROUP = 4;
 __device__ __forceinline__ bool spread_slot(int slot, int nbh, int nblk, int& bh, int& r) {
   const int x = slot % 8, m = slot / 8;
   const int gi = (m / BWD_GROUP) * 8 + x;
