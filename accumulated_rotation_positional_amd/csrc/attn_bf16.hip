@@ -856,13 +856,19 @@ hipError_t launch_bf16_cfg(const Geometry& g, const uint16_t* qr, const uint16_t
   // long (2 x 8 heads at 8192 tokens, d = 64: 182 -> 157 us; 8 x 8 at 2048:
   // 70 -> 56 us; at 16384 tokens the shorter unpaired walks keep a head's
   // K/V tiles shared in L2 better: 292 against 306 us).
+  // The d = 128 8-wave shape pairs where its grid holds two or three
+  // workgroups per CU (1 x 16 heads at 8192 tokens: 254 -> 239 us; 1 x 32:
+  // 510 -> 493 us; at four and more, rope_8k_d128's 4 x 32 heads, it stays
+  // unpaired: 2028 against 2030 us).
   // With the rotation fused into the staging the 4 x 32 shape pairs by the
   // same rule (8 x 8 heads at 2048 tokens 93.6 -> 82.1 us, 2 x 8 at 4096
   // 122.5 -> 95.7 us); the 512-query fused walk does not pair (2 x 8 heads
   // at 16384 tokens: 610 against 766 us paired).
-  constexpr bool CAN_PAIR = (QPW == 64 && NW == 8 && !FUSED) || (QPW == 32 && NW == 4);
+  constexpr bool CAN_PAIR = (QPW == 64 && NW == 8 && !FUSED) || (QPW == 32 && NW == 4) ||
+                           (QPW == 32 && NW == 8 && !FUSED);
   const bool pair_ok = (QPW == 64 && NW == 8) ||
-                       (QPW == 32 && NW == 4 && g.L <= 8192 && total / 2 >= device_cus());
+                       (QPW == 32 && NW == 4 && g.L <= 8192 && total / 2 >= device_cus()) ||
+                       (QPW == 32 && NW == 8 && total / 2 >= device_cus() && total / 2 < 4 * device_cus());
   const bool paired = CAN_PAIR && pair_ok && bias == 0 && total % 16 == 0;
   // spread (biased, pre-rotation): every head's groups of SG query
   // tiles, a whole number of rounds over the 8 XCDs
