@@ -440,12 +440,14 @@ __device__ __forceinline__ void attn_tile(
   f32x16 s[KB][QB];      // logits of the tile in flight
   bf16x8 pop[KS2][QB];   // its probabilities, P^T operand layout
 
-  // On the diagonal-first (biased) walk the biases ride in the accumulator
-  // input of Q K^T with -m: per element the distance bias (one fused
-  // multiply-add) and minus the key's gate offset (one subtraction), formed
-  // before the products, so the pass over the logits after them (soft,
-  // below) is left to the diagonal tile's mask
-  f32x16 cb[DESC ? KB : 1][DESC ? QB : 1];
+  // On the diagonal-first (biased) walk, and with the distance bias on the
+  // fused walk, the biases ride in the accumulator input of Q K^T with -m:
+  // per element the distance bias (one fused multiply-add) and minus the
+  // key's gate offset (one subtraction), formed before the products, so the
+  // pass over the logits after them (soft, below) is left to the diagonal
+  // tile's mask
+  constexpr bool CB = DESC || (FUSED && ALIBI);
+  f32x16 cb[CB ? KB : 1][CB ? QB : 1];
   auto bias_init = [&](int n, int t) __attribute__((always_inline)) {
     const int j0 = t * BN;
     const float* gt = reinterpret_cast<const float*>(smem + (n % NST) * STAGE + KTILE + VTILE);
@@ -484,7 +486,7 @@ __device__ __forceinline__ void attn_tile(
         ka[ks] = *reinterpret_cast<const bf16x8*>(kt + row * KROW + (((2 * ks + hf) ^ swz<KROW>(row)) << 4));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        s[kb][qb] = mfma32(ka[0], qop[qb][0], DESC ? cb[kb][qb] : cneg[qb]);
+        s[kb][qb] = mfma32(ka[0], qop[qb][0], CB ? cb[kb][qb] : cneg[qb]);
 #pragma unroll
         for (int ks = 1; ks < KS; ++ks) s[kb][qb] = mfma32(ka[ks], qop[qb][ks], s[kb][qb]);
       }
@@ -500,7 +502,7 @@ __device__ __forceinline__ void attn_tile(
     // Element r of s[kb][qb] on this lane is key j0 + koff(kb, r) + 8 hf,
     // koff = 32 kb + 16 (r>>3) + 4 ((r>>2)&1) + (r&3); query qw + 32 qb + ln.
     const bool diag = (t == last_w);
-    if ((ALIBI && !DESC) || diag) {
+    if (diag) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -509,13 +511,11 @@ __device__ __forceinline__ void attn_tile(
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             const int base = j0 + 8 * hf - (qw + 32 * qb + ln);  // key - query minus koff
-            const float fb = slope2 * (float)base;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int r = 8 * h2 + e;
               const int koff = 32 * kb + 16 * h2 + 4 * (e >> 2) + (e & 3);
               float x = s[kb][qb][r];
-              if (ALIBI && !DESC) x += fmaf(slope2, (float)koff, fb);
               if (diag && koff + base > 0) x = -INFINITY;
               s[kb][qb][r] = x;
             }
@@ -748,6 +748,7 @@ __device__ __forceinline__ void attn_tile(
     for (int n = 0; n <= last_tile; ++n) {
       if (n + 1 <= last_tile) fetch(n + 1);
       if (n <= last_w) {
+        if constexpr (ALIBI) bias_init(n, n);
         qk(n);
         soft(n, n, n == 0);
         pv(n);
